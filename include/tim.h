@@ -1,0 +1,262 @@
+/*
+ * tim.h — batch-invariant selected-token log-probabilities and
+ * training/rollout mismatch ("TIM") statistics for AMD Instinct MI355X
+ * (gfx950).  C ABI of libtim.so.
+ *
+ * What is computed (sources are the pages this library follows; each entry
+ * point below names the passage that defines it):
+ *
+ *   logits  z[t,v] = sum_k h[t,k] * W[v,k]           (LM head, no bias)
+ *   logp[t]        = z[t, a_t] - log sum_v exp z[t,v] (log-softmax + gather)
+ *
+ *     "RL: Training Inference Mismatch", section "log p": the chain
+ *     final hidden states -> LM head -> logits -> log-softmax -> gather of
+ *     the realised token id, and its PyTorch rendering with log_softmax and
+ *     gather along the vocabulary axis.
+ *
+ *   delta_t = logp_train[t] - logp_rollout[t],  r_t = exp(delta_t),
+ *   k1 = -delta, k2 = delta^2 / 2, k3 = (r - 1) - delta,
+ *   token-level truncated IS weight, per-sequence geometric-mean-ratio
+ *   rejection and the batch monitoring aggregates.
+ *
+ *     "Diagnosing Training Inference Mismatch in LLM Reinforcement Learning
+ *     (VeXact)", eq. (1) (token-level TIM), the K1/K3 estimators and the
+ *     "Algorithmic TIM Compensation Results" table (TIS and r_corr-based
+ *     sequence rejection); "训推一致性与 determinism" (LLM Infra Atlas),
+ *     section 2 (Delta_t and r_t = e^Delta_t); "RL: Training Inference
+ *     Mismatch", section on the three KL estimators and the monitoring
+ *     flow (per-token KL, mean per completion, mean over the batch);
+ *     "Train-Inference Consistency" (LoongSage), section 5 (metric names
+ *     is_approx_k3_kl, is_clip_ratio, is_nan_ratio) and section 4 (IS
+ *     correction clips out-of-bound weights).
+ *
+ * Determinism contract.  For one build and one device, every output bit of
+ * tim_logprob_forward for row t depends only on (h[t,:], W, a_t, V, D,
+ * dtype, flags): not on N, not on the row's position in the batch and not
+ * on the other rows ("训推一致性与 determinism", section 1.2, batch
+ * invariance).  Repeated calls return identical bits (same page, 1.1).
+ * The per-sequence outputs of tim_mismatch_stats depend only on that
+ * sequence's tokens; batch aggregates are reduced in a fixed order.
+ *
+ * Memory.  Every pointer is DEVICE memory unless marked (host).  The caller
+ * owns every buffer; the library never allocates device memory and keeps
+ * no pointer after a call returns.  Scratch memory is passed in as a
+ * workspace whose size is returned by the *_workspace_bytes query.
+ *
+ * Execution.  Calls enqueue kernels on `stream` (a hipStream_t; NULL means
+ * the null stream) and return without synchronising.  They are re-entrant;
+ * two calls may share a workspace only if they are ordered on one stream.
+ *
+ * Errors.  Argument problems found on the host are reported before any
+ * launch, and then no output is written.  Data anomalies never fail a call:
+ * they are counted (out-of-range ids, non-finite log-ratios).
+ */
+#ifndef TIM_H
+#define TIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TIM_ABI_VERSION 1
+
+typedef enum {
+    TIM_OK = 0,
+    TIM_EINVAL = 1,        /* null required pointer, negative size, ld < d,
+                              bad dtype/flags, bad stats parameters        */
+    TIM_EUNSUPPORTED = 2,  /* d % 64 != 0, misaligned pointer or leading
+                              dimension (see tim_logprob_forward)          */
+    TIM_EWORKSPACE = 3,    /* workspace null or smaller than the query    */
+    TIM_EHIP = 4           /* a HIP launch or runtime call failed          */
+} tim_status;
+
+/* Element type shared by h and W. */
+typedef enum {
+    TIM_BF16 = 0,          /* bfloat16 inputs, fp32 MFMA accumulation      */
+    TIM_F32 = 1            /* fp32 inputs, fp32 MFMA ("FP32 LM head":
+                              "Train-Inference Consistency", section 3)    */
+} tim_dtype;
+
+/* Schedule flags for tim_logprob_forward. */
+enum {
+    TIM_SCHED_INVARIANT = 0u, /* vocabulary split and tile order are functions
+                                 of (V, D, dtype) only: batch invariant      */
+    TIM_SCHED_FREE = 1u       /* split chosen from N for speed; results are
+                                 deterministic for a fixed N but NOT batch
+                                 invariant.  Exists to price invariance.     */
+};
+
+/* Library version of this header (TIM_ABI_VERSION). */
+int tim_abi_version(void);
+
+/* Static, never-freed description of a status code; unknown codes give a
+ * generic string. */
+const char* tim_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Selected-token log-probabilities.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace tim_logprob_forward needs for these sizes.
+ * Returns 0 for sizes the library rejects (negative sizes, unknown dtype or
+ * flags).  Pure host function; never touches the device. */
+size_t tim_logprob_workspace_bytes(int64_t n, int64_t d, int64_t v,
+                                   int dtype, unsigned flags);
+
+/*
+ * logp[t] = log softmax(h[t,:] . W^T)[ids[t]]   for t in [0, n).
+ *
+ * Defined by "RL: Training Inference Mismatch", section "log p" (the
+ * hidden -> LM head -> log-softmax -> gather chain).  The caller passes the
+ * rows already shifted so that h[t] is the state whose next token is
+ * ids[t] (same page, section on shift and mask alignment).  No bias, no
+ * temperature, no logits processors: raw logits at temperature 1 (same
+ * page, section on logits processors, which asks for all processors off).
+ *
+ *  h          [n, d] row-major, leading dimension ldh (elements), dtype.
+ *  ldh        >= d; ldh % 8 == 0 (bf16) or % 4 == 0 (fp32).
+ *  w          [v, d] row-major (the nn.Linear [out, in] layout), ldw >= d,
+ *             same alignment rule as ldh.  h and w 16-byte aligned.
+ *  ids        [n] int32 target token ids.  An id outside [0, v) is not an
+ *             error: its logp is NaN and it is counted in *n_bad_ids.
+ *  n          rows, >= 0.  n == 0 returns TIM_OK without a launch.
+ *  d          hidden size, > 0, d % 64 == 0 (else TIM_EUNSUPPORTED).
+ *  v          vocabulary size, 1 <= v <= 2^31 - 1.
+ *  dtype      TIM_BF16 or TIM_F32.
+ *  flags      TIM_SCHED_INVARIANT or TIM_SCHED_FREE.
+ *  logp       [n] fp32 out.
+ *  lse        [n] fp32 out, nullable: log sum_v exp z[t,v].
+ *  n_bad_ids  [1] int32 out, nullable: number of ids outside [0, v).
+ *  workspace  device scratch of at least tim_logprob_workspace_bytes(...)
+ *             bytes, 256-byte aligned (else TIM_EWORKSPACE / TIM_EINVAL).
+ *  stream     hipStream_t to enqueue on (NULL = null stream).
+ *
+ * Arithmetic: products of bf16 (or fp32) inputs accumulate in fp32 in a
+ * fixed K order with no split-K; the log-sum-exp is carried in fp32 over
+ * vocabulary tiles in a fixed order and merged across vocabulary chunks in
+ * ascending chunk order.  The logits are never written to memory.
+ */
+int tim_logprob_forward(const void* h, int64_t ldh,
+                        const void* w, int64_t ldw,
+                        const int32_t* ids,
+                        int64_t n, int64_t d, int64_t v,
+                        int dtype, unsigned flags,
+                        float* logp, float* lse, int32_t* n_bad_ids,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Mismatch statistics between trainer and rollout log-probabilities.
+ * ---------------------------------------------------------------------- */
+
+/* (host) parameters of tim_mismatch_stats. */
+typedef struct {
+    double tis_clip_c; /* C > 0.  Token-level truncated IS weight
+                          w = min(e^delta, C); a token is "clipped" iff
+                          delta > log(C) (log(C) evaluated once, in fp64).
+                          "Train-Inference Consistency", section 4, and the
+                          TIS rows of the VeXact compensation table.       */
+    double seq_lo;     /* reject sequence iff mean delta < seq_lo ...      */
+    double seq_hi;     /* ... or mean delta > seq_hi; seq_lo <= seq_hi.
+                          Log-domain bounds: the geometric mean of r over a
+                          sequence's tokens is exp(mean delta), so a ratio
+                          window [a, b] is passed as [log a, log b].      */
+} tim_stats_params;
+
+/* (host struct) optional per-token outputs, each [n], each nullable.
+ * A position with mask == 0 is not scored: delta = 0, ratio = 1,
+ * k1 = k2 = k3 = 0, tis_w = 0, clipped = 0.  A scored position whose delta
+ * is not finite gets delta/ratio/k's as computed (NaN/inf), tis_w = 0 and
+ * clipped = 0. */
+typedef struct {
+    float* delta;      /* logp_train - logp_rollout (computed in fp64)     */
+    float* ratio;      /* exp(delta)                                       */
+    float* k1;         /* -delta                                           */
+    float* k2;         /* delta^2 / 2                                      */
+    float* k3;         /* exp(delta) - 1 - delta                           */
+    float* tis_w;      /* clipped ? C : exp(delta)                         */
+    uint8_t* clipped;  /* 1 iff delta > log C                              */
+} tim_token_out;
+
+/* (host struct) optional per-sequence outputs, each [s], each nullable.
+ * Means are over the sequence's valid tokens (mask != 0 and finite delta);
+ * a sequence with no valid token has means 0 and is never rejected. */
+typedef struct {
+    int32_t* n_valid;
+    int32_t* n_clipped;
+    int32_t* n_nan;        /* mask != 0 but delta not finite               */
+    double* mean_delta;
+    double* mean_k1;
+    double* mean_k2;
+    double* mean_k3;
+    double* mean_tis_w;
+    uint8_t* reject;       /* 1 iff mean_delta < seq_lo || > seq_hi        */
+} tim_seq_out;
+
+/* Indices of the batch aggregate vector (fp64).  Token means are over all
+ * valid tokens of the batch; sequence means are the mean, over sequences
+ * with at least one valid token, of the per-sequence means ("RL: Training
+ * Inference Mismatch", monitoring flow: mean per completion, then mean
+ * over completions).  Ratios with a zero denominator are 0. */
+enum {
+    TIM_B_TOK_MEAN_DELTA = 0,
+    TIM_B_TOK_MEAN_K1 = 1,
+    TIM_B_TOK_MEAN_K2 = 2,
+    TIM_B_TOK_MEAN_K3 = 3,     /* train/is_approx_k3_kl                    */
+    TIM_B_SEQ_MEAN_DELTA = 4,
+    TIM_B_SEQ_MEAN_K1 = 5,
+    TIM_B_SEQ_MEAN_K2 = 6,
+    TIM_B_SEQ_MEAN_K3 = 7,
+    TIM_B_TOK_MEAN_TIS_W = 8,
+    TIM_B_CLIP_RATIO = 9,      /* train/is_clip_ratio = n_clipped / n_valid */
+    TIM_B_NAN_RATIO = 10,      /* train/is_nan_ratio = n_nan / n_masked_in  */
+    TIM_B_REJECT_FRAC = 11,    /* rejected / sequences with a valid token  */
+    TIM_B_MEAN_ABS_DELTA = 12,
+    TIM_B_MAX_ABS_DELTA = 13,
+    TIM_B_N_VALID = 14,
+    TIM_B_N_NAN = 15,
+    TIM_B_N_CLIPPED = 16,
+    TIM_B_N_SEQ_NONEMPTY = 17,
+    TIM_B_N_SEQ_REJECTED = 18,
+    TIM_B_NFIELDS = 19
+};
+
+/* Bytes of device workspace tim_mismatch_stats needs; 0 for negative
+ * sizes.  Pure host function. */
+size_t tim_stats_workspace_bytes(int64_t n, int64_t s);
+
+/*
+ * Per-token log-ratio statistics, per-sequence means and rejection flags,
+ * and batch aggregates.
+ *
+ *  logp_train    [n] fp32: trainer-side log pi_old^train(a_t|s_t).
+ *  logp_rollout  [n] fp32: log pi_old^rollout(a_t|s_t) recorded at rollout.
+ *  mask          [n] uint8, nullable (= every token scored).  Tokens with
+ *                mask == 0 (prompt, padding) are left out of every sum.
+ *  cu_seqlens    [s+1] int32, 0 = c0 <= c1 <= ... <= cs = n (precondition,
+ *                not checked on the device): sequence j is [c_j, c_{j+1}).
+ *  n, s          tokens and sequences; n >= 0, s >= 1 unless n == 0.
+ *  p             (host) clip constant and rejection window.
+ *  tok, seq      (host structs) nullable; their members are nullable.
+ *  batch         [TIM_B_NFIELDS] fp64 out, nullable.
+ *  workspace     >= tim_stats_workspace_bytes(n, s) bytes, 256-byte aligned.
+ *
+ * delta is computed in fp64 from the fp32 inputs, so both signs and the
+ * clip decision are exact; exp/expm1 are evaluated in fp64.
+ */
+int tim_mismatch_stats(const float* logp_train, const float* logp_rollout,
+                       const uint8_t* mask, const int32_t* cu_seqlens,
+                       int64_t n, int64_t s, const tim_stats_params* p,
+                       const tim_token_out* tok, const tim_seq_out* seq,
+                       double* batch,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIM_H */

@@ -1,0 +1,193 @@
+"""fp64 CPU oracle for selected-token log-probabilities and mismatch statistics.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The library
+path (``invariant_logprobs_amd``) never imports it, and this package imports
+nothing from the library: the two share no code.
+
+The arithmetic lives in ``tim_oracle.c`` (plain C, fp64, sequential sums in
+the order the definitions give).  This module only builds that file with gcc
+and marshals numpy arrays into it.
+
+Functions and the passages they follow:
+
+* :func:`logprob` -- ``logp_t = z_t[a_t] - log sum_v exp z_t[v]`` with
+  ``z_t = W h_t``: "RL: Training Inference Mismatch", section "log p".
+* :func:`mismatch_stats` -- token-level TIM ``delta = train - rollout``
+  ("Diagnosing Training Inference Mismatch ... (VeXact)", eq. (1)), ratio,
+  k1/k2/k3 ("RL: Training Inference Mismatch", KL-estimator table), TIS
+  weight and clip flag ("Train-Inference Consistency", section 4), per-sequence
+  and batch means (same "RL" page, monitoring flow), geometric-mean-ratio
+  rejection (VeXact compensation table).
+* :func:`bf16_decode`, :func:`bf16_round_rne` -- bf16 <-> double, ties to
+  even ("Train-infer mismatch for Open-weight MoE RL", figure "Rounding
+  depends on the order of additions").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tim_oracle.c")
+_OUT_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_OUT_DIR, "libtim_oracle.so")
+
+BF16 = 0
+F32 = 1
+
+# Batch vector field names, in index order (restated from the definitions;
+# not imported from the library).
+BATCH_FIELDS = (
+    "tok_mean_delta", "tok_mean_k1", "tok_mean_k2", "tok_mean_k3",
+    "seq_mean_delta", "seq_mean_k1", "seq_mean_k2", "seq_mean_k3",
+    "tok_mean_tis_w", "clip_ratio", "nan_ratio", "reject_frac",
+    "mean_abs_delta", "max_abs_delta", "n_valid", "n_nan", "n_clipped",
+    "n_seq_nonempty", "n_seq_rejected",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``tim_oracle.c`` into ``_build/libtim_oracle.so`` with gcc."""
+    os.makedirs(_OUT_DIR, exist_ok=True)
+    if not force and os.path.exists(_LIB_PATH) and \
+            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+           "-pthread", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = build(force=False)
+        lib = ctypes.CDLL(path)
+        c_i64, c_int, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.or_bf16_decode.restype = ctypes.c_double
+        lib.or_bf16_decode.argtypes = [ctypes.c_uint16]
+        lib.or_bf16_round_rne.restype = ctypes.c_uint16
+        lib.or_bf16_round_rne.argtypes = [ctypes.c_double]
+        lib.or_available_cpus.restype = c_int
+        lib.or_batch_nfields.restype = c_int
+        lib.or_logprob_rows.restype = c_int
+        lib.or_logprob_rows.argtypes = [vp, c_i64, vp, c_i64, vp, c_int, c_i64,
+                                        c_i64, vp, c_i64, vp, vp, vp, c_int]
+        lib.or_mismatch_stats.restype = c_int
+        lib.or_mismatch_stats.argtypes = [vp, vp, vp, vp, c_i64, c_i64,
+                                          ctypes.c_double, ctypes.c_double,
+                                          ctypes.c_double] + [vp] * 17
+        assert lib.or_batch_nfields() == len(BATCH_FIELDS)
+        _lib = lib
+        return lib
+
+
+def available_cpus() -> int:
+    return int(_load().or_available_cpus())
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _as_host_array(x, dtype):
+    """numpy (or CPU torch) -> C-contiguous numpy array of ``dtype``."""
+    if hasattr(x, "detach"):  # torch tensor: raw bits for bf16
+        import torch  # local: only needed when called with tensors
+        x = x.detach().cpu()
+        if x.dtype == torch.bfloat16:
+            x = x.view(torch.int16).numpy().view(np.uint16)
+        else:
+            x = x.numpy()
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def bf16_decode(bits) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.or_bf16_decode(int(v)) for v in b], dtype=np.float64)
+
+
+def bf16_round_rne(x) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(x, dtype=np.float64).ravel()
+    return np.array([lib.or_bf16_round_rne(float(v)) for v in a], dtype=np.uint16)
+
+
+def logprob(h, w, ids, *, dtype: int, rows=None, nthreads: int = 0):
+    """fp64 ``(logp, lse, zsel)`` for token rows ``rows`` (default: all).
+
+    ``h``: [N, D] and ``w``: [V, D]; for ``dtype == BF16`` pass uint16 bit
+    patterns (or bf16 torch tensors), for ``F32`` float32.  ``ids``: [N]
+    int32.  Returns float64 arrays indexed like ``rows`` and the number of
+    threads used.
+    """
+    el = np.uint16 if dtype == BF16 else np.float32
+    h = _as_host_array(h, el)
+    w = _as_host_array(w, el)
+    ids = _as_host_array(ids, np.int32)
+    n, d = h.shape
+    v, d2 = w.shape
+    assert d == d2 and ids.shape == (n,)
+    if rows is None:
+        rows_arr = None
+        nr = n
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows_arr.ndim == 1 and (rows_arr.size == 0 or
+                                       (rows_arr.min() >= 0 and rows_arr.max() < n))
+        nr = rows_arr.size
+    logp = np.empty(nr, np.float64)
+    lse = np.empty(nr, np.float64)
+    zsel = np.empty(nr, np.float64)
+    if nr == 0:
+        return logp, lse, zsel, 0
+    used = _load().or_logprob_rows(_ptr(h), d, _ptr(w), d, _ptr(ids), dtype, d, v,
+                                   _ptr(rows_arr), nr, _ptr(logp), _ptr(lse),
+                                   _ptr(zsel), int(nthreads))
+    if used < 0:
+        raise ValueError("or_logprob_rows rejected its arguments")
+    return logp, lse, zsel, used
+
+
+def mismatch_stats(lt, lr, mask, cu_seqlens, *, clip_c: float, seq_lo: float,
+                   seq_hi: float) -> dict:
+    """fp64 token, sequence and batch statistics (see module docstring)."""
+    lt = _as_host_array(lt, np.float32)
+    lr = _as_host_array(lr, np.float32)
+    cu = _as_host_array(cu_seqlens, np.int32)
+    m = None if mask is None else _as_host_array(mask, np.uint8)
+    n = lt.size
+    s = cu.size - 1
+    tok = {k: np.empty(n, np.float64) for k in ("delta", "ratio", "k1", "k2", "k3", "tis_w")}
+    tok["clipped"] = np.empty(n, np.uint8)
+    seq = {k: np.empty(s, np.int32) for k in ("n_valid", "n_clipped", "n_nan")}
+    seq.update({k: np.empty(s, np.float64) for k in
+                ("mean_delta", "mean_k1", "mean_k2", "mean_k3", "mean_tis_w")})
+    seq["reject"] = np.empty(s, np.uint8)
+    batch = np.empty(len(BATCH_FIELDS), np.float64)
+    rc = _load().or_mismatch_stats(
+        _ptr(lt), _ptr(lr), _ptr(m), _ptr(cu), n, s, float(clip_c), float(seq_lo),
+        float(seq_hi),
+        _ptr(tok["delta"]), _ptr(tok["ratio"]), _ptr(tok["k1"]), _ptr(tok["k2"]),
+        _ptr(tok["k3"]), _ptr(tok["tis_w"]), _ptr(tok["clipped"]),
+        _ptr(seq["n_valid"]), _ptr(seq["n_clipped"]), _ptr(seq["n_nan"]),
+        _ptr(seq["mean_delta"]), _ptr(seq["mean_k1"]), _ptr(seq["mean_k2"]),
+        _ptr(seq["mean_k3"]), _ptr(seq["mean_tis_w"]), _ptr(seq["reject"]),
+        _ptr(batch))
+    if rc != 0:
+        raise ValueError("or_mismatch_stats rejected its arguments")
+    return {"token": tok, "seq": seq,
+            "batch": dict(zip(BATCH_FIELDS, (float(x) for x in batch)))}

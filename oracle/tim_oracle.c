@@ -1,0 +1,353 @@
+/*
+ * tim_oracle.c — plain, slow, fp64 CPU reference ("the oracle").
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load this file's library.  The HIP
+ * library never links, calls or includes it, and it includes nothing of the
+ * HIP library: the two share no code, headers, tables or constants.
+ *
+ * Everything here is the textbook definition written out in double
+ * precision, in the order the definitions state, with no blocking or fusion
+ * that changes the arithmetic:
+ *
+ *   or_logprob_rows     z_v = sum_k h_k W_vk (k ascending, fp64),
+ *                       lse = m + log sum_v exp(z_v - m) (v ascending),
+ *                       logp = z_a - lse.
+ *                       "RL: Training Inference Mismatch", section "log p"
+ *                       (hidden -> LM head -> log-softmax -> gather).
+ *   or_mismatch_stats   delta = train - rollout ("Diagnosing Training
+ *                       Inference Mismatch ... (VeXact)", eq. (1)),
+ *                       r = exp(delta) ("训推一致性与 determinism", section 2),
+ *                       k1 = -log r, k2 = (log r)^2 / 2, k3 = (r-1) - log r
+ *                       ("RL: Training Inference Mismatch", KL-estimator
+ *                       table; VeXact K1/K3), truncated IS weight and
+ *                       clip flag ("Train-Inference Consistency", section 4),
+ *                       per-sequence mean then batch mean ("RL: Training
+ *                       Inference Mismatch", monitoring flow, steps 2-3),
+ *                       geometric-mean-ratio sequence rejection (VeXact
+ *                       compensation table, r_corr-based rejection).
+ *   or_bf16_decode /    exact bf16 -> double, and double -> bf16 with
+ *   or_bf16_round_rne   round-to-nearest, ties-to-even ("Train-infer
+ *                       mismatch for Open-weight MoE RL", figure "Rounding
+ *                       depends on the order of additions").
+ *
+ * Readings where the pages leave a step open (sign of delta, clip form,
+ * NaN handling, empty sequences, log-domain rejection bounds) are the ones
+ * documented with the C ABI: delta = train - rollout; clipped iff
+ * delta > log C; non-finite delta is counted and left out of every sum;
+ * a sequence with no valid token has means 0 and is never rejected.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread -lm
+ * (no -ffast-math: IEEE semantics and the written summation order are kept).
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------ */
+/* bfloat16                                                            */
+/* ------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32: decode by placing the 16
+ * bits in the high half of a float.  Exact (every bf16 is a float, every
+ * float is a double). */
+double or_bf16_decode(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, and return its
+ * bits.  Written from the definition: find the two bf16 neighbours of |x|
+ * on the grid of its binade and pick the nearer, the even one on a tie. */
+uint16_t or_bf16_round_rne(double x)
+{
+    if (isnan(x)) return (uint16_t)0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    /* bf16: 8 exponent bits (bias 127), 7 stored fraction bits.
+     * Normal numbers span [2^-126, (2 - 2^-7) 2^127]; the subnormal grid
+     * spacing is 2^-133. */
+    int e;
+    frexp(a, &e);               /* a = m 2^e, m in [0.5, 1) */
+    int unit_exp = e - 8;       /* 8 significant bits: spacing 2^(e-8) */
+    if (unit_exp < -133) unit_exp = -133;   /* subnormal range */
+    double scaled = ldexp(a, -unit_exp);    /* exact: power-of-two scale */
+    double q = floor(scaled);
+    double rem = scaled - q;                /* exact */
+    if (rem > 0.5 || (rem == 0.5 && fmod(q, 2.0) != 0.0)) q += 1.0;
+    double r = ldexp(q, unit_exp);
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);  /* inf */
+    float f = (float)r;         /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFF));
+}
+
+/* ------------------------------------------------------------------ */
+/* Selected-token log-probability                                      */
+/* ------------------------------------------------------------------ */
+
+enum { OR_BF16 = 0, OR_F32 = 1 };
+
+static double load_elem(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == OR_BF16) return or_bf16_decode(((const uint16_t*)base)[idx]);
+    return (double)((const float*)base)[idx];
+}
+
+typedef struct {
+    const void* h; int64_t ldh;
+    const void* w; int64_t ldw;
+    const int32_t* ids;
+    int dtype; int64_t d, v;
+    const int64_t* rows;   /* NULL: rows 0..nrows-1 */
+    int64_t nrows;
+    double* logp; double* lse; double* zsel;
+    int64_t begin, end;    /* slice of the row list owned by one thread */
+} lp_job;
+
+/* Rows handled together share one pass over W (cache reuse only: each
+ * logit is still one sequential fp64 sum over k). */
+#define OR_ROW_BLOCK 8
+
+static void* lp_worker(void* arg)
+{
+    lp_job* j = (lp_job*)arg;
+    const int64_t d = j->d, v = j->v;
+    double* hd = (double*)malloc(sizeof(double) * (size_t)(OR_ROW_BLOCK * d));
+    double* wd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* z = (double*)malloc(sizeof(double) * (size_t)(OR_ROW_BLOCK * v));
+    if (!hd || !wd || !z) {
+        for (int64_t i = j->begin; i < j->end; ++i) j->logp[i] = NAN;
+        free(hd); free(wd); free(z);
+        return NULL;
+    }
+    for (int64_t i0 = j->begin; i0 < j->end; i0 += OR_ROW_BLOCK) {
+        int64_t nb = j->end - i0 < OR_ROW_BLOCK ? j->end - i0 : OR_ROW_BLOCK;
+        for (int64_t r = 0; r < nb; ++r) {
+            int64_t t = j->rows ? j->rows[i0 + r] : i0 + r;
+            for (int64_t k = 0; k < d; ++k)
+                hd[r * d + k] = load_elem(j->h, j->dtype, t * j->ldh + k);
+        }
+        /* logits: z[t, v] = sum_k h[t, k] W[v, k] */
+        for (int64_t c = 0; c < v; ++c) {
+            for (int64_t k = 0; k < d; ++k)
+                wd[k] = load_elem(j->w, j->dtype, c * j->ldw + k);
+            for (int64_t r = 0; r < nb; ++r) {
+                const double* hr = hd + r * d;
+                double acc = 0.0;
+                for (int64_t k = 0; k < d; ++k) acc += hr[k] * wd[k];
+                z[r * v + c] = acc;
+            }
+        }
+        /* log-softmax and gather */
+        for (int64_t r = 0; r < nb; ++r) {
+            int64_t t = j->rows ? j->rows[i0 + r] : i0 + r;
+            const double* zr = z + r * v;
+            double m = -INFINITY;
+            for (int64_t c = 0; c < v; ++c)
+                if (zr[c] > m) m = zr[c];
+            double s = 0.0;
+            for (int64_t c = 0; c < v; ++c) s += exp(zr[c] - m);
+            double l = m + log(s);
+            int32_t a = j->ids[t];
+            int ok = a >= 0 && (int64_t)a < v;
+            if (j->lse) j->lse[i0 + r] = l;
+            if (j->zsel) j->zsel[i0 + r] = ok ? zr[a] : NAN;
+            j->logp[i0 + r] = ok ? zr[a] - l : NAN;
+        }
+    }
+    free(hd); free(wd); free(z);
+    return NULL;
+}
+
+/* Number of CPUs this process may run on. */
+int or_available_cpus(void)
+{
+    cpu_set_t set;
+    CPU_ZERO(&set);
+    if (sched_getaffinity(0, sizeof set, &set) == 0) {
+        int c = CPU_COUNT(&set);
+        if (c > 0) return c;
+    }
+    long c = sysconf(_SC_NPROCESSORS_ONLN);
+    return c > 0 ? (int)c : 1;
+}
+
+/*
+ * logp[i], lse[i], zsel[i] for token row t = rows[i] (rows == NULL: t = i),
+ * i in [0, nrows).  h: [*, ldh], W: [v, ldw], ids indexed by t.
+ * An id outside [0, v) gives NaN logp and zsel.  lse/zsel nullable.
+ * nthreads <= 0: all available CPUs.  Returns the thread count used, or -1
+ * on bad arguments.
+ */
+int or_logprob_rows(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                    const int32_t* ids, int dtype, int64_t d, int64_t v,
+                    const int64_t* rows, int64_t nrows,
+                    double* logp, double* lse, double* zsel, int nthreads)
+{
+    if (!h || !w || !ids || !logp || d <= 0 || v <= 0 || nrows < 0 ||
+        ldh < d || ldw < d || (dtype != OR_BF16 && dtype != OR_F32))
+        return -1;
+    if (nthreads <= 0) nthreads = or_available_cpus();
+    if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+    lp_job* jobs = (lp_job*)calloc((size_t)nthreads, sizeof(lp_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -1; }
+    for (int i = 0; i < nthreads; ++i) {
+        lp_job* j = &jobs[i];
+        j->h = h; j->ldh = ldh; j->w = w; j->ldw = ldw; j->ids = ids;
+        j->dtype = dtype; j->d = d; j->v = v; j->rows = rows;
+        j->nrows = nrows; j->logp = logp; j->lse = lse; j->zsel = zsel;
+        j->begin = nrows * i / nthreads;
+        j->end = nrows * (i + 1) / nthreads;
+    }
+    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, lp_worker, &jobs[i]);
+    lp_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(jobs); free(th);
+    return nthreads;
+}
+
+/* ------------------------------------------------------------------ */
+/* Mismatch statistics                                                 */
+/* ------------------------------------------------------------------ */
+
+/* Batch vector layout (same meaning as the library's, restated here). */
+enum {
+    OB_TOK_MEAN_DELTA, OB_TOK_MEAN_K1, OB_TOK_MEAN_K2, OB_TOK_MEAN_K3,
+    OB_SEQ_MEAN_DELTA, OB_SEQ_MEAN_K1, OB_SEQ_MEAN_K2, OB_SEQ_MEAN_K3,
+    OB_TOK_MEAN_TIS_W, OB_CLIP_RATIO, OB_NAN_RATIO, OB_REJECT_FRAC,
+    OB_MEAN_ABS_DELTA, OB_MAX_ABS_DELTA, OB_N_VALID, OB_N_NAN, OB_N_CLIPPED,
+    OB_N_SEQ_NONEMPTY, OB_N_SEQ_REJECTED, OB_NFIELDS
+};
+
+int or_batch_nfields(void) { return OB_NFIELDS; }
+
+static double safe_div(double a, double b) { return b != 0.0 ? a / b : 0.0; }
+
+/*
+ * Token outputs (each [n], nullable), sequence outputs (each [s],
+ * nullable) and batch[OB_NFIELDS] (nullable).  mask nullable = all scored.
+ * cu: [s+1] with 0 = cu[0] <= ... <= cu[s] = n.  Returns 0, or -1 on bad
+ * arguments.
+ */
+int or_mismatch_stats(const float* lt, const float* lr, const uint8_t* mask,
+                      const int32_t* cu, int64_t n, int64_t s,
+                      double clip_c, double seq_lo, double seq_hi,
+                      double* t_delta, double* t_ratio, double* t_k1,
+                      double* t_k2, double* t_k3, double* t_w,
+                      uint8_t* t_clipped,
+                      int32_t* s_n_valid, int32_t* s_n_clipped,
+                      int32_t* s_n_nan, double* s_mean_delta,
+                      double* s_mean_k1, double* s_mean_k2, double* s_mean_k3,
+                      double* s_mean_w, uint8_t* s_reject, double* batch)
+{
+    if (n < 0 || s < 0 || (n > 0 && (!lt || !lr || !cu || s < 1)) ||
+        !(clip_c > 0.0) || !(seq_lo <= seq_hi))
+        return -1;
+    for (int64_t j = 0; j < s; ++j)
+        if (cu[j] > cu[j + 1]) return -1;
+    if (s > 0 && (cu[0] != 0 || cu[s] != n)) return -1;
+
+    const double log_c = log(clip_c);
+
+    /* batch token sums, accumulated over tokens in index order */
+    double b_delta = 0, b_k1 = 0, b_k2 = 0, b_k3 = 0, b_w = 0, b_abs = 0;
+    double b_max = 0;
+    int64_t b_valid = 0, b_nan = 0, b_clip = 0, b_in = 0;
+    /* batch sequence sums, accumulated over sequences in index order */
+    double bs_delta = 0, bs_k1 = 0, bs_k2 = 0, bs_k3 = 0;
+    int64_t bs_nonempty = 0, bs_rejected = 0;
+
+    for (int64_t j = 0; j < s; ++j) {
+        double q_delta = 0, q_k1 = 0, q_k2 = 0, q_k3 = 0, q_w = 0;
+        int64_t q_valid = 0, q_nan = 0, q_clip = 0;
+        for (int64_t t = cu[j]; t < cu[j + 1]; ++t) {
+            int scored = mask ? mask[t] != 0 : 1;
+            double delta = 0, ratio = 1, k1 = 0, k2 = 0, k3 = 0, w = 0;
+            int clipped = 0;
+            if (scored) {
+                b_in++;
+                delta = (double)lt[t] - (double)lr[t];
+                ratio = exp(delta);
+                k1 = -delta;                  /* -log r            */
+                k2 = 0.5 * delta * delta;     /* (log r)^2 / 2     */
+                k3 = expm1(delta) - delta;    /* (r - 1) - log r   */
+                if (!isfinite(delta)) {
+                    q_nan++;
+                    b_nan++;
+                    w = 0;
+                } else {
+                    clipped = delta > log_c;
+                    w = clipped ? clip_c : ratio;
+                    q_valid++; q_delta += delta; q_k1 += k1; q_k2 += k2;
+                    q_k3 += k3; q_w += w; q_clip += clipped;
+                    b_valid++; b_delta += delta; b_k1 += k1; b_k2 += k2;
+                    b_k3 += k3; b_w += w; b_clip += clipped;
+                    b_abs += fabs(delta);
+                    if (fabs(delta) > b_max) b_max = fabs(delta);
+                }
+            }
+            if (t_delta) t_delta[t] = delta;
+            if (t_ratio) t_ratio[t] = ratio;
+            if (t_k1) t_k1[t] = k1;
+            if (t_k2) t_k2[t] = k2;
+            if (t_k3) t_k3[t] = k3;
+            if (t_w) t_w[t] = w;
+            if (t_clipped) t_clipped[t] = (uint8_t)clipped;
+        }
+        double m_delta = safe_div(q_delta, (double)q_valid);
+        double m_k1 = safe_div(q_k1, (double)q_valid);
+        double m_k2 = safe_div(q_k2, (double)q_valid);
+        double m_k3 = safe_div(q_k3, (double)q_valid);
+        double m_w = safe_div(q_w, (double)q_valid);
+        int reject = q_valid > 0 && (m_delta < seq_lo || m_delta > seq_hi);
+        if (q_valid > 0) {
+            bs_nonempty++;
+            bs_rejected += reject;
+            bs_delta += m_delta; bs_k1 += m_k1; bs_k2 += m_k2; bs_k3 += m_k3;
+        }
+        if (s_n_valid) s_n_valid[j] = (int32_t)q_valid;
+        if (s_n_clipped) s_n_clipped[j] = (int32_t)q_clip;
+        if (s_n_nan) s_n_nan[j] = (int32_t)q_nan;
+        if (s_mean_delta) s_mean_delta[j] = m_delta;
+        if (s_mean_k1) s_mean_k1[j] = m_k1;
+        if (s_mean_k2) s_mean_k2[j] = m_k2;
+        if (s_mean_k3) s_mean_k3[j] = m_k3;
+        if (s_mean_w) s_mean_w[j] = m_w;
+        if (s_reject) s_reject[j] = (uint8_t)reject;
+    }
+    if (batch) {
+        double nv = (double)b_valid, ns = (double)bs_nonempty;
+        batch[OB_TOK_MEAN_DELTA] = safe_div(b_delta, nv);
+        batch[OB_TOK_MEAN_K1] = safe_div(b_k1, nv);
+        batch[OB_TOK_MEAN_K2] = safe_div(b_k2, nv);
+        batch[OB_TOK_MEAN_K3] = safe_div(b_k3, nv);
+        batch[OB_SEQ_MEAN_DELTA] = safe_div(bs_delta, ns);
+        batch[OB_SEQ_MEAN_K1] = safe_div(bs_k1, ns);
+        batch[OB_SEQ_MEAN_K2] = safe_div(bs_k2, ns);
+        batch[OB_SEQ_MEAN_K3] = safe_div(bs_k3, ns);
+        batch[OB_TOK_MEAN_TIS_W] = safe_div(b_w, nv);
+        batch[OB_CLIP_RATIO] = safe_div((double)b_clip, nv);
+        batch[OB_NAN_RATIO] = safe_div((double)b_nan, (double)b_in);
+        batch[OB_REJECT_FRAC] = safe_div((double)bs_rejected, ns);
+        batch[OB_MEAN_ABS_DELTA] = safe_div(b_abs, nv);
+        batch[OB_MAX_ABS_DELTA] = b_max;
+        batch[OB_N_VALID] = nv;
+        batch[OB_N_NAN] = (double)b_nan;
+        batch[OB_N_CLIPPED] = (double)b_clip;
+        batch[OB_N_SEQ_NONEMPTY] = ns;
+        batch[OB_N_SEQ_REJECTED] = (double)bs_rejected;
+    }
+    return 0;
+}

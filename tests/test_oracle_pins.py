@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these checks re-types the oracle's formula: each expected value comes
+from a value the pages print (``tests/golden``), a closed form, an invariant,
+exact rational arithmetic, or a brute-force evaluation by a different route
+(normalised probabilities in 50-digit decimal arithmetic).  The last test
+plants mistakes in a copy of the oracle and checks that these pins catch them.
+"""
+import json
+import math
+import os
+import re
+import subprocess
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+getcontext().prec = 50
+
+
+def _dec(fr: Fraction) -> Decimal:
+    return Decimal(fr.numerator) / Decimal(fr.denominator)
+
+
+def _exact_logits(h, w):
+    """z[t, v] as exact rationals from float inputs."""
+    hf = [[Fraction(float(x)) for x in row] for row in h]
+    wf = [[Fraction(float(x)) for x in row] for row in w]
+    return [[sum(a * b for a, b in zip(hr, wr)) for wr in wf] for hr in hf]
+
+
+def _brute_logp(z_row, a):
+    """log of the normalised probability p_a = e^{z_a} / sum_v e^{z_v}."""
+    ez = [_dec(z).exp() for z in z_row]
+    p = ez[a] / sum(ez)
+    return float(p.ln())
+
+
+# ---------------------------------------------------------------------------
+# bf16 (the pages' rounding example)
+# ---------------------------------------------------------------------------
+
+def test_bf16_order_of_addition_example():
+    g = json.load(open(os.path.join(GOLDEN, "bf16_rounding_order.json")))
+    a, b, c = g["a"], g["b"], g["c"]
+
+    def rnd(x):
+        return float(oracle.bf16_decode(oracle.bf16_round_rne([x]))[0])
+
+    assert rnd(1.0 + 2.0 ** -7) == g["next_above_one"]
+    assert rnd(a + b) == 1.0                      # exact tie -> even -> 1
+    left = rnd(rnd(a + b) + c)
+    right = rnd(a + rnd(b + c))
+    assert left == g["left_assoc_result"]
+    assert right == g["right_assoc_result"]
+    assert int(oracle.bf16_round_rne([left])[0]) == int(g["left_assoc_bits"], 16)
+    assert int(oracle.bf16_round_rne([right])[0]) == int(g["right_assoc_bits"], 16)
+    # torch's float32 -> bfloat16 conversion (used to make bf16 inputs) agrees
+    t = lambda x: torch.tensor([x], dtype=torch.float32).to(torch.bfloat16).float().item()
+    assert t(t(a + b) + c) == left and t(a + t(b + c)) == right
+
+
+def test_bf16_decode_known_patterns():
+    pats = {0x3F80: 1.0, 0x3F81: 1.0 + 2 ** -7, 0xC000: -2.0, 0x0001: 2.0 ** -133,
+            0x0080: 2.0 ** -126, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127, 0x0000: 0.0}
+    got = oracle.bf16_decode(list(pats))
+    assert list(got) == list(pats.values())
+    inf = oracle.bf16_decode([0x7F80, 0xFF80, 0x7FC0])
+    assert inf[0] == math.inf and inf[1] == -math.inf and math.isnan(inf[2])
+
+
+def test_bf16_rne_matches_torch_conversion():
+    """Round-to-nearest-even is also what torch implements for fp32 -> bf16;
+    compare on random values, exact ties and subnormals."""
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * np.float32(3.0),
+        # exact ties: bf16 value + half an ulp (low 16 bits = 0x8000)
+        (rng.integers(0x3000, 0x4F00, 500, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+        np.array([2.0 ** -130, 3 * 2.0 ** -134, -2.0 ** -127], np.float32),
+    ])
+    ours = oracle.bf16_round_rne(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# selected-token log-probability
+# ---------------------------------------------------------------------------
+
+def _lp(h, w, ids, dtype=oracle.F32, rows=None):
+    logp, lse, zsel, _ = oracle.logprob(h, w, ids, dtype=dtype, rows=rows, nthreads=2)
+    return logp, lse, zsel
+
+
+def test_equal_logits_give_minus_log_v():
+    rng = np.random.default_rng(1)
+    v, d = 1024, 256
+    h = rng.standard_normal((8, d)).astype(np.float32)
+    ids = rng.integers(0, v, 8).astype(np.int32)
+    logp, lse, _ = _lp(h, np.zeros((v, d), np.float32), ids)
+    np.testing.assert_allclose(logp, -math.log(v), rtol=0, atol=1e-13)
+    assert abs(-math.log(1024) - (-6.931471805599453)) < 1e-15
+    w = rng.standard_normal((v, d)).astype(np.float32)
+    logp, _, _ = _lp(np.zeros((8, d), np.float32), w, ids)
+    np.testing.assert_allclose(logp, -math.log(v), rtol=0, atol=1e-13)
+    # the Qwen3-8B vocabulary: -log 151936
+    assert abs(-math.log(151936) - (-11.931215)) < 1e-6
+
+
+def test_single_entry_vocabulary_is_certain():
+    h = np.array([[0.5, -1.25]], np.float32)
+    logp, lse, zsel = _lp(h, np.array([[2.0, 3.0]], np.float32), np.array([0], np.int32))
+    assert logp[0] == 0.0 and lse[0] == zsel[0] == 0.5 * 2.0 - 1.25 * 3.0
+
+
+def test_two_entry_vocabulary_closed_form_including_large_logits():
+    # z_0 = 3 h, z_1 = -2 h: logp_0 = -log1p(exp(z_1 - z_0))
+    for hv in (0.25, -1.5, 300.0, -400.0):
+        h = np.array([[hv]] * 2, np.float32)
+        w = np.array([[3.0], [-2.0]], np.float32)
+        logp, lse, _ = _lp(np.repeat(h, 64, 1), np.repeat(w, 64, 1) / 64, np.array([0, 1], np.int32))
+        z0, z1 = 3.0 * hv, -2.0 * hv
+        np.testing.assert_allclose(logp[0], -math.log1p(math.exp(z1 - z0)) if z1 < z0
+                                   else (z0 - z1) - math.log1p(math.exp(z0 - z1)), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(logp[1], -math.log1p(math.exp(z0 - z1)) if z0 < z1
+                                   else (z1 - z0) - math.log1p(math.exp(z1 - z0)), rtol=1e-14, atol=1e-15)
+        assert np.all(np.isfinite(lse))
+
+
+def test_brute_force_against_exact_logits_and_decimal_softmax():
+    rng = np.random.default_rng(2)
+    n, d, v = 5, 3, 7                      # non-square: a transposed W fails
+    h = rng.standard_normal((n, d)).astype(np.float32)
+    w = (rng.standard_normal((v, d)) * 2).astype(np.float32)
+    ids = rng.integers(0, v, n).astype(np.int32)
+    logp, lse, zsel = _lp(h, w, ids)
+    z = _exact_logits(h, w)
+    for t in range(n):
+        assert abs(zsel[t] - float(z[t][ids[t]])) <= 1e-15 * max(1.0, abs(float(z[t][ids[t]])))
+        assert abs(logp[t] - _brute_logp(z[t], int(ids[t]))) < 1e-13
+    # every id of one row: the probabilities sum to one
+    ids_all = np.arange(v, dtype=np.int32)
+    logp_all, lse_all, _ = _lp(np.repeat(h[:1], v, 0), w, ids_all)
+    assert abs(np.exp(logp_all).sum() - 1.0) < 1e-14
+    assert np.all(lse_all == lse_all[0])
+
+
+def test_integer_exact_logits_bf16():
+    """Inputs are small multiples of 2^-3 (exact in bf16): every logit is an
+    exact rational, so zsel must equal the integer-arithmetic value."""
+    rng = np.random.default_rng(3)
+    n, d, v = 6, 128, 50
+    hq = rng.integers(-16, 17, (n, d))
+    wq = rng.integers(-16, 17, (v, d))
+    h_bits = torch.from_numpy((hq / 8.0).astype(np.float32)).to(torch.bfloat16)
+    w_bits = torch.from_numpy((wq / 8.0).astype(np.float32)).to(torch.bfloat16)
+    ids = rng.integers(0, v, n).astype(np.int32)
+    _, _, zsel = _lp(h_bits, w_bits, ids, dtype=oracle.BF16)
+    exact = (hq * wq[ids]).sum(1) / 64.0
+    np.testing.assert_array_equal(zsel, exact)
+    # same values through the fp32 path give identical results
+    a = _lp(h_bits.float().numpy(), w_bits.float().numpy(), ids, dtype=oracle.F32)
+    b = _lp(h_bits, w_bits, ids, dtype=oracle.BF16)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_one_hot_rows_select_weight_entries():
+    rng = np.random.default_rng(4)
+    d, v = 64, 40
+    w = rng.standard_normal((v, d)).astype(np.float32)
+    ks = [0, 17, 63]
+    h = np.zeros((3, d), np.float32)
+    for r, k in enumerate(ks):
+        h[r, k] = 1.0
+    ids = np.array([5, 0, 39], np.int32)
+    logp, lse, zsel = _lp(h, w, ids)
+    for r, k in enumerate(ks):
+        assert zsel[r] == float(w[ids[r], k])
+        col = [Fraction(float(x)) for x in w[:, k]]
+        ref = float((sum(_dec(c).exp() for c in col)).ln())
+        assert abs(lse[r] - ref) < 1e-13
+
+
+def test_out_of_range_ids_are_nan_and_rows_subset_matches():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((10, 64)).astype(np.float32)
+    w = rng.standard_normal((33, 64)).astype(np.float32)
+    ids = rng.integers(0, 33, 10).astype(np.int32)
+    ids[2], ids[7] = -100, 33               # ignore-index style and one past the end
+    logp, lse, _ = _lp(h, w, ids)
+    assert np.isnan(logp[2]) and np.isnan(logp[7]) and np.all(np.isfinite(lse))
+    rows = np.array([9, 0, 4], np.int64)
+    sub = _lp(h, w, ids, rows=rows)
+    np.testing.assert_array_equal(sub[0], logp[rows])
+
+
+# ---------------------------------------------------------------------------
+# mismatch statistics
+# ---------------------------------------------------------------------------
+
+def _stats(lt, lr, cu, mask=None, c=2.0, lo=-0.01, hi=0.01):
+    return oracle.mismatch_stats(np.asarray(lt, np.float32), np.asarray(lr, np.float32),
+                                 mask, np.asarray(cu, np.int32), clip_c=c, seq_lo=lo, seq_hi=hi)
+
+
+def test_vexact_table1_sign_and_derived_estimators():
+    g = json.load(open(os.path.join(GOLDEN, "vexact_table1.json")))
+    r = _stats(g["logp_train"], g["logp_rollout"], [0, 8])
+    tol = 1.5 * 10.0 ** -g["printed_decimals"]    # three roundings of 5e-4
+    np.testing.assert_allclose(r["token"]["delta"], g["delta"], rtol=0, atol=tol)
+    # sign: the flipped token has delta = train - rollout < 0
+    i = g["argmax_flip_index"]
+    assert r["token"]["delta"][i] < -0.1
+    d = Decimal(repr(float(np.float32(g["logp_train"][i])))) - \
+        Decimal(repr(float(np.float32(g["logp_rollout"][i]))))
+    assert abs(r["token"]["k1"][i] - float(-d)) < 1e-15
+    assert abs(r["token"]["k2"][i] - float(d * d / 2)) < 1e-16
+    assert abs(r["token"]["k3"][i] - float(d.exp() - 1 - d)) < 1e-16
+    assert abs(r["token"]["k1"][i] - 0.133) < 1e-7
+    assert abs(r["token"]["k2"][i] - 0.0088445) < 1e-7
+    assert abs(r["token"]["k3"][i] - 0.0084651) < 1e-7
+    # mean delta = -0.0175 -> geometric mean ratio 0.983 < 0.99 -> rejected
+    assert r["seq"]["reject"][0] == 1
+    r2 = _stats(g["logp_train"], g["logp_rollout"], [0, 8], lo=math.log(0.99), hi=math.log(1.01))
+    assert r2["seq"]["reject"][0] == 1
+
+
+def test_zero_mismatch_gives_zero_estimators():
+    rng = np.random.default_rng(6)
+    lt = -np.abs(rng.standard_normal(100)).astype(np.float32)
+    r = _stats(lt, lt, [0, 30, 30, 100])
+    t = r["token"]
+    assert np.all(t["delta"] == 0) and np.all(t["k1"] == 0) and np.all(t["k2"] == 0)
+    assert np.all(t["k3"] == 0) and np.all(t["ratio"] == 1) and np.all(t["tis_w"] == 1)
+    assert not t["clipped"].any() and not r["seq"]["reject"].any()
+    b = r["batch"]
+    assert b["tok_mean_k3"] == 0 and b["clip_ratio"] == 0 and b["n_valid"] == 100
+    assert b["n_seq_nonempty"] == 2 and b["tok_mean_tis_w"] == 1.0
+
+
+def test_k3_nonnegative_and_matches_closed_form():
+    deltas = np.concatenate([np.geomspace(1e-12, 20, 200), -np.geomspace(1e-12, 20, 200)])
+    lr = np.full(deltas.size, -30.0, np.float32)
+    lt = (lr.astype(np.float64) + deltas).astype(np.float32)
+    r = _stats(lt, lr, [0, deltas.size])
+    t = r["token"]
+    assert np.all(t["k3"] >= 0)
+    for i in range(0, deltas.size, 7):
+        d = Decimal(float(t["delta"][i]))
+        ref = d.exp() - 1 - d
+        # (r - 1) - log r evaluated in fp64: each operand of the final
+        # subtraction is within an ulp, so the error is bounded by a few ulps
+        # of |delta| + |k3| (the cancellation of the definition itself)
+        bound = Decimal(2) ** -51 * (abs(d) + abs(ref))
+        assert abs(Decimal(float(t["k3"][i])) - ref) <= bound
+        assert t["k2"][i] == float(t["delta"][i]) ** 2 / 2
+        assert t["ratio"][i] == pytest.approx(float(d.exp()), rel=1e-15)
+
+
+def test_constant_delta_means_are_exact():
+    c = 2.0 ** -6
+    lr = np.full(48, -1.0, np.float32)
+    lt = lr + np.float32(c)
+    r = _stats(lt, lr, [0, 16, 48])
+    assert np.all(r["seq"]["mean_delta"] == c) and np.all(r["seq"]["mean_k1"] == -c)
+    assert np.all(r["seq"]["mean_k2"] == c * c / 2)
+    assert r["batch"]["tok_mean_delta"] == c and r["batch"]["seq_mean_delta"] == c
+    assert r["seq"]["reject"].all()          # 2^-6 = 0.015625 > 0.01
+
+
+def test_truncated_is_clips_above_log_c():
+    lr = np.full(10, -2.0, np.float32)
+    r = _stats(lr + np.float32(1.0), lr, [0, 10])          # delta 1 > log 2
+    assert r["token"]["clipped"].all() and np.all(r["token"]["tis_w"] == 2.0)
+    assert r["batch"]["clip_ratio"] == 1.0 and r["batch"]["tok_mean_tis_w"] == 2.0
+    r = _stats(lr + np.float32(0.5), lr, [0, 10])          # delta 0.5 < log 2
+    assert not r["token"]["clipped"].any()
+    np.testing.assert_allclose(r["token"]["tis_w"], math.exp(0.5), rtol=1e-15)
+
+
+def test_sequence_mean_then_batch_mean_differs_from_token_mean():
+    # sequence A: two tokens with delta 1; sequence B: three tokens with delta 0
+    lr = np.zeros(5, np.float32) - 1.0
+    lt = lr.copy()
+    lt[:2] = 0.0
+    r = _stats(lt, lr, [0, 2, 5])
+    assert r["batch"]["tok_mean_delta"] == 0.4
+    assert r["batch"]["seq_mean_delta"] == 0.5
+    assert r["batch"]["seq_mean_k2"] == 0.25 and r["batch"]["tok_mean_k2"] == 0.2
+    assert list(r["seq"]["mean_delta"]) == [1.0, 0.0]
+    assert list(r["seq"]["reject"]) == [1, 0]
+    assert r["batch"]["reject_frac"] == 0.5
+
+
+def test_mask_nan_and_empty_sequences():
+    lt = np.array([-1, -1, -1, -1, -1, -1, -1], np.float32)
+    lr = np.array([-1.5, np.nan, -1, -1, -1, -1, np.inf], np.float32)
+    mask = np.array([1, 1, 0, 0, 1, 0, 1], np.uint8)
+    cu = [0, 2, 2, 4, 7]                    # sequence 1 empty, sequence 2 all masked
+    r = _stats(lt, lr, cu, mask=mask)
+    s = r["seq"]
+    assert list(s["n_valid"]) == [1, 0, 0, 1]
+    assert list(s["n_nan"]) == [1, 0, 0, 1]
+    assert list(s["reject"]) == [1, 0, 0, 0]
+    assert s["mean_delta"][0] == 0.5 and s["mean_delta"][1] == 0 and s["mean_delta"][2] == 0
+    b = r["batch"]
+    assert b["n_valid"] == 2 and b["n_nan"] == 2 and b["nan_ratio"] == 2 / 4
+    assert b["n_seq_nonempty"] == 2 and b["seq_mean_delta"] == 0.25
+    t = r["token"]
+    assert t["tis_w"][1] == 0 and t["ratio"][2] == 1 and t["tis_w"][2] == 0
+    assert b["max_abs_delta"] == 0.5
+
+
+def test_rejection_window_in_log_domain():
+    lo, hi = math.log(0.99), math.log(1.01)
+    base = np.full(4, -3.0, np.float32)
+    cases = {lo - 1e-4: 1, lo + 1e-4: 0, 0.0: 0, hi - 1e-4: 0, hi + 1e-4: 1}
+    for mean, want in cases.items():
+        lt = (base.astype(np.float64) + mean).astype(np.float32)
+        r = _stats(lt, base, [0, 4], lo=lo, hi=hi)
+        m = r["seq"]["mean_delta"][0]
+        gm = Decimal(float(m)).exp()            # geometric mean of the ratios
+        assert (gm < Decimal("0.99") or gm > Decimal("1.01")) == bool(want)
+        assert r["seq"]["reject"][0] == want
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by one of the pins above
+# ---------------------------------------------------------------------------
+
+MUTATIONS = [
+    ("no max subtraction", "s += exp(zr[c] - m);", "s += exp(zr[c]);",
+     "test_two_entry_vocabulary_closed_form_including_large_logits"),
+    ("gather off by one", "ok ? zr[a] - l : NAN", "ok ? zr[(a + 1) % v] - l : NAN",
+     "test_brute_force_against_exact_logits_and_decimal_softmax"),
+    ("transposed W", "c * j->ldw + k", "k * j->ldw + c",
+     "test_brute_force_against_exact_logits_and_decimal_softmax"),
+    ("delta sign", "delta = (double)lt[t] - (double)lr[t];",
+     "delta = (double)lr[t] - (double)lt[t];", "test_vexact_table1_sign_and_derived_estimators"),
+    ("k3 without -delta", "k3 = expm1(delta) - delta;", "k3 = expm1(delta);",
+     "test_k3_nonnegative_and_matches_closed_form"),
+    ("k3 without -1", "k3 = expm1(delta) - delta;", "k3 = exp(delta) - delta;",
+     "test_zero_mismatch_gives_zero_estimators"),
+    ("token mean for sequence mean", "bs_delta += m_delta;", "bs_delta += q_delta;",
+     "test_sequence_mean_then_batch_mean_differs_from_token_mean"),
+    ("clip at C instead of log C", "clipped = delta > log_c;", "clipped = delta > clip_c;",
+     "test_truncated_is_clips_above_log_c"),
+]
+
+
+@pytest.mark.parametrize("label,old,new,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, monkeypatch, label, old, new, pin):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, label
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-pthread", "-o", str(so), str(mutated), "-lm"], check=True)
+    good = oracle._load()
+    monkeypatch.setattr(oracle, "_lib", None)
+    monkeypatch.setattr(oracle, "_LIB_PATH", str(so))
+    monkeypatch.setattr(oracle, "build", lambda force=True: str(so))
+    # the transposed-W mutant reads W[k, c]; keep its reads in bounds
+    fn = globals()[pin]
+    with pytest.raises(AssertionError):
+        fn()
+    monkeypatch.setattr(oracle, "_lib", good)
