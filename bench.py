@@ -1,0 +1,249 @@
+"""Benchmark: batch-invariant selected-token log-probabilities + mismatch stats.
+
+One *step* is the whole hot path over one batch already resident in HBM:
+``tim_logprob_forward`` (fused bf16 LM-head contraction, online log-sum-exp,
+gather, chunk merge) followed by ``tim_mismatch_stats`` (delta, ratio,
+k1/k2/k3, truncated IS, per-sequence rejection, batch aggregates) on the
+Qwen3-8B-shaped workload: N=8192 tokens in 16 sequences of 512, D=4096,
+V=151936, bf16 inputs, fp32 accumulation.
+
+Prints ONE JSON line on stdout.  Diagnostics go to stderr.  Also reported:
+the stats pass on 2^28 tokens (HBM bandwidth), the price of batch invariance
+against the free schedule, and the fp64 oracle timed on a bounded sample on
+the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "selected-token logprobs/s at D=4096,V=151936 (bf16) + MFMA util; batch-invariant"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_bf16_qwen3_8b_counters.json")
+LMHEAD_SRC = os.path.join(ROOT, "invariant_logprobs_amd", "csrc", "lmhead.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_unit):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on a different kernel source."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256_16") != source_digest(LMHEAD_SRC):
+        return None
+    if s.get("launch_unit") != launch_unit:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle rows for the CPU baseline (0: ~15 s of work)")
+    ap.add_argument("--stats-log2", type=int, default=28)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the stats-scale and invariance-cost measurements")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the hot path shards by rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import invariant_logprobs_amd as tim
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    name = "qwen3_8b"
+    log(f"generating workload {name}")
+    wl = workloads.make(name, device=dev)
+    sp = wl.spec
+    n, d, v = sp.n, sp.d, sp.v
+    torch.cuda.synchronize()
+
+    # preallocated outputs and workspaces: the timed region only launches
+    lt = torch.empty(n, dtype=torch.float32, device=dev)
+    ws_lp = torch.empty(tim.logprob_workspace_bytes(n, d, v, tim.TIM_BF16), dtype=torch.uint8,
+                        device=dev)
+    ws_st = torch.empty(max(1, tim.stats_workspace_bytes(n, sp.n_seqs)), dtype=torch.uint8,
+                        device=dev)
+
+    def step():
+        tim.tim_logprob_forward(wl.h, wl.w, wl.ids, out=lt, workspace=ws_lp)
+        return tim.tim_mismatch_stats(lt, wl.logp_rollout, wl.mask, wl.cu_seqlens,
+                                      tis_clip=sp.clip_c, seq_bounds=(sp.seq_lo, sp.seq_hi),
+                                      workspace=ws_st)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        tim.tim_logprob_forward(wl.h, wl.w, wl.ids, out=lt, workspace=ws_lp)
+        ev[i][1].record(stream)
+        res = tim.tim_mismatch_stats(lt, wl.logp_rollout, wl.mask, wl.cu_seqlens,
+                                     tis_clip=sp.clip_c, seq_bounds=(sp.seq_lo, sp.seq_hi),
+                                     workspace=ws_st)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_lp = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]     # ms
+    t_st = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_step = wall * 1e3 / K
+    value = n / (ms_step / 1e3)
+    lp_avg = float(np.mean(t_lp))
+    flops = 2.0 * n * d * v
+    achieved = flops / (lp_avg / 1e3) / 1e12
+    log(f"step {ms_step:.3f} ms (wall), forward avg {lp_avg:.3f} ms "
+        f"(p10 {np.percentile(t_lp, 10):.3f}, p90 {np.percentile(t_lp, 90):.3f}), "
+        f"stats avg {np.mean(t_st) * 1e3:.1f} us, {achieved:.1f} TFLOP/s")
+    bsum = tim.batch_dict(res["batch"])
+    log(f"is_approx_k3_kl {bsum['is_approx_k3_kl']:.3e}, reject_frac {bsum['reject_frac']}")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sp.desc, "n_tokens": n, "hidden": d, "vocab": v,
+                   "sequences": sp.n_seqs, "schedule": "invariant",
+                   "accumulation": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(f"{name}:N={n}"),
+                     "kernel": "lmhead_partials_kernel<bf16> + lse_merge (one forward call)",
+                     "flops_per_launch": flops, "avg_launch_ms": lp_avg},
+        "stats_step_us": float(np.mean(t_st)) * 1e3,
+    }
+
+    if not args.no_extras:
+        out["stats_scale"] = stats_scale(tim, workloads, torch, np, args.stats_log2)
+        out["invariance_cost"] = invariance_cost(tim, wl, torch, np)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, np, args.cpu_rows)
+
+    print(json.dumps(out), flush=True)
+
+
+def time_calls(fn, torch, np, reps=10, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def stats_scale(tim, workloads, torch, np, log2n):
+    n = 1 << log2n
+    log(f"stats at 2^{log2n} tokens")
+    lt, lr, mask, cu = workloads.stats_scale(n, seed=7, device="cuda")
+    s = cu.numel() - 1
+    ws = torch.empty(tim.stats_workspace_bytes(n, s), dtype=torch.uint8, device="cuda")
+    fn = lambda: tim.tim_mismatch_stats(lt, lr, mask, cu, seq_bounds=(math.log(0.99),
+                                        math.log(1.01)), workspace=ws)
+    ms = time_calls(fn, torch, np)
+    # algorithmic bytes: lt, lr (4 B) + mask (1 B) per token, cu_seqlens,
+    # per-sequence outputs (3 int32, 5 fp64, 1 u8), the batch vector
+    algo = 9 * n + 4 * (s + 1) + s * (12 + 40 + 1) + 8 * len(tim.BATCH_FIELDS)
+    gbs = algo / (ms / 1e3) / 1e9
+    log(f"stats 2^{log2n}: {ms:.3f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    del lt, lr, mask, cu, ws
+    torch.cuda.empty_cache()
+    return {"tokens": n, "sequences": s, "ms": ms, "algorithmic_bytes": algo,
+            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
+            "tokens_per_s": n / (ms / 1e3)}
+
+
+def invariance_cost(tim, wl, torch, np):
+    """t(invariant) / t(free) - 1 for the forward at several batch sizes."""
+    res = {}
+    for b in (1, 7, 64, 1000, 8192):
+        h, ids = wl.h[:b], wl.ids[:b]
+        ti = time_calls(lambda: tim.tim_logprob_forward(h, wl.w, ids), torch, np, reps=5)
+        tf = time_calls(lambda: tim.tim_logprob_forward(h, wl.w, ids, schedule="free"),
+                        torch, np, reps=5)
+        res[str(b)] = {"invariant_ms": ti, "free_ms": tf, "cost": ti / tf - 1.0}
+        log(f"invariance cost b={b}: {ti:.3f} ms vs {tf:.3f} ms ({ti / tf - 1:+.1%})")
+    return res
+
+
+def cpu_baseline(wl, np, rows):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    h = wl.h.cpu()
+    w = wl.w.cpu()
+    ids = wl.ids.cpu()
+    threads = min(oracle.available_cpus(), oracle.MAX_THREADS)
+    if rows <= 0:
+        # calibrate: one row per thread, then size to ~15 s
+        t = time.perf_counter()
+        oracle.logprob(h, w, ids, dtype=oracle.BF16, rows=np.arange(threads), nthreads=threads)
+        per_round = time.perf_counter() - t
+        rows = max(threads, int(15.0 / max(per_round, 1e-3)) * threads)
+        rows = min(rows, wl.spec.n)
+    sample = np.linspace(0, wl.spec.n - 1, rows).astype(np.int64)
+    log(f"cpu baseline: oracle on {rows} rows with {threads} threads")
+    t = time.perf_counter()
+    _, _, _, used = oracle.logprob(h, w, ids, dtype=oracle.BF16, rows=sample, nthreads=threads)
+    t_lp = time.perf_counter() - t
+    lt = wl.logp_sampler.cpu()
+    lr = wl.logp_rollout.cpu()
+    cu = wl.cu_seqlens.cpu()
+    t = time.perf_counter()
+    oracle.mismatch_stats(lt, lr, None, cu, clip_c=wl.spec.clip_c, seq_lo=wl.spec.seq_lo,
+                          seq_hi=wl.spec.seq_hi)
+    t_st = time.perf_counter() - t
+    per_token = t_lp / rows + t_st / wl.spec.n
+    log(f"cpu baseline: {rows / t_lp:.2f} rows/s logprob, stats {t_st * 1e3:.1f} ms")
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{rows} of {wl.spec.n} rows of the workload (fp64 logprob, evenly "
+                      f"spaced) + stats over all {wl.spec.n} tokens; full-N time extrapolated "
+                      f"from the sample", "logprob_rows_per_s": rows / t_lp,
+            "stats_ms_full_n": t_st * 1e3}
+
+
+if __name__ == "__main__":
+    main()

@@ -131,7 +131,8 @@ size_t tim_logprob_workspace_bytes(int64_t n, int64_t d, int64_t v,
  *  lse        [n] fp32 out, nullable: log sum_v exp z[t,v].
  *  n_bad_ids  [1] int32 out, nullable: number of ids outside [0, v).
  *  workspace  device scratch of at least tim_logprob_workspace_bytes(...)
- *             bytes, 256-byte aligned (else TIM_EWORKSPACE / TIM_EINVAL).
+ *             bytes (null or smaller: TIM_EWORKSPACE), 256-byte aligned
+ *             (else TIM_EUNSUPPORTED).
  *  stream     hipStream_t to enqueue on (NULL = null stream).
  *
  * Arithmetic: products of bf16 (or fp32) inputs accumulate in fp32 in a
@@ -242,7 +243,12 @@ size_t tim_stats_workspace_bytes(int64_t n, int64_t s);
  *  p             (host) clip constant and rejection window.
  *  tok, seq      (host structs) nullable; their members are nullable.
  *  batch         [TIM_B_NFIELDS] fp64 out, nullable.
- *  workspace     >= tim_stats_workspace_bytes(n, s) bytes, 256-byte aligned.
+ *  workspace     >= tim_stats_workspace_bytes(n, s) bytes (else
+ *                TIM_EWORKSPACE), 256-byte aligned (else TIM_EUNSUPPORTED).
+ *  Errors: TIM_EINVAL for n < 0, s < 0, n > 0 with s == 0, null p, C not a
+ *  finite positive number, seq_lo > seq_hi or a NaN bound, null lt/lr when
+ *  n > 0, null cu_seqlens; TIM_EUNSUPPORTED for n or s beyond int32.
+ *  n == 0 and s == 0 returns TIM_OK without a launch.
  *
  * delta is computed in fp64 from the fp32 inputs, so both signs and the
  * clip decision are exact; exp/expm1 are evaluated in fp64.

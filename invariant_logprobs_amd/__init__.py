@@ -1,0 +1,264 @@
+"""Batch-invariant selected-token log-probabilities and train/rollout mismatch
+statistics on AMD Instinct MI355X (gfx950).
+
+This module is the thin Python binding of ``libtim.so`` (C ABI in
+``include/tim.h``).  It only marshals arguments: tensors must already live in
+GPU memory, torch supplies the allocation of outputs and workspace and the
+current HIP stream, and every step of the computation runs in the library's
+HIP kernels.  There is no CPU path: if the library is not built, or a tensor
+is not on the GPU, a call raises.
+
+Entry points (same names as the C ABI):
+
+* :func:`tim_logprob_forward` -- ``logp[t] = log softmax(h[t] W^T)[ids[t]]``
+  ("RL: Training Inference Mismatch", section "log p").
+* :func:`tim_mismatch_stats` -- delta, ratio, k1/k2/k3, truncated IS weight,
+  per-sequence means and geometric-mean-ratio rejection, batch aggregates
+  ("Diagnosing Training Inference Mismatch ... (VeXact)", eq. (1) and its
+  compensation table; "Train-Inference Consistency", sections 4-5).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH
+
+TIM_OK, TIM_EINVAL, TIM_EUNSUPPORTED, TIM_EWORKSPACE, TIM_EHIP = range(5)
+TIM_BF16, TIM_F32 = 0, 1
+TIM_SCHED_INVARIANT, TIM_SCHED_FREE = 0, 1
+
+# Names of the batch aggregate vector, in TIM_B_* index order.  The
+# is_approx_k3_kl / is_clip_ratio / is_nan_ratio names are the monitoring
+# metrics of "Train-Inference Consistency", section 5.
+BATCH_FIELDS = (
+    "tok_mean_delta", "tok_mean_k1", "tok_mean_k2", "is_approx_k3_kl",
+    "seq_mean_delta", "seq_mean_k1", "seq_mean_k2", "seq_mean_k3",
+    "tok_mean_tis_w", "is_clip_ratio", "is_nan_ratio", "reject_frac",
+    "mean_abs_delta", "max_abs_delta", "n_valid", "n_nan", "n_clipped",
+    "n_seq_nonempty", "n_seq_rejected",
+)
+
+# Exported symbols of libtim.so (checked against include/tim.h by the tests).
+EXPORTS = ("tim_abi_version", "tim_status_string", "tim_logprob_workspace_bytes",
+           "tim_logprob_forward", "tim_stats_workspace_bytes", "tim_mismatch_stats")
+
+
+class TimError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class _StatsParams(ctypes.Structure):
+    _fields_ = [("tis_clip_c", ctypes.c_double), ("seq_lo", ctypes.c_double),
+                ("seq_hi", ctypes.c_double)]
+
+
+class _TokenOut(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("delta", "ratio", "k1", "k2", "k3", "tis_w", "clipped")]
+
+
+class _SeqOut(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("n_valid", "n_clipped", "n_nan", "mean_delta", "mean_k1", "mean_k2",
+                 "mean_k3", "mean_tis_w", "reject")]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libtim.so (built by ``invariant_logprobs_amd.build``); raise if absent."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m invariant_logprobs_amd.build` "
+                               "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        lib.tim_abi_version.restype = ctypes.c_int
+        lib.tim_status_string.restype = ctypes.c_char_p
+        lib.tim_status_string.argtypes = [ctypes.c_int]
+        lib.tim_logprob_workspace_bytes.restype = sz
+        lib.tim_logprob_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_uint]
+        lib.tim_logprob_forward.restype = ctypes.c_int
+        lib.tim_logprob_forward.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, ctypes.c_int,
+                                            ctypes.c_uint, vp, vp, vp, vp, sz, vp]
+        lib.tim_stats_workspace_bytes.restype = sz
+        lib.tim_stats_workspace_bytes.argtypes = [i64, i64]
+        lib.tim_mismatch_stats.restype = ctypes.c_int
+        lib.tim_mismatch_stats.argtypes = [vp, vp, vp, vp, i64, i64,
+                                           ctypes.POINTER(_StatsParams),
+                                           ctypes.POINTER(_TokenOut), ctypes.POINTER(_SeqOut),
+                                           vp, vp, sz, vp]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tim_status_string(int(status)).decode()
+
+
+def _dptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _require_gpu(name: str, t: torch.Tensor):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a torch tensor in GPU memory")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+_DTYPES = {torch.bfloat16: TIM_BF16, torch.float32: TIM_F32}
+
+
+def logprob_workspace_bytes(n: int, d: int, v: int, dtype: int, schedule: str = "invariant") -> int:
+    flags = TIM_SCHED_FREE if schedule == "free" else TIM_SCHED_INVARIANT
+    return int(load_library().tim_logprob_workspace_bytes(n, d, v, dtype, flags))
+
+
+def stats_workspace_bytes(n: int, s: int) -> int:
+    return int(load_library().tim_stats_workspace_bytes(n, s))
+
+
+def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
+                        schedule: str = "invariant", return_lse: bool = False,
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Selected-token log-probabilities ``logp[t] = log softmax(h[t] W^T)[ids[t]]``.
+
+    ``h``: [N, D] and ``w``: [V, D], both bf16 or both fp32, rows contiguous
+    (a leading dimension larger than D is allowed via a strided 2-D view).
+    ``ids``: [N] int32.  Returns ``logp`` (fp32 [N]) or, with
+    ``return_lse``, ``(logp, lse, n_bad_ids)``.  Asynchronous on ``stream``
+    (default: torch's current stream).
+    """
+    lib = load_library()
+    for name, t in (("h", h), ("w", w), ("ids", ids)):
+        _require_gpu(name, t)
+    if h.dtype not in _DTYPES or w.dtype != h.dtype:
+        raise ValueError("h and w must share dtype bfloat16 or float32")
+    if h.dim() != 2 or w.dim() != 2 or h.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("h and w must be 2-D with unit stride along D")
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous 1-D int32 tensor")
+    n, d = h.shape
+    v, d2 = w.shape
+    if d2 != d or ids.shape[0] != n:
+        raise ValueError(f"shape mismatch: h {tuple(h.shape)}, w {tuple(w.shape)}, ids {tuple(ids.shape)}")
+    dtype = _DTYPES[h.dtype]
+    flags = {"invariant": TIM_SCHED_INVARIANT, "free": TIM_SCHED_FREE}[schedule]
+    dev = h.device
+    logp = out if out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if return_lse else None
+    nbad = torch.zeros(1, dtype=torch.int32, device=dev) if return_lse else None
+    need = lib.tim_logprob_workspace_bytes(n, d, v, dtype, flags)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    st = lib.tim_logprob_forward(_dptr(h), h.stride(0), _dptr(w), w.stride(0), _dptr(ids),
+                                 n, d, v, dtype, flags, _dptr(logp), _dptr(lse), _dptr(nbad),
+                                 _dptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_logprob_forward")
+    if return_lse:
+        return logp, lse, nbad
+    return logp
+
+
+def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
+                       mask: Optional[torch.Tensor], cu_seqlens: torch.Tensor, *,
+                       tis_clip: float = 2.0, seq_bounds=(-0.01, 0.01),
+                       token_outputs: bool = False, seq_outputs: bool = True,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Mismatch statistics between trainer and rollout log-probabilities.
+
+    ``seq_bounds`` are log-domain bounds on a sequence's mean delta; a
+    geometric-mean-ratio window ``[a, b]`` is ``(log a, log b)``.  Returns a
+    dict with ``"batch"`` (a tensor of ``len(BATCH_FIELDS)`` fp64 values on the
+    GPU), and optionally ``"seq"`` and ``"token"`` dicts of GPU tensors.
+    """
+    lib = load_library()
+    for name, t in (("logp_train", logp_train), ("logp_rollout", logp_rollout),
+                    ("cu_seqlens", cu_seqlens)):
+        _require_gpu(name, t)
+    if mask is not None:
+        _require_gpu("mask", mask)
+        if mask.dtype != torch.uint8 or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 tensor")
+    if logp_train.dtype != torch.float32 or logp_rollout.dtype != torch.float32:
+        raise ValueError("log-probabilities must be float32")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor")
+    if not (logp_train.is_contiguous() and logp_rollout.is_contiguous()):
+        raise ValueError("log-probabilities must be contiguous")
+    n = logp_train.numel()
+    s = cu_seqlens.numel() - 1
+    if logp_rollout.numel() != n or (mask is not None and mask.numel() != n) or s < 0:
+        raise ValueError("inconsistent sizes")
+    dev = logp_train.device
+    res = {}
+    batch = torch.empty(len(BATCH_FIELDS), dtype=torch.float64, device=dev)
+    res["batch"] = batch
+    tok = None
+    if token_outputs:
+        t = {k: torch.empty(n, dtype=torch.float32, device=dev)
+             for k in ("delta", "ratio", "k1", "k2", "k3", "tis_w")}
+        t["clipped"] = torch.empty(n, dtype=torch.uint8, device=dev)
+        res["token"] = t
+        tok = _TokenOut(*[_dptr(t[k]) for k in ("delta", "ratio", "k1", "k2", "k3", "tis_w",
+                                                 "clipped")])
+    seq = None
+    if seq_outputs:
+        q = {k: torch.empty(s, dtype=torch.int32, device=dev)
+             for k in ("n_valid", "n_clipped", "n_nan")}
+        q.update({k: torch.empty(s, dtype=torch.float64, device=dev)
+                  for k in ("mean_delta", "mean_k1", "mean_k2", "mean_k3", "mean_tis_w")})
+        q["reject"] = torch.empty(s, dtype=torch.uint8, device=dev)
+        res["seq"] = q
+        seq = _SeqOut(*[_dptr(q[k]) for k in ("n_valid", "n_clipped", "n_nan", "mean_delta",
+                                               "mean_k1", "mean_k2", "mean_k3", "mean_tis_w",
+                                               "reject")])
+    need = lib.tim_stats_workspace_bytes(n, s)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    prm = _StatsParams(float(tis_clip), float(seq_bounds[0]), float(seq_bounds[1]))
+    st = lib.tim_mismatch_stats(_dptr(logp_train), _dptr(logp_rollout), _dptr(mask),
+                                _dptr(cu_seqlens), n, s, ctypes.byref(prm),
+                                ctypes.byref(tok) if tok is not None else None,
+                                ctypes.byref(seq) if seq is not None else None,
+                                _dptr(batch), _dptr(workspace),
+                                workspace.numel() * workspace.element_size(),
+                                _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_mismatch_stats")
+    return res
+
+
+def batch_dict(batch: torch.Tensor) -> dict:
+    """Host dict {name: value} of a batch aggregate tensor (synchronises)."""
+    return dict(zip(BATCH_FIELDS, (float(x) for x in batch.cpu().tolist())))
+
+
+def log_window(lo_ratio: float, hi_ratio: float):
+    """Log-domain bounds of a geometric-mean-ratio window ``[lo, hi]``."""
+    return (math.log(lo_ratio), math.log(hi_ratio))

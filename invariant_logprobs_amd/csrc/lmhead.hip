@@ -1,0 +1,438 @@
+// lmhead.hip — fused LM-head contraction, online log-sum-exp and token
+// gather for gfx950, plus the fixed-order merge of vocabulary-chunk partials.
+//
+// What is computed ("RL: Training Inference Mismatch", section "log p": the
+// chain hidden -> LM head -> logits -> log-softmax -> gather):
+//     z[t,v]  = sum_k h[t,k] W[v,k]
+//     logp[t] = z[t,a_t] - log sum_v exp z[t,v]
+// The logits live only in MFMA accumulators; they are never written.
+//
+// Batch invariance ("训推一致性与 determinism", section 1.2: a request's
+// result must not depend on which other requests share its batch): every
+// reduction order here is a function of (V, D, dtype) alone.
+//   * K order: ascending D in 128-byte stages, one MFMA accumulator chain per
+//     logit, no split-K.  A logit's bits do not depend on which MFMA column
+//     (token slot) it occupies: every column runs the same instruction
+//     sequence on its own data.
+//   * Vocabulary: fixed chunks of kInvariantChunkTiles tiles of 256 rows.
+//     Inside a chunk each lane folds its 64 rows of a tile into a running
+//     (max, sum-exp) in a fixed order, tile after tile; at the end of the
+//     chunk the two half-waves and then the two vocabulary waves are merged
+//     in a fixed order.  The merge kernel folds the chunks in ascending
+//     chunk order.
+//   * N only sets how many token tiles are launched; rows past N are clamped
+//     loads whose results are discarded.
+// This is the single-GPU form of the batch-invariant matmul/reduction the
+// pages list ("训推一致性与 determinism", section 6 table; VeXact
+// methodology), written for CDNA4 MFMA rather than copied from any design.
+
+#include "tim_internal.h"
+
+#include <math.h>
+
+namespace tim {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// LDS: two pipeline stages, each holding a 256-row W tile and a 256-row h
+// tile of kStageBytes per row (64 bf16 or 32 fp32 of K).  16-byte chunks of
+// a row are XOR-swizzled with the row index so that the 8 lanes of a
+// ds_read_b128 phase, which read 8 consecutive rows at one logical chunk,
+// hit 8 different bank groups.
+constexpr int kOperandBytes = kTileV * kStageBytes;   // 32 KiB
+constexpr int kStageLds = 2 * kOperandBytes;          // 64 KiB
+constexpr int kLdsBytes = 2 * kStageLds;              // 128 KiB
+static_assert(kTileV == kTileT, "one staging loop serves both operands");
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * kStageBytes + ((chunk ^ (row & 7)) << 4);
+}
+
+template <bool B> struct BoolConst { static constexpr bool value = B; };
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// (m, s) with s = sum exp(z - m): merge b into a.  Symmetric in its two
+// operands up to the commutativity of + and max, so two lanes that merge
+// each other's state obtain identical bits.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float mb, float sb) {
+    float mm = fmaxf(m, mb);
+    if (mm == -INFINITY) { m = mm; s = 0.f; return; }
+    float mL = mm * kLog2e;
+    float fa = (m == mm) ? 1.f : fast_exp2(fmaf(m, kLog2e, -mL));
+    float fb = (mb == mm) ? 1.f : fast_exp2(fmaf(mb, kLog2e, -mL));
+    s = s * fa + sb * fb;
+    m = mm;
+}
+
+// XCD-aware order of workgroups.  The dispatcher hands workgroup b to XCD
+// b % 8; renumber so that each XCD receives one contiguous range of logical
+// tiles, and inside the range walk groups of kGroupChunks vocabulary chunks
+// by all token tiles.  Workgroups resident on one XCD at a time then share
+// W and h stages in that XCD's L2.  Changes only who computes a tile, never
+// how: results are unaffected.
+constexpr int kGroupChunks = 4;
+__device__ __forceinline__ void tile_of_block(int64_t nchunks, int64_t nttiles,
+                                              int64_t& chunk, int64_t& ttile) {
+    const int64_t G = gridDim.x, b = blockIdx.x;
+    const int64_t per = G >> 3, rem = G & 7, x = b & 7, i = b >> 3;
+    const int64_t L = x * per + (x < rem ? x : rem) + i;
+    const int64_t span = (int64_t)kGroupChunks * nttiles;
+    const int64_t group = L / span;
+    const int64_t first = group * kGroupChunks;
+    const int64_t gm = nchunks - first < kGroupChunks ? nchunks - first : kGroupChunks;
+    const int64_t within = L - group * span;
+    chunk = first + within % gm;
+    ttile = within / gm;
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
+                       const unsigned char* __restrict__ w, int64_t ldw_b,
+                       const int32_t* __restrict__ ids, int64_t n, int64_t v,
+                       int nk, int chunk_tiles, int64_t nvtiles, int64_t nchunks,
+                       int64_t nttiles, float2* __restrict__ part,
+                       float* __restrict__ zsel, int32_t* __restrict__ n_bad_ids) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wv = wave & 1;        // vocabulary half of the tile (128 rows)
+    const int wt = wave >> 1;       // token half of the tile (128 tokens)
+    const int lrow = lane & 31;
+    const int lhalf = lane >> 5;
+
+    if (blockIdx.x == 0 && tid == 0 && n_bad_ids) *n_bad_ids = 0;
+
+    int64_t chunk, ttile;
+    tile_of_block(nchunks, nttiles, chunk, ttile);
+    const int64_t t0 = ttile * kTileT;
+    const int64_t vt_first = chunk * chunk_tiles;
+    const int ntiles_here = (int)((nvtiles - vt_first) < chunk_tiles ? (nvtiles - vt_first)
+                                                                      : chunk_tiles);
+
+    // staging assignment: 8 rows x one 16-byte chunk per operand per thread
+    const int srow = tid >> 3;      // + 32 i
+    const int schunk = tid & 7;
+    const unsigned char* hrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t t = t0 + srow + 32 * i;
+        if (t > n - 1) t = n - 1;
+        hrow[i] = h + t * ldh_b + schunk * 16;
+    }
+
+    // the 4 tokens of this lane (one per 32-column block), their target ids
+    int32_t my_id[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        int64_t t = t0 + wt * 128 + bj * 32 + lrow;
+        my_id[bj] = t < n ? ids[t] : -1;
+    }
+
+    f32x16 acc[4][4];
+    float m_run[4], s_run[4];
+    float zsel_reg[4] = {0.f, 0.f, 0.f, 0.f};   // selected logit, if owned
+    bool have_zsel = false;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) { m_run[bj] = -INFINITY; s_run[bj] = 0.f; }
+
+    u32x4 rw[8], rh[8];
+    auto load_stage = [&](int vt_local, int kb) {
+        const int64_t vbase = (vt_first + vt_local) * kTileV;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int64_t r = vbase + srow + 32 * i;
+            if (r > v - 1) r = v - 1;
+            rw[i] = *(const u32x4*)(w + r * ldw_b + schunk * 16 + (int64_t)kb * kStageBytes);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rh[i] = *(const u32x4*)(hrow[i] + (int64_t)kb * kStageBytes);
+    };
+    auto store_stage = [&](int stage) {
+        unsigned char* base = lds + stage * kStageLds;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            *(u32x4*)(base + swz(srow + 32 * i, schunk)) = rw[i];
+            *(u32x4*)(base + kOperandBytes + swz(srow + 32 * i, schunk)) = rh[i];
+        }
+    };
+
+    load_stage(0, 0);
+    store_stage(0);
+    __syncthreads();
+
+    int stage = 0;
+    for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+
+        for (int kb = 0; kb < nk; ++kb) {
+            // prefetch the next stage (next K slice, or the next tile's first)
+            const bool last_k = kb + 1 == nk;
+            const bool has_next = !last_k || vt_local + 1 < ntiles_here;
+            if (has_next) load_stage(last_k ? vt_local + 1 : vt_local, last_k ? 0 : kb + 1);
+            const unsigned char* Ws = lds + stage * kStageLds;
+            const unsigned char* Hs = Ws + kOperandBytes;
+            if constexpr (kBf16) {
+                // 4 K-steps of 16 bf16: lanes 0-31 supply K 0-7, lanes 32-63 K 8-15
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int c = ks * 2 + lhalf;
+                    bf16x8 a[4], b[4];
+#pragma unroll
+                    for (int bi = 0; bi < 4; ++bi)
+                        a[bi] = *(const bf16x8*)(Ws + swz(wv * 128 + bi * 32 + lrow, c));
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj)
+                        b[bj] = *(const bf16x8*)(Hs + swz(wt * 128 + bj * 32 + lrow, c));
+#pragma unroll
+                    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                        for (int bj = 0; bj < 4; ++bj)
+                            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+                }
+            } else {
+                // 32 fp32 of K per stage: lane half g supplies K = 16 g + 4 q + e to
+                // MFMA (q, e); each 32x32x2 instruction consumes one K of each half.
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = lhalf * 4 + q;
+                    f32x4 a[4], b[4];
+#pragma unroll
+                    for (int bi = 0; bi < 4; ++bi)
+                        a[bi] = *(const f32x4*)(Ws + swz(wv * 128 + bi * 32 + lrow, c));
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj)
+                        b[bj] = *(const f32x4*)(Hs + swz(wt * 128 + bj * 32 + lrow, c));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                            for (int bj = 0; bj < 4; ++bj)
+                                acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                    a[bi][e], b[bj][e], acc[bi][bj], 0, 0, 0);
+                }
+            }
+
+            if (has_next) store_stage(stage ^ 1);
+            __syncthreads();
+            stage ^= 1;
+        }
+
+        // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
+        // Per token column, the lane's 64 rows are folded block by block
+        // (32-row MFMA blocks bi = 0..3, 16 rows per lane each) into the
+        // running (max, sum-exp); inside a block the 16 exponentials are
+        // summed by a fixed pairwise tree.  Rows past V (last tile only) are
+        // -inf.  Branch-free apart from one uniform tail test per tile.
+        const int64_t vbase_w = (vt_first + vt_local) * kTileV + wv * 128;
+        const int64_t lim64 = v - vbase_w - lhalf * 4;    // rows < lim are valid
+        const int lim = lim64 > 128 ? 128 : (int)lim64;
+        auto fold = [&](auto masked_tag) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi) {
+                    float z[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        z[r] = acc[bi][bj][r];
+                        if constexpr (kMasked) {
+                            const int off = bi * 32 + (r >> 2) * 8 + (r & 3);
+                            z[r] = off < lim ? z[r] : -INFINITY;
+                        }
+                    }
+                    float bmax = z[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, z[r]);
+                    const float m_new = fmaxf(m_run[bj], bmax);
+                    const float mL = m_new == -INFINITY ? 0.f : m_new * kLog2e;
+                    const float scale = m_run[bj] == m_new
+                                            ? 1.f : fast_exp2(fmaf(m_run[bj], kLog2e, -mL));
+                    float e[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(z[r], kLog2e, -mL));
+#pragma unroll
+                    for (int width = 8; width >= 1; width >>= 1)
+#pragma unroll
+                        for (int r = 0; r < width; ++r) e[r] = e[r] + e[r + width];
+                    s_run[bj] = fmaf(s_run[bj], scale, e[0]);
+                    m_run[bj] = m_new;
+                }
+            }
+        };
+        if (lim < 128) fold(BoolConst<true>{});
+        else fold(BoolConst<false>{});
+
+        // gather: exactly one lane of the grid holds z[t, a_t]; rare, so one
+        // divergent region per tile keeps the value in a register
+        int tgt[4];
+        bool any_tgt = false;
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t rel = (int64_t)my_id[bj] - vbase_w;
+            const bool mine = rel >= 0 && rel < 128 && (((rel & 31) >> 2) & 1) == lhalf;
+            tgt[bj] = mine ? (int)((rel >> 5) * 16 + ((rel & 31) >> 3) * 4 + (rel & 3)) : -1;
+            any_tgt |= mine;
+        }
+        if (any_tgt) {
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        zsel_reg[bj] = tgt[bj] == bi * 16 + r ? acc[bi][bj][r] : zsel_reg[bj];
+            have_zsel |= any_tgt;
+        }
+    }
+
+    // ---- the selected logits this lane owns (one owner per token)
+    if (have_zsel) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t rel = (int64_t)my_id[bj] - vt_first * kTileV - wv * 128;
+            // owned iff the id lies in this chunk, in this wave's 128-row half
+            // of its tile, in this lane's row set
+            const int64_t chunk_rows = (int64_t)ntiles_here * kTileV;
+            const int64_t in_chunk = (int64_t)my_id[bj] - vt_first * kTileV;
+            if (in_chunk >= 0 && in_chunk < chunk_rows && ((in_chunk & 255) >> 7) == wv &&
+                (((in_chunk & 31) >> 2) & 1) == lhalf)
+                zsel[t0 + wt * 128 + bj * 32 + lrow] = zsel_reg[bj];
+            (void)rel;
+        }
+    }
+
+    // ---- end of chunk: merge half-waves, then the two vocabulary waves
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        const float mo = __shfl_xor(m_run[bj], 32);
+        const float so = __shfl_xor(s_run[bj], 32);
+        lse_combine(m_run[bj], s_run[bj], mo, so);
+    }
+    float2* xch = (float2*)lds;     // [2 token halves][128 tokens]
+    if (wv == 1 && lhalf == 0) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+            xch[wt * 128 + bj * 32 + lrow] = make_float2(m_run[bj], s_run[bj]);
+    }
+    __syncthreads();
+    if (wv == 0 && lhalf == 0) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const float2 o = xch[wt * 128 + bj * 32 + lrow];
+            float m = m_run[bj], s = s_run[bj];
+            lse_combine(m, s, o.x, o.y);
+            const int64_t t = t0 + wt * 128 + bj * 32 + lrow;
+            if (t < n) part[chunk * n + t] = make_float2(m, s);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ zsel,
+                 const int32_t* __restrict__ ids, int64_t n, int64_t nchunks, int64_t v,
+                 float* __restrict__ logp, float* __restrict__ lse,
+                 int32_t* __restrict__ n_bad_ids) {
+    __shared__ int bad_count;
+    if (threadIdx.x == 0) bad_count = 0;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < n) {
+        float m = -INFINITY, s = 0.f;
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const float2 p = part[c * n + t];
+            lse_combine(m, s, p.x, p.y);
+        }
+        const float l = m + fast_log2(s) * kLn2;
+        const int32_t a = ids[t];
+        const bool bad = a < 0 || (int64_t)a >= v;
+        logp[t] = bad ? __builtin_nanf("") : zsel[t] - l;
+        if (lse) lse[t] = l;
+        if (bad) atomicAdd(&bad_count, 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && n_bad_ids && bad_count) atomicAdd(n_bad_ids, bad_count);
+}
+
+}  // namespace
+
+bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
+                       LogprobPlan* p) {
+    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != 0 && dtype != 1) || flags > 1u)
+        return false;
+    p->n = n; p->d = d; p->v = v; p->dtype = dtype;
+    p->nvtiles = (v + kTileV - 1) / kTileV;
+    p->nttiles = (n + kTileT - 1) / kTileT;
+    if (flags == 0u) {
+        p->chunk_tiles = kInvariantChunkTiles;
+    } else {
+        // free schedule: about two workgroups per compute unit, whatever N is
+        const int64_t want = 512;
+        int64_t ct = (p->nvtiles * (p->nttiles > 0 ? p->nttiles : 1) + want - 1) / want;
+        if (ct < 1) ct = 1;
+        if (ct > p->nvtiles) ct = p->nvtiles;
+        p->chunk_tiles = (int)ct;
+    }
+    p->nchunks = (p->nvtiles + p->chunk_tiles - 1) / p->chunk_tiles;
+    p->part_bytes = align_up((size_t)p->nchunks * (size_t)n * sizeof(float2), 256);
+    p->zsel_off = p->part_bytes;
+    p->total_bytes = p->zsel_off + align_up((size_t)n * sizeof(float), 256);
+    if (p->total_bytes == 0) p->total_bytes = 256;
+    return true;
+}
+
+hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t ldh,
+                                  const void* w, int64_t ldw, const int32_t* ids,
+                                  void* workspace, int32_t* n_bad_ids, hipStream_t st) {
+    const int64_t esz = p.dtype == 0 ? 2 : 4;
+    const int nk = (int)(p.d * esz / kStageBytes);
+    const int64_t grid = p.nchunks * p.nttiles;
+    if (grid <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;
+    float2* part = (float2*)workspace;
+    float* zsel = (float*)((unsigned char*)workspace + p.zsel_off);
+    if (p.dtype == 0) {
+        hipLaunchKernelGGL(lmhead_partials_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
+                           ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
+                           part, zsel, n_bad_ids);
+    } else {
+        hipLaunchKernelGGL(lmhead_partials_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
+                           ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
+                           part, zsel, n_bad_ids);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const void* workspace,
+                            float* logp, float* lse, int32_t* n_bad_ids, hipStream_t st) {
+    const float2* part = (const float2*)workspace;
+    const float* zsel = (const float*)((const unsigned char*)workspace + p.zsel_off);
+    const int64_t blocks = (p.n + 255) / 256;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, zsel,
+                       ids, p.n, p.nchunks, p.v, logp, lse, n_bad_ids);
+    return hipGetLastError();
+}
+
+}  // namespace tim

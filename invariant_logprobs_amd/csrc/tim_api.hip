@@ -1,0 +1,103 @@
+// tim_api.hip — the C ABI of libtim.so (declared in include/tim.h): argument
+// validation on the host, workspace sizing, and kernel launches on the
+// caller's stream.  No device memory is allocated here and no call
+// synchronises.
+
+#include "tim.h"
+#include "tim_internal.h"
+
+#include <math.h>
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int tim_abi_version(void) { return TIM_ABI_VERSION; }
+
+const char* tim_status_string(int status) {
+    switch (status) {
+        case TIM_OK: return "TIM_OK: success";
+        case TIM_EINVAL: return "TIM_EINVAL: invalid argument";
+        case TIM_EUNSUPPORTED: return "TIM_EUNSUPPORTED: unsupported size, leading dimension or alignment";
+        case TIM_EWORKSPACE: return "TIM_EWORKSPACE: workspace missing or too small";
+        case TIM_EHIP: return "TIM_EHIP: HIP launch or runtime error";
+        default: return "unknown tim_status";
+    }
+}
+
+size_t tim_logprob_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags) {
+    tim::LogprobPlan p;
+    if (!tim::make_logprob_plan(n, d, v, dtype, flags, &p)) return 0;
+    return p.total_bytes;
+}
+
+int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                        const int32_t* ids, int64_t n, int64_t d, int64_t v, int dtype,
+                        unsigned flags, float* logp, float* lse, int32_t* n_bad_ids,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != TIM_BF16 && dtype != TIM_F32) ||
+        flags > TIM_SCHED_FREE)
+        return TIM_EINVAL;
+    if (ldh < d || ldw < d) return TIM_EINVAL;
+    if (n == 0) return TIM_OK;
+    if (!h || !w || !ids || !logp) return TIM_EINVAL;
+    const int64_t esz = dtype == TIM_BF16 ? 2 : 4;
+    if (d % 64 != 0) return TIM_EUNSUPPORTED;
+    if ((ldh * esz) % 16 != 0 || (ldw * esz) % 16 != 0) return TIM_EUNSUPPORTED;
+    if (!aligned(h, 16) || !aligned(w, 16)) return TIM_EUNSUPPORTED;
+    tim::LogprobPlan p;
+    if (!tim::make_logprob_plan(n, d, v, dtype, flags, &p)) return TIM_EINVAL;
+    if (p.nchunks * p.nttiles > INT32_MAX) return TIM_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (tim::launch_lmhead_partials(p, h, ldh, w, ldw, ids, workspace, n_bad_ids, st) != hipSuccess)
+        return TIM_EHIP;
+    if (tim::launch_lse_merge(p, ids, workspace, logp, lse, n_bad_ids, st) != hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
+size_t tim_stats_workspace_bytes(int64_t n, int64_t s) {
+    tim::StatsPlan p;
+    if (!tim::make_stats_plan(n, s, &p)) return 0;
+    return p.total_bytes;
+}
+
+int tim_mismatch_stats(const float* logp_train, const float* logp_rollout, const uint8_t* mask,
+                       const int32_t* cu_seqlens, int64_t n, int64_t s, const tim_stats_params* p,
+                       const tim_token_out* tok, const tim_seq_out* seq, double* batch,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || s < 0 || !p) return TIM_EINVAL;
+    if (!(p->tis_clip_c > 0.0) || !isfinite(p->tis_clip_c)) return TIM_EINVAL;
+    if (!(p->seq_lo <= p->seq_hi)) return TIM_EINVAL;
+    if (n > 0 && s < 1) return TIM_EINVAL;
+    if (n == 0 && s == 0) return TIM_OK;
+    if (n > 0 && (!logp_train || !logp_rollout)) return TIM_EINVAL;
+    if (!cu_seqlens) return TIM_EINVAL;
+    tim::StatsPlan plan;
+    if (!tim::make_stats_plan(n, s, &plan)) return TIM_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < plan.total_bytes) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+
+    tim::StatsParamsDev prm;
+    prm.clip_c = p->tis_clip_c;
+    prm.log_c = log(p->tis_clip_c);
+    prm.seq_lo = p->seq_lo;
+    prm.seq_hi = p->seq_hi;
+    tim::TokenOutPtrs to{};
+    if (tok) to = {tok->delta, tok->ratio, tok->k1, tok->k2, tok->k3, tok->tis_w, tok->clipped};
+    tim::SeqOutPtrs so{};
+    if (seq) so = {seq->n_valid, seq->n_clipped, seq->n_nan, seq->mean_delta, seq->mean_k1,
+                   seq->mean_k2, seq->mean_k3, seq->mean_tis_w, seq->reject};
+    if (tim::launch_mismatch_stats(plan, logp_train, logp_rollout, mask, cu_seqlens, prm, to, so,
+                                   batch, workspace, (hipStream_t)stream) != hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
+}  // extern "C"

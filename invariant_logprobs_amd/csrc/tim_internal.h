@@ -1,0 +1,88 @@
+// tim_internal.h — kernel launch interfaces shared by the C-ABI layer and
+// the kernel translation units of libtim.so.  Not installed; not part of
+// the public ABI (that is include/tim.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tim {
+
+// ---------------------------------------------------------------------------
+// LM-head log-probability kernels (lmhead.hip)
+// ---------------------------------------------------------------------------
+
+// Tile geometry of the fused contraction + online log-sum-exp kernel.
+// A workgroup owns kTileV vocabulary rows x kTileT tokens of the logit
+// matrix at a time and walks one vocabulary *chunk* (kChunkTiles tiles in
+// the batch-invariant schedule) in ascending order, carrying a running
+// (max, sum-exp) per token in registers.
+constexpr int kTileV = 256;
+constexpr int kTileT = 256;
+constexpr int kStageBytes = 128;   // bytes of K per row per pipeline stage
+constexpr int kThreads = 256;      // 4 waves of 64
+constexpr int kInvariantChunkTiles = 2;   // 512 vocabulary entries per chunk
+
+// Workspace layout of tim_logprob_forward (all offsets 256-byte aligned):
+//   [0, part_bytes)           float2 partials[nchunks][n]: (max, sum-exp)
+//   [zsel_off, +4n)           float  zsel[n]: the selected logit
+struct LogprobPlan {
+    int64_t n, d, v;
+    int dtype;            // 0 bf16, 1 fp32
+    int chunk_tiles;      // vocabulary tiles per chunk
+    int64_t nvtiles;      // ceil(v / kTileV)
+    int64_t nchunks;      // ceil(nvtiles / chunk_tiles)
+    int64_t nttiles;      // ceil(n / kTileT)
+    size_t part_bytes, zsel_off, total_bytes;
+};
+
+// Fills `p`; returns false for sizes the library does not accept.
+bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
+                       LogprobPlan* p);
+
+hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t ldh,
+                                  const void* w, int64_t ldw, const int32_t* ids,
+                                  void* workspace, int32_t* n_bad_ids, hipStream_t st);
+hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const void* workspace,
+                            float* logp, float* lse, int32_t* n_bad_ids, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Mismatch statistics kernels (stats.hip)
+// ---------------------------------------------------------------------------
+
+// Tokens per sub-chunk.  Every sequence is cut into sub-chunks that start at
+// the sequence's first token and every kSubChunk tokens after it, so a
+// sequence's reduction order depends on nothing but its own length.
+constexpr int kSubChunk = 1024;
+
+struct StatsParamsDev {
+    double clip_c, log_c, seq_lo, seq_hi;
+};
+
+struct StatsPlan {
+    int64_t n, s, nwin, nblk_seq;
+    size_t fmap_off, first_off, tail_off, blk_off, total_bytes;
+};
+
+bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p);
+
+struct TokenOutPtrs {
+    float *delta, *ratio, *k1, *k2, *k3, *tis_w;
+    uint8_t* clipped;
+};
+struct SeqOutPtrs {
+    int32_t *n_valid, *n_clipped, *n_nan;
+    double *mean_delta, *mean_k1, *mean_k2, *mean_k3, *mean_tis_w;
+    uint8_t* reject;
+};
+
+hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const float* lr,
+                                 const uint8_t* mask, const int32_t* cu,
+                                 const StatsParamsDev& prm, const TokenOutPtrs& tok,
+                                 const SeqOutPtrs& seq, double* batch, void* workspace,
+                                 hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace tim

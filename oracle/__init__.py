@@ -39,6 +39,8 @@ _LIB_PATH = os.path.join(_OUT_DIR, "libtim_oracle.so")
 
 BF16 = 0
 F32 = 1
+# default thread cap: the oracle shares its host with the GPU job
+MAX_THREADS = 16
 
 # Batch vector field names, in index order (restated from the definitions;
 # not imported from the library).
@@ -154,6 +156,8 @@ def logprob(h, w, ids, *, dtype: int, rows=None, nthreads: int = 0):
     zsel = np.empty(nr, np.float64)
     if nr == 0:
         return logp, lse, zsel, 0
+    if nthreads <= 0:
+        nthreads = min(available_cpus(), MAX_THREADS)
     used = _load().or_logprob_rows(_ptr(h), d, _ptr(w), d, _ptr(ids), dtype, d, v,
                                    _ptr(rows_arr), nr, _ptr(logp), _ptr(lse),
                                    _ptr(zsel), int(nthreads))

@@ -1,0 +1,125 @@
+"""Host-side checks of libtim.so: it loads, exports every symbol the header
+declares, sizes workspaces as documented, and rejects bad arguments before any
+launch.  No call here reaches the GPU (every checked path returns during host
+validation), so these run without one."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_logprobs_amd as tim
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tim.h")
+FAKE = 0x10000           # non-null, 256-byte aligned host value; never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tim_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tim.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert declared == sorted(tim.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.tim_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert tim.status_string(st).startswith("TIM_")
+    assert "unknown" in tim.status_string(99)
+
+
+def test_logprob_workspace_layout(lib):
+    # invariant schedule: 512-entry vocabulary chunks, (max, sum) fp32 pairs
+    n, d, v = 8192, 4096, 151936
+    chunks = -(-v // 512)
+    assert chunks == 297
+    want = -(-(chunks * n * 8) // 256) * 256 + -(-(n * 4) // 256) * 256
+    assert lib.tim_logprob_workspace_bytes(n, d, v, tim.TIM_BF16, tim.TIM_SCHED_INVARIANT) == want
+    # the invariant layout does not depend on dtype; it scales with n only linearly
+    assert lib.tim_logprob_workspace_bytes(n, d, v, tim.TIM_F32, 0) == want
+    assert lib.tim_logprob_workspace_bytes(-1, d, v, 0, 0) == 0
+    assert lib.tim_logprob_workspace_bytes(n, d, v, 7, 0) == 0
+    assert lib.tim_logprob_workspace_bytes(n, d, v, 0, 5) == 0
+    assert lib.tim_stats_workspace_bytes(1 << 20, 1000) > 0
+    assert lib.tim_stats_workspace_bytes(-1, 3) == 0
+
+
+def _fwd(lib, **kw):
+    a = dict(h=FAKE, ldh=64, w=FAKE, ldw=64, ids=FAKE, n=4, d=64, v=100, dtype=0, flags=0,
+             logp=FAKE, lse=None, nbad=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.tim_logprob_forward(a["h"], a["ldh"], a["w"], a["ldw"], a["ids"], a["n"], a["d"],
+                                   a["v"], a["dtype"], a["flags"], a["logp"], a["lse"],
+                                   a["nbad"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_logprob_argument_errors(lib):
+    assert _fwd(lib, n=-1) == tim.TIM_EINVAL
+    assert _fwd(lib, d=0) == tim.TIM_EINVAL
+    assert _fwd(lib, v=0) == tim.TIM_EINVAL
+    assert _fwd(lib, v=1 << 31) == tim.TIM_EINVAL
+    assert _fwd(lib, dtype=2) == tim.TIM_EINVAL
+    assert _fwd(lib, flags=2) == tim.TIM_EINVAL
+    assert _fwd(lib, ldh=32) == tim.TIM_EINVAL
+    assert _fwd(lib, ldw=63) == tim.TIM_EINVAL
+    assert _fwd(lib, h=None) == tim.TIM_EINVAL
+    assert _fwd(lib, ids=None) == tim.TIM_EINVAL
+    assert _fwd(lib, logp=None) == tim.TIM_EINVAL
+    assert _fwd(lib, d=96, ldh=96, ldw=96) == tim.TIM_EUNSUPPORTED      # d % 64
+    assert _fwd(lib, ldh=68) == tim.TIM_EUNSUPPORTED                     # 136 B rows
+    assert _fwd(lib, dtype=1, ldh=66, ldw=64) == tim.TIM_EUNSUPPORTED    # fp32, 264 B rows
+    assert _fwd(lib, h=FAKE + 8) == tim.TIM_EUNSUPPORTED                 # 16-byte alignment
+    assert _fwd(lib, ws=None) == tim.TIM_EWORKSPACE
+    assert _fwd(lib, wsb=16) == tim.TIM_EWORKSPACE
+    assert _fwd(lib, ws=FAKE + 16) == tim.TIM_EUNSUPPORTED               # 256-byte alignment
+    # n == 0: success with no launch and no pointer needed
+    assert _fwd(lib, n=0, h=None, w=None, ids=None, logp=None, ws=None) == tim.TIM_OK
+
+
+def _stats(lib, n=10, s=2, c=2.0, lo=-0.01, hi=0.01, lt=FAKE, lr=FAKE, cu=FAKE, ws=FAKE,
+           wsb=1 << 30, params=True):
+    p = tim._StatsParams(c, lo, hi)
+    return lib.tim_mismatch_stats(lt, lr, None, cu, n, s, ctypes.byref(p) if params else None,
+                                  None, None, None, ws, wsb, None)
+
+
+def test_stats_argument_errors(lib):
+    assert _stats(lib, n=-1) == tim.TIM_EINVAL
+    assert _stats(lib, s=-1) == tim.TIM_EINVAL
+    assert _stats(lib, s=0) == tim.TIM_EINVAL
+    assert _stats(lib, params=False) == tim.TIM_EINVAL
+    assert _stats(lib, c=0.0) == tim.TIM_EINVAL
+    assert _stats(lib, c=-2.0) == tim.TIM_EINVAL
+    assert _stats(lib, c=float("inf")) == tim.TIM_EINVAL
+    assert _stats(lib, c=float("nan")) == tim.TIM_EINVAL
+    assert _stats(lib, lo=0.1, hi=0.0) == tim.TIM_EINVAL
+    assert _stats(lib, lo=float("nan")) == tim.TIM_EINVAL
+    assert _stats(lib, lt=None) == tim.TIM_EINVAL
+    assert _stats(lib, cu=None) == tim.TIM_EINVAL
+    assert _stats(lib, ws=None) == tim.TIM_EWORKSPACE
+    assert _stats(lib, wsb=8) == tim.TIM_EWORKSPACE
+    assert _stats(lib, ws=FAKE + 64) == tim.TIM_EUNSUPPORTED
+    assert _stats(lib, n=1 << 31, s=2) == tim.TIM_EUNSUPPORTED
+    assert _stats(lib, n=0, s=0, lt=None, lr=None, cu=None, ws=None) == tim.TIM_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    h = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        tim.tim_logprob_forward(h, h, torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        tim.tim_mismatch_stats(torch.zeros(4), torch.zeros(4), None,
+                               torch.tensor([0, 4], dtype=torch.int32))
