@@ -102,7 +102,7 @@ def test_workload_stats_parity(name):
 
 def _stress(n, seed):
     lt, lr, mask, cu = workloads.stats_scale(n, seed=seed, device=DEV)
-    # add empty sequences and an all-masked sequence
+    # add empty sequences (index 2 and the last two) and an all-masked one (4)
     cu_h = cu.cpu().numpy().tolist()
     cu_h = cu_h[:3] + [cu_h[2]] + cu_h[3:] + [cu_h[-1], cu_h[-1]]
     cu2 = torch.tensor(cu_h, dtype=torch.int32, device=DEV)
@@ -118,7 +118,9 @@ def test_stress_input_parity():
     res, ref = run_both(lt, lr, mask, cu, 2.0, lo, hi)
     got = compare(res, ref, lo, hi, cu, "stress")
     assert got["n_nan"] > 0 and got["n_clipped"] > 0 and got["n_seq_rejected"] > 0
-    assert res["seq"]["n_valid"].cpu()[3].item() == 0       # the inserted empty sequence
+    nv = res["seq"]["n_valid"].cpu()
+    assert nv[2].item() == 0            # the inserted empty sequence [c2, c2)
+    assert nv[4].item() == 0            # the all-masked sequence
 
 
 def test_large_stats_parity_without_token_outputs():
