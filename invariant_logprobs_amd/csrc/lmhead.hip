@@ -18,8 +18,8 @@
 //     Inside a chunk each lane folds its 64 rows of a tile into a running
 //     (max, sum-exp) in a fixed order, tile after tile; at the end of the
 //     chunk the two half-waves and then the two vocabulary waves are merged
-//     in a fixed order.  The merge kernel folds the chunks in ascending
-//     chunk order.
+//     in a fixed order.  The merge kernel folds the chunks in a fixed order
+//     that depends on the number of chunks only.
 //   * N only sets how many token tiles are launched; rows past N are clamped
 //     loads whose results are discarded.
 // This is the single-GPU form of the batch-invariant matmul/reduction the
@@ -349,22 +349,46 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     }
 }
 
-__global__ void __launch_bounds__(256)
+// Merge of the vocabulary-chunk partials.  A block serves 64 tokens with
+// kMergeWaves waves: wave w folds chunks w, w + kMergeWaves, ... in ascending
+// order for its 64 tokens (coalesced 8-byte loads, kMergeUnroll in flight),
+// then wave 0 folds the kMergeWaves strands in order.  The order depends on
+// the number of chunks only.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeUnroll = 4;
+
+__global__ void __launch_bounds__(64 * kMergeWaves)
 lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ zsel,
                  const int32_t* __restrict__ ids, int64_t n, int64_t nchunks, int64_t v,
                  float* __restrict__ logp, float* __restrict__ lse,
                  int32_t* __restrict__ n_bad_ids) {
+    __shared__ float2 strand[kMergeWaves][64];
     __shared__ int bad_count;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) bad_count = 0;
+    const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t tc = t < n ? t : n - 1;
+    float m = -INFINITY, s = 0.f;
+    int64_t c = wave;
+    for (; c + (kMergeUnroll - 1) * kMergeWaves < nchunks; c += kMergeUnroll * kMergeWaves) {
+        float2 p[kMergeUnroll];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) p[u] = part[(c + u * kMergeWaves) * n + tc];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) lse_combine(m, s, p[u].x, p[u].y);
+    }
+    for (; c < nchunks; c += kMergeWaves) {
+        const float2 p = part[c * n + tc];
+        lse_combine(m, s, p.x, p.y);
+    }
+    strand[wave][lane] = make_float2(m, s);
     __syncthreads();
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < n) {
-        float m = -INFINITY, s = 0.f;
-        for (int64_t c = 0; c < nchunks; ++c) {
-            const float2 p = part[c * n + t];
-            lse_combine(m, s, p.x, p.y);
-        }
-        const float l = m + fast_log2(s) * kLn2;
+    if (wave == 0 && t < n) {
+        float mm = strand[0][lane].x, ss = strand[0][lane].y;
+#pragma unroll
+        for (int w = 1; w < kMergeWaves; ++w) lse_combine(mm, ss, strand[w][lane].x, strand[w][lane].y);
+        const float l = mm + fast_log2(ss) * kLn2;
         const int32_t a = ids[t];
         const bool bad = a < 0 || (int64_t)a >= v;
         logp[t] = bad ? __builtin_nanf("") : zsel[t] - l;
@@ -429,8 +453,8 @@ hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const void
                             float* logp, float* lse, int32_t* n_bad_ids, hipStream_t st) {
     const float2* part = (const float2*)workspace;
     const float* zsel = (const float*)((const unsigned char*)workspace + p.zsel_off);
-    const int64_t blocks = (p.n + 255) / 256;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, zsel,
+    const int64_t blocks = (p.n + 63) / 64;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0, st, part, zsel,
                        ids, p.n, p.nchunks, p.v, logp, lse, n_bad_ids);
     return hipGetLastError();
 }

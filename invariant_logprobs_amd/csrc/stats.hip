@@ -13,20 +13,24 @@
 // Mismatch", monitoring flow), and the is_* ratios named in
 // "Train-Inference Consistency", section 5.
 //
-// The pass is HBM-bound: 9 bytes per token are read once.  Layout of the
-// work:
-//   1. window_map: for every window of kSubChunk tokens, the first sequence
-//      starting at or after the window start (one thread per sequence).
-//   2. stream: one wavefront per window.  It reduces every sub-chunk that
-//      *starts* in its window (a sequence's first kSubChunk tokens, or a
-//      continuation kSubChunk * k tokens into a sequence), so each wave
-//      reads at most 2 * kSubChunk tokens and no search is needed.  A
-//      sub-chunk is folded lane-locally in token order, then across the
-//      wave with a fixed butterfly; its reduction order depends only on the
-//      token offsets inside the sub-chunk, so per-sequence sums do not
-//      depend on the rest of the batch.
+// The pass is HBM-bound: 9 bytes per token are read once.  Every sequence is
+// cut into sub-chunks of at most kSubChunk tokens that start at the
+// sequence's first token and every kSubChunk tokens after it; a sub-chunk's
+// sums are folded in an order that depends only on token offsets inside it,
+// so a sequence's results never depend on the rest of the batch.
+//
+//   1. plan_count / plan_scan / plan_write: integer prefix sum of the
+//      sub-chunk counts; writes one (start, length) descriptor per
+//      sub-chunk, in token order, and each sequence's first descriptor.
+//   2. stats_stream: each wave takes kSubPerWave consecutive descriptors and
+//      streams their tokens through a kRing-slot LDS ring in kPiece-token
+//      pieces.  Pieces are copied global -> LDS with global_load_lds_dword
+//      (no registers held by loads in flight), kRing - 1 pieces ahead of the
+//      fold, with exact vmcnt waits.  Sub-chunk partials are staged in LDS
+//      and written once when the wave is done, so no store is ever counted
+//      among the ring's loads.
 //   3. seq_finalize: one thread per sequence folds its sub-chunks in
-//      ascending order, writes means and flags, and each block folds its
+//      ascending order, writes means and flags; each block folds its
 //      sequences into a block partial with a fixed tree.
 //   4. batch_finalize: one block folds the block partials in a fixed tree.
 
@@ -42,6 +46,7 @@ struct alignas(16) SubPartial {
     double sd, sk2, sk3, sw, sabs, maxabs;
     int32_t nvalid, nclip, nnan, pad;
 };
+static_assert(sizeof(SubPartial) == 64, "four 16-byte quarters");
 
 // Contribution of one sequence to the batch, and the running fold of many.
 struct alignas(16) BatchAcc {
@@ -50,49 +55,95 @@ struct alignas(16) BatchAcc {
     int64_t nvalid, nclip, nnan, nonempty, rejected;
 };
 
+struct SubDesc {
+    uint32_t start, len;
+};
+
 constexpr int kWave = 64;
-constexpr int kPerLane = kSubChunk / kWave;   // tokens per lane per sub-chunk
 constexpr int kFinBlock = 256;
+constexpr int kScanBlock = 1024;
+constexpr int kPiece = 256;                 // tokens per ring slot
+constexpr int kRing = 4;                    // ring slots per wave
+constexpr int kSubPerWave = 16;             // descriptors per wave
+constexpr int kStreamWaves = 4;             // waves per block
 
-__device__ __forceinline__ double shfl_xor_d(double x, int m) {
-    int lo = __double2loint(x), hi = __double2hiint(x);
-    lo = __shfl_xor(lo, m);
-    hi = __shfl_xor(hi, m);
-    return __hiloint2double(hi, lo);
+
+__device__ __forceinline__ int64_t clamp_cu(const int32_t* cu, int64_t j, int64_t n) {
+    // cu_seqlens is a documented precondition; clamping keeps a malformed one
+    // from producing an out-of-range access (it can only give wrong numbers)
+    const int64_t c = cu[j];
+    return c < 0 ? 0 : (c > n ? n : c);
 }
 
-// e^d - 1 - d and e^d - 1 for finite d.  For |d| <= 1/32 a degree-8 Taylor
-// polynomial evaluated as d^2 * P(d) (no cancellation; truncation error
-// < 2^-60 relative); otherwise the library expm1.
-__device__ __forceinline__ void k3_em1(double d, double& k3, double& em1) {
-    if (fabs(d) <= 0.03125) {
-        double p = 1.0 / 40320.0;
-        p = fma(p, d, 1.0 / 5040.0);
-        p = fma(p, d, 1.0 / 720.0);
-        p = fma(p, d, 1.0 / 120.0);
-        p = fma(p, d, 1.0 / 24.0);
-        p = fma(p, d, 1.0 / 6.0);
-        p = fma(p, d, 0.5);
-        k3 = (d * d) * p;
-        em1 = d + k3;
-    } else {
-        em1 = expm1(d);
-        k3 = em1 - d;
+__device__ __forceinline__ uint32_t subchunks_of(const int32_t* cu, int64_t j, int64_t n) {
+    const int64_t a = clamp_cu(cu, j, n), e = clamp_cu(cu, j + 1, n);
+    return e > a ? (uint32_t)((e - a + kSubChunk - 1) / kSubChunk) : 0u;
+}
+
+// Inclusive scan of one value per thread over a kScanBlock-thread block.
+__device__ uint32_t block_scan_incl(uint32_t x, uint32_t* sh) {
+    const int tid = threadIdx.x;
+    sh[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < kScanBlock; off <<= 1) {
+        const uint32_t y = tid >= off ? sh[tid - off] : 0u;
+        __syncthreads();
+        sh[tid] += y;
+        __syncthreads();
     }
+    const uint32_t r = sh[tid];
+    __syncthreads();
+    return r;
 }
 
-__global__ void __launch_bounds__(256)
-window_map_kernel(const int32_t* __restrict__ cu, int64_t s, int64_t nwin,
-                  int32_t* __restrict__ fmap) {
-    // fmap[w] = first sequence j with cu[j] >= w * kSubChunk, for w < nwin.
-    // Sequence j owns the windows w with cu[j-1] < w*SC <= cu[j].
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j > s) return;
-    const int64_t hi = cu[j];
-    const int64_t lo = j == 0 ? -1 : (int64_t)cu[j - 1];
-    const int64_t w_begin = lo < 0 ? 0 : lo / kSubChunk + 1;
-    const int64_t w_end = hi / kSubChunk;       // inclusive: w * SC <= hi
-    for (int64_t wdx = w_begin; wdx <= w_end && wdx < nwin; ++wdx) fmap[wdx] = (int32_t)j;
+__global__ void __launch_bounds__(kScanBlock)
+plan_count_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, uint32_t* __restrict__ bsum) {
+    __shared__ uint32_t sh[kScanBlock];
+    const int64_t j = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
+    const uint32_t c = j < s ? subchunks_of(cu, j, n) : 0u;
+    const uint32_t incl = block_scan_incl(c, sh);
+    if (threadIdx.x == kScanBlock - 1) bsum[blockIdx.x] = incl;
+}
+
+__global__ void __launch_bounds__(kScanBlock)
+plan_scan_kernel(const uint32_t* __restrict__ bsum, int64_t nb, uint32_t* __restrict__ boff,
+                 uint32_t* __restrict__ total) {
+    __shared__ uint32_t sh[kScanBlock];
+    __shared__ uint32_t last;
+    uint32_t carry = 0;
+    for (int64_t b0 = 0; b0 < nb; b0 += kScanBlock) {
+        const int64_t b = b0 + threadIdx.x;
+        const uint32_t x = b < nb ? bsum[b] : 0u;
+        const uint32_t incl = block_scan_incl(x, sh);
+        if (b < nb) boff[b] = carry + incl - x;
+        if (threadIdx.x == kScanBlock - 1) last = incl;
+        __syncthreads();
+        carry += last;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *total = carry;
+}
+
+__global__ void __launch_bounds__(kScanBlock)
+plan_write_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_t tmax,
+                  const uint32_t* __restrict__ boff, uint32_t* __restrict__ seq_off,
+                  SubDesc* __restrict__ desc) {
+    __shared__ uint32_t sh[kScanBlock];
+    const int64_t j = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
+    const uint32_t c = j < s ? subchunks_of(cu, j, n) : 0u;
+    const uint32_t incl = block_scan_incl(c, sh);
+    if (j < s) {
+        const uint32_t off = boff[blockIdx.x] + incl - c;
+        seq_off[j] = off;
+        const int64_t a = clamp_cu(cu, j, n), e = clamp_cu(cu, j + 1, n);
+        // a well-formed cu_seqlens never reaches tmax; the bound keeps a
+        // malformed one inside the descriptor array
+        for (uint32_t k = 0; k < c && (int64_t)off + k < tmax; ++k) {
+            const int64_t st = a + (int64_t)k * kSubChunk;
+            const int64_t en = st + kSubChunk < e ? st + kSubChunk : e;
+            desc[off + k] = SubDesc{(uint32_t)st, (uint32_t)(en - st)};
+        }
+    }
 }
 
 struct TokOut {
@@ -100,112 +151,302 @@ struct TokOut {
     uint8_t* clipped;
 };
 
-// Reduce tokens [a, b) (b - a <= kSubChunk) with one wavefront.  All lanes
-// return identical sums.
-__device__ __forceinline__ SubPartial reduce_subchunk(
-    int64_t a, int64_t b, int lane, const float* __restrict__ lt, const float* __restrict__ lr,
-    const uint8_t* __restrict__ mask, const StatsParamsDev& prm, const TokOut& tok) {
-    double sd = 0, sk2 = 0, sk3 = 0, sw = 0, sabs = 0, mx = 0;
-    int nvalid = 0, nclip = 0, nnan = 0;
-    const int iters = (int)((b - a + kWave - 1) / kWave);
-    for (int i = 0; i < iters; ++i) {
-        const int64_t t = a + lane + (int64_t)kWave * i;
-        if (t >= b) continue;
-        const bool scored = mask ? mask[t] != 0 : true;
-        double d = 0, r = 1, k1 = 0, k2 = 0, k3 = 0, wgt = 0;
-        bool clipped = false;
-        if (scored) {
-            d = (double)lt[t] - (double)lr[t];
-            k1 = -d;
-            k2 = 0.5 * d * d;
-            if (isfinite(d)) {
-                double em1;
-                k3_em1(d, k3, em1);
-                r = 1.0 + em1;
-                clipped = d > prm.log_c;
-                wgt = clipped ? prm.clip_c : r;
-                nvalid += 1;
-                nclip += clipped;
-                sd += d; sk2 += k2; sk3 += k3; sw += wgt;
-                const double ad = fabs(d);
-                sabs += ad;
-                mx = fmax(mx, ad);
-            } else {
-                nnan += 1;
-                r = exp(d);
-                k3 = expm1(d) - d;
-            }
-        }
-        if (tok.delta) tok.delta[t] = (float)d;
-        if (tok.ratio) tok.ratio[t] = (float)r;
-        if (tok.k1) tok.k1[t] = (float)k1;
-        if (tok.k2) tok.k2[t] = (float)k2;
-        if (tok.k3) tok.k3[t] = (float)k3;
-        if (tok.tis_w) tok.tis_w[t] = (float)wgt;
-        if (tok.clipped) tok.clipped[t] = clipped ? 1 : 0;
-    }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        sd += shfl_xor_d(sd, m);
-        sk2 += shfl_xor_d(sk2, m);
-        sk3 += shfl_xor_d(sk3, m);
-        sw += shfl_xor_d(sw, m);
-        sabs += shfl_xor_d(sabs, m);
-        mx = fmax(mx, shfl_xor_d(mx, m));
-        nvalid += __shfl_xor(nvalid, m);
-        nclip += __shfl_xor(nclip, m);
-        nnan += __shfl_xor(nnan, m);
-    }
-    SubPartial p;
-    p.sd = sd; p.sk2 = sk2; p.sk3 = sk3; p.sw = sw; p.sabs = sabs; p.maxabs = mx;
-    p.nvalid = nvalid; p.nclip = nclip; p.nnan = nnan; p.pad = 0;
-    return p;
+// One ring slot: a piece of lt and lr, and the 4-byte words holding its
+// mask bytes (a piece's bytes span at most kPiece/4 + 1 words).  A slot is
+// also the scratch of the cross-lane fold (64 lanes x 6 doubles), so it is
+// sized to hold that.
+constexpr int kFoldVals = 6;
+struct alignas(16) Slot {
+    float lt[kPiece];
+    float lr[kPiece];
+    uint32_t mw[4 * kWave];
+};
+static_assert(sizeof(Slot) >= kWave * kFoldVals * sizeof(double), "fold scratch fits a slot");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma_dword(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0);
 }
 
-__global__ void __launch_bounds__(256)
-stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
-                    const uint8_t* __restrict__ mask, const int32_t* __restrict__ cu,
-                    int64_t n, int64_t s, int64_t nwin, const int32_t* __restrict__ fmap,
-                    StatsParamsDev prm, TokOut tok, SubPartial* __restrict__ first,
-                    SubPartial* __restrict__ tail) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wdx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    if (wdx >= nwin) return;
-    const int64_t win0 = wdx * kSubChunk;
-    const int64_t win1 = win0 + kSubChunk < n ? win0 + kSubChunk : n;
-    // cu values are clamped to [0, n] and f to [0, s] so that a malformed
-    // cu_seqlens (a documented precondition) can give wrong numbers but never
-    // an out-of-range access
-    auto cuc = [&](int64_t j) -> int64_t {
-        const int64_t c = cu[j];
-        return c < 0 ? 0 : (c > n ? n : c);
-    };
-    int64_t f = fmap[wdx];                          // first sequence starting >= win0
-    f = f < 0 ? 0 : (f > s ? s : f);
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt low
+// bits [3:0] and high bits [15:14]; expcnt [6:4] = 7 and lgkmcnt [11:8] = 15
+// mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-    // continuation sub-chunk of the sequence that started before the window
-    const int64_t cf = cuc(f);
-    if (f > 0 && cf > win0) {
-        const int64_t j = f - 1;
-        const int64_t c0 = cuc(j);                  // c0 < win0 < cu[j+1] = cf
-        const int64_t k = (win0 - c0 + kSubChunk - 1) / kSubChunk;
-        const int64_t a = c0 + k * kSubChunk;
-        if (a < win1 && a < cf) {
-            const int64_t b = a + kSubChunk < cf ? a + kSubChunk : cf;
-            const SubPartial p = reduce_subchunk(a, b, lane, lt, lr, mask, prm, tok);
-            if (lane == 0) tail[wdx] = p;
+// Wait until at most `ahead` pieces (kPer loads each) remain in flight.
+template <int kPer>
+__device__ __forceinline__ void wait_pieces_ahead(uint32_t ahead) {
+    static_assert(kRing == 4, "cases cover up to three pieces ahead");
+    switch (ahead) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<kPer>(); break;
+        case 2: wait_vmcnt<2 * kPer>(); break;
+        default: wait_vmcnt<3 * kPer>(); break;
+    }
+}
+
+// e^d - 1 for finite |d| > 1/32 (the rare branch; |d| <= 1/32 uses a Taylor
+// polynomial for e^d - 1 - d).  Range reduction d = k ln2 + r with
+// |r| <= ln2 / 2 (ln2 split in a high part exact in 32 bits and a low part),
+// e^r - 1 by a degree-12 Taylor polynomial (truncation < 1e-15 relative),
+// then e^d - 1 = 2^k (e^r - 1) + (2^k - 1); both terms are exact-sign sums, so
+// no cancellation beyond one rounding.  d > 709.78 overflows to +inf and
+// d < -745 gives -1, as the exact value rounds.
+__device__ __forceinline__ double expm1_large(double d) {
+    if (d > 709.782712893384) return INFINITY;
+    if (d < -745.0) return -1.0;
+    const double kLn2Hi = 6.93147180369123816490e-01;   // 0x3FE62E42FEE00000
+    const double kLn2Lo = 1.90821492927058770002e-10;
+    const double k = rint(d * 1.4426950408889634);
+    const double r = fma(-k, kLn2Lo, fma(-k, kLn2Hi, d));
+    // e^r - 1 = r + r^2/2! + ... + r^12/12!
+    double q = 1.0 / 479001600.0;
+    q = fma(q, r, 1.0 / 39916800.0);
+    q = fma(q, r, 1.0 / 3628800.0);
+    q = fma(q, r, 1.0 / 362880.0);
+    q = fma(q, r, 1.0 / 40320.0);
+    q = fma(q, r, 1.0 / 5040.0);
+    q = fma(q, r, 1.0 / 720.0);
+    q = fma(q, r, 1.0 / 120.0);
+    q = fma(q, r, 1.0 / 24.0);
+    q = fma(q, r, 1.0 / 6.0);
+    q = fma(q, r, 0.5);
+    const double er1 = fma(q * r, r, r);                 // e^r - 1
+    const int ki = (int)k;
+    if (ki > 1023) {                                      // 2^k itself overflows
+        return ldexp(er1 + 1.0, ki);
+    }
+    const double p2 = ldexp(1.0, ki);                     // 2^k, exact
+    return fma(p2, er1, p2 - 1.0);
+}
+
+struct Acc {
+    double sd, sd2, sk3, sem1, sabs, mx;   // sem1: sum of e^d - 1 over unclipped tokens
+    uint32_t nvalid, nclip, nnan;
+    __device__ void zero() { sd = sd2 = sk3 = sem1 = sabs = mx = 0; nvalid = nclip = nnan = 0; }
+};
+
+// Fold the piece of a sub-chunk (start sub_start, length len) that begins at
+// offset off0, read from slot `sl`: lane l takes offsets off0 + l + 64 i, i
+// ascending, so across a sub-chunk's pieces each lane folds its offsets in
+// ascending order.  Straight-line code: every slot entry is a valid copy, so
+// the LDS reads are unconditional; a token that does not count (outside the
+// sub-chunk, masked out or non-finite) gets delta = 0, which makes its d,
+// d^2, k3 and |d| contributions exactly 0 with no further selects.  Counts
+// come from ballots of single compares combined on the scalar unit.  k2 is
+// accumulated as d^2 and halved once (a power-of-two scale: exact).  The
+// truncated weight sum is assembled as n_unclipped + sum(e^d - 1 over
+// unclipped) + C n_clipped, with e^d - 1 = d + k3.
+template <bool kTok, bool kMask>
+__device__ __forceinline__ void fold_piece(Acc& A, const Slot& sl, uint32_t mshift,
+                                           uint32_t sub_start, uint32_t off0, uint32_t len,
+                                           int lane, const StatsParamsDev& prm,
+                                           const TokOut& tok) {
+    const unsigned char* mb = (const unsigned char*)sl.mw;
+    const uint32_t lim = len - off0;                          // valid piece offsets < lim
+#pragma unroll
+    for (int i = 0; i < kPiece / kWave; ++i) {
+        if ((uint32_t)(i * kWave) >= lim) break;              // uniform: rest of piece empty
+        const uint32_t po = (uint32_t)(i * kWave + lane);      // offset in the piece
+        const float x = sl.lt[po];
+        const float y = sl.lr[po];
+        const double draw = (double)x - (double)y;
+        const uint64_t b_in = __builtin_amdgcn_ballot_w64(po < lim);
+        const uint64_t b_m = kMask ? __builtin_amdgcn_ballot_w64(mb[mshift + po] != 0) : ~0ull;
+        const uint64_t b_f = __builtin_amdgcn_ballot_w64(isfinite(draw));
+        const uint64_t b_scored = b_in & b_m;
+        const uint64_t b_fin = b_scored & b_f;
+        const uint64_t bit = 1ull << lane;
+        const bool fin = (b_fin & bit) != 0;
+        const double d = fin ? draw : 0.0;
+        // e^d - 1 - d without cancellation for |d| <= 1/32 (degree-6 Taylor,
+        // truncation below 2e-11 relative)
+        const double d2 = d * d;
+        double p = 1.0 / 720.0;
+        p = fma(p, d, 1.0 / 120.0);
+        p = fma(p, d, 1.0 / 24.0);
+        p = fma(p, d, 1.0 / 6.0);
+        p = fma(p, d, 0.5);
+        double k3 = d2 * p;
+        if (!(fabs(d) <= 0.03125)) k3 = expm1_large(d) - d;            // rare
+        const double em1 = d + k3;
+        const uint64_t b_clip = __builtin_amdgcn_ballot_w64(draw > prm.log_c) & b_fin;
+        const bool clipped = (b_clip & bit) != 0;
+        A.sd += d;
+        A.sd2 += d2;
+        A.sk3 += k3;
+        A.sem1 += clipped ? 0.0 : em1;
+        A.sabs += fabs(d);
+        A.mx = fmax(A.mx, fabs(d));
+        A.nvalid += (uint32_t)__popcll(b_fin);
+        A.nclip += (uint32_t)__popcll(b_clip);
+        A.nnan += (uint32_t)__popcll(b_scored & ~b_f);
+        if (kTok && po < lim) {
+            // per-token outputs; a non-finite delta reports exp/expm1 as computed
+            const bool scored = (b_scored & bit) != 0;
+            const uint32_t t = sub_start + off0 + po;
+            const double dd = scored ? draw : 0.0;
+            const double r = 1.0 + em1;
+            const double wgt = clipped ? prm.clip_c : (fin ? r : 0.0);
+            const double rr = fin ? r : (scored ? exp(dd) : 1.0);
+            const double kk3 = fin ? k3 : (scored ? expm1(dd) - dd : 0.0);
+            if (tok.delta) tok.delta[t] = (float)dd;
+            if (tok.ratio) tok.ratio[t] = (float)rr;
+            if (tok.k1) tok.k1[t] = (float)(-dd);
+            if (tok.k2) tok.k2[t] = (float)(0.5 * (dd * dd));
+            if (tok.k3) tok.k3[t] = (float)kk3;
+            if (tok.tis_w) tok.tis_w[t] = (float)wgt;
+            if (tok.clipped) tok.clipped[t] = clipped ? 1 : 0;
         }
     }
-    // first sub-chunk of every sequence that starts inside the window
-    for (int64_t j = f; j < s; ++j) {
-        const int64_t a = cuc(j);
-        if (a >= win1) break;
-        const int64_t e = cuc(j + 1);
-        if (e <= a) continue;                       // empty sequence
-        const int64_t b = a + kSubChunk < e ? a + kSubChunk : e;
-        const SubPartial p = reduce_subchunk(a, b, lane, lt, lr, mask, prm, tok);
-        if (lane == 0) first[j] = p;
+}
+
+// Cross-lane fold of a sub-chunk's six fp64 sums through LDS scratch, in a
+// fixed order: each lane stores its six values; lane j < 48 sums lanes
+// 8 (j % 8) .. 8 (j % 8) + 7 of value j / 8 in lane order; lanes 0..5 sum
+// the eight partials of their value in order.  Returns the sub-chunk's
+// partial (valid in every lane).  Counts come from ballots already.
+__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int lane, void* scratch) {
+    double* v = (double*)scratch;                 // [kFoldVals][64]
+    v[0 * kWave + lane] = A.sd;
+    v[1 * kWave + lane] = A.sd2;
+    v[2 * kWave + lane] = A.sk3;
+    v[3 * kWave + lane] = A.sem1;
+    v[4 * kWave + lane] = A.sabs;
+    v[5 * kWave + lane] = A.mx;
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    double part = 0.0;
+    const int val = lane >> 3, grp = lane & 7;
+    if (lane < kFoldVals * 8) {
+        const double* src = v + val * kWave + grp * 8;
+        part = src[0];
+        if (val == 5) {
+#pragma unroll
+            for (int i = 1; i < 8; ++i) part = fmax(part, src[i]);
+        } else {
+#pragma unroll
+            for (int i = 1; i < 8; ++i) part += src[i];
+        }
     }
+    // the 48 partials overwrite the head of the scratch: LDS operations of a
+    // wave complete in order, so every read above has its value first
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    if (lane < kFoldVals * 8) v[lane] = part;
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    double tot = 0.0;
+    if (lane < kFoldVals) {
+        const double* src = v + lane * 8;
+        tot = src[0];
+        if (lane == 5) {
+#pragma unroll
+            for (int i = 1; i < 8; ++i) tot = fmax(tot, src[i]);
+        } else {
+#pragma unroll
+            for (int i = 1; i < 8; ++i) tot += src[i];
+        }
+    }
+    const double sd = __shfl(tot, 0), sd2 = __shfl(tot, 1), sk3 = __shfl(tot, 2);
+    const double sem1 = __shfl(tot, 3), sabs = __shfl(tot, 4), mx = __shfl(tot, 5);
+    SubPartial q;
+    q.sd = sd; q.sk2 = 0.5 * sd2; q.sk3 = sk3;
+    q.sw = ((double)(A.nvalid - A.nclip) + sem1) + clip_c * (double)A.nclip;
+    q.sabs = sabs;
+    q.maxabs = mx; q.nvalid = (int32_t)A.nvalid; q.nclip = (int32_t)A.nclip;
+    q.nnan = (int32_t)A.nnan; q.pad = 0;
+    return q;
+}
+
+template <bool kTok, bool kMask>
+__global__ void __launch_bounds__(kWave * kStreamWaves)
+stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
+                    const uint8_t* __restrict__ mask, const SubDesc* __restrict__ desc,
+                    const uint32_t* __restrict__ total, uint32_t tmax, StatsParamsDev prm,
+                    TokOut tok, SubPartial* __restrict__ partial) {
+    __shared__ Slot ring[kStreamWaves][kRing];
+    __shared__ SubPartial stage[kStreamWaves][kSubPerWave];
+    constexpr int kPer = 2 * (kPiece / kWave) + (kMask ? 2 : 0);   // DMA loads per piece
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    uint32_t T = __builtin_amdgcn_readfirstlane(*total);
+    T = T < tmax ? T : tmax;
+    const uint64_t k0 = ((uint64_t)blockIdx.x * kStreamWaves + wv) * kSubPerWave;
+    if (k0 >= T) return;
+    const uint32_t nsub = (uint32_t)(T - k0 < kSubPerWave ? T - k0 : kSubPerWave);
+    Slot* R = ring[wv];
+
+    // this wave's descriptors, one per lane; read by any lane with shfl
+    const SubDesc my = lane < (int)nsub ? desc[k0 + lane] : SubDesc{0u, 0u};
+    auto d_start = [&](uint32_t k) { return (uint32_t)__shfl((int)my.start, (int)k); };
+    auto d_len = [&](uint32_t k) { return (uint32_t)__shfl((int)my.len, (int)k); };
+
+    uint32_t npieces = 0;
+    for (uint32_t k = 0; k < nsub; ++k) npieces += (d_len(k) + kPiece - 1) / kPiece;
+
+    // issue iterator: (sub-chunk ik, piece ip)
+    uint32_t ik = 0, ip = 0, is0 = d_start(0), il = d_len(0);
+    auto issue = [&](uint32_t slot) {
+        Slot& S = R[slot];
+        const uint32_t st = is0 + ip * kPiece;
+        const uint32_t en = st + kPiece < is0 + il ? st + kPiece : is0 + il;
+        const uint32_t cnt = en - st;
+        const float* blt = lt + st;              // uniform bases, small per-lane offsets
+        const float* blr = lr + st;
+#pragma unroll
+        for (int j = 0; j < kPiece / kWave; ++j) {
+            uint32_t o = (uint32_t)(j * kWave + lane);
+            o = o < cnt ? o : cnt - 1;
+            dma_dword(blt + o, S.lt + j * kWave);
+            dma_dword(blr + o, S.lr + j * kWave);
+        }
+        if (kMask) {
+            const uintptr_t m0 = (uintptr_t)(mask + st) & ~(uintptr_t)3;
+            const uintptr_t m1 = ((uintptr_t)(mask + en) + 3) & ~(uintptr_t)3;
+            const uint32_t nw = (uint32_t)((m1 - m0) >> 2);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint32_t wd = (uint32_t)(j * kWave + lane);
+                wd = wd < nw ? wd : nw - 1;
+                dma_dword((const void*)(m0 + 4 * (uintptr_t)wd), S.mw + j * kWave);
+            }
+        }
+        if (++ip * kPiece >= il) {
+            ip = 0;
+            if (++ik < nsub) { is0 = d_start(ik); il = d_len(ik); }
+        }
+    };
+
+    uint32_t issued = 0;
+    for (; issued < kRing - 1 && issued < npieces; ++issued) issue(issued);
+
+    Acc A;
+    A.zero();
+    uint32_t fk = 0, fp = 0, fs = d_start(0), fl = d_len(0);
+    for (uint32_t c = 0; c < npieces; ++c) {
+        // the slot refilled here held piece c - 1, folded in the last iteration
+        if (issued < npieces) { issue(issued % kRing); ++issued; }
+        if (kTok) wait_vmcnt<0>();          // token stores share the counter
+        else wait_pieces_ahead<kPer>(issued - c - 1);
+        const Slot& S = R[c % kRing];
+        const uint32_t mshift = kMask ? (uint32_t)((uintptr_t)(mask + fs + fp * kPiece) & 3) : 0u;
+        fold_piece<kTok, kMask>(A, S, mshift, fs, fp * kPiece, fl, lane, prm, tok);
+        if (++fp * kPiece >= fl) {
+            const SubPartial q = finish(A, prm.clip_c, lane, (void*)&R[c % kRing]);
+            if (lane == 0) stage[wv][fk] = q;
+            A.zero();
+            fp = 0;
+            if (++fk < nsub) { fs = d_start(fk); fl = d_len(fk); }
+        }
+    }
+    // every ring load has completed (the last fold waited for vmcnt(0));
+    // lane l writes 16 bytes of staged partial l / 4
+    __builtin_amdgcn_s_waitcnt(0);
+    const int e = lane >> 2, q4 = lane & 3;
+    if (e < (int)nsub) ((uint4*)&partial[k0 + e])[q4] = ((const uint4*)&stage[wv][e])[q4];
 }
 
 __device__ __forceinline__ void acc_add(BatchAcc& x, const BatchAcc& y) {
@@ -239,22 +480,21 @@ struct SeqOut {
 };
 
 __global__ void __launch_bounds__(kFinBlock)
-seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, StatsParamsDev prm,
-                    const SubPartial* __restrict__ first, const SubPartial* __restrict__ tail,
+seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_t tmax,
+                    StatsParamsDev prm,
+                    const uint32_t* __restrict__ seq_off, const SubPartial* __restrict__ partial,
                     SeqOut so, BatchAcc* __restrict__ blk) {
     __shared__ BatchAcc buf[kFinBlock];
     const int64_t j = (int64_t)blockIdx.x * kFinBlock + threadIdx.x;
     BatchAcc c = acc_zero();
     if (j < s) {
-        int64_t a = cu[j], e = cu[j + 1];
-        a = a < 0 ? 0 : (a > n ? n : a);            // see stats_stream_kernel
-        e = e < a ? a : (e > n ? n : e);
+        const uint32_t nsub = subchunks_of(cu, j, n);
         double sd = 0, sk2 = 0, sk3 = 0, sw = 0, sabs = 0, mx = 0;
         int64_t nvalid = 0, nclip = 0, nnan = 0;
-        if (e > a) {
-            const int64_t nsub = (e - a + kSubChunk - 1) / kSubChunk;
-            for (int64_t k = 0; k < nsub; ++k) {
-                const SubPartial p = k == 0 ? first[j] : tail[(a + k * kSubChunk) / kSubChunk];
+        if (nsub > 0) {
+            const uint32_t off = seq_off[j];
+            for (uint32_t k = 0; k < nsub && (int64_t)off + k < tmax; ++k) {
+                const SubPartial p = partial[off + k];
                 sd += p.sd; sk2 += p.sk2; sk3 += p.sk3; sw += p.sw; sabs += p.sabs;
                 mx = fmax(mx, p.maxabs);
                 nvalid += p.nvalid; nclip += p.nclip; nnan += p.nnan;
@@ -331,13 +571,23 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     if (n < 0 || s < 0 || s > INT32_MAX - 1 || n > INT32_MAX) return false;
     p->n = n;
     p->s = s;
-    p->nwin = (n + kSubChunk - 1) / kSubChunk;
+    // sum over sequences of ceil(len / SC) <= n / SC + s
+    p->tmax = (n + kSubChunk - 1) / kSubChunk + s;
+    p->nblk_scan = (s + kScanBlock - 1) / kScanBlock;
     p->nblk_seq = (s + kFinBlock - 1) / kFinBlock;
     size_t off = 0;
-    p->fmap_off = off;  off += align_up((size_t)(p->nwin + 1) * sizeof(int32_t), 256);
-    p->first_off = off; off += align_up((size_t)s * sizeof(SubPartial), 256);
-    p->tail_off = off;  off += align_up((size_t)p->nwin * sizeof(SubPartial), 256);
-    p->blk_off = off;   off += align_up((size_t)(p->nblk_seq > 0 ? p->nblk_seq : 1) * sizeof(BatchAcc), 256);
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes > 0 ? bytes : 1, 256);
+        return o;
+    };
+    p->bsum_off = take((size_t)p->nblk_scan * 4);
+    p->boff_off = take((size_t)p->nblk_scan * 4);
+    p->total_off = take(4);
+    p->seqoff_off = take((size_t)s * 4);
+    p->desc_off = take((size_t)p->tmax * sizeof(SubDesc));
+    p->part_off = take((size_t)p->tmax * sizeof(SubPartial));
+    p->blk_off = take((size_t)(p->nblk_seq > 0 ? p->nblk_seq : 1) * sizeof(BatchAcc));
     p->total_bytes = off;
     return true;
 }
@@ -348,23 +598,45 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
                                  const SeqOutPtrs& seq, double* batch, void* workspace,
                                  hipStream_t st) {
     unsigned char* ws = (unsigned char*)workspace;
-    int32_t* fmap = (int32_t*)(ws + p.fmap_off);
-    SubPartial* first = (SubPartial*)(ws + p.first_off);
-    SubPartial* tail = (SubPartial*)(ws + p.tail_off);
+    uint32_t* bsum = (uint32_t*)(ws + p.bsum_off);
+    uint32_t* boff = (uint32_t*)(ws + p.boff_off);
+    uint32_t* total = (uint32_t*)(ws + p.total_off);
+    uint32_t* seq_off = (uint32_t*)(ws + p.seqoff_off);
+    SubDesc* desc = (SubDesc*)(ws + p.desc_off);
+    SubPartial* partial = (SubPartial*)(ws + p.part_off);
     BatchAcc* blk = (BatchAcc*)(ws + p.blk_off);
     TokOut to{tok.delta, tok.ratio, tok.k1, tok.k2, tok.k3, tok.tis_w, tok.clipped};
     SeqOut so{seq.n_valid, seq.n_clipped, seq.n_nan, seq.mean_delta, seq.mean_k1,
               seq.mean_k2, seq.mean_k3, seq.mean_tis_w, seq.reject};
-    if (p.nwin > 0) {
-        hipLaunchKernelGGL(window_map_kernel, dim3((unsigned)((p.s + 1 + 255) / 256)), dim3(256),
-                           0, st, cu, p.s, p.nwin, fmap);
-        const int64_t threads = p.nwin * 64;
-        hipLaunchKernelGGL(stats_stream_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                           0, st, lt, lr, mask, cu, p.n, p.s, p.nwin, fmap, prm, to, first, tail);
-    }
-    if (p.s > 0)
+    if (p.s > 0) {
+        hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
+                           cu, p.n, p.s, bsum);
+        hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kScanBlock), 0, st, bsum, p.nblk_scan,
+                           boff, total);
+        hipLaunchKernelGGL(plan_write_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
+                           cu, p.n, p.s, p.tmax, boff, seq_off, desc);
+        if (p.n > 0) {
+            const int64_t waves = (p.tmax + kSubPerWave - 1) / kSubPerWave;
+            const dim3 grid((unsigned)((waves + kStreamWaves - 1) / kStreamWaves));
+            const dim3 bdim(kWave * kStreamWaves);
+            const bool want_tok = to.delta || to.ratio || to.k1 || to.k2 || to.k3 || to.tis_w ||
+                                  to.clipped;
+            if (want_tok && mask)
+                hipLaunchKernelGGL((stats_stream_kernel<true, true>), grid, bdim, 0, st, lt, lr,
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+            else if (want_tok)
+                hipLaunchKernelGGL((stats_stream_kernel<true, false>), grid, bdim, 0, st, lt, lr,
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+            else if (mask)
+                hipLaunchKernelGGL((stats_stream_kernel<false, true>), grid, bdim, 0, st, lt, lr,
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+            else
+                hipLaunchKernelGGL((stats_stream_kernel<false, false>), grid, bdim, 0, st, lt, lr,
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+        }
         hipLaunchKernelGGL(seq_finalize_kernel, dim3((unsigned)p.nblk_seq), dim3(kFinBlock), 0, st,
-                           cu, p.n, p.s, prm, first, tail, so, blk);
+                           cu, p.n, p.s, p.tmax, prm, seq_off, partial, so, blk);
+    }
     if (batch)
         hipLaunchKernelGGL(batch_finalize_kernel, dim3(1), dim3(kFinBlock), 0, st, blk,
                            p.nblk_seq, batch);

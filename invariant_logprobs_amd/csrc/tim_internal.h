@@ -60,9 +60,13 @@ struct StatsParamsDev {
     double clip_c, log_c, seq_lo, seq_hi;
 };
 
+// Workspace layout of tim_mismatch_stats (offsets 256-byte aligned): scan
+// block sums and offsets, the sub-chunk count, each sequence's first
+// sub-chunk index, the sub-chunk descriptors and partials (at most
+// tmax = ceil(n / kSubChunk) + s of each), and per-block batch partials.
 struct StatsPlan {
-    int64_t n, s, nwin, nblk_seq;
-    size_t fmap_off, first_off, tail_off, blk_off, total_bytes;
+    int64_t n, s, tmax, nblk_scan, nblk_seq;
+    size_t bsum_off, boff_off, total_off, seqoff_off, desc_off, part_off, blk_off, total_bytes;
 };
 
 bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p);
