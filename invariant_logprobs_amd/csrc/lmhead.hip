@@ -10,7 +10,7 @@
 // Batch invariance ("训推一致性与 determinism", section 1.2: a request's
 // result must not depend on which other requests share its batch): every
 // reduction order here is a function of (V, D, dtype) alone.
-//   * K order: ascending D in 128-byte stages, one MFMA accumulator chain per
+//   * K order: ascending D in 64-byte stages, one MFMA accumulator chain per
 //     logit, no split-K.  A logit's bits do not depend on which MFMA column
 //     (token slot) it occupies: every column runs the same instruction
 //     sequence on its own data.
@@ -41,18 +41,66 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// LDS: two pipeline stages, each holding a 256-row W tile and a 256-row h
-// tile of kStageBytes per row (64 bf16 or 32 fp32 of K).  16-byte chunks of
-// a row are XOR-swizzled with the row index so that the 8 lanes of a
-// ds_read_b128 phase, which read 8 consecutive rows at one logical chunk,
-// hit 8 different bank groups.
-constexpr int kOperandBytes = kTileV * kStageBytes;   // 32 KiB
-constexpr int kStageLds = 2 * kOperandBytes;          // 64 KiB
-constexpr int kLdsBytes = 2 * kStageLds;              // 128 KiB
+// LDS: a ring of kRing pipeline stages, each holding a 256-row W tile and a
+// 256-row h tile of kStageBytes per row (32 bf16 or 16 fp32 of K).  Stages
+// are filled by global_load_lds_dwordx4 (64 lanes x 16 bytes = 16 rows per
+// instruction) kRing - 1 stages ahead of the MFMAs.  The four 16-byte chunks
+// of a row are XOR-swizzled with (row >> 2) & 3: the 16 lanes of one
+// ds_read_b128 phase read 16 consecutive rows at one logical chunk, and
+// with 64-byte rows those land on 16 distinct 16-byte bank groups of the
+// 64-bank LDS.
+constexpr int kRing = 4;
+constexpr int kOperandBytes = kTileV * kStageBytes;   // 16 KiB
+constexpr int kStageLds = 2 * kOperandBytes;          // 32 KiB
+constexpr int kLdsBytes = kRing * kStageLds;          // 128 KiB
+constexpr int kDmaPerStage = 8;                       // per wave: 4 W + 4 h blocks
 static_assert(kTileV == kTileT, "one staging loop serves both operands");
+static_assert(kStageBytes == 64, "swizzle and fragment mapping assume 64-byte rows");
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kStageBytes + ((chunk ^ (row & 7)) << 4);
+    return row * kStageBytes + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+}
+
+// Eight 16-byte LDS reads followed by s_waitcnt lgkmcnt(0), in one asm block.
+// The ring is filled by LDS DMA; written as ordinary loads, the compiler
+// cannot tell the slot being read from the slots still being filled and
+// waits for every copy in flight (vmcnt(0)) before each read, which would
+// serialise the pipeline.  The explicit vmcnt waits in the main loop are what
+// order these reads after the copies of their own stage.  Every read of the
+// block has completed when it returns, so no LDS operation issued here is
+// left outstanding for the compiler's own lgkmcnt bookkeeping.
+__device__ __forceinline__ void lds_read_8x16(u32x4 (&r)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt vmcnt(N) only (gfx9 encoding; expcnt and lgkmcnt fields at max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <bool B> struct BoolConst { static constexpr bool value = B; };
@@ -66,9 +114,8 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ void lse_combine(float& m, float& s, float mb, float sb) {
     float mm = fmaxf(m, mb);
     if (mm == -INFINITY) { m = mm; s = 0.f; return; }
-    float mL = mm * kLog2e;
-    float fa = (m == mm) ? 1.f : fast_exp2(fmaf(m, kLog2e, -mL));
-    float fb = (mb == mm) ? 1.f : fast_exp2(fmaf(mb, kLog2e, -mL));
+    float fa = (m == mm) ? 1.f : fast_exp2((m - mm) * kLog2e);
+    float fb = (mb == mm) ? 1.f : fast_exp2((mb - mm) * kLog2e);
     s = s * fa + sb * fb;
     m = mm;
 }
@@ -122,17 +169,6 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     const int ntiles_here = (int)((nvtiles - vt_first) < chunk_tiles ? (nvtiles - vt_first)
                                                                       : chunk_tiles);
 
-    // staging assignment: 8 rows x one 16-byte chunk per operand per thread
-    const int srow = tid >> 3;      // + 32 i
-    const int schunk = tid & 7;
-    const unsigned char* hrow[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int64_t t = t0 + srow + 32 * i;
-        if (t > n - 1) t = n - 1;
-        hrow[i] = h + t * ldh_b + schunk * 16;
-    }
-
     // the 4 tokens of this lane (one per 32-column block), their target ids
     int32_t my_id[4];
 #pragma unroll
@@ -148,33 +184,71 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) { m_run[bj] = -INFINITY; s_run[bj] = 0.f; }
 
-    u32x4 rw[8], rh[8];
-    auto load_stage = [&](int vt_local, int kb) {
-        const int64_t vbase = (vt_first + vt_local) * kTileV;
+    // DMA assignment: wave `wave` fills 16-row blocks 4 wave .. 4 wave + 3 of
+    // both operands; lane i writes physical chunk i % 4 of row 16 blk + i / 4,
+    // i.e. logical chunk (i % 4) ^ ((row >> 2) & 3).  Addresses are a uniform
+    // 64-bit base plus a 32-bit per-lane byte offset (a tile spans well under
+    // 4 GiB of rows).  Rows past N or V are redirected to the last valid row;
+    // their results are discarded or masked.
+    uint32_t hoff[4], wrow_off[4], wtail_off[4];
+    int drow[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int64_t r = vbase + srow + 32 * i;
-            if (r > v - 1) r = v - 1;
-            rw[i] = *(const u32x4*)(w + r * ldw_b + schunk * 16 + (int64_t)kb * kStageBytes);
-        }
+    for (int j = 0; j < 4; ++j) {
+        drow[j] = (wave * 4 + j) * 16 + (lane >> 2);
+        const uint32_t cb = (uint32_t)(((lane & 3) ^ ((drow[j] >> 2) & 3)) * 16);
+        int64_t t = t0 + drow[j];
+        if (t > n - 1) t = n - 1;
+        hoff[j] = (uint32_t)((t - t0) * ldh_b) + cb;
+        wrow_off[j] = (uint32_t)(drow[j] * ldw_b) + cb;
+        wtail_off[j] = cb;             // + (v - 1 - vbase) * ldw_b, set per tile
+    }
+    const unsigned char* hbase = h + t0 * ldh_b;
+    uint32_t woff[4];
+    const unsigned char* wbase = w;
+    auto set_wtile = [&](int vt_l) {
+        const int64_t vbase = (vt_first + vt_l) * kTileV;
+        wbase = w + vbase * ldw_b;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            rh[i] = *(const u32x4*)(hrow[i] + (int64_t)kb * kStageBytes);
-    };
-    auto store_stage = [&](int stage) {
-        unsigned char* base = lds + stage * kStageLds;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            *(u32x4*)(base + swz(srow + 32 * i, schunk)) = rw[i];
-            *(u32x4*)(base + kOperandBytes + swz(srow + 32 * i, schunk)) = rh[i];
-        }
+        for (int j = 0; j < 4; ++j)
+            woff[j] = vbase + drow[j] < v ? wrow_off[j]
+                                          : (uint32_t)((v - 1 - vbase) * ldw_b) + wtail_off[j];
     };
 
-    load_stage(0, 0);
-    store_stage(0);
-    __syncthreads();
+    // per-lane LDS byte offsets of the 8 fragments of each of the 2 k-steps
+    const uint32_t lds_base = lds_addr(lds);
+    uint32_t frag_off[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int c = kBf16 ? ks * 2 + lhalf : lhalf * 2 + ks;
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) frag_off[ks][bi] = (uint32_t)swz(wv * 128 + bi * 32 + lrow, c);
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+            frag_off[ks][4 + bj] = (uint32_t)(kOperandBytes + swz(wt * 128 + bj * 32 + lrow, c));
+    }
 
-    int stage = 0;
+    const int nsteps = ntiles_here * nk;
+    int iss = 0, iss_vt = 0, iss_kb = 0;
+    set_wtile(0);
+    auto issue_next = [&]() {
+        unsigned char* base = lds + (iss & (kRing - 1)) * kStageLds;
+        const int64_t koff = (int64_t)iss_kb * kStageBytes;
+        const unsigned char* wb = wbase + koff;
+        const unsigned char* hb = hbase + koff;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dma16(wb + woff[j], base + (wave * 4 + j) * 1024);
+            dma16(hb + hoff[j], base + kOperandBytes + (wave * 4 + j) * 1024);
+        }
+        ++iss;
+        if (++iss_kb == nk) {
+            iss_kb = 0;
+            if (++iss_vt < ntiles_here) set_wtile(iss_vt);
+        }
+    };
+    for (int i = 0; i < kRing - 1 && iss < nsteps; ++i) issue_next();
+
+    int st = 0;
     for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)
@@ -183,45 +257,46 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-        for (int kb = 0; kb < nk; ++kb) {
-            // prefetch the next stage (next K slice, or the next tile's first)
-            const bool last_k = kb + 1 == nk;
-            const bool has_next = !last_k || vt_local + 1 < ntiles_here;
-            if (has_next) load_stage(last_k ? vt_local + 1 : vt_local, last_k ? 0 : kb + 1);
-            const unsigned char* Ws = lds + stage * kStageLds;
-            const unsigned char* Hs = Ws + kOperandBytes;
-            if constexpr (kBf16) {
-                // 4 K-steps of 16 bf16: lanes 0-31 supply K 0-7, lanes 32-63 K 8-15
+        for (int kb = 0; kb < nk; ++kb, ++st) {
+            // this wave's copies for stage st have landed ...
+            const int ahead = iss - st - 1;
+            if (ahead >= 2) wait_vmcnt<2 * kDmaPerStage>();
+            else if (ahead == 1) wait_vmcnt<kDmaPerStage>();
+            else wait_vmcnt<0>();
+            // ... and everyone's have; everyone is also done reading stage
+            // st - 1, whose slot the next issue refills
+            __syncthreads();
+            if (iss < nsteps) issue_next();
+
+            const uint32_t sbase = lds_base + (uint32_t)((st & (kRing - 1)) * kStageLds);
+            // fragment k-step ks: A rows wv*128 + bi*32 + lrow, B rows
+            // wt*128 + bj*32 + lrow, logical chunk ks*2 + lhalf (bf16) or
+            // lhalf*2 + ks (fp32)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int c = ks * 2 + lhalf;
-                    bf16x8 a[4], b[4];
+            for (int ks = 0; ks < 2; ++ks) {
+                uint32_t ad[8];
 #pragma unroll
-                    for (int bi = 0; bi < 4; ++bi)
-                        a[bi] = *(const bf16x8*)(Ws + swz(wv * 128 + bi * 32 + lrow, c));
-#pragma unroll
-                    for (int bj = 0; bj < 4; ++bj)
-                        b[bj] = *(const bf16x8*)(Hs + swz(wt * 128 + bj * 32 + lrow, c));
+                for (int i = 0; i < 8; ++i) ad[i] = sbase + frag_off[ks][i];
+                u32x4 f[8];
+                lds_read_8x16(f, ad);
+                if constexpr (kBf16) {
+                    // lanes 0-31 supply K 0-7 of the 16-K step, lanes 32-63 K 8-15
 #pragma unroll
                     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
                         for (int bj = 0; bj < 4; ++bj)
                             acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                a[bi], b[bj], acc[bi][bj], 0, 0, 0);
-                }
-            } else {
-                // 32 fp32 of K per stage: lane half g supplies K = 16 g + 4 q + e to
-                // MFMA (q, e); each 32x32x2 instruction consumes one K of each half.
+                                __builtin_bit_cast(bf16x8, f[bi]), __builtin_bit_cast(bf16x8, f[4 + bj]),
+                                acc[bi][bj], 0, 0, 0);
+                } else {
+                    // 16 fp32 of K per stage: lane half g supplies K = 8 g + 4 ks + e
+                    // to MFMA (ks, e); each 32x32x2 instruction consumes one K of
+                    // each half.  Whole vectors are cast before indexing: casting
+                    // single elements of the asm outputs made this compiler
+                    // pass element 0 for every e.
+                    f32x4 ff[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = lhalf * 4 + q;
-                    f32x4 a[4], b[4];
-#pragma unroll
-                    for (int bi = 0; bi < 4; ++bi)
-                        a[bi] = *(const f32x4*)(Ws + swz(wv * 128 + bi * 32 + lrow, c));
-#pragma unroll
-                    for (int bj = 0; bj < 4; ++bj)
-                        b[bj] = *(const f32x4*)(Hs + swz(wt * 128 + bj * 32 + lrow, c));
+                    for (int i = 0; i < 8; ++i) ff[i] = __builtin_bit_cast(f32x4, f[i]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -229,13 +304,9 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
                             for (int bj = 0; bj < 4; ++bj)
                                 acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                    a[bi][e], b[bj][e], acc[bi][bj], 0, 0, 0);
+                                    ff[bi][e], ff[4 + bj][e], acc[bi][bj], 0, 0, 0);
                 }
             }
-
-            if (has_next) store_stage(stage ^ 1);
-            __syncthreads();
-            stage ^= 1;
         }
 
         // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
@@ -266,12 +337,14 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
                     for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, z[r]);
                     const float m_new = fmaxf(m_run[bj], bmax);
-                    const float mL = m_new == -INFINITY ? 0.f : m_new * kLog2e;
+                    // exponents as (z - m) log2 e: exactly 0 for the maximum, so
+                    // its term is exactly 1 (a V = 1 row gets logp = 0 exactly)
+                    const float mref = m_new == -INFINITY ? 0.f : m_new;
                     const float scale = m_run[bj] == m_new
-                                            ? 1.f : fast_exp2(fmaf(m_run[bj], kLog2e, -mL));
+                                            ? 1.f : fast_exp2((m_run[bj] - mref) * kLog2e);
                     float e[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(z[r], kLog2e, -mL));
+                    for (int r = 0; r < 16; ++r) e[r] = fast_exp2((z[r] - mref) * kLog2e);
 #pragma unroll
                     for (int width = 8; width >= 1; width >>= 1)
 #pragma unroll
@@ -330,7 +403,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         const float so = __shfl_xor(s_run[bj], 32);
         lse_combine(m_run[bj], s_run[bj], mo, so);
     }
-    float2* xch = (float2*)lds;     // [2 token halves][128 tokens]
+    __shared__ float2 xch[2 * 128];  // [token half][token]
     if (wv == 1 && lhalf == 0) {
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj)

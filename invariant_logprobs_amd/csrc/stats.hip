@@ -152,16 +152,13 @@ struct TokOut {
 };
 
 // One ring slot: a piece of lt and lr, and the 4-byte words holding its
-// mask bytes (a piece's bytes span at most kPiece/4 + 1 words).  A slot is
-// also the scratch of the cross-lane fold (64 lanes x 6 doubles), so it is
-// sized to hold that.
-constexpr int kFoldVals = 6;
+// mask bytes (a piece's bytes span at most kPiece/4 + 1 words; 2 x 64 words
+// are copied).
 struct alignas(16) Slot {
     float lt[kPiece];
     float lr[kPiece];
-    uint32_t mw[4 * kWave];
+    uint32_t mw[2 * kWave];
 };
-static_assert(sizeof(Slot) >= kWave * kFoldVals * sizeof(double), "fold scratch fits a slot");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -231,6 +228,58 @@ struct Acc {
     __device__ void zero() { sd = sd2 = sk3 = sem1 = sabs = mx = 0; nvalid = nclip = nnan = 0; }
 };
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The slot entries lane `lane` folds: lt and lr at offsets lane + 64 i and,
+// with a mask, the mask bytes at mshift + lane + 64 i (i = 0..3), read in one
+// asm block that ends with s_waitcnt lgkmcnt(0).  The ring is filled by LDS
+// DMA; written as ordinary loads, the compiler cannot tell this slot from the
+// ones still being filled and waits for every copy in flight (vmcnt(0))
+// first, which would serialise the ring.  The explicit vmcnt waits of the
+// main loop are what order these reads after the copies of their piece.
+template <bool kMask>
+__device__ __forceinline__ void read_slot(const Slot& sl, uint32_t mshift, int lane,
+                                          float (&x)[4], float (&y)[4], uint32_t (&m)[4]) {
+    const uint32_t a = lds_addr(&sl) + 4u * (uint32_t)lane;
+    uint64_t p0, p1, p2, p3;
+    if constexpr (kMask) {
+        const uint32_t am = lds_addr(sl.mw) + mshift + (uint32_t)lane;
+        asm volatile(
+            "ds_read2st64_b32 %0, %8 offset1:4\n\t"
+            "ds_read2st64_b32 %1, %8 offset0:1 offset1:5\n\t"
+            "ds_read2st64_b32 %2, %8 offset0:2 offset1:6\n\t"
+            "ds_read2st64_b32 %3, %8 offset0:3 offset1:7\n\t"
+            "ds_read_u8 %4, %9\n\t"
+            "ds_read_u8 %5, %9 offset:64\n\t"
+            "ds_read_u8 %6, %9 offset:128\n\t"
+            "ds_read_u8 %7, %9 offset:192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3), "=&v"(m[0]), "=&v"(m[1]), "=&v"(m[2]),
+              "=&v"(m[3])
+            : "v"(a), "v"(am)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read2st64_b32 %0, %4 offset1:4\n\t"
+            "ds_read2st64_b32 %1, %4 offset0:1 offset1:5\n\t"
+            "ds_read2st64_b32 %2, %4 offset0:2 offset1:6\n\t"
+            "ds_read2st64_b32 %3, %4 offset0:3 offset1:7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
+            : "v"(a)
+            : "memory");
+        m[0] = m[1] = m[2] = m[3] = 1u;
+    }
+    const uint64_t p[4] = {p0, p1, p2, p3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = __uint_as_float((uint32_t)p[i]);
+        y[i] = __uint_as_float((uint32_t)(p[i] >> 32));
+    }
+}
+
 // Fold the piece of a sub-chunk (start sub_start, length len) that begins at
 // offset off0, read from slot `sl`: lane l takes offsets off0 + l + 64 i, i
 // ascending, so across a sub-chunk's pieces each lane folds its offsets in
@@ -247,17 +296,20 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Slot& sl, uint32_t mshi
                                            uint32_t sub_start, uint32_t off0, uint32_t len,
                                            int lane, const StatsParamsDev& prm,
                                            const TokOut& tok) {
-    const unsigned char* mb = (const unsigned char*)sl.mw;
+    static_assert(kPiece == 4 * kWave, "four slot entries per lane");
+    float xs[4], ys[4];
+    uint32_t ms[4];
+    read_slot<kMask>(sl, mshift, lane, xs, ys, ms);
     const uint32_t lim = len - off0;                          // valid piece offsets < lim
 #pragma unroll
     for (int i = 0; i < kPiece / kWave; ++i) {
         if ((uint32_t)(i * kWave) >= lim) break;              // uniform: rest of piece empty
         const uint32_t po = (uint32_t)(i * kWave + lane);      // offset in the piece
-        const float x = sl.lt[po];
-        const float y = sl.lr[po];
+        const float x = xs[i];
+        const float y = ys[i];
         const double draw = (double)x - (double)y;
         const uint64_t b_in = __builtin_amdgcn_ballot_w64(po < lim);
-        const uint64_t b_m = kMask ? __builtin_amdgcn_ballot_w64(mb[mshift + po] != 0) : ~0ull;
+        const uint64_t b_m = kMask ? __builtin_amdgcn_ballot_w64(ms[i] != 0) : ~0ull;
         const uint64_t b_f = __builtin_amdgcn_ballot_w64(isfinite(draw));
         const uint64_t b_scored = b_in & b_m;
         const uint64_t b_fin = b_scored & b_f;
@@ -306,57 +358,36 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Slot& sl, uint32_t mshi
     }
 }
 
-// Cross-lane fold of a sub-chunk's six fp64 sums through LDS scratch, in a
-// fixed order: each lane stores its six values; lane j < 48 sums lanes
-// 8 (j % 8) .. 8 (j % 8) + 7 of value j / 8 in lane order; lanes 0..5 sum
-// the eight partials of their value in order.  Returns the sub-chunk's
-// partial (valid in every lane).  Counts come from ballots already.
-__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int lane, void* scratch) {
-    double* v = (double*)scratch;                 // [kFoldVals][64]
-    v[0 * kWave + lane] = A.sd;
-    v[1 * kWave + lane] = A.sd2;
-    v[2 * kWave + lane] = A.sk3;
-    v[3 * kWave + lane] = A.sem1;
-    v[4 * kWave + lane] = A.sabs;
-    v[5 * kWave + lane] = A.mx;
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    double part = 0.0;
-    const int val = lane >> 3, grp = lane & 7;
-    if (lane < kFoldVals * 8) {
-        const double* src = v + val * kWave + grp * 8;
-        part = src[0];
-        if (val == 5) {
+// Cross-lane fold of a sub-chunk's fp64 sums: a fixed xor butterfly over the
+// 64 lanes (partner distance 1, 2, 4, ..., 32).  Each step adds two values
+// whose order does not matter (a + b == b + a bit for bit), so every lane ends
+// with the same bits and the tree depends on lane positions only.  Lane
+// shuffles touch no LDS memory, so nothing here has to wait for the ring's
+// copies still in flight.
+__device__ __forceinline__ double bfly_sum(double x) {
 #pragma unroll
-            for (int i = 1; i < 8; ++i) part = fmax(part, src[i]);
-        } else {
+    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ double bfly_max(double x) {
 #pragma unroll
-            for (int i = 1; i < 8; ++i) part += src[i];
-        }
-    }
-    // the 48 partials overwrite the head of the scratch: LDS operations of a
-    // wave complete in order, so every read above has its value first
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
-    if (lane < kFoldVals * 8) v[lane] = part;
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
-    double tot = 0.0;
-    if (lane < kFoldVals) {
-        const double* src = v + lane * 8;
-        tot = src[0];
-        if (lane == 5) {
-#pragma unroll
-            for (int i = 1; i < 8; ++i) tot = fmax(tot, src[i]);
-        } else {
-#pragma unroll
-            for (int i = 1; i < 8; ++i) tot += src[i];
-        }
-    }
-    const double sd = __shfl(tot, 0), sd2 = __shfl(tot, 1), sk3 = __shfl(tot, 2);
-    const double sem1 = __shfl(tot, 3), sabs = __shfl(tot, 4), mx = __shfl(tot, 5);
+    for (int m = 1; m < kWave; m <<= 1) x = fmax(x, __shfl_xor(x, m));
+    return x;
+}
+
+// The sub-chunk's partial (valid in every lane).  Counts come from ballots
+// already and are wave-uniform.
+__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c) {
     SubPartial q;
-    q.sd = sd; q.sk2 = 0.5 * sd2; q.sk3 = sk3;
+    q.sd = bfly_sum(A.sd);
+    q.sk2 = 0.5 * bfly_sum(A.sd2);
+    q.sk3 = bfly_sum(A.sk3);
+    const double sem1 = bfly_sum(A.sem1);
     q.sw = ((double)(A.nvalid - A.nclip) + sem1) + clip_c * (double)A.nclip;
-    q.sabs = sabs;
-    q.maxabs = mx; q.nvalid = (int32_t)A.nvalid; q.nclip = (int32_t)A.nclip;
+    q.sabs = bfly_sum(A.sabs);
+    q.maxabs = bfly_max(A.mx);
+    q.nvalid = (int32_t)A.nvalid; q.nclip = (int32_t)A.nclip;
     q.nnan = (int32_t)A.nnan; q.pad = 0;
     return q;
 }
@@ -371,7 +402,7 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     __shared__ SubPartial stage[kStreamWaves][kSubPerWave];
     constexpr int kPer = 2 * (kPiece / kWave) + (kMask ? 2 : 0);   // DMA loads per piece
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     uint32_t T = __builtin_amdgcn_readfirstlane(*total);
     T = T < tmax ? T : tmax;
     const uint64_t k0 = ((uint64_t)blockIdx.x * kStreamWaves + wv) * kSubPerWave;
@@ -381,8 +412,12 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
 
     // this wave's descriptors, one per lane; read by any lane with shfl
     const SubDesc my = lane < (int)nsub ? desc[k0 + lane] : SubDesc{0u, 0u};
-    auto d_start = [&](uint32_t k) { return (uint32_t)__shfl((int)my.start, (int)k); };
-    auto d_len = [&](uint32_t k) { return (uint32_t)__shfl((int)my.len, (int)k); };
+    auto d_start = [&](uint32_t k) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane(__shfl((int)my.start, (int)k));
+    };
+    auto d_len = [&](uint32_t k) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane(__shfl((int)my.len, (int)k));
+    };
 
     uint32_t npieces = 0;
     for (uint32_t k = 0; k < nsub; ++k) npieces += (d_len(k) + kPiece - 1) / kPiece;
@@ -435,7 +470,7 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         const uint32_t mshift = kMask ? (uint32_t)((uintptr_t)(mask + fs + fp * kPiece) & 3) : 0u;
         fold_piece<kTok, kMask>(A, S, mshift, fs, fp * kPiece, fl, lane, prm, tok);
         if (++fp * kPiece >= fl) {
-            const SubPartial q = finish(A, prm.clip_c, lane, (void*)&R[c % kRing]);
+            const SubPartial q = finish(A, prm.clip_c);
             if (lane == 0) stage[wv][fk] = q;
             A.zero();
             fp = 0;
