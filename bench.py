@@ -67,7 +67,25 @@ def main():
     ap.add_argument("--stats-log2", type=int, default=28)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the stats-scale and invariance-cost measurements")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for a rocprofv3 counter pass: a 1 GiB copy kernel "
+                         "(calibrates the byte counters), then the timed steps only")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of --profile-pass runs into the traffic summary and exit")
+    ap.add_argument("--stats-scale-only", action="store_true",
+                    help="run only the stats pass at 2^stats-log2 tokens (for a kernel trace)")
+    ap.add_argument("--traffic-out", default=PMC_SUMMARY)
+    ap.add_argument("--traffic-command", default="",
+                    help="the commands that made the CSV files, recorded in the summary")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_out,
+                      args.traffic_command)
+        return
+    if args.profile_pass:
+        args.no_extras = True
+        args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the hot path shards by rows with no exchange; see the design notes)",
@@ -83,6 +101,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.profile_pass:
+        copy_calibration(torch)
+    if args.stats_scale_only:
+        print(json.dumps(stats_scale(tim, workloads, torch, np, args.stats_log2)), flush=True)
+        return
     name = "qwen3_8b"
     log(f"generating workload {name}")
     wl = workloads.make(name, device=dev)
@@ -159,6 +182,77 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, np, args.cpu_rows)
 
     print(json.dumps(out), flush=True)
+
+
+COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration kernel
+COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
+LMHEAD_KERNEL = "lmhead_partials_kernel<true>"
+STATS_KERNEL = "stats_stream_kernel"
+
+
+def copy_calibration(torch):
+    """A plain elementwise kernel over 1 GiB in and 1 GiB out, three times:
+    the counters' reading for it gives bytes-per-counted-byte."""
+    n = COPY_BYTES // 4
+    src = torch.zeros(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def _counter_means(path, counter):
+    """Mean Counter_Value (KiB) per dispatch for each kernel name of interest."""
+    import csv
+    vals = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            for key in (COPY_KERNEL, LMHEAD_KERNEL, STATS_KERNEL):
+                if key in name:
+                    # one row per dispatch (values already summed over the chip)
+                    vals.setdefault(key, []).append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def write_traffic(fetch_csv, write_csv, out_path, command):
+    """Per-dispatch bytes of the LM-head kernel (bench run) or of the stats
+    kernel (stats-only run), each counter scaled by its reading for the copy
+    kernel of known size."""
+    fr = _counter_means(fetch_csv, "FETCH_SIZE")
+    wr = _counter_means(write_csv, "WRITE_SIZE")
+    if COPY_KERNEL not in fr or COPY_KERNEL not in wr:
+        raise SystemExit("no copy-calibration dispatches in the counter files")
+    rf = fr[COPY_KERNEL][0] * 1024 / COPY_BYTES      # counted bytes per true byte read
+    wf = wr[COPY_KERNEL][0] * 1024 / COPY_BYTES
+    summary = {
+        "copy_calibration": {"kernel": "torch.bitwise_not over 2^28 int32 "
+                                       "(1 GiB read, 1 GiB written)",
+                             "fetch_factor": rf, "write_factor": wf,
+                             "dispatches": fr[COPY_KERNEL][1]},
+        "command": command,
+    }
+    for key, tag in ((LMHEAD_KERNEL, "lmhead"), (STATS_KERNEL, "stats_stream")):
+        if key in fr and key in wr:
+            summary[tag] = {"kernel": key, "fetch_kib_raw": fr[key][0],
+                            "write_kib_raw": wr[key][0],
+                            "fetch_bytes": fr[key][0] * 1024 / rf,
+                            "write_bytes": wr[key][0] * 1024 / wf,
+                            "dispatches": fr[key][1]}
+    if "lmhead" in summary:
+        summary["kernel"] = LMHEAD_KERNEL
+        summary["kernel_source_sha256_16"] = source_digest(LMHEAD_SRC)
+        summary["launch_unit"] = "qwen3_8b:N=8192"
+        summary["hbm_bytes_per_launch"] = summary["lmhead"]["fetch_bytes"] + \
+            summary["lmhead"]["write_bytes"]
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    print(json.dumps(summary, indent=1))
 
 
 def time_calls(fn, torch, np, reps=10, warm=2):
