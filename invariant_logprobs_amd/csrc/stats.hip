@@ -22,13 +22,13 @@
 //   1. plan_count / plan_scan / plan_write: integer prefix sum of the
 //      sub-chunk counts; writes one (start, length) descriptor per
 //      sub-chunk, in token order, and each sequence's first descriptor.
-//   2. stats_stream: each wave takes kSubPerWave consecutive descriptors and
-//      streams their tokens through a kRing-slot LDS ring in kPiece-token
-//      pieces.  Pieces are copied global -> LDS with global_load_lds_dword
-//      (no registers held by loads in flight), kRing - 1 pieces ahead of the
-//      fold, with exact vmcnt waits.  Sub-chunk partials are staged in LDS
-//      and written once when the wave is done, so no store is ever counted
-//      among the ring's loads.
+//   2. stats_stream: each wave takes a few (at most 16) consecutive
+//      descriptors and streams their tokens in kPiece-token pieces: lane l
+//      holds piece offsets l + 64 i (i = 0..3) of lt, lr and the mask in
+//      registers, with kBufs pieces in flight, and folds one piece while the
+//      next ones load.  A sub-chunk's lanes are folded across the wave with a
+//      fixed LDS transpose + DPP tree.  Sub-chunk partials are staged in LDS
+//      and written once when the wave is done.
 //   3. seq_finalize: one thread per sequence folds its sub-chunks in
 //      ascending order, writes means and flags; each block folds its
 //      sequences into a block partial with a fixed tree.
@@ -62,11 +62,11 @@ struct SubDesc {
 constexpr int kWave = 64;
 constexpr int kFinBlock = 256;
 constexpr int kScanBlock = 1024;
-constexpr int kPiece = 256;                 // tokens per ring slot
-constexpr int kRing = 4;                    // ring slots per wave
-constexpr int kSubPerWave = 16;             // descriptors per wave
+constexpr int kPiece = 256;                 // tokens per piece (4 per lane)
+constexpr int kMaxSubPerWave = 16;          // descriptors per wave, at most
 constexpr int kStreamWaves = 4;             // waves per block
-
+constexpr uint32_t kBufs = 3;               // pieces in flight per wave (registers)
+constexpr int kFoldVals = 6;                // fp64 sums folded across lanes
 
 __device__ __forceinline__ int64_t clamp_cu(const int32_t* cu, int64_t j, int64_t n) {
     // cu_seqlens is a documented precondition; clamping keeps a malformed one
@@ -151,42 +151,6 @@ struct TokOut {
     uint8_t* clipped;
 };
 
-// One ring slot: a piece of lt and lr, and the 4-byte words holding its
-// mask bytes (a piece's bytes span at most kPiece/4 + 1 words; 2 x 64 words
-// are copied).
-struct alignas(16) Slot {
-    float lt[kPiece];
-    float lr[kPiece];
-    uint32_t mw[2 * kWave];
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma_dword(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt low
-// bits [3:0] and high bits [15:14]; expcnt [6:4] = 7 and lgkmcnt [11:8] = 15
-// mean "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Wait until at most `ahead` pieces (kPer loads each) remain in flight.
-template <int kPer>
-__device__ __forceinline__ void wait_pieces_ahead(uint32_t ahead) {
-    static_assert(kRing == 4, "cases cover up to three pieces ahead");
-    switch (ahead) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<kPer>(); break;
-        case 2: wait_vmcnt<2 * kPer>(); break;
-        default: wait_vmcnt<3 * kPer>(); break;
-    }
-}
-
 // e^d - 1 for finite |d| > 1/32 (the rare branch; |d| <= 1/32 uses a Taylor
 // polynomial for e^d - 1 - d).  Range reduction d = k ln2 + r with
 // |r| <= ln2 / 2 (ln2 split in a high part exact in 32 bits and a low part),
@@ -194,7 +158,7 @@ __device__ __forceinline__ void wait_pieces_ahead(uint32_t ahead) {
 // then e^d - 1 = 2^k (e^r - 1) + (2^k - 1); both terms are exact-sign sums, so
 // no cancellation beyond one rounding.  d > 709.78 overflows to +inf and
 // d < -745 gives -1, as the exact value rounds.
-__device__ __forceinline__ double expm1_large(double d) {
+__device__ __attribute__((noinline)) double expm1_large(double d) {
     if (d > 709.782712893384) return INFINITY;
     if (d < -745.0) return -1.0;
     const double kLn2Hi = 6.93147180369123816490e-01;   // 0x3FE62E42FEE00000
@@ -223,126 +187,120 @@ __device__ __forceinline__ double expm1_large(double d) {
 }
 
 struct Acc {
-    double sd, sd2, sk3, sem1, sabs, mx;   // sem1: sum of e^d - 1 over unclipped tokens
+    // sclip: sum of e^d - 1 over clipped tokens; the unclipped sum the
+    // truncated weight needs is (sd + sk3) - sclip
+    double sd, sd2, sk3, sclip, sabs, mx;
     uint32_t nvalid, nclip, nnan;
-    __device__ void zero() { sd = sd2 = sk3 = sem1 = sabs = mx = 0; nvalid = nclip = nnan = 0; }
+    __device__ void zero() { sd = sd2 = sk3 = sclip = sabs = mx = 0; nvalid = nclip = nnan = 0; }
 };
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
+// A piece held in registers: the lane's tokens at piece offsets lane + 64 i.
+struct Regs {
+    float x[4], y[4];
+    uint32_t m[4];
+};
 
-// The slot entries lane `lane` folds: lt and lr at offsets lane + 64 i and,
-// with a mask, the mask bytes at mshift + lane + 64 i (i = 0..3), read in one
-// asm block that ends with s_waitcnt lgkmcnt(0).  The ring is filled by LDS
-// DMA; written as ordinary loads, the compiler cannot tell this slot from the
-// ones still being filled and waits for every copy in flight (vmcnt(0))
-// first, which would serialise the ring.  The explicit vmcnt waits of the
-// main loop are what order these reads after the copies of their piece.
 template <bool kMask>
-__device__ __forceinline__ void read_slot(const Slot& sl, uint32_t mshift, int lane,
-                                          float (&x)[4], float (&y)[4], uint32_t (&m)[4]) {
-    const uint32_t a = lds_addr(&sl) + 4u * (uint32_t)lane;
-    uint64_t p0, p1, p2, p3;
-    if constexpr (kMask) {
-        const uint32_t am = lds_addr(sl.mw) + mshift + (uint32_t)lane;
-        asm volatile(
-            "ds_read2st64_b32 %0, %8 offset1:4\n\t"
-            "ds_read2st64_b32 %1, %8 offset0:1 offset1:5\n\t"
-            "ds_read2st64_b32 %2, %8 offset0:2 offset1:6\n\t"
-            "ds_read2st64_b32 %3, %8 offset0:3 offset1:7\n\t"
-            "ds_read_u8 %4, %9\n\t"
-            "ds_read_u8 %5, %9 offset:64\n\t"
-            "ds_read_u8 %6, %9 offset:128\n\t"
-            "ds_read_u8 %7, %9 offset:192\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3), "=&v"(m[0]), "=&v"(m[1]), "=&v"(m[2]),
-              "=&v"(m[3])
-            : "v"(a), "v"(am)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read2st64_b32 %0, %4 offset1:4\n\t"
-            "ds_read2st64_b32 %1, %4 offset0:1 offset1:5\n\t"
-            "ds_read2st64_b32 %2, %4 offset0:2 offset1:6\n\t"
-            "ds_read2st64_b32 %3, %4 offset0:3 offset1:7\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
-            : "v"(a)
-            : "memory");
-        m[0] = m[1] = m[2] = m[3] = 1u;
-    }
-    const uint64_t p[4] = {p0, p1, p2, p3};
+__device__ __forceinline__ void load_piece(Regs& r, const float* __restrict__ lt,
+                                           const float* __restrict__ lr,
+                                           const uint8_t* __restrict__ mask, uint32_t st,
+                                           uint32_t cnt, int lane) {
+    // uniform bases (scalar registers) and 32-bit lane offsets: one address
+    // computation per entry, shared by the three streams
+    const float* blt = lt + st;
+    const float* blr = lr + st;
+    const uint8_t* bm = kMask ? mask + st : mask;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        x[i] = __uint_as_float((uint32_t)p[i]);
-        y[i] = __uint_as_float((uint32_t)(p[i] >> 32));
+        uint32_t o = (uint32_t)(i * kWave + lane);
+        o = o < cnt ? o : cnt - 1;                 // clamped: a valid copy, ignored later
+        const uint32_t ob = o << 2;                // byte offset, 32-bit
+        r.x[i] = *(const float*)((const char*)blt + ob);
+        r.y[i] = *(const float*)((const char*)blr + ob);
+        r.m[i] = kMask ? (uint32_t)bm[o] : 1u;
     }
+}
+
+// Wave mask of the lanes whose x is finite (v_cmp_class with the six finite
+// classes: -normal, -denormal, -0, +0, +denormal, +normal), straight into
+// scalar registers.  Every lane of the wave is active where this is used.
+__device__ __forceinline__ uint64_t finite_mask(double x) {
+    uint64_t m;
+    asm("v_cmp_class_f64_e64 %0, %1, %2" : "=s"(m) : "v"(x), "s"(0x1F8));
+    return m;
+}
+
+// max(m, |d|) as one v_max_f64 (both operands are finite, so no
+// canonicalisation is needed)
+__device__ __forceinline__ double max_abs(double m, double d) {
+    double r;
+    asm("v_max_f64 %0, %1, |%2|" : "=v"(r) : "v"(m), "v"(d));
+    return r;
+}
+
+// fma(a, b, c) as one v_fma_f64 with c in scalar registers (the compiler
+// otherwise copies loop-invariant constants before a two-address fmac)
+__device__ __forceinline__ double fma_s(double a, double b, double c) {
+    double r;
+    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
 }
 
 // Fold the piece of a sub-chunk (start sub_start, length len) that begins at
-// offset off0, read from slot `sl`: lane l takes offsets off0 + l + 64 i, i
-// ascending, so across a sub-chunk's pieces each lane folds its offsets in
-// ascending order.  Straight-line code: every slot entry is a valid copy, so
-// the LDS reads are unconditional; a token that does not count (outside the
-// sub-chunk, masked out or non-finite) gets delta = 0, which makes its d,
-// d^2, k3 and |d| contributions exactly 0 with no further selects.  Counts
-// come from ballots of single compares combined on the scalar unit.  k2 is
-// accumulated as d^2 and halved once (a power-of-two scale: exact).  The
-// truncated weight sum is assembled as n_unclipped + sum(e^d - 1 over
-// unclipped) + C n_clipped, with e^d - 1 = d + k3.
+// offset off0: lane l takes offsets off0 + l + 64 i, i ascending, so across a
+// sub-chunk's pieces each lane folds its offsets in ascending order.  A token
+// that does not count (outside the sub-chunk, masked out or non-finite) gets
+// d = 0, which makes its d, d^2, k3 and |d| contributions exactly 0 with no
+// further selects.  Counts are popcounts of the wave masks.  k2 is
+// accumulated as d^2 and halved once (a power-of-two scale: exact).  For the
+// truncated weight only the clipped tokens' e^d - 1 is summed (rare path);
+// the unclipped sum is recovered as (sum d + sum k3) - that.
 template <bool kTok, bool kMask>
-__device__ __forceinline__ void fold_piece(Acc& A, const Slot& sl, uint32_t mshift,
+__device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg,
                                            uint32_t sub_start, uint32_t off0, uint32_t len,
                                            int lane, const StatsParamsDev& prm,
                                            const TokOut& tok) {
-    static_assert(kPiece == 4 * kWave, "four slot entries per lane");
-    float xs[4], ys[4];
-    uint32_t ms[4];
-    read_slot<kMask>(sl, mshift, lane, xs, ys, ms);
+    static_assert(kPiece == 4 * kWave, "four piece entries per lane");
     const uint32_t lim = len - off0;                          // valid piece offsets < lim
 #pragma unroll
     for (int i = 0; i < kPiece / kWave; ++i) {
         if ((uint32_t)(i * kWave) >= lim) break;              // uniform: rest of piece empty
         const uint32_t po = (uint32_t)(i * kWave + lane);      // offset in the piece
-        const float x = xs[i];
-        const float y = ys[i];
-        const double draw = (double)x - (double)y;
-        const uint64_t b_in = __builtin_amdgcn_ballot_w64(po < lim);
-        const uint64_t b_m = kMask ? __builtin_amdgcn_ballot_w64(ms[i] != 0) : ~0ull;
-        const uint64_t b_f = __builtin_amdgcn_ballot_w64(isfinite(draw));
-        const uint64_t b_scored = b_in & b_m;
-        const uint64_t b_fin = b_scored & b_f;
-        const uint64_t bit = 1ull << lane;
-        const bool fin = (b_fin & bit) != 0;
-        const double d = fin ? draw : 0.0;
-        // e^d - 1 - d without cancellation for |d| <= 1/32 (degree-6 Taylor,
-        // truncation below 2e-11 relative)
-        const double d2 = d * d;
-        double p = 1.0 / 720.0;
-        p = fma(p, d, 1.0 / 120.0);
-        p = fma(p, d, 1.0 / 24.0);
-        p = fma(p, d, 1.0 / 6.0);
-        p = fma(p, d, 0.5);
-        double k3 = d2 * p;
-        if (!(fabs(d) <= 0.03125)) k3 = expm1_large(d) - d;            // rare
-        const double em1 = d + k3;
-        const uint64_t b_clip = __builtin_amdgcn_ballot_w64(draw > prm.log_c) & b_fin;
-        const bool clipped = (b_clip & bit) != 0;
+        const double draw = (double)rg.x[i] - (double)rg.y[i];
+        // lane predicates as wave masks: each ballot is one compare, the
+        // combinations are scalar, and inverse_ballot reads a lane's bit back
+        const uint64_t m_scored = __builtin_amdgcn_ballot_w64(po < lim) &
+                                  (kMask ? __builtin_amdgcn_ballot_w64(rg.m[i] != 0) : ~0ull);
+        const uint64_t m_fin = m_scored & finite_mask(draw);
+        const uint64_t m_clip = m_fin & __builtin_amdgcn_ballot_w64(draw > prm.log_c);
+        A.nvalid += (uint32_t)__popcll(m_fin);
+        A.nnan += (uint32_t)__popcll(m_scored & ~m_fin);
+        A.nclip += (uint32_t)__popcll(m_clip);
+        const double d = __builtin_amdgcn_inverse_ballot_w64(m_fin) ? draw : 0.0;
+        // e^d - 1 - d for |d| <= 1/32: d^2 (1/2 + d/6 + d^2/24 + d^3/120),
+        // truncation below 4e-9 relative
+        double p = fma_s(d, 1.0 / 120.0, 1.0 / 24.0);
+        p = fma_s(p, d, 1.0 / 6.0);
+        p = fma_s(p, d, 0.5);
+        double k3 = d * (d * p);
+        const uint64_t m_big = __builtin_amdgcn_ballot_w64(!(fabs(d) <= 0.03125));
+        if ((m_big | m_clip) != 0) {                                    // rare, uniform test
+            if (__builtin_amdgcn_inverse_ballot_w64(m_big)) k3 = expm1_large(d) - d;
+            if (__builtin_amdgcn_inverse_ballot_w64(m_clip)) A.sclip += d + k3;
+        }
         A.sd += d;
-        A.sd2 += d2;
+        A.sd2 = fma(d, d, A.sd2);
         A.sk3 += k3;
-        A.sem1 += clipped ? 0.0 : em1;
         A.sabs += fabs(d);
-        A.mx = fmax(A.mx, fabs(d));
-        A.nvalid += (uint32_t)__popcll(b_fin);
-        A.nclip += (uint32_t)__popcll(b_clip);
-        A.nnan += (uint32_t)__popcll(b_scored & ~b_f);
+        A.mx = max_abs(A.mx, d);
         if (kTok && po < lim) {
             // per-token outputs; a non-finite delta reports exp/expm1 as computed
-            const bool scored = (b_scored & bit) != 0;
+            const bool scored = __builtin_amdgcn_inverse_ballot_w64(m_scored);
+            const bool fin = __builtin_amdgcn_inverse_ballot_w64(m_fin);
+            const bool clipped = __builtin_amdgcn_inverse_ballot_w64(m_clip);
             const uint32_t t = sub_start + off0 + po;
             const double dd = scored ? draw : 0.0;
+            const double em1 = d + k3;
             const double r = 1.0 + em1;
             const double wgt = clipped ? prm.clip_c : (fin ? r : 0.0);
             const double rr = fin ? r : (scored ? exp(dd) : 1.0);
@@ -358,38 +316,96 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Slot& sl, uint32_t mshi
     }
 }
 
-// Cross-lane fold of a sub-chunk's fp64 sums: a fixed xor butterfly over the
-// 64 lanes (partner distance 1, 2, 4, ..., 32).  Each step adds two values
-// whose order does not matter (a + b == b + a bit for bit), so every lane ends
-// with the same bits and the tree depends on lane positions only.  Lane
-// shuffles touch no LDS memory, so nothing here has to wait for the ring's
-// copies still in flight.
-__device__ __forceinline__ double bfly_sum(double x) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
-    return x;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ __forceinline__ double bfly_max(double x) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x = fmax(x, __shfl_xor(x, m));
-    return x;
+// 64-bit value of the lane selected by a DPP control (both 32-bit halves
+// moved with v_mov_b32_dpp).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, 0xf,
+                                                              0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// The sub-chunk's partial (valid in every lane).  Counts come from ballots
-// already and are wave-uniform.
-__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c) {
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Cross-lane fold of a sub-chunk's six fp64 sums, in a fixed order that
+// depends on lane positions only:
+//   1. every lane stores its six values to the wave's scratch: v[value][lane];
+//   2. lane j < 48 sums v[j / 8][8 (j % 8) .. 8 (j % 8) + 7] left to right
+//      (the maximum for value 5);
+//   3. the eight partials of a value (lanes 8 v .. 8 v + 7) are combined by
+//      three DPP steps: neighbours (quad_perm 1,0,3,2), pairs (quad_perm
+//      2,3,0,1), half-rows (row_half_mirror);
+//   4. lane 8 v holds value v and is read into scalar registers.
+// A wave's LDS operations complete in issue order, so the reads see the
+// writes without a wait between them; the read block ends in lgkmcnt(0).
+__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int lane, const double* scratch) {
+    const uint32_t base = lds_addr(scratch);
+    const uint32_t aw = base + 8u * (uint32_t)lane;               // v[0][lane]
+    asm volatile(
+        "ds_write2st64_b64 %0, %1, %2 offset1:1\n\t"
+        "ds_write2st64_b64 %0, %3, %4 offset0:2 offset1:3\n\t"
+        "ds_write2st64_b64 %0, %5, %6 offset0:4 offset1:5"
+        :
+        : "v"(aw), "v"(A.sd), "v"(A.sd2), "v"(A.sk3), "v"(A.sclip), "v"(A.sabs), "v"(A.mx)
+        : "memory");
+    // lanes 48..63 repeat lanes 32..47 (in range; their results are unused)
+    const int j = lane < kFoldVals * 8 ? lane : lane - 16;
+    const uint32_t ar = base + 8u * (uint32_t)((j >> 3) * kWave + (j & 7) * 8);
+    typedef __attribute__((__vector_size__(2 * sizeof(double)))) double f64x2;
+    f64x2 r0, r1, r2, r3;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:16\n\t"
+        "ds_read_b128 %2, %4 offset:32\n\t"
+        "ds_read_b128 %3, %4 offset:48\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(ar)
+        : "memory");
+    const double e[8] = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+    const bool is_max = (j >> 3) == 5;
+    double t = e[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) t = is_max ? fmax(t, e[i]) : t + e[i];
+    double o = dpp_f64<0xB1>(t);                                    // quad_perm 1,0,3,2
+    t = is_max ? fmax(t, o) : t + o;
+    o = dpp_f64<0x4E>(t);                                           // quad_perm 2,3,0,1
+    t = is_max ? fmax(t, o) : t + o;
+    o = dpp_f64<0x141>(t);                                          // row_half_mirror
+    t = is_max ? fmax(t, o) : t + o;
     SubPartial q;
-    q.sd = bfly_sum(A.sd);
-    q.sk2 = 0.5 * bfly_sum(A.sd2);
-    q.sk3 = bfly_sum(A.sk3);
-    const double sem1 = bfly_sum(A.sem1);
+    q.sd = readlane_f64(t, 0);
+    q.sk2 = 0.5 * readlane_f64(t, 8);
+    q.sk3 = readlane_f64(t, 16);
+    const double sem1 = (q.sd + q.sk3) - readlane_f64(t, 24);     // unclipped e^d - 1
     q.sw = ((double)(A.nvalid - A.nclip) + sem1) + clip_c * (double)A.nclip;
-    q.sabs = bfly_sum(A.sabs);
-    q.maxabs = bfly_max(A.mx);
+    q.sabs = readlane_f64(t, 32);
+    q.maxabs = readlane_f64(t, 40);
     q.nvalid = (int32_t)A.nvalid; q.nclip = (int32_t)A.nclip;
     q.nnan = (int32_t)A.nnan; q.pad = 0;
     return q;
+}
+
+// Descriptors per wave: enough waves to cover the chip several times over at
+// any size (a wave's descriptors are folded one after another), at most
+// kMaxSubPerWave.  Which wave folds a sub-chunk never changes its result.
+inline uint32_t subs_per_wave(int64_t tmax) {
+    constexpr int64_t kTargetWaves = 16384;
+    int64_t k = (tmax + kTargetWaves - 1) / kTargetWaves;
+    if (k < 1) k = 1;
+    if (k > 4) k = 4;
+    return (uint32_t)k;
 }
 
 template <bool kTok, bool kMask>
@@ -397,89 +413,74 @@ __global__ void __launch_bounds__(kWave * kStreamWaves)
 stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                     const uint8_t* __restrict__ mask, const SubDesc* __restrict__ desc,
                     const uint32_t* __restrict__ total, uint32_t tmax, StatsParamsDev prm,
-                    TokOut tok, SubPartial* __restrict__ partial) {
-    __shared__ Slot ring[kStreamWaves][kRing];
-    __shared__ SubPartial stage[kStreamWaves][kSubPerWave];
-    constexpr int kPer = 2 * (kPiece / kWave) + (kMask ? 2 : 0);   // DMA loads per piece
+                    TokOut tok, SubPartial* __restrict__ partial, uint32_t spw) {
+    __shared__ __attribute__((aligned(16))) double scratch[kStreamWaves][kFoldVals * kWave];
+    __shared__ SubPartial stage[kStreamWaves][kMaxSubPerWave];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     uint32_t T = __builtin_amdgcn_readfirstlane(*total);
     T = T < tmax ? T : tmax;
-    const uint64_t k0 = ((uint64_t)blockIdx.x * kStreamWaves + wv) * kSubPerWave;
+    const uint64_t k0 = ((uint64_t)blockIdx.x * kStreamWaves + wv) * spw;
     if (k0 >= T) return;
-    const uint32_t nsub = (uint32_t)(T - k0 < kSubPerWave ? T - k0 : kSubPerWave);
-    Slot* R = ring[wv];
+    const uint32_t nsub = (uint32_t)(T - k0 < spw ? T - k0 : spw);
 
-    // this wave's descriptors, one per lane; read by any lane with shfl
+    // this wave's descriptors, one per lane, read into scalar registers
     const SubDesc my = lane < (int)nsub ? desc[k0 + lane] : SubDesc{0u, 0u};
-    auto d_start = [&](uint32_t k) {
-        return (uint32_t)__builtin_amdgcn_readfirstlane(__shfl((int)my.start, (int)k));
-    };
-    auto d_len = [&](uint32_t k) {
-        return (uint32_t)__builtin_amdgcn_readfirstlane(__shfl((int)my.len, (int)k));
-    };
+    auto d_start = [&](uint32_t k) { return (uint32_t)__builtin_amdgcn_readlane((int)my.start, (int)k); };
+    auto d_len = [&](uint32_t k) { return (uint32_t)__builtin_amdgcn_readlane((int)my.len, (int)k); };
 
     uint32_t npieces = 0;
     for (uint32_t k = 0; k < nsub; ++k) npieces += (d_len(k) + kPiece - 1) / kPiece;
 
     // issue iterator: (sub-chunk ik, piece ip)
     uint32_t ik = 0, ip = 0, is0 = d_start(0), il = d_len(0);
-    auto issue = [&](uint32_t slot) {
-        Slot& S = R[slot];
-        const uint32_t st = is0 + ip * kPiece;
-        const uint32_t en = st + kPiece < is0 + il ? st + kPiece : is0 + il;
-        const uint32_t cnt = en - st;
-        const float* blt = lt + st;              // uniform bases, small per-lane offsets
-        const float* blr = lr + st;
-#pragma unroll
-        for (int j = 0; j < kPiece / kWave; ++j) {
-            uint32_t o = (uint32_t)(j * kWave + lane);
-            o = o < cnt ? o : cnt - 1;
-            dma_dword(blt + o, S.lt + j * kWave);
-            dma_dword(blr + o, S.lr + j * kWave);
-        }
-        if (kMask) {
-            const uintptr_t m0 = (uintptr_t)(mask + st) & ~(uintptr_t)3;
-            const uintptr_t m1 = ((uintptr_t)(mask + en) + 3) & ~(uintptr_t)3;
-            const uint32_t nw = (uint32_t)((m1 - m0) >> 2);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                uint32_t wd = (uint32_t)(j * kWave + lane);
-                wd = wd < nw ? wd : nw - 1;
-                dma_dword((const void*)(m0 + 4 * (uintptr_t)wd), S.mw + j * kWave);
+    // Every call issues the same loads, on every path: past the last piece it
+    // reloads the first piece of the wave (never folded again).  The
+    // compiler's load counting then sees a fixed number of loads between a
+    // buffer's refill and its use, and waits for exactly that piece.
+    const uint32_t s_first = d_start(0);
+    const uint32_t c_first = d_len(0) < (uint32_t)kPiece ? d_len(0) : (uint32_t)kPiece;
+    auto issue = [&](Regs& r) {
+        if (ik < nsub) {
+            const uint32_t st = is0 + ip * kPiece;
+            const uint32_t en = st + kPiece < is0 + il ? st + kPiece : is0 + il;
+            load_piece<kMask>(r, lt, lr, mask, st, en - st, lane);
+            if (++ip * kPiece >= il) {
+                ip = 0;
+                if (++ik < nsub) { is0 = d_start(ik); il = d_len(ik); }
             }
-        }
-        if (++ip * kPiece >= il) {
-            ip = 0;
-            if (++ik < nsub) { is0 = d_start(ik); il = d_len(ik); }
+        } else {
+            load_piece<kMask>(r, lt, lr, mask, s_first, c_first, lane);
         }
     };
-
-    uint32_t issued = 0;
-    for (; issued < kRing - 1 && issued < npieces; ++issued) issue(issued);
 
     Acc A;
     A.zero();
     uint32_t fk = 0, fp = 0, fs = d_start(0), fl = d_len(0);
-    for (uint32_t c = 0; c < npieces; ++c) {
-        // the slot refilled here held piece c - 1, folded in the last iteration
-        if (issued < npieces) { issue(issued % kRing); ++issued; }
-        if (kTok) wait_vmcnt<0>();          // token stores share the counter
-        else wait_pieces_ahead<kPer>(issued - c - 1);
-        const Slot& S = R[c % kRing];
-        const uint32_t mshift = kMask ? (uint32_t)((uintptr_t)(mask + fs + fp * kPiece) & 3) : 0u;
-        fold_piece<kTok, kMask>(A, S, mshift, fs, fp * kPiece, fl, lane, prm, tok);
-        if (++fp * kPiece >= fl) {
-            const SubPartial q = finish(A, prm.clip_c);
-            if (lane == 0) stage[wv][fk] = q;
-            A.zero();
-            fp = 0;
-            if (++fk < nsub) { fs = d_start(fk); fl = d_len(fk); }
+    // fold piece c from r (if it exists), then refill r with piece c + kBufs
+    auto step = [&](Regs& r, uint32_t c) {
+        if (c < npieces) {
+            fold_piece<kTok, kMask>(A, r, fs, fp * kPiece, fl, lane, prm, tok);
+            if (++fp * kPiece >= fl) {
+                const SubPartial q = finish(A, prm.clip_c, lane, scratch[wv]);
+                if (lane == 0) stage[wv][fk] = q;
+                A.zero();
+                fp = 0;
+                if (++fk < nsub) { fs = d_start(fk); fl = d_len(fk); }
+            }
         }
+        issue(r);
+    };
+    Regs b0, b1, b2;
+    issue(b0);
+    issue(b1);
+    issue(b2);
+    for (uint32_t c = 0; c < npieces; c += kBufs) {
+        step(b0, c);
+        step(b1, c + 1);
+        step(b2, c + 2);
     }
-    // every ring load has completed (the last fold waited for vmcnt(0));
-    // lane l writes 16 bytes of staged partial l / 4
-    __builtin_amdgcn_s_waitcnt(0);
+    // stage[wv] is this wave's own: lane 0's LDS writes precede these reads in order
     const int e = lane >> 2, q4 = lane & 3;
     if (e < (int)nsub) ((uint4*)&partial[k0 + e])[q4] = ((const uint4*)&stage[wv][e])[q4];
 }
@@ -651,23 +652,24 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
         hipLaunchKernelGGL(plan_write_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
                            cu, p.n, p.s, p.tmax, boff, seq_off, desc);
         if (p.n > 0) {
-            const int64_t waves = (p.tmax + kSubPerWave - 1) / kSubPerWave;
+            const uint32_t spw = subs_per_wave(p.tmax);
+            const int64_t waves = (p.tmax + spw - 1) / spw;
             const dim3 grid((unsigned)((waves + kStreamWaves - 1) / kStreamWaves));
             const dim3 bdim(kWave * kStreamWaves);
             const bool want_tok = to.delta || to.ratio || to.k1 || to.k2 || to.k3 || to.tis_w ||
                                   to.clipped;
             if (want_tok && mask)
                 hipLaunchKernelGGL((stats_stream_kernel<true, true>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
             else if (want_tok)
                 hipLaunchKernelGGL((stats_stream_kernel<true, false>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
             else if (mask)
                 hipLaunchKernelGGL((stats_stream_kernel<false, true>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
             else
                 hipLaunchKernelGGL((stats_stream_kernel<false, false>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
         }
         hipLaunchKernelGGL(seq_finalize_kernel, dim3((unsigned)p.nblk_seq), dim3(kFinBlock), 0, st,
                            cu, p.n, p.s, p.tmax, prm, seq_off, partial, so, blk);
