@@ -10,7 +10,7 @@
 // Batch invariance ("训推一致性与 determinism", section 1.2: a request's
 // result must not depend on which other requests share its batch): every
 // reduction order here is a function of (V, D, dtype) alone.
-//   * K order: ascending D in 64-byte stages, one MFMA accumulator chain per
+//   * K order: ascending D in 128-byte stages, one MFMA accumulator chain per
 //     logit, no split-K.  A logit's bits do not depend on which MFMA column
 //     (token slot) it occupies: every column runs the same instruction
 //     sequence on its own data.
@@ -41,55 +41,76 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// LDS: a ring of kRing pipeline stages, each holding a 256-row W tile and a
-// 256-row h tile of kStageBytes per row (32 bf16 or 16 fp32 of K).  Stages
-// are filled by global_load_lds_dwordx4 (64 lanes x 16 bytes = 16 rows per
-// instruction) kRing - 1 stages ahead of the MFMAs.  The four 16-byte chunks
-// of a row are XOR-swizzled with (row >> 2) & 3: the 16 lanes of one
-// ds_read_b128 phase read 16 consecutive rows at one logical chunk, and
-// with 64-byte rows those land on 16 distinct 16-byte bank groups of the
-// 64-bank LDS.
-constexpr int kRing = 4;
-constexpr int kOperandBytes = kTileV * kStageBytes;   // 16 KiB
-constexpr int kStageLds = 2 * kOperandBytes;          // 32 KiB
+// LDS: two pipeline slots, each holding a 256-row W tile and a 256-row h
+// tile of kStageBytes (128) per row: 64 bf16 or 32 fp32 of K, four MFMA
+// k-steps.  A slot is filled by buffer_load_dwordx4 ... lds (64 lanes x 16
+// bytes = 8 rows of 128 bytes per instruction), one stage ahead of the
+// MFMAs.  The eight 16-byte chunks of a row are XOR-swizzled with
+// (row >> 1) & 7: the 16 lanes of one ds_read_b128 phase read 16
+// consecutive rows at one logical chunk, and with 128-byte rows those land
+// on 16 distinct 16-byte bank groups of the 64-bank LDS.
+constexpr int kRing = 2;
+constexpr int kOperandBytes = kTileV * kStageBytes;   // 32 KiB
+constexpr int kStageLds = 2 * kOperandBytes;          // 64 KiB
 constexpr int kLdsBytes = kRing * kStageLds;          // 128 KiB
-constexpr int kDmaPerStage = 8;                       // per wave: 4 W + 4 h blocks
+constexpr int kDmaPerStage = 16;                      // per wave: 8 W + 8 h blocks
 static_assert(kTileV == kTileT, "one staging loop serves both operands");
-static_assert(kStageBytes == 64, "swizzle and fragment mapping assume 64-byte rows");
+static_assert(kStageBytes == 128, "swizzle and fragment mapping assume 128-byte rows");
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kStageBytes + ((chunk ^ ((row >> 2) & 3)) << 4);
+    return row * kStageBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+// 16 bytes per lane from a raw buffer (base and size in the descriptor) at
+// voffset + soffset, written to LDS at l + 16 * lane.  The row offsets are
+// per lane and fixed; the K offset of a stage is the scalar soffset.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, voff, soff, 0, 0);
 }
+constexpr int kRsrcWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data format,
+                                         // no swizzle, no thread-id add
 
-// Eight 16-byte LDS reads followed by s_waitcnt lgkmcnt(0), in one asm block.
-// The ring is filled by LDS DMA; written as ordinary loads, the compiler
-// cannot tell the slot being read from the slots still being filled and
-// waits for every copy in flight (vmcnt(0)) before each read, which would
-// serialise the pipeline.  The explicit vmcnt waits in the main loop are what
-// order these reads after the copies of their own stage.  Every read of the
-// block has completed when it returns, so no LDS operation issued here is
-// left outstanding for the compiler's own lgkmcnt bookkeeping.
-__device__ __forceinline__ void lds_read_8x16(u32x4 (&r)[8], const uint32_t (&a)[8]) {
+// Eight 16-byte LDS reads issued in one asm block, not waited for.  The ring
+// is filled by LDS DMA; written as ordinary loads, the compiler cannot tell
+// the slot being read from the slots still being filled and waits for every
+// copy in flight (vmcnt(0)) before each read, which would serialise the
+// pipeline.  The explicit vmcnt waits and barriers of the main loop order
+// these reads after the copies of their stage; frags_ready() below waits for
+// the reads themselves.  Outputs are early-clobber: a read's destination must
+// not overlap a later read's address.
+__device__ __forceinline__ void lds_issue_8x16(u32x4 (&r)[8], uint32_t aA, uint32_t aB) {
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
+        "ds_read_b128 %1, %8 offset:4096\n\t"
+        "ds_read_b128 %2, %8 offset:8192\n\t"
+        "ds_read_b128 %3, %8 offset:12288\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:4096\n\t"
+        "ds_read_b128 %6, %9 offset:8192\n\t"
+        "ds_read_b128 %7, %9 offset:12288"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
           "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "v"(aA), "v"(aB)
         : "memory");
+}
+
+// Wait until at most N LDS operations are outstanding; the fragments are
+// passed through so that no use of them can be scheduled before the wait.
+// LDS operations of a wave complete in order, so with the 8 reads of the
+// other fragment set issued later, lgkmcnt(8) means this set has arrived.
+template <int N>
+__device__ __forceinline__ void frags_ready(u32x4 (&f)[8]) {
+    static_assert(N == 0 || N == 8, "lgkmcnt values used here");
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                       "+v"(f[6]), "+v"(f[7]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(8)"
+                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                       "+v"(f[6]), "+v"(f[7]));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -154,7 +175,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wv = wave & 1;        // vocabulary half of the tile (128 rows)
     const int wt = wave >> 1;       // token half of the tile (128 tokens)
     const int lrow = lane & 31;
@@ -184,18 +205,19 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) { m_run[bj] = -INFINITY; s_run[bj] = 0.f; }
 
-    // DMA assignment: wave `wave` fills 16-row blocks 4 wave .. 4 wave + 3 of
-    // both operands; lane i writes physical chunk i % 4 of row 16 blk + i / 4,
-    // i.e. logical chunk (i % 4) ^ ((row >> 2) & 3).  Addresses are a uniform
-    // 64-bit base plus a 32-bit per-lane byte offset (a tile spans well under
-    // 4 GiB of rows).  Rows past N or V are redirected to the last valid row;
-    // their results are discarded or masked.
-    uint32_t hoff[4], wrow_off[4], wtail_off[4];
-    int drow[4];
+    // Copy assignment: wave `wave` fills 8-row blocks 8 wave .. 8 wave + 7 of
+    // both operands; lane i writes physical chunk i % 8 of row 8 blk + i / 8,
+    // i.e. logical chunk (i % 8) ^ ((row >> 1) & 7).  Addresses are a buffer
+    // descriptor per operand tile (base, byte extent), a fixed 32-bit per-lane
+    // row offset and the stage's K offset.  Rows past N or V are redirected to
+    // the last valid row; their results are discarded or masked.  Every
+    // access then lies inside the tensors, and inside the descriptor's extent.
+    uint32_t hoff[8], wrow_off[8], wtail_off[8];
+    int drow[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        drow[j] = (wave * 4 + j) * 16 + (lane >> 2);
-        const uint32_t cb = (uint32_t)(((lane & 3) ^ ((drow[j] >> 2) & 3)) * 16);
+    for (int j = 0; j < 8; ++j) {
+        drow[j] = (wave * 8 + j) * 8 + (lane >> 3);
+        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((drow[j] >> 1) & 7)) * 16);
         int64_t t = t0 + drow[j];
         if (t > n - 1) t = n - 1;
         hoff[j] = (uint32_t)((t - t0) * ldh_b) + cb;
@@ -203,50 +225,109 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         wtail_off[j] = cb;             // + (v - 1 - vbase) * ldw_b, set per tile
     }
     const unsigned char* hbase = h + t0 * ldh_b;
-    uint32_t woff[4];
+    const int64_t hrows = (n - t0) < kTileT ? (n - t0) : kTileT;
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)hbase, (short)0, (int)((hrows - 1) * ldh_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+    uint32_t woff[8];
     const unsigned char* wbase = w;
+    __amdgpu_buffer_rsrc_t wrs = hrs;
     auto set_wtile = [&](int vt_l) {
         const int64_t vbase = (vt_first + vt_l) * kTileV;
         wbase = w + vbase * ldw_b;
+        const int64_t wrows = (v - vbase) < kTileV ? (v - vbase) : kTileV;
+        wrs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0,
+                                                (int)((wrows - 1) * ldw_b + (int64_t)nk * kStageBytes), kRsrcWord3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
             woff[j] = vbase + drow[j] < v ? wrow_off[j]
                                           : (uint32_t)((v - 1 - vbase) * ldw_b) + wtail_off[j];
     };
 
-    // per-lane LDS byte offsets of the 8 fragments of each of the 2 k-steps
+    // per-lane LDS byte offset of k-step ks inside an operand tile: row lrow
+    // of each 32-row block (the swizzle does not depend on the block), logical
+    // chunk ks*2 + lhalf (bf16) or lhalf*4 + ks (fp32)
     const uint32_t lds_base = lds_addr(lds);
-    uint32_t frag_off[2][8];
+    uint32_t kofs[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int c = kBf16 ? ks * 2 + lhalf : lhalf * 2 + ks;
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi) frag_off[ks][bi] = (uint32_t)swz(wv * 128 + bi * 32 + lrow, c);
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-            frag_off[ks][4 + bj] = (uint32_t)(kOperandBytes + swz(wt * 128 + bj * 32 + lrow, c));
+    for (int ks = 0; ks < 4; ++ks) {
+        const int c = kBf16 ? ks * 2 + lhalf : lhalf * 4 + ks;
+        kofs[ks] = (uint32_t)swz(lrow, c);
     }
 
-    const int nsteps = ntiles_here * nk;
     int iss = 0, iss_vt = 0, iss_kb = 0;
     set_wtile(0);
+    // Issue the copies of stage `iss` into slot iss % kRing.  Every call
+    // issues the same sixteen copies: past the last stage the iterator has
+    // wrapped to K offset 0 of the last tile, so the extra copies re-read
+    // valid rows into a slot that is never read again.  The vmcnt waits are
+    // then the same at every stage.
     auto issue_next = [&]() {
         unsigned char* base = lds + (iss & (kRing - 1)) * kStageLds;
         const int64_t koff = (int64_t)iss_kb * kStageBytes;
-        const unsigned char* wb = wbase + koff;
-        const unsigned char* hb = hbase + koff;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            dma16(wb + woff[j], base + (wave * 4 + j) * 1024);
-            dma16(hb + hoff[j], base + kOperandBytes + (wave * 4 + j) * 1024);
+        for (int j = 0; j < 8; ++j) {
+            dma16_buf(wrs, base + (wave * 8 + j) * 1024, woff[j], (uint32_t)koff);
+            dma16_buf(hrs, base + kOperandBytes + (wave * 8 + j) * 1024, hoff[j], (uint32_t)koff);
         }
+    };
+    auto advance = [&]() {
         ++iss;
         if (++iss_kb == nk) {
             iss_kb = 0;
             if (++iss_vt < ntiles_here) set_wtile(iss_vt);
         }
     };
-    for (int i = 0; i < kRing - 1 && iss < nsteps; ++i) issue_next();
+    // fragment k-step ks of stage `stage`: A rows wv*128 + bi*32 + lrow, B
+    // rows wt*128 + bj*32 + lrow (block bi / bj is an immediate 4 KiB step)
+    auto issue_frags = [&](u32x4 (&f)[8], int stage, int ks) {
+        const uint32_t sbase = lds_base + (uint32_t)((stage & (kRing - 1)) * kStageLds) + kofs[ks];
+        lds_issue_8x16(f, sbase + (uint32_t)(wv * 128 * kStageBytes),
+                       sbase + (uint32_t)(kOperandBytes + wt * 128 * kStageBytes));
+    };
+    auto mfma_step = [&](const u32x4 (&f)[8]) {
+        if constexpr (kBf16) {
+            // lanes 0-31 supply K 0-7 of the 16-K step, lanes 32-63 K 8-15
+#pragma unroll
+            for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, f[bi]), __builtin_bit_cast(bf16x8, f[4 + bj]),
+                        acc[bi][bj], 0, 0, 0);
+        } else {
+            // 32 fp32 of K per stage: lane half g supplies K = 16 g + 4 ks + e
+            // to MFMA (ks, e); each 32x32x2 instruction consumes one K of each
+            // half.  Whole vectors are cast before indexing: casting single
+            // elements of the asm outputs made this compiler pass element 0
+            // for every e.
+            f32x4 ff[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ff[i] = __builtin_bit_cast(f32x4, f[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            ff[bi][e], ff[4 + bj][e], acc[bi][bj], 0, 0, 0);
+        }
+    };
+
+    // Pipeline: the copies of stage st + 1 are in flight while stage st
+    // computes; fragment reads run one k-step ahead of the MFMAs (fa, fb
+    // alternate).  After the third k-step's MFMAs of stage st every wave waits
+    // for its own copies of stage st + 1 and for its last reads of stage st;
+    // past the barrier stage st + 1 is complete in LDS and slot st % 2 is free:
+    // k-step 0 of stage st + 1 is read and stage st + 2's copies are issued
+    // into slot st % 2, one after each MFMA of the fourth k-step.
+    // sched_barrier(0) keeps the compiler from moving MFMAs across the waits
+    // and the reads that feed the next k-step.
+    for (int i = 0; i < kRing; ++i) { issue_next(); advance(); }
+    wait_vmcnt<(kRing - 1) * kDmaPerStage>();        // stage 0 (own copies)
+    __syncthreads();                                   // ... everyone's
+    u32x4 fa[8], fb[8];
+    issue_frags(fa, 0, 0);
 
     int st = 0;
     for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
@@ -258,55 +339,32 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                 for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
         for (int kb = 0; kb < nk; ++kb, ++st) {
-            // this wave's copies for stage st have landed ...
-            const int ahead = iss - st - 1;
-            if (ahead >= 2) wait_vmcnt<2 * kDmaPerStage>();
-            else if (ahead == 1) wait_vmcnt<kDmaPerStage>();
-            else wait_vmcnt<0>();
-            // ... and everyone's have; everyone is also done reading stage
-            // st - 1, whose slot the next issue refills
+            issue_frags(fb, st, 1);
+            frags_ready<8>(fa);
+            mfma_step(fa);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_frags(fa, st, 2);
+            frags_ready<8>(fb);
+            mfma_step(fb);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_frags(fb, st, 3);
+            frags_ready<8>(fa);
+            mfma_step(fa);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(kRing - 2) * kDmaPerStage>();
+            frags_ready<0>(fb);
             __syncthreads();
-            if (iss < nsteps) issue_next();
-
-            const uint32_t sbase = lds_base + (uint32_t)((st & (kRing - 1)) * kStageLds);
-            // fragment k-step ks: A rows wv*128 + bi*32 + lrow, B rows
-            // wt*128 + bj*32 + lrow, logical chunk ks*2 + lhalf (bf16) or
-            // lhalf*2 + ks (fp32)
+            issue_frags(fa, st + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_next();
+            mfma_step(fb);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                uint32_t ad[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ad[i] = sbase + frag_off[ks][i];
-                u32x4 f[8];
-                lds_read_8x16(f, ad);
-                if constexpr (kBf16) {
-                    // lanes 0-31 supply K 0-7 of the 16-K step, lanes 32-63 K 8-15
-#pragma unroll
-                    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-                        for (int bj = 0; bj < 4; ++bj)
-                            acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, f[bi]), __builtin_bit_cast(bf16x8, f[4 + bj]),
-                                acc[bi][bj], 0, 0, 0);
-                } else {
-                    // 16 fp32 of K per stage: lane half g supplies K = 8 g + 4 ks + e
-                    // to MFMA (ks, e); each 32x32x2 instruction consumes one K of
-                    // each half.  Whole vectors are cast before indexing: casting
-                    // single elements of the asm outputs made this compiler
-                    // pass element 0 for every e.
-                    f32x4 ff[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) ff[i] = __builtin_bit_cast(f32x4, f[i]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-#pragma unroll
-                        for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-                            for (int bj = 0; bj < 4; ++bj)
-                                acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                    ff[bi][e], ff[4 + bj][e], acc[bi][bj], 0, 0, 0);
-                }
+            for (int i = 0; i < kDmaPerStage; ++i) {       // MFMA, copy, MFMA, copy, ...
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
         }
 
         // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
@@ -379,6 +437,9 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
             have_zsel |= any_tgt;
         }
     }
+    // drain: the last stage's look-ahead read and the extra copies
+    frags_ready<0>(fa);
+    wait_vmcnt<0>();
 
     // ---- the selected logits this lane owns (one owner per token)
     if (have_zsel) {

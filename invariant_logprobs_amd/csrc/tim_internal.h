@@ -20,7 +20,7 @@ namespace tim {
 // (max, sum-exp) per token in registers.
 constexpr int kTileV = 256;
 constexpr int kTileT = 256;
-constexpr int kStageBytes = 64;    // bytes of K per row per pipeline stage
+constexpr int kStageBytes = 128;   // bytes of K per row per pipeline stage
 constexpr int kThreads = 256;      // 4 waves of 64
 constexpr int kInvariantChunkTiles = 2;   // 512 vocabulary entries per chunk
 
