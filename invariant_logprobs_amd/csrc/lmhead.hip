@@ -41,18 +41,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// LDS: two pipeline slots, each holding a 256-row W tile and a 256-row h
-// tile of kStageBytes (128) per row: 64 bf16 or 32 fp32 of K, four MFMA
-// k-steps.  A slot is filled by buffer_load_dwordx4 ... lds (64 lanes x 16
-// bytes = 8 rows of 128 bytes per instruction), one stage ahead of the
-// MFMAs.  The eight 16-byte chunks of a row are XOR-swizzled with
-// (row >> 1) & 7: the 16 lanes of one ds_read_b128 phase read 16
-// consecutive rows at one logical chunk, and with 128-byte rows those land
-// on 16 distinct 16-byte bank groups of the 64-bank LDS.
-constexpr int kRing = 2;
+// LDS: a ring of five positions, each holding one operand tile of a
+// pipeline stage: 256 rows (W or h) of kStageBytes (128) per row, i.e. 64
+// bf16 or 32 fp32 of K, four MFMA k-steps.  Tiles are filled by
+// buffer_load_dwordx4 ... lds (64 lanes x 16 bytes = 8 rows of 128 bytes per
+// instruction) one (W) or two (h) stages ahead of the MFMAs.  The eight
+// 16-byte chunks of a row are XOR-swizzled with (row >> 1) & 7: the 16 lanes
+// of one ds_read_b128 phase read 16 consecutive rows at one logical chunk,
+// and with 128-byte rows those land on 16 distinct 16-byte bank groups of
+// the 64-bank LDS.
+constexpr int kPos = 5;                               // ring positions, one operand tile each
 constexpr int kOperandBytes = kTileV * kStageBytes;   // 32 KiB
-constexpr int kStageLds = 2 * kOperandBytes;          // 64 KiB
-constexpr int kLdsBytes = kRing * kStageLds;          // 128 KiB
+constexpr int kLdsBytes = kPos * kOperandBytes;       // 160 KiB
 constexpr int kDmaPerStage = 16;                      // per wave: 8 W + 8 h blocks
 static_assert(kTileV == kTileT, "one staging loop serves both operands");
 static_assert(kStageBytes == 128, "swizzle and fragment mapping assume 128-byte rows");
@@ -254,35 +254,46 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         kofs[ks] = (uint32_t)swz(lrow, c);
     }
 
-    int iss = 0, iss_vt = 0, iss_kb = 0;
+    // Copy iterators: W of stage st + 1 and h of stage st + 2 are copied
+    // while stage st computes.  Past the last stage both wrap to K offset 0
+    // (of the last W tile): the extra copies read valid rows into positions
+    // that are never read again, and every stage issues the same copies.
+    int w_kb = 0, w_vt = 0, h_kb = 0;
     set_wtile(0);
-    // Issue the copies of stage `iss` into slot iss % kRing.  Every call
-    // issues the same sixteen copies: past the last stage the iterator has
-    // wrapped to K offset 0 of the last tile, so the extra copies re-read
-    // valid rows into a slot that is never read again.  The vmcnt waits are
-    // then the same at every stage.
-    auto issue_next = [&]() {
-        unsigned char* base = lds + (iss & (kRing - 1)) * kStageLds;
-        const int64_t koff = (int64_t)iss_kb * kStageBytes;
+    auto copy_w = [&](int part, int pos) {
+        unsigned char* base = lds + pos * kOperandBytes;
+        const uint32_t koff = (uint32_t)(w_kb * kStageBytes);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            dma16_buf(wrs, base + (wave * 8 + j) * 1024, woff[j], (uint32_t)koff);
-            dma16_buf(hrs, base + kOperandBytes + (wave * 8 + j) * 1024, hoff[j], (uint32_t)koff);
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = part * 4 + jj;
+            dma16_buf(wrs, base + (wave * 8 + j) * 1024, woff[j], koff);
         }
     };
-    auto advance = [&]() {
-        ++iss;
-        if (++iss_kb == nk) {
-            iss_kb = 0;
-            if (++iss_vt < ntiles_here) set_wtile(iss_vt);
+    auto copy_h = [&](int part, int pos) {
+        unsigned char* base = lds + pos * kOperandBytes;
+        const uint32_t koff = (uint32_t)(h_kb * kStageBytes);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = part * 4 + jj;
+            dma16_buf(hrs, base + (wave * 8 + j) * 1024, hoff[j], koff);
         }
     };
-    // fragment k-step ks of stage `stage`: A rows wv*128 + bi*32 + lrow, B
-    // rows wt*128 + bj*32 + lrow (block bi / bj is an immediate 4 KiB step)
-    auto issue_frags = [&](u32x4 (&f)[8], int stage, int ks) {
-        const uint32_t sbase = lds_base + (uint32_t)((stage & (kRing - 1)) * kStageLds) + kofs[ks];
-        lds_issue_8x16(f, sbase + (uint32_t)(wv * 128 * kStageBytes),
-                       sbase + (uint32_t)(kOperandBytes + wt * 128 * kStageBytes));
+    auto advance_w = [&]() {
+        if (++w_kb == nk) {
+            w_kb = 0;
+            if (++w_vt < ntiles_here) set_wtile(w_vt);
+        }
+    };
+    auto advance_h = [&]() {
+        if (++h_kb == nk) h_kb = 0;
+    };
+    auto next_pos = [](int p) { return p + 2 >= kPos ? p + 2 - kPos : p + 2; };
+    // fragment k-step ks: A rows wv*128 + bi*32 + lrow from the W tile at
+    // ring position pw, B rows wt*128 + bj*32 + lrow from the h tile at ph
+    // (block bi / bj is an immediate 4 KiB step)
+    auto issue_frags = [&](u32x4 (&f)[8], int pw, int ph, int ks) {
+        lds_issue_8x16(f, lds_base + (uint32_t)(pw * kOperandBytes) + kofs[ks] + (uint32_t)(wv * 128 * kStageBytes),
+                       lds_base + (uint32_t)(ph * kOperandBytes) + kofs[ks] + (uint32_t)(wt * 128 * kStageBytes));
     };
     auto mfma_step = [&](const u32x4 (&f)[8]) {
         if constexpr (kBf16) {
@@ -314,20 +325,26 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         }
     };
 
-    // Pipeline: the copies of stage st + 1 are in flight while stage st
-    // computes; fragment reads run one k-step ahead of the MFMAs (fa, fb
-    // alternate).  After the third k-step's MFMAs of stage st every wave waits
-    // for its own copies of stage st + 1 and for its last reads of stage st;
-    // past the barrier stage st + 1 is complete in LDS and slot st % 2 is free:
-    // k-step 0 of stage st + 1 is read and stage st + 2's copies are issued
-    // into slot st % 2, one after each MFMA of the fourth k-step.
-    // sched_barrier(0) keeps the compiler from moving MFMAs across the waits
-    // and the reads that feed the next k-step.
-    for (int i = 0; i < kRing; ++i) { issue_next(); advance(); }
-    wait_vmcnt<(kRing - 1) * kDmaPerStage>();        // stage 0 (own copies)
+    // Pipeline.  The ring holds operand tiles at positions (2 stage + op) % 5
+    // (op 0: h, op 1: W).  While stage st computes, its two tiles and the h
+    // tile of stage st + 1 are resident or landing, and the two free
+    // positions (those of stage st - 1) take the W tile of stage st + 1
+    // (copied during k-steps 0 and 1) and the h tile of stage st + 2 (k-steps
+    // 2 and 3): four copies per k-step, one after every four MFMAs.  Fragment
+    // reads run one k-step ahead of the MFMAs (fa, fb alternate).  Before the
+    // barrier that ends stage st every wave waits for its copies of stage
+    // st + 1 and for its last reads of stage st.  sched_barrier(0) keeps the
+    // compiler from moving MFMAs across those waits and the reads that feed
+    // the next k-step.
+    int rd_h = 0, rd_w = 1;                            // positions of stage st
+    int cp_w = 3, cp_h = 4;                            // W of st + 1, h of st + 2
+    copy_h(0, 0); copy_h(1, 0); advance_h();           // h, stage 0
+    copy_w(0, 1); copy_w(1, 1); advance_w();           // W, stage 0
+    copy_h(0, 2); copy_h(1, 2); advance_h();           // h, stage 1
+    wait_vmcnt<kDmaPerStage / 2>();                    // stage 0 (own copies)
     __syncthreads();                                   // ... everyone's
     u32x4 fa[8], fb[8];
-    issue_frags(fa, 0, 0);
+    issue_frags(fa, rd_w, rd_h, 0);
 
     int st = 0;
     for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
@@ -339,32 +356,67 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                 for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
         for (int kb = 0; kb < nk; ++kb, ++st) {
-            issue_frags(fb, st, 1);
+            issue_frags(fb, rd_w, rd_h, 1);
             frags_ready<8>(fa);
+            copy_w(0, cp_w);
             mfma_step(fa);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
-            issue_frags(fa, st, 2);
+            issue_frags(fa, rd_w, rd_h, 2);
             frags_ready<8>(fb);
+            copy_w(1, cp_w);
             mfma_step(fb);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
-            issue_frags(fb, st, 3);
+            advance_w();
+            issue_frags(fb, rd_w, rd_h, 3);
             frags_ready<8>(fa);
+            copy_h(0, cp_h);
             mfma_step(fa);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<(kRing - 2) * kDmaPerStage>();
+            wait_vmcnt<kDmaPerStage / 4>();            // all but h of st + 2, part 0
             frags_ready<0>(fb);
-            __syncthreads();
-            issue_frags(fa, st + 1, 0);
+            asm volatile("s_barrier" ::: "memory");
+            rd_h = next_pos(rd_h);
+            rd_w = next_pos(rd_w);
+            issue_frags(fa, rd_w, rd_h, 0);
             __builtin_amdgcn_sched_barrier(0);
-            issue_next();
+            copy_h(1, cp_h);
             mfma_step(fb);
-#pragma unroll
-            for (int i = 0; i < kDmaPerStage; ++i) {       // MFMA, copy, MFMA, copy, ...
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
-            advance();
+            advance_h();
+            cp_w = next_pos(cp_w);
+            cp_h = next_pos(cp_h);
         }
 
         // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
@@ -437,9 +489,11 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
             have_zsel |= any_tgt;
         }
     }
-    // drain: the last stage's look-ahead read and the extra copies
+    // drain: the last stage's look-ahead read and the extra copies; the ring
+    // is reused for the wave exchange below
     frags_ready<0>(fa);
     wait_vmcnt<0>();
+    __syncthreads();
 
     // ---- the selected logits this lane owns (one owner per token)
     if (have_zsel) {
@@ -464,7 +518,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         const float so = __shfl_xor(s_run[bj], 32);
         lse_combine(m_run[bj], s_run[bj], mo, so);
     }
-    __shared__ float2 xch[2 * 128];  // [token half][token]
+    float2* xch = (float2*)lds;      // [token half][token]; the ring is drained
     if (wv == 1 && lhalf == 0) {
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj)
