@@ -66,7 +66,8 @@ constexpr int kPiece = 256;                 // tokens per piece (4 per lane)
 constexpr int kMaxSubPerWave = 16;          // descriptors per wave, at most
 constexpr int kStreamWaves = 4;             // waves per block
 constexpr uint32_t kBufs = 3;               // pieces in flight per wave (registers)
-constexpr int kFoldVals = 6;                // fp64 sums folded across lanes
+constexpr int kFoldVals = 4;                // fp64 sums folded across lanes per sub-chunk
+constexpr int kWavesPerFinBlock = 4 * 256;  // streaming-wave partials per finalize block
 
 __device__ __forceinline__ int64_t clamp_cu(const int32_t* cu, int64_t j, int64_t n) {
     // cu_seqlens is a documented precondition; clamping keeps a malformed one
@@ -187,11 +188,14 @@ __device__ __attribute__((noinline)) double expm1_large(double d) {
 }
 
 struct Acc {
-    // sclip: sum of e^d - 1 over clipped tokens; the unclipped sum the
-    // truncated weight needs is (sd + sk3) - sclip
-    double sd, sd2, sk3, sclip, sabs, mx;
+    // Per sub-chunk.  sclip: sum of e^d - 1 over clipped tokens; the
+    // unclipped sum the truncated weight needs is (sd + sk3) - sclip.
+    double sd, sd2, sk3, sclip;
     uint32_t nvalid, nclip, nnan;
-    __device__ void zero() { sd = sd2 = sk3 = sclip = sabs = mx = 0; nvalid = nclip = nnan = 0; }
+    // Per wave, over all its sub-chunks: sum and maximum of |d|, which only
+    // the batch aggregates use (no per-sequence output depends on them).
+    double sabs, mx;
+    __device__ void zero() { sd = sd2 = sk3 = sclip = 0; nvalid = nclip = nnan = 0; }
 };
 
 // A piece held in registers: the lane's tokens at piece offsets lane + 64 i.
@@ -210,14 +214,24 @@ __device__ __forceinline__ void load_piece(Regs& r, const float* __restrict__ lt
     const float* blt = lt + st;
     const float* blr = lr + st;
     const uint8_t* bm = kMask ? mask + st : mask;
+    if (cnt == (uint32_t)kPiece) {                 // full piece: fixed lane offsets
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t o = (uint32_t)(i * kWave + lane);
-        o = o < cnt ? o : cnt - 1;                 // clamped: a valid copy, ignored later
-        const uint32_t ob = o << 2;                // byte offset, 32-bit
-        r.x[i] = *(const float*)((const char*)blt + ob);
-        r.y[i] = *(const float*)((const char*)blr + ob);
-        r.m[i] = kMask ? (uint32_t)bm[o] : 1u;
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = (uint32_t)(i * kWave + lane);
+            r.x[i] = *(const float*)((const char*)blt + (o << 2));
+            r.y[i] = *(const float*)((const char*)blr + (o << 2));
+            r.m[i] = kMask ? (uint32_t)bm[o] : 1u;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t o = (uint32_t)(i * kWave + lane);
+            o = o < cnt ? o : cnt - 1;             // clamped: a valid copy, ignored later
+            const uint32_t ob = o << 2;            // byte offset, 32-bit
+            r.x[i] = *(const float*)((const char*)blt + ob);
+            r.y[i] = *(const float*)((const char*)blr + ob);
+            r.m[i] = kMask ? (uint32_t)bm[o] : 1u;
+        }
     }
 }
 
@@ -269,8 +283,9 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg,
         const double draw = (double)rg.x[i] - (double)rg.y[i];
         // lane predicates as wave masks: each ballot is one compare, the
         // combinations are scalar, and inverse_ballot reads a lane's bit back
-        const uint64_t m_scored = __builtin_amdgcn_ballot_w64(po < lim) &
-                                  (kMask ? __builtin_amdgcn_ballot_w64(rg.m[i] != 0) : ~0ull);
+        uint64_t m_in = ~0ull;                                    // full row: all lanes in
+        if ((uint32_t)((i + 1) * kWave) > lim) m_in = __builtin_amdgcn_ballot_w64(po < lim);
+        const uint64_t m_scored = m_in & (kMask ? __builtin_amdgcn_ballot_w64(rg.m[i] != 0) : ~0ull);
         const uint64_t m_fin = m_scored & finite_mask(draw);
         const uint64_t m_clip = m_fin & __builtin_amdgcn_ballot_w64(draw > prm.log_c);
         A.nvalid += (uint32_t)__popcll(m_fin);
@@ -338,11 +353,10 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Cross-lane fold of a sub-chunk's six fp64 sums, in a fixed order that
+// Cross-lane fold of a sub-chunk's four fp64 sums, in a fixed order that
 // depends on lane positions only:
-//   1. every lane stores its six values to the wave's scratch: v[value][lane];
-//   2. lane j < 48 sums v[j / 8][8 (j % 8) .. 8 (j % 8) + 7] left to right
-//      (the maximum for value 5);
+//   1. every lane stores its four values to the wave's scratch: v[value][lane];
+//   2. lane j < 32 sums v[j / 8][8 (j % 8) .. 8 (j % 8) + 7] left to right;
 //   3. the eight partials of a value (lanes 8 v .. 8 v + 7) are combined by
 //      three DPP steps: neighbours (quad_perm 1,0,3,2), pairs (quad_perm
 //      2,3,0,1), half-rows (row_half_mirror);
@@ -354,13 +368,12 @@ __device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int la
     const uint32_t aw = base + 8u * (uint32_t)lane;               // v[0][lane]
     asm volatile(
         "ds_write2st64_b64 %0, %1, %2 offset1:1\n\t"
-        "ds_write2st64_b64 %0, %3, %4 offset0:2 offset1:3\n\t"
-        "ds_write2st64_b64 %0, %5, %6 offset0:4 offset1:5"
+        "ds_write2st64_b64 %0, %3, %4 offset0:2 offset1:3"
         :
-        : "v"(aw), "v"(A.sd), "v"(A.sd2), "v"(A.sk3), "v"(A.sclip), "v"(A.sabs), "v"(A.mx)
+        : "v"(aw), "v"(A.sd), "v"(A.sd2), "v"(A.sk3), "v"(A.sclip)
         : "memory");
-    // lanes 48..63 repeat lanes 32..47 (in range; their results are unused)
-    const int j = lane < kFoldVals * 8 ? lane : lane - 16;
+    // lanes 32..63 repeat lanes 0..31 (in range; their results are unused)
+    const int j = lane & 31;
     const uint32_t ar = base + 8u * (uint32_t)((j >> 3) * kWave + (j & 7) * 8);
     typedef __attribute__((__vector_size__(2 * sizeof(double)))) double f64x2;
     f64x2 r0, r1, r2, r3;
@@ -373,28 +386,42 @@ __device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int la
         : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
         : "v"(ar)
         : "memory");
-    const double e[8] = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-    const bool is_max = (j >> 3) == 5;
-    double t = e[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) t = is_max ? fmax(t, e[i]) : t + e[i];
-    double o = dpp_f64<0xB1>(t);                                    // quad_perm 1,0,3,2
-    t = is_max ? fmax(t, o) : t + o;
-    o = dpp_f64<0x4E>(t);                                           // quad_perm 2,3,0,1
-    t = is_max ? fmax(t, o) : t + o;
-    o = dpp_f64<0x141>(t);                                          // row_half_mirror
-    t = is_max ? fmax(t, o) : t + o;
+    double t = r0[0];
+    t += r0[1];
+    t += r1[0];
+    t += r1[1];
+    t += r2[0];
+    t += r2[1];
+    t += r3[0];
+    t += r3[1];
+    t += dpp_f64<0xB1>(t);                                         // quad_perm 1,0,3,2
+    t += dpp_f64<0x4E>(t);                                         // quad_perm 2,3,0,1
+    t += dpp_f64<0x141>(t);                                        // row_half_mirror
     SubPartial q;
     q.sd = readlane_f64(t, 0);
     q.sk2 = 0.5 * readlane_f64(t, 8);
     q.sk3 = readlane_f64(t, 16);
     const double sem1 = (q.sd + q.sk3) - readlane_f64(t, 24);     // unclipped e^d - 1
     q.sw = ((double)(A.nvalid - A.nclip) + sem1) + clip_c * (double)A.nclip;
-    q.sabs = readlane_f64(t, 32);
-    q.maxabs = readlane_f64(t, 40);
+    q.sabs = 0.0;                                                  // per wave instead
+    q.maxabs = 0.0;
     q.nvalid = (int32_t)A.nvalid; q.nclip = (int32_t)A.nclip;
     q.nnan = (int32_t)A.nnan; q.pad = 0;
     return q;
+}
+
+// Fixed xor butterfly over the 64 lanes (partner distance 1, 2, ..., 32);
+// a + b == b + a bit for bit, so every lane ends with the same bits.
+__device__ __forceinline__ double bfly_sum(double x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ double bfly_max(double x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x = fmax(x, __shfl_xor(x, m));
+    return x;
 }
 
 // Descriptors per wave: enough waves to cover the chip several times over at
@@ -413,15 +440,20 @@ __global__ void __launch_bounds__(kWave * kStreamWaves)
 stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                     const uint8_t* __restrict__ mask, const SubDesc* __restrict__ desc,
                     const uint32_t* __restrict__ total, uint32_t tmax, StatsParamsDev prm,
-                    TokOut tok, SubPartial* __restrict__ partial, uint32_t spw) {
+                    TokOut tok, SubPartial* __restrict__ partial, uint32_t spw,
+                    double2* __restrict__ wpart) {
     __shared__ __attribute__((aligned(16))) double scratch[kStreamWaves][kFoldVals * kWave];
     __shared__ SubPartial stage[kStreamWaves][kMaxSubPerWave];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     uint32_t T = __builtin_amdgcn_readfirstlane(*total);
     T = T < tmax ? T : tmax;
-    const uint64_t k0 = ((uint64_t)blockIdx.x * kStreamWaves + wv) * spw;
-    if (k0 >= T) return;
+    const uint64_t wid = (uint64_t)blockIdx.x * kStreamWaves + wv;
+    const uint64_t k0 = wid * spw;
+    if (k0 >= T) {                                 // no sub-chunk for this wave
+        if (lane == 0) wpart[wid] = make_double2(0.0, 0.0);
+        return;
+    }
     const uint32_t nsub = (uint32_t)(T - k0 < spw ? T - k0 : spw);
 
     // this wave's descriptors, one per lane, read into scalar registers
@@ -456,6 +488,8 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
 
     Acc A;
     A.zero();
+    A.sabs = 0.0;
+    A.mx = 0.0;
     uint32_t fk = 0, fp = 0, fs = d_start(0), fl = d_len(0);
     // fold piece c from r (if it exists), then refill r with piece c + kBufs
     auto step = [&](Regs& r, uint32_t c) {
@@ -483,6 +517,8 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     // stage[wv] is this wave's own: lane 0's LDS writes precede these reads in order
     const int e = lane >> 2, q4 = lane & 3;
     if (e < (int)nsub) ((uint4*)&partial[k0 + e])[q4] = ((const uint4*)&stage[wv][e])[q4];
+    const double wsabs = bfly_sum(A.sabs), wmx = bfly_max(A.mx);
+    if (lane == 0) wpart[wid] = make_double2(wsabs, wmx);
 }
 
 __device__ __forceinline__ void acc_add(BatchAcc& x, const BatchAcc& y) {
@@ -519,6 +555,7 @@ __global__ void __launch_bounds__(kFinBlock)
 seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_t tmax,
                     StatsParamsDev prm,
                     const uint32_t* __restrict__ seq_off, const SubPartial* __restrict__ partial,
+                    const double2* __restrict__ wpart, int64_t nw,
                     SeqOut so, BatchAcc* __restrict__ blk) {
     __shared__ BatchAcc buf[kFinBlock];
     const int64_t j = (int64_t)blockIdx.x * kFinBlock + threadIdx.x;
@@ -558,6 +595,16 @@ seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_
             c.md = md; c.mk1 = mk1; c.mk2 = mk2; c.mk3 = mk3;
             c.nonempty = 1;
             c.rejected = rej ? 1 : 0;
+        }
+    }
+    // this block's slice of the streaming waves' sum and maximum of |delta|
+#pragma unroll
+    for (int r = 0; r < kWavesPerFinBlock / kFinBlock; ++r) {
+        const int64_t i = (int64_t)blockIdx.x * kWavesPerFinBlock + r * kFinBlock + threadIdx.x;
+        if (i < nw) {
+            const double2 q = wpart[i];
+            c.sabs += q.x;
+            c.maxabs = fmax(c.maxabs, q.y);
         }
     }
     buf[threadIdx.x] = c;
@@ -611,6 +658,12 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     p->tmax = (n + kSubChunk - 1) / kSubChunk + s;
     p->nblk_scan = (s + kScanBlock - 1) / kScanBlock;
     p->nblk_seq = (s + kFinBlock - 1) / kFinBlock;
+    p->spw = subs_per_wave(p->tmax);
+    p->nwaves = ((p->tmax + p->spw - 1) / p->spw + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
+    {
+        const int64_t nbw = (p->nwaves + kWavesPerFinBlock - 1) / kWavesPerFinBlock;
+        p->nblk_fin = p->nblk_seq > nbw ? p->nblk_seq : nbw;
+    }
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -623,7 +676,8 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     p->seqoff_off = take((size_t)s * 4);
     p->desc_off = take((size_t)p->tmax * sizeof(SubDesc));
     p->part_off = take((size_t)p->tmax * sizeof(SubPartial));
-    p->blk_off = take((size_t)(p->nblk_seq > 0 ? p->nblk_seq : 1) * sizeof(BatchAcc));
+    p->blk_off = take((size_t)(p->nblk_fin > 0 ? p->nblk_fin : 1) * sizeof(BatchAcc));
+    p->wpart_off = take((size_t)p->nwaves * sizeof(double2));
     p->total_bytes = off;
     return true;
 }
@@ -641,6 +695,8 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
     SubDesc* desc = (SubDesc*)(ws + p.desc_off);
     SubPartial* partial = (SubPartial*)(ws + p.part_off);
     BatchAcc* blk = (BatchAcc*)(ws + p.blk_off);
+    double2* wpart = (double2*)(ws + p.wpart_off);
+    const bool streamed = p.s > 0 && p.n > 0;
     TokOut to{tok.delta, tok.ratio, tok.k1, tok.k2, tok.k3, tok.tis_w, tok.clipped};
     SeqOut so{seq.n_valid, seq.n_clipped, seq.n_nan, seq.mean_delta, seq.mean_k1,
               seq.mean_k2, seq.mean_k3, seq.mean_tis_w, seq.reject};
@@ -652,31 +708,31 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
         hipLaunchKernelGGL(plan_write_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
                            cu, p.n, p.s, p.tmax, boff, seq_off, desc);
         if (p.n > 0) {
-            const uint32_t spw = subs_per_wave(p.tmax);
-            const int64_t waves = (p.tmax + spw - 1) / spw;
-            const dim3 grid((unsigned)((waves + kStreamWaves - 1) / kStreamWaves));
+            const uint32_t spw = p.spw;
+            const dim3 grid((unsigned)(p.nwaves / kStreamWaves));
             const dim3 bdim(kWave * kStreamWaves);
             const bool want_tok = to.delta || to.ratio || to.k1 || to.k2 || to.k3 || to.tis_w ||
                                   to.clipped;
             if (want_tok && mask)
                 hipLaunchKernelGGL((stats_stream_kernel<true, true>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
             else if (want_tok)
                 hipLaunchKernelGGL((stats_stream_kernel<true, false>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
             else if (mask)
                 hipLaunchKernelGGL((stats_stream_kernel<false, true>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
             else
                 hipLaunchKernelGGL((stats_stream_kernel<false, false>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw);
+                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
         }
-        hipLaunchKernelGGL(seq_finalize_kernel, dim3((unsigned)p.nblk_seq), dim3(kFinBlock), 0, st,
-                           cu, p.n, p.s, p.tmax, prm, seq_off, partial, so, blk);
+        hipLaunchKernelGGL(seq_finalize_kernel, dim3((unsigned)p.nblk_fin), dim3(kFinBlock), 0, st,
+                           cu, p.n, p.s, p.tmax, prm, seq_off, partial, (const double2*)wpart,
+                           streamed ? p.nwaves : (int64_t)0, so, blk);
     }
     if (batch)
         hipLaunchKernelGGL(batch_finalize_kernel, dim3(1), dim3(kFinBlock), 0, st, blk,
-                           p.nblk_seq, batch);
+                           p.s > 0 ? p.nblk_fin : (int64_t)0, batch);
     return hipGetLastError();
 }
 

@@ -66,7 +66,11 @@ struct StatsParamsDev {
 // tmax = ceil(n / kSubChunk) + s of each), and per-block batch partials.
 struct StatsPlan {
     int64_t n, s, tmax, nblk_scan, nblk_seq;
-    size_t bsum_off, boff_off, total_off, seqoff_off, desc_off, part_off, blk_off, total_bytes;
+    int64_t nblk_fin;    // finalize blocks: 256 sequences and 1024 streaming waves each
+    uint32_t spw;        // sub-chunk descriptors per streaming wave
+    int64_t nwaves;      // streaming waves launched (a multiple of the waves per block)
+    size_t bsum_off, boff_off, total_off, seqoff_off, desc_off, part_off, blk_off, wpart_off,
+        total_bytes;
 };
 
 bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p);
