@@ -18,7 +18,11 @@ Functions and the passages they follow:
   k1/k2/k3 ("RL: Training Inference Mismatch", KL-estimator table), TIS
   weight and clip flag ("Train-Inference Consistency", section 4), per-sequence
   and batch means (same "RL" page, monitoring flow), geometric-mean-ratio
-  rejection (VeXact compensation table).
+  rejection and its K3 form (VeXact compensation table, srs-k1 / srs-k3).
+* :func:`mismatch_extras` -- extreme-token rate, quantiles of the ratio and
+  of ``|delta|`` ("训推一致性与 determinism", section 7, metric table) and
+  the masked mean of ``|lt - lr| / (|lt| + 1e-8)`` ("RL: Training Inference
+  Mismatch", training/inference consistency).
 * :func:`bf16_decode`, :func:`bf16_round_rne` -- bf16 <-> double, ties to
   even ("Train-infer mismatch for Open-weight MoE RL", figure "Rounding
   depends on the order of additions").
@@ -49,8 +53,15 @@ BATCH_FIELDS = (
     "seq_mean_delta", "seq_mean_k1", "seq_mean_k2", "seq_mean_k3",
     "tok_mean_tis_w", "clip_ratio", "nan_ratio", "reject_frac",
     "mean_abs_delta", "max_abs_delta", "n_valid", "n_nan", "n_clipped",
-    "n_seq_nonempty", "n_seq_rejected",
+    "n_seq_nonempty", "n_seq_rejected", "reject_k3_frac", "n_seq_rejected_k3",
 )
+# Output vector of :func:`mismatch_extras`, in index order.
+EXTRAS_FIELDS = (
+    "n_valid", "n_extreme", "extreme_frac", "mean_rel_diff",
+    "ratio_q0", "ratio_q1", "ratio_q2", "ratio_q3",
+    "abs_q0", "abs_q1", "abs_q2", "abs_q3",
+)
+MAX_Q = 4
 
 _lock = threading.Lock()
 _lib = None
@@ -90,8 +101,13 @@ def _load():
         lib.or_mismatch_stats.restype = c_int
         lib.or_mismatch_stats.argtypes = [vp, vp, vp, vp, c_i64, c_i64,
                                           ctypes.c_double, ctypes.c_double,
-                                          ctypes.c_double] + [vp] * 17
+                                          ctypes.c_double, ctypes.c_double] + [vp] * 18
+        lib.or_mismatch_extras.restype = c_int
+        lib.or_mismatch_extras.argtypes = [vp, vp, vp, c_i64, ctypes.c_double, vp, c_int,
+                                           vp, c_int, vp]
+        lib.or_extras_nfields.restype = c_int
         assert lib.or_batch_nfields() == len(BATCH_FIELDS)
+        assert lib.or_extras_nfields() == len(EXTRAS_FIELDS)
         _lib = lib
         return lib
 
@@ -167,8 +183,13 @@ def logprob(h, w, ids, *, dtype: int, rows=None, nthreads: int = 0):
 
 
 def mismatch_stats(lt, lr, mask, cu_seqlens, *, clip_c: float, seq_lo: float,
-                   seq_hi: float) -> dict:
-    """fp64 token, sequence and batch statistics (see module docstring)."""
+                   seq_hi: float, seq_k3_hi: float = float("inf")) -> dict:
+    """fp64 token, sequence and batch statistics (see module docstring).
+
+    A sequence with a valid token is rejected when its mean delta is outside
+    ``[seq_lo, seq_hi]`` (``seq["reject"]``) and K3-rejected when its mean k3
+    exceeds ``seq_k3_hi`` (``seq["reject_k3"]``).
+    """
     lt = _as_host_array(lt, np.float32)
     lr = _as_host_array(lr, np.float32)
     cu = _as_host_array(cu_seqlens, np.int32)
@@ -181,17 +202,45 @@ def mismatch_stats(lt, lr, mask, cu_seqlens, *, clip_c: float, seq_lo: float,
     seq.update({k: np.empty(s, np.float64) for k in
                 ("mean_delta", "mean_k1", "mean_k2", "mean_k3", "mean_tis_w")})
     seq["reject"] = np.empty(s, np.uint8)
+    seq["reject_k3"] = np.empty(s, np.uint8)
     batch = np.empty(len(BATCH_FIELDS), np.float64)
     rc = _load().or_mismatch_stats(
         _ptr(lt), _ptr(lr), _ptr(m), _ptr(cu), n, s, float(clip_c), float(seq_lo),
-        float(seq_hi),
+        float(seq_hi), float(seq_k3_hi),
         _ptr(tok["delta"]), _ptr(tok["ratio"]), _ptr(tok["k1"]), _ptr(tok["k2"]),
         _ptr(tok["k3"]), _ptr(tok["tis_w"]), _ptr(tok["clipped"]),
         _ptr(seq["n_valid"]), _ptr(seq["n_clipped"]), _ptr(seq["n_nan"]),
         _ptr(seq["mean_delta"]), _ptr(seq["mean_k1"]), _ptr(seq["mean_k2"]),
         _ptr(seq["mean_k3"]), _ptr(seq["mean_tis_w"]), _ptr(seq["reject"]),
-        _ptr(batch))
+        _ptr(seq["reject_k3"]), _ptr(batch))
     if rc != 0:
         raise ValueError("or_mismatch_stats rejected its arguments")
     return {"token": tok, "seq": seq,
             "batch": dict(zip(BATCH_FIELDS, (float(x) for x in batch)))}
+
+
+def mismatch_extras(lt, lr, mask, *, tok_tau: float, ratio_q=(), abs_q=()) -> dict:
+    """fp64 extreme-token rate, mean relative difference and quantiles.
+
+    Returns ``{"n_valid", "n_extreme", "extreme_frac", "mean_rel_diff",
+    "ratio_q": [...], "abs_q": [...], "vector": np.ndarray}`` where the
+    quantile lists follow ``ratio_q`` / ``abs_q`` and ``vector`` is the full
+    output in ``EXTRAS_FIELDS`` order.
+    """
+    lt = _as_host_array(lt, np.float32)
+    lr = _as_host_array(lr, np.float32)
+    m = None if mask is None else _as_host_array(mask, np.uint8)
+    n = lt.size
+    rq = np.ascontiguousarray(ratio_q, dtype=np.float64)
+    aq = np.ascontiguousarray(abs_q, dtype=np.float64)
+    out = np.empty(len(EXTRAS_FIELDS), np.float64)
+    rc = _load().or_mismatch_extras(_ptr(lt), _ptr(lr), _ptr(m), n, float(tok_tau),
+                                    _ptr(rq) if rq.size else None, int(rq.size),
+                                    _ptr(aq) if aq.size else None, int(aq.size), _ptr(out))
+    if rc != 0:
+        raise ValueError("or_mismatch_extras rejected its arguments")
+    res = dict(zip(EXTRAS_FIELDS[:4], (float(x) for x in out[:4])))
+    res["ratio_q"] = [float(x) for x in out[4:4 + rq.size]]
+    res["abs_q"] = [float(x) for x in out[8:8 + aq.size]]
+    res["vector"] = out
+    return res

@@ -24,8 +24,15 @@
  *                       clip flag ("Train-Inference Consistency", section 4),
  *                       per-sequence mean then batch mean ("RL: Training
  *                       Inference Mismatch", monitoring flow, steps 2-3),
- *                       geometric-mean-ratio sequence rejection (VeXact
- *                       compensation table, r_corr-based rejection).
+ *                       geometric-mean-ratio sequence rejection and its
+ *                       K3 form, mean k3 above a bound (VeXact
+ *                       compensation table, srs-k1 / srs-k3 rows).
+ *   or_mismatch_extras  over the valid tokens of a batch: extreme-token
+ *                       rate |delta| > tau, quantiles of r and of |delta|
+ *                       ("训推一致性与 determinism", section 7, metric
+ *                       table), and the masked mean of
+ *                       |lt - lr| / (|lt| + 1e-8) ("RL: Training Inference
+ *                       Mismatch", training/inference consistency).
  *   or_bf16_decode /    exact bf16 -> double, and double -> bf16 with
  *   or_bf16_round_rne   round-to-nearest, ties-to-even ("Train-infer
  *                       mismatch for Open-weight MoE RL", figure "Rounding
@@ -228,7 +235,8 @@ enum {
     OB_SEQ_MEAN_DELTA, OB_SEQ_MEAN_K1, OB_SEQ_MEAN_K2, OB_SEQ_MEAN_K3,
     OB_TOK_MEAN_TIS_W, OB_CLIP_RATIO, OB_NAN_RATIO, OB_REJECT_FRAC,
     OB_MEAN_ABS_DELTA, OB_MAX_ABS_DELTA, OB_N_VALID, OB_N_NAN, OB_N_CLIPPED,
-    OB_N_SEQ_NONEMPTY, OB_N_SEQ_REJECTED, OB_NFIELDS
+    OB_N_SEQ_NONEMPTY, OB_N_SEQ_REJECTED, OB_REJECT_K3_FRAC,
+    OB_N_SEQ_REJECTED_K3, OB_NFIELDS
 };
 
 int or_batch_nfields(void) { return OB_NFIELDS; }
@@ -239,21 +247,25 @@ static double safe_div(double a, double b) { return b != 0.0 ? a / b : 0.0; }
  * Token outputs (each [n], nullable), sequence outputs (each [s],
  * nullable) and batch[OB_NFIELDS] (nullable).  mask nullable = all scored.
  * cu: [s+1] with 0 = cu[0] <= ... <= cu[s] = n.  Returns 0, or -1 on bad
- * arguments.
+ * arguments.  A sequence is rejected (s_reject) when its mean delta lies
+ * outside [seq_lo, seq_hi], and K3-rejected (s_reject_k3) when its mean k3
+ * exceeds seq_k3_hi (+inf: never); empty sequences are never rejected.
  */
 int or_mismatch_stats(const float* lt, const float* lr, const uint8_t* mask,
                       const int32_t* cu, int64_t n, int64_t s,
                       double clip_c, double seq_lo, double seq_hi,
+                      double seq_k3_hi,
                       double* t_delta, double* t_ratio, double* t_k1,
                       double* t_k2, double* t_k3, double* t_w,
                       uint8_t* t_clipped,
                       int32_t* s_n_valid, int32_t* s_n_clipped,
                       int32_t* s_n_nan, double* s_mean_delta,
                       double* s_mean_k1, double* s_mean_k2, double* s_mean_k3,
-                      double* s_mean_w, uint8_t* s_reject, double* batch)
+                      double* s_mean_w, uint8_t* s_reject,
+                      uint8_t* s_reject_k3, double* batch)
 {
     if (n < 0 || s < 0 || (n > 0 && (!lt || !lr || !cu || s < 1)) ||
-        !(clip_c > 0.0) || !(seq_lo <= seq_hi))
+        !(clip_c > 0.0) || !(seq_lo <= seq_hi) || isnan(seq_k3_hi))
         return -1;
     for (int64_t j = 0; j < s; ++j)
         if (cu[j] > cu[j + 1]) return -1;
@@ -267,7 +279,7 @@ int or_mismatch_stats(const float* lt, const float* lr, const uint8_t* mask,
     int64_t b_valid = 0, b_nan = 0, b_clip = 0, b_in = 0;
     /* batch sequence sums, accumulated over sequences in index order */
     double bs_delta = 0, bs_k1 = 0, bs_k2 = 0, bs_k3 = 0;
-    int64_t bs_nonempty = 0, bs_rejected = 0;
+    int64_t bs_nonempty = 0, bs_rejected = 0, bs_rejected_k3 = 0;
 
     for (int64_t j = 0; j < s; ++j) {
         double q_delta = 0, q_k1 = 0, q_k2 = 0, q_k3 = 0, q_w = 0;
@@ -312,9 +324,13 @@ int or_mismatch_stats(const float* lt, const float* lr, const uint8_t* mask,
         double m_k3 = safe_div(q_k3, (double)q_valid);
         double m_w = safe_div(q_w, (double)q_valid);
         int reject = q_valid > 0 && (m_delta < seq_lo || m_delta > seq_hi);
+        /* K3 form of the sequence rejection: the sequence's mean k3 (its
+         * sampled estimate of the rollout-to-trainer KL) above a bound */
+        int reject_k3 = q_valid > 0 && m_k3 > seq_k3_hi;
         if (q_valid > 0) {
             bs_nonempty++;
             bs_rejected += reject;
+            bs_rejected_k3 += reject_k3;
             bs_delta += m_delta; bs_k1 += m_k1; bs_k2 += m_k2; bs_k3 += m_k3;
         }
         if (s_n_valid) s_n_valid[j] = (int32_t)q_valid;
@@ -326,6 +342,7 @@ int or_mismatch_stats(const float* lt, const float* lr, const uint8_t* mask,
         if (s_mean_k3) s_mean_k3[j] = m_k3;
         if (s_mean_w) s_mean_w[j] = m_w;
         if (s_reject) s_reject[j] = (uint8_t)reject;
+        if (s_reject_k3) s_reject_k3[j] = (uint8_t)reject_k3;
     }
     if (batch) {
         double nv = (double)b_valid, ns = (double)bs_nonempty;
@@ -348,6 +365,109 @@ int or_mismatch_stats(const float* lt, const float* lr, const uint8_t* mask,
         batch[OB_N_CLIPPED] = (double)b_clip;
         batch[OB_N_SEQ_NONEMPTY] = ns;
         batch[OB_N_SEQ_REJECTED] = (double)bs_rejected;
+        batch[OB_REJECT_K3_FRAC] = safe_div((double)bs_rejected_k3, ns);
+        batch[OB_N_SEQ_REJECTED_K3] = (double)bs_rejected_k3;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Extra mismatch metrics: quantiles, extreme tokens, relative diff    */
+/* ------------------------------------------------------------------ */
+
+/* Output layout of or_mismatch_extras (restated from the definitions). */
+enum {
+    OX_N_VALID, OX_N_EXTREME, OX_EXTREME_FRAC, OX_MEAN_REL_DIFF,
+    OX_RATIO_Q0, OX_ABS_Q0 = OX_RATIO_Q0 + 4, OX_NFIELDS = OX_ABS_Q0 + 4
+};
+#define OX_MAX_Q 4
+
+int or_extras_nfields(void) { return OX_NFIELDS; }
+
+static int cmp_double(const void* a, const void* b)
+{
+    double x = *(const double*)a, y = *(const double*)b;
+    return (x > y) - (x < y);
+}
+
+/* Quantile q of the ascending array x[0..m) with linear interpolation
+ * between order statistics: position q (m - 1), lower index its floor,
+ * upper index one above (capped at m - 1), weight the fractional part.
+ * Empty array: 0. */
+static double quantile_sorted(const double* x, int64_t m, double q)
+{
+    if (m == 0) return 0.0;
+    double pos = q * (double)(m - 1);
+    double fl = floor(pos);
+    int64_t lo = (int64_t)fl;
+    int64_t hi = lo + 1 < m ? lo + 1 : lo;
+    double frac = pos - fl;
+    return x[lo] + (x[hi] - x[lo]) * frac;
+}
+
+/*
+ * Batch metrics over the valid tokens (mask != 0 and a finite
+ * delta = lt - lr computed in double):
+ *   out[OX_N_VALID]        number of valid tokens;
+ *   out[OX_N_EXTREME]      valid tokens with |delta| > tok_tau, and
+ *   out[OX_EXTREME_FRAC]   their share of the valid tokens ("训推一致性与
+ *                          determinism", section 7: the extreme-token rate);
+ *   out[OX_MEAN_REL_DIFF]  mean of |lt - lr| / (|lt| + 1e-8) ("RL: Training
+ *                          Inference Mismatch", training/inference
+ *                          consistency section: masked mean of rel_diff);
+ *   out[OX_RATIO_Q0 + i]   quantile ratio_q[i] of r = exp(delta), and
+ *   out[OX_ABS_Q0 + i]     quantile abs_q[i] of |delta| (same Atlas section:
+ *                          ratio quantiles and the p95 of the absolute
+ *                          difference), each by sorting the values and
+ *                          interpolating linearly; unused slots are 0.
+ * With no valid token every ratio and quantile is 0.  Returns 0, or -1 on
+ * bad arguments (probabilities outside [0, 1], NaN tok_tau, more than
+ * OX_MAX_Q probabilities of a kind, null required pointer).
+ */
+int or_mismatch_extras(const float* lt, const float* lr, const uint8_t* mask,
+                       int64_t n, double tok_tau,
+                       const double* ratio_q, int n_ratio_q,
+                       const double* abs_q, int n_abs_q, double* out)
+{
+    if (n < 0 || (n > 0 && (!lt || !lr)) || !out || isnan(tok_tau) ||
+        n_ratio_q < 0 || n_ratio_q > OX_MAX_Q || n_abs_q < 0 ||
+        n_abs_q > OX_MAX_Q || (n_ratio_q > 0 && !ratio_q) ||
+        (n_abs_q > 0 && !abs_q))
+        return -1;
+    for (int i = 0; i < n_ratio_q; ++i)
+        if (!(ratio_q[i] >= 0.0 && ratio_q[i] <= 1.0)) return -1;
+    for (int i = 0; i < n_abs_q; ++i)
+        if (!(abs_q[i] >= 0.0 && abs_q[i] <= 1.0)) return -1;
+
+    double* ratio = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double* absd = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!ratio || !absd) { free(ratio); free(absd); return -1; }
+
+    int64_t m = 0, n_ext = 0;
+    double rel_sum = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+        if (mask && mask[t] == 0) continue;
+        double delta = (double)lt[t] - (double)lr[t];
+        if (!isfinite(delta)) continue;
+        ratio[m] = exp(delta);
+        absd[m] = fabs(delta);
+        if (fabs(delta) > tok_tau) n_ext++;
+        rel_sum += fabs(delta) / (fabs((double)lt[t]) + 1e-8);
+        m++;
+    }
+    qsort(ratio, (size_t)m, sizeof(double), cmp_double);
+    qsort(absd, (size_t)m, sizeof(double), cmp_double);
+
+    for (int i = 0; i < OX_NFIELDS; ++i) out[i] = 0.0;
+    out[OX_N_VALID] = (double)m;
+    out[OX_N_EXTREME] = (double)n_ext;
+    out[OX_EXTREME_FRAC] = safe_div((double)n_ext, (double)m);
+    out[OX_MEAN_REL_DIFF] = safe_div(rel_sum, (double)m);
+    for (int i = 0; i < n_ratio_q; ++i)
+        out[OX_RATIO_Q0 + i] = quantile_sorted(ratio, m, ratio_q[i]);
+    for (int i = 0; i < n_abs_q; ++i)
+        out[OX_ABS_Q0 + i] = quantile_sorted(absd, m, abs_q[i]);
+    free(ratio);
+    free(absd);
     return 0;
 }

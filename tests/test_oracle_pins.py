@@ -332,6 +332,147 @@ def test_rejection_window_in_log_domain():
         assert r["seq"]["reject"][0] == want
 
 
+def test_k3_rejection_uses_mean_k3_not_k2():
+    # constant delta c per sequence: mean k3 = e^c - 1 - c exactly as its own
+    # closed form, mean k2 = c^2 / 2.  For c = +-0.3 the two k2 are equal
+    # (0.045) while k3(+0.3) = 0.04986 > 0.0475 > k3(-0.3) = 0.04082, so only
+    # a K3 test separates them.
+    n = 8
+    lr = np.full(3 * n, -2.0, np.float32)
+    lt = lr.astype(np.float64).copy()
+    lt[:n] += 0.3
+    lt[n:2 * n] -= 0.3
+    lt = lt.astype(np.float32)
+    cu = [0, n, 2 * n, 2 * n, 3 * n]          # third sequence empty, fourth zero delta
+    r = oracle.mismatch_stats(lt, lr, None, np.asarray(cu, np.int32), clip_c=2.0,
+                              seq_lo=-1.0, seq_hi=1.0, seq_k3_hi=0.0475)
+    d = r["token"]["delta"]
+    for j, (a, b) in enumerate([(0, n), (n, 2 * n)]):
+        c = Decimal(float(d[a]))
+        assert np.all(d[a:b] == d[a])
+        assert abs(Decimal(float(r["seq"]["mean_k3"][j])) - (c.exp() - 1 - c)) < Decimal(1e-15)
+    assert list(r["seq"]["reject_k3"]) == [1, 0, 0, 0]
+    assert list(r["seq"]["reject"]) == [0, 0, 0, 0]
+    assert r["batch"]["n_seq_rejected_k3"] == 1 and r["batch"]["n_seq_nonempty"] == 3
+    assert r["batch"]["reject_k3_frac"] == 1 / 3
+    # strict bound: a bound equal to a sequence's mean k3 does not reject it
+    r2 = oracle.mismatch_stats(lt, lr, None, np.asarray(cu, np.int32), clip_c=2.0,
+                               seq_lo=-1.0, seq_hi=1.0, seq_k3_hi=float(r["seq"]["mean_k3"][1]))
+    assert list(r2["seq"]["reject_k3"]) == [1, 0, 0, 0]
+    # the default bound (+inf) never rejects
+    r3 = oracle.mismatch_stats(lt, lr, None, np.asarray(cu, np.int32), clip_c=2.0,
+                               seq_lo=-1.0, seq_hi=1.0)
+    assert not r3["seq"]["reject_k3"].any() and r3["batch"]["reject_k3_frac"] == 0
+
+
+# ---------------------------------------------------------------------------
+# extra metrics: extreme-token rate, relative difference, quantiles
+# ---------------------------------------------------------------------------
+
+def _extras(lt, lr, mask=None, tau=0.1, rq=(), aq=()):
+    return oracle.mismatch_extras(np.asarray(lt, np.float32), np.asarray(lr, np.float32),
+                                  None if mask is None else np.asarray(mask, np.uint8),
+                                  tok_tau=tau, ratio_q=rq, abs_q=aq)
+
+
+def test_extreme_rate_is_strict_and_two_sided():
+    lr = np.full(10, -4.0, np.float32)
+    offs = np.array([0.25, -0.25, 0.125, -0.125, 0.5, -0.5, 0, 0, 1.0, -1.0])
+    lt = (lr + offs).astype(np.float32)         # exact: dyadic offsets
+    r = _extras(lt, lr, tau=0.25)
+    assert r["n_extreme"] == 4                   # |delta| = 0.5, 0.5, 1, 1; 0.25 is not > 0.25
+    assert r["extreme_frac"] == 0.4 and r["n_valid"] == 10
+    mask = np.array([1] * 8 + [0, 0], np.uint8)  # masking drops the two |delta| = 1
+    r = _extras(lt, lr, mask=mask, tau=0.25)
+    assert r["n_extreme"] == 2 and r["n_valid"] == 8 and r["extreme_frac"] == 0.25
+    r = _extras(lt, lr, tau=float("inf"))
+    assert r["n_extreme"] == 0 and r["extreme_frac"] == 0
+
+
+def test_rel_diff_equals_mean_abs_delta_when_train_logp_is_minus_one():
+    # |lt| = 1 everywhere: the mean of |delta| / (1 + 1e-8) is the pinned
+    # mean |delta| of the statistics pass, divided once by 1 + 1e-8
+    rng = np.random.default_rng(11)
+    n = 200
+    lt = np.full(n, -1.0, np.float32)
+    lr = (lt + rng.normal(0, 0.05, n)).astype(np.float32)
+    mask = (rng.random(n) < 0.8).astype(np.uint8)
+    lr[3] = np.nan                               # non-finite delta: left out of both
+    mask[3] = 1
+    r = _extras(lt, lr, mask=mask)
+    st = oracle.mismatch_stats(lt, lr, mask, np.asarray([0, n], np.int32), clip_c=2.0,
+                               seq_lo=-1.0, seq_hi=1.0)
+    assert r["n_valid"] == st["batch"]["n_valid"]
+    assert r["mean_rel_diff"] == pytest.approx(st["batch"]["mean_abs_delta"] / (1 + 1e-8),
+                                               rel=1e-14)
+    # the denominator is the trainer side: varying |lr| instead changes nothing
+    # in this construction, while varying |lt| does
+    lt2 = (lt * 2).astype(np.float32)            # |lt| = 2, same deltas after shifting lr
+    lr2 = (lr.astype(np.float64) - 1.0).astype(np.float32)
+    r2 = _extras(lt2, lr2, mask=mask)
+    assert r2["mean_rel_diff"] == pytest.approx(r["mean_rel_diff"] / 2, rel=1e-6)
+
+
+def test_rel_diff_zero_train_logp_and_scale_invariance():
+    # lt = 0 exactly (a certain token): |delta| / 1e-8
+    r = _extras([0.0], [-(2.0 ** -20)])
+    assert r["mean_rel_diff"] == pytest.approx(95.367431640625, rel=1e-15)
+    # scaling both log-probabilities by 2^k leaves |delta| / |lt| unchanged up
+    # to the 1e-8 guard
+    rng = np.random.default_rng(12)
+    lt = -rng.uniform(0.5, 3.0, 64).astype(np.float32)
+    lr = (lt + rng.normal(0, 0.01, 64)).astype(np.float32)
+    a = _extras(lt, lr)["mean_rel_diff"]
+    b = _extras(lt * np.float32(8), lr * np.float32(8))["mean_rel_diff"]
+    assert b == pytest.approx(a, rel=1e-7) and a > 1e-4
+
+
+def test_quantiles_match_numpy_linear_method():
+    rng = np.random.default_rng(13)
+    for n in (1, 2, 3, 7, 100, 1001):
+        lr = -rng.uniform(0.0, 5.0, n).astype(np.float32)
+        lt = (lr + rng.normal(0, 0.02, n)).astype(np.float32)
+        mask = (rng.random(n) < 0.7).astype(np.uint8)
+        mask[0] = 1
+        qs = (0.01, 0.5, 0.99)
+        r = _extras(lt, lr, mask=mask, rq=qs, aq=(0.95,))
+        d = lt.astype(np.float64)[mask != 0] - lr.astype(np.float64)[mask != 0]
+        want_r = np.quantile(np.exp(d), qs, method="linear")
+        want_a = np.quantile(np.abs(d), 0.95, method="linear")
+        np.testing.assert_allclose(r["ratio_q"], want_r, rtol=1e-14, atol=0)
+        assert r["abs_q"][0] == pytest.approx(want_a, rel=1e-14, abs=1e-300)
+
+
+def test_quantile_order_statistics_and_edge_cases():
+    lr = np.full(5, -1.0, np.float32)
+    offs = np.array([0.5, -0.25, 0.0, 0.125, -1.0])
+    lt = (lr + offs).astype(np.float32)
+    r = _extras(lt, lr, rq=(0.0, 0.5, 1.0, 0.25), aq=(0.0, 1.0, 0.5, 0.375))
+    # five values: q = 0.25 lands on the second order statistic exactly,
+    # q = 0.375 half-way between the second and third
+    assert r["ratio_q"] == [math.exp(-1.0), 1.0, math.exp(0.5), math.exp(-0.25)]
+    assert r["abs_q"][:3] == [0.0, 1.0, 0.25]
+    assert r["abs_q"][3] == 0.125 + (0.25 - 0.125) * 0.5
+    # order of the tokens does not matter
+    for perm in ([4, 3, 2, 1, 0], [2, 0, 4, 1, 3]):
+        rp = _extras(lt[perm], lr[perm], rq=(0.0, 0.5, 1.0, 0.25), aq=(0.0, 1.0, 0.5, 0.375))
+        assert rp["ratio_q"] == r["ratio_q"] and rp["abs_q"] == r["abs_q"]
+    # one valid token: every quantile is its value; none: zeros
+    m1 = np.array([0, 0, 0, 1, 0], np.uint8)
+    r1 = _extras(lt, lr, mask=m1, rq=(0.01, 0.99), aq=(0.95,))
+    assert r1["ratio_q"] == [math.exp(0.125)] * 2 and r1["abs_q"] == [0.125]
+    r0 = _extras(lt, lr, mask=np.zeros(5, np.uint8), rq=(0.5,), aq=(0.95,))
+    assert r0["ratio_q"] == [0.0] and r0["abs_q"] == [0.0] and r0["n_valid"] == 0
+    assert r0["mean_rel_diff"] == 0 and r0["extreme_frac"] == 0
+    # all deltas equal (zero mismatch): every quantile is that value
+    rz = _extras(lr, lr, rq=(0.01, 0.5, 0.99), aq=(0.95,))
+    assert rz["ratio_q"] == [1.0, 1.0, 1.0] and rz["abs_q"] == [0.0]
+    with pytest.raises(ValueError):
+        _extras(lt, lr, rq=(1.5,))
+    with pytest.raises(ValueError):
+        _extras(lt, lr, tau=float("nan"))
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ---------------------------------------------------------------------------
@@ -343,8 +484,12 @@ MUTATIONS = [
      "test_brute_force_against_exact_logits_and_decimal_softmax"),
     ("transposed W", "c * j->ldw + k", "k * j->ldw + c",
      "test_brute_force_against_exact_logits_and_decimal_softmax"),
-    ("delta sign", "delta = (double)lt[t] - (double)lr[t];",
-     "delta = (double)lr[t] - (double)lt[t];", "test_vexact_table1_sign_and_derived_estimators"),
+    ("delta sign", "                delta = (double)lt[t] - (double)lr[t];",
+     "                delta = (double)lr[t] - (double)lt[t];",
+     "test_vexact_table1_sign_and_derived_estimators"),
+    ("extras delta sign", "double delta = (double)lt[t] - (double)lr[t];",
+     "double delta = (double)lr[t] - (double)lt[t];",
+     "test_quantile_order_statistics_and_edge_cases"),
     ("k3 without -delta", "k3 = expm1(delta) - delta;", "k3 = expm1(delta);",
      "test_k3_nonnegative_and_matches_closed_form"),
     ("k3 without -1", "k3 = expm1(delta) - delta;", "k3 = exp(delta) - delta;",
@@ -353,6 +498,28 @@ MUTATIONS = [
      "test_sequence_mean_then_batch_mean_differs_from_token_mean"),
     ("clip at C instead of log C", "clipped = delta > log_c;", "clipped = delta > clip_c;",
      "test_truncated_is_clips_above_log_c"),
+    ("K3 rejection on k2", "int reject_k3 = q_valid > 0 && m_k3 > seq_k3_hi;",
+     "int reject_k3 = q_valid > 0 && m_k2 > seq_k3_hi;",
+     "test_k3_rejection_uses_mean_k3_not_k2"),
+    ("K3 rejection not strict", "int reject_k3 = q_valid > 0 && m_k3 > seq_k3_hi;",
+     "int reject_k3 = q_valid > 0 && m_k3 >= seq_k3_hi;",
+     "test_k3_rejection_uses_mean_k3_not_k2"),
+    ("extreme without abs", "if (fabs(delta) > tok_tau) n_ext++;",
+     "if (delta > tok_tau) n_ext++;", "test_extreme_rate_is_strict_and_two_sided"),
+    ("extreme not strict", "if (fabs(delta) > tok_tau) n_ext++;",
+     "if (fabs(delta) >= tok_tau) n_ext++;", "test_extreme_rate_is_strict_and_two_sided"),
+    ("rel diff over rollout", "rel_sum += fabs(delta) / (fabs((double)lt[t]) + 1e-8);",
+     "rel_sum += fabs(delta) / (fabs((double)lr[t]) + 1e-8);",
+     "test_rel_diff_equals_mean_abs_delta_when_train_logp_is_minus_one"),
+    ("rel diff guard 1e-6", "rel_sum += fabs(delta) / (fabs((double)lt[t]) + 1e-8);",
+     "rel_sum += fabs(delta) / (fabs((double)lt[t]) + 1e-6);",
+     "test_rel_diff_zero_train_logp_and_scale_invariance"),
+    ("quantile without interpolation", "return x[lo] + (x[hi] - x[lo]) * frac;",
+     "return x[lo];", "test_quantile_order_statistics_and_edge_cases"),
+    ("quantile of unsorted values", "qsort(ratio, (size_t)m, sizeof(double), cmp_double);",
+     "(void)cmp_double;", "test_quantile_order_statistics_and_edge_cases"),
+    ("quantile position over m", "double pos = q * (double)(m - 1);",
+     "double pos = q * (double)m;", "test_quantiles_match_numpy_linear_method"),
 ]
 
 
