@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define TIM_ABI_VERSION 1
+#define TIM_ABI_VERSION 2
 
 typedef enum {
     TIM_OK = 0,
@@ -165,6 +165,10 @@ typedef struct {
                           Log-domain bounds: the geometric mean of r over a
                           sequence's tokens is exp(mean delta), so a ratio
                           window [a, b] is passed as [log a, log b].      */
+    double seq_k3_hi;  /* K3-rejects a sequence iff its mean k3 > seq_k3_hi
+                          (not NaN; +inf never rejects).  The K3 form of the
+                          r_corr sequence rejection: VeXact compensation
+                          table, srs-k3 rows.                              */
 } tim_stats_params;
 
 /* (host struct) optional per-token outputs, each [n], each nullable.
@@ -195,6 +199,7 @@ typedef struct {
     double* mean_k3;
     double* mean_tis_w;
     uint8_t* reject;       /* 1 iff mean_delta < seq_lo || > seq_hi        */
+    uint8_t* reject_k3;    /* 1 iff mean_k3 > seq_k3_hi                    */
 } tim_seq_out;
 
 /* Indices of the batch aggregate vector (fp64).  Token means are over all
@@ -222,7 +227,9 @@ enum {
     TIM_B_N_CLIPPED = 16,
     TIM_B_N_SEQ_NONEMPTY = 17,
     TIM_B_N_SEQ_REJECTED = 18,
-    TIM_B_NFIELDS = 19
+    TIM_B_REJECT_K3_FRAC = 19, /* K3-rejected / sequences with a valid token */
+    TIM_B_N_SEQ_REJECTED_K3 = 20,
+    TIM_B_NFIELDS = 21
 };
 
 /* Bytes of device workspace tim_mismatch_stats needs; 0 for negative
@@ -246,7 +253,8 @@ size_t tim_stats_workspace_bytes(int64_t n, int64_t s);
  *  workspace     >= tim_stats_workspace_bytes(n, s) bytes (else
  *                TIM_EWORKSPACE), 256-byte aligned (else TIM_EUNSUPPORTED).
  *  Errors: TIM_EINVAL for n < 0, s < 0, n > 0 with s == 0, null p, C not a
- *  finite positive number, seq_lo > seq_hi or a NaN bound, null lt/lr when
+ *  finite positive number, seq_lo > seq_hi or a NaN bound (seq_k3_hi
+ *  included), null lt/lr when
  *  n > 0, null cu_seqlens; TIM_EUNSUPPORTED for n or s beyond int32.
  *  n == 0 and s == 0 returns TIM_OK without a launch.
  *
@@ -260,6 +268,78 @@ int tim_mismatch_stats(const float* logp_train, const float* logp_rollout,
                        double* batch,
                        void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Extra mismatch metrics: extreme-token rate, relative difference and
+ * quantiles of the ratio and of |delta|.
+ * ---------------------------------------------------------------------- */
+
+#define TIM_X_MAX_Q 4      /* probabilities per call, both kinds together */
+
+/* (host) parameters of tim_mismatch_extras. */
+typedef struct {
+    double tok_tau;        /* a valid token is "extreme" iff |delta| > tok_tau
+                              (not NaN; +inf counts none)                   */
+    int32_t n_ratio_q;     /* number of quantiles of r = exp(delta) ...     */
+    int32_t n_abs_q;       /* ... and of |delta|; n_ratio_q + n_abs_q <=
+                              TIM_X_MAX_Q, both >= 0                        */
+    double ratio_q[TIM_X_MAX_Q];   /* probabilities in [0, 1]               */
+    double abs_q[TIM_X_MAX_Q];     /* probabilities in [0, 1]               */
+} tim_extras_params;
+
+/* Indices of the fp64 output vector of tim_mismatch_extras. */
+enum {
+    TIM_X_N_VALID = 0,         /* valid tokens: mask != 0, finite delta     */
+    TIM_X_N_EXTREME = 1,       /* valid tokens with |delta| > tok_tau       */
+    TIM_X_EXTREME_FRAC = 2,    /* n_extreme / n_valid                       */
+    TIM_X_MEAN_REL_DIFF = 3,   /* mean of |delta| / (|logp_train| + 1e-8)   */
+    TIM_X_RATIO_Q = 4,         /* 4 slots: quantile ratio_q[i] of r         */
+    TIM_X_ABS_Q = 8,           /* 4 slots: quantile abs_q[i] of |delta|     */
+    TIM_X_NFIELDS = 12
+};
+
+/* Bytes of device workspace tim_mismatch_extras needs; 0 for n < 0 or
+ * n > 2^31 - 1.  Pure host function. */
+size_t tim_extras_workspace_bytes(int64_t n);
+
+/*
+ * Batch metrics over the valid tokens (mask != 0 and a finite
+ * delta = logp_train - logp_rollout, computed in fp64):
+ *
+ *   - the extreme-token rate, the share of valid tokens with
+ *     |delta| > tok_tau ("训推一致性与 determinism", section 7, metric
+ *     table, the fraction of tokens above a threshold);
+ *   - the mean of |delta| / (|logp_train| + 1e-8) ("RL: Training Inference
+ *     Mismatch", training/inference consistency section, rel_diff and its
+ *     masked mean);
+ *   - quantiles of r = exp(delta) and of |delta| (same Atlas table: ratio
+ *     quantiles 0.01 / 0.5 / 0.99 and the p95 of the absolute difference).
+ *     Quantile q of m sorted values x is x[lo] + (x[hi] - x[lo]) * f with
+ *     pos = q (m - 1), lo = floor(pos), hi = min(lo + 1, m - 1),
+ *     f = pos - lo, each operation rounded in fp64.
+ *
+ *  logp_train, logp_rollout  [n] fp32;  mask [n] uint8, nullable (= all).
+ *  n          tokens, 0 <= n <= 2^31 - 1.
+ *  p          (host) threshold and probabilities.
+ *  out        [TIM_X_NFIELDS] fp64 out, nullable (then nothing is written).
+ *             With no valid token every ratio and quantile is 0.  Unused
+ *             quantile slots are 0.
+ *  workspace  >= tim_extras_workspace_bytes(n) bytes (else TIM_EWORKSPACE),
+ *             256-byte aligned (else TIM_EUNSUPPORTED).
+ *  Errors: TIM_EINVAL for n < 0, null p, a NaN tok_tau, a probability
+ *  outside [0, 1], a negative count or more than TIM_X_MAX_Q of them, null
+ *  logp_train / logp_rollout when n > 0; TIM_EUNSUPPORTED for n > 2^31 - 1.
+ *
+ * The order statistics are selected exactly (a radix select over 64-bit
+ * keys of the fp64 deltas, integer histograms), so the |delta| quantiles
+ * are correctly rounded functions of the inputs and every output is
+ * deterministic; the relative-difference sum is reduced in an order that
+ * depends only on n.
+ */
+int tim_mismatch_extras(const float* logp_train, const float* logp_rollout,
+                        const uint8_t* mask, int64_t n, const tim_extras_params* p,
+                        double* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 #ifdef __cplusplus
 }

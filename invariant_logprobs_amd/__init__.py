@@ -15,7 +15,12 @@ Entry points (same names as the C ABI):
 * :func:`tim_mismatch_stats` -- delta, ratio, k1/k2/k3, truncated IS weight,
   per-sequence means and geometric-mean-ratio rejection, batch aggregates
   ("Diagnosing Training Inference Mismatch ... (VeXact)", eq. (1) and its
-  compensation table; "Train-Inference Consistency", sections 4-5).
+  compensation table; "Train-Inference Consistency", sections 4-5), and the
+  K3 form of the sequence rejection (srs-k3 rows of the same table).
+* :func:`tim_mismatch_extras` -- extreme-token rate, quantiles of the ratio
+  and of ``|delta|`` ("训推一致性与 determinism", section 7, metric table)
+  and the masked mean relative difference ("RL: Training Inference
+  Mismatch", training/inference consistency).
 """
 from __future__ import annotations
 
@@ -41,12 +46,22 @@ BATCH_FIELDS = (
     "seq_mean_delta", "seq_mean_k1", "seq_mean_k2", "seq_mean_k3",
     "tok_mean_tis_w", "is_clip_ratio", "is_nan_ratio", "reject_frac",
     "mean_abs_delta", "max_abs_delta", "n_valid", "n_nan", "n_clipped",
-    "n_seq_nonempty", "n_seq_rejected",
+    "n_seq_nonempty", "n_seq_rejected", "reject_k3_frac", "n_seq_rejected_k3",
 )
+
+# Names of the tim_mismatch_extras output vector, in TIM_X_* index order.
+EXTRAS_FIELDS = (
+    "n_valid", "n_extreme", "extreme_frac", "mean_rel_diff",
+    "ratio_q0", "ratio_q1", "ratio_q2", "ratio_q3",
+    "abs_q0", "abs_q1", "abs_q2", "abs_q3",
+)
+X_MAX_Q = 4
+ABI_VERSION = 2
 
 # Exported symbols of libtim.so (checked against include/tim.h by the tests).
 EXPORTS = ("tim_abi_version", "tim_status_string", "tim_logprob_workspace_bytes",
-           "tim_logprob_forward", "tim_stats_workspace_bytes", "tim_mismatch_stats")
+           "tim_logprob_forward", "tim_stats_workspace_bytes", "tim_mismatch_stats",
+           "tim_extras_workspace_bytes", "tim_mismatch_extras")
 
 
 class TimError(RuntimeError):
@@ -57,7 +72,13 @@ class TimError(RuntimeError):
 
 class _StatsParams(ctypes.Structure):
     _fields_ = [("tis_clip_c", ctypes.c_double), ("seq_lo", ctypes.c_double),
-                ("seq_hi", ctypes.c_double)]
+                ("seq_hi", ctypes.c_double), ("seq_k3_hi", ctypes.c_double)]
+
+
+class _ExtrasParams(ctypes.Structure):
+    _fields_ = [("tok_tau", ctypes.c_double), ("n_ratio_q", ctypes.c_int32),
+                ("n_abs_q", ctypes.c_int32), ("ratio_q", ctypes.c_double * X_MAX_Q),
+                ("abs_q", ctypes.c_double * X_MAX_Q)]
 
 
 class _TokenOut(ctypes.Structure):
@@ -68,7 +89,7 @@ class _TokenOut(ctypes.Structure):
 class _SeqOut(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in
                 ("n_valid", "n_clipped", "n_nan", "mean_delta", "mean_k1", "mean_k2",
-                 "mean_k3", "mean_tis_w", "reject")]
+                 "mean_k3", "mean_tis_w", "reject", "reject_k3")]
 
 
 _lock = threading.Lock()
@@ -106,6 +127,14 @@ def load_library():
                                            ctypes.POINTER(_StatsParams),
                                            ctypes.POINTER(_TokenOut), ctypes.POINTER(_SeqOut),
                                            vp, vp, sz, vp]
+        lib.tim_extras_workspace_bytes.restype = sz
+        lib.tim_extras_workspace_bytes.argtypes = [i64]
+        lib.tim_mismatch_extras.restype = ctypes.c_int
+        lib.tim_mismatch_extras.argtypes = [vp, vp, vp, i64, ctypes.POINTER(_ExtrasParams), vp,
+                                            vp, sz, vp]
+        if lib.tim_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.tim_abi_version()}, "
+                               f"expected {ABI_VERSION}: rebuild it")
         _lib = lib
         return lib
 
@@ -188,12 +217,14 @@ def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
 def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
                        mask: Optional[torch.Tensor], cu_seqlens: torch.Tensor, *,
                        tis_clip: float = 2.0, seq_bounds=(-0.01, 0.01),
+                       seq_k3_max: float = math.inf,
                        token_outputs: bool = False, seq_outputs: bool = True,
                        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Mismatch statistics between trainer and rollout log-probabilities.
 
     ``seq_bounds`` are log-domain bounds on a sequence's mean delta; a
-    geometric-mean-ratio window ``[a, b]`` is ``(log a, log b)``.  Returns a
+    geometric-mean-ratio window ``[a, b]`` is ``(log a, log b)``.  A sequence
+    whose mean k3 exceeds ``seq_k3_max`` is K3-rejected (``inf``: never).  Returns a
     dict with ``"batch"`` (a tensor of ``len(BATCH_FIELDS)`` fp64 values on the
     GPU), and optionally ``"seq"`` and ``"token"`` dicts of GPU tensors.
     """
@@ -234,14 +265,16 @@ def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
         q.update({k: torch.empty(s, dtype=torch.float64, device=dev)
                   for k in ("mean_delta", "mean_k1", "mean_k2", "mean_k3", "mean_tis_w")})
         q["reject"] = torch.empty(s, dtype=torch.uint8, device=dev)
+        q["reject_k3"] = torch.empty(s, dtype=torch.uint8, device=dev)
         res["seq"] = q
         seq = _SeqOut(*[_dptr(q[k]) for k in ("n_valid", "n_clipped", "n_nan", "mean_delta",
                                                "mean_k1", "mean_k2", "mean_k3", "mean_tis_w",
-                                               "reject")])
+                                               "reject", "reject_k3")])
     need = lib.tim_stats_workspace_bytes(n, s)
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
-    prm = _StatsParams(float(tis_clip), float(seq_bounds[0]), float(seq_bounds[1]))
+    prm = _StatsParams(float(tis_clip), float(seq_bounds[0]), float(seq_bounds[1]),
+                       float(seq_k3_max))
     st = lib.tim_mismatch_stats(_dptr(logp_train), _dptr(logp_rollout), _dptr(mask),
                                 _dptr(cu_seqlens), n, s, ctypes.byref(prm),
                                 ctypes.byref(tok) if tok is not None else None,
@@ -251,6 +284,63 @@ def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
                                 _stream_handle(stream))
     if st != TIM_OK:
         raise TimError(st, "tim_mismatch_stats")
+    return res
+
+
+def extras_workspace_bytes(n: int) -> int:
+    return int(load_library().tim_extras_workspace_bytes(n))
+
+
+def tim_mismatch_extras(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
+                        mask: Optional[torch.Tensor], *, tok_tau: float,
+                        ratio_q=(0.01, 0.5, 0.99), abs_q=(0.95,),
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Extreme-token rate, mean relative difference and quantiles.
+
+    Returns a GPU fp64 tensor of ``len(EXTRAS_FIELDS)`` values; quantile
+    ``ratio_q[i]`` of ``exp(delta)`` is at ``ratio_q{i}`` and quantile
+    ``abs_q[i]`` of ``|delta|`` at ``abs_q{i}`` (see :func:`extras_dict`).
+    """
+    lib = load_library()
+    _require_gpu("logp_train", logp_train)
+    _require_gpu("logp_rollout", logp_rollout)
+    if logp_train.dtype != torch.float32 or logp_rollout.dtype != torch.float32:
+        raise ValueError("log-probabilities must be float32")
+    if not (logp_train.is_contiguous() and logp_rollout.is_contiguous()):
+        raise ValueError("log-probabilities must be contiguous")
+    n = logp_train.numel()
+    if logp_rollout.numel() != n:
+        raise ValueError("inconsistent sizes")
+    if mask is not None:
+        _require_gpu("mask", mask)
+        if mask.dtype != torch.uint8 or not mask.is_contiguous() or mask.numel() != n:
+            raise ValueError("mask must be a contiguous uint8 tensor of n entries")
+    ratio_q, abs_q = tuple(ratio_q), tuple(abs_q)
+    if len(ratio_q) + len(abs_q) > X_MAX_Q:
+        raise ValueError(f"at most {X_MAX_Q} probabilities per call")
+    prm = _ExtrasParams(float(tok_tau), len(ratio_q), len(abs_q),
+                        (ctypes.c_double * X_MAX_Q)(*(list(ratio_q) + [0.0] * (X_MAX_Q - len(ratio_q)))),
+                        (ctypes.c_double * X_MAX_Q)(*(list(abs_q) + [0.0] * (X_MAX_Q - len(abs_q)))))
+    dev = logp_train.device
+    out = torch.empty(len(EXTRAS_FIELDS), dtype=torch.float64, device=dev)
+    need = lib.tim_extras_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    st = lib.tim_mismatch_extras(_dptr(logp_train), _dptr(logp_rollout), _dptr(mask), n,
+                                 ctypes.byref(prm), _dptr(out), _dptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_mismatch_extras")
+    return out
+
+
+def extras_dict(out: torch.Tensor, n_ratio_q: int = 3, n_abs_q: int = 1) -> dict:
+    """Host dict of a tim_mismatch_extras output (synchronises)."""
+    v = [float(x) for x in out.cpu().tolist()]
+    res = dict(zip(EXTRAS_FIELDS[:4], v[:4]))
+    res["ratio_q"] = v[4:4 + n_ratio_q]
+    res["abs_q"] = v[8:8 + n_abs_q]
     return res
 
 

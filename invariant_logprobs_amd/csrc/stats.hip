@@ -6,9 +6,10 @@
 // k3 = (r - 1) - delta ("RL: Training Inference Mismatch", KL-estimator
 // table; VeXact K1/K3), truncated IS weight w = min(r, C) with a clip flag
 // ("Train-Inference Consistency", section 4).  Per sequence: means over the
-// valid tokens and the geometric-mean-ratio rejection flag (VeXact
+// valid tokens, the geometric-mean-ratio rejection flag (VeXact
 // compensation table, r_corr-based sequence rejection; exp(mean delta) is
-// the geometric mean of r, tested in the log domain).  Per batch: token
+// the geometric mean of r, tested in the log domain) and its K3 form (mean
+// k3 above a bound, the srs-k3 rows of the same table).  Per batch: token
 // means and the mean of per-sequence means ("RL: Training Inference
 // Mismatch", monitoring flow), and the is_* ratios named in
 // "Train-Inference Consistency", section 5.
@@ -52,7 +53,7 @@ static_assert(sizeof(SubPartial) == 64, "four 16-byte quarters");
 struct alignas(16) BatchAcc {
     double sd, sk2, sk3, sw, sabs, maxabs;           // token sums
     double md, mk1, mk2, mk3;                        // sums of sequence means
-    int64_t nvalid, nclip, nnan, nonempty, rejected;
+    int64_t nvalid, nclip, nnan, nonempty, rejected, rejected_k3;
 };
 
 struct SubDesc {
@@ -526,14 +527,14 @@ __device__ __forceinline__ void acc_add(BatchAcc& x, const BatchAcc& y) {
     x.maxabs = fmax(x.maxabs, y.maxabs);
     x.md += y.md; x.mk1 += y.mk1; x.mk2 += y.mk2; x.mk3 += y.mk3;
     x.nvalid += y.nvalid; x.nclip += y.nclip; x.nnan += y.nnan;
-    x.nonempty += y.nonempty; x.rejected += y.rejected;
+    x.nonempty += y.nonempty; x.rejected += y.rejected; x.rejected_k3 += y.rejected_k3;
 }
 
 __device__ __forceinline__ BatchAcc acc_zero() {
     BatchAcc a;
     a.sd = a.sk2 = a.sk3 = a.sw = a.sabs = a.maxabs = 0;
     a.md = a.mk1 = a.mk2 = a.mk3 = 0;
-    a.nvalid = a.nclip = a.nnan = a.nonempty = a.rejected = 0;
+    a.nvalid = a.nclip = a.nnan = a.nonempty = a.rejected = a.rejected_k3 = 0;
     return a;
 }
 
@@ -548,7 +549,7 @@ __device__ void block_tree(BatchAcc* buf) {
 struct SeqOut {
     int32_t *n_valid, *n_clipped, *n_nan;
     double *mean_delta, *mean_k1, *mean_k2, *mean_k3, *mean_tis_w;
-    uint8_t* reject;
+    uint8_t *reject, *reject_k3;
 };
 
 __global__ void __launch_bounds__(kFinBlock)
@@ -580,6 +581,7 @@ seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_
         const double mk3 = nvalid ? sk3 / nv : 0.0;
         const double mw = nvalid ? sw / nv : 0.0;
         const bool rej = nvalid > 0 && (md < prm.seq_lo || md > prm.seq_hi);
+        const bool rej_k3 = nvalid > 0 && mk3 > prm.seq_k3_hi;   // K3 form
         if (so.n_valid) so.n_valid[j] = (int32_t)nvalid;
         if (so.n_clipped) so.n_clipped[j] = (int32_t)nclip;
         if (so.n_nan) so.n_nan[j] = (int32_t)nnan;
@@ -589,12 +591,14 @@ seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_
         if (so.mean_k3) so.mean_k3[j] = mk3;
         if (so.mean_tis_w) so.mean_tis_w[j] = mw;
         if (so.reject) so.reject[j] = rej ? 1 : 0;
+        if (so.reject_k3) so.reject_k3[j] = rej_k3 ? 1 : 0;
         c.sd = sd; c.sk2 = sk2; c.sk3 = sk3; c.sw = sw; c.sabs = sabs; c.maxabs = mx;
         c.nvalid = nvalid; c.nclip = nclip; c.nnan = nnan;
         if (nvalid > 0) {
             c.md = md; c.mk1 = mk1; c.mk2 = mk2; c.mk3 = mk3;
             c.nonempty = 1;
             c.rejected = rej ? 1 : 0;
+            c.rejected_k3 = rej_k3 ? 1 : 0;
         }
     }
     // this block's slice of the streaming waves' sum and maximum of |delta|
@@ -645,6 +649,8 @@ batch_finalize_kernel(const BatchAcc* __restrict__ blk, int64_t nblk, double* __
         out[16] = (double)a.nclip;
         out[17] = ns;
         out[18] = (double)a.rejected;
+        out[19] = dv((double)a.rejected_k3, ns);  // TIM_B_REJECT_K3_FRAC
+        out[20] = (double)a.rejected_k3;
     }
 }
 
@@ -699,7 +705,7 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
     const bool streamed = p.s > 0 && p.n > 0;
     TokOut to{tok.delta, tok.ratio, tok.k1, tok.k2, tok.k3, tok.tis_w, tok.clipped};
     SeqOut so{seq.n_valid, seq.n_clipped, seq.n_nan, seq.mean_delta, seq.mean_k1,
-              seq.mean_k2, seq.mean_k3, seq.mean_tis_w, seq.reject};
+              seq.mean_k2, seq.mean_k3, seq.mean_tis_w, seq.reject, seq.reject_k3};
     if (p.s > 0) {
         hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
                            cu, p.n, p.s, bsum);

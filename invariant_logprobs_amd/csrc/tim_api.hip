@@ -74,7 +74,7 @@ int tim_mismatch_stats(const float* logp_train, const float* logp_rollout, const
                        void* workspace, size_t workspace_bytes, void* stream) {
     if (n < 0 || s < 0 || !p) return TIM_EINVAL;
     if (!(p->tis_clip_c > 0.0) || !isfinite(p->tis_clip_c)) return TIM_EINVAL;
-    if (!(p->seq_lo <= p->seq_hi)) return TIM_EINVAL;
+    if (!(p->seq_lo <= p->seq_hi) || isnan(p->seq_k3_hi)) return TIM_EINVAL;
     if (n > 0 && s < 1) return TIM_EINVAL;
     if (n == 0 && s == 0) return TIM_OK;
     if (n > 0 && (!logp_train || !logp_rollout)) return TIM_EINVAL;
@@ -89,13 +89,52 @@ int tim_mismatch_stats(const float* logp_train, const float* logp_rollout, const
     prm.log_c = log(p->tis_clip_c);
     prm.seq_lo = p->seq_lo;
     prm.seq_hi = p->seq_hi;
+    prm.seq_k3_hi = p->seq_k3_hi;
     tim::TokenOutPtrs to{};
     if (tok) to = {tok->delta, tok->ratio, tok->k1, tok->k2, tok->k3, tok->tis_w, tok->clipped};
     tim::SeqOutPtrs so{};
     if (seq) so = {seq->n_valid, seq->n_clipped, seq->n_nan, seq->mean_delta, seq->mean_k1,
-                   seq->mean_k2, seq->mean_k3, seq->mean_tis_w, seq->reject};
+                   seq->mean_k2, seq->mean_k3, seq->mean_tis_w, seq->reject, seq->reject_k3};
     if (tim::launch_mismatch_stats(plan, logp_train, logp_rollout, mask, cu_seqlens, prm, to, so,
                                    batch, workspace, (hipStream_t)stream) != hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
+size_t tim_extras_workspace_bytes(int64_t n) {
+    tim::ExtrasPlan p;
+    if (!tim::make_extras_plan(n, &p)) return 0;
+    return p.total_bytes;
+}
+
+int tim_mismatch_extras(const float* logp_train, const float* logp_rollout, const uint8_t* mask,
+                        int64_t n, const tim_extras_params* p, double* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    static_assert(TIM_X_MAX_Q == tim::kXMaxQ && TIM_X_NFIELDS == tim::kXOutFields &&
+                      TIM_X_RATIO_Q == tim::kXOutRatioQ && TIM_X_ABS_Q == tim::kXOutAbsQ,
+                  "extras layout");
+    if (n < 0 || !p || isnan(p->tok_tau)) return TIM_EINVAL;
+    if (p->n_ratio_q < 0 || p->n_abs_q < 0 || p->n_ratio_q + p->n_abs_q > TIM_X_MAX_Q)
+        return TIM_EINVAL;
+    for (int i = 0; i < p->n_ratio_q; ++i)
+        if (!(p->ratio_q[i] >= 0.0 && p->ratio_q[i] <= 1.0)) return TIM_EINVAL;
+    for (int i = 0; i < p->n_abs_q; ++i)
+        if (!(p->abs_q[i] >= 0.0 && p->abs_q[i] <= 1.0)) return TIM_EINVAL;
+    if (n > 0 && (!logp_train || !logp_rollout)) return TIM_EINVAL;
+    tim::ExtrasPlan plan;
+    if (!tim::make_extras_plan(n, &plan)) return TIM_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < plan.total_bytes) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+    tim::XParamsDev prm{};
+    prm.tok_tau = p->tok_tau;
+    prm.nrq = p->n_ratio_q;
+    prm.naq = p->n_abs_q;
+    for (int i = 0; i < tim::kXMaxQ; ++i) {
+        prm.rq[i] = i < p->n_ratio_q ? p->ratio_q[i] : 0.0;
+        prm.aq[i] = i < p->n_abs_q ? p->abs_q[i] : 0.0;
+    }
+    if (tim::launch_mismatch_extras(plan, logp_train, logp_rollout, mask, prm, out, workspace,
+                                    (hipStream_t)stream) != hipSuccess)
         return TIM_EHIP;
     return TIM_OK;
 }

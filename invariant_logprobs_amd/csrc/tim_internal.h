@@ -57,7 +57,7 @@ hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const void
 constexpr int kSubChunk = 1024;
 
 struct StatsParamsDev {
-    double clip_c, log_c, seq_lo, seq_hi;
+    double clip_c, log_c, seq_lo, seq_hi, seq_k3_hi;
 };
 
 // Workspace layout of tim_mismatch_stats (offsets 256-byte aligned): scan
@@ -82,7 +82,7 @@ struct TokenOutPtrs {
 struct SeqOutPtrs {
     int32_t *n_valid, *n_clipped, *n_nan;
     double *mean_delta, *mean_k1, *mean_k2, *mean_k3, *mean_tis_w;
-    uint8_t* reject;
+    uint8_t *reject, *reject_k3;
 };
 
 hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const float* lr,
@@ -90,6 +90,38 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
                                  const StatsParamsDev& prm, const TokenOutPtrs& tok,
                                  const SeqOutPtrs& seq, double* batch, void* workspace,
                                  hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Extra mismatch metrics (extras.hip)
+// ---------------------------------------------------------------------------
+
+constexpr int kXMaxQ = 4;          // probabilities per call, both kinds together
+constexpr int kXPasses = 6;        // radix-select passes over the tokens
+constexpr int kXMaxBlocks = 512;   // blocks of a pass
+
+// Output vector layout (the TIM_X_* indices of tim.h).
+constexpr int kXOutNValid = 0, kXOutNExtreme = 1, kXOutExtremeFrac = 2, kXOutMeanRelDiff = 3,
+              kXOutRatioQ = 4, kXOutAbsQ = 8, kXOutFields = 12;
+
+struct XParamsDev {
+    double tok_tau;
+    int32_t nrq, naq;      // ratio and |delta| probabilities; nrq + naq <= kXMaxQ
+    double rq[kXMaxQ], aq[kXMaxQ];
+};
+
+// Workspace layout of tim_mismatch_extras (offsets 256-byte aligned): the
+// select state, per-block histograms and key ranges, the summed histogram
+// and per-block partial sums.  nblk depends on n only.
+struct ExtrasPlan {
+    int64_t n, nblk;
+    size_t state_off, bhist_off, bmm_off, ghist_off, part_off, total_bytes;
+};
+
+bool make_extras_plan(int64_t n, ExtrasPlan* p);
+
+hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const float* lr,
+                                  const uint8_t* mask, const XParamsDev& prm, double* out,
+                                  void* workspace, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

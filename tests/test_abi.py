@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == sorted(tim.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.tim_abi_version() == 1
+    assert lib.tim_abi_version() == tim.ABI_VERSION == 2
 
 
 def test_status_strings(lib):
@@ -89,8 +89,8 @@ def test_logprob_argument_errors(lib):
 
 
 def _stats(lib, n=10, s=2, c=2.0, lo=-0.01, hi=0.01, lt=FAKE, lr=FAKE, cu=FAKE, ws=FAKE,
-           wsb=1 << 30, params=True):
-    p = tim._StatsParams(c, lo, hi)
+           wsb=1 << 30, params=True, k3=float("inf")):
+    p = tim._StatsParams(c, lo, hi, k3)
     return lib.tim_mismatch_stats(lt, lr, None, cu, n, s, ctypes.byref(p) if params else None,
                                   None, None, None, ws, wsb, None)
 
@@ -106,6 +106,7 @@ def test_stats_argument_errors(lib):
     assert _stats(lib, c=float("nan")) == tim.TIM_EINVAL
     assert _stats(lib, lo=0.1, hi=0.0) == tim.TIM_EINVAL
     assert _stats(lib, lo=float("nan")) == tim.TIM_EINVAL
+    assert _stats(lib, k3=float("nan")) == tim.TIM_EINVAL
     assert _stats(lib, lt=None) == tim.TIM_EINVAL
     assert _stats(lib, cu=None) == tim.TIM_EINVAL
     assert _stats(lib, ws=None) == tim.TIM_EWORKSPACE
@@ -123,3 +124,40 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         tim.tim_mismatch_stats(torch.zeros(4), torch.zeros(4), None,
                                torch.tensor([0, 4], dtype=torch.int32))
+
+
+def _extras(lib, n=10, tau=0.1, rq=(0.5,), aq=(0.95,), lt=FAKE, lr=FAKE, ws=FAKE, wsb=1 << 30,
+            params=True, nrq=None, naq=None):
+    q = lambda v: (ctypes.c_double * tim.X_MAX_Q)(*(list(v) + [0.0] * (tim.X_MAX_Q - len(v))))
+    p = tim._ExtrasParams(tau, len(rq) if nrq is None else nrq, len(aq) if naq is None else naq,
+                          q(rq), q(aq))
+    return lib.tim_mismatch_extras(lt, lr, None, n, ctypes.byref(p) if params else None, None,
+                                   ws, wsb, None)
+
+
+def test_extras_workspace_and_argument_errors(lib):
+    # the workspace depends on n only and grows with the number of pass blocks
+    small, big = lib.tim_extras_workspace_bytes(100), lib.tim_extras_workspace_bytes(1 << 28)
+    assert 0 < small < big < (64 << 20)
+    assert lib.tim_extras_workspace_bytes(0) > 0
+    assert lib.tim_extras_workspace_bytes(-1) == 0
+    assert lib.tim_extras_workspace_bytes(1 << 31) == 0
+    assert _extras(lib, n=-1) == tim.TIM_EINVAL
+    assert _extras(lib, params=False) == tim.TIM_EINVAL
+    assert _extras(lib, tau=float("nan")) == tim.TIM_EINVAL
+    assert _extras(lib, rq=(1.5,)) == tim.TIM_EINVAL
+    assert _extras(lib, aq=(-0.1,)) == tim.TIM_EINVAL
+    assert _extras(lib, rq=(float("nan"),)) == tim.TIM_EINVAL
+    assert _extras(lib, rq=(0.1, 0.2, 0.3), aq=(0.4, 0.5)) == tim.TIM_EINVAL   # 5 > 4
+    assert _extras(lib, nrq=-1) == tim.TIM_EINVAL
+    assert _extras(lib, lt=None) == tim.TIM_EINVAL
+    assert _extras(lib, ws=None) == tim.TIM_EWORKSPACE
+    assert _extras(lib, wsb=8) == tim.TIM_EWORKSPACE
+    assert _extras(lib, ws=FAKE + 64) == tim.TIM_EUNSUPPORTED
+    assert _extras(lib, n=1 << 31) == tim.TIM_EUNSUPPORTED
+
+
+def test_binding_extras_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tim.tim_mismatch_extras(torch.zeros(4), torch.zeros(4), None, tok_tau=0.1)

@@ -62,6 +62,13 @@ class Spec:
     clip_c: float = 2.0
     seq_lo: float = -0.01
     seq_hi: float = 0.01
+    # K3-form rejection bound on a sequence's mean k3, and the extreme-token
+    # threshold on |delta|; the pages give neither value.  5e-5 is the k3 of
+    # a constant log-ratio of 0.01 to leading order (0.01^2 / 2), the K3
+    # counterpart of the +-0.01 window; 0.1 flags the injected spikes and not
+    # the per-token noise.
+    seq_k3_hi: float = 5e-5
+    tok_tau: float = 0.1
     seed: int = 0
     gen_on_cpu: bool = True
     desc: str = ""
