@@ -8,9 +8,10 @@ Qwen3-8B-shaped workload: N=8192 tokens in 16 sequences of 512, D=4096,
 V=151936, bf16 inputs, fp32 accumulation.
 
 Prints ONE JSON line on stdout.  Diagnostics go to stderr.  Also reported:
-the stats pass on 2^28 tokens (HBM bandwidth), the price of batch invariance
-against the free schedule, and the fp64 oracle timed on a bounded sample on
-the host cores.
+the stats pass on 2^28 tokens (HBM bandwidth), the extra metrics (extreme
+rate, relative difference, ratio quantiles, |delta| p95) on the workload and
+on 2^28 tokens, the price of batch invariance against the free schedule, and
+the fp64 oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -75,6 +76,8 @@ def main():
                          "WRITE_SIZE) of --profile-pass runs into the traffic summary and exit")
     ap.add_argument("--stats-scale-only", action="store_true",
                     help="run only the stats pass at 2^stats-log2 tokens (for a kernel trace)")
+    ap.add_argument("--extras-scale-only", action="store_true",
+                    help="run only the extra metrics at 2^stats-log2 tokens (for a kernel trace)")
     ap.add_argument("--traffic-out", default=PMC_SUMMARY)
     ap.add_argument("--traffic-command", default="",
                     help="the commands that made the CSV files, recorded in the summary")
@@ -105,6 +108,11 @@ def main():
         copy_calibration(torch)
     if args.stats_scale_only:
         print(json.dumps(stats_scale(tim, workloads, torch, np, args.stats_log2)), flush=True)
+        return
+    if args.extras_scale_only:
+        tau = workloads.SPECS["qwen3_8b"].tok_tau
+        print(json.dumps(extras_scale(tim, workloads, torch, np, args.stats_log2, tau)),
+              flush=True)
         return
     name = "qwen3_8b"
     log(f"generating workload {name}")
@@ -175,6 +183,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["extras"] = extras_measure(tim, workloads, wl, torch, np, args.stats_log2)
         out["stats_scale"] = stats_scale(tim, workloads, torch, np, args.stats_log2)
         out["invariance_cost"] = invariance_cost(tim, wl, torch, np)
 
@@ -188,6 +197,7 @@ COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration 
 COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
 LMHEAD_KERNEL = "lmhead_partials_kernel<true>"
 STATS_KERNEL = "stats_stream_kernel"
+EXTRAS_KERNEL = "xsel_pass_kernel"
 
 
 def copy_calibration(torch):
@@ -203,8 +213,8 @@ def copy_calibration(torch):
     torch.cuda.empty_cache()
 
 
-def _counter_means(path, counter):
-    """Mean Counter_Value (KiB) per dispatch for each kernel name of interest."""
+def _counter_values(path, counter):
+    """Counter_Value (KiB) of every dispatch, in order, per kernel of interest."""
     import csv
     vals = {}
     with open(path, newline="") as f:
@@ -212,11 +222,16 @@ def _counter_means(path, counter):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            for key in (COPY_KERNEL, LMHEAD_KERNEL, STATS_KERNEL):
+            for key in (COPY_KERNEL, LMHEAD_KERNEL, STATS_KERNEL, EXTRAS_KERNEL):
                 if key in name:
                     # one row per dispatch (values already summed over the chip)
                     vals.setdefault(key, []).append(float(row["Counter_Value"]))
-    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+    return vals
+
+
+def _counter_means(path, counter):
+    """Mean Counter_Value (KiB) per dispatch for each kernel name of interest."""
+    return {k: (sum(v) / len(v), len(v)) for k, v in _counter_values(path, counter).items()}
 
 
 def write_traffic(fetch_csv, write_csv, out_path, command):
@@ -243,6 +258,15 @@ def write_traffic(fetch_csv, write_csv, out_path, command):
                             "fetch_bytes": fr[key][0] * 1024 / rf,
                             "write_bytes": wr[key][0] * 1024 / wf,
                             "dispatches": fr[key][1]}
+    # the radix-select pass: passes after the last target is resolved return
+    # at once, so the bytes of every dispatch are kept, in launch order
+    fv = _counter_values(fetch_csv, "FETCH_SIZE").get(EXTRAS_KERNEL)
+    wv = _counter_values(write_csv, "WRITE_SIZE").get(EXTRAS_KERNEL)
+    if fv and wv:
+        summary["extras_pass"] = {"kernel": EXTRAS_KERNEL,
+                                  "fetch_bytes_per_dispatch": [x * 1024 / rf for x in fv],
+                                  "write_bytes_per_dispatch": [x * 1024 / wf for x in wv],
+                                  "dispatches": len(fv)}
     if "lmhead" in summary:
         summary["kernel"] = LMHEAD_KERNEL
         summary["kernel_source_sha256_16"] = source_digest(LMHEAD_SRC)
@@ -289,6 +313,49 @@ def stats_scale(tim, workloads, torch, np, log2n):
     return {"tokens": n, "sequences": s, "ms": ms, "algorithmic_bytes": algo,
             "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
             "tokens_per_s": n / (ms / 1e3)}
+
+
+XQ_RATIO = (0.01, 0.5, 0.99)   # ratio quantiles of the mismatch metric table
+XQ_ABS = (0.95,)                # p95 of |delta|
+
+
+def extras_measure(tim, workloads, wl, torch, np, log2n):
+    """tim_mismatch_extras (extreme rate, mean relative difference, ratio
+    quantiles, |delta| p95) on the bench workload and on 2^log2n tokens."""
+    sp = wl.spec
+    ws = torch.empty(tim.extras_workspace_bytes(sp.n), dtype=torch.uint8, device="cuda")
+    fn = lambda: tim.tim_mismatch_extras(wl.logp_sampler, wl.logp_rollout, wl.mask,
+                                         tok_tau=sp.tok_tau, ratio_q=XQ_RATIO, abs_q=XQ_ABS,
+                                         workspace=ws)
+    us_small = time_calls(fn, torch, np, reps=20) * 1e3
+    log(f"extras: {us_small:.1f} us at N={sp.n}")
+    out = extras_scale(tim, workloads, torch, np, log2n, sp.tok_tau)
+    out.update({"workload_us": us_small, "workload_tokens": sp.n})
+    return out
+
+
+def extras_scale(tim, workloads, torch, np, log2n, tok_tau):
+    """The extra metrics on 2^log2n tokens of the statistics workload.
+    Algorithmic bytes are the inputs read once (9 B per token); the radix
+    select reads them once per pass, so its fraction of that bound shows the
+    price of the passes."""
+    n = 1 << log2n
+    lt, lr, mask, _ = workloads.stats_scale(n, seed=7, device="cuda")
+    wsl = torch.empty(tim.extras_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    fl = lambda: tim.tim_mismatch_extras(lt, lr, mask, tok_tau=tok_tau, ratio_q=XQ_RATIO,
+                                         abs_q=XQ_ABS, workspace=wsl)
+    ms = time_calls(fl, torch, np, reps=5)
+    res = tim.extras_dict(fl(), len(XQ_RATIO), len(XQ_ABS))
+    algo = 9 * n + 8 * len(tim.EXTRAS_FIELDS)
+    gbs = algo / (ms / 1e3) / 1e9
+    log(f"extras 2^{log2n}: {ms:.3f} ms, {gbs:.0f} GB/s of one input read "
+        f"({gbs / PEAK_HBM_GBS:.1%}); ratio q {res['ratio_q']}, |d| p95 {res['abs_q'][0]:.4g}, "
+        f"extreme {res['extreme_frac']:.3e}")
+    del lt, lr, mask, wsl
+    torch.cuda.empty_cache()
+    return {"tokens": n, "ms": ms, "algorithmic_bytes": algo, "achieved_GBs": gbs,
+            "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS, "ratio_q": list(XQ_RATIO),
+            "abs_q": list(XQ_ABS), "tok_tau": tok_tau}
 
 
 def invariance_cost(tim, wl, torch, np):

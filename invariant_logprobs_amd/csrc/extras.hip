@@ -18,25 +18,27 @@
 //
 //   pass 0: top 13 bits; passes 1-4: 11 bits each; pass 5: the last 7.
 //
-//   1. xsel_init: targets (a lower and an upper order statistic per
-//      probability) and the root slots, one per key kind.
-//   2. per pass:
-//      xsel_pass    every block histograms its share of the tokens in LDS,
-//                   one histogram per slot (a distinct (kind, prefix)), and
-//                   writes it with plain stores, with the minimum and
-//                   maximum key it saw per slot.  Pass 0 also folds the
-//                   extreme count and the relative difference of its
-//                   tokens, in a fixed order, into a block partial.
-//      xsel_reduce  sums the block histograms bin by bin (integers: the
-//                   order does not matter).
-//      xsel_select  one block: pass 0 turns probabilities into ranks; every
-//                   pass moves each unresolved target into the bin that
-//                   holds its rank.  A slot whose minimum equals its maximum
-//                   resolves its targets at once (ties, zero mismatch).
-//                   When every target is resolved the later passes return
-//                   at their first instruction.
-//   3. xsel_final: folds the block partials in a fixed tree and writes the
-//      outputs.
+// A slot is a distinct (kind, prefix) that some unresolved target lies in.
+// After each pass a select step moves every unresolved target into the bin
+// that holds its rank; a slot whose smallest and largest key are equal
+// resolves its targets at once (ties, zero mismatch).  Pass 0 also folds
+// the extreme count and the relative difference in a fixed order.
+//
+// Up to kXFusedMax tokens, one block does everything (xsel_fused): the
+// tokens' keys and every histogram live in LDS.  Above,
+// each pass is three launches:
+//
+//   xsel_pass    every block histograms its share in LDS and writes it with
+//                plain stores, with its key range per slot.  Pass 1 also
+//                copies the keys that lie in any slot into a region of the
+//                workspace owned by the block (capped; an overflow is
+//                flagged), and passes 2-5 read those regions instead of the
+//                9 bytes per token of the inputs.
+//   xsel_reduce  sums the block histograms bin by bin (integers: the order
+//                does not matter).
+//   xsel_select  one block runs the select step.
+//
+// Once every target is resolved the remaining launches return at once.
 //
 // Every step is exact integer work except the per-token relative
 // difference (one fp64 division, as the definition states) and its sum,
@@ -50,12 +52,15 @@
 namespace tim {
 namespace {
 
-constexpr int kXThreads = 1024;          // threads per pass block
+constexpr int kXThreads = 1024;          // threads per block of the pass, select and fused kernels
 constexpr int kXUnroll = 8;              // tokens per thread per loop trip
 constexpr int kXMaxTargets = 2 * kXMaxQ;
 constexpr int kXMaxSlots = kXMaxTargets;
 constexpr int kXLdsBins = 16384;         // 2 slots x 2^13 or 8 slots x 2^11
-constexpr int kXReduceThreads = 256;
+constexpr int kXPerThreadFused = kXFusedMax / kXThreads;
+constexpr int kXReduceBins = 64;         // bins per reduce block
+constexpr int kXReduceGroups = 16;       // pass-block groups per bin
+constexpr int kXReduceThreads = kXReduceBins * kXReduceGroups;
 constexpr int kXFinThreads = 256;
 
 __host__ __device__ constexpr int digit_bits(int pass) {
@@ -67,6 +72,7 @@ __host__ __device__ constexpr int bits_before(int pass) {
 static_assert(bits_before(kXPasses - 1) + digit_bits(kXPasses - 1) == 64, "64 key bits");
 static_assert(2 * (1 << digit_bits(0)) <= kXLdsBins, "pass 0: one slot per key kind");
 static_assert(kXMaxSlots * (1 << digit_bits(1)) <= kXLdsBins, "later passes: one slot per target");
+static_assert(kXFusedMax % kXThreads == 0, "whole tokens per thread in the fused kernel");
 
 struct XTarget {
     uint64_t prefix;   // key bits fixed so far (the top bits_before(pass) bits)
@@ -101,8 +107,10 @@ __device__ __forceinline__ uint64_t key_delta(double d) {
     const uint64_t u = __builtin_bit_cast(uint64_t, d);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
-__device__ __forceinline__ uint64_t key_abs(double d) {
-    return (__builtin_bit_cast(uint64_t, d) & 0x7FFFFFFFFFFFFFFFull) << 1;
+// |delta|'s key from delta's key: the bit pattern of |delta| shifted left
+__device__ __forceinline__ uint64_t key_abs_of(uint64_t k0) {
+    const uint64_t u = (k0 >> 63) ? k0 : ~k0;       // |delta|'s bits with the top bit set
+    return u << 1;
 }
 __device__ __forceinline__ double value_of(uint64_t k, int kind) {
     uint64_t u;
@@ -111,18 +119,23 @@ __device__ __forceinline__ double value_of(uint64_t k, int kind) {
     return __builtin_bit_cast(double, u);
 }
 
-// Position q (m - 1) of probability q among m >= 1 sorted values: lower and
-// upper index and the interpolation weight.
-// Each operation is rounded on its own: no fused multiply-add may join the
+struct QPos {
+    uint64_t lo, hi;   // the two order statistics' ranks
+    double frac;       // interpolation weight
+};
+
+// Position q (m - 1) of probability q among m >= 1 sorted values.  Each
+// operation is rounded on its own: no fused multiply-add may join the
 // product and the subtraction.
-__device__ __attribute__((noinline)) void quantile_pos(double q, uint64_t m, uint64_t* lo,
-                                                        uint64_t* hi, double* frac) {
+__device__ __attribute__((noinline)) QPos quantile_pos(double q, uint64_t m) {
 #pragma clang fp contract(off)
     const double pos = q * (double)(m - 1);
     const double fl = floor(pos);
-    *lo = (uint64_t)fl;
-    *hi = *lo + 1 < m ? *lo + 1 : *lo;
-    *frac = pos - fl;
+    QPos r;
+    r.lo = (uint64_t)fl;
+    r.hi = r.lo + 1 < m ? r.lo + 1 : r.lo;
+    r.frac = pos - fl;
+    return r;
 }
 
 // a + (b - a) f with each of the three operations rounded on its own (no
@@ -162,13 +175,11 @@ __device__ uint64_t block_excl_scan(uint64_t x, uint64_t* sh) {
     return r;
 }
 
-__global__ void __launch_bounds__(64)
-xsel_init_kernel(XParamsDev prm, XState* __restrict__ st) {
-    if (threadIdx.x != 0) return;
-    const int ntgt = 2 * (prm.nrq + prm.naq);
-    // one root slot per key kind present: delta first, then |delta|
+// Targets (a lower and an upper order statistic per probability, delta's
+// first) and one root slot per key kind present.  One thread.
+__device__ void init_state(XState* st, const XParamsDev& prm) {
     const int root_abs = prm.nrq > 0 ? 1 : 0;
-    st->ntgt = ntgt;
+    st->ntgt = 2 * (prm.nrq + prm.naq);
     st->nslots = (prm.nrq > 0 ? 1 : 0) + (prm.naq > 0 ? 1 : 0);
     st->all_done = 0;
     st->pad = 0;
@@ -181,78 +192,66 @@ xsel_init_kernel(XParamsDev prm, XState* __restrict__ st) {
     if (prm.naq > 0) st->slot[root_abs].kind = 1;
 }
 
-// One histogram pass.  Block b takes tokens b*1024 + tid + j*stride, j >= 0,
-// stride = grid * 1024, kXUnroll of them per loop trip.
-template <bool kMask>
-__global__ void __launch_bounds__(kXThreads)
-xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
-                 const uint8_t* __restrict__ mask, uint32_t n, int pass, XParamsDev prm,
-                 const XState* __restrict__ st, uint32_t* __restrict__ bhist,
-                 ulonglong2* __restrict__ bmm, XPart* __restrict__ part) {
-    __shared__ uint32_t hist[kXLdsBins];
-    __shared__ unsigned long long smn[kXMaxSlots], smx[kXMaxSlots];
-    __shared__ double rsh[kXThreads];
-    const bool first = pass == 0;
-    if (!first && st->all_done) return;
-    const int nslots = st->nslots;
-    const int bits = digit_bits(pass), before = bits_before(pass);
-    const int shift = 64 - before - bits;
-    const uint64_t dmask = (1ull << bits) - 1;
-    const int tid = threadIdx.x;
-    const int nbins = nslots << bits;
-    for (int i = tid; i < nbins; i += kXThreads) hist[i] = 0;
-    if (tid < kXMaxSlots) { smn[tid] = ~0ull; smx[tid] = 0ull; }
-    uint64_t spre[kXMaxSlots];
-    int skind[kXMaxSlots];
+// Pass 0, once the number of valid tokens is known: each probability's two
+// ranks.  One thread.
+__device__ void set_ranks(XState& st, uint64_t nv, const XParamsDev& prm) {
+    st.nvalid = nv;
+    for (int t = 0; t < st.ntgt; t += 2) {
+        const int i = t / 2;
+        const double q = i < prm.nrq ? prm.rq[i] : prm.aq[i - prm.nrq];
+        const QPos qp = nv > 0 ? quantile_pos(q, nv) : QPos{0, 0, 0.0};
+        st.tgt[t].rank = qp.lo;
+        st.tgt[t + 1].rank = qp.hi;
+        if (nv == 0) st.tgt[t].resolved = st.tgt[t + 1].resolved = 1;
+    }
+    if (nv == 0 || st.ntgt == 0) st.all_done = 1;
+}
+
+// The slots of a pass, in registers (the same values in every lane).
+struct Slots {
+    uint64_t pre[kXMaxSlots];
+    int kind[kXMaxSlots];
+    int n;
+};
+
+__device__ __forceinline__ void load_slots(Slots& sl, const XState* st) {
+    sl.n = st->nslots;
 #pragma unroll
     for (int s = 0; s < kXMaxSlots; ++s) {
-        spre[s] = s < nslots ? st->slot[s].prefix : 0;
-        skind[s] = s < nslots ? st->slot[s].kind : 0;
+        sl.pre[s] = s < sl.n ? st->slot[s].prefix : 0;
+        sl.kind[s] = s < sl.n ? st->slot[s].kind : 0;
     }
-    __syncthreads();
+}
 
-    uint64_t lmn[kXMaxSlots], lmx[kXMaxSlots];
+// Counts a token's keys in every slot whose prefix they share; returns
+// whether any slot took it.
+__device__ __forceinline__ bool visit(uint64_t k0, const Slots& sl, int before, int bits,
+                                      uint32_t* hist, uint64_t (&lmn)[kXMaxSlots],
+                                      uint64_t (&lmx)[kXMaxSlots]) {
+    const uint64_t k1 = key_abs_of(k0);
+    const int shift = 64 - before - bits;
+    const uint64_t dmask = (1ull << bits) - 1;
+    bool any = false;
 #pragma unroll
-    for (int s = 0; s < kXMaxSlots; ++s) { lmn[s] = ~0ull; lmx[s] = 0; }
-    double rel = 0.0;
-    uint32_t next = 0, nval = 0;
-    const uint32_t stride = gridDim.x * kXThreads;
-    for (uint32_t base = blockIdx.x * kXThreads + tid; base < n; base += kXUnroll * stride) {
-        float x[kXUnroll], y[kXUnroll];
-        uint32_t m[kXUnroll];
-#pragma unroll
-        for (int j = 0; j < kXUnroll; ++j) {
-            const uint64_t t64 = (uint64_t)base + (uint64_t)j * stride;
-            const uint32_t t = t64 < n ? (uint32_t)t64 : base;    // base < n: in bounds
-            x[j] = lt[t];
-            y[j] = lr[t];
-            m[j] = (t64 < n) && (kMask ? mask[t] != 0 : true);
-        }
-#pragma unroll
-        for (int j = 0; j < kXUnroll; ++j) {
-            const double d = (double)x[j] - (double)y[j];
-            const bool valid = m[j] && isfinite(d);
-            if (!valid) continue;
-            if (first) {
-                rel += fabs(d) / (fabs((double)x[j]) + 1e-8);
-                next += fabs(d) > prm.tok_tau ? 1u : 0u;
-                ++nval;
-            }
-            const uint64_t k0 = key_delta(d), k1 = key_abs(d);
-#pragma unroll
-            for (int s = 0; s < kXMaxSlots; ++s) {
-                if (s >= nslots) break;
-                const uint64_t k = skind[s] ? k1 : k0;
-                const bool match = before == 0 || (k >> (64 - before)) == spre[s];
-                if (match) {
-                    atomicAdd(&hist[(s << bits) | (uint32_t)((k >> shift) & dmask)], 1u);
-                    lmn[s] = k < lmn[s] ? k : lmn[s];
-                    lmx[s] = k > lmx[s] ? k : lmx[s];
-                }
-            }
+    for (int s = 0; s < kXMaxSlots; ++s) {
+        if (s >= sl.n) break;
+        const uint64_t k = sl.kind[s] ? k1 : k0;
+        const bool match = before == 0 || (k >> (64 - before)) == sl.pre[s];
+        if (match) {
+            atomicAdd(&hist[(s << bits) | (uint32_t)((k >> shift) & dmask)], 1u);
+            lmn[s] = k < lmn[s] ? k : lmn[s];
+            lmx[s] = k > lmx[s] ? k : lmx[s];
+            any = true;
         }
     }
-    // per-slot minimum and maximum: wave butterflies, then one LDS atomic per wave
+    return any;
+}
+
+// Per-slot minimum and maximum into LDS: wave butterflies, then one LDS
+// atomic per wave.  Every lane of the wave takes part.
+__device__ __forceinline__ void flush_range(int nslots, uint64_t (&lmn)[kXMaxSlots],
+                                            uint64_t (&lmx)[kXMaxSlots],
+                                            unsigned long long* smn, unsigned long long* smx) {
 #pragma unroll
     for (int s = 0; s < kXMaxSlots; ++s) {
         if (s >= nslots) break;
@@ -262,11 +261,310 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
             a = a2 < a ? a2 : a;
             b = b2 > b ? b2 : b;
         }
-        if ((tid & 63) == 0) {
+        if ((threadIdx.x & 63) == 0) {
             atomicMin(&smn[s], (unsigned long long)a);
             atomicMax(&smx[s], (unsigned long long)b);
         }
     }
+}
+
+// One select step over this pass's histograms (slot s at h + (s << bits))
+// and key ranges.  Every thread of a kXThreads block calls it; st is in LDS.
+// Ends with a barrier, st then holds the next pass's slots.
+__device__ void select_step(XState& st, int pass, const uint32_t* h,
+                            const unsigned long long* mn, const unsigned long long* mx,
+                            uint64_t* sh, uint64_t* fdig, uint64_t* frank) {
+    const int tid = threadIdx.x;
+    const int ntgt = st.ntgt, nslots = st.nslots;
+    const int bits = digit_bits(pass), before = bits_before(pass);
+    const int nb = 1 << bits;
+    const int per = nb > kXThreads ? nb / kXThreads : 1;   // bins per thread (<= 8)
+    // a bucket holding one key value resolves its targets at once
+    if (tid == 0) {
+        for (int t = 0; t < ntgt; ++t) {
+            XTarget& g = st.tgt[t];
+            if (!g.resolved && mn[g.slot] == mx[g.slot]) { g.resolved = 1; g.key = mn[g.slot]; }
+        }
+    }
+    __syncthreads();
+    // one scan per slot; every unresolved target of the slot finds its bin in
+    // it (the thread holding that bin records digit and remaining rank)
+    const int b0 = tid * per;
+    for (int s = 0; s < nslots; ++s) {
+        bool used = false;
+        for (int t = 0; t < ntgt; ++t) used |= !st.tgt[t].resolved && st.tgt[t].slot == s;
+        if (!used) continue;                                // uniform: same LDS state
+        const uint32_t* hs = h + ((size_t)s << bits);
+        uint32_t hv[8];
+        uint64_t mine = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            hv[k] = (k < per && b0 + k < nb) ? hs[b0 + k] : 0u;
+            mine += hv[k];
+        }
+        const uint64_t c0 = block_excl_scan<kXThreads>(mine, sh);
+        for (int t = 0; t < ntgt; ++t) {
+            if (st.tgt[t].resolved || st.tgt[t].slot != s) continue;
+            const uint64_t rank = st.tgt[t].rank;
+            uint64_t c = c0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (c <= rank && rank < c + hv[k]) { fdig[t] = (uint64_t)(b0 + k); frank[t] = rank - c; }
+                c += hv[k];
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int t = 0; t < ntgt; ++t) {
+            XTarget& g = st.tgt[t];
+            if (g.resolved) continue;
+            g.prefix = before == 0 ? fdig[t] : ((g.prefix << bits) | fdig[t]);
+            g.rank = frank[t];
+            if (before + bits == 64) { g.resolved = 1; g.key = g.prefix; }
+        }
+        // slots of the next pass: one per distinct (kind, prefix) among the
+        // unresolved targets, in target order
+        int ns = 0;
+        for (int t = 0; t < ntgt; ++t) {
+            XTarget& g = st.tgt[t];
+            if (g.resolved) continue;
+            int k = 0;
+            while (k < ns && !(st.slot[k].kind == g.kind && st.slot[k].prefix == g.prefix)) ++k;
+            if (k == ns) {
+                st.slot[ns].prefix = g.prefix;
+                st.slot[ns].kind = g.kind;
+                ++ns;
+            }
+            g.slot = k;
+        }
+        st.nslots = ns;
+        if (ns == 0) st.all_done = 1;
+    }
+    __syncthreads();
+}
+
+// The output vector.  One thread.
+__device__ void write_outputs(double* out, const XParamsDev& prm, const XState& st, double rel,
+                              uint64_t next, uint64_t nv) {
+    const double dnv = (double)nv;
+    out[kXOutNValid] = dnv;
+    out[kXOutNExtreme] = (double)next;
+    out[kXOutExtremeFrac] = nv ? (double)next / dnv : 0.0;
+    out[kXOutMeanRelDiff] = nv ? rel / dnv : 0.0;
+    for (int i = 0; i < kXMaxQ; ++i) {
+        out[kXOutRatioQ + i] = 0.0;
+        out[kXOutAbsQ + i] = 0.0;
+    }
+    if (nv == 0) return;
+    const int nq = prm.nrq + prm.naq;
+    for (int i = 0; i < nq; ++i) {
+        const bool ratio = i < prm.nrq;
+        const double q = ratio ? prm.rq[i] : prm.aq[i - prm.nrq];
+        const QPos qp = quantile_pos(q, nv);
+        const int kind = ratio ? 0 : 1;
+        double a = value_of(st.tgt[2 * i].key, kind);
+        double b = value_of(st.tgt[2 * i + 1].key, kind);
+        if (ratio) { a = exp(a); b = exp(b); }
+        const double v = interpolate(a, b, qp.frac);
+        if (ratio) out[kXOutRatioQ + i] = v;
+        else out[kXOutAbsQ + i - prm.nrq] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Up to kXFusedMax tokens: one block, keys and histograms in LDS.  Thread
+// tid takes tokens tid + kXThreads j.
+// ---------------------------------------------------------------------------
+
+template <bool kMask>
+__global__ void __launch_bounds__(kXThreads)
+xsel_fused_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
+                  const uint8_t* __restrict__ mask, uint32_t n, XParamsDev prm,
+                  double* __restrict__ out) {
+    __shared__ uint32_t hist[kXLdsBins];
+    // delta's key per token; 0 (the bit pattern of a NaN, which no finite
+    // delta has) marks a token that does not count
+    __shared__ uint64_t keys[kXFusedMax];
+    __shared__ XState st;
+    __shared__ uint64_t sh[kXThreads];
+    __shared__ unsigned long long smn[kXMaxSlots], smx[kXMaxSlots];
+    __shared__ uint64_t fdig[kXMaxTargets], frank[kXMaxTargets];
+    const int tid = threadIdx.x;
+    if (tid == 0) init_state(&st, prm);
+
+    double rel = 0.0;
+    uint32_t next = 0, nval = 0;
+    if (n == 0)                                            // uniform; pointers may be null
+        for (int j = 0; j < kXPerThreadFused; ++j) keys[tid + kXThreads * j] = 0;
+    else
+#pragma unroll
+    for (int j = 0; j < kXPerThreadFused; ++j) {
+        const uint32_t t = (uint32_t)(tid + kXThreads * j);
+        const uint32_t tc = t < n ? t : 0;                 // n >= 1 here: in bounds
+        const float x = lt[tc];
+        const float y = lr[tc];
+        const bool in = t < n && (!kMask || mask[tc] != 0);
+        const double d = (double)x - (double)y;
+        const bool valid = in && isfinite(d);
+        uint64_t k = 0;
+        if (valid) {
+            k = key_delta(d);
+            rel += fabs(d) / (fabs((double)x) + 1e-8);
+            next += fabs(d) > prm.tok_tau ? 1u : 0u;
+            ++nval;
+        }
+        keys[t] = k;
+    }
+    double* dsh = reinterpret_cast<double*>(sh);
+    rel = block_sum<kXThreads>(rel, dsh);
+    const uint64_t next_all = block_sum<kXThreads>((uint64_t)next, sh);
+    const uint64_t nv = block_sum<kXThreads>((uint64_t)nval, sh);
+    if (tid == 0) set_ranks(st, nv, prm);
+    __syncthreads();
+
+    for (int pass = 0; pass < kXPasses; ++pass) {
+        if (st.all_done) break;                             // uniform: read after a barrier
+        const int nslots = st.nslots;
+        const int bits = digit_bits(pass), before = bits_before(pass);
+        const int shift = 64 - before - bits;
+        const uint64_t dmask = (1ull << bits) - 1;
+        for (int i = tid; i < (nslots << bits); i += kXThreads) hist[i] = 0;
+        if (tid < kXMaxSlots) { smn[tid] = ~0ull; smx[tid] = 0ull; }
+        __syncthreads();
+        for (int s = 0; s < nslots; ++s) {
+            const uint64_t pre = st.slot[s].prefix;
+            const int kind = st.slot[s].kind;
+            uint64_t a = ~0ull, b = 0;
+            for (int j = 0; j < kXPerThreadFused; ++j) {
+                const uint64_t k0 = keys[tid + kXThreads * j];
+                const uint64_t k = kind ? key_abs_of(k0) : k0;
+                if (k0 != 0 && (before == 0 || (k >> (64 - before)) == pre)) {
+                    atomicAdd(&hist[(s << bits) | (uint32_t)((k >> shift) & dmask)], 1u);
+                    a = k < a ? k : a;
+                    b = k > b ? k : b;
+                }
+            }
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint64_t a2 = __shfl_xor(a, o), b2 = __shfl_xor(b, o);
+                a = a2 < a ? a2 : a;
+                b = b2 > b ? b2 : b;
+            }
+            if ((tid & 63) == 0) {
+                atomicMin(&smn[s], (unsigned long long)a);
+                atomicMax(&smx[s], (unsigned long long)b);
+            }
+        }
+        __syncthreads();
+        select_step(st, pass, hist, smn, smx, sh, fdig, frank);
+    }
+    if (tid == 0) write_outputs(out, prm, st, rel, next_all, nv);
+}
+
+// ---------------------------------------------------------------------------
+// Above kXFusedMax tokens: pass / reduce / select launches.
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(64)
+xsel_init_kernel(XParamsDev prm, XState* __restrict__ st, uint32_t* __restrict__ cflag) {
+    if (threadIdx.x != 0) return;
+    init_state(st, prm);
+    *cflag = 0;
+}
+
+// One histogram pass.  Passes 0 and 1 (and later passes when the candidate
+// regions overflowed) read the tokens: block b takes tokens b*1024 + tid +
+// j*stride, stride = grid * 1024.  Pass 1 copies the keys that any slot
+// takes into the block's region cand[b*cap ...]; passes 2-5 read the region.
+template <bool kMask>
+__global__ void __launch_bounds__(kXThreads)
+xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
+                 const uint8_t* __restrict__ mask, uint32_t n, int pass, XParamsDev prm,
+                 const XState* __restrict__ st, uint32_t* __restrict__ bhist,
+                 ulonglong2* __restrict__ bmm, XPart* __restrict__ part,
+                 uint64_t* __restrict__ cand, uint32_t* __restrict__ ccnt, uint32_t cap,
+                 uint32_t* __restrict__ cflag) {
+    __shared__ uint32_t hist[kXLdsBins];
+    __shared__ unsigned long long smn[kXMaxSlots], smx[kXMaxSlots];
+    __shared__ double rsh[kXThreads];
+    __shared__ uint32_t lcount;
+    const bool first = pass == 0;
+    if (!first && st->all_done) return;
+    Slots sl;
+    load_slots(sl, st);
+    const int bits = digit_bits(pass), before = bits_before(pass);
+    const int tid = threadIdx.x;
+    const int nbins = sl.n << bits;
+    for (int i = tid; i < nbins; i += kXThreads) hist[i] = 0;
+    if (tid < kXMaxSlots) { smn[tid] = ~0ull; smx[tid] = 0ull; }
+    if (tid == 0) lcount = 0;
+    const bool collect = pass == 1;
+    const bool from_cand = pass >= 2 && *cflag == 0;
+    __syncthreads();
+
+    uint64_t lmn[kXMaxSlots], lmx[kXMaxSlots];
+#pragma unroll
+    for (int s = 0; s < kXMaxSlots; ++s) { lmn[s] = ~0ull; lmx[s] = 0; }
+    double rel = 0.0;
+    uint32_t next = 0, nval = 0;
+    if (from_cand) {
+        const uint32_t cnt = ccnt[blockIdx.x];
+        const uint64_t* reg = cand + (size_t)blockIdx.x * cap;
+        for (uint32_t i = tid; i < cnt; i += kXThreads) visit(reg[i], sl, before, bits, hist, lmn, lmx);
+    } else {
+        const uint32_t stride = gridDim.x * kXThreads;
+        uint64_t* reg = cand + (size_t)blockIdx.x * cap;
+        for (uint32_t base = blockIdx.x * kXThreads + tid; base < n; base += kXUnroll * stride) {
+            float x[kXUnroll], y[kXUnroll];
+            uint32_t m[kXUnroll];
+#pragma unroll
+            for (int j = 0; j < kXUnroll; ++j) {
+                const uint64_t t64 = (uint64_t)base + (uint64_t)j * stride;
+                const uint32_t t = t64 < n ? (uint32_t)t64 : base;    // base < n: in bounds
+                // every load is issued, in bounds, whatever the token's fate: a
+                // short-circuit would put each mask load behind its own wait
+                x[j] = lt[t];
+                y[j] = lr[t];
+                m[j] = (uint32_t)(t64 < n) & (kMask ? (uint32_t)(mask[t] != 0) : 1u);
+            }
+#pragma unroll
+            for (int j = 0; j < kXUnroll; ++j) {
+                const double d = (double)x[j] - (double)y[j];
+                const bool valid = m[j] && isfinite(d);
+                bool take = false;
+                uint64_t k0 = 0;
+                if (valid) {
+                    if (first) {
+                        rel += fabs(d) / (fabs((double)x[j]) + 1e-8);
+                        next += fabs(d) > prm.tok_tau ? 1u : 0u;
+                        ++nval;
+                    }
+                    k0 = key_delta(d);
+                    take = visit(k0, sl, before, bits, hist, lmn, lmx);
+                }
+                if (collect) {
+                    // wave-aggregated append to this block's region; near the
+                    // end of the loop some lanes have left it, so the first
+                    // active lane leads
+                    const uint64_t ball = __ballot(take);
+                    if (ball) {
+                        const int leader = __ffsll((unsigned long long)__ballot(1)) - 1;
+                        uint32_t base_pos = 0;
+                        if ((tid & 63) == leader)
+                            base_pos = atomicAdd(&lcount, (uint32_t)__popcll(ball));
+                        base_pos = __shfl(base_pos, leader);
+                        const uint32_t pos =
+                            base_pos + (uint32_t)__popcll(ball & ((1ull << (tid & 63)) - 1));
+                        if (take) {
+                            if (pos < cap) reg[pos] = k0;
+                            else *cflag = 1;               // every writer stores the same value
+                        }
+                    }
+                }
+            }
+        }
+    }
+    flush_range(sl.n, lmn, lmx, smn, smx);
     if (first) {
         const double r = block_sum<kXThreads>(rel, rsh);
         const double ne = block_sum<kXThreads>((double)next, rsh);   // exact: < 2^53
@@ -274,22 +572,44 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         if (tid == 0) part[blockIdx.x] = XPart{r, (uint64_t)ne, (uint64_t)nv, 0};
     }
     __syncthreads();
-    uint32_t* out = bhist + (size_t)blockIdx.x * kXLdsBins;
-    for (int i = tid; i < nbins; i += kXThreads) out[i] = hist[i];
-    if (tid < nslots) bmm[(size_t)blockIdx.x * kXMaxSlots + tid] = make_ulonglong2(smn[tid], smx[tid]);
+    uint32_t* outh = bhist + (size_t)blockIdx.x * kXLdsBins;
+    for (int i = tid; i < nbins; i += kXThreads) outh[i] = hist[i];
+    if (tid < sl.n) bmm[(size_t)blockIdx.x * kXMaxSlots + tid] = make_ulonglong2(smn[tid], smx[tid]);
+    if (collect && tid == 0) ccnt[blockIdx.x] = lcount;
 }
 
-// ghist[i] = sum over blocks of bhist[b][i], for the active bins.
+// ghist[i] = sum over blocks of bhist[b][i], for the active bins.  A block
+// takes kXReduceBins bins; its kXReduceGroups thread groups sum interleaved
+// subsets of the pass blocks, then add their partial sums in LDS.
 __global__ void __launch_bounds__(kXReduceThreads)
 xsel_reduce_kernel(const uint32_t* __restrict__ bhist, int nblk, int pass,
                    const XState* __restrict__ st, uint32_t* __restrict__ ghist) {
+    __shared__ uint32_t part[kXReduceGroups][kXReduceBins];
     if (pass > 0 && st->all_done) return;
     const int nbins = st->nslots << digit_bits(pass);
-    const int i = blockIdx.x * kXReduceThreads + threadIdx.x;
-    if (i >= nbins) return;
-    uint32_t s = 0;
-    for (int b = 0; b < nblk; ++b) s += bhist[(size_t)b * kXLdsBins + i];
-    ghist[i] = s;
+    const int i0 = blockIdx.x * kXReduceBins;
+    if (i0 >= nbins) return;                                  // uniform
+    const int lane = threadIdx.x % kXReduceBins, g = threadIdx.x / kXReduceBins;
+    const int i = i0 + lane;
+    uint32_t acc = 0;
+    if (i < nbins) {
+        int b = g;
+        for (; b + 3 * kXReduceGroups < nblk; b += 4 * kXReduceGroups) {
+            const uint32_t a0 = bhist[(size_t)b * kXLdsBins + i];
+            const uint32_t a1 = bhist[(size_t)(b + kXReduceGroups) * kXLdsBins + i];
+            const uint32_t a2 = bhist[(size_t)(b + 2 * kXReduceGroups) * kXLdsBins + i];
+            const uint32_t a3 = bhist[(size_t)(b + 3 * kXReduceGroups) * kXLdsBins + i];
+            acc += (a0 + a1) + (a2 + a3);
+        }
+        for (; b < nblk; b += kXReduceGroups) acc += bhist[(size_t)b * kXLdsBins + i];
+    }
+    part[g][lane] = acc;
+    __syncthreads();
+    if (g == 0 && i < nbins) {
+        uint32_t sum = 0;
+        for (int k = 0; k < kXReduceGroups; ++k) sum += part[k][lane];
+        ghist[i] = sum;
+    }
 }
 
 __global__ void __launch_bounds__(kXThreads)
@@ -299,31 +619,16 @@ xsel_select_kernel(int pass, int nblk, XParamsDev prm, XState* __restrict__ gst,
     __shared__ XState st;                    // working copy; thread 0 writes it back
     __shared__ uint64_t sh[kXThreads];
     __shared__ unsigned long long mn[kXMaxSlots], mx[kXMaxSlots];
-    __shared__ uint64_t found_digit, found_rank;
+    __shared__ uint64_t fdig[kXMaxTargets], frank[kXMaxTargets];
     const int tid = threadIdx.x;
     if (tid == 0) st = *gst;
     __syncthreads();
     if (pass > 0 && st.all_done) return;
-    const int ntgt = st.ntgt;
     if (pass == 0) {
-        // number of valid tokens, then each probability's two ranks
         uint64_t nv = 0;
         for (int b = tid; b < nblk; b += kXThreads) nv += part[b].nvalid;
         nv = block_sum<kXThreads>(nv, sh);
-        if (tid == 0) {
-            st.nvalid = nv;
-            for (int t = 0; t < ntgt; t += 2) {
-                const int i = t / 2;
-                const double q = i < prm.nrq ? prm.rq[i] : prm.aq[i - prm.nrq];
-                uint64_t lo = 0, hi = 0;
-                double frac = 0.0;
-                if (nv > 0) quantile_pos(q, nv, &lo, &hi, &frac);
-                st.tgt[t].rank = lo;
-                st.tgt[t + 1].rank = hi;
-                if (nv == 0) st.tgt[t].resolved = st.tgt[t + 1].resolved = 1;
-            }
-            if (nv == 0 || ntgt == 0) st.all_done = 1;
-        }
+        if (tid == 0) set_ranks(st, nv, prm);
         __syncthreads();
         if (st.all_done) {
             if (tid == 0) *gst = st;
@@ -341,64 +646,8 @@ xsel_select_kernel(int pass, int nblk, XParamsDev prm, XState* __restrict__ gst,
         }
     }
     __syncthreads();
-    const int bits = digit_bits(pass), before = bits_before(pass);
-    const int nb = 1 << bits;
-    const int per = nb > kXThreads ? nb / kXThreads : 1;   // bins per thread
-    for (int t = 0; t < ntgt; ++t) {
-        // every thread reads target t before thread 0 may change it, so the
-        // branches below are taken by the whole block (each wave then meets
-        // the same barriers)
-        const bool done_t = st.tgt[t].resolved;
-        const int s = st.tgt[t].slot;
-        const uint64_t rank = st.tgt[t].rank;
-        __syncthreads();
-        if (done_t) continue;
-        if (mn[s] == mx[s]) {                               // one key value in the bucket
-            if (tid == 0) { st.tgt[t].resolved = 1; st.tgt[t].key = mn[s]; }
-            continue;
-        }
-        const uint32_t* h = ghist + ((size_t)s << bits);
-        const int b0 = tid * per;
-        uint64_t mine = 0;
-        if (b0 < nb)
-            for (int k = 0; k < per; ++k) mine += h[b0 + k];
-        uint64_t c = block_excl_scan<kXThreads>(mine, sh);
-        if (b0 < nb) {
-            for (int k = 0; k < per; ++k) {
-                const uint64_t hk = h[b0 + k];
-                if (c <= rank && rank < c + hk) { found_digit = (uint64_t)(b0 + k); found_rank = rank - c; }
-                c += hk;
-            }
-        }
-        __syncthreads();
-        if (tid == 0) {
-            XTarget& g = st.tgt[t];
-            g.prefix = before == 0 ? found_digit : ((g.prefix << bits) | found_digit);
-            g.rank = found_rank;
-            if (before + bits == 64) { g.resolved = 1; g.key = g.prefix; }
-        }
-        __syncthreads();
-    }
-    // slots of the next pass: one per distinct (kind, prefix) among the
-    // unresolved targets, in target order
-    if (tid == 0) {
-        int ns = 0;
-        for (int t = 0; t < ntgt; ++t) {
-            XTarget& g = st.tgt[t];
-            if (g.resolved) continue;
-            int k = 0;
-            while (k < ns && !(st.slot[k].kind == g.kind && st.slot[k].prefix == g.prefix)) ++k;
-            if (k == ns) {
-                st.slot[ns].prefix = g.prefix;
-                st.slot[ns].kind = g.kind;
-                ++ns;
-            }
-            g.slot = k;
-        }
-        st.nslots = ns;
-        if (ns == 0) st.all_done = 1;
-        *gst = st;
-    }
+    select_step(st, pass, ghist, mn, mx, sh, fdig, frank);
+    if (tid == 0) *gst = st;
 }
 
 __global__ void __launch_bounds__(kXFinThreads)
@@ -416,32 +665,7 @@ xsel_final_kernel(int nblk, XParamsDev prm, const XState* __restrict__ st,
     rel = block_sum<kXFinThreads>(rel, sh);
     next = block_sum<kXFinThreads>(next, shu);
     nv = block_sum<kXFinThreads>(nv, shu);
-    if (threadIdx.x != 0) return;
-    const double dnv = (double)nv;
-    out[kXOutNValid] = dnv;
-    out[kXOutNExtreme] = (double)next;
-    out[kXOutExtremeFrac] = nv ? (double)next / dnv : 0.0;
-    out[kXOutMeanRelDiff] = nv ? rel / dnv : 0.0;
-    for (int i = 0; i < kXMaxQ; ++i) {
-        out[kXOutRatioQ + i] = 0.0;
-        out[kXOutAbsQ + i] = 0.0;
-    }
-    if (nv == 0) return;
-    const int nq = prm.nrq + prm.naq;
-    for (int i = 0; i < nq; ++i) {
-        const bool ratio = i < prm.nrq;
-        const double q = ratio ? prm.rq[i] : prm.aq[i - prm.nrq];
-        uint64_t lo, hi;
-        double frac;
-        quantile_pos(q, nv, &lo, &hi, &frac);
-        const int kind = ratio ? 0 : 1;
-        double a = value_of(st->tgt[2 * i].key, kind);
-        double b = value_of(st->tgt[2 * i + 1].key, kind);
-        if (ratio) { a = exp(a); b = exp(b); }
-        const double v = interpolate(a, b, frac);
-        if (ratio) out[kXOutRatioQ + i] = v;
-        else out[kXOutAbsQ + i - prm.nrq] = v;
-    }
+    if (threadIdx.x == 0) write_outputs(out, prm, *st, rel, next, nv);
 }
 
 }  // namespace
@@ -449,21 +673,34 @@ xsel_final_kernel(int nblk, XParamsDev prm, const XState* __restrict__ st,
 bool make_extras_plan(int64_t n, ExtrasPlan* p) {
     if (n < 0 || n > INT32_MAX) return false;
     p->n = n;
+    p->fused = n <= kXFusedMax;
     int64_t g = (n + 16383) / 16384;
     if (g < 1) g = 1;
     if (g > kXMaxBlocks) g = kXMaxBlocks;
-    p->nblk = g;
+    p->nblk = p->fused ? 0 : g;
+    // a block's region holds a quarter of its tokens, plus a margin
+    const int64_t per_blk = p->fused ? 0 : (n + g - 1) / g;
+    p->cap = p->fused ? 0 : (uint32_t)(per_blk / 4 + 4096);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
         off += align_up(bytes > 0 ? bytes : 1, 256);
         return o;
     };
+    if (p->fused) {
+        p->state_off = p->bhist_off = p->bmm_off = p->ghist_off = p->part_off = 0;
+        p->cand_off = p->ccnt_off = p->cflag_off = 0;
+        p->total_bytes = 256;                      // unused: the fused kernel keeps all in LDS
+        return true;
+    }
     p->state_off = take(sizeof(XState));
     p->bhist_off = take((size_t)g * kXLdsBins * sizeof(uint32_t));
     p->bmm_off = take((size_t)g * kXMaxSlots * sizeof(ulonglong2));
     p->ghist_off = take((size_t)kXLdsBins * sizeof(uint32_t));
     p->part_off = take((size_t)g * sizeof(XPart));
+    p->cand_off = take((size_t)g * p->cap * sizeof(uint64_t));
+    p->ccnt_off = take((size_t)g * sizeof(uint32_t));
+    p->cflag_off = take(sizeof(uint32_t));
     p->total_bytes = off;
     return true;
 }
@@ -471,25 +708,40 @@ bool make_extras_plan(int64_t n, ExtrasPlan* p) {
 hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const float* lr,
                                   const uint8_t* mask, const XParamsDev& prm, double* out,
                                   void* workspace, hipStream_t st) {
+    if (p.fused) {
+        if (!out) return hipSuccess;           // nothing to write
+        if (mask)
+            hipLaunchKernelGGL((xsel_fused_kernel<true>), dim3(1), dim3(kXThreads), 0, st, lt, lr,
+                               mask, (uint32_t)p.n, prm, out);
+        else
+            hipLaunchKernelGGL((xsel_fused_kernel<false>), dim3(1), dim3(kXThreads), 0, st, lt, lr,
+                               mask, (uint32_t)p.n, prm, out);
+        return hipGetLastError();
+    }
     unsigned char* ws = (unsigned char*)workspace;
     XState* state = (XState*)(ws + p.state_off);
     uint32_t* bhist = (uint32_t*)(ws + p.bhist_off);
     ulonglong2* bmm = (ulonglong2*)(ws + p.bmm_off);
     uint32_t* ghist = (uint32_t*)(ws + p.ghist_off);
     XPart* part = (XPart*)(ws + p.part_off);
+    uint64_t* cand = (uint64_t*)(ws + p.cand_off);
+    uint32_t* ccnt = (uint32_t*)(ws + p.ccnt_off);
+    uint32_t* cflag = (uint32_t*)(ws + p.cflag_off);
     const int nblk = (int)p.nblk;
     const uint32_t n = (uint32_t)p.n;
-    hipLaunchKernelGGL(xsel_init_kernel, dim3(1), dim3(64), 0, st, prm, state);
+    hipLaunchKernelGGL(xsel_init_kernel, dim3(1), dim3(64), 0, st, prm, state, cflag);
     for (int pass = 0; pass < kXPasses; ++pass) {
         if (mask)
             hipLaunchKernelGGL((xsel_pass_kernel<true>), dim3(nblk), dim3(kXThreads), 0, st, lt,
-                               lr, mask, n, pass, prm, (const XState*)state, bhist, bmm, part);
+                               lr, mask, n, pass, prm, (const XState*)state, bhist, bmm, part,
+                               cand, ccnt, p.cap, cflag);
         else
             hipLaunchKernelGGL((xsel_pass_kernel<false>), dim3(nblk), dim3(kXThreads), 0, st, lt,
-                               lr, mask, n, pass, prm, (const XState*)state, bhist, bmm, part);
+                               lr, mask, n, pass, prm, (const XState*)state, bhist, bmm, part,
+                               cand, ccnt, p.cap, cflag);
         const int nbins_max = pass == 0 ? 2 << digit_bits(0) : kXMaxSlots << digit_bits(pass);
         hipLaunchKernelGGL(xsel_reduce_kernel,
-                           dim3((nbins_max + kXReduceThreads - 1) / kXReduceThreads),
+                           dim3((nbins_max + kXReduceBins - 1) / kXReduceBins),
                            dim3(kXReduceThreads), 0, st, (const uint32_t*)bhist, nblk, pass,
                            (const XState*)state, ghist);
         hipLaunchKernelGGL(xsel_select_kernel, dim3(1), dim3(kXThreads), 0, st, pass, nblk, prm,

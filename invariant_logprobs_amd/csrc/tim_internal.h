@@ -98,6 +98,7 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
 constexpr int kXMaxQ = 4;          // probabilities per call, both kinds together
 constexpr int kXPasses = 6;        // radix-select passes over the tokens
 constexpr int kXMaxBlocks = 512;   // blocks of a pass
+constexpr int kXFusedMax = 8192;   // up to this many tokens, one block does everything
 
 // Output vector layout (the TIM_X_* indices of tim.h).
 constexpr int kXOutNValid = 0, kXOutNExtreme = 1, kXOutExtremeFrac = 2, kXOutMeanRelDiff = 3,
@@ -110,11 +111,15 @@ struct XParamsDev {
 };
 
 // Workspace layout of tim_mismatch_extras (offsets 256-byte aligned): the
-// select state, per-block histograms and key ranges, the summed histogram
-// and per-block partial sums.  nblk depends on n only.
+// select state, per-block histograms and key ranges, the summed histogram,
+// per-block partial sums, and the per-block candidate regions with their
+// counts and overflow flag.  nblk and cap depend on n only.
 struct ExtrasPlan {
     int64_t n, nblk;
-    size_t state_off, bhist_off, bmm_off, ghist_off, part_off, total_bytes;
+    bool fused;        // n <= kXFusedMax: one block, no workspace use
+    uint32_t cap;      // keys per block in the candidate regions
+    size_t state_off, bhist_off, bmm_off, ghist_off, part_off, cand_off, ccnt_off, cflag_off,
+        total_bytes;
 };
 
 bool make_extras_plan(int64_t n, ExtrasPlan* p);

@@ -136,9 +136,13 @@ def _extras(lib, n=10, tau=0.1, rq=(0.5,), aq=(0.95,), lt=FAKE, lr=FAKE, ws=FAKE
 
 
 def test_extras_workspace_and_argument_errors(lib):
-    # the workspace depends on n only and grows with the number of pass blocks
-    small, big = lib.tim_extras_workspace_bytes(100), lib.tim_extras_workspace_bytes(1 << 28)
-    assert 0 < small < big < (64 << 20)
+    # the workspace depends on n only: none is used up to 8192 tokens (one
+    # block keeps everything in LDS); above, it is dominated by the candidate
+    # regions, a quarter of the keys (2 bytes per token) plus a margin
+    small, big = lib.tim_extras_workspace_bytes(8192), lib.tim_extras_workspace_bytes(1 << 28)
+    assert 0 < small <= 256
+    assert 2 * (1 << 28) < big < 3 * (1 << 28)
+    assert lib.tim_extras_workspace_bytes(8193) > small
     assert lib.tim_extras_workspace_bytes(0) > 0
     assert lib.tim_extras_workspace_bytes(-1) == 0
     assert lib.tim_extras_workspace_bytes(1 << 31) == 0

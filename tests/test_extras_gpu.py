@@ -62,7 +62,7 @@ def test_workload_extras_parity(name):
     check(w.logp_sampler, w.logp_rollout, w.mask, w.spec.tok_tau, label=name)
 
 
-@pytest.mark.parametrize("n", [1, 7, 1000, 16384, 16384 + 37, 200_003, 1 << 22])
+@pytest.mark.parametrize("n", [1, 7, 1000, 8192, 8193, 16384 + 37, 200_003, 1 << 22])
 def test_stress_extras_parity(n):
     # lognormal lengths, per-sequence drift, spikes of +1, NaN entries and a
     # masked prompt; sizes across one block, many blocks and a ragged tail
@@ -115,12 +115,30 @@ def test_keys_differing_only_in_the_last_bits():
     assert got["n_extreme"] == int((d > 1.0).sum())
 
 
+def test_candidate_overflow_falls_back_to_the_inputs():
+    # every delta in [1, 1.4): one first-pass bucket holds all keys, more than
+    # the candidate regions take, so the later passes read the tokens again
+    n = 400_000
+    g = torch.Generator(device="cpu").manual_seed(8)
+    lr = -torch.rand(n, generator=g) * 4
+    lt = (lr.double() + 1.0 + 0.4 * torch.rand(n, generator=g, dtype=torch.float64)).float()
+    check(lt.to(DEV), lr.to(DEV), None, 1.2, rq=(0.01, 0.5, 0.99), aq=(0.95,), label="overflow")
+    # and the same law on a tenth of the tokens, inside regions of their own
+    m = (torch.rand(n, generator=g) < 0.1).to(torch.uint8)
+    check(lt.to(DEV), lr.to(DEV), m.to(DEV), 1.2, rq=(0.01, 0.5, 0.99), aq=(0.95,),
+          label="masked to a tenth")
+
+
 def test_extras_run_to_run_determinism():
     lt, lr, mask, _ = workloads.stats_scale(1 << 21, seed=10, device=DEV)
     outs = [tim.tim_mismatch_extras(lt, lr, mask, tok_tau=0.1) for _ in range(3)]
+    small = [tim.tim_mismatch_extras(lt[:5000], lr[:5000], mask[:5000], tok_tau=0.1)
+             for _ in range(3)]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int64), outs[0].view(torch.int64))
+    for o in small[1:]:
+        assert torch.equal(o.view(torch.int64), small[0].view(torch.int64))
 
 
 def k3_margin(ref, bound):
