@@ -13,10 +13,13 @@
 // Order statistics are found exactly by a radix select over 64-bit keys
 // that order like the values: delta's key is its bit pattern with the sign
 // bit set for positive values and every bit inverted for negative ones;
-// |delta|'s key is its bit pattern shifted left by one (the sign bit is 0).
+// |delta|'s key is its bit pattern (the sign bit is 0).  The first digit of
+// |delta|'s key, [0, exponent, two fraction bits], therefore counts the two
+// delta digits [1, e, m] and [0, ~e, ~m]: pass 0 histograms delta's keys
+// only and derives the other.
 // Each pass histograms one digit of the keys that share a target's prefix:
 //
-//   pass 0: top 13 bits; passes 1-4: 11 bits each; pass 5: the last 7.
+//   pass 0: top 14 bits; passes 1-4: 11 bits each; pass 5: the last 6.
 //
 // A slot is a distinct (kind, prefix) that some unresolved target lies in.
 // After each pass a select step moves every unresolved target into the bin
@@ -64,13 +67,13 @@ constexpr int kXReduceThreads = kXReduceBins * kXReduceGroups;
 constexpr int kXFinThreads = 256;
 
 __host__ __device__ constexpr int digit_bits(int pass) {
-    return pass == 0 ? 13 : (pass < kXPasses - 1 ? 11 : 7);
+    return pass == 0 ? 14 : (pass < kXPasses - 1 ? 11 : 6);
 }
 __host__ __device__ constexpr int bits_before(int pass) {
-    return pass == 0 ? 0 : 13 + 11 * (pass - 1);
+    return pass == 0 ? 0 : 14 + 11 * (pass - 1);
 }
 static_assert(bits_before(kXPasses - 1) + digit_bits(kXPasses - 1) == 64, "64 key bits");
-static_assert(2 * (1 << digit_bits(0)) <= kXLdsBins, "pass 0: one slot per key kind");
+static_assert((1 << digit_bits(0)) <= kXLdsBins, "pass 0: delta's first digit");
 static_assert(kXMaxSlots * (1 << digit_bits(1)) <= kXLdsBins, "later passes: one slot per target");
 static_assert(kXFusedMax % kXThreads == 0, "whole tokens per thread in the fused kernel");
 
@@ -107,15 +110,19 @@ __device__ __forceinline__ uint64_t key_delta(double d) {
     const uint64_t u = __builtin_bit_cast(uint64_t, d);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
-// |delta|'s key from delta's key: the bit pattern of |delta| shifted left
+// |delta|'s key from delta's key: the bit pattern of |delta|
 __device__ __forceinline__ uint64_t key_abs_of(uint64_t k0) {
-    const uint64_t u = (k0 >> 63) ? k0 : ~k0;       // |delta|'s bits with the top bit set
-    return u << 1;
+    return ((k0 >> 63) ? k0 : ~k0) & 0x7FFFFFFFFFFFFFFFull;
+}
+
+// Bin D of |delta|'s first-pass histogram from delta's (14-bit digits).
+__device__ __forceinline__ uint32_t abs_root_bin(const uint32_t* h, int d) {
+    return d < 0x2000 ? h[0x2000 | d] + h[0x1FFF ^ d] : 0u;
 }
 __device__ __forceinline__ double value_of(uint64_t k, int kind) {
     uint64_t u;
     if (kind == 0) u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
-    else u = k >> 1;
+    else u = k;
     return __builtin_bit_cast(double, u);
 }
 
@@ -159,19 +166,32 @@ __device__ T block_sum(T x, T* sh) {
     return r;
 }
 
-// Exclusive prefix sum over a block of kT threads.
+// Exclusive prefix sum of integers over a block of kT threads: shuffle scans
+// within each wave, then one wave scans the wave totals (sh holds them).
 template <int kT>
 __device__ uint64_t block_excl_scan(uint64_t x, uint64_t* sh) {
-    sh[threadIdx.x] = x;
-    __syncthreads();
-    for (int off = 1; off < kT; off <<= 1) {
-        const uint64_t y = (int)threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
-        __syncthreads();
-        sh[threadIdx.x] += y;
-        __syncthreads();
+    static_assert(kT % 64 == 0 && kT / 64 <= 64, "whole waves, at most 64");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint64_t v = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(v, o);
+        if (lane >= o) v += y;
     }
-    const uint64_t r = sh[threadIdx.x] - x;
+    if (lane == 63) sh[w] = v;                           // inclusive wave total
     __syncthreads();
+    if (w == 0) {
+        uint64_t t = lane < kT / 64 ? sh[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t y = __shfl_up(t, o);
+            if (lane >= o) t += y;
+        }
+        if (lane < kT / 64) sh[lane] = t;
+    }
+    __syncthreads();
+    const uint64_t r = (w > 0 ? sh[w - 1] : 0) + v - x;
+    __syncthreads();                                     // sh is free again
     return r;
 }
 
@@ -223,21 +243,48 @@ __device__ __forceinline__ void load_slots(Slots& sl, const XState* st) {
     }
 }
 
-// Counts a token's keys in every slot whose prefix they share; returns
-// whether any slot took it.
+// Pass 0: delta's key into the one first-digit histogram, and its range.
+__device__ __forceinline__ void visit_root(uint64_t k0, uint32_t* hist, uint64_t& a, uint64_t& b) {
+    atomicAdd(&hist[(uint32_t)(k0 >> 50)], 1u);
+    a = k0 < a ? k0 : a;
+    b = k0 > b ? k0 : b;
+}
+
+// Passes 1-5: counts a token's keys in every slot whose prefix they share;
+// returns whether any slot took it.  kHigh: prefix and digit lie in the top
+// 32 bits (pass 1), and the tests use the keys' upper halves.
+template <bool kHigh>
 __device__ __forceinline__ bool visit(uint64_t k0, const Slots& sl, int before, int bits,
                                       uint32_t* hist, uint64_t (&lmn)[kXMaxSlots],
                                       uint64_t (&lmx)[kXMaxSlots]) {
     const uint64_t k1 = key_abs_of(k0);
+    bool any = false;
+    if (kHigh) {
+        const uint32_t h0 = (uint32_t)(k0 >> 32), h1 = (uint32_t)(k1 >> 32);
+        const int ps = 32 - before, ds = 32 - before - bits;
+        const uint32_t p0 = h0 >> ps, p1 = h1 >> ps;
+        const uint32_t dm = (1u << bits) - 1;
+#pragma unroll
+        for (int s = 0; s < kXMaxSlots; ++s) {
+            if (s >= sl.n) break;
+            const bool ka = sl.kind[s] != 0;
+            if ((ka ? p1 : p0) == (uint32_t)sl.pre[s]) {
+                atomicAdd(&hist[(s << bits) | (((ka ? h1 : h0) >> ds) & dm)], 1u);
+                const uint64_t k = ka ? k1 : k0;
+                lmn[s] = k < lmn[s] ? k : lmn[s];
+                lmx[s] = k > lmx[s] ? k : lmx[s];
+                any = true;
+            }
+        }
+        return any;
+    }
     const int shift = 64 - before - bits;
     const uint64_t dmask = (1ull << bits) - 1;
-    bool any = false;
 #pragma unroll
     for (int s = 0; s < kXMaxSlots; ++s) {
         if (s >= sl.n) break;
         const uint64_t k = sl.kind[s] ? k1 : k0;
-        const bool match = before == 0 || (k >> (64 - before)) == sl.pre[s];
-        if (match) {
+        if ((k >> (64 - before)) == sl.pre[s]) {
             atomicAdd(&hist[(s << bits) | (uint32_t)((k >> shift) & dmask)], 1u);
             lmn[s] = k < lmn[s] ? k : lmn[s];
             lmx[s] = k > lmx[s] ? k : lmx[s];
@@ -278,12 +325,14 @@ __device__ void select_step(XState& st, int pass, const uint32_t* h,
     const int ntgt = st.ntgt, nslots = st.nslots;
     const int bits = digit_bits(pass), before = bits_before(pass);
     const int nb = 1 << bits;
-    const int per = nb > kXThreads ? nb / kXThreads : 1;   // bins per thread (<= 8)
+    const int per = nb > kXThreads ? nb / kXThreads : 1;   // bins per thread
     // a bucket holding one key value resolves its targets at once
     if (tid == 0) {
         for (int t = 0; t < ntgt; ++t) {
             XTarget& g = st.tgt[t];
-            if (!g.resolved && mn[g.slot] == mx[g.slot]) { g.resolved = 1; g.key = mn[g.slot]; }
+            // pass 0 knows the range of delta's keys only (range slot 0)
+            const bool ranged = pass > 0 || st.slot[g.slot].kind == 0;
+            if (!g.resolved && ranged && mn[g.slot] == mx[g.slot]) { g.resolved = 1; g.key = mn[g.slot]; }
         }
     }
     __syncthreads();
@@ -294,23 +343,27 @@ __device__ void select_step(XState& st, int pass, const uint32_t* h,
         bool used = false;
         for (int t = 0; t < ntgt; ++t) used |= !st.tgt[t].resolved && st.tgt[t].slot == s;
         if (!used) continue;                                // uniform: same LDS state
-        const uint32_t* hs = h + ((size_t)s << bits);
-        uint32_t hv[8];
-        uint64_t mine = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            hv[k] = (k < per && b0 + k < nb) ? hs[b0 + k] : 0u;
-            mine += hv[k];
-        }
-        const uint64_t c0 = block_excl_scan<kXThreads>(mine, sh);
+        // pass 0 holds delta's histogram only: |delta|'s root is derived
+        const bool derive = pass == 0 && st.slot[s].kind == 1;
+        const uint32_t* hs = pass == 0 ? h : h + ((size_t)s << bits);
+        // counts and ranks are below 2^31 (n is): 32-bit sums; the bins are
+        // read again per target rather than held in registers
+        auto bin = [&](int k) -> uint32_t {
+            return derive ? abs_root_bin(h, b0 + k) : hs[b0 + k];
+        };
+        uint32_t mine = 0;
+        if (b0 < nb)
+            for (int k = 0; k < per; ++k) mine += bin(k);
+        const uint32_t c0 = (uint32_t)block_excl_scan<kXThreads>(mine, sh);
         for (int t = 0; t < ntgt; ++t) {
             if (st.tgt[t].resolved || st.tgt[t].slot != s) continue;
-            const uint64_t rank = st.tgt[t].rank;
-            uint64_t c = c0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                if (c <= rank && rank < c + hv[k]) { fdig[t] = (uint64_t)(b0 + k); frank[t] = rank - c; }
-                c += hv[k];
+            const uint32_t rank = (uint32_t)st.tgt[t].rank;
+            if (b0 >= nb || rank - c0 >= mine) continue;    // not among this thread's bins
+            uint32_t c = c0;
+            for (int k = 0; k < per; ++k) {
+                const uint32_t hk = bin(k);
+                if (rank - c < hk) { fdig[t] = (uint64_t)(b0 + k); frank[t] = rank - c; }
+                c += hk;
             }
         }
     }
@@ -429,17 +482,36 @@ xsel_fused_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         const int bits = digit_bits(pass), before = bits_before(pass);
         const int shift = 64 - before - bits;
         const uint64_t dmask = (1ull << bits) - 1;
-        for (int i = tid; i < (nslots << bits); i += kXThreads) hist[i] = 0;
+        const int nbins = pass == 0 ? 1 << bits : nslots << bits;
+        for (int i = tid; i < nbins; i += kXThreads) hist[i] = 0;
         if (tid < kXMaxSlots) { smn[tid] = ~0ull; smx[tid] = 0ull; }
         __syncthreads();
-        for (int s = 0; s < nslots; ++s) {
+        if (pass == 0) {
+            // delta's keys only, with their range in slot 0
+            uint64_t a = ~0ull, b = 0;
+            for (int j = 0; j < kXPerThreadFused; ++j) {
+                const uint64_t k0 = keys[tid + kXThreads * j];
+                if (k0 != 0) visit_root(k0, hist, a, b);
+            }
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint64_t a2 = __shfl_xor(a, o), b2 = __shfl_xor(b, o);
+                a = a2 < a ? a2 : a;
+                b = b2 > b ? b2 : b;
+            }
+            if ((tid & 63) == 0) {
+                atomicMin(&smn[0], (unsigned long long)a);
+                atomicMax(&smx[0], (unsigned long long)b);
+            }
+        }
+        // passes 1-5 slot by slot, so that one slot's key range is live at a time
+        for (int s = 0; s < (pass == 0 ? 0 : nslots); ++s) {
             const uint64_t pre = st.slot[s].prefix;
             const int kind = st.slot[s].kind;
             uint64_t a = ~0ull, b = 0;
             for (int j = 0; j < kXPerThreadFused; ++j) {
                 const uint64_t k0 = keys[tid + kXThreads * j];
                 const uint64_t k = kind ? key_abs_of(k0) : k0;
-                if (k0 != 0 && (before == 0 || (k >> (64 - before)) == pre)) {
+                if (k0 != 0 && (k >> (64 - before)) == pre) {
                     atomicAdd(&hist[(s << bits) | (uint32_t)((k >> shift) & dmask)], 1u);
                     a = k < a ? k : a;
                     b = k > b ? k : b;
@@ -472,11 +544,12 @@ xsel_init_kernel(XParamsDev prm, XState* __restrict__ st, uint32_t* __restrict__
     *cflag = 0;
 }
 
-// One histogram pass.  Passes 0 and 1 (and later passes when the candidate
-// regions overflowed) read the tokens: block b takes tokens b*1024 + tid +
-// j*stride, stride = grid * 1024.  Pass 1 copies the keys that any slot
-// takes into the block's region cand[b*cap ...]; passes 2-5 read the region.
-template <bool kMask>
+// One histogram pass; kMode 0: pass 0, 1: pass 1, 2: passes 2-5.  Passes
+// 0 and 1 (and later passes when a candidate region overflowed) read the
+// tokens: block b takes tokens b*1024 + tid + j*stride, stride = grid *
+// 1024.  Pass 1 copies the keys that any slot takes into the block's region
+// cand[b*cap ...]; passes 2-5 read the region.
+template <bool kMask, int kMode>
 __global__ void __launch_bounds__(kXThreads)
 xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                  const uint8_t* __restrict__ mask, uint32_t n, int pass, XParamsDev prm,
@@ -488,18 +561,34 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     __shared__ unsigned long long smn[kXMaxSlots], smx[kXMaxSlots];
     __shared__ double rsh[kXThreads];
     __shared__ uint32_t lcount;
-    const bool first = pass == 0;
+    __shared__ uint32_t mark[(1 << 14) / 32];   // pass 1: root digits some slot covers
+    constexpr bool first = kMode == 0;
     if (!first && st->all_done) return;
     Slots sl;
     load_slots(sl, st);
     const int bits = digit_bits(pass), before = bits_before(pass);
     const int tid = threadIdx.x;
-    const int nbins = sl.n << bits;
+    const int nbins = first ? 1 << bits : sl.n << bits;    // pass 0: delta's histogram only
+    const int nranges = first ? 1 : sl.n;
     for (int i = tid; i < nbins; i += kXThreads) hist[i] = 0;
     if (tid < kXMaxSlots) { smn[tid] = ~0ull; smx[tid] = 0ull; }
     if (tid == 0) lcount = 0;
-    const bool collect = pass == 1;
-    const bool from_cand = pass >= 2 && *cflag == 0;
+    constexpr bool collect = kMode == 1;
+    if (collect) {
+        for (int i = tid; i < (1 << 14) / 32; i += kXThreads) mark[i] = 0;
+        __syncthreads();
+        if (tid < sl.n) {
+            // delta's root digit of the slot, or the two that |delta|'s covers
+            const uint32_t d = (uint32_t)st->slot[tid].prefix;
+            if (st->slot[tid].kind == 0) {
+                atomicOr(&mark[d >> 5], 1u << (d & 31));
+            } else {
+                atomicOr(&mark[(0x2000 | d) >> 5], 1u << ((0x2000 | d) & 31));
+                atomicOr(&mark[(0x1FFF ^ d) >> 5], 1u << ((0x1FFF ^ d) & 31));
+            }
+        }
+    }
+    const bool from_cand = kMode == 2 && *cflag == 0;
     __syncthreads();
 
     uint64_t lmn[kXMaxSlots], lmx[kXMaxSlots];
@@ -510,7 +599,8 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     if (from_cand) {
         const uint32_t cnt = ccnt[blockIdx.x];
         const uint64_t* reg = cand + (size_t)blockIdx.x * cap;
-        for (uint32_t i = tid; i < cnt; i += kXThreads) visit(reg[i], sl, before, bits, hist, lmn, lmx);
+        for (uint32_t i = tid; i < cnt; i += kXThreads)
+            visit<false>(reg[i], sl, before, bits, hist, lmn, lmx);
     } else {
         const uint32_t stride = gridDim.x * kXThreads;
         uint64_t* reg = cand + (size_t)blockIdx.x * cap;
@@ -540,7 +630,15 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                         ++nval;
                     }
                     k0 = key_delta(d);
-                    take = visit(k0, sl, before, bits, hist, lmn, lmx);
+                    if (first) {
+                        visit_root(k0, hist, lmn[0], lmx[0]);
+                    } else if (collect) {
+                        const uint32_t r = (uint32_t)(k0 >> 50);
+                        if ((mark[r >> 5] >> (r & 31)) & 1u)
+                            take = visit<true>(k0, sl, before, bits, hist, lmn, lmx);
+                    } else {
+                        take = visit<false>(k0, sl, before, bits, hist, lmn, lmx);
+                    }
                 }
                 if (collect) {
                     // wave-aggregated append to this block's region; near the
@@ -564,7 +662,7 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
             }
         }
     }
-    flush_range(sl.n, lmn, lmx, smn, smx);
+    flush_range(nranges, lmn, lmx, smn, smx);
     if (first) {
         const double r = block_sum<kXThreads>(rel, rsh);
         const double ne = block_sum<kXThreads>((double)next, rsh);   // exact: < 2^53
@@ -574,7 +672,7 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     __syncthreads();
     uint32_t* outh = bhist + (size_t)blockIdx.x * kXLdsBins;
     for (int i = tid; i < nbins; i += kXThreads) outh[i] = hist[i];
-    if (tid < sl.n) bmm[(size_t)blockIdx.x * kXMaxSlots + tid] = make_ulonglong2(smn[tid], smx[tid]);
+    if (tid < nranges) bmm[(size_t)blockIdx.x * kXMaxSlots + tid] = make_ulonglong2(smn[tid], smx[tid]);
     if (collect && tid == 0) ccnt[blockIdx.x] = lcount;
 }
 
@@ -586,7 +684,7 @@ xsel_reduce_kernel(const uint32_t* __restrict__ bhist, int nblk, int pass,
                    const XState* __restrict__ st, uint32_t* __restrict__ ghist) {
     __shared__ uint32_t part[kXReduceGroups][kXReduceBins];
     if (pass > 0 && st->all_done) return;
-    const int nbins = st->nslots << digit_bits(pass);
+    const int nbins = pass == 0 ? 1 << digit_bits(0) : st->nslots << digit_bits(pass);
     const int i0 = blockIdx.x * kXReduceBins;
     if (i0 >= nbins) return;                                  // uniform
     const int lane = threadIdx.x % kXReduceBins, g = threadIdx.x / kXReduceBins;
@@ -635,14 +733,27 @@ xsel_select_kernel(int pass, int nblk, XParamsDev prm, XState* __restrict__ gst,
             return;
         }
     }
-    const int nslots = st.nslots;
+    const int nranges = pass == 0 ? 1 : st.nslots;
     if (tid < kXMaxSlots) { mn[tid] = ~0ull; mx[tid] = 0ull; }
     __syncthreads();
-    for (int b = tid; b < nblk; b += kXThreads) {
-        for (int s = 0; s < nslots; ++s) {
-            const ulonglong2 v = bmm[(size_t)b * kXMaxSlots + s];
-            atomicMin(&mn[s], v.x);
-            atomicMax(&mx[s], v.y);
+    // thread b takes pass block b (there are at most kXThreads of them);
+    // wave butterflies, then one LDS atomic per wave and slot
+    static_assert(kXMaxBlocks <= kXThreads, "one pass block per select thread");
+    for (int s = 0; s < nranges; ++s) {
+        uint64_t a = ~0ull, b = 0;
+        if (tid < nblk) {
+            const ulonglong2 v = bmm[(size_t)tid * kXMaxSlots + s];
+            a = v.x;
+            b = v.y;
+        }
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t a2 = __shfl_xor(a, o), b2 = __shfl_xor(b, o);
+            a = a2 < a ? a2 : a;
+            b = b2 > b ? b2 : b;
+        }
+        if ((tid & 63) == 0) {
+            atomicMin(&mn[s], (unsigned long long)a);
+            atomicMax(&mx[s], (unsigned long long)b);
         }
     }
     __syncthreads();
@@ -730,16 +841,14 @@ hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const fl
     const int nblk = (int)p.nblk;
     const uint32_t n = (uint32_t)p.n;
     hipLaunchKernelGGL(xsel_init_kernel, dim3(1), dim3(64), 0, st, prm, state, cflag);
+    static_assert(bits_before(1) + digit_bits(1) <= 32, "pass 1 tests upper halves");
     for (int pass = 0; pass < kXPasses; ++pass) {
-        if (mask)
-            hipLaunchKernelGGL((xsel_pass_kernel<true>), dim3(nblk), dim3(kXThreads), 0, st, lt,
-                               lr, mask, n, pass, prm, (const XState*)state, bhist, bmm, part,
-                               cand, ccnt, p.cap, cflag);
-        else
-            hipLaunchKernelGGL((xsel_pass_kernel<false>), dim3(nblk), dim3(kXThreads), 0, st, lt,
-                               lr, mask, n, pass, prm, (const XState*)state, bhist, bmm, part,
-                               cand, ccnt, p.cap, cflag);
-        const int nbins_max = pass == 0 ? 2 << digit_bits(0) : kXMaxSlots << digit_bits(pass);
+        auto kern = pass == 0 ? (mask ? xsel_pass_kernel<true, 0> : xsel_pass_kernel<false, 0>)
+                  : pass == 1 ? (mask ? xsel_pass_kernel<true, 1> : xsel_pass_kernel<false, 1>)
+                              : (mask ? xsel_pass_kernel<true, 2> : xsel_pass_kernel<false, 2>);
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(kXThreads), 0, st, lt, lr, mask, n, pass, prm,
+                           (const XState*)state, bhist, bmm, part, cand, ccnt, p.cap, cflag);
+        const int nbins_max = pass == 0 ? 1 << digit_bits(0) : kXMaxSlots << digit_bits(pass);
         hipLaunchKernelGGL(xsel_reduce_kernel,
                            dim3((nbins_max + kXReduceBins - 1) / kXReduceBins),
                            dim3(kXReduceThreads), 0, st, (const uint32_t*)bhist, nblk, pass,
