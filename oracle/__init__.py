@@ -23,6 +23,13 @@ Functions and the passages they follow:
   of ``|delta|`` ("训推一致性与 determinism", section 7, metric table) and
   the masked mean of ``|lt - lr| / (|lt| + 1e-8)`` ("RL: Training Inference
   Mismatch", training/inference consistency).
+* :func:`logprob_backward` -- ``dz = g ([v == a] - softmax(z))``, ``dh = dz W``,
+  ``dW = dz^T h``: the "log p" chain of "RL: Training Inference Mismatch",
+  differentiated.
+* :func:`ppo_loss` -- the clipped surrogate (VeXact eq. (2)) with the
+  recompute / bypass ratios (eq. (3)), the truncated-r_corr TIS weight (its
+  compensation table), the zero-centred contribution (eq. (5)) and the
+  gradient by the log-probability.
 * :func:`bf16_decode`, :func:`bf16_round_rne` -- bf16 <-> double, ties to
   even ("Train-infer mismatch for Open-weight MoE RL", figure "Rounding
   depends on the order of additions").
@@ -62,6 +69,9 @@ EXTRAS_FIELDS = (
     "abs_q0", "abs_q1", "abs_q2", "abs_q3",
 )
 MAX_Q = 4
+# Batch vector of :func:`ppo_loss`, in index order.
+PPO_FIELDS = ("mean_loss", "clip_frac", "mean_ratio", "mean_tis_w", "mean_contrib",
+              "n_valid", "n_clipped", "n_nan")
 
 _lock = threading.Lock()
 _lib = None
@@ -106,8 +116,16 @@ def _load():
         lib.or_mismatch_extras.argtypes = [vp, vp, vp, c_i64, ctypes.c_double, vp, c_int,
                                            vp, c_int, vp]
         lib.or_extras_nfields.restype = c_int
+        lib.or_logprob_backward.restype = c_int
+        lib.or_logprob_backward.argtypes = [vp, c_i64, vp, c_i64, vp, vp, c_int, c_i64, c_i64,
+                                            c_i64, vp, c_i64, vp, vp, c_i64, vp, c_int]
+        lib.or_ppo_loss.restype = c_int
+        lib.or_ppo_loss.argtypes = [vp, vp, vp, vp, vp, c_i64, ctypes.c_double,
+                                    ctypes.c_double, c_int, ctypes.c_double] + [vp] * 6
+        lib.or_ppo_nfields.restype = c_int
         assert lib.or_batch_nfields() == len(BATCH_FIELDS)
         assert lib.or_extras_nfields() == len(EXTRAS_FIELDS)
+        assert lib.or_ppo_nfields() == len(PPO_FIELDS)
         _lib = lib
         return lib
 
@@ -244,3 +262,51 @@ def mismatch_extras(lt, lr, mask, *, tok_tau: float, ratio_q=(), abs_q=()) -> di
     res["abs_q"] = [float(x) for x in out[8:8 + aq.size]]
     res["vector"] = out
     return res
+
+
+def logprob_backward(h, w, ids, g, *, dtype: int, dh_rows=None, dw_rows=None, nthreads: int = 0):
+    """fp64 ``(dh[dh_rows], dW[dw_rows])`` for the upstream gradient ``g``
+    (``dL/dlogp``, one value per token); rows default to all.  Only tokens with
+    ``g != 0`` cost anything."""
+    el = np.uint16 if dtype == BF16 else np.float32
+    h = _as_host_array(h, el)
+    w = _as_host_array(w, el)
+    ids = _as_host_array(ids, np.int32)
+    g = _as_host_array(g, np.float64)
+    n, d = h.shape
+    v, d2 = w.shape
+    assert d == d2 and ids.shape == (n,) and g.shape == (n,)
+    dh_rows = np.arange(n, dtype=np.int64) if dh_rows is None else \
+        np.ascontiguousarray(dh_rows, dtype=np.int64)
+    dw_rows = np.arange(v, dtype=np.int64) if dw_rows is None else \
+        np.ascontiguousarray(dw_rows, dtype=np.int64)
+    dh = np.empty((dh_rows.size, d), np.float64)
+    dw = np.empty((dw_rows.size, d), np.float64)
+    if nthreads <= 0:
+        nthreads = min(available_cpus(), MAX_THREADS)
+    rc = _load().or_logprob_backward(_ptr(h), d, _ptr(w), d, _ptr(ids), _ptr(g), dtype, n, d, v,
+                                     _ptr(dh_rows), dh_rows.size, _ptr(dh), _ptr(dw_rows),
+                                     dw_rows.size, _ptr(dw), int(nthreads))
+    if rc != 0:
+        raise ValueError("or_logprob_backward rejected its arguments")
+    return dh, dw
+
+
+def ppo_loss(logp, old_train, old_rollout, adv, mask, *, eps_lo: float, eps_hi: float,
+             bypass: bool = False, tis_c: float = 0.0) -> dict:
+    """fp64 per-token loss, gradient (of the token mean), ratio,
+    contribution and clip flag, and the batch vector (``PPO_FIELDS``)."""
+    arrs = [_as_host_array(x, np.float32) for x in (logp, old_train, old_rollout, adv)]
+    m = None if mask is None else _as_host_array(mask, np.uint8)
+    n = arrs[0].size
+    out = {k: np.empty(n, np.float64) for k in ("loss", "grad", "ratio", "contrib")}
+    out["clipped"] = np.empty(n, np.uint8)
+    batch = np.empty(len(PPO_FIELDS), np.float64)
+    rc = _load().or_ppo_loss(*[_ptr(a) for a in arrs], _ptr(m), n, float(eps_lo), float(eps_hi),
+                             int(bool(bypass)), float(tis_c), _ptr(out["loss"]), _ptr(out["grad"]),
+                             _ptr(out["ratio"]), _ptr(out["contrib"]), _ptr(out["clipped"]),
+                             _ptr(batch))
+    if rc != 0:
+        raise ValueError("or_ppo_loss rejected its arguments")
+    out["batch"] = dict(zip(PPO_FIELDS, (float(x) for x in batch)))
+    return out

@@ -471,3 +471,264 @@ int or_mismatch_extras(const float* lt, const float* lr, const uint8_t* mask,
     free(absd);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Backward of the selected-token log-probability                      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * With logp_t = z_t[a_t] - log sum_v exp z_t[v] and z_t = W h_t, the
+ * derivative of logp_t by the logit z_t[v] is [v == a_t] - p_t[v], p_t the
+ * softmax of z_t.  For an upstream gradient g_t = dL/dlogp_t:
+ *   dz_t[v]  = g_t ([v == a_t] - p_t[v])
+ *   dh_t[k]  = sum_v dz_t[v] W[v, k]            (v ascending)
+ *   dW[v, k] = sum_t dz_t[v] h[t, k]            (t ascending)
+ * ("RL: Training Inference Mismatch", "log p" chain, differentiated; the
+ * policy-gradient term grad log q of its importance-sampling section.)
+ *
+ * Only tokens with g_t != 0 contribute.  dh is written for the token rows
+ * dh_rows[0..n_dh) ([n_dh, d]), dW for the vocabulary rows dw_rows[0..n_dw)
+ * ([n_dw, d]).  An out-of-range id contributes nothing (its logp is NaN in
+ * the forward).  nthreads <= 0: all CPUs.  Returns 0, or -1 on bad
+ * arguments or memory.
+ */
+typedef struct {
+    const void* h; int64_t ldh; const void* w; int64_t ldw;
+    const int32_t* ids; const double* g; int dtype; int64_t d, v;
+    const int64_t* tok; int64_t ntok;     /* tokens with g != 0 */
+    double* dz;                           /* [ntok, v] */
+    int64_t begin, end;
+} bw_job;
+
+static void* bw_dz_worker(void* arg)
+{
+    bw_job* j = (bw_job*)arg;
+    const int64_t d = j->d, v = j->v;
+    double* hd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* z = (double*)malloc(sizeof(double) * (size_t)v);
+    if (!hd || !z) { free(hd); free(z); return (void*)1; }
+    for (int64_t i = j->begin; i < j->end; ++i) {
+        const int64_t t = j->tok[i];
+        double* dz = j->dz + i * v;
+        const int32_t a = j->ids[t];
+        if (!(a >= 0 && (int64_t)a < v)) {
+            for (int64_t c = 0; c < v; ++c) dz[c] = 0.0;
+            continue;
+        }
+        for (int64_t k = 0; k < d; ++k) hd[k] = load_elem(j->h, j->dtype, t * j->ldh + k);
+        double m = -INFINITY;
+        for (int64_t c = 0; c < v; ++c) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < d; ++k) acc += hd[k] * load_elem(j->w, j->dtype, c * j->ldw + k);
+            z[c] = acc;
+            if (acc > m) m = acc;
+        }
+        double s = 0.0;
+        for (int64_t c = 0; c < v; ++c) s += exp(z[c] - m);
+        const double lse = m + log(s);
+        const double g = j->g[t];
+        for (int64_t c = 0; c < v; ++c) {
+            const double p = exp(z[c] - lse);
+            dz[c] = g * ((c == a ? 1.0 : 0.0) - p);
+        }
+    }
+    free(hd); free(z);
+    return NULL;
+}
+
+typedef struct {
+    const void* h; int64_t ldh; const void* w; int64_t ldw; int dtype; int64_t d, v;
+    const int64_t* tok; int64_t ntok; const double* dz;
+    const int64_t* rows; double* out; int64_t begin, end;
+    int which;                            /* 0: dh rows (tokens), 1: dW rows (vocab) */
+    const int64_t* tok_index;             /* dh: position of a token in tok, or -1 */
+} bw_out_job;
+
+static void* bw_out_worker(void* arg)
+{
+    bw_out_job* j = (bw_out_job*)arg;
+    const int64_t d = j->d, v = j->v;
+    for (int64_t i = j->begin; i < j->end; ++i) {
+        double* o = j->out + i * d;
+        for (int64_t k = 0; k < d; ++k) o[k] = 0.0;
+        if (j->which == 0) {
+            const int64_t pos = j->tok_index[i];
+            if (pos < 0) continue;                       /* g_t == 0: dh_t = 0 */
+            const double* dz = j->dz + pos * v;
+            for (int64_t c = 0; c < v; ++c) {
+                const double f = dz[c];
+                for (int64_t k = 0; k < d; ++k) o[k] += f * load_elem(j->w, j->dtype, c * j->ldw + k);
+            }
+        } else {
+            const int64_t c = j->rows[i];
+            for (int64_t q = 0; q < j->ntok; ++q) {
+                const int64_t t = j->tok[q];
+                const double f = j->dz[q * v + c];
+                for (int64_t k = 0; k < d; ++k) o[k] += f * load_elem(j->h, j->dtype, t * j->ldh + k);
+            }
+        }
+    }
+    return NULL;
+}
+
+static int run_threads(void* jobs, size_t job_size, int nthreads, void* (*fn)(void*))
+{
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!th) return -1;
+    int bad = 0;
+    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, fn, (char*)jobs + i * job_size);
+    if (fn((char*)jobs) != NULL) bad = 1;
+    for (int i = 1; i < nthreads; ++i) {
+        void* r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) bad = 1;
+    }
+    free(th);
+    return bad ? -1 : 0;
+}
+
+int or_logprob_backward(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                        const int32_t* ids, const double* g, int dtype,
+                        int64_t n, int64_t d, int64_t v,
+                        const int64_t* dh_rows, int64_t n_dh, double* dh,
+                        const int64_t* dw_rows, int64_t n_dw, double* dw, int nthreads)
+{
+    if (!h || !w || !ids || !g || n < 0 || d <= 0 || v <= 0 || ldh < d || ldw < d ||
+        (dtype != OR_BF16 && dtype != OR_F32) || n_dh < 0 || n_dw < 0 ||
+        (n_dh > 0 && (!dh_rows || !dh)) || (n_dw > 0 && (!dw_rows || !dw)))
+        return -1;
+    for (int64_t i = 0; i < n_dh; ++i) if (dh_rows[i] < 0 || dh_rows[i] >= n) return -1;
+    for (int64_t i = 0; i < n_dw; ++i) if (dw_rows[i] < 0 || dw_rows[i] >= v) return -1;
+    if (nthreads <= 0) nthreads = or_available_cpus();
+
+    /* tokens that contribute, ascending */
+    int64_t ntok = 0;
+    for (int64_t t = 0; t < n; ++t) ntok += g[t] != 0.0;
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)(ntok > 0 ? ntok : 1));
+    double* dz = (double*)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok * v : 1));
+    int64_t* tok_index = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_dh > 0 ? n_dh : 1));
+    if (!tok || !dz || !tok_index) { free(tok); free(dz); free(tok_index); return -1; }
+    for (int64_t t = 0, q = 0; t < n; ++t) if (g[t] != 0.0) tok[q++] = t;
+    for (int64_t i = 0; i < n_dh; ++i) {
+        tok_index[i] = -1;
+        for (int64_t q = 0; q < ntok; ++q) if (tok[q] == dh_rows[i]) { tok_index[i] = q; break; }
+    }
+    int rc = 0;
+    {
+        int nt = nthreads < ntok ? nthreads : (int)(ntok > 0 ? ntok : 1);
+        bw_job* jobs = (bw_job*)calloc((size_t)nt, sizeof(bw_job));
+        if (!jobs) rc = -1;
+        for (int i = 0; rc == 0 && i < nt; ++i) {
+            bw_job* j = &jobs[i];
+            j->h = h; j->ldh = ldh; j->w = w; j->ldw = ldw; j->ids = ids; j->g = g;
+            j->dtype = dtype; j->d = d; j->v = v; j->tok = tok; j->ntok = ntok; j->dz = dz;
+            j->begin = ntok * i / nt; j->end = ntok * (i + 1) / nt;
+        }
+        if (rc == 0) rc = run_threads(jobs, sizeof(bw_job), nt, bw_dz_worker);
+        free(jobs);
+    }
+    for (int which = 0; rc == 0 && which < 2; ++which) {
+        const int64_t nrows = which == 0 ? n_dh : n_dw;
+        if (nrows == 0) continue;
+        int nt = nthreads < nrows ? nthreads : (int)nrows;
+        bw_out_job* jobs = (bw_out_job*)calloc((size_t)nt, sizeof(bw_out_job));
+        if (!jobs) { rc = -1; break; }
+        for (int i = 0; i < nt; ++i) {
+            bw_out_job* j = &jobs[i];
+            j->h = h; j->ldh = ldh; j->w = w; j->ldw = ldw; j->dtype = dtype; j->d = d; j->v = v;
+            j->tok = tok; j->ntok = ntok; j->dz = dz; j->which = which;
+            j->rows = which == 0 ? dh_rows : dw_rows; j->out = which == 0 ? dh : dw;
+            j->tok_index = tok_index;
+            j->begin = nrows * i / nt; j->end = nrows * (i + 1) / nt;
+        }
+        rc = run_threads(jobs, sizeof(bw_out_job), nt, bw_out_worker);
+        free(jobs);
+    }
+    free(tok); free(dz); free(tok_index);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* PPO / GRPO clipped surrogate with truncated importance weights      */
+/* ------------------------------------------------------------------ */
+
+enum {
+    OP_MEAN_LOSS, OP_CLIP_FRAC, OP_MEAN_RATIO, OP_MEAN_TIS_W, OP_MEAN_CONTRIB,
+    OP_N_VALID, OP_N_CLIPPED, OP_N_NAN, OP_NFIELDS
+};
+
+int or_ppo_nfields(void) { return OP_NFIELDS; }
+
+/*
+ * Per token (mask != 0): the PPO ratio r = exp(logp - logp_old), with
+ * logp_old the trainer's recomputed old log-probability ("recompute") or
+ * the rollout's ("bypass") (VeXact eq. (3)); the clipped surrogate
+ * loss = -w min(r A, clip(r, 1 - eps_lo, 1 + eps_hi) A) (VeXact eq. (2)),
+ * w = min(exp(old_train - old_rollout), C) the truncated r_corr weight when
+ * tis_c > 0, else 1 (VeXact compensation table, TIS rows: TIS moves the
+ * ratio from the trainer's to the rollout's denominator); the zero-centred
+ * contribution -(r - 1) A (VeXact eq. (5)); and d loss / d logp =
+ * -w [unclipped] r A, where the clip is active iff A > 0 and r > 1 + eps_hi
+ * or A < 0 and r < 1 - eps_lo ("RL: Training Inference Mismatch", clipped
+ * importance ratios: the gradient is dropped once the ratio leaves the
+ * interval on the side that the advantage's sign favours).
+ * A token whose inputs give a non-finite r, weight or advantage is counted
+ * in n_nan and left out.  grad[t] is the derivative of the token mean of
+ * loss over the valid tokens (0 for tokens left out).  Outputs nullable.
+ */
+int or_ppo_loss(const float* logp, const float* old_train, const float* old_rollout,
+                const float* adv, const uint8_t* mask, int64_t n,
+                double eps_lo, double eps_hi, int bypass, double tis_c,
+                double* loss, double* grad, double* ratio, double* contrib,
+                uint8_t* clipped, double* batch)
+{
+    if (n < 0 || (n > 0 && (!logp || !old_train || !old_rollout || !adv)) ||
+        !(eps_lo >= 0.0) || !(eps_hi >= 0.0) || isnan(tis_c))
+        return -1;
+    double s_loss = 0, s_r = 0, s_w = 0, s_c = 0;
+    int64_t nv = 0, nclip = 0, nnan = 0;
+    for (int64_t t = 0; t < n; ++t) {
+        double l_t = 0, g_t = 0, r_t = 1, c_t = 0;
+        int clip_t = 0;
+        if (!mask || mask[t] != 0) {
+            const double old = bypass ? (double)old_rollout[t] : (double)old_train[t];
+            const double r = exp((double)logp[t] - old);
+            const double w = tis_c > 0.0
+                ? fmin(exp((double)old_train[t] - (double)old_rollout[t]), tis_c) : 1.0;
+            const double a = (double)adv[t];
+            if (!isfinite(r) || !isfinite(w) || !isfinite(a)) {
+                nnan++;
+            } else {
+                const double rc = r < 1.0 - eps_lo ? 1.0 - eps_lo : (r > 1.0 + eps_hi ? 1.0 + eps_hi : r);
+                const double sur = fmin(r * a, rc * a);
+                const int active = (a > 0.0 && r > 1.0 + eps_hi) || (a < 0.0 && r < 1.0 - eps_lo);
+                l_t = -w * sur;
+                g_t = active ? 0.0 : -w * r * a;
+                r_t = r;
+                c_t = -(r - 1.0) * a;
+                clip_t = active;
+                nv++; nclip += active;
+                s_loss += l_t; s_r += r; s_w += w; s_c += c_t;
+            }
+        }
+        if (loss) loss[t] = l_t;
+        if (grad) grad[t] = g_t;        /* scaled below */
+        if (ratio) ratio[t] = r_t;
+        if (contrib) contrib[t] = c_t;
+        if (clipped) clipped[t] = (uint8_t)clip_t;
+    }
+    if (grad && nv > 0)
+        for (int64_t t = 0; t < n; ++t) grad[t] /= (double)nv;
+    if (batch) {
+        const double dn = (double)nv;
+        batch[OP_MEAN_LOSS] = safe_div(s_loss, dn);
+        batch[OP_CLIP_FRAC] = safe_div((double)nclip, dn);
+        batch[OP_MEAN_RATIO] = safe_div(s_r, dn);
+        batch[OP_MEAN_TIS_W] = safe_div(s_w, dn);
+        batch[OP_MEAN_CONTRIB] = safe_div(s_c, dn);
+        batch[OP_N_VALID] = dn;
+        batch[OP_N_CLIPPED] = (double)nclip;
+        batch[OP_N_NAN] = (double)nnan;
+    }
+    return 0;
+}

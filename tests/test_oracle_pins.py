@@ -474,6 +474,161 @@ def test_quantile_order_statistics_and_edge_cases():
 
 
 # ---------------------------------------------------------------------------
+# backward of the selected-token log-probability
+# ---------------------------------------------------------------------------
+
+def _bw_case(seed=21, n=6, d=16, v=11):
+    rng = np.random.default_rng(seed)
+    # dyadic values: h +- 2^-12 and W +- 2^-12 are exact in fp32
+    h = (np.round(rng.standard_normal((n, d)) * 64) / 64).astype(np.float32)
+    w = (np.round(rng.standard_normal((v, d)) * 16) / 64).astype(np.float32)
+    ids = rng.integers(0, v, n).astype(np.int32)
+    g = rng.standard_normal(n)
+    g[2] = 0.0                                   # a token that does not contribute
+    return h, w, ids, g
+
+
+def _objective(h, w, ids, g):
+    """sum_t g_t logp_t with the (separately pinned) fp64 forward."""
+    logp, _, _ = _lp(h, w, ids, dtype=oracle.F32)
+    return float(np.dot(g, logp))
+
+
+def test_backward_matches_central_differences_of_the_forward():
+    h, w, ids, g = _bw_case()
+    dh, dw = oracle.logprob_backward(h, w, ids, g, dtype=oracle.F32)
+    eps = 2.0 ** -12
+    rng = np.random.default_rng(3)
+    for _ in range(12):
+        t, k = int(rng.integers(0, h.shape[0])), int(rng.integers(0, h.shape[1]))
+        hp, hm = h.copy(), h.copy()
+        hp[t, k] += np.float32(eps)
+        hm[t, k] -= np.float32(eps)
+        fd = (_objective(hp, w, ids, g) - _objective(hm, w, ids, g)) / (2 * eps)
+        assert abs(fd - dh[t, k]) <= 1e-6 * (1 + abs(dh[t, k])), (t, k, fd, dh[t, k])
+    for _ in range(12):
+        c, k = int(rng.integers(0, w.shape[0])), int(rng.integers(0, w.shape[1]))
+        wp, wm = w.copy(), w.copy()
+        wp[c, k] += np.float32(eps)
+        wm[c, k] -= np.float32(eps)
+        fd = (_objective(h, wp, ids, g) - _objective(h, wm, ids, g)) / (2 * eps)
+        assert abs(fd - dw[c, k]) <= 1e-6 * (1 + abs(dw[c, k])), (c, k, fd, dw[c, k])
+
+
+def test_backward_invariants_and_row_selection():
+    h, w, ids, g = _bw_case(seed=22, n=9, d=8, v=13)
+    dh, dw = oracle.logprob_backward(h, w, ids, g, dtype=oracle.F32)
+    # the softmax derivative sums to zero over the vocabulary, so the rows
+    # of dW sum to zero; a token with g = 0 has dh = 0
+    assert np.abs(dw.sum(axis=0)).max() < 1e-12
+    assert np.all(dh[2] == 0)
+    # linear in g
+    dh2, dw2 = oracle.logprob_backward(h, w, ids, 2 * g, dtype=oracle.F32)
+    np.testing.assert_allclose(dh2, 2 * dh, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dw2, 2 * dw, rtol=1e-14, atol=1e-15)
+    # selected rows are the same rows
+    sdh, sdw = oracle.logprob_backward(h, w, ids, g, dtype=oracle.F32, dh_rows=[4, 0],
+                                       dw_rows=[12, 3, 3])
+    np.testing.assert_array_equal(sdh, dh[[4, 0]])
+    np.testing.assert_array_equal(sdw, dw[[12, 3, 3]])
+
+
+# ---------------------------------------------------------------------------
+# PPO / GRPO clipped surrogate
+# ---------------------------------------------------------------------------
+
+def _ppo(lp, ot, orr, a, mask=None, lo=0.2, hi=0.28, bypass=False, c=0.0):
+    f = lambda x: np.asarray(x, np.float32)
+    return oracle.ppo_loss(f(lp), f(ot), f(orr), f(a), mask, eps_lo=lo, eps_hi=hi,
+                           bypass=bypass, tis_c=c)
+
+
+def test_ppo_clip_branches_closed_form():
+    # ratios 1.5 (above 1 + 0.28) and 0.5 (below 1 - 0.2) with both signs of A
+    old = np.zeros(4, np.float32) - 2.0
+    d = np.array([math.log(1.5), math.log(1.5), math.log(0.5), math.log(0.5)])
+    lp = (old.astype(np.float64) + d).astype(np.float32)
+    a = [1.0, -1.0, 1.0, -1.0]
+    r = _ppo(lp, old, old, a)
+    rr = np.exp(lp.astype(np.float64) - old.astype(np.float64))
+    # A > 0, r > 1 + eps: clipped at (1 + eps) A, no gradient
+    assert r["loss"][0] == -1.28 and r["grad"][0] == 0 and r["clipped"][0] == 1
+    # A < 0, r > 1 + eps: r A is the smaller term, gradient flows
+    assert r["loss"][1] == rr[1] and r["clipped"][1] == 0
+    assert r["grad"][1] == pytest.approx(rr[1] / 4, rel=1e-15)   # -(r A) / n with A = -1
+    # A > 0, r < 1 - eps: r A is the smaller term, gradient flows
+    assert r["loss"][2] == -rr[2] and r["clipped"][2] == 0
+    # A < 0, r < 1 - eps: clipped at (1 - eps) A
+    assert r["loss"][3] == pytest.approx(0.8, rel=1e-15) and r["grad"][3] == 0
+    assert r["batch"]["clip_frac"] == 0.5 and r["batch"]["n_valid"] == 4
+
+
+def test_ppo_gradient_matches_central_differences():
+    rng = np.random.default_rng(31)
+    n = 40
+    ot = (-rng.uniform(0.5, 3, n)).astype(np.float32)
+    orr = (ot + rng.normal(0, 0.05, n)).astype(np.float32)
+    lp = (ot + rng.normal(0, 0.2, n)).astype(np.float32)
+    a = rng.normal(0, 1, n).astype(np.float32)
+    for bypass, c in ((False, 0.0), (False, 2.0), (True, 0.0)):
+        base = _ppo(lp, ot, orr, a, bypass=bypass, c=c)
+        eps = 2.0 ** -16
+        for t in range(0, n, 3):
+            r_t = base["ratio"][t]
+            # skip tokens within reach of a clip boundary
+            if min(abs(r_t - 1.28), abs(r_t - 0.8)) < 1e-3:
+                continue
+            lpp, lpm = lp.copy(), lp.copy()
+            lpp[t] += np.float32(eps)
+            lpm[t] -= np.float32(eps)
+            fd = (_ppo(lpp, ot, orr, a, bypass=bypass, c=c)["batch"]["mean_loss"] -
+                  _ppo(lpm, ot, orr, a, bypass=bypass, c=c)["batch"]["mean_loss"]) / (2 * eps)
+            assert abs(fd - base["grad"][t]) < 1e-7, (bypass, c, t, fd, base["grad"][t])
+
+
+def test_ppo_contribution_has_the_gradient_of_minus_r_a_and_tis_moves_the_ratio():
+    rng = np.random.default_rng(32)
+    n = 16
+    ot = (-rng.uniform(0.5, 3, n)).astype(np.float32)
+    orr = (ot + rng.normal(0, 0.02, n)).astype(np.float32)
+    lp = (ot + rng.normal(0, 0.02, n)).astype(np.float32)
+    a = rng.normal(0, 1, n).astype(np.float32)
+    base = _ppo(lp, ot, orr, a)
+    eps = 2.0 ** -16
+    for t in range(n):
+        lpp, lpm = lp.copy(), lp.copy()
+        lpp[t] += np.float32(eps)
+        lpm[t] -= np.float32(eps)
+        fd = (_ppo(lpp, ot, orr, a)["contrib"][t] - _ppo(lpm, ot, orr, a)["contrib"][t]) / (2 * eps)
+        assert fd == pytest.approx(-base["ratio"][t] * float(a[t]), rel=1e-6, abs=1e-9)
+        assert base["contrib"][t] == pytest.approx(-(base["ratio"][t] - 1) * float(a[t]),
+                                                   rel=1e-12, abs=1e-15)
+    # an untruncated r_corr weight times the trainer-side ratio is the
+    # rollout-side ratio: recompute + TIS equals bypass where nothing clips
+    rec = _ppo(lp, ot, orr, a, c=100.0)
+    byp = _ppo(lp, ot, orr, a, bypass=True)
+    ok = (rec["clipped"] == 0) & (byp["clipped"] == 0)
+    assert ok.sum() >= n - 2
+    np.testing.assert_allclose(rec["loss"][ok], byp["loss"][ok], rtol=1e-14, atol=1e-16)
+    # truncation: with C below every r_corr the weight is C
+    low = _ppo(lp, ot, orr, a, c=1e-3)
+    assert low["batch"]["mean_tis_w"] == pytest.approx(1e-3, rel=1e-15)
+
+
+def test_ppo_mask_and_nan_tokens():
+    lp = np.array([-1.0, -1.0, np.nan, -1.0], np.float32)
+    ot = np.array([-1.1, -1.1, -1.1, -1.1], np.float32)
+    a = np.array([1.0, 2.0, 1.0, 5.0], np.float32)
+    mask = np.array([1, 1, 1, 0], np.uint8)
+    r = _ppo(lp, ot, ot, a, mask=mask)
+    b = r["batch"]
+    assert b["n_valid"] == 2 and b["n_nan"] == 1
+    assert r["loss"][2] == 0 and r["grad"][2] == 0 and r["loss"][3] == 0
+    rr = math.exp(float(np.float32(-1.0)) - float(np.float32(-1.1)))
+    assert b["mean_loss"] == pytest.approx(-(rr * 1 + rr * 2) / 2, rel=1e-15)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ---------------------------------------------------------------------------
 
@@ -482,7 +637,8 @@ MUTATIONS = [
      "test_two_entry_vocabulary_closed_form_including_large_logits"),
     ("gather off by one", "ok ? zr[a] - l : NAN", "ok ? zr[(a + 1) % v] - l : NAN",
      "test_brute_force_against_exact_logits_and_decimal_softmax"),
-    ("transposed W", "c * j->ldw + k", "k * j->ldw + c",
+    ("transposed W", "wd[k] = load_elem(j->w, j->dtype, c * j->ldw + k);",
+     "wd[k] = load_elem(j->w, j->dtype, k * j->ldw + c);",
      "test_brute_force_against_exact_logits_and_decimal_softmax"),
     ("delta sign", "                delta = (double)lt[t] - (double)lr[t];",
      "                delta = (double)lr[t] - (double)lt[t];",
@@ -520,6 +676,27 @@ MUTATIONS = [
      "(void)cmp_double;", "test_quantile_order_statistics_and_edge_cases"),
     ("quantile position over m", "double pos = q * (double)(m - 1);",
      "double pos = q * (double)m;", "test_quantiles_match_numpy_linear_method"),
+    ("softmax derivative sign", "dz[c] = g * ((c == a ? 1.0 : 0.0) - p);",
+     "dz[c] = g * (p - (c == a ? 1.0 : 0.0));",
+     "test_backward_matches_central_differences_of_the_forward"),
+    ("upstream gradient dropped", "dz[c] = g * ((c == a ? 1.0 : 0.0) - p);",
+     "dz[c] = ((c == a ? 1.0 : 0.0) - p);", "test_backward_invariants_and_row_selection"),
+    ("dW from W instead of h", "o[k] += f * load_elem(j->h, j->dtype, t * j->ldh + k);",
+     "o[k] += f * load_elem(j->w, j->dtype, t * j->ldw + k);",
+     "test_backward_matches_central_differences_of_the_forward"),
+    ("ppo max instead of min", "const double sur = fmin(r * a, rc * a);",
+     "const double sur = fmax(r * a, rc * a);", "test_ppo_clip_branches_closed_form"),
+    ("ppo clip side", "const int active = (a > 0.0 && r > 1.0 + eps_hi) || (a < 0.0 && r < 1.0 - eps_lo);",
+     "const int active = (a > 0.0 && r < 1.0 - eps_lo) || (a < 0.0 && r > 1.0 + eps_hi);",
+     "test_ppo_clip_branches_closed_form"),
+    ("ppo bypass ignored", "const double old = bypass ? (double)old_rollout[t] : (double)old_train[t];",
+     "const double old = (double)old_train[t];",
+     "test_ppo_contribution_has_the_gradient_of_minus_r_a_and_tis_moves_the_ratio"),
+    ("tis weight untruncated", "? fmin(exp((double)old_train[t] - (double)old_rollout[t]), tis_c) : 1.0;",
+     "? exp((double)old_train[t] - (double)old_rollout[t]) : 1.0;",
+     "test_ppo_contribution_has_the_gradient_of_minus_r_a_and_tis_moves_the_ratio"),
+    ("ppo gradient without weight", "g_t = active ? 0.0 : -w * r * a;", "g_t = active ? 0.0 : -r * a;",
+     "test_ppo_gradient_matches_central_differences"),
 ]
 
 
