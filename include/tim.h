@@ -341,6 +341,134 @@ int tim_mismatch_extras(const float* logp_train, const float* logp_rollout,
                         double* out, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of the selected-token log-probability.
+ * ---------------------------------------------------------------------- */
+
+enum {
+    TIM_BWD_ACCUMULATE_DW = 1u  /* dw is read and the sum over this batch's
+                                   tokens continues from it (see below)      */
+};
+
+/* Bytes of device workspace tim_logprob_backward needs; 0 for sizes or a
+ * dtype it does not accept (only TIM_BF16 is).  Pure host function. */
+size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype);
+
+/*
+ * Gradients of L through logp[t] = log softmax(h[t,:] . W^T)[ids[t]], given
+ * grad_logp[t] = dL/dlogp[t]:
+ *     dz[t, v] = grad_logp[t] ([v == ids[t]] - softmax(z_t)[v])
+ *     dh[t, :] = sum_v dz[t, v] W[v, :]          (v ascending)
+ *     dw[v, :] = sum_t dz[t, v] h[t, :]          (t ascending)
+ * ("RL: Training Inference Mismatch", the "log p" chain differentiated; the
+ * policy-gradient term g_t grad log q_t of its importance-sampling section.)
+ *
+ *  h, ldh, w, ldw, ids, n, d, v  as for tim_logprob_forward; dtype must be
+ *             TIM_BF16 (else TIM_EUNSUPPORTED).
+ *  lse        [n] fp32: the lse output of tim_logprob_forward on the same
+ *             inputs (the softmax is exp(z - lse)).
+ *  grad_logp  [n] fp32.  A token with grad 0, or an id outside [0, v),
+ *             contributes nothing.
+ *  dh         [n, d] fp32 out (row stride d), nullable.
+ *  dw         [v, d] fp32 out (row stride d), nullable.  With
+ *             TIM_BWD_ACCUMULATE_DW its incoming values start the sums.
+ *  flags      0 or TIM_BWD_ACCUMULATE_DW.
+ *  workspace  >= tim_logprob_backward_workspace_bytes(...) bytes,
+ *             256-byte aligned.
+ *
+ * Arithmetic: the logits are recomputed exactly as tim_logprob_forward does
+ * (same K order and instructions); dz is rounded to bf16 once; dh and dw are
+ * bf16 x bf16 products accumulated in fp32, one chain per output element in
+ * ascending K, no split-K and no atomics.  dh[t] depends only on token t.
+ * dw's chain over tokens continues across calls in accumulate mode, so
+ * accumulating batches whose sizes are multiples of 64 tokens reproduces
+ * the bits of one call over their concatenation.
+ * Errors as tim_logprob_forward, plus TIM_EINVAL for null lse / grad_logp
+ * when n > 0 and for flags other than 0 and TIM_BWD_ACCUMULATE_DW.
+ */
+int tim_logprob_backward(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                         const int32_t* ids, const float* lse, const float* grad_logp,
+                         int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
+                         float* dh, float* dw, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * PPO / GRPO clipped surrogate with truncated importance weights.
+ * ---------------------------------------------------------------------- */
+
+/* (host) parameters of tim_ppo_loss. */
+typedef struct {
+    double eps_low;    /* ratios below 1 - eps_low are clipped (>= 0)        */
+    double eps_high;   /* ratios above 1 + eps_high are clipped (>= 0)       */
+    int32_t bypass;    /* 0: ratio over the trainer's recomputed old logp
+                          ("recompute"); 1: over the rollout's ("bypass")
+                          (VeXact eq. (3))                                   */
+    double tis_c;      /* > 0: weight w = min(exp(old_train - old_rollout),
+                          tis_c), the truncated r_corr of the VeXact
+                          compensation table's TIS rows; <= 0: w = 1.  Not
+                          NaN.                                               */
+} tim_ppo_params;
+
+/* (host struct) optional per-token outputs, each [n] fp32 (clipped uint8),
+ * each nullable.  Tokens left out (mask 0, non-finite) get loss 0, grad 0,
+ * ratio 1, contrib 0, clipped 0. */
+typedef struct {
+    float* loss;       /* -w min(r A, clip(r, 1 - eps_low, 1 + eps_high) A)
+                          (VeXact eq. (2))                                   */
+    float* grad;       /* d(mean loss)/d logp[t] = -w [not clipped] r A / n_valid */
+    float* ratio;      /* r = exp(logp - logp_old)                           */
+    float* contrib;    /* -(r - 1) A, the zero-centred contribution (VeXact
+                          eq. (5))                                           */
+    uint8_t* clipped;  /* 1 iff A > 0 and r > 1 + eps_high, or A < 0 and
+                          r < 1 - eps_low (the gradient is dropped)          */
+} tim_ppo_token_out;
+
+/* Indices of the fp64 batch vector of tim_ppo_loss (means over valid
+ * tokens: mask != 0 and finite r, w and A; 0 when there is none). */
+enum {
+    TIM_P_MEAN_LOSS = 0,
+    TIM_P_CLIP_FRAC = 1,
+    TIM_P_MEAN_RATIO = 2,
+    TIM_P_MEAN_TIS_W = 3,
+    TIM_P_MEAN_CONTRIB = 4,
+    TIM_P_N_VALID = 5,
+    TIM_P_N_CLIPPED = 6,
+    TIM_P_N_NAN = 7,
+    TIM_P_NFIELDS = 8
+};
+
+/* Bytes of device workspace tim_ppo_loss needs (independent of n; 0 for
+ * n < 0).  Pure host function. */
+size_t tim_ppo_workspace_bytes(int64_t n);
+
+/*
+ * The token-level clipped surrogate of VeXact eq. (2) with the ratios of
+ * eq. (3), the truncated importance weight of its TIS rows and the
+ * contribution of eq. (5), and the gradient of the token-mean loss by the
+ * current log-probabilities.  The clip test follows "RL: Training Inference
+ * Mismatch" (clipped importance ratios: the gradient is dropped once the
+ * ratio leaves the interval on the side the advantage favours).
+ *
+ *  logp              [n] fp32: current policy log pi_theta(a_t|s_t).
+ *  logp_old_train    [n] fp32: log pi_old^train (trainer recompute).
+ *  logp_old_rollout  [n] fp32: log pi_old^rollout (rollout engine).
+ *  advantages        [n] fp32.
+ *  mask              [n] uint8, nullable (= all tokens).
+ *  p                 (host) parameters.
+ *  tok               (host struct) nullable; members nullable.
+ *  batch             [TIM_P_NFIELDS] fp64 out, nullable.
+ *  workspace         >= tim_ppo_workspace_bytes(n) bytes, 256-byte aligned.
+ *  Errors: TIM_EINVAL for n < 0, null p, negative or NaN eps, NaN tis_c,
+ *  bypass not 0/1, null inputs when n > 0; TIM_EWORKSPACE, TIM_EUNSUPPORTED
+ *  (alignment) as elsewhere.  n == 0 writes the batch vector (zeros).
+ * Per-token arithmetic is fp64 from the fp32 inputs; the sums are reduced in
+ * a fixed order that depends only on n.
+ */
+int tim_ppo_loss(const float* logp, const float* logp_old_train, const float* logp_old_rollout,
+                 const float* advantages, const uint8_t* mask, int64_t n,
+                 const tim_ppo_params* p, const tim_ppo_token_out* tok, double* batch,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,12 @@ Entry points (same names as the C ABI):
   ("Diagnosing Training Inference Mismatch ... (VeXact)", eq. (1) and its
   compensation table; "Train-Inference Consistency", sections 4-5), and the
   K3 form of the sequence rejection (srs-k3 rows of the same table).
+* :func:`tim_logprob_backward` -- ``dh``, ``dW`` of ``L`` through the
+  selected-token log-probability ("RL: Training Inference Mismatch", "log p"
+  chain differentiated), deterministic, no atomics.
+* :func:`tim_ppo_loss` -- the clipped surrogate with recompute / bypass
+  ratios, truncated-r_corr TIS weight and zero-centred contribution
+  (VeXact eqs. (2), (3), (5) and compensation table).
 * :func:`tim_mismatch_extras` -- extreme-token rate, quantiles of the ratio
   and of ``|delta|`` ("训推一致性与 determinism", section 7, metric table)
   and the masked mean relative difference ("RL: Training Inference
@@ -57,11 +63,18 @@ EXTRAS_FIELDS = (
 )
 X_MAX_Q = 4
 ABI_VERSION = 2
+TIM_BWD_ACCUMULATE_DW = 1
+
+# Names of the tim_ppo_loss batch vector, in TIM_P_* index order.
+PPO_FIELDS = ("mean_loss", "clip_frac", "mean_ratio", "mean_tis_w", "mean_contrib",
+              "n_valid", "n_clipped", "n_nan")
 
 # Exported symbols of libtim.so (checked against include/tim.h by the tests).
 EXPORTS = ("tim_abi_version", "tim_status_string", "tim_logprob_workspace_bytes",
            "tim_logprob_forward", "tim_stats_workspace_bytes", "tim_mismatch_stats",
-           "tim_extras_workspace_bytes", "tim_mismatch_extras")
+           "tim_extras_workspace_bytes", "tim_mismatch_extras",
+           "tim_logprob_backward_workspace_bytes", "tim_logprob_backward",
+           "tim_ppo_workspace_bytes", "tim_ppo_loss")
 
 
 class TimError(RuntimeError):
@@ -79,6 +92,15 @@ class _ExtrasParams(ctypes.Structure):
     _fields_ = [("tok_tau", ctypes.c_double), ("n_ratio_q", ctypes.c_int32),
                 ("n_abs_q", ctypes.c_int32), ("ratio_q", ctypes.c_double * X_MAX_Q),
                 ("abs_q", ctypes.c_double * X_MAX_Q)]
+
+
+class _PpoParams(ctypes.Structure):
+    _fields_ = [("eps_low", ctypes.c_double), ("eps_high", ctypes.c_double),
+                ("bypass", ctypes.c_int32), ("tis_c", ctypes.c_double)]
+
+
+class _PpoTokenOut(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("loss", "grad", "ratio", "contrib", "clipped")]
 
 
 class _TokenOut(ctypes.Structure):
@@ -132,6 +154,16 @@ def load_library():
         lib.tim_mismatch_extras.restype = ctypes.c_int
         lib.tim_mismatch_extras.argtypes = [vp, vp, vp, i64, ctypes.POINTER(_ExtrasParams), vp,
                                             vp, sz, vp]
+        lib.tim_logprob_backward_workspace_bytes.restype = sz
+        lib.tim_logprob_backward_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+        lib.tim_logprob_backward.restype = ctypes.c_int
+        lib.tim_logprob_backward.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i64,
+                                             ctypes.c_int, ctypes.c_uint, vp, vp, vp, sz, vp]
+        lib.tim_ppo_workspace_bytes.restype = sz
+        lib.tim_ppo_workspace_bytes.argtypes = [i64]
+        lib.tim_ppo_loss.restype = ctypes.c_int
+        lib.tim_ppo_loss.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(_PpoParams),
+                                     ctypes.POINTER(_PpoTokenOut), vp, vp, sz, vp]
         if lib.tim_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {lib.tim_abi_version()}, "
                                f"expected {ABI_VERSION}: rebuild it")
@@ -341,6 +373,103 @@ def extras_dict(out: torch.Tensor, n_ratio_q: int = 3, n_abs_q: int = 1) -> dict
     res = dict(zip(EXTRAS_FIELDS[:4], v[:4]))
     res["ratio_q"] = v[4:4 + n_ratio_q]
     res["abs_q"] = v[8:8 + n_abs_q]
+    return res
+
+
+def backward_workspace_bytes(n: int, d: int, v: int) -> int:
+    return int(load_library().tim_logprob_backward_workspace_bytes(n, d, v, TIM_BF16))
+
+
+def tim_logprob_backward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
+                         lse: torch.Tensor, grad_logp: torch.Tensor, *, want_dh: bool = True,
+                         want_dw: bool = True, dw: Optional[torch.Tensor] = None,
+                         accumulate_dw: bool = False, workspace: Optional[torch.Tensor] = None,
+                         stream=None):
+    """``(dh, dw)`` (fp32, ``[N, D]`` and ``[V, D]``) of ``L`` through
+    ``logp = log softmax(h W^T)[ids]`` given ``grad_logp = dL/dlogp`` and the
+    forward's ``lse``.  bf16 ``h`` and ``W`` only.  With ``accumulate_dw`` the
+    given ``dw`` is read and the sum over this batch's tokens continues from
+    it."""
+    lib = load_library()
+    for name, t in (("h", h), ("w", w), ("ids", ids), ("lse", lse), ("grad_logp", grad_logp)):
+        _require_gpu(name, t)
+    if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("the backward takes bf16 h and W")
+    if h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
+        raise ValueError("h must be [N, D] and w [V, D]")
+    if h.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("h and w must have unit stride along D")
+    n, d = h.shape
+    v = w.shape[0]
+    for name, t, dt in (("ids", ids, torch.int32), ("lse", lse, torch.float32),
+                        ("grad_logp", grad_logp, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of N entries")
+    dev = h.device
+    dh = torch.empty(n, d, dtype=torch.float32, device=dev) if want_dh else None
+    if want_dw:
+        if dw is None:
+            if accumulate_dw:
+                raise ValueError("accumulate_dw needs the dw tensor to continue from")
+            dw = torch.empty(v, d, dtype=torch.float32, device=dev)
+        elif dw.dtype != torch.float32 or not dw.is_contiguous() or tuple(dw.shape) != (v, d):
+            raise ValueError("dw must be a contiguous fp32 [V, D] tensor")
+    else:
+        dw = None
+    need = lib.tim_logprob_backward_workspace_bytes(n, d, v, TIM_BF16)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    flags = TIM_BWD_ACCUMULATE_DW if accumulate_dw else 0
+    st = lib.tim_logprob_backward(_dptr(h), h.stride(0), _dptr(w), w.stride(0), _dptr(ids),
+                                  _dptr(lse), _dptr(grad_logp), n, d, v, TIM_BF16, flags,
+                                  _dptr(dh), _dptr(dw), _dptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_logprob_backward")
+    return dh, dw
+
+
+def tim_ppo_loss(logp: torch.Tensor, logp_old_train: torch.Tensor,
+                 logp_old_rollout: torch.Tensor, advantages: torch.Tensor,
+                 mask: Optional[torch.Tensor], *, eps_low: float = 0.2, eps_high: float = 0.28,
+                 bypass: bool = False, tis_c: float = 0.0, token_outputs: bool = True,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Clipped surrogate, gradient of its token mean by ``logp``, ratios,
+    zero-centred contributions and clip flags (GPU tensors), and the batch
+    vector (``"batch"``, ``PPO_FIELDS`` order)."""
+    lib = load_library()
+    ins = (logp, logp_old_train, logp_old_rollout, advantages)
+    for name, t in zip(("logp", "logp_old_train", "logp_old_rollout", "advantages"), ins):
+        _require_gpu(name, t)
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    n = logp.numel()
+    if any(t.numel() != n for t in ins):
+        raise ValueError("inconsistent sizes")
+    if mask is not None:
+        _require_gpu("mask", mask)
+        if mask.dtype != torch.uint8 or not mask.is_contiguous() or mask.numel() != n:
+            raise ValueError("mask must be a contiguous uint8 tensor of n entries")
+    dev = logp.device
+    res = {"batch": torch.empty(len(PPO_FIELDS), dtype=torch.float64, device=dev)}
+    tok = None
+    if token_outputs:
+        t = {k: torch.empty(n, dtype=torch.float32, device=dev)
+             for k in ("loss", "grad", "ratio", "contrib")}
+        t["clipped"] = torch.empty(n, dtype=torch.uint8, device=dev)
+        res["token"] = t
+        tok = _PpoTokenOut(*[_dptr(t[k]) for k in ("loss", "grad", "ratio", "contrib", "clipped")])
+    need = lib.tim_ppo_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    prm = _PpoParams(float(eps_low), float(eps_high), int(bool(bypass)), float(tis_c))
+    st = lib.tim_ppo_loss(*[_dptr(x) for x in ins], _dptr(mask), n, ctypes.byref(prm),
+                          ctypes.byref(tok) if tok is not None else None, _dptr(res["batch"]),
+                          _dptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_ppo_loss")
     return res
 
 

@@ -1,0 +1,111 @@
+// mfma_pipe.h — pieces shared by the MFMA tile kernels of libtim.so
+// (lmhead.hip, bwd.hip): operand types, the LDS ring geometry and swizzle,
+// the buffer-to-LDS copy, the fragment reads and the wait helpers.  A tile
+// kernel stages 256-row operand tiles of 128 bytes of K per pipeline stage
+// through a five-position LDS ring and feeds 32x32x16 bf16 (or 32x32x2 fp32)
+// MFMAs from it.
+#pragma once
+
+#include "tim_internal.h"
+
+namespace tim {
+namespace mfma {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// LDS: a ring of five positions, each holding one operand tile of a
+// pipeline stage: 256 rows (W or h) of kStageBytes (128) per row, i.e. 64
+// bf16 or 32 fp32 of K, four MFMA k-steps.  Tiles are filled by
+// buffer_load_dwordx4 ... lds (64 lanes x 16 bytes = 8 rows of 128 bytes per
+// instruction) one (W) or two (h) stages ahead of the MFMAs.  The eight
+// 16-byte chunks of a row are XOR-swizzled with (row >> 1) & 7: the 16 lanes
+// of one ds_read_b128 phase read 16 consecutive rows at one logical chunk,
+// and with 128-byte rows those land on 16 distinct 16-byte bank groups of
+// the 64-bank LDS.
+constexpr int kPos = 5;                               // ring positions, one operand tile each
+constexpr int kOperandBytes = kTileV * kStageBytes;   // 32 KiB
+constexpr int kLdsBytes = kPos * kOperandBytes;       // 160 KiB
+constexpr int kDmaPerStage = 16;                      // per wave: 8 W + 8 h blocks
+static_assert(kTileV == kTileT, "one staging loop serves both operands");
+static_assert(kStageBytes == 128, "swizzle and fragment mapping assume 128-byte rows");
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * kStageBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a raw buffer (base and size in the descriptor) at
+// voffset + soffset, written to LDS at l + 16 * lane.  The row offsets are
+// per lane and fixed; the K offset of a stage is the scalar soffset.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, voff, soff, 0, 0);
+}
+constexpr int kRsrcWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data format,
+                                         // no swizzle, no thread-id add
+
+// Eight 16-byte LDS reads issued in one asm block, not waited for.  The ring
+// is filled by LDS DMA; written as ordinary loads, the compiler cannot tell
+// the slot being read from the slots still being filled and waits for every
+// copy in flight (vmcnt(0)) before each read, which would serialise the
+// pipeline.  The explicit vmcnt waits and barriers of the main loop order
+// these reads after the copies of their stage; frags_ready() below waits for
+// the reads themselves.  Outputs are early-clobber: a read's destination must
+// not overlap a later read's address.
+__device__ __forceinline__ void lds_issue_8x16(u32x4 (&r)[8], uint32_t aA, uint32_t aB) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:4096\n\t"
+        "ds_read_b128 %2, %8 offset:8192\n\t"
+        "ds_read_b128 %3, %8 offset:12288\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:4096\n\t"
+        "ds_read_b128 %6, %9 offset:8192\n\t"
+        "ds_read_b128 %7, %9 offset:12288"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "v"(aA), "v"(aB)
+        : "memory");
+}
+
+// Wait until at most N LDS operations are outstanding; the fragments are
+// passed through so that no use of them can be scheduled before the wait.
+// LDS operations of a wave complete in order, so with the 8 reads of the
+// other fragment set issued later, lgkmcnt(8) means this set has arrived.
+template <int N>
+__device__ __forceinline__ void frags_ready(u32x4 (&f)[8]) {
+    static_assert(N == 0 || N == 8, "lgkmcnt values used here");
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                       "+v"(f[6]), "+v"(f[7]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(8)"
+                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                       "+v"(f[6]), "+v"(f[7]));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt vmcnt(N) only (gfx9 encoding; expcnt and lgkmcnt fields at max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool B> struct BoolConst { static constexpr bool value = B; };
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace mfma
+}  // namespace tim

@@ -139,4 +139,70 @@ int tim_mismatch_extras(const float* logp_train, const float* logp_rollout, cons
     return TIM_OK;
 }
 
+size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype) {
+    if (dtype != TIM_BF16) return 0;
+    tim::BackwardPlan p;
+    if (!tim::make_backward_plan(n, d, v, &p)) return 0;
+    return p.total_bytes;
+}
+
+int tim_logprob_backward(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                         const int32_t* ids, const float* lse, const float* grad_logp,
+                         int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
+                         float* dh, float* dw, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != TIM_BF16 && dtype != TIM_F32) ||
+        flags > TIM_BWD_ACCUMULATE_DW)
+        return TIM_EINVAL;
+    if (ldh < d || ldw < d) return TIM_EINVAL;
+    if (dtype != TIM_BF16) return TIM_EUNSUPPORTED;
+    if (n == 0 && !(dw && !(flags & TIM_BWD_ACCUMULATE_DW))) return TIM_OK;
+    if (!w || (n > 0 && (!h || !ids || !lse || !grad_logp))) return TIM_EINVAL;
+    if (d % 64 != 0) return TIM_EUNSUPPORTED;
+    if ((ldh * 2) % 16 != 0 || (ldw * 2) % 16 != 0) return TIM_EUNSUPPORTED;
+    if ((h && !aligned(h, 16)) || !aligned(w, 16)) return TIM_EUNSUPPORTED;
+    if (n > INT32_MAX) return TIM_EUNSUPPORTED;
+    tim::BackwardPlan p;
+    if (!tim::make_backward_plan(n, d, v, &p)) return TIM_EINVAL;
+    if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+    if (n == 0) {
+        // a batch with no token: dh is empty and dw's sums are zero
+        if (tim::launch_fill_zero(dw, v * d, (hipStream_t)stream) != hipSuccess) return TIM_EHIP;
+        return TIM_OK;
+    }
+    if (tim::launch_logprob_backward(p, h, ldh, w, ldw, ids, lse, grad_logp, dh, dw,
+                                     (flags & TIM_BWD_ACCUMULATE_DW) != 0, workspace,
+                                     (hipStream_t)stream) != hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
+size_t tim_ppo_workspace_bytes(int64_t n) {
+    if (n < 0) return 0;
+    return tim::ppo_workspace_bytes();
+}
+
+int tim_ppo_loss(const float* logp, const float* logp_old_train, const float* logp_old_rollout,
+                 const float* advantages, const uint8_t* mask, int64_t n,
+                 const tim_ppo_params* p, const tim_ppo_token_out* tok, double* batch,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    static_assert(TIM_P_NFIELDS == tim::kPpoOutFields, "ppo layout");
+    if (n < 0 || !p) return TIM_EINVAL;
+    if (!(p->eps_low >= 0.0) || !(p->eps_high >= 0.0) || isnan(p->tis_c) ||
+        (p->bypass != 0 && p->bypass != 1))
+        return TIM_EINVAL;
+    if (n > 0 && (!logp || !logp_old_train || !logp_old_rollout || !advantages)) return TIM_EINVAL;
+    if (!workspace || workspace_bytes < tim::ppo_workspace_bytes()) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+    tim_ppo_token_out t{};
+    if (tok) t = *tok;
+    if (tim::launch_ppo_loss(logp, logp_old_train, logp_old_rollout, advantages, mask, n,
+                             p->eps_low, p->eps_high, p->bypass, p->tis_c, t.loss, t.grad,
+                             t.ratio, t.contrib, t.clipped, batch, workspace,
+                             (hipStream_t)stream) != hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
 }  // extern "C"

@@ -128,6 +128,40 @@ hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const fl
                                   const uint8_t* mask, const XParamsDev& prm, double* out,
                                   void* workspace, hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Backward of the log-probability and the PPO surrogate (bwd.hip)
+// ---------------------------------------------------------------------------
+
+// Workspace of tim_logprob_backward (offsets 256-byte aligned): W^T [D][Vp],
+// h^T [D][Np], dz^T [Vp][Np] and dz [Np][Vp], bf16, with Vp and Np the
+// vocabulary and token counts rounded up to multiples of 64.
+struct BackwardPlan {
+    int64_t n, d, v, npad, vpad;
+    size_t wt_off, ht_off, dzt_off, dz_off, total_bytes;
+};
+
+bool make_backward_plan(int64_t n, int64_t d, int64_t v, BackwardPlan* p);
+
+hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t ldh,
+                                   const void* w, int64_t ldw, const int32_t* ids,
+                                   const float* lse, const float* g, float* dh, float* dw,
+                                   bool accumulate_dw, void* workspace, hipStream_t st);
+
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t st);
+
+// Batch vector of tim_ppo_loss (the TIM_P_* indices of tim.h).
+constexpr int kPpoOutMeanLoss = 0, kPpoOutClipFrac = 1, kPpoOutMeanRatio = 2,
+              kPpoOutMeanTisW = 3, kPpoOutMeanContrib = 4, kPpoOutNValid = 5,
+              kPpoOutNClipped = 6, kPpoOutNNan = 7, kPpoOutFields = 8;
+
+size_t ppo_workspace_bytes();
+
+hipError_t launch_ppo_loss(const float* logp, const float* old_train, const float* old_rollout,
+                           const float* adv, const uint8_t* mask, int64_t n, double eps_lo,
+                           double eps_hi, int bypass, double tis_c, float* loss, float* grad,
+                           float* ratio, float* contrib, uint8_t* clipped, double* batch,
+                           void* workspace, hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace tim

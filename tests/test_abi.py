@@ -165,3 +165,38 @@ def test_binding_extras_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         tim.tim_mismatch_extras(torch.zeros(4), torch.zeros(4), None, tok_tau=0.1)
+
+
+def test_backward_and_ppo_argument_errors(lib):
+    fwd = lambda **kw: lib.tim_logprob_backward(
+        kw.get("h", FAKE), kw.get("ldh", 64), kw.get("w", FAKE), kw.get("ldw", 64),
+        kw.get("ids", FAKE), kw.get("lse", FAKE), kw.get("g", FAKE), kw.get("n", 4),
+        kw.get("d", 64), kw.get("v", 100), kw.get("dtype", 0), kw.get("flags", 0),
+        kw.get("dh", FAKE), kw.get("dw", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
+    assert fwd(n=-1) == tim.TIM_EINVAL
+    assert fwd(flags=2) == tim.TIM_EINVAL
+    assert fwd(dtype=1) == tim.TIM_EUNSUPPORTED                     # bf16 only
+    assert fwd(lse=None) == tim.TIM_EINVAL
+    assert fwd(g=None) == tim.TIM_EINVAL
+    assert fwd(d=96, ldh=96, ldw=96) == tim.TIM_EUNSUPPORTED
+    assert fwd(ws=None) == tim.TIM_EWORKSPACE
+    assert fwd(ws=FAKE + 16) == tim.TIM_EUNSUPPORTED
+    assert lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 1) == 0
+    b = lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 0)
+    # W^T, h^T and dz in both layouts, bf16, vocabulary padded to 151936 (a
+    # multiple of 64 already)
+    assert b >= 2 * (4096 * 151936 + 4096 * 8192 + 2 * 151936 * 8192)
+    p = tim._PpoParams(0.2, 0.28, 0, 2.0)
+    ppo = lambda **kw: lib.tim_ppo_loss(FAKE, FAKE, FAKE, FAKE, None, kw.get("n", 10),
+                                        ctypes.byref(kw.get("p", p)) if kw.get("params", True)
+                                        else None, None, None, kw.get("ws", FAKE),
+                                        kw.get("wsb", 1 << 20), None)
+    assert ppo(n=-1) == tim.TIM_EINVAL
+    assert ppo(params=False) == tim.TIM_EINVAL
+    assert ppo(p=tim._PpoParams(-0.1, 0.28, 0, 0.0)) == tim.TIM_EINVAL
+    assert ppo(p=tim._PpoParams(0.2, float("nan"), 0, 0.0)) == tim.TIM_EINVAL
+    assert ppo(p=tim._PpoParams(0.2, 0.28, 2, 0.0)) == tim.TIM_EINVAL
+    assert ppo(p=tim._PpoParams(0.2, 0.28, 0, float("nan"))) == tim.TIM_EINVAL
+    assert ppo(ws=None) == tim.TIM_EWORKSPACE
+    assert ppo(wsb=8) == tim.TIM_EWORKSPACE
+    assert ppo(ws=FAKE + 8) == tim.TIM_EUNSUPPORTED

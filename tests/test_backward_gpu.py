@@ -1,0 +1,197 @@
+"""GPU parity of tim_logprob_backward and tim_ppo_loss against the fp64 oracle.
+
+Backward tolerances follow from the arithmetic: dz is rounded to bf16 once
+(relative error <= 2^-9 per element) and the fp32 logits carry ~1e-5 of
+absolute error into the softmax, so |dh - dh_ref|[t, k] <= 2^-7 * 2 |g_t| *
+max_v |W[v, k]| (sum_v |dz[t, v]| <= 2 |g_t|) and |dW - dW_ref|[v, k] <=
+2^-7 * sum_t |dz[t, v]| |h[t, k]| + 1e-6 * max |g| max |h|, both with a 4x
+margin over the rounding bound.  Invariance and determinism are bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_logprobs_amd as tim
+import oracle
+import workloads
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[backward-gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bf16_bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _case(n, d, v, seed, zero_frac=0.2):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    h = torch.randn(n, d, generator=g).to(torch.bfloat16)
+    w = (torch.randn(v, d, generator=g) * 0.05).to(torch.bfloat16)
+    ids = torch.randint(0, v, (n,), generator=g, dtype=torch.int32)
+    gr = torch.randn(n, generator=g, dtype=torch.float32)
+    gr[torch.rand(n, generator=g) < zero_frac] = 0.0
+    return h.to(DEV), w.to(DEV), ids.to(DEV), gr.to(DEV)
+
+
+def _dz_abs(h, w, ids, gr, rows_v):
+    """|dz[:, rows_v]| in fp64 from the oracle's lse (for the dW bound)."""
+    hd = h.float().double().cpu().numpy()
+    wd = w.float().double().cpu().numpy()[rows_v]
+    _, lse, _, _ = oracle.logprob(h.cpu(), w.cpu(), ids.cpu(), dtype=oracle.BF16)
+    z = hd @ wd.T
+    p = np.exp(z - lse[:, None])
+    onehot = (ids.cpu().numpy()[:, None] == np.asarray(rows_v)[None, :]).astype(np.float64)
+    return np.abs(gr.double().cpu().numpy()[:, None] * (onehot - p))
+
+
+def check_dh(dh, dh_ref, gr, w, rows, label):
+    wmax = w.float().abs().amax(dim=0).double().cpu().numpy()          # max_v |W[v, k]|
+    g = np.abs(gr.double().cpu().numpy()[rows])
+    tol = 2.0 ** -7 * 2 * g[:, None] * wmax[None, :] + 1e-7
+    err = np.abs(dh - dh_ref)
+    say(f"{label}: dh worst err {err.max():.3e}, worst err/tol {(err / tol).max():.3f}")
+    assert np.all(err <= tol), f"{label}: dh"
+
+
+def check_dw(dw, dw_ref, dzabs, h, gr, label):
+    ha = h.float().abs().double().cpu().numpy()
+    tol = 2.0 ** -7 * (dzabs.T @ ha) + 1e-6 * float(gr.abs().max()) * float(ha.max())
+    err = np.abs(dw - dw_ref)
+    say(f"{label}: dW worst err {err.max():.3e}, worst err/tol {(err / tol).max():.3f}")
+    assert np.all(err <= tol), f"{label}: dW"
+
+
+def test_backward_parity_ragged_sizes():
+    # N, V not multiples of 64 or 256; one id out of range (contributes nothing)
+    n, d, v = 300, 256, 2000
+    h, w, ids, gr = _case(n, d, v, seed=1)
+    ids[17] = v + 5
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    torch.cuda.synchronize()
+    dh_ref, dw_ref = oracle.logprob_backward(bf16_bits(h), bf16_bits(w), ids.cpu(), gr.cpu(),
+                                             dtype=oracle.BF16)
+    check_dh(dh.double().cpu().numpy(), dh_ref, gr, w, np.arange(n), "ragged")
+    gr_eff = gr.clone()
+    gr_eff[17] = 0.0                                  # the out-of-range id's row
+    ids_c = ids.clone()
+    ids_c[17] = 0
+    dzabs = _dz_abs(h, w, ids_c, gr_eff, np.arange(v))
+    check_dw(dw.double().cpu().numpy(), dw_ref, dzabs, h, gr_eff, "ragged")
+    assert torch.all(dh[17] == 0)
+
+
+def test_backward_full_size_sparse_gradient():
+    # the Qwen3-8B-shaped head at its full size, with an upstream gradient on
+    # 16 tokens so that the oracle computes only those rows
+    w8 = workloads.make("qwen3_8b", device=DEV)
+    h, w, ids = w8.h, w8.w, w8.ids
+    n, v = h.shape[0], w.shape[0]
+    rng = np.random.default_rng(5)
+    tok = np.sort(rng.choice(n, 16, replace=False))
+    gr = torch.zeros(n, dtype=torch.float32, device=DEV)
+    gr[torch.as_tensor(tok, device=DEV)] = torch.as_tensor(rng.normal(0, 1, 16), dtype=torch.float32,
+                                                          device=DEV)
+    say("full size: forward + backward")
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    torch.cuda.synchronize()
+    rows_v = np.unique(np.concatenate([ids.cpu().numpy()[tok], rng.choice(v, 16, replace=False),
+                                       [v - 1]]))
+    zero_tok = np.setdiff1d(np.arange(n), tok)[:4]
+    dh_rows = np.concatenate([tok, zero_tok])
+    say("full size: oracle rows")
+    dh_ref, dw_ref = oracle.logprob_backward(bf16_bits(h), bf16_bits(w), ids.cpu(), gr.cpu(),
+                                             dtype=oracle.BF16, dh_rows=dh_rows, dw_rows=rows_v)
+    check_dh(dh[torch.as_tensor(dh_rows, device=DEV)].double().cpu().numpy(), dh_ref, gr, w,
+             dh_rows, "full size")
+    hs = h[torch.as_tensor(tok, device=DEV)]
+    dzabs = _dz_abs(hs, w, ids[torch.as_tensor(tok, device=DEV)], gr[torch.as_tensor(tok, device=DEV)],
+                    rows_v)
+    check_dw(dw[torch.as_tensor(rows_v, device=DEV)].double().cpu().numpy(), dw_ref, dzabs, hs,
+             gr[torch.as_tensor(tok, device=DEV)], "full size")
+
+
+def test_dh_rows_do_not_depend_on_the_batch_and_runs_repeat():
+    n, d, v = 512, 256, 3000
+    h, w, ids, gr = _case(n, d, v, seed=2)
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    dh2, dw2 = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    a, b = 64, 197
+    _, lse_s, _ = tim.tim_logprob_forward(h[a:b].contiguous(), w, ids[a:b].contiguous(),
+                                          return_lse=True)
+    dh_s, _ = tim.tim_logprob_backward(h[a:b].contiguous(), w, ids[a:b].contiguous(), lse_s,
+                                       gr[a:b].contiguous(), want_dw=False)
+    torch.cuda.synchronize()
+    assert torch.equal(lse_s.view(torch.int32), lse[a:b].view(torch.int32))
+    assert torch.equal(dh_s.view(torch.int32), dh[a:b].view(torch.int32))
+    assert torch.equal(dh.view(torch.int32), dh2.view(torch.int32))
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+
+
+def test_dw_accumulated_over_micro_batches_is_bitwise_one_batch():
+    n, d, v = 640, 256, 1500
+    h, w, ids, gr = _case(n, d, v, seed=3)
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    _, dw_full = tim.tim_logprob_backward(h, w, ids, lse, gr, want_dh=False)
+    dw = torch.zeros(v, d, dtype=torch.float32, device=DEV)
+    for a, b in ((0, 256), (256, 448), (448, 640)):     # multiples of 64 tokens
+        tim.tim_logprob_backward(h[a:b].contiguous(), w, ids[a:b].contiguous(),
+                                 lse[a:b].contiguous(), gr[a:b].contiguous(), want_dh=False,
+                                 dw=dw, accumulate_dw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), dw_full.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# surrogate
+# ---------------------------------------------------------------------------
+
+def _ppo_inputs(n, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    ot = -torch.rand(n, generator=g) * 4
+    orr = ot + torch.randn(n, generator=g) * 0.05
+    lp = ot + torch.randn(n, generator=g) * 0.3
+    adv = torch.randn(n, generator=g)
+    mask = (torch.rand(n, generator=g) < 0.85).to(torch.uint8)
+    lp[5] = float("nan")
+    mask[5] = 1
+    return [x.to(DEV) for x in (lp, ot, orr, adv, mask)]
+
+
+@pytest.mark.parametrize("n", [1, 1000, 100_003])
+@pytest.mark.parametrize("mode", ["recompute", "recompute+tis", "bypass"])
+def test_ppo_parity(n, mode):
+    lp, ot, orr, adv, mask = _ppo_inputs(max(n, 6), seed=n)
+    lp, ot, orr, adv, mask = (x[:n].contiguous() for x in (lp, ot, orr, adv, mask))
+    kw = dict(eps_low=0.2, eps_high=0.28, bypass=mode == "bypass",
+              tis_c=2.0 if mode == "recompute+tis" else 0.0)
+    res = tim.tim_ppo_loss(lp, ot, orr, adv, mask, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.ppo_loss(lp.cpu(), ot.cpu(), orr.cpu(), adv.cpu(), mask.cpu(),
+                          eps_lo=kw["eps_low"], eps_hi=kw["eps_high"], bypass=kw["bypass"],
+                          tis_c=kw["tis_c"])
+    t = res["token"]
+    np.testing.assert_array_equal(t["clipped"].cpu().numpy(), ref["clipped"])
+    for k in ("loss", "grad", "ratio", "contrib"):
+        np.testing.assert_allclose(t[k].double().cpu().numpy(), ref[k], rtol=1e-6, atol=1e-30,
+                                   err_msg=f"{mode} {k}")
+    got = dict(zip(tim.PPO_FIELDS, res["batch"].cpu().tolist()))
+    for k in tim.PPO_FIELDS:
+        if k.startswith("n_") or k == "clip_frac":
+            assert got[k] == ref["batch"][k], k
+        else:
+            m = max(got["n_valid"], 1)
+            assert got[k] == pytest.approx(ref["batch"][k], rel=2 * m * 2.0 ** -53 + 1e-15,
+                                           abs=1e-300), k
+    say(f"ppo {mode} n={n}: loss {got['mean_loss']:.4e}, clip {got['clip_frac']:.3f}")
