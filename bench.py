@@ -10,7 +10,8 @@ V=151936, bf16 inputs, fp32 accumulation.
 Prints ONE JSON line on stdout.  Diagnostics go to stderr.  Also reported:
 the stats pass on 2^28 tokens (HBM bandwidth), the extra metrics (extreme
 rate, relative difference, ratio quantiles, |delta| p95) on the workload and
-on 2^28 tokens, the price of batch invariance against the free schedule, and
+on 2^28 tokens, the backward (dh, dW) on the workload, the PPO surrogate on
+2^28 tokens, the price of batch invariance against the free schedule, and
 the fp64 oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
@@ -78,6 +79,10 @@ def main():
                     help="run only the stats pass at 2^stats-log2 tokens (for a kernel trace)")
     ap.add_argument("--extras-scale-only", action="store_true",
                     help="run only the extra metrics at 2^stats-log2 tokens (for a kernel trace)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="run only the backward on the workload (for a kernel trace)")
+    ap.add_argument("--ppo-scale-only", action="store_true",
+                    help="run only the surrogate at 2^stats-log2 tokens (for a kernel trace)")
     ap.add_argument("--traffic-out", default=PMC_SUMMARY)
     ap.add_argument("--traffic-command", default="",
                     help="the commands that made the CSV files, recorded in the summary")
@@ -114,9 +119,15 @@ def main():
         print(json.dumps(extras_scale(tim, workloads, torch, np, args.stats_log2, tau)),
               flush=True)
         return
+    if args.ppo_scale_only:
+        print(json.dumps(ppo_scale(tim, torch, np, args.stats_log2)), flush=True)
+        return
     name = "qwen3_8b"
     log(f"generating workload {name}")
     wl = workloads.make(name, device=dev)
+    if args.backward_only:
+        print(json.dumps(backward_measure(tim, wl, torch, np)), flush=True)
+        return
     sp = wl.spec
     n, d, v = sp.n, sp.d, sp.v
     torch.cuda.synchronize()
@@ -183,6 +194,8 @@ def main():
     }
 
     if not args.no_extras:
+        out["backward"] = backward_measure(tim, wl, torch, np)
+        out["ppo"] = ppo_scale(tim, torch, np, args.stats_log2)
         out["extras"] = extras_measure(tim, workloads, wl, torch, np, args.stats_log2)
         out["stats_scale"] = stats_scale(tim, workloads, torch, np, args.stats_log2)
         out["invariance_cost"] = invariance_cost(tim, wl, torch, np)
@@ -356,6 +369,68 @@ def extras_scale(tim, workloads, torch, np, log2n, tok_tau):
     return {"tokens": n, "ms": ms, "algorithmic_bytes": algo, "achieved_GBs": gbs,
             "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS, "ratio_q": list(XQ_RATIO),
             "abs_q": list(XQ_ABS), "tok_tau": tok_tau}
+
+
+def backward_measure(tim, wl, torch, np, reps=5):
+    """tim_logprob_backward on the workload with a dense upstream gradient:
+    the logits recomputed (2 N D V FLOP), dh = dz W and dW = dz^T h (2 N D V
+    each), against dense bf16 MFMA peak."""
+    sp = wl.spec
+    n, d, v = sp.n, sp.d, sp.v
+    _, lse, _ = tim.tim_logprob_forward(wl.h, wl.w, wl.ids, return_lse=True)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    grad = torch.randn(n, generator=g, device="cuda", dtype=torch.float32) / n
+    ws = torch.empty(tim.backward_workspace_bytes(n, d, v), dtype=torch.uint8, device="cuda")
+    dh = torch.empty(n, d, dtype=torch.float32, device="cuda")
+    dw = torch.empty(v, d, dtype=torch.float32, device="cuda")
+    fn = lambda: tim.tim_logprob_backward(wl.h, wl.w, wl.ids, lse, grad, dw=dw, workspace=ws)
+    ms = time_calls(fn, torch, np, reps=reps, warm=1)
+    flops = 3 * 2.0 * n * d * v
+    tf = flops / (ms / 1e3) / 1e12
+    log(f"backward: {ms:.3f} ms, {tf:.1f} TFLOP/s ({tf / PEAK_BF16_TFLOPS:.1%} of bf16 peak), "
+        f"workspace {ws.numel() / 2**30:.2f} GiB")
+    del ws, dh, dw
+    torch.cuda.empty_cache()
+    return {"ms": ms, "flops": flops, "achieved_TFLOPs": tf, "peak_TFLOPs": PEAK_BF16_TFLOPS,
+            "frac": tf / PEAK_BF16_TFLOPS, "tokens": n, "hidden": d, "vocab": v}
+
+
+def ppo_scale(tim, torch, np, log2n):
+    """tim_ppo_loss on 2^log2n tokens with every per-token output: 17 bytes
+    read (four fp32 inputs and the mask) and 17 written per token."""
+    n = 1 << log2n
+    g = torch.Generator(device="cuda").manual_seed(12)
+    ot = -torch.rand(n, generator=g, device="cuda") * 4
+    orr = ot + torch.randn(n, generator=g, device="cuda") * 0.05
+    lp = ot + torch.randn(n, generator=g, device="cuda") * 0.3
+    adv = torch.randn(n, generator=g, device="cuda")
+    mask = (torch.rand(n, generator=g, device="cuda") < 0.9).to(torch.uint8)
+    ws = torch.empty(int(tim.load_library().tim_ppo_workspace_bytes(n)), dtype=torch.uint8,
+                     device="cuda")
+    outs = {k: torch.empty(n, dtype=torch.float32, device="cuda")
+            for k in ("loss", "grad", "ratio", "contrib")}
+    clipped = torch.empty(n, dtype=torch.uint8, device="cuda")
+    lib = tim.load_library()
+    tok = tim._PpoTokenOut(*[outs[k].data_ptr() for k in ("loss", "grad", "ratio", "contrib")],
+                           clipped.data_ptr())
+    prm = tim._PpoParams(0.2, 0.28, 0, 2.0)
+    batch = torch.empty(len(tim.PPO_FIELDS), dtype=torch.float64, device="cuda")
+    import ctypes
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def fn():
+        st = lib.tim_ppo_loss(lp.data_ptr(), ot.data_ptr(), orr.data_ptr(), adv.data_ptr(),
+                              mask.data_ptr(), n, ctypes.byref(prm), ctypes.byref(tok),
+                              batch.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        assert st == tim.TIM_OK
+    ms = time_calls(fn, torch, np, reps=5)
+    algo = 34 * n + 8 * len(tim.PPO_FIELDS)
+    gbs = algo / (ms / 1e3) / 1e9
+    log(f"ppo 2^{log2n}: {ms:.3f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    del ot, orr, lp, adv, mask, outs, clipped, ws
+    torch.cuda.empty_cache()
+    return {"tokens": n, "ms": ms, "algorithmic_bytes": algo, "achieved_GBs": gbs,
+            "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
 
 
 def invariance_cost(tim, wl, torch, np):

@@ -366,7 +366,8 @@ gemm_nt_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 
 constexpr int kPpoThreads = 256;
-constexpr int kPpoMaxBlocks = 1024;
+constexpr int kPpoMaxBlocks = 16384;
+constexpr int kPpoUnroll = 4;        // tokens per thread per loop trip, loads first
 
 struct PpoPart {
     double loss, ratio, w, contrib;
@@ -384,46 +385,69 @@ struct PpoArgs {
 };
 
 // Per token, fp64 from the fp32 inputs; block partials in a fixed tree.
-// Thread tid of block b takes tokens b*256 + tid + j*grid*256.
+// Thread tid of block b takes tokens b*256 + tid + j*grid*256, kPpoUnroll of
+// them per loop trip with every load issued first.
+__device__ __forceinline__ void ppo_token(const PpoArgs& a, int64_t t, float lp, float ot,
+                                          float orr, float ad, bool in, PpoPart& acc) {
+    double l_t = 0, g_t = 0, r_t = 1, c_t = 0;
+    int clip_t = 0;
+    if (in) {
+        const double old = a.bypass ? (double)orr : (double)ot;
+        const double r = exp((double)lp - old);
+        const double w = a.tis_c > 0.0 ? fmin(exp((double)ot - (double)orr), a.tis_c) : 1.0;
+        const double adv = (double)ad;
+        if (!isfinite(r) || !isfinite(w) || !isfinite(adv)) {
+            acc.nnan++;
+        } else {
+            const double hi = 1.0 + a.eps_hi, lo = 1.0 - a.eps_lo;
+            const double rc = r < lo ? lo : (r > hi ? hi : r);
+            const double sur = fmin(r * adv, rc * adv);
+            const bool active = (adv > 0.0 && r > hi) || (adv < 0.0 && r < lo);
+            l_t = -w * sur;
+            g_t = active ? 0.0 : -w * r * adv;
+            r_t = r;
+            c_t = -(r - 1.0) * adv;
+            clip_t = active;
+            acc.nvalid++;
+            acc.nclip += active;
+            acc.loss += l_t;
+            acc.ratio += r;
+            acc.w += w;
+            acc.contrib += c_t;
+        }
+    }
+    if (a.loss) a.loss[t] = (float)l_t;
+    if (a.grad) a.grad[t] = (float)g_t;      // scaled by 1 / n_valid afterwards
+    if (a.ratio) a.ratio[t] = (float)r_t;
+    if (a.contrib) a.contrib[t] = (float)c_t;
+    if (a.clipped) a.clipped[t] = (uint8_t)clip_t;
+}
+
 __global__ void __launch_bounds__(kPpoThreads)
 ppo_token_kernel(PpoArgs a, PpoPart* __restrict__ part) {
     __shared__ PpoPart sh[kPpoThreads];
     PpoPart acc{0, 0, 0, 0, 0, 0, 0, 0};
     const int64_t stride = (int64_t)gridDim.x * kPpoThreads;
-    for (int64_t t = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; t < a.n; t += stride) {
-        double l_t = 0, g_t = 0, r_t = 1, c_t = 0;
-        int clip_t = 0;
-        if (!a.mask || a.mask[t] != 0) {
-            const double old = a.bypass ? (double)a.old_rollout[t] : (double)a.old_train[t];
-            const double r = exp((double)a.logp[t] - old);
-            const double w = a.tis_c > 0.0
-                ? fmin(exp((double)a.old_train[t] - (double)a.old_rollout[t]), a.tis_c) : 1.0;
-            const double adv = (double)a.adv[t];
-            if (!isfinite(r) || !isfinite(w) || !isfinite(adv)) {
-                acc.nnan++;
-            } else {
-                const double hi = 1.0 + a.eps_hi, lo = 1.0 - a.eps_lo;
-                const double rc = r < lo ? lo : (r > hi ? hi : r);
-                const double sur = fmin(r * adv, rc * adv);
-                const bool active = (adv > 0.0 && r > hi) || (adv < 0.0 && r < lo);
-                l_t = -w * sur;
-                g_t = active ? 0.0 : -w * r * adv;
-                r_t = r;
-                c_t = -(r - 1.0) * adv;
-                clip_t = active;
-                acc.nvalid++;
-                acc.nclip += active;
-                acc.loss += l_t;
-                acc.ratio += r;
-                acc.w += w;
-                acc.contrib += c_t;
-            }
+    for (int64_t base = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; base < a.n;
+         base += kPpoUnroll * stride) {
+        float lp[kPpoUnroll], ot[kPpoUnroll], orr[kPpoUnroll], ad[kPpoUnroll];
+        bool in[kPpoUnroll];
+#pragma unroll
+        for (int j = 0; j < kPpoUnroll; ++j) {
+            const int64_t t = base + j * stride;
+            const int64_t tc = t < a.n ? t : base;             // base < n: in bounds
+            lp[j] = a.logp[tc];
+            ot[j] = a.old_train[tc];
+            orr[j] = a.old_rollout[tc];
+            ad[j] = a.adv[tc];
+            const uint32_t mk = a.mask ? (uint32_t)(a.mask[tc] != 0) : 1u;   // no short-circuit
+            in[j] = ((uint32_t)(t < a.n) & mk) != 0;
         }
-        if (a.loss) a.loss[t] = (float)l_t;
-        if (a.grad) a.grad[t] = (float)g_t;      // scaled by 1 / n_valid afterwards
-        if (a.ratio) a.ratio[t] = (float)r_t;
-        if (a.contrib) a.contrib[t] = (float)c_t;
-        if (a.clipped) a.clipped[t] = (uint8_t)clip_t;
+#pragma unroll
+        for (int j = 0; j < kPpoUnroll; ++j) {
+            const int64_t t = base + j * stride;
+            if (t < a.n) ppo_token(a, t, lp[j], ot[j], orr[j], ad[j], in[j], acc);
+        }
     }
     sh[threadIdx.x] = acc;
     __syncthreads();
@@ -615,7 +639,7 @@ hipError_t launch_ppo_loss(const float* logp, const float* old_train, const floa
                            void* workspace, hipStream_t st) {
     PpoPart* part = (PpoPart*)workspace;
     double* inv_n = (double*)((unsigned char*)workspace + align_up(sizeof(PpoPart) * kPpoMaxBlocks, 256));
-    int64_t nblk = (n + kPpoThreads * 8 - 1) / (kPpoThreads * 8);
+    int64_t nblk = (n + kPpoThreads * kPpoUnroll * 4 - 1) / (kPpoThreads * kPpoUnroll * 4);
     if (nblk < 1) nblk = 1;
     if (nblk > kPpoMaxBlocks) nblk = kPpoMaxBlocks;
     PpoArgs a{logp, old_train, old_rollout, adv, mask, n, eps_lo, eps_hi, tis_c, bypass,
