@@ -190,7 +190,7 @@ def test_backward_and_ppo_argument_errors(lib):
     ppo = lambda **kw: lib.tim_ppo_loss(FAKE, FAKE, FAKE, FAKE, None, kw.get("n", 10),
                                         ctypes.byref(kw.get("p", p)) if kw.get("params", True)
                                         else None, None, None, kw.get("ws", FAKE),
-                                        kw.get("wsb", 1 << 20), None)
+                                        kw.get("wsb", 1 << 24), None)
     assert ppo(n=-1) == tim.TIM_EINVAL
     assert ppo(params=False) == tim.TIM_EINVAL
     assert ppo(p=tim._PpoParams(-0.1, 0.28, 0, 0.0)) == tim.TIM_EINVAL
