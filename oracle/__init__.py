@@ -13,6 +13,13 @@ Functions and the passages they follow:
 
 * :func:`logprob` -- ``logp_t = z_t[a_t] - log sum_v exp z_t[v]`` with
   ``z_t = W h_t``: "RL: Training Inference Mismatch", section "log p".
+* :func:`logprob_ex` -- the same at a sampling temperature ``tau`` (the
+  softmax of ``z / tau``) with the entropy of that distribution: "RL:
+  Training Inference Mismatch", logits-processor section; entropy as a
+  monitored quantity: "训推一致性与 determinism", section 2.
+* :func:`rmsnorm` -- ``y = gamma * x / sqrt(mean(x^2) + eps)`` per row
+  ("训推一致性与 determinism", section 6 kernel table; VeXact methodology,
+  batch-invariant RMSNorm).
 * :func:`mismatch_stats` -- token-level TIM ``delta = train - rollout``
   ("Diagnosing Training Inference Mismatch ... (VeXact)", eq. (1)), ratio,
   k1/k2/k3 ("RL: Training Inference Mismatch", KL-estimator table), TIS
@@ -105,6 +112,14 @@ def _load():
         lib.or_bf16_round_rne.argtypes = [ctypes.c_double]
         lib.or_available_cpus.restype = c_int
         lib.or_batch_nfields.restype = c_int
+        lib.or_logprob_rows_ex.restype = c_int
+        lib.or_logprob_rows_ex.argtypes = [vp, c_i64, vp, c_i64, vp, c_int, c_i64,
+                                           c_i64, vp, c_i64, ctypes.c_double, vp, vp, vp, vp,
+                                           c_int]
+        lib.or_rmsnorm.restype = c_int
+        lib.or_rmsnorm.argtypes = [vp, c_i64, vp, c_int, c_i64, c_i64, ctypes.c_double, vp, vp]
+        lib.or_bf16_round_rne_n.restype = None
+        lib.or_bf16_round_rne_n.argtypes = [vp, vp, c_i64]
         lib.or_logprob_rows.restype = c_int
         lib.or_logprob_rows.argtypes = [vp, c_i64, vp, c_i64, vp, c_int, c_i64,
                                         c_i64, vp, c_i64, vp, vp, vp, c_int]
@@ -157,9 +172,55 @@ def bf16_decode(bits) -> np.ndarray:
 
 
 def bf16_round_rne(x) -> np.ndarray:
-    lib = _load()
-    a = np.asarray(x, dtype=np.float64).ravel()
-    return np.array([lib.or_bf16_round_rne(float(v)) for v in a], dtype=np.uint16)
+    """Bits of the bf16 nearest to each element (ties to even), same shape."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, np.uint16)
+    _load().or_bf16_round_rne_n(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def rmsnorm(x, gamma, *, dtype: int, eps: float):
+    """fp64 ``(y [N, D], rstd [N])`` of ``y = gamma * x * rstd``,
+    ``rstd = 1 / sqrt(mean(x^2) + eps)``.  bf16 inputs as uint16 bits (or
+    bf16 torch tensors), fp32 as float32."""
+    el = np.uint16 if dtype == BF16 else np.float32
+    x = _as_host_array(x, el)
+    gamma = _as_host_array(gamma, el)
+    n, d = x.shape
+    assert gamma.shape == (d,)
+    y = np.empty((n, d), np.float64)
+    rstd = np.empty(n, np.float64)
+    if _load().or_rmsnorm(_ptr(x), d, _ptr(gamma), dtype, n, d, float(eps), _ptr(y),
+                          _ptr(rstd)) != 0:
+        raise ValueError("or_rmsnorm rejected its arguments")
+    return y, rstd
+
+
+def logprob_ex(h, w, ids, *, dtype: int, temperature: float = 1.0, rows=None,
+               nthreads: int = 0) -> dict:
+    """fp64 ``logp``, ``lse``, ``zsel`` (= ``z_a / tau``) and ``entropy`` of
+    ``softmax(z / tau)`` for token rows ``rows`` (default: all)."""
+    el = np.uint16 if dtype == BF16 else np.float32
+    h = _as_host_array(h, el)
+    w = _as_host_array(w, el)
+    ids = _as_host_array(ids, np.int32)
+    n, d = h.shape
+    v, d2 = w.shape
+    assert d == d2 and ids.shape == (n,)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = n if rows_arr is None else rows_arr.size
+    out = {k: np.empty(nr, np.float64) for k in ("logp", "lse", "zsel", "entropy")}
+    if nr == 0:
+        return out
+    if nthreads <= 0:
+        nthreads = min(available_cpus(), MAX_THREADS)
+    used = _load().or_logprob_rows_ex(_ptr(h), d, _ptr(w), d, _ptr(ids), dtype, d, v,
+                                      _ptr(rows_arr), nr, float(temperature),
+                                      _ptr(out["logp"]), _ptr(out["lse"]), _ptr(out["zsel"]),
+                                      _ptr(out["entropy"]), int(nthreads))
+    if used < 0:
+        raise ValueError("or_logprob_rows_ex rejected its arguments")
+    return out
 
 
 def logprob(h, w, ids, *, dtype: int, rows=None, nthreads: int = 0):

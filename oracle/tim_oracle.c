@@ -15,6 +15,11 @@
  *                       logp = z_a - lse.
  *                       "RL: Training Inference Mismatch", section "log p"
  *                       (hidden -> LM head -> log-softmax -> gather).
+ *   or_logprob_rows_ex  the same for softmax(z / tau), with its entropy
+ *                       ("RL: Training Inference Mismatch", logits-processor
+ *                       section).
+ *   or_rmsnorm          y = gamma x / sqrt(mean x^2 + eps) per row
+ *                       ("训推一致性与 determinism", section 6 kernel table).
  *   or_mismatch_stats   delta = train - rollout ("Diagnosing Training
  *                       Inference Mismatch ... (VeXact)", eq. (1)),
  *                       r = exp(delta) ("训推一致性与 determinism", section 2),
@@ -99,6 +104,47 @@ uint16_t or_bf16_round_rne(double x)
     return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFF));
 }
 
+void or_bf16_round_rne_n(const double* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = or_bf16_round_rne(x[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* RMSNorm                                                             */
+/* ------------------------------------------------------------------ */
+
+static double load_elem(const void* base, int dtype, int64_t idx);
+
+/*
+ * Root-mean-square normalisation of each row of x [n, ldx] with the gain
+ * gamma [d]: rstd_t = 1 / sqrt(mean_k x[t, k]^2 + eps) and
+ * y[t, k] = gamma[k] x[t, k] rstd_t, in fp64, the row sum in ascending k
+ * ("训推一致性与 determinism", section 6 kernel table, and "Diagnosing
+ * Training Inference Mismatch ... (VeXact)", its methodology: RMSNorm as
+ * one of the kernels made batch invariant by a fixed per-row reduction).
+ * x and gamma are both bf16 or both fp32 (dtype); y [n, d] and rstd [n]
+ * are fp64 (rstd nullable).  Returns 0, or -1 on bad arguments.
+ */
+int or_rmsnorm(const void* x, int64_t ldx, const void* gamma, int dtype, int64_t n,
+               int64_t d, double eps, double* y, double* rstd)
+{
+    if (n < 0 || d <= 0 || ldx < d || !(eps >= 0.0) || isinf(eps) ||
+        (n > 0 && (!x || !gamma || !y)))
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < d; ++k) {
+            const double xv = load_elem(x, dtype, t * ldx + k);
+            ss += xv * xv;
+        }
+        const double r = 1.0 / sqrt(ss / (double)d + eps);
+        if (rstd) rstd[t] = r;
+        for (int64_t k = 0; k < d; ++k)
+            y[t * d + k] = load_elem(gamma, dtype, k) * load_elem(x, dtype, t * ldx + k) * r;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* Selected-token log-probability                                      */
 /* ------------------------------------------------------------------ */
@@ -119,6 +165,8 @@ typedef struct {
     const int64_t* rows;   /* NULL: rows 0..nrows-1 */
     int64_t nrows;
     double* logp; double* lse; double* zsel;
+    double tau;            /* temperature: the softmax is taken of z / tau */
+    double* ent;           /* entropy of softmax(z / tau); nullable */
     int64_t begin, end;    /* slice of the row list owned by one thread */
 } lp_job;
 
@@ -156,10 +204,11 @@ static void* lp_worker(void* arg)
                 z[r * v + c] = acc;
             }
         }
-        /* log-softmax and gather */
+        /* log-softmax of z / tau and gather (tau = 1: z / 1 is z itself) */
         for (int64_t r = 0; r < nb; ++r) {
             int64_t t = j->rows ? j->rows[i0 + r] : i0 + r;
-            const double* zr = z + r * v;
+            double* zr = z + r * v;
+            for (int64_t c = 0; c < v; ++c) zr[c] = zr[c] / j->tau;
             double m = -INFINITY;
             for (int64_t c = 0; c < v; ++c)
                 if (zr[c] > m) m = zr[c];
@@ -171,6 +220,16 @@ static void* lp_worker(void* arg)
             if (j->lse) j->lse[i0 + r] = l;
             if (j->zsel) j->zsel[i0 + r] = ok ? zr[a] : NAN;
             j->logp[i0 + r] = ok ? zr[a] - l : NAN;
+            if (j->ent) {
+                /* H = -sum_v p_v log p_v = sum_v p_v (lse - z_v), p_v = exp(z_v - lse);
+                 * every term is >= 0 */
+                double hsum = 0.0;
+                for (int64_t c = 0; c < v; ++c) {
+                    const double lp = zr[c] - l;
+                    hsum += -exp(lp) * lp;
+                }
+                j->ent[i0 + r] = hsum;
+            }
         }
     }
     free(hd); free(wd); free(z);
@@ -197,13 +256,39 @@ int or_available_cpus(void)
  * nthreads <= 0: all available CPUs.  Returns the thread count used, or -1
  * on bad arguments.
  */
+int or_logprob_rows_ex(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                       const int32_t* ids, int dtype, int64_t d, int64_t v,
+                       const int64_t* rows, int64_t nrows, double tau,
+                       double* logp, double* lse, double* zsel, double* entropy,
+                       int nthreads);
+
 int or_logprob_rows(const void* h, int64_t ldh, const void* w, int64_t ldw,
                     const int32_t* ids, int dtype, int64_t d, int64_t v,
                     const int64_t* rows, int64_t nrows,
                     double* logp, double* lse, double* zsel, int nthreads)
 {
+    return or_logprob_rows_ex(h, ldh, w, ldw, ids, dtype, d, v, rows, nrows, 1.0,
+                              logp, lse, zsel, NULL, nthreads);
+}
+
+/*
+ * The same with a sampling temperature tau > 0: logp, lse and the entropy
+ * H = -sum_v p_v log p_v of p = softmax(z / tau) ("RL: Training Inference
+ * Mismatch", logits-processor section: at temperature tau the sampler draws
+ * from softmax(z / tau), so a trainer that scores the sampler's tokens must
+ * use the same tau; "训推一致性与 determinism", section 2, names entropy
+ * among the quantities a mismatch disturbs).  zsel is z_a / tau.  entropy
+ * nullable.
+ */
+int or_logprob_rows_ex(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                       const int32_t* ids, int dtype, int64_t d, int64_t v,
+                       const int64_t* rows, int64_t nrows, double tau,
+                       double* logp, double* lse, double* zsel, double* entropy,
+                       int nthreads)
+{
     if (!h || !w || !ids || !logp || d <= 0 || v <= 0 || nrows < 0 ||
-        ldh < d || ldw < d || (dtype != OR_BF16 && dtype != OR_F32))
+        ldh < d || ldw < d || (dtype != OR_BF16 && dtype != OR_F32) ||
+        !(tau > 0.0) || isinf(tau))
         return -1;
     if (nthreads <= 0) nthreads = or_available_cpus();
     if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
@@ -215,6 +300,7 @@ int or_logprob_rows(const void* h, int64_t ldh, const void* w, int64_t ldw,
         j->h = h; j->ldh = ldh; j->w = w; j->ldw = ldw; j->ids = ids;
         j->dtype = dtype; j->d = d; j->v = v; j->rows = rows;
         j->nrows = nrows; j->logp = logp; j->lse = lse; j->zsel = zsel;
+        j->tau = tau; j->ent = entropy;
         j->begin = nrows * i / nthreads;
         j->end = nrows * (i + 1) / nthreads;
     }

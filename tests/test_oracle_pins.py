@@ -629,6 +629,142 @@ def test_ppo_mask_and_nan_tokens():
 
 
 # ---------------------------------------------------------------------------
+# temperature and entropy
+# ---------------------------------------------------------------------------
+
+def _lpx(h, w, ids, tau, dtype=oracle.F32):
+    return oracle.logprob_ex(h, w, ids, dtype=dtype, temperature=tau, nthreads=2)
+
+
+def _bf16_exact(rng, shape, scale):
+    """float32 values that are exact bf16 numbers."""
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return oracle.bf16_decode(oracle.bf16_round_rne(x).ravel()).reshape(shape).astype(np.float32)
+
+
+def test_temperature_divides_the_logits():
+    # softmax(z / 2) from W is softmax(z') from W / 2: halving bf16 weights is
+    # exact, so logp, lse and entropy agree to the bit; likewise tau = 1/2 and 2 W
+    rng = np.random.default_rng(41)
+    h = _bf16_exact(rng, (6, 64), 1.0)
+    w = _bf16_exact(rng, (300, 64), 0.5)
+    ids = rng.integers(0, 300, 6).astype(np.int32)
+    for tau, wscaled in ((2.0, w / 2), (0.5, w * 2)):
+        a = _lpx(h, w, ids, tau)
+        b = _lpx(h, wscaled, ids, 1.0)
+        for k in ("logp", "lse", "entropy", "zsel"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg=f"tau={tau} {k}")
+    # tau = 1 is the plain forward
+    plain = _lp(h, w, ids)
+    one = _lpx(h, w, ids, 1.0)
+    np.testing.assert_array_equal(one["logp"], plain[0])
+    np.testing.assert_array_equal(one["lse"], plain[1])
+
+
+def test_entropy_closed_forms():
+    rng = np.random.default_rng(42)
+    # equal logits: uniform distribution, H = log V at any temperature
+    for tau in (0.3, 1.0, 7.0):
+        r = _lpx(rng.standard_normal((3, 32)).astype(np.float32), np.zeros((777, 32), np.float32),
+                 np.array([0, 5, 776], np.int32), tau)
+        np.testing.assert_allclose(r["entropy"], math.log(777), rtol=1e-12)   # 777 rounded terms
+        np.testing.assert_allclose(r["logp"], -math.log(777), rtol=1e-14)
+    # two entries: p = sigmoid(dz / tau), H = binary entropy
+    for hv in (0.25, -1.5, 6.0):
+        for tau in (0.5, 1.0, 3.0):
+            h = np.full((1, 64), hv, np.float32)
+            w = np.repeat(np.array([[3.0], [-2.0]], np.float32), 64, 1) / 64
+            r = _lpx(h, w, np.array([1], np.int32), tau)
+            x = 5.0 * hv / tau                      # (z0 - z1) / tau
+            p1 = 1.0 / (1.0 + math.exp(x))
+            hb = math.log1p(math.exp(-abs(x))) + abs(x) * (1.0 / (1.0 + math.exp(abs(x))))
+            # lp = z - lse cancels to an absolute error of ~ulp(|z| / tau)
+            np.testing.assert_allclose(r["entropy"][0], hb, rtol=1e-12, atol=1e-15 * (1 + abs(x)))
+            lp1 = -math.log1p(math.exp(x)) if x < 0 else -x - math.log1p(math.exp(-x))
+            np.testing.assert_allclose(r["logp"][0], lp1, rtol=1e-13, atol=1e-15 * (1 + abs(x)))
+            assert abs(math.exp(lp1) - p1) < 1e-15
+    # a dominant logit at a low temperature: H -> 0, logp of the winner -> 0
+    h = np.ones((1, 16), np.float32)
+    w = np.zeros((50, 16), np.float32)
+    w[7] = 1.0 / 16
+    r = _lpx(h, w, np.array([7], np.int32), 0.01)     # gap 1 / 0.01 = 100 nats
+    # 49 losers, each p = e^-100 and -log p = 100: H ~ 49 * 101 e^-100 ~ 1.8e-40
+    assert 0 <= r["entropy"][0] < 1e-39 and abs(r["logp"][0]) < 1e-40
+
+
+def test_entropy_matches_scipy_on_exact_logits():
+    import scipy.special
+    import scipy.stats
+    rng = np.random.default_rng(43)
+    # integer-valued inputs: every logit is an exact small integer in fp64
+    h = rng.integers(-3, 4, (5, 24)).astype(np.float32)
+    w = rng.integers(-2, 3, (200, 24)).astype(np.float32)
+    ids = rng.integers(0, 200, 5).astype(np.int32)
+    z = h.astype(np.float64) @ w.astype(np.float64).T
+    for tau in (0.7, 1.0, 2.5):
+        r = _lpx(h, w, ids, tau)
+        p = scipy.special.softmax(z / tau, axis=1)
+        np.testing.assert_allclose(r["entropy"], scipy.stats.entropy(p, axis=1), rtol=1e-12)
+        np.testing.assert_allclose(r["logp"], np.log(p[np.arange(5), ids]), rtol=1e-12)
+        np.testing.assert_allclose(r["lse"], scipy.special.logsumexp(z / tau, axis=1), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_constant_rows_give_the_gain():
+    rng = np.random.default_rng(44)
+    d = 96
+    gamma = _bf16_exact(rng, (d,), 1.0)
+    x = np.zeros((4, d), np.float32)
+    x[0] = 3.0
+    x[1] = -0.75
+    x[2, ::2], x[2, 1::2] = 2.0, -2.0          # |x| constant: rms = 2
+    y, rstd = oracle.rmsnorm(x, gamma, dtype=oracle.F32, eps=0.0)
+    g = gamma.astype(np.float64)
+    np.testing.assert_allclose(y[0], g, rtol=2e-16)
+    np.testing.assert_allclose(y[1], -g, rtol=2e-16)
+    np.testing.assert_allclose(y[2], np.where(np.arange(d) % 2 == 0, g, -g), rtol=2e-16)
+    np.testing.assert_allclose(rstd[:3], [1 / 3, 4 / 3, 0.5], rtol=1e-16)
+    # a zero row stays zero; its rstd is 1 / sqrt(eps)
+    y, rstd = oracle.rmsnorm(x, gamma, dtype=oracle.F32, eps=1e-6)
+    assert np.all(y[3] == 0) and rstd[3] == pytest.approx(1000.0, rel=1e-15)
+
+
+def test_rmsnorm_unit_mean_square_scale_invariance_and_torch():
+    rng = np.random.default_rng(45)
+    n, d = 7, 256
+    x = _bf16_exact(rng, (n, d), 3.0)
+    x[2] *= 128                 # a loud row (stays bf16-exact)
+    ones = np.ones(d, np.float32)
+    # eps = 0 and unit gain: every row has mean square 1; with eps the mean
+    # square is ms / (ms + eps) for the row's own mean square ms
+    y, _ = oracle.rmsnorm(x, ones, dtype=oracle.F32, eps=0.0)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, rtol=1e-14)
+    eps = 0.5
+    y, _ = oracle.rmsnorm(x, ones, dtype=oracle.F32, eps=eps)
+    ms = (x.astype(np.float64) ** 2).mean(axis=1)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), ms / (ms + eps), rtol=1e-13)
+    # scaling a row by a power of two changes nothing (eps = 0), to the bit
+    gamma = _bf16_exact(rng, (d,), 1.0)
+    y1, _ = oracle.rmsnorm(x, gamma, dtype=oracle.F32, eps=0.0)
+    y4, _ = oracle.rmsnorm(x * 4, gamma, dtype=oracle.F32, eps=0.0)
+    np.testing.assert_array_equal(y1, y4)
+    # the library routine in float64
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (d,),
+                                       weight=torch.from_numpy(gamma.astype(np.float64)),
+                                       eps=1e-6).numpy()
+    y, _ = oracle.rmsnorm(x, gamma, dtype=oracle.F32, eps=1e-6)
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-300)
+    # bf16 inputs decode exactly: the bf16 path equals the fp32 path on the same values
+    xb = oracle.bf16_round_rne(x)
+    gb = oracle.bf16_round_rne(gamma)
+    yb, _ = oracle.rmsnorm(xb, gb, dtype=oracle.BF16, eps=1e-6)
+    np.testing.assert_array_equal(yb, y)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ---------------------------------------------------------------------------
 
@@ -697,6 +833,20 @@ MUTATIONS = [
      "test_ppo_contribution_has_the_gradient_of_minus_r_a_and_tis_moves_the_ratio"),
     ("ppo gradient without weight", "g_t = active ? 0.0 : -w * r * a;", "g_t = active ? 0.0 : -r * a;",
      "test_ppo_gradient_matches_central_differences"),
+    ("temperature multiplies", "zr[c] = zr[c] / j->tau;", "zr[c] = zr[c] * j->tau;",
+     "test_temperature_divides_the_logits"),
+    ("entropy sign", "hsum += -exp(lp) * lp;", "hsum += exp(lp) * lp;",
+     "test_entropy_closed_forms"),
+    ("entropy unnormalised", "const double lp = zr[c] - l;", "const double lp = zr[c] - m;",
+     "test_entropy_matches_scipy_on_exact_logits"),
+    ("rms of the sum", "const double r = 1.0 / sqrt(ss / (double)d + eps);",
+     "const double r = 1.0 / sqrt(ss + eps);", "test_rmsnorm_constant_rows_give_the_gain"),
+    ("eps outside the root", "const double r = 1.0 / sqrt(ss / (double)d + eps);",
+     "const double r = 1.0 / (sqrt(ss / (double)d) + eps);",
+     "test_rmsnorm_unit_mean_square_scale_invariance_and_torch"),
+    ("gain not applied", "y[t * d + k] = load_elem(gamma, dtype, k) * load_elem(x, dtype, t * ldx + k) * r;",
+     "y[t * d + k] = load_elem(x, dtype, t * ldx + k) * r;",
+     "test_rmsnorm_constant_rows_give_the_gain"),
 ]
 
 
