@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define TIM_ABI_VERSION 2
+#define TIM_ABI_VERSION 3
 
 typedef enum {
     TIM_OK = 0,
@@ -148,6 +148,86 @@ int tim_logprob_forward(const void* h, int64_t ldh,
                         float* logp, float* lse, int32_t* n_bad_ids,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm in front of the head, and scoring at a sampling temperature.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * y[t, k] = gamma[k] * x[t, k] / sqrt(mean_k x[t, k]^2 + eps),  t in [0, n).
+ *
+ * The batch-invariant RMSNorm of "训推一致性与 determinism", section 6
+ * kernel table (a fixed per-row reduction), and of the VeXact methodology
+ * (its batch-invariant kernel list).  Each row is reduced on its own in a
+ * fixed order that depends only on d, in fp64; y is formed in fp64 and
+ * rounded once to dtype (bf16: nearest, ties to even).  A row's output bits
+ * depend only on that row, gamma, d, eps and dtype.
+ *
+ *  x       [n, d] row-major, ldx >= d elements, dtype (any alignment).
+ *  gamma   [d], dtype.
+ *  n       rows, >= 0 (0: TIM_OK, no launch).  d > 0.
+ *  dtype   TIM_BF16 (x, gamma, y bf16) or TIM_F32 (all fp32).
+ *  eps     >= 0, finite.
+ *  y       [n, d] out, ldy >= d; may not overlap x.
+ *  rstd    [n] fp32 out, nullable: 1 / sqrt(mean x^2 + eps).
+ */
+int tim_rmsnorm(const void* x, int64_t ldx, const void* gamma,
+                int64_t n, int64_t d, int dtype, double eps,
+                void* y, int64_t ldy, float* rstd, void* stream);
+
+/* (host) options of tim_logprob_forward_ex. */
+typedef struct {
+    double temperature;       /* tau > 0, finite.  The distribution scored is
+                                 softmax(z / tau): the rollout engine samples
+                                 from it at temperature tau, and its
+                                 log-probabilities must be compared with the
+                                 trainer's at the same tau ("RL: Training
+                                 Inference Mismatch", logits-processor
+                                 section).  1 = raw logits.                  */
+    const void* norm_gamma;   /* device [d] of dtype, or NULL.  Non-NULL: the
+                                 input rows are the pre-norm states x and the
+                                 call first applies tim_rmsnorm(x, gamma, eps)
+                                 into the workspace, then scores the
+                                 normalised rows.                            */
+    double norm_eps;          /* >= 0, finite; used with norm_gamma.         */
+} tim_forward_params;
+
+/* Workspace bytes for tim_logprob_forward_ex with these options;
+ * with_entropy != 0 when the entropy output will be requested.  0 for
+ * arguments the library rejects.  Pure host function. */
+size_t tim_logprob_ex_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype,
+                                      unsigned flags, const tim_forward_params* params,
+                                      int with_entropy);
+
+/*
+ * tim_logprob_forward with a temperature, an optional RMSNorm in front and
+ * an optional entropy output:
+ *   z       = W . norm(x_t)   (or W . h_t without norm_gamma)
+ *   logp[t] = log softmax(z / tau)[ids[t]]
+ *   lse[t]  = log sum_v exp(z_v / tau)
+ *   ent[t]  = - sum_v p_v log p_v,  p = softmax(z / tau)
+ * (entropy: one of the quantities a train-rollout mismatch disturbs,
+ * "训推一致性与 determinism", section 2).  Arguments as tim_logprob_forward;
+ * with norm_gamma the rows of h need no particular alignment (they are read
+ * by the norm, the head reads the normalised copy).  entropy [n] fp32 out,
+ * nullable.  params NULL: TIM_EINVAL.
+ *
+ * Arithmetic: as tim_logprob_forward, with the exponent scale log2(e) / tau
+ * and 1 / tau each rounded once to fp32 (both exact at tau = 1, where the
+ * results are bitwise those of tim_logprob_forward).  The entropy carries,
+ * next to the running maximum and sum, the running sum of p-weighted
+ * exponent arguments, merged in the same fixed order; it is batch
+ * invariant and deterministic like logp.
+ */
+int tim_logprob_forward_ex(const void* h, int64_t ldh,
+                           const void* w, int64_t ldw,
+                           const int32_t* ids,
+                           int64_t n, int64_t d, int64_t v,
+                           int dtype, unsigned flags,
+                           const tim_forward_params* params,
+                           float* logp, float* lse, float* entropy, int32_t* n_bad_ids,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* ------------------------------------------------------------------------
  * Mismatch statistics between trainer and rollout log-probabilities.

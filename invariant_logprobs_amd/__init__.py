@@ -12,6 +12,12 @@ Entry points (same names as the C ABI):
 
 * :func:`tim_logprob_forward` -- ``logp[t] = log softmax(h[t] W^T)[ids[t]]``
   ("RL: Training Inference Mismatch", section "log p").
+* :func:`tim_logprob_forward_ex` -- the same at a sampling temperature
+  (``softmax(z / tau)``: "RL: Training Inference Mismatch", logits-processor
+  section), with the entropy of that distribution and an optional RMSNorm
+  of the input rows in front of the head.
+* :func:`tim_rmsnorm` -- batch-invariant RMSNorm ("训推一致性与
+  determinism", section 6 kernel table; VeXact methodology).
 * :func:`tim_mismatch_stats` -- delta, ratio, k1/k2/k3, truncated IS weight,
   per-sequence means and geometric-mean-ratio rejection, batch aggregates
   ("Diagnosing Training Inference Mismatch ... (VeXact)", eq. (1) and its
@@ -62,7 +68,7 @@ EXTRAS_FIELDS = (
     "abs_q0", "abs_q1", "abs_q2", "abs_q3",
 )
 X_MAX_Q = 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 TIM_BWD_ACCUMULATE_DW = 1
 
 # Names of the tim_ppo_loss batch vector, in TIM_P_* index order.
@@ -74,7 +80,8 @@ EXPORTS = ("tim_abi_version", "tim_status_string", "tim_logprob_workspace_bytes"
            "tim_logprob_forward", "tim_stats_workspace_bytes", "tim_mismatch_stats",
            "tim_extras_workspace_bytes", "tim_mismatch_extras",
            "tim_logprob_backward_workspace_bytes", "tim_logprob_backward",
-           "tim_ppo_workspace_bytes", "tim_ppo_loss")
+           "tim_ppo_workspace_bytes", "tim_ppo_loss", "tim_rmsnorm",
+           "tim_logprob_ex_workspace_bytes", "tim_logprob_forward_ex")
 
 
 class TimError(RuntimeError):
@@ -92,6 +99,11 @@ class _ExtrasParams(ctypes.Structure):
     _fields_ = [("tok_tau", ctypes.c_double), ("n_ratio_q", ctypes.c_int32),
                 ("n_abs_q", ctypes.c_int32), ("ratio_q", ctypes.c_double * X_MAX_Q),
                 ("abs_q", ctypes.c_double * X_MAX_Q)]
+
+
+class _ForwardParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_double), ("norm_gamma", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_double)]
 
 
 class _PpoParams(ctypes.Structure):
@@ -142,6 +154,16 @@ def load_library():
         lib.tim_logprob_forward.restype = ctypes.c_int
         lib.tim_logprob_forward.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, ctypes.c_int,
                                             ctypes.c_uint, vp, vp, vp, vp, sz, vp]
+        lib.tim_rmsnorm.restype = ctypes.c_int
+        lib.tim_rmsnorm.argtypes = [vp, i64, vp, i64, i64, ctypes.c_int, ctypes.c_double, vp, i64,
+                                    vp, vp]
+        lib.tim_logprob_ex_workspace_bytes.restype = sz
+        lib.tim_logprob_ex_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_uint,
+                                                       ctypes.POINTER(_ForwardParams), ctypes.c_int]
+        lib.tim_logprob_forward_ex.restype = ctypes.c_int
+        lib.tim_logprob_forward_ex.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, ctypes.c_int,
+                                               ctypes.c_uint, ctypes.POINTER(_ForwardParams), vp,
+                                               vp, vp, vp, vp, sz, vp]
         lib.tim_stats_workspace_bytes.restype = sz
         lib.tim_stats_workspace_bytes.argtypes = [i64, i64]
         lib.tim_mismatch_stats.restype = ctypes.c_int
@@ -244,6 +266,91 @@ def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
     if return_lse:
         return logp, lse, nbad
     return logp
+
+
+def tim_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, *, eps: float = 1e-6,
+                out: Optional[torch.Tensor] = None, return_rstd: bool = False, stream=None):
+    """``y = gamma * x / sqrt(mean(x^2) + eps)`` per row of ``x`` [N, D]
+    (bf16 or fp32, unit stride along D; ``gamma`` [D] of the same dtype).
+    Returns ``y`` (same dtype, [N, D]) or ``(y, rstd)``."""
+    lib = load_library()
+    _require_gpu("x", x)
+    _require_gpu("gamma", gamma)
+    if x.dtype not in _DTYPES or gamma.dtype != x.dtype:
+        raise ValueError("x and gamma must share dtype bfloat16 or float32")
+    if x.dim() != 2 or x.stride(1) != 1 or gamma.dim() != 1 or not gamma.is_contiguous():
+        raise ValueError("x must be 2-D with unit stride along D, gamma 1-D contiguous")
+    n, d = x.shape
+    if gamma.shape[0] != d:
+        raise ValueError("gamma must have D entries")
+    y = out if out is not None else torch.empty(n, d, dtype=x.dtype, device=x.device)
+    if y.shape != (n, d) or y.dtype != x.dtype or y.stride(1) != 1:
+        raise ValueError("out must be [N, D] of x's dtype with unit stride along D")
+    rstd = torch.empty(n, dtype=torch.float32, device=x.device) if return_rstd else None
+    st = lib.tim_rmsnorm(_dptr(x), x.stride(0), _dptr(gamma), n, d, _DTYPES[x.dtype], float(eps),
+                         _dptr(y), y.stride(0), _dptr(rstd), _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_rmsnorm")
+    return (y, rstd) if return_rstd else y
+
+
+def logprob_ex_workspace_bytes(n: int, d: int, v: int, dtype: int, *, temperature: float = 1.0,
+                               norm: bool = False, entropy: bool = False,
+                               schedule: str = "invariant") -> int:
+    flags = TIM_SCHED_FREE if schedule == "free" else TIM_SCHED_INVARIANT
+    prm = _ForwardParams(float(temperature), 1 if norm else None, 1e-6)
+    return int(load_library().tim_logprob_ex_workspace_bytes(n, d, v, dtype, flags,
+                                                             ctypes.byref(prm), int(entropy)))
+
+
+def tim_logprob_forward_ex(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
+                           temperature: float = 1.0, norm_gamma: Optional[torch.Tensor] = None,
+                           norm_eps: float = 1e-6, entropy: bool = False,
+                           schedule: str = "invariant", workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> dict:
+    """Scores at temperature ``tau``: ``logp = log softmax(z / tau)[ids]``
+    with ``z = W norm(h)`` when ``norm_gamma`` is given (``h`` then holds the
+    pre-norm rows), else ``z = W h``.  Returns a dict of GPU tensors:
+    ``logp``, ``lse``, ``n_bad_ids`` and, with ``entropy``, ``entropy``."""
+    lib = load_library()
+    for name, t in (("h", h), ("w", w), ("ids", ids)):
+        _require_gpu(name, t)
+    if h.dtype not in _DTYPES or w.dtype != h.dtype:
+        raise ValueError("h and w must share dtype bfloat16 or float32")
+    if h.dim() != 2 or w.dim() != 2 or h.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("h and w must be 2-D with unit stride along D")
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous 1-D int32 tensor")
+    n, d = h.shape
+    v, d2 = w.shape
+    if d2 != d or ids.shape[0] != n:
+        raise ValueError(f"shape mismatch: h {tuple(h.shape)}, w {tuple(w.shape)}, ids {tuple(ids.shape)}")
+    if norm_gamma is not None:
+        _require_gpu("norm_gamma", norm_gamma)
+        if norm_gamma.dtype != h.dtype or norm_gamma.shape != (d,) or not norm_gamma.is_contiguous():
+            raise ValueError("norm_gamma must be a contiguous [D] tensor of h's dtype")
+    dtype = _DTYPES[h.dtype]
+    flags = {"invariant": TIM_SCHED_INVARIANT, "free": TIM_SCHED_FREE}[schedule]
+    dev = h.device
+    res = {"logp": torch.empty(n, dtype=torch.float32, device=dev),
+           "lse": torch.empty(n, dtype=torch.float32, device=dev),
+           "n_bad_ids": torch.zeros(1, dtype=torch.int32, device=dev)}
+    if entropy:
+        res["entropy"] = torch.empty(n, dtype=torch.float32, device=dev)
+    prm = _ForwardParams(float(temperature), _dptr(norm_gamma), float(norm_eps))
+    need = lib.tim_logprob_ex_workspace_bytes(n, d, v, dtype, flags, ctypes.byref(prm),
+                                              int(entropy))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    st = lib.tim_logprob_forward_ex(_dptr(h), h.stride(0), _dptr(w), w.stride(0), _dptr(ids),
+                                    n, d, v, dtype, flags, ctypes.byref(prm), _dptr(res["logp"]),
+                                    _dptr(res["lse"]), _dptr(res.get("entropy")),
+                                    _dptr(res["n_bad_ids"]), _dptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_logprob_forward_ex")
+    return res
 
 
 def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(OUT_DIR, "libtim.so")
-SOURCES = ("tim_api.hip", "lmhead.hip", "stats.hip", "extras.hip", "bwd.hip")
+SOURCES = ("tim_api.hip", "lmhead.hip", "stats.hip", "extras.hip", "bwd.hip", "norm.hip")
 ARCH = "gfx950"
 
 

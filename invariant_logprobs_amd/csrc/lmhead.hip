@@ -36,17 +36,48 @@ namespace {
 using namespace mfma;
 
 
-// (m, s) with s = sum exp(z - m): merge b into a.  Symmetric in its two
-// operands up to the commutativity of + and max, so two lanes that merge
-// each other's state obtain identical bits.
-__device__ __forceinline__ void lse_combine(float& m, float& s, float mb, float sb) {
+// Online softmax state of a set of logits at the scale c2 = log2(e) / tau
+// (tau the temperature): m = max z, s = sum 2^((z - m) c2), and, for the
+// entropy, u = sum 2^a a with a = (z - m) c2 (a <= 0, so u <= 0).  Then
+// ln sum exp(z / tau) = m / tau + ln s and the entropy of softmax(z / tau)
+// is ln 2 (log2 s - u / s).
+
+// (m, s): merge b into a.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float mb, float sb, float c2) {
     float mm = fmaxf(m, mb);
     if (mm == -INFINITY) { m = mm; s = 0.f; return; }
-    float fa = (m == mm) ? 1.f : fast_exp2((m - mm) * kLog2e);
-    float fb = (mb == mm) ? 1.f : fast_exp2((mb - mm) * kLog2e);
-    s = s * fa + sb * fb;
+    float fa = (m == mm) ? 1.f : fast_exp2((m - mm) * c2);
+    float fb = (mb == mm) ? 1.f : fast_exp2((mb - mm) * c2);
+    s = fmaf(s, fa, sb * fb);      // written out: both helpers round alike
     m = mm;
 }
+
+// (m, s, u): merge b into a.  A state's exponent arguments all shift by
+// d = (m_old - m_new) c2 when its reference moves up: s' = 2^d s and
+// u' = 2^d (u + d s).  An empty state (s = 0) stays (0, 0).
+__device__ __forceinline__ void lse_combine3(float& m, float& s, float& u, float mb, float sb,
+                                             float ub, float c2) {
+    const float mm = fmaxf(m, mb);
+    if (mm == -INFINITY) { m = mm; s = 0.f; u = 0.f; return; }
+    float fa = 1.f, fb = 1.f, ua = u, uo = ub;
+    if (m != mm) {
+        const float d = (m - mm) * c2;
+        fa = fast_exp2(d);
+        ua = s > 0.f ? fa * fmaf(d, s, u) : 0.f;
+    }
+    if (mb != mm) {
+        const float d = (mb - mm) * c2;
+        fb = fast_exp2(d);
+        uo = sb > 0.f ? fb * fmaf(d, sb, ub) : 0.f;
+    }
+    s = fmaf(s, fa, sb * fb);
+    u = ua + uo;
+    m = mm;
+}
+
+// Exponent arguments are clamped here before 2^a a is formed, so that a
+// masked logit (-inf) contributes 0 rather than 0 * inf.
+constexpr float kArgFloor = -3.0e38f;
 
 // XCD-aware order of workgroups.  The dispatcher hands workgroup b to XCD
 // b % 8; renumber so that each XCD receives one contiguous range of logical
@@ -69,15 +100,17 @@ __device__ __forceinline__ void tile_of_block(int64_t nchunks, int64_t nttiles,
     ttile = within / gm;
 }
 
-template <bool kBf16>
+// kEnt: also carry u (entropy).  c2 = log2(e) / tau.
+template <bool kBf16, bool kEnt>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                        const unsigned char* __restrict__ w, int64_t ldw_b,
                        const int32_t* __restrict__ ids, int64_t n, int64_t v,
                        int nk, int chunk_tiles, int64_t nvtiles, int64_t nchunks,
-                       int64_t nttiles, float2* __restrict__ part,
-                       float* __restrict__ zsel, int32_t* __restrict__ n_bad_ids) {
+                       int64_t nttiles, float c2, float2* __restrict__ part,
+                       float* __restrict__ upart, float* __restrict__ zsel,
+                       int32_t* __restrict__ n_bad_ids) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -106,11 +139,11 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     }
 
     f32x16 acc[4][4];
-    float m_run[4], s_run[4];
+    float m_run[4], s_run[4], u_run[4];
     float zsel_reg[4] = {0.f, 0.f, 0.f, 0.f};   // selected logit, if owned
     bool have_zsel = false;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) { m_run[bj] = -INFINITY; s_run[bj] = 0.f; }
+    for (int bj = 0; bj < 4; ++bj) { m_run[bj] = -INFINITY; s_run[bj] = 0.f; u_run[bj] = 0.f; }
 
     // Copy assignment: wave `wave` fills 8-row blocks 8 wave .. 8 wave + 7 of
     // both operands; lane i writes physical chunk i % 8 of row 8 blk + i / 8,
@@ -354,14 +387,33 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
                     for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, z[r]);
                     const float m_new = fmaxf(m_run[bj], bmax);
-                    // exponents as (z - m) log2 e: exactly 0 for the maximum, so
+                    // exponents as (z - m) c2: exactly 0 for the maximum, so
                     // its term is exactly 1 (a V = 1 row gets logp = 0 exactly)
                     const float mref = m_new == -INFINITY ? 0.f : m_new;
-                    const float scale = m_run[bj] == m_new
-                                            ? 1.f : fast_exp2((m_run[bj] - mref) * kLog2e);
+                    const float dsh = (m_run[bj] - mref) * c2;
+                    const float scale = m_run[bj] == m_new ? 1.f : fast_exp2(dsh);
                     float e[16];
+                    if constexpr (kEnt) {
+                        float ea[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) e[r] = fast_exp2((z[r] - mref) * kLog2e);
+                        for (int r = 0; r < 16; ++r) {
+                            const float a = fmaxf((z[r] - mref) * c2, kArgFloor);
+                            e[r] = fast_exp2(a);
+                            ea[r] = e[r] * a;
+                        }
+#pragma unroll
+                        for (int width = 8; width >= 1; width >>= 1)
+#pragma unroll
+                            for (int r = 0; r < width; ++r) ea[r] = ea[r] + ea[r + width];
+                        const float uo = m_run[bj] == m_new
+                                             ? u_run[bj]
+                                             : (s_run[bj] > 0.f ? scale * fmaf(dsh, s_run[bj], u_run[bj])
+                                                                : 0.f);
+                        u_run[bj] = uo + ea[0];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) e[r] = fast_exp2((z[r] - mref) * c2);
+                    }
 #pragma unroll
                     for (int width = 8; width >= 1; width >>= 1)
 #pragma unroll
@@ -423,22 +475,35 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     for (int bj = 0; bj < 4; ++bj) {
         const float mo = __shfl_xor(m_run[bj], 32);
         const float so = __shfl_xor(s_run[bj], 32);
-        lse_combine(m_run[bj], s_run[bj], mo, so);
+        if constexpr (kEnt) {
+            const float uo = __shfl_xor(u_run[bj], 32);
+            lse_combine3(m_run[bj], s_run[bj], u_run[bj], mo, so, uo, c2);
+        } else {
+            lse_combine(m_run[bj], s_run[bj], mo, so, c2);
+        }
     }
-    float2* xch = (float2*)lds;      // [token half][token]; the ring is drained
+    float2* xch = (float2*)lds;          // [token half][token]; the ring is drained
+    float* xu = (float*)(lds + 2048);    // u, same index
     if (wv == 1 && lhalf == 0) {
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
+        for (int bj = 0; bj < 4; ++bj) {
             xch[wt * 128 + bj * 32 + lrow] = make_float2(m_run[bj], s_run[bj]);
+            if constexpr (kEnt) xu[wt * 128 + bj * 32 + lrow] = u_run[bj];
+        }
     }
     __syncthreads();
     if (wv == 0 && lhalf == 0) {
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
             const float2 o = xch[wt * 128 + bj * 32 + lrow];
-            float m = m_run[bj], s = s_run[bj];
-            lse_combine(m, s, o.x, o.y);
+            float m = m_run[bj], s = s_run[bj], u = u_run[bj];
             const int64_t t = t0 + wt * 128 + bj * 32 + lrow;
+            if constexpr (kEnt) {
+                lse_combine3(m, s, u, o.x, o.y, xu[wt * 128 + bj * 32 + lrow], c2);
+                if (t < n) upart[chunk * n + t] = u;
+            } else {
+                lse_combine(m, s, o.x, o.y, c2);
+            }
             if (t < n) part[chunk * n + t] = make_float2(m, s);
         }
     }
@@ -452,42 +517,65 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 constexpr int kMergeWaves = 8;
 constexpr int kMergeUnroll = 4;
 
+// With it = 1 / tau: lse = m it + ln s and logp = (z_a - m) it - ln s (the
+// difference z_a - m is formed before the scale, so no two large terms
+// cancel); entropy = ln 2 (log2 s - u / s) when kEnt.
+template <bool kEnt>
 __global__ void __launch_bounds__(64 * kMergeWaves)
-lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ zsel,
-                 const int32_t* __restrict__ ids, int64_t n, int64_t nchunks, int64_t v,
-                 float* __restrict__ logp, float* __restrict__ lse,
+lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ upart,
+                 const float* __restrict__ zsel, const int32_t* __restrict__ ids, int64_t n,
+                 int64_t nchunks, int64_t v, float c2, float it, float* __restrict__ logp,
+                 float* __restrict__ lse, float* __restrict__ ent,
                  int32_t* __restrict__ n_bad_ids) {
     __shared__ float2 strand[kMergeWaves][64];
+    __shared__ float ustrand[kEnt ? kMergeWaves : 1][64];
     __shared__ int bad_count;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) bad_count = 0;
     const int64_t t = (int64_t)blockIdx.x * 64 + lane;
     const int64_t tc = t < n ? t : n - 1;
-    float m = -INFINITY, s = 0.f;
+    float m = -INFINITY, s = 0.f, uu = 0.f;
     int64_t c = wave;
     for (; c + (kMergeUnroll - 1) * kMergeWaves < nchunks; c += kMergeUnroll * kMergeWaves) {
         float2 p[kMergeUnroll];
+        float q[kMergeUnroll];
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) p[u] = part[(c + u * kMergeWaves) * n + tc];
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            p[u] = part[(c + u * kMergeWaves) * n + tc];
+            if constexpr (kEnt) q[u] = upart[(c + u * kMergeWaves) * n + tc];
+        }
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) lse_combine(m, s, p[u].x, p[u].y);
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            if constexpr (kEnt) lse_combine3(m, s, uu, p[u].x, p[u].y, q[u], c2);
+            else lse_combine(m, s, p[u].x, p[u].y, c2);
+        }
     }
     for (; c < nchunks; c += kMergeWaves) {
         const float2 p = part[c * n + tc];
-        lse_combine(m, s, p.x, p.y);
+        if constexpr (kEnt) lse_combine3(m, s, uu, p.x, p.y, upart[c * n + tc], c2);
+        else lse_combine(m, s, p.x, p.y, c2);
     }
     strand[wave][lane] = make_float2(m, s);
+    if constexpr (kEnt) ustrand[wave][lane] = uu;
     __syncthreads();
     if (wave == 0 && t < n) {
-        float mm = strand[0][lane].x, ss = strand[0][lane].y;
+        float mm = strand[0][lane].x, ss = strand[0][lane].y, us = 0.f;
+        if constexpr (kEnt) us = ustrand[0][lane];
 #pragma unroll
-        for (int w = 1; w < kMergeWaves; ++w) lse_combine(mm, ss, strand[w][lane].x, strand[w][lane].y);
-        const float l = mm + fast_log2(ss) * kLn2;
+        for (int w = 1; w < kMergeWaves; ++w) {
+            if constexpr (kEnt)
+                lse_combine3(mm, ss, us, strand[w][lane].x, strand[w][lane].y, ustrand[w][lane], c2);
+            else
+                lse_combine(mm, ss, strand[w][lane].x, strand[w][lane].y, c2);
+        }
+        const float l2s = fast_log2(ss);
+        const float lns = l2s * kLn2;
         const int32_t a = ids[t];
         const bool bad = a < 0 || (int64_t)a >= v;
-        logp[t] = bad ? __builtin_nanf("") : zsel[t] - l;
-        if (lse) lse[t] = l;
+        logp[t] = bad ? __builtin_nanf("") : fmaf(zsel[t] - mm, it, -lns);
+        if (lse) lse[t] = fmaf(mm, it, lns);
+        if constexpr (kEnt) ent[t] = (l2s - us / ss) * kLn2;
         if (bad) atomicAdd(&bad_count, 1);
     }
     __syncthreads();
@@ -497,7 +585,7 @@ lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ zsel
 }  // namespace
 
 bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
-                       LogprobPlan* p) {
+                       bool entropy, LogprobPlan* p) {
     if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != 0 && dtype != 1) || flags > 1u)
         return false;
     p->n = n; p->d = d; p->v = v; p->dtype = dtype;
@@ -514,43 +602,66 @@ bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flag
         p->chunk_tiles = (int)ct;
     }
     p->nchunks = (p->nvtiles + p->chunk_tiles - 1) / p->chunk_tiles;
+    p->entropy = entropy;
     p->part_bytes = align_up((size_t)p->nchunks * (size_t)n * sizeof(float2), 256);
     p->zsel_off = p->part_bytes;
-    p->total_bytes = p->zsel_off + align_up((size_t)n * sizeof(float), 256);
+    p->upart_off = p->zsel_off + align_up((size_t)n * sizeof(float), 256);
+    p->total_bytes = p->upart_off +
+                     (entropy ? align_up((size_t)p->nchunks * (size_t)n * sizeof(float), 256) : 0);
     if (p->total_bytes == 0) p->total_bytes = 256;
     return true;
 }
 
+ScoreScale make_score_scale(double temperature) {
+    ScoreScale sc;
+    sc.c2 = temperature == 1.0 ? kLog2e : (float)(1.4426950408889634 / temperature);
+    sc.it = temperature == 1.0 ? 1.f : (float)(1.0 / temperature);
+    return sc;
+}
+
 hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t ldh,
                                   const void* w, int64_t ldw, const int32_t* ids,
-                                  void* workspace, int32_t* n_bad_ids, hipStream_t st) {
+                                  const ScoreScale& sc, void* workspace, int32_t* n_bad_ids,
+                                  hipStream_t st) {
     const int64_t esz = p.dtype == 0 ? 2 : 4;
     const int nk = (int)(p.d * esz / kStageBytes);
     const int64_t grid = p.nchunks * p.nttiles;
     if (grid <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;
     float2* part = (float2*)workspace;
     float* zsel = (float*)((unsigned char*)workspace + p.zsel_off);
+    float* upart = p.entropy ? (float*)((unsigned char*)workspace + p.upart_off) : nullptr;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
+                           ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
+                           sc.c2, part, upart, zsel, n_bad_ids);
+    };
     if (p.dtype == 0) {
-        hipLaunchKernelGGL(lmhead_partials_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st,
-                           (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
-                           ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
-                           part, zsel, n_bad_ids);
+        if (p.entropy) go(lmhead_partials_kernel<true, true>);
+        else go(lmhead_partials_kernel<true, false>);
     } else {
-        hipLaunchKernelGGL(lmhead_partials_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st,
-                           (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
-                           ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
-                           part, zsel, n_bad_ids);
+        if (p.entropy) go(lmhead_partials_kernel<false, true>);
+        else go(lmhead_partials_kernel<false, false>);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const void* workspace,
-                            float* logp, float* lse, int32_t* n_bad_ids, hipStream_t st) {
+hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const ScoreScale& sc,
+                            const void* workspace, float* logp, float* lse, float* entropy,
+                            int32_t* n_bad_ids, hipStream_t st) {
     const float2* part = (const float2*)workspace;
     const float* zsel = (const float*)((const unsigned char*)workspace + p.zsel_off);
+    const float* upart = p.entropy ? (const float*)((const unsigned char*)workspace + p.upart_off)
+                                   : nullptr;
     const int64_t blocks = (p.n + 63) / 64;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0, st, part, zsel,
-                       ids, p.n, p.nchunks, p.v, logp, lse, n_bad_ids);
+    if (p.entropy)
+        hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0,
+                           st, part, upart, zsel, ids, p.n, p.nchunks, p.v, sc.c2, sc.it, logp, lse,
+                           entropy, n_bad_ids);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0,
+                           st, part, upart, zsel, ids, p.n, p.nchunks, p.v, sc.c2, sc.it, logp, lse,
+                           entropy, n_bad_ids);
     return hipGetLastError();
 }
 

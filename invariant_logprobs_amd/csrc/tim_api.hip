@@ -31,7 +31,7 @@ const char* tim_status_string(int status) {
 
 size_t tim_logprob_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags) {
     tim::LogprobPlan p;
-    if (!tim::make_logprob_plan(n, d, v, dtype, flags, &p)) return 0;
+    if (!tim::make_logprob_plan(n, d, v, dtype, flags, false, &p)) return 0;
     return p.total_bytes;
 }
 
@@ -50,14 +50,99 @@ int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
     if ((ldh * esz) % 16 != 0 || (ldw * esz) % 16 != 0) return TIM_EUNSUPPORTED;
     if (!aligned(h, 16) || !aligned(w, 16)) return TIM_EUNSUPPORTED;
     tim::LogprobPlan p;
-    if (!tim::make_logprob_plan(n, d, v, dtype, flags, &p)) return TIM_EINVAL;
+    if (!tim::make_logprob_plan(n, d, v, dtype, flags, false, &p)) return TIM_EINVAL;
     if (p.nchunks * p.nttiles > INT32_MAX) return TIM_EUNSUPPORTED;
     if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
     if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
-    if (tim::launch_lmhead_partials(p, h, ldh, w, ldw, ids, workspace, n_bad_ids, st) != hipSuccess)
+    const tim::ScoreScale sc = tim::make_score_scale(1.0);
+    if (tim::launch_lmhead_partials(p, h, ldh, w, ldw, ids, sc, workspace, n_bad_ids, st) != hipSuccess)
         return TIM_EHIP;
-    if (tim::launch_lse_merge(p, ids, workspace, logp, lse, n_bad_ids, st) != hipSuccess)
+    if (tim::launch_lse_merge(p, ids, sc, workspace, logp, lse, nullptr, n_bad_ids, st) != hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
+int tim_rmsnorm(const void* x, int64_t ldx, const void* gamma, int64_t n, int64_t d, int dtype,
+                double eps, void* y, int64_t ldy, float* rstd, void* stream) {
+    if (n < 0 || d <= 0 || (dtype != TIM_BF16 && dtype != TIM_F32) || !(eps >= 0.0) ||
+        !isfinite(eps) || ldx < d || ldy < d)
+        return TIM_EINVAL;
+    if (n == 0) return TIM_OK;
+    if (!x || !gamma || !y) return TIM_EINVAL;
+    if (tim::launch_rmsnorm(x, ldx, gamma, n, d, dtype, eps, y, ldy, rstd, (hipStream_t)stream) !=
+        hipSuccess)
+        return TIM_EHIP;
+    return TIM_OK;
+}
+
+namespace {
+
+// Workspace of tim_logprob_forward_ex: the head's plan, then (with a norm)
+// the normalised rows [n][d] of dtype.
+bool ex_layout(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
+               const tim_forward_params* prm, bool with_entropy, tim::LogprobPlan* p,
+               size_t* norm_off, size_t* total) {
+    if (!prm || !(prm->temperature > 0.0) || !isfinite(prm->temperature)) return false;
+    if (prm->norm_gamma && (!(prm->norm_eps >= 0.0) || !isfinite(prm->norm_eps))) return false;
+    if (!tim::make_logprob_plan(n, d, v, dtype, flags, with_entropy, p)) return false;
+    *norm_off = (p->total_bytes + 255) / 256 * 256;
+    const size_t esz = dtype == TIM_BF16 ? 2 : 4;
+    *total = *norm_off + (prm->norm_gamma ? ((size_t)n * (size_t)d * esz + 255) / 256 * 256 : 0);
+    return true;
+}
+
+}  // namespace
+
+size_t tim_logprob_ex_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
+                                      const tim_forward_params* params, int with_entropy) {
+    tim::LogprobPlan p;
+    size_t norm_off = 0, total = 0;
+    if (!ex_layout(n, d, v, dtype, flags, params, with_entropy != 0, &p, &norm_off, &total))
+        return 0;
+    return total;
+}
+
+int tim_logprob_forward_ex(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                           const int32_t* ids, int64_t n, int64_t d, int64_t v, int dtype,
+                           unsigned flags, const tim_forward_params* prm, float* logp, float* lse,
+                           float* entropy, int32_t* n_bad_ids, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != TIM_BF16 && dtype != TIM_F32) ||
+        flags > TIM_SCHED_FREE || !prm)
+        return TIM_EINVAL;
+    if (!(prm->temperature > 0.0) || !isfinite(prm->temperature)) return TIM_EINVAL;
+    if (prm->norm_gamma && (!(prm->norm_eps >= 0.0) || !isfinite(prm->norm_eps))) return TIM_EINVAL;
+    if (ldh < d || ldw < d) return TIM_EINVAL;
+    if (n == 0) return TIM_OK;
+    if (!h || !w || !ids || !logp) return TIM_EINVAL;
+    const int64_t esz = dtype == TIM_BF16 ? 2 : 4;
+    if (d % 64 != 0) return TIM_EUNSUPPORTED;
+    if ((ldw * esz) % 16 != 0 || !aligned(w, 16)) return TIM_EUNSUPPORTED;
+    if (!prm->norm_gamma && ((ldh * esz) % 16 != 0 || !aligned(h, 16))) return TIM_EUNSUPPORTED;
+    tim::LogprobPlan p;
+    size_t norm_off = 0, total = 0;
+    if (!ex_layout(n, d, v, dtype, flags, prm, entropy != nullptr, &p, &norm_off, &total))
+        return TIM_EINVAL;
+    if (p.nchunks * p.nttiles > INT32_MAX) return TIM_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < total) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    const void* rows = h;
+    int64_t ldr = ldh;
+    if (prm->norm_gamma) {
+        void* hn = (unsigned char*)workspace + norm_off;
+        if (tim::launch_rmsnorm(h, ldh, prm->norm_gamma, n, d, dtype, prm->norm_eps, hn, d,
+                                nullptr, st) != hipSuccess)
+            return TIM_EHIP;
+        rows = hn;
+        ldr = d;
+    }
+    const tim::ScoreScale sc = tim::make_score_scale(prm->temperature);
+    if (tim::launch_lmhead_partials(p, rows, ldr, w, ldw, ids, sc, workspace, n_bad_ids, st) !=
+        hipSuccess)
+        return TIM_EHIP;
+    if (tim::launch_lse_merge(p, ids, sc, workspace, logp, lse, entropy, n_bad_ids, st) != hipSuccess)
         return TIM_EHIP;
     return TIM_OK;
 }

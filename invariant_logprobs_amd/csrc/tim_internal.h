@@ -34,18 +34,34 @@ struct LogprobPlan {
     int64_t nvtiles;      // ceil(v / kTileV)
     int64_t nchunks;      // ceil(nvtiles / chunk_tiles)
     int64_t nttiles;      // ceil(n / kTileT)
-    size_t part_bytes, zsel_off, total_bytes;
+    bool entropy;         // carry the entropy state u as well
+    // workspace: float2 part[nchunks][n] | float zsel[n] | float upart[nchunks][n]
+    size_t part_bytes, zsel_off, upart_off, total_bytes;
 };
 
 // Fills `p`; returns false for sizes the library does not accept.
 bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
-                       LogprobPlan* p);
+                       bool entropy, LogprobPlan* p);
+
+// Temperature tau as the kernels use it: c2 = log2(e) / tau, it = 1 / tau
+// (fp32, rounded once on the host; tau = 1 gives exactly log2(e) and 1).
+struct ScoreScale {
+    float c2, it;
+};
+ScoreScale make_score_scale(double temperature);
 
 hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t ldh,
                                   const void* w, int64_t ldw, const int32_t* ids,
-                                  void* workspace, int32_t* n_bad_ids, hipStream_t st);
-hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const void* workspace,
-                            float* logp, float* lse, int32_t* n_bad_ids, hipStream_t st);
+                                  const ScoreScale& sc, void* workspace, int32_t* n_bad_ids,
+                                  hipStream_t st);
+hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const ScoreScale& sc,
+                            const void* workspace, float* logp, float* lse, float* entropy,
+                            int32_t* n_bad_ids, hipStream_t st);
+
+// RMSNorm (norm.hip): one wave per row, fp64 row sums, one rounding.
+hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, int64_t n, int64_t d,
+                          int dtype, double eps, void* y, int64_t ldy, float* rstd,
+                          hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Mismatch statistics kernels (stats.hip)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == sorted(tim.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.tim_abi_version() == tim.ABI_VERSION == 2
+    assert lib.tim_abi_version() == tim.ABI_VERSION == 3
 
 
 def test_status_strings(lib):
@@ -200,3 +200,78 @@ def test_backward_and_ppo_argument_errors(lib):
     assert ppo(ws=None) == tim.TIM_EWORKSPACE
     assert ppo(wsb=8) == tim.TIM_EWORKSPACE
     assert ppo(ws=FAKE + 8) == tim.TIM_EUNSUPPORTED
+
+
+def _fp(temperature=1.0, gamma=None, eps=1e-6):
+    return ctypes.byref(tim._ForwardParams(temperature, gamma, eps))
+
+
+def test_forward_ex_workspace_layout(lib):
+    n, d, v = 8192, 4096, 151936
+    chunks = -(-v // 512)
+    up = lambda x: -(-x // 256) * 256
+    plain = up(chunks * n * 8) + up(n * 4)
+    ws = lambda **kw: lib.tim_logprob_ex_workspace_bytes(
+        n, d, v, kw.get("dtype", 0), 0, _fp(kw.get("tau", 1.0), kw.get("g"), kw.get("eps", 1e-6)),
+        kw.get("ent", 0))
+    assert ws() == plain == lib.tim_logprob_workspace_bytes(n, d, v, 0, 0)
+    assert ws(tau=0.7) == plain
+    assert ws(ent=1) == plain + up(chunks * n * 4)                  # the entropy partials
+    assert ws(g=FAKE) == plain + up(n * d * 2)                      # normalised bf16 rows
+    assert ws(g=FAKE, dtype=1, ent=1) == plain + up(chunks * n * 4) + up(n * d * 4)
+    assert ws(tau=0.0) == 0 and ws(tau=-1.0) == 0 and ws(tau=float("inf")) == 0
+    assert ws(tau=float("nan")) == 0
+    assert ws(g=FAKE, eps=-1.0) == 0 and ws(g=FAKE, eps=float("nan")) == 0
+    assert lib.tim_logprob_ex_workspace_bytes(n, d, v, 0, 0, None, 0) == 0
+
+
+def _fwdx(lib, **kw):
+    a = dict(h=FAKE, ldh=64, w=FAKE, ldw=64, ids=FAKE, n=4, d=64, v=100, dtype=0, flags=0,
+             prm=_fp(), logp=FAKE, lse=None, ent=None, nbad=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.tim_logprob_forward_ex(a["h"], a["ldh"], a["w"], a["ldw"], a["ids"], a["n"], a["d"],
+                                      a["v"], a["dtype"], a["flags"], a["prm"], a["logp"],
+                                      a["lse"], a["ent"], a["nbad"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_forward_ex_and_rmsnorm_argument_errors(lib):
+    assert _fwdx(lib, prm=None) == tim.TIM_EINVAL
+    assert _fwdx(lib, prm=_fp(0.0)) == tim.TIM_EINVAL
+    assert _fwdx(lib, prm=_fp(float("nan"))) == tim.TIM_EINVAL
+    assert _fwdx(lib, prm=_fp(1.0, FAKE, -1.0)) == tim.TIM_EINVAL
+    assert _fwdx(lib, n=-1) == tim.TIM_EINVAL
+    assert _fwdx(lib, ldh=32) == tim.TIM_EINVAL
+    assert _fwdx(lib, logp=None) == tim.TIM_EINVAL
+    assert _fwdx(lib, d=96, ldh=96, ldw=96) == tim.TIM_EUNSUPPORTED
+    assert _fwdx(lib, h=FAKE + 2) == tim.TIM_EUNSUPPORTED            # unaligned rows ...
+    assert _fwdx(lib, h=FAKE + 2, prm=_fp(1.0, FAKE), ws=None) == tim.TIM_EWORKSPACE  # ... fine with a norm
+    assert _fwdx(lib, ws=None) == tim.TIM_EWORKSPACE
+    assert _fwdx(lib, ent=FAKE, wsb=lib.tim_logprob_workspace_bytes(4, 64, 100, 0, 0)) == \
+        tim.TIM_EWORKSPACE                                             # entropy needs more
+    assert _fwdx(lib, ws=FAKE + 8) == tim.TIM_EUNSUPPORTED
+    assert _fwdx(lib, n=0, logp=None) == tim.TIM_OK                  # nothing to do
+    norm = lambda **kw: lib.tim_rmsnorm(kw.get("x", FAKE), kw.get("ldx", 64), kw.get("g", FAKE),
+                                        kw.get("n", 4), kw.get("d", 64), kw.get("dtype", 0),
+                                        kw.get("eps", 1e-6), kw.get("y", FAKE), kw.get("ldy", 64),
+                                        None, None)
+    assert norm(n=-1) == tim.TIM_EINVAL
+    assert norm(d=0) == tim.TIM_EINVAL
+    assert norm(dtype=5) == tim.TIM_EINVAL
+    assert norm(eps=-1e-6) == tim.TIM_EINVAL
+    assert norm(eps=float("inf")) == tim.TIM_EINVAL
+    assert norm(ldx=63) == tim.TIM_EINVAL
+    assert norm(ldy=10) == tim.TIM_EINVAL
+    assert norm(x=None) == tim.TIM_EINVAL
+    assert norm(g=None) == tim.TIM_EINVAL
+    assert norm(y=None) == tim.TIM_EINVAL
+    assert norm(n=0, x=None, g=None, y=None) == tim.TIM_OK
+
+
+def test_binding_norm_and_ex_refuse_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tim.tim_rmsnorm(x, torch.ones(64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        tim.tim_logprob_forward_ex(x, torch.zeros(10, 64, dtype=torch.bfloat16),
+                                   torch.zeros(4, dtype=torch.int32), temperature=0.7)

@@ -40,7 +40,7 @@ import numpy as np
 import torch
 
 STREAMS = ("h", "w", "ids", "noise", "spike_pos", "spike_sign", "drift", "lengths",
-           "lt", "nan_pos")
+           "lt", "nan_pos", "x_pre", "row_scale", "gamma")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -276,6 +276,25 @@ def stats_scale(n: int, seed: int = 7, device: Optional[str] = None,
     prompt = torch.round(lens_t.double() * prompt_frac).long()[seq_of]
     mask = (pos_in_seq >= prompt).to(torch.uint8)
     return lt.float(), lr.float(), mask, torch.from_numpy(cu).to(device)
+
+
+def pre_norm(n: int, d: int, seed: int, dtype=torch.bfloat16, device: Optional[str] = None):
+    """Pre-norm final hidden states ``x`` [n, d] and an RMSNorm gain ``gamma``
+    [d] for the norm in front of the head.  ``x = s_t * N(0, 1)`` with a
+    per-row scale ``s_t = 8 exp(0.5 z_t)`` (rows of different loudness, as
+    residual streams are) and four fixed channels (0, 1, d/2, d - 1) ten
+    times louder (a few outlier channels); ``gamma = 1 + N(0, 0.2^2)``.  Both
+    rounded to ``dtype`` (torch's conversion: nearest, ties to even).
+    Returns ``(x, gamma)``."""
+    if device is None:
+        device = "cuda" if torch.cuda.is_available() else "cpu"
+    seeds = stream_seeds(seed)
+    x = torch.randn(n, d, generator=_gen(seeds["x_pre"], device), device=device)
+    rs = torch.randn(n, generator=_gen(seeds["row_scale"], device), device=device)
+    x.mul_((8.0 * torch.exp(0.5 * rs))[:, None])
+    x[:, [0, 1, d // 2, d - 1]] *= 10.0
+    gamma = 1.0 + 0.2 * torch.randn(d, generator=_gen(seeds["gamma"], device), device=device)
+    return x.to(dtype), gamma.to(dtype)
 
 
 def sweep_slices(n: int, batch: int):
