@@ -81,6 +81,8 @@ def main():
                     help="run only the extra metrics at 2^stats-log2 tokens (for a kernel trace)")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only the backward on the workload (for a kernel trace)")
+    ap.add_argument("--ex-only", action="store_true",
+                    help="only the tempered / entropy / RMSNorm scoring measurements")
     ap.add_argument("--ppo-scale-only", action="store_true",
                     help="run only the surrogate at 2^stats-log2 tokens (for a kernel trace)")
     ap.add_argument("--traffic-out", default=PMC_SUMMARY)
@@ -127,6 +129,9 @@ def main():
     wl = workloads.make(name, device=dev)
     if args.backward_only:
         print(json.dumps(backward_measure(tim, wl, torch, np)), flush=True)
+        return
+    if args.ex_only:
+        print(json.dumps(scoring_ex_measure(tim, workloads, wl, torch, np)), flush=True)
         return
     sp = wl.spec
     n, d, v = sp.n, sp.d, sp.v
@@ -194,6 +199,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["scoring_ex"] = scoring_ex_measure(tim, workloads, wl, torch, np)
         out["backward"] = backward_measure(tim, wl, torch, np)
         out["ppo"] = ppo_scale(tim, torch, np, args.stats_log2)
         out["extras"] = extras_measure(tim, workloads, wl, torch, np, args.stats_log2)
@@ -393,6 +399,60 @@ def backward_measure(tim, wl, torch, np, reps=5):
     torch.cuda.empty_cache()
     return {"ms": ms, "flops": flops, "achieved_TFLOPs": tf, "peak_TFLOPs": PEAK_BF16_TFLOPS,
             "frac": tf / PEAK_BF16_TFLOPS, "tokens": n, "hidden": d, "vocab": v}
+
+
+EX_TAU = 0.7
+NORM_EPS = 1e-6
+
+
+def scoring_ex_measure(tim, workloads, wl, torch, np, norm_log2_rows=18):
+    """tim_logprob_forward_ex on the workload at temperature 0.7 with the
+    entropy, without and with the RMSNorm in front (2 N D V FLOP each, like
+    the plain forward), and tim_rmsnorm alone on the workload's rows and on
+    2^norm_log2_rows rows of the same width (HBM-bound: x read and y written
+    once, 4 B per element in bf16)."""
+    sp = wl.spec
+    n, d, v = sp.n, sp.d, sp.v
+    x, gamma = workloads.pre_norm(n, d, seed=2, device="cuda")
+    flops = 2.0 * n * d * v
+    out = {"temperature": EX_TAU, "tokens": n, "hidden": d, "vocab": v}
+    for key, kw in (("plain", {}),
+                    ("tau_entropy", dict(temperature=EX_TAU, entropy=True)),
+                    ("tau_entropy_norm", dict(temperature=EX_TAU, entropy=True, norm_gamma=gamma,
+                                              norm_eps=NORM_EPS))):
+        rows = x if "norm_gamma" in kw else wl.h
+        ws = torch.empty(tim.logprob_ex_workspace_bytes(
+            n, d, v, tim.TIM_BF16, temperature=kw.get("temperature", 1.0),
+            norm="norm_gamma" in kw, entropy=kw.get("entropy", False)),
+            dtype=torch.uint8, device="cuda")
+        fn = lambda: tim.tim_logprob_forward_ex(rows, wl.w, wl.ids, workspace=ws, **kw)
+        ms = time_calls(fn, torch, np, reps=5, warm=1)
+        tf = flops / (ms / 1e3) / 1e12
+        out[key] = {"ms": ms, "achieved_TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS}
+        log(f"scoring {key}: {ms:.3f} ms, {tf:.0f} TFLOP/s ({tf / PEAK_BF16_TFLOPS:.1%})")
+        del ws
+    y = torch.empty_like(x)
+    us = time_calls(lambda: tim.tim_rmsnorm(x, gamma, eps=NORM_EPS, out=y), torch, np,
+                    reps=20) * 1e3
+    algo = 4 * n * d + 2 * d
+    out["rmsnorm_workload"] = {"rows": n, "us": us, "algorithmic_bytes": algo,
+                               "achieved_GBs": algo / (us / 1e6) / 1e9}
+    del x, y
+    torch.cuda.empty_cache()
+    nb = 1 << norm_log2_rows
+    xb, gb = workloads.pre_norm(nb, d, seed=3, device="cuda")
+    yb = torch.empty_like(xb)
+    ms = time_calls(lambda: tim.tim_rmsnorm(xb, gb, eps=NORM_EPS, out=yb), torch, np, reps=10)
+    algo = 4 * nb * d + 2 * d
+    gbs = algo / (ms / 1e3) / 1e9
+    out["rmsnorm_scale"] = {"rows": nb, "hidden": d, "ms": ms, "algorithmic_bytes": algo,
+                            "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS,
+                            "frac": gbs / PEAK_HBM_GBS}
+    log(f"rmsnorm: {us:.1f} us at {n} rows; {ms:.3f} ms at 2^{norm_log2_rows} rows = "
+        f"{gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    del xb, yb, gb
+    torch.cuda.empty_cache()
+    return out
 
 
 def ppo_scale(tim, torch, np, log2n):
