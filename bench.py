@@ -214,7 +214,7 @@ def main():
 
 COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration kernel
 COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
-LMHEAD_KERNEL = "lmhead_partials_kernel<true>"
+LMHEAD_KERNEL = "lmhead_partials_kernel<true, false>"
 STATS_KERNEL = "stats_stream_kernel"
 EXTRAS_KERNEL = "xsel_pass_kernel"
 
