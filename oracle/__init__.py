@@ -262,7 +262,8 @@ def logprob(h, w, ids, *, dtype: int, rows=None, nthreads: int = 0):
 
 
 def mismatch_stats(lt, lr, mask, cu_seqlens, *, clip_c: float, seq_lo: float,
-                   seq_hi: float, seq_k3_hi: float = float("inf")) -> dict:
+                   seq_hi: float, seq_k3_hi: float = float("inf"),
+                   token_outputs: bool = True) -> dict:
     """fp64 token, sequence and batch statistics (see module docstring).
 
     A sequence with a valid token is rejected when its mean delta is outside
@@ -275,8 +276,11 @@ def mismatch_stats(lt, lr, mask, cu_seqlens, *, clip_c: float, seq_lo: float,
     m = None if mask is None else _as_host_array(mask, np.uint8)
     n = lt.size
     s = cu.size - 1
-    tok = {k: np.empty(n, np.float64) for k in ("delta", "ratio", "k1", "k2", "k3", "tis_w")}
-    tok["clipped"] = np.empty(n, np.uint8)
+    if token_outputs:
+        tok = {k: np.empty(n, np.float64) for k in ("delta", "ratio", "k1", "k2", "k3", "tis_w")}
+        tok["clipped"] = np.empty(n, np.uint8)
+    else:   # large inputs: sequence and batch results only
+        tok = {k: None for k in ("delta", "ratio", "k1", "k2", "k3", "tis_w", "clipped")}
     seq = {k: np.empty(s, np.int32) for k in ("n_valid", "n_clipped", "n_nan")}
     seq.update({k: np.empty(s, np.float64) for k in
                 ("mean_delta", "mean_k1", "mean_k2", "mean_k3", "mean_tis_w")})
@@ -354,14 +358,17 @@ def logprob_backward(h, w, ids, g, *, dtype: int, dh_rows=None, dw_rows=None, nt
 
 
 def ppo_loss(logp, old_train, old_rollout, adv, mask, *, eps_lo: float, eps_hi: float,
-             bypass: bool = False, tis_c: float = 0.0) -> dict:
+             bypass: bool = False, tis_c: float = 0.0, token_outputs: bool = True) -> dict:
     """fp64 per-token loss, gradient (of the token mean), ratio,
     contribution and clip flag, and the batch vector (``PPO_FIELDS``)."""
     arrs = [_as_host_array(x, np.float32) for x in (logp, old_train, old_rollout, adv)]
     m = None if mask is None else _as_host_array(mask, np.uint8)
     n = arrs[0].size
-    out = {k: np.empty(n, np.float64) for k in ("loss", "grad", "ratio", "contrib")}
-    out["clipped"] = np.empty(n, np.uint8)
+    if token_outputs:
+        out = {k: np.empty(n, np.float64) for k in ("loss", "grad", "ratio", "contrib")}
+        out["clipped"] = np.empty(n, np.uint8)
+    else:   # large inputs: the batch vector only
+        out = {k: None for k in ("loss", "grad", "ratio", "contrib", "clipped")}
     batch = np.empty(len(PPO_FIELDS), np.float64)
     rc = _load().or_ppo_loss(*[_ptr(a) for a in arrs], _ptr(m), n, float(eps_lo), float(eps_hi),
                              int(bool(bypass)), float(tis_c), _ptr(out["loss"]), _ptr(out["grad"]),
