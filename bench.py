@@ -193,7 +193,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(f"{name}:N={n}"),
-                     "kernel": "lmhead_partials_kernel<bf16> + lse_merge (one forward call)",
+                     "kernel": "lmhead8w_kernel (bf16) + lse_merge (one forward call)",
                      "flops_per_launch": flops, "avg_launch_ms": lp_avg},
         "stats_step_us": float(np.mean(t_st)) * 1e3,
     }
@@ -214,7 +214,7 @@ def main():
 
 COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration kernel
 COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
-LMHEAD_KERNEL = "lmhead_partials_kernel<true, false>"
+LMHEAD_KERNEL = "lmhead8w_kernel<false>"
 STATS_KERNEL = "stats_stream_kernel"
 EXTRAS_KERNEL = "xsel_pass_kernel"
 

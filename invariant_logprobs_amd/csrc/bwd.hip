@@ -13,8 +13,9 @@
 //   1. transpose_bf16: W^T [D][Vp] and h^T [D][Np], zero-padded to multiples
 //      of 64 along the contracted dimension.
 //   2. gemm_nt<kEpiDz>: the logits of a 256 x 256 (vocabulary x token) tile,
-//      recomputed with the forward's K order and MFMA, so they are the
-//      forward's bits; the epilogue forms dz with the forward's lse and writes
+//      recomputed in ascending K with fp32 accumulation (32x32x16 MFMAs; the
+//      bf16 forward uses 16x16x32, so a logit can differ from the forward's
+//      in its last bits); the epilogue forms dz with the forward's lse and writes
 //      dz^T [Vp][Np] (bf16, zero outside V x N).
 //   3. transpose_bf16: dz [Np][Vp].
 //   4. gemm_nt<kEpiStore>: dh[t, d] = sum_v dz[t, v] W^T[d, v].

@@ -6,6 +6,9 @@
 //     z[t,v]  = sum_k h[t,k] W[v,k]
 //     logp[t] = z[t,a_t] - log sum_v exp z[t,v]
 // The logits live only in MFMA accumulators; they are never written.
+// bf16 inputs run lmhead8w_kernel (16x16x32 MFMAs, eight waves), fp32
+// inputs lmhead_partials_kernel (32x32x2 MFMAs, four waves); both follow
+// the same tiles, chunks and merge order, described first for the latter.
 //
 // Batch invariance ("训推一致性与 determinism", section 1.2: a request's
 // result must not depend on which other requests share its batch): every
@@ -509,6 +512,402 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     }
 }
 
+// bf16 partials: 16x16x32 MFMAs, eight waves, two per SIMD.
+//
+// Same tiles, vocabulary chunks, LDS ring, copies and chunk-merge order as
+// lmhead_partials_kernel (which serves fp32).  On this chip a 16x16x32 bf16
+// MFMA stream sustains 2.08 PFLOP/s against 1.75 for 32x32x16; and with two
+// waves per SIMD one wave's MFMAs keep the matrix unit busy while the other
+// waits on the issue of its buffer-to-LDS copies or at a barrier.  The
+// workgroup has 8 waves: wave w owns vocabulary rows (w & 1) * 128 .. + 127
+// and tokens (w >> 1) * 64 .. + 63 of the tile, as 8 x 4 MFMA blocks of
+// 16 x 16 (acc[bi][bj]: rows bi * 16 + .., tokens bj * 16 + ..; 128
+// accumulator registers, so two waves fit a SIMD).  A fragment (16 rows x
+// 32 K): lane l holds row l & 15, K 8 (l >> 4) .. + 7; an output block: lane
+// l holds rows 4 (l >> 4) + i of column l & 15.  A stage (128 bytes of K) is
+// two k-steps; each wave copies 4 units of W and 4 of h (1 KiB each) per
+// stage.
+//
+// Fragment registers: A[8] (one per row block), B0[4] and B1[4] (the column
+// blocks of the stage's two k-steps).  Reads run ahead of the MFMAs:
+//   ks0: read B1 (this stage's ks1); per row r: wait, 4 MFMAs (a W copy for
+//        stage + 1 in rows 0-3), read A[r] <- ks1 row r.
+//   ks1: rows 0-3: wait, 4 MFMAs, an h copy (stage + 2); then wait for this
+//        wave's copies of stage + 1 and for all its reads, barrier, read B0
+//        and A[0..3] <- next stage ks0; rows 4-7: 4 MFMAs, read A[r] <- next
+//        stage ks0 row r.
+// LDS reads of a wave complete in order; counting the reads issued after
+// the one a row needs gives the waits: 11 for every ks0 row, 7 - r for ks1
+// rows 0-3 (ks1 rows 4-7 need nothing new).
+template <bool kEnt>
+__global__ void __launch_bounds__(2 * kThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
+                const unsigned char* __restrict__ w, int64_t ldw_b,
+                const int32_t* __restrict__ ids, int64_t n, int64_t v,
+                int nk, int chunk_tiles, int64_t nvtiles, int64_t nchunks,
+                int64_t nttiles, float c2, float2* __restrict__ part,
+                float* __restrict__ upart, float* __restrict__ zsel,
+                int32_t* __restrict__ n_bad_ids) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wv = wave & 1;        // vocabulary half of the tile (128 rows)
+    const int wt = wave >> 1;       // token quarter of the tile (64 tokens)
+    const int col = lane & 15;      // token column inside a 16 x 16 block
+    const int grp = lane >> 4;      // row group: rows 4 grp .. 4 grp + 3 of a block
+
+    if (blockIdx.x == 0 && tid == 0 && n_bad_ids) *n_bad_ids = 0;
+
+    int64_t chunk, ttile;
+    tile_of_block(nchunks, nttiles, chunk, ttile);
+    const int64_t t0 = ttile * kTileT;
+    const int64_t vt_first = chunk * chunk_tiles;
+    const int ntiles_here = (int)((nvtiles - vt_first) < chunk_tiles ? (nvtiles - vt_first)
+                                                                      : chunk_tiles);
+
+    // the 4 tokens of this lane (one per 16-column block) and their ids
+    int32_t my_id[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        const int64_t t = t0 + wt * 64 + bj * 16 + col;
+        my_id[bj] = t < n ? ids[t] : -1;
+    }
+
+    f32x4 acc[8][4];
+    float m_run[4], s_run[4], u_run[4];
+    float zsel_reg[4];
+    bool have_zsel = false;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        m_run[bj] = -INFINITY; s_run[bj] = 0.f; u_run[bj] = 0.f; zsel_reg[bj] = 0.f;
+    }
+
+    // Copies: as in lmhead_partials_kernel, with eight waves: 8-row blocks
+    // 4 wave .. 4 wave + 3 of both operands, swizzled chunks, rows past N or
+    // V redirected to the last valid row.
+    uint32_t hoff[4], wrow_off[4], wtail_off[4];
+    int drow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        drow[j] = (wave * 4 + j) * 8 + (lane >> 3);
+        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((drow[j] >> 1) & 7)) * 16);
+        int64_t t = t0 + drow[j];
+        if (t > n - 1) t = n - 1;
+        hoff[j] = (uint32_t)((t - t0) * ldh_b) + cb;
+        wrow_off[j] = (uint32_t)(drow[j] * ldw_b) + cb;
+        wtail_off[j] = cb;
+    }
+    const unsigned char* hbase = h + t0 * ldh_b;
+    const int64_t hrows = (n - t0) < kTileT ? (n - t0) : kTileT;
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)hbase, (short)0, (int)((hrows - 1) * ldh_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+    uint32_t woff[4];
+    __amdgpu_buffer_rsrc_t wrs = hrs;
+    auto set_wtile = [&](int vt_l) {
+        const int64_t vbase = (vt_first + vt_l) * kTileV;
+        const unsigned char* wbase = w + vbase * ldw_b;
+        const int64_t wrows = (v - vbase) < kTileV ? (v - vbase) : kTileV;
+        wrs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0,
+                                                (int)((wrows - 1) * ldw_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            woff[j] = vbase + drow[j] < v ? wrow_off[j]
+                                          : (uint32_t)((v - 1 - vbase) * ldw_b) + wtail_off[j];
+    };
+
+    // fragment addresses: row col of a 16-row block, logical chunk ks*4 + grp
+    const uint32_t lds_base = lds_addr(lds);
+    const uint32_t kofs0 = (uint32_t)swz(col, 0 * 4 + grp);
+    const uint32_t kofs1 = (uint32_t)swz(col, 1 * 4 + grp);
+    const uint32_t a_half = (uint32_t)(wv * 128 * kStageBytes);   // this wave's W rows
+    const uint32_t b_half = (uint32_t)(wt * 64 * kStageBytes);    // this wave's h rows
+
+    int w_kb = 0, w_vt = 0, h_kb = 0;
+    set_wtile(0);
+    auto copy_w = [&](int j, int pos) {
+        dma16_buf(wrs, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, woff[j],
+                  (uint32_t)(w_kb * kStageBytes));
+    };
+    auto copy_h = [&](int j, int pos) {
+        dma16_buf(hrs, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, hoff[j],
+                  (uint32_t)(h_kb * kStageBytes));
+    };
+    auto advance_w = [&]() {
+        if (++w_kb == nk) {
+            w_kb = 0;
+            if (++w_vt < ntiles_here) set_wtile(w_vt);
+        }
+    };
+    auto advance_h = [&]() {
+        if (++h_kb == nk) h_kb = 0;
+    };
+    auto next_pos = [](int p) { return p + 2 >= kPos ? p + 2 - kPos : p + 2; };
+
+    u32x4 A[8], B0[4], B1[4];
+    // reads of one k-step's fragments (block offsets as immediates)
+    auto read_a = [&](int r, uint32_t base) {
+        switch (r) {
+            case 0: lds_read16<0 * 2048>(A[0], base); break;
+            case 1: lds_read16<1 * 2048>(A[1], base); break;
+            case 2: lds_read16<2 * 2048>(A[2], base); break;
+            case 3: lds_read16<3 * 2048>(A[3], base); break;
+            case 4: lds_read16<4 * 2048>(A[4], base); break;
+            case 5: lds_read16<5 * 2048>(A[5], base); break;
+            case 6: lds_read16<6 * 2048>(A[6], base); break;
+            default: lds_read16<7 * 2048>(A[7], base); break;
+        }
+    };
+    auto read_b = [&](u32x4 (&B)[4], uint32_t base) {
+        lds_read16<0 * 2048>(B[0], base);
+        lds_read16<1 * 2048>(B[1], base);
+        lds_read16<2 * 2048>(B[2], base);
+        lds_read16<3 * 2048>(B[3], base);
+    };
+    // The MFMAs are written as asm with the accumulator tied ("+a": the same
+    // AGPRs are source C and destination).  With the builtin, and every
+    // accumulator register taken, the register allocator picked untied forms
+    // and shuffled accumulators between registers inside the K loop.  The hazard recognizer does not see
+    // into asm, so the wait states it would insert around MFMAs are written
+    // out below: after zeroing the accumulators and before the epilogue
+    // reads them.
+    auto mfma = [&](int r, int bj, const u32x4& b) {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                     : "+a"(acc[r][bj]) : "v"(A[r]), "v"(b));
+    };
+
+    // Ring positions as in lmhead_partials_kernel: (2 stage + op) % 5.
+    int rd_h = 0, rd_w = 1;
+    int cp_w = 3, cp_h = 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_h(j, 0);
+    advance_h();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_w(j, 1);
+    advance_w();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_h(j, 2);
+    advance_h();
+    wait_vmcnt<4>();
+    __syncthreads();
+    {
+        const uint32_t aw = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
+        const uint32_t bh = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
+        read_b(B0, bh + kofs0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) read_a(r, aw + kofs0);
+    }
+
+    for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
+#pragma unroll
+        for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // accumulator writes, then MFMAs that read them as source C
+        asm volatile("s_nop 4" ::: "memory");
+
+        for (int kb = 0; kb < nk; ++kb) {
+            const uint32_t aw = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
+            const uint32_t bh = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
+            // ---- ks0: W(s+1) copies at rows 0-3
+            read_b(B1, bh + kofs1);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (r == 0) wait16_4<11>(A[0], B0);
+                else wait16<11>(A[r]);
+                mfma(r, 0, B0[0]); mfma(r, 1, B0[1]);
+                if (r < 4) copy_w(r, cp_w);
+                mfma(r, 2, B0[2]); mfma(r, 3, B0[3]);
+                read_a(r, aw + kofs1);
+            }
+            advance_w();
+            // ---- ks1, rows 0-3: h(s+2) copies
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (r == 0) wait16_4<7>(A[0], B1);
+                else if (r == 1) wait16<6>(A[1]);
+                else if (r == 2) wait16<5>(A[2]);
+                else wait16<4>(A[3]);
+                mfma(r, 0, B1[0]); mfma(r, 1, B1[1]);
+                copy_h(r, cp_h);
+                mfma(r, 2, B1[2]); mfma(r, 3, B1[3]);
+            }
+            // stage + 1 resident (this wave's copies, then everyone's) and
+            // every read of this stage done before its slots are reused
+            wait_vmcnt<4>();
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
+            asm volatile("s_barrier" ::: "memory");
+            rd_h = next_pos(rd_h);
+            rd_w = next_pos(rd_w);
+            const uint32_t aw2 = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
+            const uint32_t bh2 = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
+            read_b(B0, bh2 + kofs0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) read_a(r, aw2 + kofs0);
+            // ---- ks1, rows 4-7
+#pragma unroll
+            for (int r = 4; r < 8; ++r) {
+                wait16<11>(A[r]);
+                mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]); mfma(r, 3, B1[3]);
+                read_a(r, aw2 + kofs0);
+            }
+            advance_h();
+            cp_w = next_pos(cp_w);
+            cp_h = next_pos(cp_h);
+        }
+
+        // the last MFMAs' results, then accumulator reads: wait states
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+        // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
+        // Per token column bj the lane's 32 rows (bi = 0..7, i = 0..3) are
+        // folded as two 16-value groups (bi 0-3, then 4-7) into the running
+        // state; inside a group the exponentials are summed by a fixed
+        // pairwise tree.  Rows past V (last tile only) are -inf.
+        const int64_t vbase_w = (vt_first + vt_local) * kTileV + wv * 128;
+        const int64_t lim64 = v - vbase_w - grp * 4;     // row offsets bi*16 + i < lim are valid
+        const int lim = lim64 > 128 ? 128 : (int)lim64;
+        auto fold = [&](auto masked_tag) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+                for (int part = 0; part < 4; ++part) {      // bi = 2 part, 2 part + 1
+                    float z[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int bi = part * 2 + (q >> 2), i = q & 3;
+                        z[q] = acc[bi][bj][i];
+                        if constexpr (kMasked) z[q] = bi * 16 + i < lim ? z[q] : -INFINITY;
+                    }
+                    float bmax = z[0];
+#pragma unroll
+                    for (int q = 1; q < 8; ++q) bmax = fmaxf(bmax, z[q]);
+                    const float m_new = fmaxf(m_run[bj], bmax);
+                    const float mref = m_new == -INFINITY ? 0.f : m_new;
+                    const float dsh = (m_run[bj] - mref) * c2;
+                    const float scale = m_run[bj] == m_new ? 1.f : fast_exp2(dsh);
+                    float e[8];
+                    if constexpr (kEnt) {
+                        float ea[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const float a = fmaxf((z[q] - mref) * c2, kArgFloor);
+                            e[q] = fast_exp2(a);
+                            ea[q] = e[q] * a;
+                        }
+#pragma unroll
+                        for (int width = 4; width >= 1; width >>= 1)
+#pragma unroll
+                            for (int q = 0; q < width; ++q) ea[q] = ea[q] + ea[q + width];
+                        const float uo = m_run[bj] == m_new
+                                             ? u_run[bj]
+                                             : (s_run[bj] > 0.f ? scale * fmaf(dsh, s_run[bj], u_run[bj])
+                                                                : 0.f);
+                        u_run[bj] = uo + ea[0];
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) e[q] = fast_exp2((z[q] - mref) * c2);
+                    }
+#pragma unroll
+                    for (int width = 4; width >= 1; width >>= 1)
+#pragma unroll
+                        for (int q = 0; q < width; ++q) e[q] = e[q] + e[q + width];
+                    s_run[bj] = fmaf(s_run[bj], scale, e[0]);
+                    m_run[bj] = m_new;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        if (lim < 128) fold(BoolConst<true>{});
+        else fold(BoolConst<false>{});
+
+        // gather: exactly one lane of the grid holds z[t, a_t]
+        int tgt[4];
+        bool any_tgt = false;
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t rel = (int64_t)my_id[bj] - vbase_w;
+            const bool mine = rel >= 0 && rel < 128 && (int)((rel & 15) >> 2) == grp;
+            tgt[bj] = mine ? (int)((rel >> 4) * 4 + (rel & 3)) : -1;
+            any_tgt |= mine;
+        }
+        if (any_tgt) {
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+                for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        zsel_reg[bj] = tgt[bj] == bi * 4 + i ? acc[bi][bj][i] : zsel_reg[bj];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            have_zsel = true;
+        }
+    }
+    // drain: the look-ahead reads and the extra copies; the ring is reused below
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3]),
+                 "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B0[0]), "+v"(B0[1]), "+v"(B0[2]), "+v"(B0[3]));
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // ---- the selected logits this lane owns (one owner per token)
+    if (have_zsel) {
+        const int64_t chunk_rows = (int64_t)ntiles_here * kTileV;
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t in_chunk = (int64_t)my_id[bj] - vt_first * kTileV;
+            if (in_chunk >= 0 && in_chunk < chunk_rows && ((in_chunk & 255) >> 7) == wv &&
+                (int)((in_chunk & 15) >> 2) == grp)
+                zsel[t0 + wt * 64 + bj * 16 + col] = zsel_reg[bj];
+        }
+    }
+
+    // ---- end of chunk: merge the four row groups (xor 16, then 32), then
+    // the two vocabulary waves
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+        for (int sh = 16; sh <= 32; sh <<= 1) {
+            const float mo = __shfl_xor(m_run[bj], sh);
+            const float so = __shfl_xor(s_run[bj], sh);
+            if constexpr (kEnt) {
+                const float uo = __shfl_xor(u_run[bj], sh);
+                lse_combine3(m_run[bj], s_run[bj], u_run[bj], mo, so, uo, c2);
+            } else {
+                lse_combine(m_run[bj], s_run[bj], mo, so, c2);
+            }
+        }
+    }
+    float2* xch = (float2*)lds;          // [token quarter][token]; the ring is drained
+    float* xu = (float*)(lds + 2048);    // u, same index
+    if (wv == 1 && grp == 0) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            xch[wt * 64 + bj * 16 + col] = make_float2(m_run[bj], s_run[bj]);
+            if constexpr (kEnt) xu[wt * 64 + bj * 16 + col] = u_run[bj];
+        }
+    }
+    __syncthreads();
+    if (wv == 0 && grp == 0) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const float2 o = xch[wt * 64 + bj * 16 + col];
+            float m = m_run[bj], s = s_run[bj], u = u_run[bj];
+            const int64_t t = t0 + wt * 64 + bj * 16 + col;
+            if constexpr (kEnt) {
+                lse_combine3(m, s, u, o.x, o.y, xu[wt * 64 + bj * 16 + col], c2);
+                if (t < n) upart[chunk * n + t] = u;
+            } else {
+                lse_combine(m, s, o.x, o.y, c2);
+            }
+            if (t < n) part[chunk * n + t] = make_float2(m, s);
+        }
+    }
+}
+
 // Merge of the vocabulary-chunk partials.  A block serves 64 tokens with
 // kMergeWaves waves: wave w folds chunks w, w + kMergeWaves, ... in ascending
 // order for its 64 tokens (coalesced 8-byte loads, kMergeUnroll in flight),
@@ -637,8 +1036,14 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
                            sc.c2, part, upart, zsel, n_bad_ids);
     };
     if (p.dtype == 0) {
-        if (p.entropy) go(lmhead_partials_kernel<true, true>);
-        else go(lmhead_partials_kernel<true, false>);
+        auto go8 = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(2 * kThreads), 0, st,
+                               (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
+                               ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
+                               sc.c2, part, upart, zsel, n_bad_ids);
+        };
+        if (p.entropy) go8(lmhead8w_kernel<true>);
+        else go8(lmhead8w_kernel<false>);
     } else {
         if (p.entropy) go(lmhead_partials_kernel<false, true>);
         else go(lmhead_partials_kernel<false, false>);

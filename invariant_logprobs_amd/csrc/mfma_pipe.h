@@ -91,6 +91,39 @@ __device__ __forceinline__ void frags_ready(u32x4 (&f)[8]) {
                        "+v"(f[6]), "+v"(f[7]));
 }
 
+// 16x16x32 pipeline.  One 16-byte LDS read per fragment, issued alone (the
+// immediate offset selects the 16-row block), not waited for; wait16<N>
+// waits until at most N LDS operations are outstanding and passes the
+// fragments that the next MFMAs read through the asm, so that no use of
+// them can be scheduled before the wait.  It ends with one wait state, as
+// the compiler places between such a wait and an MFMA reading its result.
+template <int kOff>
+__device__ __forceinline__ void lds_read16(u32x4& r, uint32_t addr) {
+    static_assert(kOff >= 0 && kOff < 65536, "ds_read immediate offset");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait16(u32x4& a) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%1)\n\ts_nop 0" : "+v"(a) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void wait16(u32x4& a, u32x4 (&b)[8]) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%9)\n\ts_nop 0"
+                 : "+v"(a), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]),
+                   "+v"(b[5]), "+v"(b[6]), "+v"(b[7])
+                 : "i"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void wait16_4(u32x4& a, u32x4 (&b)[4]) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%5)\n\ts_nop 0"
+                 : "+v"(a), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 : "i"(N));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
