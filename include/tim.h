@@ -449,9 +449,11 @@ size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int
  *             inputs (the softmax is exp(z - lse)).
  *  grad_logp  [n] fp32.  A token with grad 0, or an id outside [0, v),
  *             contributes nothing.
- *  dh         [n, d] fp32 out (row stride d), nullable.
- *  dw         [v, d] fp32 out (row stride d), nullable.  With
- *             TIM_BWD_ACCUMULATE_DW its incoming values start the sums.
+ *  dh         [n, d] fp32 out (row stride d), nullable; 16-byte aligned
+ *             (else TIM_EUNSUPPORTED).
+ *  dw         [v, d] fp32 out (row stride d), nullable; 16-byte aligned
+ *             (else TIM_EUNSUPPORTED).  With TIM_BWD_ACCUMULATE_DW its
+ *             incoming values start the sums.
  *  flags      0 or TIM_BWD_ACCUMULATE_DW.
  *  workspace  >= tim_logprob_backward_workspace_bytes(...) bytes,
  *             256-byte aligned.

@@ -10,16 +10,16 @@
 //     dW = dz^T h         (K = tokens, ascending)
 // bf16 operands, fp32 accumulation; dz is rounded to bf16 once (as the
 // logits' gradient enters a bf16 GEMM in a bf16 trainer).  Steps:
-//   1. transpose_bf16: W^T [D][Vp] and h^T [D][Np], zero-padded to multiples
-//      of 64 along the contracted dimension.
-//   2. gemm_nt<kEpiDz>: the logits of a 256 x 256 (vocabulary x token) tile,
-//      recomputed in ascending K with fp32 accumulation (32x32x16 MFMAs; the
-//      bf16 forward uses 16x16x32, so a logit can differ from the forward's
-//      in its last bits); the epilogue forms dz with the forward's lse and writes
-//      dz^T [Vp][Np] (bf16, zero outside V x N).
-//   3. transpose_bf16: dz [Np][Vp].
-//   4. gemm_nt<kEpiStore>: dh[t, d] = sum_v dz[t, v] W^T[d, v].
-//   5. gemm_nt<kEpiStore>: dW[v, d] = sum_t dz^T[v, t] h^T[d, t].
+//   1. gemm8w<kEpiDz>: the logits of a 256 x 256 (vocabulary x token) tile,
+//      recomputed as the bf16 forward forms them (16x16x32 MFMAs, same
+//      operand order, ascending K from zero, fp32 accumulation); the
+//      epilogue forms dz with the forward's lse and writes it twice, as
+//      dz^T [Vp][Np] and dz [Np][Vp] (bf16, zero outside V x N; Vp, Np =
+//      V, N rounded up to multiples of 64), so no transpose of dz is needed.
+//   2. transpose_bf16: W^T [D][Vp] (zero-padded); gemm8w<kEpiStore>:
+//      dh[t, d] = sum_v dz[t, v] W^T[d, v].
+//   3. transpose_bf16: h^T [D][Np]; gemm8w<kEpiStore>:
+//      dW[v, d] = sum_t dz^T[v, t] h^T[d, t].
 // Every output element is one fp32 MFMA accumulator chain in ascending K, no
 // split-K, no atomics: dh's row t depends only on token t (batch invariant),
 // and dW in accumulate mode continues the chain from the stored value, so
@@ -82,12 +82,13 @@ struct GemmArgs {
     const unsigned char* b; int64_t ldb_b; int64_t n;   // B: n rows, K contiguous
     int nk;                                             // K / 64 stages
     int64_t mtiles, ntiles;
-    // kEpiStore
+    // kEpiStore, kEpiStoreAcc: c 16-byte aligned, ldc and n multiples of 4
     float* c; int64_t ldc;
     // kEpiDz (A = W, B = h): logits of valid rows m < vtrue, n < ntrue
     const float* lse; const float* g; const int32_t* ids;
     int64_t vtrue, ntrue;
-    uint16_t* dzt; int64_t lddz;                        // dz^T [Vp][Np]
+    uint16_t* dzt; int64_t lddz;                        // dz^T [Vp][Np], or null
+    uint16_t* dz; int64_t ldz;                          // dz [Np][Vp], or null
     int64_t vpad, npad;
 };
 
@@ -117,69 +118,80 @@ __device__ __forceinline__ void gemm_tile_of_block(int64_t mtiles, int64_t ntile
     nt = within / gm;
 }
 
+// Eight waves, two per SIMD, as the bf16 head kernel (its pipeline without
+// the walk over vocabulary tiles): one 256 x 256 tile of C per workgroup;
+// wave w owns A rows (w & 1) * 128 .. + 127 and B rows (w >> 1) * 64 .. + 63
+// of the tile as 8 x 4 blocks of 16 x 16 (acc[bi][bj], 128 accumulator
+// registers); 16x16x32 MFMAs, two k-steps per 128-byte stage, A of stage
+// s + 1 and B of stage s + 2 copied while stage s computes, four copies of
+// each per wave per stage.
+//
+// kEpiDz gives the MFMAs the operands in the head kernel's order (A = W
+// fragments first, same K order from zero), so the recomputed logits are
+// the ones the forward formed; a lane then holds rows 4 grp + i of column
+// col of each block.  The store epilogues swap the two sources (B
+// fragments first), so that a lane holds four consecutive columns
+// 4 grp .. 4 grp + 3 of row col: one 16-byte store (and load) per block.
 template <int kEpi>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_nt_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(2 * kThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm8w_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    constexpr bool kSwap = kEpi != kEpiDz;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int wv = wave & 1;        // row half of the tile (128 rows of A)
-    const int wt = wave >> 1;       // column half of the tile (128 rows of B)
-    const int lrow = lane & 31;
-    const int lhalf = lane >> 5;
+    const int wv = wave & 1;        // A half of the tile (128 rows)
+    const int wt = wave >> 1;       // B quarter of the tile (64 rows)
+    const int col = lane & 15;
+    const int grp = lane >> 4;
 
     int64_t mt, nt;
     gemm_tile_of_block(p.mtiles, p.ntiles, mt, nt);
-    // the tile indices are uniform; saying so keeps the buffer descriptors
-    // built from them in scalar registers (else every copy is a waterfall loop)
+    // uniform tile indices keep the buffer descriptors in scalar registers
     const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)mt) * kTileV;
     const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((int)nt) * kTileT;
+    const int64_t mw = m0 + wv * 128;     // first A row (row of C) of this wave
+    const int64_t nw = n0 + wt * 64;      // first B row (column of C) of this wave
     const int nk = p.nk;
 
-    f32x16 acc[4][4];
-    // output element of acc[bi][bj][r]: row m0 + wv*128 + bi*32 + (r/4)*8 +
-    // lhalf*4 + r%4, column n0 + wt*128 + bj*32 + lrow
-    auto row_of = [&](int bi, int r) -> int64_t {
-        return m0 + wv * 128 + bi * 32 + (r >> 2) * 8 + lhalf * 4 + (r & 3);
-    };
-    auto col_of = [&](int bj) -> int64_t { return n0 + wt * 128 + bj * 32 + lrow; };
+    f32x4 acc[8][4];
     if constexpr (kEpi == kEpiStoreAcc) {
-        // the chain continues from the stored value
+        // the chain continues from the stored value (swapped layout: row
+        // mw + bi 16 + col, columns nw + bj 16 + 4 grp .. + 3: one 16-byte
+        // load; n is a multiple of 4)
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
+        for (int bi = 0; bi < 8; ++bi) {
+            const int64_t row = mw + bi * 16 + col;
+            const float* crow = p.c + (row < p.m ? row : 0) * p.ldc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = row_of(bi, r);
-                const float* crow = p.c + (row < p.m ? row : 0) * p.ldc;
-#pragma unroll
-                for (int bj = 0; bj < 4; ++bj) {
-                    const int64_t col = col_of(bj);
-                    acc[bi][bj][r] = (row < p.m && col < p.n) ? crow[col] : 0.f;
-                }
-                // a few loads in flight at a time: unbounded, the compiler
-                // issues all 256 at once and spills their destinations
-                if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            for (int bj = 0; bj < 4; ++bj) {
+                const int64_t c0 = nw + bj * 16 + grp * 4;
+                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (row < p.m && c0 < p.n) q = *(const float4*)(crow + c0);
+                acc[bi][bj] = f32x4{q.x, q.y, q.z, q.w};
+                // into the accumulator registers now, not held in VGPRs
+                asm volatile("" : "+a"(acc[bi][bj]));
             }
+            // a few loads in flight at a time, not all 128 at once
+            if (bi & 1) __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
+        for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+            for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Copy assignment as in the forward kernel: wave `wave` fills 8-row
-    // blocks 8 wave .. 8 wave + 7 of both operand tiles; rows past m or n are
-    // redirected to the last valid row (results discarded), so every access
-    // lies inside the operands and inside the descriptors' extents.
-    uint32_t aoff[8], boff[8];
+    // Copies: wave `wave` fills 8-row blocks 4 wave .. 4 wave + 3 of both
+    // operand tiles (swizzled chunks); rows past m or n are redirected to the
+    // last valid row (results discarded), so every access lies inside the
+    // operands and inside the descriptors' extents.
+    uint32_t aoff[4], boff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int drow = (wave * 8 + j) * 8 + (lane >> 3);
+    for (int j = 0; j < 4; ++j) {
+        const int drow = (wave * 4 + j) * 8 + (lane >> 3);
         const uint32_t cb = (uint32_t)(((lane & 7) ^ ((drow >> 1) & 7)) * 16);
         int64_t ra = m0 + drow, rb = n0 + drow;
         if (ra > p.m - 1) ra = p.m - 1;
@@ -196,168 +208,197 @@ gemm_nt_kernel(GemmArgs p) {
         (void*)(p.b + n0 * p.ldb_b), (short)0,
         (int)((brows - 1) * p.ldb_b + (int64_t)nk * kStageBytes), kRsrcWord3);
 
+    // fragment addresses: row col of a 16-row block, logical chunk ks 4 + grp
     const uint32_t lds_base = lds_addr(lds);
-    uint32_t kofs[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kofs[ks] = (uint32_t)swz(lrow, ks * 2 + lhalf);
+    const uint32_t kofs0 = (uint32_t)swz(col, 0 * 4 + grp);
+    const uint32_t kofs1 = (uint32_t)swz(col, 1 * 4 + grp);
+    const uint32_t a_half = (uint32_t)(wv * 128 * kStageBytes);
+    const uint32_t b_quarter = (uint32_t)(wt * 64 * kStageBytes);
 
-    // A of stage st + 1 and B of stage st + 2 are copied while stage st
-    // computes; past the last stage both wrap to K offset 0 (valid rows into
-    // positions that are never read again).
     int a_kb = 0, b_kb = 0;
-    auto copy_a = [&](int part, int pos) {
-        unsigned char* base = lds + pos * kOperandBytes;
-        const uint32_t koff = (uint32_t)(a_kb * kStageBytes);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int j = part * 4 + jj;
-            dma16_buf(ars, base + (wave * 8 + j) * 1024, aoff[j], koff);
-        }
+    auto copy_a = [&](int j, int pos) {
+        dma16_buf(ars, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, aoff[j],
+                  (uint32_t)(a_kb * kStageBytes));
     };
-    auto copy_b = [&](int part, int pos) {
-        unsigned char* base = lds + pos * kOperandBytes;
-        const uint32_t koff = (uint32_t)(b_kb * kStageBytes);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int j = part * 4 + jj;
-            dma16_buf(brs, base + (wave * 8 + j) * 1024, boff[j], koff);
-        }
+    auto copy_b = [&](int j, int pos) {
+        dma16_buf(brs, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, boff[j],
+                  (uint32_t)(b_kb * kStageBytes));
     };
     auto advance_a = [&]() { if (++a_kb == nk) a_kb = 0; };
     auto advance_b = [&]() { if (++b_kb == nk) b_kb = 0; };
     auto next_pos = [](int q) { return q + 2 >= kPos ? q + 2 - kPos : q + 2; };
-    auto issue_frags = [&](u32x4 (&f)[8], int pa, int pb, int ks) {
-        lds_issue_8x16(f, lds_base + (uint32_t)(pa * kOperandBytes) + kofs[ks] + (uint32_t)(wv * 128 * kStageBytes),
-                       lds_base + (uint32_t)(pb * kOperandBytes) + kofs[ks] + (uint32_t)(wt * 128 * kStageBytes));
+
+    u32x4 A[8], B0[4], B1[4];
+    auto read_a = [&](int r, uint32_t base) {
+        switch (r) {
+            case 0: lds_read16<0 * 2048>(A[0], base); break;
+            case 1: lds_read16<1 * 2048>(A[1], base); break;
+            case 2: lds_read16<2 * 2048>(A[2], base); break;
+            case 3: lds_read16<3 * 2048>(A[3], base); break;
+            case 4: lds_read16<4 * 2048>(A[4], base); break;
+            case 5: lds_read16<5 * 2048>(A[5], base); break;
+            case 6: lds_read16<6 * 2048>(A[6], base); break;
+            default: lds_read16<7 * 2048>(A[7], base); break;
+        }
     };
-    auto mfma_step = [&](const u32x4 (&f)[8]) {
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
-                acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, f[bi]), __builtin_bit_cast(bf16x8, f[4 + bj]),
-                    acc[bi][bj], 0, 0, 0);
+    auto read_b = [&](u32x4 (&B)[4], uint32_t base) {
+        lds_read16<0 * 2048>(B[0], base);
+        lds_read16<1 * 2048>(B[1], base);
+        lds_read16<2 * 2048>(B[2], base);
+        lds_read16<3 * 2048>(B[3], base);
+    };
+    // tied-accumulator asm MFMAs (mfma_pipe.h); the store epilogues swap
+    // the sources
+    auto mfma = [&](int r, int bj, const u32x4& b) {
+        if constexpr (kSwap) mfma16_tied(acc[r][bj], b, A[r]);
+        else mfma16_tied(acc[r][bj], A[r], b);
+    };
+    auto mfma_last = [&](const u32x4& b, int last) {
+        if constexpr (kSwap) mfma16_tied_last(acc[7][3], b, A[7], last);
+        else mfma16_tied_last(acc[7][3], A[7], b, last);
     };
 
-    // Pipeline of the forward kernel (ring positions (2 stage + op) % 5, op 0:
-    // B, op 1: A; four copies per k-step, one after every four MFMAs).
+    // Ring positions (2 stage + op) % 5, op 0: B, op 1: A.  LDS reads of a
+    // wave complete in order; the waits count the reads issued after the
+    // one a row needs: 11 for every ks0 row, 7 - r for ks1 rows 0-3.
     int rd_b = 0, rd_a = 1;
     int cp_a = 3, cp_b = 4;
-    copy_b(0, 0); copy_b(1, 0); advance_b();
-    copy_a(0, 1); copy_a(1, 1); advance_a();
-    copy_b(0, 2); copy_b(1, 2); advance_b();
-    wait_vmcnt<kDmaPerStage / 2>();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_b(j, 0);
+    advance_b();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_a(j, 1);
+    advance_a();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_b(j, 2);
+    advance_b();
+    wait_vmcnt<4>();
     __syncthreads();
-    u32x4 fa[8], fb[8];
-    issue_frags(fa, rd_a, rd_b, 0);
+    {
+        const uint32_t aw = lds_base + (uint32_t)(rd_a * kOperandBytes) + a_half;
+        const uint32_t bw = lds_base + (uint32_t)(rd_b * kOperandBytes) + b_quarter;
+        read_b(B0, bw + kofs0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) read_a(r, aw + kofs0);
+    }
 
     for (int kb = 0; kb < nk; ++kb) {
-        issue_frags(fb, rd_a, rd_b, 1);
-        frags_ready<8>(fa);
-        copy_a(0, cp_a);
-        mfma_step(fa);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_frags(fa, rd_a, rd_b, 2);
-        frags_ready<8>(fb);
-        copy_a(1, cp_a);
-        mfma_step(fb);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t aw = lds_base + (uint32_t)(rd_a * kOperandBytes) + a_half;
+        const uint32_t bw = lds_base + (uint32_t)(rd_b * kOperandBytes) + b_quarter;
+        // ---- ks0: A(s+1) copies at rows 0-3
+        read_b(B1, bw + kofs1);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (r == 0) wait16_4<11>(A[0], B0);
+            else wait16<11>(A[r]);
+            mfma(r, 0, B0[0]); mfma(r, 1, B0[1]);
+            if (r < 4) copy_a(r, cp_a);
+            mfma(r, 2, B0[2]); mfma(r, 3, B0[3]);
+            read_a(r, aw + kofs1);
+        }
         advance_a();
-        issue_frags(fb, rd_a, rd_b, 3);
-        frags_ready<8>(fa);
-        copy_b(0, cp_b);
-        mfma_step(fa);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<kDmaPerStage / 4>();
-        frags_ready<0>(fb);
+        // ---- ks1, rows 0-3: B(s+2) copies
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (r == 0) wait16_4<7>(A[0], B1);
+            else if (r == 1) wait16<6>(A[1]);
+            else if (r == 2) wait16<5>(A[2]);
+            else wait16<4>(A[3]);
+            mfma(r, 0, B1[0]); mfma(r, 1, B1[1]);
+            copy_b(r, cp_b);
+            mfma(r, 2, B1[2]); mfma(r, 3, B1[3]);
+        }
+        // stage + 1 resident (this wave's copies, then everyone's) and every
+        // read of this stage done before its slots are reused
+        wait_vmcnt<4>();
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
         asm volatile("s_barrier" ::: "memory");
         rd_b = next_pos(rd_b);
         rd_a = next_pos(rd_a);
-        issue_frags(fa, rd_a, rd_b, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        copy_b(1, cp_b);
-        mfma_step(fb);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t aw2 = lds_base + (uint32_t)(rd_a * kOperandBytes) + a_half;
+        const uint32_t bw2 = lds_base + (uint32_t)(rd_b * kOperandBytes) + b_quarter;
+        read_b(B0, bw2 + kofs0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) read_a(r, aw2 + kofs0);
+        // ---- ks1, rows 4-7
+#pragma unroll
+        for (int r = 4; r < 8; ++r) {
+            wait16<11>(A[r]);
+            mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]);
+            if (r < 7) mfma(r, 3, B1[3]);
+            else mfma_last(B1[3], __builtin_amdgcn_readfirstlane(kb == nk - 1));   // + epilogue wait
+            read_a(r, aw2 + kofs0);
+        }
         advance_b();
         cp_a = next_pos(cp_a);
         cp_b = next_pos(cp_b);
     }
-    // drain: the last look-ahead read and the extra copies
-    frags_ready<0>(fa);
+    // drain: the look-ahead reads and the extra copies (the LDS must be
+    // quiet before the workgroup ends)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3]),
+                 "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B0[0]), "+v"(B0[1]), "+v"(B0[2]), "+v"(B0[3]));
     wait_vmcnt<0>();
 
     if constexpr (kEpi != kEpiDz) {
+        // addresses formed anew (an opaque copy of the lane index): shared
+        // with the loads above, they would stay live across the K loop
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int col_e = lane_e & 15, grp_e = lane_e >> 4;
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
+        for (int bi = 0; bi < 8; ++bi) {
+            const int64_t row = mw + bi * 16 + col_e;
+            if (row >= p.m) continue;
+            float* crow = p.c + row * p.ldc;
 #pragma unroll
             for (int bj = 0; bj < 4; ++bj) {
-                const int64_t col = col_of(bj);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = row_of(bi, r);
-                    if (row < p.m && col < p.n) p.c[row * p.ldc + col] = acc[bi][bj][r];
-                }
+                const int64_t c0 = nw + bj * 16 + grp_e * 4;
+                if (c0 < p.n)
+                    *(float4*)(crow + c0) = make_float4(acc[bi][bj][0], acc[bi][bj][1],
+                                                        acc[bi][bj][2], acc[bi][bj][3]);
             }
+        }
     } else {
         // dz = g_t ([v == a_t] - exp(z - lse_t)) for v < V, t < N; 0 in the
         // padding (rows V..Vp-1, columns N..Np-1); an id outside [0, V)
-        // contributes nothing
+        // contributes nothing.  A lane holds dz[t][v0 .. v0 + 3] of each
+        // block: written to dz^T one element per row and to dz as one
+        // 8-byte store (v0 is a multiple of 4 and Vp of 64).
+        // Branch-free per element: rows past V of the tile hold finite
+        // logits of a clamped row, and their dz is selected away.
+        const int32_t vtrue = (int32_t)p.vtrue;
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
-            const int64_t t = col_of(bj);
-            if (t >= p.npad) continue;
+            const int64_t t = nw + bj * 16 + col;
             const bool tv = t < p.ntrue;
             const int64_t tc = tv ? t : 0;
             const float g = tv ? p.g[tc] : 0.f;
             const float l = tv ? p.lse[tc] : 0.f;
             const int32_t a = tv ? p.ids[tc] : -1;
-            const bool ok = tv && a >= 0 && (int64_t)a < p.vtrue && g != 0.f;
+            const bool ok = tv && a >= 0 && a < vtrue && g != 0.f;
+            const bool t_in = t < p.npad;
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+            for (int bi = 0; bi < 8; ++bi) {
+                const int32_t v0 = (int32_t)(mw + bi * 16 + grp * 4);   // < 2^31 (V < 2^31)
+                uint32_t q[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t v = row_of(bi, r);
-                    if (v >= p.vpad) continue;
-                    float dz = 0.f;
-                    if (ok && v < p.vtrue) {
-                        const float pz = fast_exp2((acc[bi][bj][r] - l) * kLog2e);
-                        dz = g * ((v == (int64_t)a ? 1.f : 0.f) - pz);
-                    }
-                    p.dzt[v * p.lddz + t] = bf16_rne(dz);
+                for (int i = 0; i < 4; ++i) {
+                    const int32_t v = v0 + i;
+                    const float pz = fast_exp2((acc[bi][bj][i] - l) * kLog2e);
+                    const float dz = g * ((v == a ? 1.f : 0.f) - pz);
+                    q[i] = (ok && v < vtrue) ? bf16_rne(dz) : 0u;
                 }
+                if (t_in && (int64_t)v0 < p.vpad) {
+                    if (p.dzt) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) p.dzt[(v0 + i) * p.lddz + t] = (uint16_t)q[i];
+                    }
+                    if (p.dz)
+                        *(uint2*)(p.dz + t * p.ldz + v0) = make_uint2(q[0] | (q[1] << 16),
+                                                                      q[2] | (q[3] << 16));
+                }
+            }
         }
     }
 }
@@ -559,12 +600,13 @@ static hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t ro
 static hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
     const int64_t grid = a.mtiles * a.ntiles;
     if (grid <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 block(2 * kThreads);
     if (epi == kEpiDz)
-        hipLaunchKernelGGL(gemm_nt_kernel<kEpiDz>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL(gemm8w_kernel<kEpiDz>, dim3((unsigned)grid), block, 0, st, a);
     else if (epi == kEpiStore)
-        hipLaunchKernelGGL(gemm_nt_kernel<kEpiStore>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL(gemm8w_kernel<kEpiStore>, dim3((unsigned)grid), block, 0, st, a);
     else
-        hipLaunchKernelGGL(gemm_nt_kernel<kEpiStoreAcc>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL(gemm8w_kernel<kEpiStoreAcc>, dim3((unsigned)grid), block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -579,7 +621,8 @@ hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t
     uint16_t* dz = (uint16_t*)(ws + p.dz_off);     // dz [Np][Vp]
     hipError_t e;
 
-    // 1. dz^T from the recomputed logits (A = W rows, B = h rows, K = D)
+    // 1. dz^T (for dW) and dz (for dh) from the recomputed logits (A = W
+    //    rows, B = h rows, K = D)
     GemmArgs z{};
     z.a = (const unsigned char*)w; z.lda_b = ldw * 2; z.m = p.v;
     z.b = (const unsigned char*)h; z.ldb_b = ldh * 2; z.n = p.n;
@@ -587,13 +630,13 @@ hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t
     z.mtiles = (p.vpad + kTileV - 1) / kTileV;
     z.ntiles = (p.npad + kTileT - 1) / kTileT;
     z.lse = lse; z.g = g; z.ids = ids; z.vtrue = p.v; z.ntrue = p.n;
-    z.dzt = dzt; z.lddz = p.npad; z.vpad = p.vpad; z.npad = p.npad;
+    z.dzt = dw ? dzt : nullptr; z.lddz = p.npad;
+    z.dz = dh ? dz : nullptr; z.ldz = p.vpad;
+    z.vpad = p.vpad; z.npad = p.npad;
     if ((e = launch_gemm(z, kEpiDz, st)) != hipSuccess) return e;
 
     if (dh) {
-        // 2. dz = (dz^T)^T and W^T, then dh = dz W (K = vocabulary)
-        if ((e = launch_transpose(dzt, p.npad, p.vpad, p.npad, dz, p.vpad, p.vpad, st)) != hipSuccess)
-            return e;
+        // 2. W^T, then dh = dz W (K = vocabulary)
         if ((e = launch_transpose((const uint16_t*)w, ldw, p.v, p.d, wt, p.vpad, p.vpad, st)) != hipSuccess)
             return e;
         GemmArgs a{};

@@ -666,17 +666,8 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         lds_read16<2 * 2048>(B[2], base);
         lds_read16<3 * 2048>(B[3], base);
     };
-    // The MFMAs are written as asm with the accumulator tied ("+a": the same
-    // AGPRs are source C and destination).  With the builtin, and every
-    // accumulator register taken, the register allocator picked untied forms
-    // and shuffled accumulators between registers inside the K loop.  The hazard recognizer does not see
-    // into asm, so the wait states it would insert around MFMAs are written
-    // out below: after zeroing the accumulators and before the epilogue
-    // reads them.
-    auto mfma = [&](int r, int bj, const u32x4& b) {
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-                     : "+a"(acc[r][bj]) : "v"(A[r]), "v"(b));
-    };
+    // tied-accumulator asm MFMAs (mfma_pipe.h)
+    auto mfma = [&](int r, int bj, const u32x4& b) { mfma16_tied(acc[r][bj], A[r], b); };
 
     // Ring positions as in lmhead_partials_kernel: (2 stage + op) % 5.
     int rd_h = 0, rd_w = 1;
@@ -705,8 +696,6 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // accumulator writes, then MFMAs that read them as source C
-        asm volatile("s_nop 4" ::: "memory");
 
         for (int kb = 0; kb < nk; ++kb) {
             const uint32_t aw = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
@@ -750,7 +739,10 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
             for (int r = 4; r < 8; ++r) {
                 wait16<11>(A[r]);
-                mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]); mfma(r, 3, B1[3]);
+                mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]);
+                if (r < 7) mfma(r, 3, B1[3]);
+                else mfma16_tied_last(acc[7][3], A[7], B1[3],   // + the epilogue's wait
+                                      __builtin_amdgcn_readfirstlane(kb == nk - 1));
                 read_a(r, aw2 + kofs0);
             }
             advance_h();
@@ -758,8 +750,6 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
             cp_h = next_pos(cp_h);
         }
 
-        // the last MFMAs' results, then accumulator reads: wait states
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
         // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
         // Per token column bj the lane's 32 rows (bi = 0..7, i = 0..3) are
         // folded as two 16-value groups (bi 0-3, then 4-7) into the running

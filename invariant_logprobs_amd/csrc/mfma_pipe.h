@@ -124,6 +124,36 @@ __device__ __forceinline__ void wait16_4(u32x4& a, u32x4 (&b)[4]) {
                  : "i"(N));
 }
 
+// 16x16x32 bf16 MFMA with the accumulator tied (the same AGPRs are source C
+// and destination).  With the builtin, and every accumulator register
+// taken, the register allocator picked untied forms and shuffled
+// accumulators between registers inside the K loops.  The hazard recognizer
+// does not look into asm: the kernels place these so that the wait states
+// it would insert are there anyway (the first MFMA of a tile follows its
+// accumulator writes by more than the two wait states a VALU write needs:
+// the loop opens with four LDS reads and a wait), and the stage's last MFMA
+// is mfma16_tied_last below.
+__device__ __forceinline__ void mfma16_tied(f32x4& acc, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// The same, followed when `last` (an SGPR value) is non-zero by 20 wait
+// states, more than the 19 that the longest case needs between an MFMA and a
+// read of its result: the last MFMA of a tile.  MFMAs complete in issue
+// order, so after it every accumulator may be read.  One asm statement:
+// nothing the compiler places after the loop (a copy, a spill) can come
+// between.  (A separate wait after the loop let such code in; peeling the
+// last stage, or a wait taking every accumulator as an operand, made the
+// register allocator copy accumulators inside the loop.)
+__device__ __forceinline__ void mfma16_tied_last(f32x4& acc, const u32x4& a, const u32x4& b,
+                                                 int last) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\t"
+                 "s_cmp_eq_u32 %3, 0\n\t"
+                 "s_cbranch_scc1 .Lmfma_no_wait%=\n\t"
+                 "s_nop 7\n\ts_nop 7\n\ts_nop 3\n"
+                 ".Lmfma_no_wait%=:"
+                 : "+a"(acc) : "v"(a), "v"(b), "s"(last) : "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -241,6 +241,7 @@ int tim_logprob_backward(const void* h, int64_t ldh, const void* w, int64_t ldw,
         return TIM_EINVAL;
     if (ldh < d || ldw < d) return TIM_EINVAL;
     if (dtype != TIM_BF16) return TIM_EUNSUPPORTED;
+    if ((dh && !aligned(dh, 16)) || (dw && !aligned(dw, 16))) return TIM_EUNSUPPORTED;
     if (n == 0 && !(dw && !(flags & TIM_BWD_ACCUMULATE_DW))) return TIM_OK;
     if (!w || (n > 0 && (!h || !ids || !lse || !grad_logp))) return TIM_EINVAL;
     if (d % 64 != 0) return TIM_EUNSUPPORTED;

@@ -181,6 +181,9 @@ def test_backward_and_ppo_argument_errors(lib):
     assert fwd(d=96, ldh=96, ldw=96) == tim.TIM_EUNSUPPORTED
     assert fwd(ws=None) == tim.TIM_EWORKSPACE
     assert fwd(ws=FAKE + 16) == tim.TIM_EUNSUPPORTED
+    assert fwd(dh=FAKE + 4) == tim.TIM_EUNSUPPORTED                 # 16-byte aligned outputs
+    assert fwd(dw=FAKE + 8) == tim.TIM_EUNSUPPORTED
+    assert fwd(n=0, dw=FAKE + 8) == tim.TIM_EUNSUPPORTED
     assert lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 1) == 0
     b = lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 0)
     # W^T, h^T and dz in both layouts, bf16, vocabulary padded to 151936 (a

@@ -151,6 +151,13 @@ def test_dw_accumulated_over_micro_batches_is_bitwise_one_batch():
                                  dw=dw, accumulate_dw=True)
     torch.cuda.synchronize()
     assert torch.equal(dw.view(torch.int32), dw_full.view(torch.int32))
+    # an output that is not 16-byte aligned is refused, and left untouched
+    buf = torch.zeros(v * d + 1, dtype=torch.float32, device=DEV)
+    dw_u = buf[1:].view(v, d)
+    with pytest.raises(tim.TimError):
+        tim.tim_logprob_backward(h, w, ids, lse, gr, want_dh=False, dw=dw_u)
+    torch.cuda.synchronize()
+    assert torch.all(buf == 0)
 
 
 # ---------------------------------------------------------------------------
