@@ -90,6 +90,33 @@ def test_backward_parity_ragged_sizes():
     assert torch.all(dh[17] == 0)
 
 
+@pytest.mark.parametrize("n,d,v", [(1, 64, 5), (3, 64, 257), (65, 128, 64), (256, 64, 1)])
+def test_backward_parity_edge_sizes(n, d, v):
+    # one token, a vocabulary smaller than one MFMA block, one K stage
+    # (D = 64), N just past a 64-token stage, V = 1 (p = 1: dz = 0)
+    h, w, ids, gr = _case(n, d, v, seed=n + v, zero_frac=0.0)
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    torch.cuda.synchronize()
+    dh_ref, dw_ref = oracle.logprob_backward(bf16_bits(h), bf16_bits(w), ids.cpu(), gr.cpu(),
+                                             dtype=oracle.BF16)
+    check_dh(dh.double().cpu().numpy(), dh_ref, gr, w, np.arange(n), f"n={n} d={d} v={v}")
+    dzabs = _dz_abs(h, w, ids, gr, np.arange(v))
+    check_dw(dw.double().cpu().numpy(), dw_ref, dzabs, h, gr, f"n={n} d={d} v={v}")
+    if v == 1:
+        assert torch.all(dh == 0) and torch.all(dw == 0)
+
+
+def test_backward_zero_gradient_gives_zeros():
+    n, d, v = 100, 128, 700
+    h, w, ids, _ = _case(n, d, v, seed=8)
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dw = torch.full((v, d), 7.0, device=DEV)
+    dh, _ = tim.tim_logprob_backward(h, w, ids, lse, torch.zeros(n, device=DEV), dw=dw)
+    torch.cuda.synchronize()
+    assert torch.all(dh == 0) and torch.all(dw == 0)
+
+
 def test_backward_full_size_sparse_gradient():
     # the Qwen3-8B-shaped head at its full size, with an upstream gradient on
     # 16 tokens so that the oracle computes only those rows
