@@ -31,16 +31,21 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "selected-token logprobs/s at D=4096,V=151936 (bf16) + MFMA util; batch-invariant"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_bf16_qwen3_8b_counters.json")
-LMHEAD_SRC = os.path.join(ROOT, "invariant_logprobs_amd", "csrc", "lmhead.hip")
+# the sources the head kernel is built from (its tiles, pipeline and chunking)
+LMHEAD_SRC = tuple(os.path.join(ROOT, "invariant_logprobs_amd", "csrc", f)
+                   for f in ("lmhead.hip", "mfma_pipe.h", "tim_internal.h"))
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(launch_unit):

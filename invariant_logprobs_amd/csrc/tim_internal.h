@@ -22,7 +22,7 @@ constexpr int kTileV = 256;
 constexpr int kTileT = 256;
 constexpr int kStageBytes = 128;   // bytes of K per row per pipeline stage
 constexpr int kThreads = 256;      // 4 waves of 64
-constexpr int kInvariantChunkTiles = 2;   // 512 vocabulary entries per chunk
+constexpr int kInvariantChunkTiles = 1;   // 256 vocabulary entries per chunk
 
 // Workspace layout of tim_logprob_forward (all offsets 256-byte aligned):
 //   [0, part_bytes)           float2 partials[nchunks][n]: (max, sum-exp)

@@ -41,10 +41,10 @@ def test_status_strings(lib):
 
 
 def test_logprob_workspace_layout(lib):
-    # invariant schedule: 512-entry vocabulary chunks, (max, sum) fp32 pairs
+    # invariant schedule: 256-entry vocabulary chunks, (max, sum) fp32 pairs
     n, d, v = 8192, 4096, 151936
-    chunks = -(-v // 512)
-    assert chunks == 297
+    chunks = -(-v // 256)
+    assert chunks == 594
     want = -(-(chunks * n * 8) // 256) * 256 + -(-(n * 4) // 256) * 256
     assert lib.tim_logprob_workspace_bytes(n, d, v, tim.TIM_BF16, tim.TIM_SCHED_INVARIANT) == want
     # the invariant layout does not depend on dtype; it scales with n only linearly
@@ -211,7 +211,7 @@ def _fp(temperature=1.0, gamma=None, eps=1e-6):
 
 def test_forward_ex_workspace_layout(lib):
     n, d, v = 8192, 4096, 151936
-    chunks = -(-v // 512)
+    chunks = -(-v // 256)
     up = lambda x: -(-x // 256) * 256
     plain = up(chunks * n * 8) + up(n * 4)
     ws = lambda **kw: lib.tim_logprob_ex_workspace_bytes(
