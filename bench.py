@@ -210,6 +210,7 @@ def main():
         out["extras"] = extras_measure(tim, workloads, wl, torch, np, args.stats_log2)
         out["stats_scale"] = stats_scale(tim, workloads, torch, np, args.stats_log2)
         out["invariance_cost"] = invariance_cost(tim, wl, torch, np)
+        out["dsv3"] = dsv3_measure(tim, workloads, torch, np)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, np, args.cpu_rows)
@@ -380,6 +381,36 @@ def extras_scale(tim, workloads, torch, np, log2n, tok_tau):
     return {"tokens": n, "ms": ms, "algorithmic_bytes": algo, "achieved_GBs": gbs,
             "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS, "ratio_q": list(XQ_RATIO),
             "abs_q": list(XQ_ABS), "tok_tau": tok_tau}
+
+
+def dsv3_measure(tim, workloads, torch, np):
+    """The largest configuration, a DeepSeek-V3-shaped head (N = 32768 in 64
+    log-normal sequences, D = 7168, V = 129280, bf16): forward (logits,
+    log-sum-exp, gather, merge) and the mismatch statistics, each timed
+    alone, median of 5 calls."""
+    wl = workloads.make("dsv3", device="cuda")
+    sp = wl.spec
+    n, d, v = sp.n, sp.d, sp.v
+    lt = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws_lp = torch.empty(tim.logprob_workspace_bytes(n, d, v, tim.TIM_BF16), dtype=torch.uint8,
+                        device="cuda")
+    ws_st = torch.empty(max(1, tim.stats_workspace_bytes(n, sp.n_seqs)), dtype=torch.uint8,
+                        device="cuda")
+    fwd = lambda: tim.tim_logprob_forward(wl.h, wl.w, wl.ids, out=lt, workspace=ws_lp)
+    ms = time_calls(fwd, torch, np, reps=5, warm=1)
+    st = lambda: tim.tim_mismatch_stats(lt, wl.logp_rollout, wl.mask, wl.cu_seqlens,
+                                        tis_clip=sp.clip_c, seq_bounds=(sp.seq_lo, sp.seq_hi),
+                                        workspace=ws_st)
+    ms_st = time_calls(st, torch, np, reps=5, warm=1)
+    flops = 2.0 * n * d * v
+    tf = flops / (ms / 1e3) / 1e12
+    log(f"dsv3 forward: {ms:.3f} ms, {tf:.1f} TFLOP/s ({tf / PEAK_BF16_TFLOPS:.1%} of bf16 peak); "
+        f"stats {ms_st * 1e3:.1f} us")
+    del wl, ws_lp, ws_st, lt
+    torch.cuda.empty_cache()
+    return {"workload": sp.desc, "forward_ms": ms, "stats_us": ms_st * 1e3,
+            "tokens_per_s": n / ((ms + ms_st) / 1e3), "flops": flops, "achieved_TFLOPs": tf,
+            "peak_TFLOPs": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
 
 
 def backward_measure(tim, wl, torch, np, reps=5):
