@@ -103,8 +103,8 @@ __device__ __forceinline__ void tile_of_block(int64_t nchunks, int64_t nttiles,
     ttile = within / gm;
 }
 
-// kEnt: also carry u (entropy).  c2 = log2(e) / tau.
-template <bool kBf16, bool kEnt>
+// fp32 inputs.  kEnt: also carry u (entropy).  c2 = log2(e) / tau.
+template <bool kEnt>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
@@ -188,13 +188,12 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 
     // per-lane LDS byte offset of k-step ks inside an operand tile: row lrow
     // of each 32-row block (the swizzle does not depend on the block), logical
-    // chunk ks*2 + lhalf (bf16) or lhalf*4 + ks (fp32)
+    // chunk lhalf*4 + ks
     const uint32_t lds_base = lds_addr(lds);
     uint32_t kofs[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const int c = kBf16 ? ks * 2 + lhalf : lhalf * 4 + ks;
-        kofs[ks] = (uint32_t)swz(lrow, c);
+        kofs[ks] = (uint32_t)swz(lrow, lhalf * 4 + ks);
     }
 
     // Copy iterators: W of stage st + 1 and h of stage st + 2 are copied
@@ -239,33 +238,22 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                        lds_base + (uint32_t)(ph * kOperandBytes) + kofs[ks] + (uint32_t)(wt * 128 * kStageBytes));
     };
     auto mfma_step = [&](const u32x4 (&f)[8]) {
-        if constexpr (kBf16) {
-            // lanes 0-31 supply K 0-7 of the 16-K step, lanes 32-63 K 8-15
+        // 32 fp32 of K per stage: lane half g supplies K = 16 g + 4 ks + e
+        // to MFMA (ks, e); each 32x32x2 instruction consumes one K of each
+        // half.  Whole vectors are cast before indexing: casting single
+        // elements of the asm outputs made this compiler pass element 0
+        // for every e.
+        f32x4 ff[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ff[i] = __builtin_bit_cast(f32x4, f[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, f[bi]), __builtin_bit_cast(bf16x8, f[4 + bj]),
-                        acc[bi][bj], 0, 0, 0);
-        } else {
-            // 32 fp32 of K per stage: lane half g supplies K = 16 g + 4 ks + e
-            // to MFMA (ks, e); each 32x32x2 instruction consumes one K of each
-            // half.  Whole vectors are cast before indexing: casting single
-            // elements of the asm outputs made this compiler pass element 0
-            // for every e.
-            f32x4 ff[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ff[i] = __builtin_bit_cast(f32x4, f[i]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < 4; ++bj)
-                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            ff[bi][e], ff[4 + bj][e], acc[bi][bj], 0, 0, 0);
-        }
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        ff[bi][e], ff[4 + bj][e], acc[bi][bj], 0, 0, 0);
     };
 
     // Pipeline.  The ring holds operand tiles at positions (2 stage + op) % 5
@@ -1035,8 +1023,8 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
         if (p.entropy) go8(lmhead8w_kernel<true>);
         else go8(lmhead8w_kernel<false>);
     } else {
-        if (p.entropy) go(lmhead_partials_kernel<false, true>);
-        else go(lmhead_partials_kernel<false, false>);
+        if (p.entropy) go(lmhead_partials_kernel<true>);
+        else go(lmhead_partials_kernel<false>);
     }
     return hipGetLastError();
 }

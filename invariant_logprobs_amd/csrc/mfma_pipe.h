@@ -2,8 +2,9 @@
 // (lmhead.hip, bwd.hip): operand types, the LDS ring geometry and swizzle,
 // the buffer-to-LDS copy, the fragment reads and the wait helpers.  A tile
 // kernel stages 256-row operand tiles of 128 bytes of K per pipeline stage
-// through a five-position LDS ring and feeds 32x32x16 bf16 (or 32x32x2 fp32)
-// MFMAs from it.
+// through a five-position LDS ring and feeds MFMAs from it: 16x16x32 bf16 in
+// the eight-wave kernels (the head's bf16 path, the backward's GEMMs),
+// 32x32x2 fp32 in the head's four-wave fp32 kernel.
 #pragma once
 
 #include "tim_internal.h"
