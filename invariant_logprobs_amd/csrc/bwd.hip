@@ -47,27 +47,42 @@ using namespace mfma;
 
 constexpr int kTrTile = 64;
 constexpr int kTrThreads = 256;
+constexpr int kTrPitch = kTrTile + 8;   // LDS row pitch in elements: rows stay 16-byte aligned
 
 // out[c][r] = in[r][c] for r < rows, c < cols; out[c][r] = 0 for
-// rows <= r < out_cols.  Grid: (ceil(out_cols / 64), ceil(cols / 64)).
+// rows <= r < out_cols.  Grid: (out_cols / 64, ceil(cols / 64)).  Every
+// global access moves 16 bytes: a thread loads 8 consecutive elements of an
+// input row into the LDS tile, then gathers 8 consecutive rows of one tile
+// column and stores them as 8 consecutive elements of an output row.
+// Requires cols % 8 == 0, out_cols % 64 == 0, in, out, ld_in and ld_out
+// 16-byte aligned (in elements: multiples of 8), which the backward's
+// operands meet (D % 64 == 0, 16-byte aligned rows, padded sizes).
 __global__ void __launch_bounds__(kTrThreads)
 transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t rows, int64_t cols,
                       uint16_t* __restrict__ out, int64_t ld_out, int64_t out_cols) {
-    __shared__ uint16_t tile[kTrTile][kTrTile + 2];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kTrTile][kTrPitch];
     const int64_t r0 = (int64_t)blockIdx.x * kTrTile, c0 = (int64_t)blockIdx.y * kTrTile;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;       // 64 x 4
+    const int g = threadIdx.x & 7;          // 8-element group
+    const int q = threadIdx.x >> 3;         // 0..31
 #pragma unroll
-    for (int k = 0; k < kTrTile / 4; ++k) {
-        const int lr = ty + 4 * k;
-        const int64_t r = r0 + lr, c = c0 + tx;
-        tile[lr][tx] = (r < rows && c < cols) ? in[r * ld_in + c] : (uint16_t)0;
+    for (int k = 0; k < kTrTile / 32; ++k) {
+        const int lr = q + 32 * k;
+        const int64_t r = r0 + lr, c = c0 + g * 8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < rows && c < cols) v = *(const uint4*)(in + r * ld_in + c);
+        *(uint4*)&tile[lr][g * 8] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kTrTile / 4; ++k) {
-        const int lc = ty + 4 * k;
-        const int64_t c = c0 + lc, r = r0 + tx;
-        if (c < cols && r < out_cols) out[c * ld_out + r] = tile[tx][lc];
+    for (int k = 0; k < kTrTile / 32; ++k) {
+        const int lc = q + 32 * k;                 // tile column = output row
+        const int64_t c = c0 + lc, r = r0 + g * 8; // output row, first output column
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = tile[g * 8 + j][lc];
+        if (c < cols && r < out_cols)
+            *(uint4*)(out + c * ld_out + r) = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
+                                                         e[4] | (e[5] << 16), e[6] | (e[7] << 16));
     }
 }
 
@@ -592,6 +607,9 @@ static hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t ro
                                    hipStream_t st) {
     const int64_t gx = (out_cols + kTrTile - 1) / kTrTile, gy = (cols + kTrTile - 1) / kTrTile;
     if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
+    if (cols % 8 != 0 || out_cols % kTrTile != 0 || ld_in % 8 != 0 || ld_out % 8 != 0 ||
+        (uintptr_t)in % 16 != 0 || (uintptr_t)out % 16 != 0)
+        return hipErrorInvalidValue;                   // the kernel's 16-byte accesses
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kTrThreads),
                        0, st, in, ld_in, rows, cols, out, ld_out, out_cols);
     return hipGetLastError();
