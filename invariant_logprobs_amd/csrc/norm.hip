@@ -192,6 +192,59 @@ rmsnorm_wave_kernel(const void* __restrict__ x, int64_t ldx, const void* __restr
     }
 }
 
+// The same for rows of at most 64 kPer groups: a lane keeps its groups
+// l, l + 64, ... in registers, so all of them are in flight at once and x is
+// read once.  Same fold order as above (ascending groups, a column at a
+// time, then the butterfly), so the same bits.
+template <bool kBf16, bool kVec, int kPer>
+__global__ void __launch_bounds__(kNormThreads)
+rmsnorm_reg_kernel(const void* __restrict__ x, int64_t ldx, const void* __restrict__ gamma,
+                   int64_t n, int64_t d, double eps, void* __restrict__ y, int64_t ldy,
+                   float* __restrict__ rstd_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kNormWaves + (threadIdx.x >> 6);
+    if (t >= n) return;                                  // whole wave leaves together
+    const int64_t groups = (d + 7) / 8;
+    Group<kBf16> xg[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t g = lane + 64 * i;
+        if (g < groups) load_group<kBf16, kVec>(x, t * ldx, g * 8, d, xg[i]);
+        else xg[i] = Group<kBf16>{};
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        double v[8];
+        unpack<kBf16>(xg[i], v);               // groups past the row are zeros: exact no-ops
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fma(v[j], v[j], ss);
+    }
+    // keep the raw groups, not their fp64 unpacking, alive for the second
+    // pass (the unpacking is cheap; holding it would cost 4x the registers)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+#pragma unroll
+        for (int k = 0; k < (kBf16 ? 1 : 2); ++k)
+            asm volatile("" : "+v"(xg[i].q[k].x), "+v"(xg[i].q[k].y), "+v"(xg[i].q[k].z),
+                              "+v"(xg[i].q[k].w));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off);
+    const double r = 1.0 / sqrt(ss / (double)d + eps);
+    if (rstd_out && lane == 0) rstd_out[t] = (float)r;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t g = lane + 64 * i;
+        if (g >= groups) break;
+        Group<kBf16> gg;
+        load_group<kBf16, kVec>(gamma, 0, g * 8, d, gg);
+        double v[8], gm[8];
+        unpack<kBf16>(xg[i], v);
+        unpack<kBf16>(gg, gm);
+        store_group<kBf16, kVec>(v, gm, r, y, t * ldy, g * 8, d);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, int64_t n, int64_t d,
@@ -208,12 +261,26 @@ hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, int64_t
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNormThreads), 0, st, x, ldx, gamma,
                            n, d, eps, y, ldy, rstd);
     };
+    const int64_t groups = (d + 7) / 8;
     if (dtype == 0) {
-        if (vec) go(rmsnorm_wave_kernel<true, true>);
-        else go(rmsnorm_wave_kernel<true, false>);
+        if (groups <= 64 * 8) {              // D <= 4096: 32 registers of row per lane
+            if (vec) go(rmsnorm_reg_kernel<true, true, 8>);
+            else go(rmsnorm_reg_kernel<true, false, 8>);
+        } else if (groups <= 64 * 16) {      // D <= 8192
+            if (vec) go(rmsnorm_reg_kernel<true, true, 16>);
+            else go(rmsnorm_reg_kernel<true, false, 16>);
+        } else {
+            if (vec) go(rmsnorm_wave_kernel<true, true>);
+            else go(rmsnorm_wave_kernel<true, false>);
+        }
     } else {
-        if (vec) go(rmsnorm_wave_kernel<false, true>);
-        else go(rmsnorm_wave_kernel<false, false>);
+        if (groups <= 64 * 8) {              // D <= 4096: 64 registers of row per lane
+            if (vec) go(rmsnorm_reg_kernel<false, true, 8>);
+            else go(rmsnorm_reg_kernel<false, false, 8>);
+        } else {
+            if (vec) go(rmsnorm_wave_kernel<false, true>);
+            else go(rmsnorm_wave_kernel<false, false>);
+        }
     }
     return hipGetLastError();
 }
