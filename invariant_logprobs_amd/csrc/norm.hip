@@ -12,8 +12,9 @@
 // rounded once to the output type (bf16: nearest, ties to even), so the
 // only rounding between the definition and the stored value is that last
 // one.  Work per element: one fp64 fold, two fp64 products, one conversion
-// and three integer steps for the rounding; x is read twice (the second
-// time mostly from cache) and y written once.
+// and three integer steps for the rounding.  Rows of up to 4096 elements
+// (8192 in bf16) are held in registers and read once; wider rows are read
+// twice (the second time mostly from cache).  y is written once.
 
 #include "tim_internal.h"
 
