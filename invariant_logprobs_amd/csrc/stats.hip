@@ -426,13 +426,16 @@ __device__ __forceinline__ double bfly_max(double x) {
 }
 
 // Descriptors per wave: enough waves to cover the chip several times over at
-// any size (a wave's descriptors are folded one after another), at most
-// kMaxSubPerWave.  Which wave folds a sub-chunk never changes its result.
+// any size (a wave's descriptors are folded one after another, its pieces
+// streamed through one pipeline), at most kMaxSubPerWave: with many short
+// sequences the longer per-wave stream hides the pipeline's start (at 2^28
+// tokens in log-normal sequences, 16 per wave instead of 4 is ~7 % faster).
+// Which wave folds a sub-chunk never changes its result.
 inline uint32_t subs_per_wave(int64_t tmax) {
     constexpr int64_t kTargetWaves = 16384;
     int64_t k = (tmax + kTargetWaves - 1) / kTargetWaves;
     if (k < 1) k = 1;
-    if (k > 4) k = 4;
+    if (k > kMaxSubPerWave) k = kMaxSubPerWave;
     return (uint32_t)k;
 }
 
