@@ -77,7 +77,15 @@ def check_norm(x, g, y_gpu, rstd_gpu, label):
                                            (300, 4096, torch.bfloat16, 4096),
                                            (64, 4096, torch.bfloat16, 4160),
                                            (50, 1000, torch.float32, 1000),
-                                           (129, 7168, torch.float32, 7168)])
+                                           (129, 7168, torch.float32, 7168),
+                                           # register-resident rows: the limits of
+                                           # each variant and the next width past them
+                                           (40, 4096, torch.float32, 4096),
+                                           (21, 4104, torch.float32, 4104),
+                                           (33, 7168, torch.bfloat16, 7168),
+                                           (20, 8192, torch.bfloat16, 8192),
+                                           (17, 8200, torch.bfloat16, 8200),
+                                           (9, 4100, torch.bfloat16, 4100)])
 def test_rmsnorm_parity(n, d, dtype, ldx):
     x_full, g = workloads.pre_norm(n, ldx, seed=n + d, dtype=dtype, device=DEV)
     x = x_full[:, :d]
