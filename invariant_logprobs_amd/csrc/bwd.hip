@@ -273,6 +273,22 @@ gemm8w_kernel(GemmArgs p) {
         else mfma16_tied_last(acc[7][3], A[7], b, last);
     };
 
+    // kEpiDz: the per-token inputs of the epilogue, loaded before the K loop
+    // so that their latency is hidden behind it
+    float tok_g[4], tok_l[4];
+    int32_t tok_a[4];
+    if constexpr (kEpi == kEpiDz) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t t = nw + bj * 16 + col;
+            const bool tv = t < p.ntrue;
+            const int64_t tc = tv ? t : 0;
+            tok_g[bj] = tv ? p.g[tc] : 0.f;
+            tok_l[bj] = tv ? p.lse[tc] : 0.f;
+            tok_a[bj] = tv ? p.ids[tc] : -1;
+        }
+    }
+
     // Ring positions (2 stage + op) % 5, op 0: B, op 1: A.  LDS reads of a
     // wave complete in order; the waits count the reads issued after the
     // one a row needs: 11 for every ks0 row, 7 - r for ks1 rows 0-3.
@@ -387,10 +403,8 @@ gemm8w_kernel(GemmArgs p) {
         for (int bj = 0; bj < 4; ++bj) {
             const int64_t t = nw + bj * 16 + col;
             const bool tv = t < p.ntrue;
-            const int64_t tc = tv ? t : 0;
-            const float g = tv ? p.g[tc] : 0.f;
-            const float l = tv ? p.lse[tc] : 0.f;
-            const int32_t a = tv ? p.ids[tc] : -1;
+            const float g = tok_g[bj], l = tok_l[bj];
+            const int32_t a = tok_a[bj];
             const bool ok = tv && a >= 0 && a < vtrue && g != 0.f;
             const bool t_in = t < p.npad;
 #pragma unroll
