@@ -500,20 +500,138 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     }
 }
 
-// bf16 partials: 16x16x32 MFMAs, eight waves, two per SIMD.
+// ---------------------------------------------------------------------------
+// bf16: 16x16x32 MFMAs.  A wave holds 128 vocabulary rows (8 blocks of 16)
+// by NB token blocks of 16 as acc[bi][bj] (rows bi * 16 + .., tokens
+// bj * 16 + ..).  A fragment (16 rows x 32 K): lane l holds row l & 15, K
+// 8 (l >> 4) .. + 7; an output block: lane l holds rows 4 (l >> 4) + i of
+// column l & 15.  The helpers below are the epilogue every bf16 kernel runs
+// on such a wave tile, so that a logit's fold does not depend on which
+// kernel (which token-tile width) computed it.
+
+// Fold the wave tile's logits into the running per-token state.  Per token
+// column bj the lane's 32 rows (bi = 0..7, i = 0..3) are folded as four
+// groups of 8 (blocks 2p, 2p + 1) in ascending p; inside a group the block
+// maximum first, then the 8 exponentials summed by a fixed pairwise tree.
+// Rows with offset bi * 16 + i >= lim (past V, last tile only) are -inf.
+template <bool kEnt, bool kMasked, int NB>
+__device__ __forceinline__ void fold16(const f32x4 (&acc)[8][NB], int lim, float c2,
+                                       float (&m_run)[NB], float (&s_run)[NB],
+                                       float (&u_run)[NB]) {
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {      // bi = 2 part, 2 part + 1
+            float z[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int bi = part * 2 + (q >> 2), i = q & 3;
+                z[q] = acc[bi][bj][i];
+                if constexpr (kMasked) z[q] = bi * 16 + i < lim ? z[q] : -INFINITY;
+            }
+            float bmax = z[0];
+#pragma unroll
+            for (int q = 1; q < 8; ++q) bmax = fmaxf(bmax, z[q]);
+            const float m_new = fmaxf(m_run[bj], bmax);
+            // exponents as (z - m) c2: exactly 0 for the maximum, so its
+            // term is exactly 1 (a V = 1 row gets logp = 0 exactly)
+            const float mref = m_new == -INFINITY ? 0.f : m_new;
+            const float dsh = (m_run[bj] - mref) * c2;
+            const float scale = m_run[bj] == m_new ? 1.f : fast_exp2(dsh);
+            float e[8];
+            if constexpr (kEnt) {
+                float ea[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float a = fmaxf((z[q] - mref) * c2, kArgFloor);
+                    e[q] = fast_exp2(a);
+                    ea[q] = e[q] * a;
+                }
+#pragma unroll
+                for (int width = 4; width >= 1; width >>= 1)
+#pragma unroll
+                    for (int q = 0; q < width; ++q) ea[q] = ea[q] + ea[q + width];
+                const float uo = m_run[bj] == m_new
+                                     ? u_run[bj]
+                                     : (s_run[bj] > 0.f ? scale * fmaf(dsh, s_run[bj], u_run[bj])
+                                                        : 0.f);
+                u_run[bj] = uo + ea[0];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e[q] = fast_exp2((z[q] - mref) * c2);
+            }
+#pragma unroll
+            for (int width = 4; width >= 1; width >>= 1)
+#pragma unroll
+                for (int q = 0; q < width; ++q) e[q] = e[q] + e[q + width];
+            s_run[bj] = fmaf(s_run[bj], scale, e[0]);
+            m_run[bj] = m_new;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Gather: the lane whose row set holds id my_id[bj] (relative row
+// rel = id - vbase_w in [0, 128), row group (rel & 15) >> 2 == grp) keeps
+// z[t, id] in zsel_reg[bj] and returns its index there (else -1).  Exactly
+// one lane of the grid holds each token's selected logit.
+template <int NB>
+__device__ __forceinline__ void gather16(const f32x4 (&acc)[8][NB], const int32_t (&my_id)[NB],
+                                         int64_t vbase_w, int grp, float (&zsel_reg)[NB],
+                                         int (&tgt)[NB]) {
+    bool any_tgt = false;
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+        const int64_t rel = (int64_t)my_id[bj] - vbase_w;
+        const bool mine = rel >= 0 && rel < 128 && (int)((rel & 15) >> 2) == grp;
+        tgt[bj] = mine ? (int)((rel >> 4) * 4 + (rel & 3)) : -1;
+        any_tgt |= mine;
+    }
+    if (any_tgt) {
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) {
+#pragma unroll
+            for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    zsel_reg[bj] = tgt[bj] == bi * 4 + i ? acc[bi][bj][i] : zsel_reg[bj];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The wave's four row groups of each token column, merged: xor 16, then 32.
+template <bool kEnt, int NB>
+__device__ __forceinline__ void merge_row_groups(float (&m_run)[NB], float (&s_run)[NB],
+                                                 float (&u_run)[NB], float c2) {
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+#pragma unroll
+        for (int sh = 16; sh <= 32; sh <<= 1) {
+            const float mo = __shfl_xor(m_run[bj], sh);
+            const float so = __shfl_xor(s_run[bj], sh);
+            if constexpr (kEnt) {
+                const float uo = __shfl_xor(u_run[bj], sh);
+                lse_combine3(m_run[bj], s_run[bj], u_run[bj], mo, so, uo, c2);
+            } else {
+                lse_combine(m_run[bj], s_run[bj], mo, so, c2);
+            }
+        }
+    }
+}
+
+// bf16 partials: one 256-vocabulary x 256-token tile per workgroup, eight
+// waves, two per SIMD.
 //
-// Same tiles, vocabulary chunks, LDS ring, copies and chunk-merge order as
-// lmhead_partials_kernel (which serves fp32).  On this chip a 16x16x32 bf16
-// MFMA stream sustains 2.08 PFLOP/s against 1.75 for 32x32x16; and with two
-// waves per SIMD one wave's MFMAs keep the matrix unit busy while the other
-// waits on the issue of its buffer-to-LDS copies or at a barrier.  The
-// workgroup has 8 waves: wave w owns vocabulary rows (w & 1) * 128 .. + 127
-// and tokens (w >> 1) * 64 .. + 63 of the tile, as 8 x 4 MFMA blocks of
-// 16 x 16 (acc[bi][bj]: rows bi * 16 + .., tokens bj * 16 + ..; 128
-// accumulator registers, so two waves fit a SIMD).  A fragment (16 rows x
-// 32 K): lane l holds row l & 15, K 8 (l >> 4) .. + 7; an output block: lane
-// l holds rows 4 (l >> 4) + i of column l & 15.  A stage (128 bytes of K) is
-// two k-steps; each wave copies 4 units of W and 4 of h (1 KiB each) per
+// Same tiles, vocabulary chunks (one tile each), LDS ring, copies and
+// chunk-merge order as lmhead_partials_kernel (which serves fp32).  On this
+// chip a 16x16x32 bf16 MFMA stream sustains 2.08 PFLOP/s against 1.75 for
+// 32x32x16; and with two waves per SIMD one wave's MFMAs keep the matrix
+// unit busy while the other waits on the issue of its buffer-to-LDS copies
+// or at a barrier.  Wave w owns vocabulary rows (w & 1) * 128 .. + 127 and
+// tokens (w >> 1) * 64 .. + 63 of the tile as 8 x 4 MFMA blocks (128
+// accumulator registers, so two waves fit a SIMD).  A stage (128 bytes of K)
+// is two k-steps; each wave copies 4 units of W and 4 of h (1 KiB each) per
 // stage.
 //
 // Fragment registers: A[8] (one per row block), B0[4] and B1[4] (the column
@@ -526,17 +644,20 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 //        stage ks0 row r.
 // LDS reads of a wave complete in order; counting the reads issued after
 // the one a row needs gives the waits: 11 for every ks0 row, 7 - r for ks1
-// rows 0-3 (ks1 rows 4-7 need nothing new).
+// rows 0-3 (ks1 rows 4-7 need nothing new).  Past the last stage the copies
+// wrap to K offset 0 and the reads continue into positions never used: every
+// stage issues the same instructions, so the counts hold everywhere.  The
+// look-ahead reads of the last stage are waited for right after the K loop,
+// so that none of the fragment registers is live in the epilogue.
 template <bool kEnt>
 __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                 const unsigned char* __restrict__ w, int64_t ldw_b,
                 const int32_t* __restrict__ ids, int64_t n, int64_t v,
-                int nk, int chunk_tiles, int64_t nvtiles, int64_t nchunks,
-                int64_t nttiles, float c2, float2* __restrict__ part,
-                float* __restrict__ upart, float* __restrict__ zsel,
-                int32_t* __restrict__ n_bad_ids) {
+                int nk, int64_t nchunks, int64_t nttiles, float c2,
+                float2* __restrict__ part, float* __restrict__ upart,
+                float* __restrict__ zsel, int32_t* __restrict__ n_bad_ids) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -552,59 +673,30 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     int64_t chunk, ttile;
     tile_of_block(nchunks, nttiles, chunk, ttile);
     const int64_t t0 = ttile * kTileT;
-    const int64_t vt_first = chunk * chunk_tiles;
-    const int ntiles_here = (int)((nvtiles - vt_first) < chunk_tiles ? (nvtiles - vt_first)
-                                                                      : chunk_tiles);
-
-    // the 4 tokens of this lane (one per 16-column block) and their ids
-    int32_t my_id[4];
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-        const int64_t t = t0 + wt * 64 + bj * 16 + col;
-        my_id[bj] = t < n ? ids[t] : -1;
-    }
-
-    f32x4 acc[8][4];
-    float m_run[4], s_run[4], u_run[4];
-    float zsel_reg[4];
-    bool have_zsel = false;
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-        m_run[bj] = -INFINITY; s_run[bj] = 0.f; u_run[bj] = 0.f; zsel_reg[bj] = 0.f;
-    }
+    const int64_t vbase = chunk * kTileV;
 
     // Copies: as in lmhead_partials_kernel, with eight waves: 8-row blocks
     // 4 wave .. 4 wave + 3 of both operands, swizzled chunks, rows past N or
-    // V redirected to the last valid row.
-    uint32_t hoff[4], wrow_off[4], wtail_off[4];
-    int drow[4];
+    // V redirected to the last valid row.  Every access lies inside the
+    // tensors and inside the descriptor's extent.
+    uint32_t hoff[4], woff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        drow[j] = (wave * 4 + j) * 8 + (lane >> 3);
-        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((drow[j] >> 1) & 7)) * 16);
-        int64_t t = t0 + drow[j];
-        if (t > n - 1) t = n - 1;
+        const int drow = (wave * 4 + j) * 8 + (lane >> 3);
+        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((drow >> 1) & 7)) * 16);
+        const int64_t t = t0 + drow < n ? t0 + drow : n - 1;
+        const int64_t r = vbase + drow < v ? vbase + drow : v - 1;
         hoff[j] = (uint32_t)((t - t0) * ldh_b) + cb;
-        wrow_off[j] = (uint32_t)(drow[j] * ldw_b) + cb;
-        wtail_off[j] = cb;
+        woff[j] = (uint32_t)((r - vbase) * ldw_b) + cb;
     }
-    const unsigned char* hbase = h + t0 * ldh_b;
     const int64_t hrows = (n - t0) < kTileT ? (n - t0) : kTileT;
+    const int64_t wrows = (v - vbase) < kTileV ? (v - vbase) : kTileV;
     const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)hbase, (short)0, (int)((hrows - 1) * ldh_b + (int64_t)nk * kStageBytes), kRsrcWord3);
-    uint32_t woff[4];
-    __amdgpu_buffer_rsrc_t wrs = hrs;
-    auto set_wtile = [&](int vt_l) {
-        const int64_t vbase = (vt_first + vt_l) * kTileV;
-        const unsigned char* wbase = w + vbase * ldw_b;
-        const int64_t wrows = (v - vbase) < kTileV ? (v - vbase) : kTileV;
-        wrs = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0,
-                                                (int)((wrows - 1) * ldw_b + (int64_t)nk * kStageBytes), kRsrcWord3);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            woff[j] = vbase + drow[j] < v ? wrow_off[j]
-                                          : (uint32_t)((v - 1 - vbase) * ldw_b) + wtail_off[j];
-    };
+        (void*)(h + t0 * ldh_b), (short)0,
+        (int)((hrows - 1) * ldh_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w + vbase * ldw_b), (short)0,
+        (int)((wrows - 1) * ldw_b + (int64_t)nk * kStageBytes), kRsrcWord3);
 
     // fragment addresses: row col of a 16-row block, logical chunk ks*4 + grp
     const uint32_t lds_base = lds_addr(lds);
@@ -613,8 +705,7 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     const uint32_t a_half = (uint32_t)(wv * 128 * kStageBytes);   // this wave's W rows
     const uint32_t b_half = (uint32_t)(wt * 64 * kStageBytes);    // this wave's h rows
 
-    int w_kb = 0, w_vt = 0, h_kb = 0;
-    set_wtile(0);
+    int w_kb = 0, h_kb = 0;
     auto copy_w = [&](int j, int pos) {
         dma16_buf(wrs, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, woff[j],
                   (uint32_t)(w_kb * kStageBytes));
@@ -623,17 +714,11 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         dma16_buf(hrs, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, hoff[j],
                   (uint32_t)(h_kb * kStageBytes));
     };
-    auto advance_w = [&]() {
-        if (++w_kb == nk) {
-            w_kb = 0;
-            if (++w_vt < ntiles_here) set_wtile(w_vt);
-        }
-    };
-    auto advance_h = [&]() {
-        if (++h_kb == nk) h_kb = 0;
-    };
+    auto advance_w = [&]() { if (++w_kb == nk) w_kb = 0; };
+    auto advance_h = [&]() { if (++h_kb == nk) h_kb = 0; };
     auto next_pos = [](int p) { return p + 2 >= kPos ? p + 2 - kPos : p + 2; };
 
+    f32x4 acc[8][4];
     u32x4 A[8], B0[4], B1[4];
     // reads of one k-step's fragments (block offsets as immediates)
     auto read_a = [&](int r, uint32_t base) {
@@ -669,6 +754,10 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
     for (int j = 0; j < 4; ++j) copy_h(j, 2);
     advance_h();
+#pragma unroll
+    for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
     wait_vmcnt<4>();
     __syncthreads();
     {
@@ -679,187 +768,101 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         for (int r = 0; r < 8; ++r) read_a(r, aw + kofs0);
     }
 
-    for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
+    for (int kb = 0; kb < nk; ++kb) {
+        const uint32_t aw = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
+        const uint32_t bh = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
+        // ---- ks0: W(s+1) copies at rows 0-3
+        read_b(B1, bh + kofs1);
 #pragma unroll
-        for (int bi = 0; bi < 8; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int kb = 0; kb < nk; ++kb) {
-            const uint32_t aw = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
-            const uint32_t bh = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
-            // ---- ks0: W(s+1) copies at rows 0-3
-            read_b(B1, bh + kofs1);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                if (r == 0) wait16_4<11>(A[0], B0);
-                else wait16<11>(A[r]);
-                mfma(r, 0, B0[0]); mfma(r, 1, B0[1]);
-                if (r < 4) copy_w(r, cp_w);
-                mfma(r, 2, B0[2]); mfma(r, 3, B0[3]);
-                read_a(r, aw + kofs1);
-            }
-            advance_w();
-            // ---- ks1, rows 0-3: h(s+2) copies
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (r == 0) wait16_4<7>(A[0], B1);
-                else if (r == 1) wait16<6>(A[1]);
-                else if (r == 2) wait16<5>(A[2]);
-                else wait16<4>(A[3]);
-                mfma(r, 0, B1[0]); mfma(r, 1, B1[1]);
-                copy_h(r, cp_h);
-                mfma(r, 2, B1[2]); mfma(r, 3, B1[3]);
-            }
-            // stage + 1 resident (this wave's copies, then everyone's) and
-            // every read of this stage done before its slots are reused
-            wait_vmcnt<4>();
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
-            asm volatile("s_barrier" ::: "memory");
-            rd_h = next_pos(rd_h);
-            rd_w = next_pos(rd_w);
-            const uint32_t aw2 = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
-            const uint32_t bh2 = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
-            read_b(B0, bh2 + kofs0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) read_a(r, aw2 + kofs0);
-            // ---- ks1, rows 4-7
-#pragma unroll
-            for (int r = 4; r < 8; ++r) {
-                wait16<11>(A[r]);
-                mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]);
-                if (r < 7) mfma(r, 3, B1[3]);
-                else mfma16_tied_last(acc[7][3], A[7], B1[3],   // + the epilogue's wait
-                                      __builtin_amdgcn_readfirstlane(kb == nk - 1));
-                read_a(r, aw2 + kofs0);
-            }
-            advance_h();
-            cp_w = next_pos(cp_w);
-            cp_h = next_pos(cp_h);
+        for (int r = 0; r < 8; ++r) {
+            if (r == 0) wait16_4<11>(A[0], B0);
+            else wait16<11>(A[r]);
+            mfma(r, 0, B0[0]); mfma(r, 1, B0[1]);
+            if (r < 4) copy_w(r, cp_w);
+            mfma(r, 2, B0[2]); mfma(r, 3, B0[3]);
+            read_a(r, aw + kofs1);
         }
-
-        // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
-        // Per token column bj the lane's 32 rows (bi = 0..7, i = 0..3) are
-        // folded as two 16-value groups (bi 0-3, then 4-7) into the running
-        // state; inside a group the exponentials are summed by a fixed
-        // pairwise tree.  Rows past V (last tile only) are -inf.
-        const int64_t vbase_w = (vt_first + vt_local) * kTileV + wv * 128;
-        const int64_t lim64 = v - vbase_w - grp * 4;     // row offsets bi*16 + i < lim are valid
-        const int lim = lim64 > 128 ? 128 : (int)lim64;
-        auto fold = [&](auto masked_tag) {
-            constexpr bool kMasked = decltype(masked_tag)::value;
+        advance_w();
+        // ---- ks1, rows 0-3: h(s+2) copies
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-#pragma unroll
-                for (int part = 0; part < 4; ++part) {      // bi = 2 part, 2 part + 1
-                    float z[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const int bi = part * 2 + (q >> 2), i = q & 3;
-                        z[q] = acc[bi][bj][i];
-                        if constexpr (kMasked) z[q] = bi * 16 + i < lim ? z[q] : -INFINITY;
-                    }
-                    float bmax = z[0];
-#pragma unroll
-                    for (int q = 1; q < 8; ++q) bmax = fmaxf(bmax, z[q]);
-                    const float m_new = fmaxf(m_run[bj], bmax);
-                    const float mref = m_new == -INFINITY ? 0.f : m_new;
-                    const float dsh = (m_run[bj] - mref) * c2;
-                    const float scale = m_run[bj] == m_new ? 1.f : fast_exp2(dsh);
-                    float e[8];
-                    if constexpr (kEnt) {
-                        float ea[8];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const float a = fmaxf((z[q] - mref) * c2, kArgFloor);
-                            e[q] = fast_exp2(a);
-                            ea[q] = e[q] * a;
-                        }
-#pragma unroll
-                        for (int width = 4; width >= 1; width >>= 1)
-#pragma unroll
-                            for (int q = 0; q < width; ++q) ea[q] = ea[q] + ea[q + width];
-                        const float uo = m_run[bj] == m_new
-                                             ? u_run[bj]
-                                             : (s_run[bj] > 0.f ? scale * fmaf(dsh, s_run[bj], u_run[bj])
-                                                                : 0.f);
-                        u_run[bj] = uo + ea[0];
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) e[q] = fast_exp2((z[q] - mref) * c2);
-                    }
-#pragma unroll
-                    for (int width = 4; width >= 1; width >>= 1)
-#pragma unroll
-                        for (int q = 0; q < width; ++q) e[q] = e[q] + e[q + width];
-                    s_run[bj] = fmaf(s_run[bj], scale, e[0]);
-                    m_run[bj] = m_new;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        };
-        if (lim < 128) fold(BoolConst<true>{});
-        else fold(BoolConst<false>{});
-
-        // gather: exactly one lane of the grid holds z[t, a_t]
-        int tgt[4];
-        bool any_tgt = false;
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const int64_t rel = (int64_t)my_id[bj] - vbase_w;
-            const bool mine = rel >= 0 && rel < 128 && (int)((rel & 15) >> 2) == grp;
-            tgt[bj] = mine ? (int)((rel >> 4) * 4 + (rel & 3)) : -1;
-            any_tgt |= mine;
+        for (int r = 0; r < 4; ++r) {
+            if (r == 0) wait16_4<7>(A[0], B1);
+            else if (r == 1) wait16<6>(A[1]);
+            else if (r == 2) wait16<5>(A[2]);
+            else wait16<4>(A[3]);
+            mfma(r, 0, B1[0]); mfma(r, 1, B1[1]);
+            copy_h(r, cp_h);
+            mfma(r, 2, B1[2]); mfma(r, 3, B1[3]);
         }
-        if (any_tgt) {
+        // stage + 1 resident (this wave's copies, then everyone's) and
+        // every read of this stage done before its slots are reused
+        wait_vmcnt<4>();
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
+        asm volatile("s_barrier" ::: "memory");
+        rd_h = next_pos(rd_h);
+        rd_w = next_pos(rd_w);
+        const uint32_t aw2 = lds_base + (uint32_t)(rd_w * kOperandBytes) + a_half;
+        const uint32_t bh2 = lds_base + (uint32_t)(rd_h * kOperandBytes) + b_half;
+        read_b(B0, bh2 + kofs0);
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
+        for (int r = 0; r < 4; ++r) read_a(r, aw2 + kofs0);
+        // ---- ks1, rows 4-7
 #pragma unroll
-                for (int bi = 0; bi < 8; ++bi)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        zsel_reg[bj] = tgt[bj] == bi * 4 + i ? acc[bi][bj][i] : zsel_reg[bj];
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            have_zsel = true;
+        for (int r = 4; r < 8; ++r) {
+            wait16<11>(A[r]);
+            mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]);
+            if (r < 7) mfma(r, 3, B1[3]);
+            else mfma16_tied_last(acc[7][3], A[7], B1[3],   // + the epilogue's wait
+                                  __builtin_amdgcn_readfirstlane(kb == nk - 1));
+            read_a(r, aw2 + kofs0);
         }
+        advance_h();
+        cp_w = next_pos(cp_w);
+        cp_h = next_pos(cp_h);
     }
-    // drain: the look-ahead reads and the extra copies; the ring is reused below
+    // The 4 tokens of this lane (one per 16-column block) and their ids,
+    // loaded here rather than before the K loop, where every register is
+    // taken: from clamped rows, issued together, -1 for a column past N.
+    // Their latency hides under the fold below.
+    int32_t my_id[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        const int64_t t = t0 + wt * 64 + bj * 16 + col;
+        my_id[bj] = ids[t < n ? t : n - 1];
+    }
+    // the last stage's look-ahead reads: waited for here, so that no
+    // fragment register is live (or still being written) in the epilogue
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3]),
                  "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B0[0]), "+v"(B0[1]), "+v"(B0[2]), "+v"(B0[3]));
-    wait_vmcnt<0>();
-    __syncthreads();
 
-    // ---- the selected logits this lane owns (one owner per token)
-    if (have_zsel) {
-        const int64_t chunk_rows = (int64_t)ntiles_here * kTileV;
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const int64_t in_chunk = (int64_t)my_id[bj] - vt_first * kTileV;
-            if (in_chunk >= 0 && in_chunk < chunk_rows && ((in_chunk & 255) >> 7) == wv &&
-                (int)((in_chunk & 15) >> 2) == grp)
-                zsel[t0 + wt * 64 + bj * 16 + col] = zsel_reg[bj];
-        }
-    }
-
-    // ---- end of chunk: merge the four row groups (xor 16, then 32), then
-    // the two vocabulary waves
+    // ---- epilogue: online log-sum-exp + gather over the tile
+    float m_run[4], s_run[4], u_run[4], zsel_reg[4];
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-#pragma unroll
-        for (int sh = 16; sh <= 32; sh <<= 1) {
-            const float mo = __shfl_xor(m_run[bj], sh);
-            const float so = __shfl_xor(s_run[bj], sh);
-            if constexpr (kEnt) {
-                const float uo = __shfl_xor(u_run[bj], sh);
-                lse_combine3(m_run[bj], s_run[bj], u_run[bj], mo, so, uo, c2);
-            } else {
-                lse_combine(m_run[bj], s_run[bj], mo, so, c2);
-            }
-        }
+        m_run[bj] = -INFINITY; s_run[bj] = 0.f; u_run[bj] = 0.f; zsel_reg[bj] = 0.f;
     }
-    float2* xch = (float2*)lds;          // [token quarter][token]; the ring is drained
+    const int64_t vbase_w = vbase + wv * 128;
+    const int64_t lim64 = v - vbase_w - grp * 4;     // row offsets bi*16 + i < lim are valid
+    const int lim = lim64 > 128 ? 128 : (int)lim64;
+    if (lim < 128) fold16<kEnt, true, 4>(acc, lim, c2, m_run, s_run, u_run);
+    else fold16<kEnt, false, 4>(acc, lim, c2, m_run, s_run, u_run);
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+        if (t0 + wt * 64 + bj * 16 + col >= n) my_id[bj] = -1;
+    int tgt[4];
+    gather16<4>(acc, my_id, vbase_w, grp, zsel_reg, tgt);
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+        if (tgt[bj] >= 0) zsel[t0 + wt * 64 + bj * 16 + col] = zsel_reg[bj];
+
+    // ---- end of chunk: merge the four row groups, then the two vocabulary
+    // waves.  The extra copies of the last stages land in the ring, which
+    // the exchange reuses: wait for them first.
+    merge_row_groups<kEnt, 4>(m_run, s_run, u_run, c2);
+    wait_vmcnt<0>();
+    __syncthreads();
+    float2* xch = (float2*)lds;          // [token quarter][token]
     float* xu = (float*)(lds + 2048);    // u, same index
     if (wv == 1 && grp == 0) {
 #pragma unroll
@@ -968,7 +971,7 @@ bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flag
     p->n = n; p->d = d; p->v = v; p->dtype = dtype;
     p->nvtiles = (v + kTileV - 1) / kTileV;
     p->nttiles = (n + kTileT - 1) / kTileT;
-    if (flags == 0u) {
+    if (flags == 0u || dtype == 0) {
         p->chunk_tiles = kInvariantChunkTiles;
     } else {
         // free schedule: about two workgroups per compute unit, whatever N is
@@ -1014,11 +1017,12 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
                            sc.c2, part, upart, zsel, n_bad_ids);
     };
     if (p.dtype == 0) {
+        if (p.chunk_tiles != 1) return hipErrorInvalidValue;   // one tile per chunk
         auto go8 = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(2 * kThreads), 0, st,
                                (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
-                               ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
-                               sc.c2, part, upart, zsel, n_bad_ids);
+                               ids, p.n, p.v, nk, p.nchunks, p.nttiles, sc.c2, part, upart, zsel,
+                               n_bad_ids);
         };
         if (p.entropy) go8(lmhead8w_kernel<true>);
         else go8(lmhead8w_kernel<false>);
