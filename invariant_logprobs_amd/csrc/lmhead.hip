@@ -889,18 +889,238 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     }
 }
 
+// bf16 partials for small batches: one wave per 128-row half of a
+// vocabulary chunk and 16 NB tokens (NB = 1 or 2 column blocks; the kernel
+// also takes several token groups of 32, unused while kNarrowMaxTokens is 32).
+//
+// At a few tokens the 256-token tile of lmhead8w_kernel spends almost all
+// of its MFMA work on padding, while the call is bound by reading W once
+// (V D 2 bytes).  This kernel streams W straight from HBM into registers:
+// no LDS ring and no barrier, and at the Qwen3-8B shape 1187 independent
+// waves keep the whole matrix in flight.  It computes each logit with the
+// same instruction as lmhead8w_kernel (v_mfma_f32_16x16x32_bf16, W rows as
+// the first source, tokens as the second, the same K -> lane assignment, k
+// steps in ascending order from a zero accumulator) and folds it with the
+// same helpers (fold16, gather16, merge_row_groups) in the same lane
+// layout, so every per-token state it writes has the bits lmhead8w_kernel
+// forms for the same half of the same chunk.  The only difference: the two
+// halves of a chunk are separate waves here, so each writes its own state
+// (hpart[2 chunk + half][n]) and the merge combines the pair in the order
+// lmhead8w_kernel's exchange uses (half 0 first, half 1 merged into it).
+// The MFMAs are tied-accumulator asm, as in lmhead8w_kernel (with the
+// builtin the allocator moves all accumulators between registers every
+// round, and each move waits for its MFMA); the wait states asm hides from
+// the compiler's hazard recognizer are mfma_drain's after the loop, and the
+// code as built is checked for MFMA hazards on every path.
+//
+// Operand path: k-step j of this wave (32 K; 2 per 128-byte stage) needs 8 A
+// fragments (row block r: lane l holds row r*16 + (l & 15), K 8 (l >> 4) ..
+// + 7) and NB B fragments, each one 16-byte buffer load per lane.  They go
+// to a ring of R register sets, R - 1 k-steps ahead of the MFMAs; every
+// k-step issues the same number of loads (past the last k-step the loads
+// repeat the last k-step's addresses, cache hits).  The descriptors are
+// built from the tensors' own pointers; rows past V or N are redirected to
+// the last valid row (their results are masked or dropped), and every
+// access stays inside the descriptor's extent.
+//
+// Work map: unit u = (chunk u >> 1, half u & 1), token group g.  Block b
+// serves unit ((b >> 3) / ntg) * 8 + (b & 7) and group (b >> 3) % ntg: the
+// groups of a unit run on one XCD (b & 7) next to each other, so W is read
+// from HBM once and from that XCD's L2 by the other group.
+template <int NB> struct NarrowCfg;
+template <> struct NarrowCfg<1> { static constexpr int R = 4; };
+template <> struct NarrowCfg<2> { static constexpr int R = 4; };
+constexpr int kNarrowMaxTokens = 32;   // above: two token groups re-read W, and the
+                                        // 256-token kernel is faster
+
+template <bool kEnt, int NB>
+__global__ void __launch_bounds__(64)
+lmhead_narrow_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
+                     const unsigned char* __restrict__ w, int64_t ldw_b,
+                     const int32_t* __restrict__ ids, int64_t n, int64_t v, int nk,
+                     int64_t nchunks, int ntg, float c2, float2* __restrict__ hpart,
+                     float* __restrict__ hupart, float* __restrict__ zsel,
+                     int32_t* __restrict__ n_bad_ids) {
+    constexpr int R = NarrowCfg<NB>::R;
+    constexpr int L = 8 + NB;                 // loads per k-step
+    const int lane = threadIdx.x;
+    const int col = lane & 15, grp = lane >> 4;
+    if (blockIdx.x == 0 && lane == 0 && n_bad_ids) *n_bad_ids = 0;
+
+    const int64_t q = blockIdx.x >> 3;
+    const int g = (int)(q % ntg);
+    const int64_t unit = (q / ntg) * 8 + (blockIdx.x & 7);
+    if (unit >= 2 * nchunks) return;
+    const int64_t chunk = unit >> 1;
+    const int wv = (int)(unit & 1);
+    const int64_t vbase_w = chunk * kTileV + wv * 128;
+    const int64_t t0 = (int64_t)g * 16 * NB;
+    if (vbase_w >= v) {
+        // the upper half of a last chunk with at most 128 rows: the state
+        // lmhead8w_kernel forms for a half with no valid row
+        if (grp == 0) {
+#pragma unroll
+            for (int bj = 0; bj < NB; ++bj) {
+                const int64_t t = t0 + bj * 16 + col;
+                if (t < n) {
+                    hpart[unit * n + t] = make_float2(-INFINITY, 0.f);
+                    if constexpr (kEnt) hupart[unit * n + t] = 0.f;
+                }
+            }
+        }
+        return;
+    }
+    const int64_t wrows = (v - vbase_w) < 128 ? (v - vbase_w) : 128;
+    const int64_t hrows = (n - t0) < 16 * NB ? (n - t0) : 16 * NB;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w + vbase_w * ldw_b), (short)0,
+        (int)((wrows - 1) * ldw_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(h + t0 * ldh_b), (short)0,
+        (int)((hrows - 1) * ldh_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+    uint32_t aoff[8], boff[NB];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int64_t row = r * 16 + col < wrows ? r * 16 + col : wrows - 1;
+        aoff[r] = (uint32_t)(row * ldw_b) + (uint32_t)(grp * 16);
+    }
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+        const int64_t row = bj * 16 + col < hrows ? bj * 16 + col : hrows - 1;
+        boff[bj] = (uint32_t)(row * ldh_b) + (uint32_t)(grp * 16);
+    }
+
+    u32x4 A[R][8], B[R][NB];
+    f32x4 acc[8][NB];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) acc[r][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nks = 2 * nk;                   // k-steps of 32 K
+    // loads of k-step j (clamped to the last one) into ring slot `slot`
+    auto issue = [&](auto slot_tag, int j) {
+        constexpr int slot = decltype(slot_tag)::value;
+        const int jj = j < nks ? j : nks - 1;
+        const uint32_t koff = (uint32_t)__builtin_amdgcn_readfirstlane(jj * 64);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            A[slot][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       wrs, aoff[r], koff, 0));
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+            B[slot][bj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        hrs, boff[bj], koff, 0));
+    };
+    auto compute = [&](auto slot_tag) {
+        constexpr int slot = decltype(slot_tag)::value;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int bj = 0; bj < NB; ++bj) mfma16_tied(acc[r][bj], A[slot][r], B[slot][bj]);
+    };
+    // k-step j: its loads were issued R - 1 k-steps ago; issue j + R - 1
+    // into the slot k-step j - 1 freed, then wait for k-step j's.
+    auto step = [&](auto slot_tag, int j) {
+        constexpr int slot = decltype(slot_tag)::value;
+        issue(IntConst<(slot + R - 1) % R>{}, j + R - 1);
+        __builtin_amdgcn_sched_barrier(0);      // keep the load order the counts assume
+        wait_vmcnt<(R - 1) * L>();
+        compute(slot_tag);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) {
+        if (i == 0) issue(IntConst<0>{}, 0);
+        if (i == 1) issue(IntConst<1 % R>{}, 1);
+        if (i == 2) issue(IntConst<2 % R>{}, 2);
+    }
+    // whole rounds of R k-steps (no branch inside), then the remainder
+    int j = 0;
+    for (; j + R <= nks; j += R) {
+        step(IntConst<0>{}, j);
+        step(IntConst<1 % R>{}, j + 1);
+        if constexpr (R > 2) step(IntConst<2 % R>{}, j + 2);
+        if constexpr (R > 3) step(IntConst<3 % R>{}, j + 3);
+    }
+    const int rem = __builtin_amdgcn_readfirstlane(nks - j);
+    if (rem >= 1) step(IntConst<0>{}, j);
+    if constexpr (R > 2) { if (rem >= 2) step(IntConst<1 % R>{}, j + 1); }
+    if constexpr (R > 3) { if (rem >= 3) step(IntConst<2 % R>{}, j + 2); }
+    wait_vmcnt<0>();
+    mfma_drain<NB>(acc);
+
+    // ---- epilogue, as lmhead8w_kernel's for one wave
+    float m_run[NB], s_run[NB], u_run[NB], zsel_reg[NB];
+    int32_t my_id[NB];
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+        m_run[bj] = -INFINITY; s_run[bj] = 0.f; u_run[bj] = 0.f; zsel_reg[bj] = 0.f;
+        const int64_t t = t0 + bj * 16 + col;
+        my_id[bj] = t < n ? ids[t] : -1;
+    }
+    const int64_t lim64 = v - vbase_w - grp * 4;
+    const int lim = lim64 > 128 ? 128 : (int)lim64;
+    if (lim < 128) fold16<kEnt, true, NB>(acc, lim, c2, m_run, s_run, u_run);
+    else fold16<kEnt, false, NB>(acc, lim, c2, m_run, s_run, u_run);
+    int tgt[NB];
+    gather16<NB>(acc, my_id, vbase_w, grp, zsel_reg, tgt);
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+        if (tgt[bj] >= 0) zsel[t0 + bj * 16 + col] = zsel_reg[bj];
+    merge_row_groups<kEnt, NB>(m_run, s_run, u_run, c2);
+    if (grp == 0) {
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) {
+            const int64_t t = t0 + bj * 16 + col;
+            if (t < n) {
+                hpart[unit * n + t] = make_float2(m_run[bj], s_run[bj]);
+                if constexpr (kEnt) hupart[unit * n + t] = u_run[bj];
+            }
+        }
+    }
+}
+
 // Merge of the vocabulary-chunk partials.  A block serves 64 tokens with
 // kMergeWaves waves: wave w folds chunks w, w + kMergeWaves, ... in ascending
 // order for its 64 tokens (coalesced 8-byte loads, kMergeUnroll in flight),
 // then wave 0 folds the kMergeWaves strands in order.  The order depends on
 // the number of chunks only.
 constexpr int kMergeWaves = 8;
-constexpr int kMergeUnroll = 4;
+// chunks in flight per strand step: 4 for the whole-chunk layout (many
+// tokens per block keep the loads busy), 16 for the half-chunk layout of
+// small batches, where a lane's loads are the only ones in flight
+template <bool kHalves> struct MergeUnroll { static constexpr int value = kHalves ? 16 : 4; };
 
 // With it = 1 / tau: lse = m it + ln s and logp = (z_a - m) it - ln s (the
 // difference z_a - m is formed before the scale, so no two large terms
 // cancel); entropy = ln 2 (log2 s - u / s) when kEnt.
-template <bool kEnt>
+//
+// kHalves: the partials are per half chunk (lmhead_narrow_kernel): chunk c's
+// state is half 2c with half 2c + 1 merged into it, the order in which
+// lmhead8w_kernel's wave exchange forms it.
+template <bool kEnt, bool kHalves>
+__device__ __forceinline__ void load_chunk(const float2* __restrict__ part,
+                                           const float* __restrict__ upart, int64_t c, int64_t n,
+                                           int64_t tc, float c2, float2& p, float& q) {
+    if constexpr (kHalves) {
+        const float2 p0 = part[(2 * c) * n + tc], p1 = part[(2 * c + 1) * n + tc];
+        float m = p0.x, s = p0.y, u = 0.f;
+        if constexpr (kEnt) {
+            u = upart[(2 * c) * n + tc];
+            lse_combine3(m, s, u, p1.x, p1.y, upart[(2 * c + 1) * n + tc], c2);
+        } else {
+            lse_combine(m, s, p1.x, p1.y, c2);
+        }
+        p = make_float2(m, s);
+        q = u;
+    } else {
+        p = part[c * n + tc];
+        if constexpr (kEnt) q = upart[c * n + tc];
+    }
+}
+
+template <bool kEnt, bool kHalves>
 __global__ void __launch_bounds__(64 * kMergeWaves)
 lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ upart,
                  const float* __restrict__ zsel, const int32_t* __restrict__ ids, int64_t n,
@@ -917,14 +1137,13 @@ lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ upar
     const int64_t tc = t < n ? t : n - 1;
     float m = -INFINITY, s = 0.f, uu = 0.f;
     int64_t c = wave;
+    constexpr int kMergeUnroll = MergeUnroll<kHalves>::value;
     for (; c + (kMergeUnroll - 1) * kMergeWaves < nchunks; c += kMergeUnroll * kMergeWaves) {
         float2 p[kMergeUnroll];
         float q[kMergeUnroll];
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            p[u] = part[(c + u * kMergeWaves) * n + tc];
-            if constexpr (kEnt) q[u] = upart[(c + u * kMergeWaves) * n + tc];
-        }
+        for (int u = 0; u < kMergeUnroll; ++u)
+            load_chunk<kEnt, kHalves>(part, upart, c + u * kMergeWaves, n, tc, c2, p[u], q[u]);
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
             if constexpr (kEnt) lse_combine3(m, s, uu, p[u].x, p[u].y, q[u], c2);
@@ -932,8 +1151,10 @@ lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ upar
         }
     }
     for (; c < nchunks; c += kMergeWaves) {
-        const float2 p = part[c * n + tc];
-        if constexpr (kEnt) lse_combine3(m, s, uu, p.x, p.y, upart[c * n + tc], c2);
+        float2 p;
+        float q = 0.f;
+        load_chunk<kEnt, kHalves>(part, upart, c, n, tc, c2, p, q);
+        if constexpr (kEnt) lse_combine3(m, s, uu, p.x, p.y, q, c2);
         else lse_combine(m, s, p.x, p.y, c2);
     }
     strand[wave][lane] = make_float2(m, s);
@@ -983,11 +1204,14 @@ bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flag
     }
     p->nchunks = (p->nvtiles + p->chunk_tiles - 1) / p->chunk_tiles;
     p->entropy = entropy;
-    p->part_bytes = align_up((size_t)p->nchunks * (size_t)n * sizeof(float2), 256);
+    p->narrow = dtype == 0 && n >= 1 && n <= kNarrowMaxTokens;
+    p->nb = n <= 16 ? 1 : 2;
+    p->ntg = (int)((n + 16 * p->nb - 1) / (16 * p->nb));
+    const size_t nparts = (size_t)p->nchunks * (p->narrow ? 2 : 1);
+    p->part_bytes = align_up(nparts * (size_t)n * sizeof(float2), 256);
     p->zsel_off = p->part_bytes;
     p->upart_off = p->zsel_off + align_up((size_t)n * sizeof(float), 256);
-    p->total_bytes = p->upart_off +
-                     (entropy ? align_up((size_t)p->nchunks * (size_t)n * sizeof(float), 256) : 0);
+    p->total_bytes = p->upart_off + (entropy ? align_up(nparts * (size_t)n * sizeof(float), 256) : 0);
     if (p->total_bytes == 0) p->total_bytes = 256;
     return true;
 }
@@ -1016,7 +1240,24 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
                            ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
                            sc.c2, part, upart, zsel, n_bad_ids);
     };
-    if (p.dtype == 0) {
+    if (p.dtype == 0 && p.narrow) {
+        // units (chunk halves) rounded up to the 8 XCDs, times the token groups
+        const int64_t blocks = (2 * p.nchunks + 7) / 8 * 8 * p.ntg;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        auto gon = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64), 0, st,
+                               (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
+                               ids, p.n, p.v, nk, p.nchunks, p.ntg, sc.c2, part, upart, zsel,
+                               n_bad_ids);
+        };
+        if (p.entropy) {
+            if (p.nb == 1) gon(lmhead_narrow_kernel<true, 1>);
+            else gon(lmhead_narrow_kernel<true, 2>);
+        } else {
+            if (p.nb == 1) gon(lmhead_narrow_kernel<false, 1>);
+            else gon(lmhead_narrow_kernel<false, 2>);
+        }
+    } else if (p.dtype == 0) {
         if (p.chunk_tiles != 1) return hipErrorInvalidValue;   // one tile per chunk
         auto go8 = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(2 * kThreads), 0, st,
@@ -1041,14 +1282,18 @@ hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const Scor
     const float* upart = p.entropy ? (const float*)((const unsigned char*)workspace + p.upart_off)
                                    : nullptr;
     const int64_t blocks = (p.n + 63) / 64;
-    if (p.entropy)
-        hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0,
-                           st, part, upart, zsel, ids, p.n, p.nchunks, p.v, sc.c2, sc.it, logp, lse,
-                           entropy, n_bad_ids);
-    else
-        hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0,
-                           st, part, upart, zsel, ids, p.n, p.nchunks, p.v, sc.c2, sc.it, logp, lse,
-                           entropy, n_bad_ids);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0, st, part, upart,
+                           zsel, ids, p.n, p.nchunks, p.v, sc.c2, sc.it, logp, lse, entropy,
+                           n_bad_ids);
+    };
+    if (p.entropy) {
+        if (p.narrow) go(lse_merge_kernel<true, true>);
+        else go(lse_merge_kernel<true, false>);
+    } else {
+        if (p.narrow) go(lse_merge_kernel<false, true>);
+        else go(lse_merge_kernel<false, false>);
+    }
     return hipGetLastError();
 }
 

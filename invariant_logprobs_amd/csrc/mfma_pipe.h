@@ -155,6 +155,28 @@ __device__ __forceinline__ void mfma16_tied_last(f32x4& acc, const u32x4& a, con
                  : "+a"(acc) : "v"(a), "v"(b), "s"(last) : "scc");
 }
 
+// The wait after the last of a sequence of tied asm MFMAs on acc[8][NB]:
+// 20 wait states, more than any MFMA result needs before another instruction
+// reads it, with every accumulator block an operand so that no read of one
+// can be placed before it.  For the small accumulator sets of the narrow
+// kernels (NB = 1, 2).
+template <int NB>
+__device__ __forceinline__ void mfma_drain(f32x4 (&acc)[8][NB]);
+template <>
+__device__ __forceinline__ void mfma_drain<1>(f32x4 (&a)[8][1]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+a"(a[0][0]), "+a"(a[1][0]), "+a"(a[2][0]), "+a"(a[3][0]), "+a"(a[4][0]),
+                   "+a"(a[5][0]), "+a"(a[6][0]), "+a"(a[7][0]));
+}
+template <>
+__device__ __forceinline__ void mfma_drain<2>(f32x4 (&a)[8][2]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+a"(a[0][0]), "+a"(a[1][0]), "+a"(a[2][0]), "+a"(a[3][0]), "+a"(a[4][0]),
+                   "+a"(a[5][0]), "+a"(a[6][0]), "+a"(a[7][0]), "+a"(a[0][1]), "+a"(a[1][1]),
+                   "+a"(a[2][1]), "+a"(a[3][1]), "+a"(a[4][1]), "+a"(a[5][1]), "+a"(a[6][1]),
+                   "+a"(a[7][1]));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -167,6 +189,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <bool B> struct BoolConst { static constexpr bool value = B; };
+template <int I> struct IntConst { static constexpr int value = I; };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

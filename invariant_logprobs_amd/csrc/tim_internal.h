@@ -35,7 +35,12 @@ struct LogprobPlan {
     int64_t nchunks;      // ceil(nvtiles / chunk_tiles)
     int64_t nttiles;      // ceil(n / kTileT)
     bool entropy;         // carry the entropy state u as well
-    // workspace: float2 part[nchunks][n] | float zsel[n] | float upart[nchunks][n]
+    bool narrow;          // bf16, n <= 32: one wave per half chunk (lmhead_narrow_kernel),
+                          // partials per half chunk
+    int nb;               // narrow: token column blocks of 16 per wave (1 or 2)
+    int ntg;              // narrow: token groups of 16 nb (1 or 2)
+    // workspace: float2 part[P][n] | float zsel[n] | float upart[P][n], with
+    // P = nchunks, or 2 nchunks (one state per half chunk) when narrow
     size_t part_bytes, zsel_off, upart_off, total_bytes;
 };
 
