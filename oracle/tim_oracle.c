@@ -476,6 +476,56 @@ static int cmp_double(const void* a, const void* b)
     return (x > y) - (x < y);
 }
 
+/* Ascending sort of x[0..m): up to nthreads pieces sorted by qsort, each in
+ * its own thread, then merged (at every step the smallest head of the
+ * pieces, the first piece on a tie).  Sorting fixes the sequence, so the
+ * result is the one a single qsort gives; the pieces only spread the work
+ * of a few hundred million keys over the host's cores. */
+typedef struct { double* a; size_t n; } sort_job;
+
+static void* sort_worker(void* arg)
+{
+    sort_job* j = (sort_job*)arg;
+    qsort(j->a, j->n, sizeof(double), cmp_double);
+    return NULL;
+}
+
+#define OX_MAX_SORT_PIECES 16
+
+static int sort_doubles(double* x, int64_t m, int nthreads)
+{
+    if (nthreads > OX_MAX_SORT_PIECES) nthreads = OX_MAX_SORT_PIECES;
+    if (nthreads < 2 || m < (int64_t)1 << 20) {
+        qsort(x, (size_t)m, sizeof(double), cmp_double);
+        return 0;
+    }
+    sort_job jobs[OX_MAX_SORT_PIECES];
+    pthread_t th[OX_MAX_SORT_PIECES];
+    size_t pos[OX_MAX_SORT_PIECES], end[OX_MAX_SORT_PIECES];
+    const int64_t per = (m + nthreads - 1) / nthreads;
+    int np = 0;
+    for (int64_t b = 0; b < m; b += per, ++np) {
+        const int64_t e = b + per < m ? b + per : m;
+        jobs[np].a = x + b;
+        jobs[np].n = (size_t)(e - b);
+        pos[np] = (size_t)b;
+        end[np] = (size_t)e;
+    }
+    for (int i = 0; i < np; ++i) pthread_create(&th[i], NULL, sort_worker, &jobs[i]);
+    for (int i = 0; i < np; ++i) pthread_join(th[i], NULL);
+    double* out = (double*)malloc(sizeof(double) * (size_t)m);
+    if (!out) return -1;
+    for (int64_t k = 0; k < m; ++k) {
+        int best = -1;
+        for (int i = 0; i < np; ++i)
+            if (pos[i] < end[i] && (best < 0 || x[pos[i]] < x[pos[best]])) best = i;
+        out[k] = x[pos[best]++];
+    }
+    memcpy(x, out, sizeof(double) * (size_t)m);
+    free(out);
+    return 0;
+}
+
 /* Quantile q of the ascending array x[0..m) with linear interpolation
  * between order statistics: position q (m - 1), lower index its floor,
  * upper index one above (capped at m - 1), weight the fractional part.
@@ -541,8 +591,12 @@ int or_mismatch_extras(const float* lt, const float* lr, const uint8_t* mask,
         rel_sum += fabs(delta) / (fabs((double)lt[t]) + 1e-8);
         m++;
     }
-    qsort(ratio, (size_t)m, sizeof(double), cmp_double);
-    qsort(absd, (size_t)m, sizeof(double), cmp_double);
+    const int nsort = or_available_cpus();
+    if (sort_doubles(ratio, m, nsort) != 0 || sort_doubles(absd, m, nsort) != 0) {
+        free(ratio);
+        free(absd);
+        return -1;
+    }
 
     for (int i = 0; i < OX_NFIELDS; ++i) out[i] = 0.0;
     out[OX_N_VALID] = (double)m;

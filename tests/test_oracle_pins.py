@@ -443,6 +443,25 @@ def test_quantiles_match_numpy_linear_method():
         assert r["abs_q"][0] == pytest.approx(want_a, rel=1e-14, abs=1e-300)
 
 
+def test_quantiles_of_many_tokens_match_numpy():
+    """Above 2^20 valid tokens the oracle sorts in pieces on several threads
+    and merges them; the quantiles must still be numpy's on the same data."""
+    rng = np.random.default_rng(29)
+    n = (1 << 21) + 12345
+    lr = -rng.uniform(0.0, 5.0, n).astype(np.float32)
+    lt = (lr + rng.normal(0, 0.02, n)).astype(np.float32)
+    mask = (rng.random(n) < 0.9).astype(np.uint8)
+    qs = (0.0, 0.01, 0.5, 0.99)
+    r = _extras(lt, lr, mask=mask, rq=qs, aq=())
+    d = lt.astype(np.float64)[mask != 0] - lr.astype(np.float64)[mask != 0]
+    np.testing.assert_allclose(r["ratio_q"], np.quantile(np.exp(d), qs, method="linear"),
+                               rtol=1e-14, atol=0)
+    for aq in ((0.95, 1.0, 0.25, 0.5),):
+        ra = _extras(lt, lr, mask=mask, rq=(), aq=aq)
+        np.testing.assert_allclose(ra["abs_q"], np.quantile(np.abs(d), aq, method="linear"),
+                                   rtol=1e-14, atol=0)
+
+
 def test_quantile_order_statistics_and_edge_cases():
     lr = np.full(5, -1.0, np.float32)
     offs = np.array([0.5, -0.25, 0.0, 0.125, -1.0])
@@ -808,8 +827,15 @@ MUTATIONS = [
      "test_rel_diff_zero_train_logp_and_scale_invariance"),
     ("quantile without interpolation", "return x[lo] + (x[hi] - x[lo]) * frac;",
      "return x[lo];", "test_quantile_order_statistics_and_edge_cases"),
-    ("quantile of unsorted values", "qsort(ratio, (size_t)m, sizeof(double), cmp_double);",
-     "(void)cmp_double;", "test_quantile_order_statistics_and_edge_cases"),
+    ("quantile of unsorted values",
+     "if (sort_doubles(ratio, m, nsort) != 0 || sort_doubles(absd, m, nsort) != 0) {",
+     "if (sort_doubles(absd, m, nsort) != 0) {", "test_quantile_order_statistics_and_edge_cases"),
+    ("pieces merged by the largest head",
+     "if (pos[i] < end[i] && (best < 0 || x[pos[i]] < x[pos[best]])) best = i;",
+     "if (pos[i] < end[i] && (best < 0 || x[pos[i]] > x[pos[best]])) best = i;",
+     "test_quantiles_of_many_tokens_match_numpy"),
+    ("pieces merged unsorted", "    qsort(j->a, j->n, sizeof(double), cmp_double);\n    return NULL;",
+     "    (void)j;\n    return NULL;", "test_quantiles_of_many_tokens_match_numpy"),
     ("quantile position over m", "double pos = q * (double)(m - 1);",
      "double pos = q * (double)m;", "test_quantiles_match_numpy_linear_method"),
     ("softmax derivative sign", "dz[c] = g * ((c == a ? 1.0 : 0.0) - p);",
