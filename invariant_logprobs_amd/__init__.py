@@ -37,6 +37,7 @@ Entry points (same names as the C ABI):
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 import threading
@@ -211,6 +212,41 @@ def _stream_handle(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _on_stream(fn):
+    """Run a wrapper on the caller's ``stream=`` (a ``torch.cuda.Stream``)
+    with torch's stream-ordered memory rules kept:
+
+    * the given stream first waits for torch's current stream, so inputs
+      written there are complete before the library reads them;
+    * outputs and any internal workspace are allocated while the given
+      stream is current, so torch's caching allocator ties them to it (an
+      internal workspace freed on return is only reused by later work on
+      the same stream, which runs after these kernels);
+    * every tensor argument (inputs, ``out``, ``workspace``, ``dw``) is
+      recorded on the given stream, so its memory is not handed to another
+      allocation before the stream's kernels are done with it.
+
+    Results live on the given stream: a caller that reads them on another
+    stream makes that stream wait first, as with any torch tensor."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        if not isinstance(stream, torch.cuda.Stream):
+            raise TypeError("stream must be a torch.cuda.Stream")
+        cur = torch.cuda.current_stream(stream.device)
+        if stream == cur:
+            return fn(*args, **kwargs)
+        stream.wait_stream(cur)
+        with torch.cuda.stream(stream):
+            res = fn(*args, **kwargs)
+        for t in list(args) + list(kwargs.values()):
+            if isinstance(t, torch.Tensor) and t.is_cuda:
+                t.record_stream(stream)
+        return res
+    return wrapper
+
+
 _DTYPES = {torch.bfloat16: TIM_BF16, torch.float32: TIM_F32}
 
 
@@ -223,6 +259,7 @@ def stats_workspace_bytes(n: int, s: int) -> int:
     return int(load_library().tim_stats_workspace_bytes(n, s))
 
 
+@_on_stream
 def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
                         schedule: str = "invariant", return_lse: bool = False,
                         out: Optional[torch.Tensor] = None,
@@ -268,6 +305,7 @@ def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
     return logp
 
 
+@_on_stream
 def tim_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, *, eps: float = 1e-6,
                 out: Optional[torch.Tensor] = None, return_rstd: bool = False, stream=None):
     """``y = gamma * x / sqrt(mean(x^2) + eps)`` per row of ``x`` [N, D]
@@ -303,6 +341,7 @@ def logprob_ex_workspace_bytes(n: int, d: int, v: int, dtype: int, *, temperatur
                                                              ctypes.byref(prm), int(entropy)))
 
 
+@_on_stream
 def tim_logprob_forward_ex(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
                            temperature: float = 1.0, norm_gamma: Optional[torch.Tensor] = None,
                            norm_eps: float = 1e-6, entropy: bool = False,
@@ -353,6 +392,7 @@ def tim_logprob_forward_ex(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, 
     return res
 
 
+@_on_stream
 def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
                        mask: Optional[torch.Tensor], cu_seqlens: torch.Tensor, *,
                        tis_clip: float = 2.0, seq_bounds=(-0.01, 0.01),
@@ -430,6 +470,7 @@ def extras_workspace_bytes(n: int) -> int:
     return int(load_library().tim_extras_workspace_bytes(n))
 
 
+@_on_stream
 def tim_mismatch_extras(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
                         mask: Optional[torch.Tensor], *, tok_tau: float,
                         ratio_q=(0.01, 0.5, 0.99), abs_q=(0.95,),
@@ -487,6 +528,7 @@ def backward_workspace_bytes(n: int, d: int, v: int) -> int:
     return int(load_library().tim_logprob_backward_workspace_bytes(n, d, v, TIM_BF16))
 
 
+@_on_stream
 def tim_logprob_backward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
                          lse: torch.Tensor, grad_logp: torch.Tensor, *, want_dh: bool = True,
                          want_dw: bool = True, dw: Optional[torch.Tensor] = None,
@@ -537,6 +579,7 @@ def tim_logprob_backward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
     return dh, dw
 
 
+@_on_stream
 def tim_ppo_loss(logp: torch.Tensor, logp_old_train: torch.Tensor,
                  logp_old_rollout: torch.Tensor, advantages: torch.Tensor,
                  mask: Optional[torch.Tensor], *, eps_low: float = 0.2, eps_high: float = 0.28,

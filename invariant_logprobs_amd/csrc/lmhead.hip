@@ -1091,6 +1091,7 @@ constexpr int kMergeWaves = 8;
 // tokens per block keep the loads busy), 16 for the half-chunk layout of
 // small batches, where a lane's loads are the only ones in flight
 template <bool kHalves> struct MergeUnroll { static constexpr int value = kHalves ? 16 : 4; };
+constexpr size_t kMergeTokenLdsMax = 64 * 1024;   // chunk states of one token in LDS
 
 // With it = 1 / tau: lse = m it + ln s and logp = (z_a - m) it - ln s (the
 // difference z_a - m is formed before the scale, so no two large terms
@@ -1181,6 +1182,68 @@ lse_merge_kernel(const float2* __restrict__ part, const float* __restrict__ upar
     }
     __syncthreads();
     if (threadIdx.x == 0 && n_bad_ids && bad_count) atomicAdd(n_bad_ids, bad_count);
+}
+
+// The same merge for the half-chunk partials of small batches, one block per
+// token: the block first loads every chunk's pair of half states at once
+// (combining each pair as load_chunk does) into LDS, then eight threads fold
+// the eight strands (chunks w, w + 8, ... in ascending order) and thread 0
+// folds the strands in order, the sequence lse_merge_kernel follows, so the
+// bits are the same.  With a handful of tokens lse_merge_kernel's lanes have
+// no loads but their own and wait a full memory latency per unrolled group;
+// here one latency covers them all.
+template <bool kEnt>
+__global__ void __launch_bounds__(512)
+lse_merge_token_kernel(const float2* __restrict__ part, const float* __restrict__ upart,
+                       const float* __restrict__ zsel, const int32_t* __restrict__ ids, int64_t n,
+                       int64_t nchunks, int64_t v, float c2, float it, float* __restrict__ logp,
+                       float* __restrict__ lse, float* __restrict__ ent,
+                       int32_t* __restrict__ n_bad_ids) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float2* cs = (float2*)smem;                              // [nchunks]
+    float* cu = (float*)(smem + nchunks * sizeof(float2));   // [nchunks] when kEnt
+    __shared__ float2 strand[kMergeWaves];
+    __shared__ float ustrand[kMergeWaves];
+    const int64_t t = blockIdx.x;
+    for (int64_t c = threadIdx.x; c < nchunks; c += blockDim.x) {
+        float2 p;
+        float q = 0.f;
+        load_chunk<kEnt, true>(part, upart, c, n, t, c2, p, q);
+        cs[c] = p;
+        if constexpr (kEnt) cu[c] = q;
+    }
+    __syncthreads();
+    if (threadIdx.x < kMergeWaves) {
+        const int w = threadIdx.x;
+        float m = -INFINITY, s = 0.f, uu = 0.f;
+        for (int64_t c = w; c < nchunks; c += kMergeWaves) {
+            const float2 p = cs[c];
+            if constexpr (kEnt) lse_combine3(m, s, uu, p.x, p.y, cu[c], c2);
+            else lse_combine(m, s, p.x, p.y, c2);
+        }
+        strand[w] = make_float2(m, s);
+        ustrand[w] = uu;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float mm = strand[0].x, ss = strand[0].y, us = 0.f;
+        if constexpr (kEnt) us = ustrand[0];
+#pragma unroll
+        for (int w = 1; w < kMergeWaves; ++w) {
+            if constexpr (kEnt)
+                lse_combine3(mm, ss, us, strand[w].x, strand[w].y, ustrand[w], c2);
+            else
+                lse_combine(mm, ss, strand[w].x, strand[w].y, c2);
+        }
+        const float l2s = fast_log2(ss);
+        const float lns = l2s * kLn2;
+        const int32_t a = ids[t];
+        const bool bad = a < 0 || (int64_t)a >= v;
+        logp[t] = bad ? __builtin_nanf("") : fmaf(zsel[t] - mm, it, -lns);
+        if (lse) lse[t] = fmaf(mm, it, lns);
+        if constexpr (kEnt) ent[t] = (l2s - us / ss) * kLn2;
+        if (bad && n_bad_ids) atomicAdd(n_bad_ids, 1);
+    }
 }
 
 }  // namespace
@@ -1281,6 +1344,18 @@ hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const Scor
     const float* zsel = (const float*)((const unsigned char*)workspace + p.zsel_off);
     const float* upart = p.entropy ? (const float*)((const unsigned char*)workspace + p.upart_off)
                                    : nullptr;
+    // small batches: one block per token, every chunk pair staged in LDS
+    const size_t token_lds = (size_t)p.nchunks * (sizeof(float2) + (p.entropy ? sizeof(float) : 0));
+    if (p.narrow && token_lds <= kMergeTokenLdsMax) {
+        auto gt = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)p.n), dim3(512), token_lds, st, part, upart,
+                               zsel, ids, p.n, p.nchunks, p.v, sc.c2, sc.it, logp, lse, entropy,
+                               n_bad_ids);
+        };
+        if (p.entropy) gt(lse_merge_token_kernel<true>);
+        else gt(lse_merge_token_kernel<false>);
+        return hipGetLastError();
+    }
     const int64_t blocks = (p.n + 63) / 64;
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0, st, part, upart,

@@ -12,6 +12,13 @@ namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The tile kernels address an operand tile of `rows` rows through a buffer
+// descriptor whose extent, (rows - 1) * ld_bytes + k_bytes, and per-lane
+// 32-bit offsets must stay below 2^31.
+inline bool tile_extent_ok(int64_t rows, int64_t ld_bytes, int64_t k_bytes) {
+    return (rows - 1) * ld_bytes + k_bytes < ((int64_t)1 << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,6 +56,9 @@ int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
     if (d % 64 != 0) return TIM_EUNSUPPORTED;
     if ((ldh * esz) % 16 != 0 || (ldw * esz) % 16 != 0) return TIM_EUNSUPPORTED;
     if (!aligned(h, 16) || !aligned(w, 16)) return TIM_EUNSUPPORTED;
+    if (!tile_extent_ok(tim::kTileT, ldh * esz, d * esz) ||
+        !tile_extent_ok(tim::kTileV, ldw * esz, d * esz))
+        return TIM_EUNSUPPORTED;
     tim::LogprobPlan p;
     if (!tim::make_logprob_plan(n, d, v, dtype, flags, false, &p)) return TIM_EINVAL;
     if (p.nchunks * p.nttiles > INT32_MAX) return TIM_EUNSUPPORTED;
@@ -120,6 +130,9 @@ int tim_logprob_forward_ex(const void* h, int64_t ldh, const void* w, int64_t ld
     if (d % 64 != 0) return TIM_EUNSUPPORTED;
     if ((ldw * esz) % 16 != 0 || !aligned(w, 16)) return TIM_EUNSUPPORTED;
     if (!prm->norm_gamma && ((ldh * esz) % 16 != 0 || !aligned(h, 16))) return TIM_EUNSUPPORTED;
+    if (!tile_extent_ok(tim::kTileT, (prm->norm_gamma ? d : ldh) * esz, d * esz) ||
+        !tile_extent_ok(tim::kTileV, ldw * esz, d * esz))
+        return TIM_EUNSUPPORTED;
     tim::LogprobPlan p;
     size_t norm_off = 0, total = 0;
     if (!ex_layout(n, d, v, dtype, flags, prm, entropy != nullptr, &p, &norm_off, &total))
@@ -250,6 +263,12 @@ int tim_logprob_backward(const void* h, int64_t ldh, const void* w, int64_t ldw,
     if (n > INT32_MAX) return TIM_EUNSUPPORTED;
     tim::BackwardPlan p;
     if (!tim::make_backward_plan(n, d, v, &p)) return TIM_EINVAL;
+    // the three GEMMs: W and h tiles (K = D), dz and W^T tiles (K = Vp, rows
+    // of Vp bf16), dz^T and h^T tiles (K = Np, rows of Np bf16)
+    if (!tile_extent_ok(tim::kTileV, ldw * 2, d * 2) || !tile_extent_ok(tim::kTileT, ldh * 2, d * 2) ||
+        !tile_extent_ok(tim::kTileV, p.vpad * 2, p.vpad * 2) ||
+        !tile_extent_ok(tim::kTileV, p.npad * 2, p.npad * 2))
+        return TIM_EUNSUPPORTED;
     if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
     if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
     if (n == 0) {

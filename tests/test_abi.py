@@ -278,3 +278,25 @@ def test_binding_norm_and_ex_refuse_host_tensors():
     with pytest.raises(ValueError):
         tim.tim_logprob_forward_ex(x, torch.zeros(10, 64, dtype=torch.bfloat16),
                                    torch.zeros(4, dtype=torch.int32), temperature=0.7)
+
+
+def test_buffer_extent_limits_are_refused_before_any_launch(lib):
+    """A 256-row operand tile is addressed through a buffer descriptor with
+    a 32-bit extent and 32-bit per-lane offsets: sizes whose tile would
+    reach 2^31 bytes are refused on the host."""
+    big_ld = (1 << 31) // 255 // 2 + 64            # bf16 elements: 255 rows past 2^31
+    big_ld -= big_ld % 64
+    assert 255 * big_ld * 2 + 64 * 2 >= 1 << 31
+    assert _fwd(lib, ldh=big_ld) == tim.TIM_EUNSUPPORTED
+    assert _fwd(lib, ldw=big_ld) == tim.TIM_EUNSUPPORTED
+    ok_ld = big_ld - 1024                           # just below: accepted by the check
+    assert 255 * ok_ld * 2 + 64 * 2 < 1 << 31
+    assert _fwd(lib, ldh=ok_ld, wsb=16) == tim.TIM_EWORKSPACE     # gets past it
+    assert _fwdx(lib, ldw=big_ld) == tim.TIM_EUNSUPPORTED
+    bwd = lambda **kw: lib.tim_logprob_backward(
+        FAKE, kw.get("ldh", 64), FAKE, kw.get("ldw", 64), FAKE, FAKE, FAKE, kw.get("n", 4),
+        64, kw.get("v", 100), 0, 0, FAKE, FAKE, FAKE, 1 << 62, None)
+    # dW = dz^T h has K = tokens (rows of Np bf16), dh = dz W has K = vocabulary
+    assert bwd(n=(1 << 22)) == tim.TIM_EUNSUPPORTED               # 512 Np >= 2^31
+    assert bwd(v=(1 << 22)) == tim.TIM_EUNSUPPORTED
+    assert bwd(ldh=big_ld) == tim.TIM_EUNSUPPORTED

@@ -128,35 +128,56 @@ def test_ragged_shapes(n, d, v, dtype):
         assert torch.all(logp == 0)
 
 
-def test_qwen3_8b_shape_sampled_rows():
+def tile_slot_rows(n, k, seed):
+    """About k rows of [0, n): every slot of the 256-token tile once (in a
+    seeded random tile), the first and last row of every tile, then seeded
+    random rows up to k."""
+    rng = np.random.default_rng(seed)
+    tiles = (n + 255) // 256
+    rows = {int(rng.integers(0, tiles)) * 256 + s for s in range(256)}
+    rows.update(t * 256 for t in range(tiles))
+    rows.update(min(n - 1, t * 256 + 255) for t in range(tiles))
+    rows = {r for r in rows if r < n}
+    while len(rows) < k:
+        rows.add(int(rng.integers(0, n)))
+    return sorted(rows)
+
+
+def test_qwen3_8b_shape_512_oracle_rows():
     w = wl("qwen3_8b")
     say("qwen3_8b forward")
     logp = tim.tim_logprob_forward(w.h, w.w, w.ids)
     torch.cuda.synchronize()
-    rows = spread_rows(w.n, 20, 2, extra=[511, 512, 4095, 4096, 8191])
+    rows = tile_slot_rows(w.n, 512, 2)
+    assert len(rows) >= 512 and {r % 256 for r in rows} == set(range(256))
     check_rows(w.h, w.w, w.ids, logp, rows, "qwen3_8b",
                h_host=host("qwen3_8b", "h"), w_host=host("qwen3_8b", "w"))
 
 
-def test_dsv3_shape_sampled_rows():
+def test_dsv3_shape_256_oracle_rows_with_every_sequence_boundary():
     w = wl("dsv3")
     say("dsv3 forward")
     logp = tim.tim_logprob_forward(w.h, w.w, w.ids)
     torch.cuda.synchronize()
     cu = w.cu_seqlens.cpu().numpy()
-    ends = [cu[j] for j in range(0, 64, 8)] + [cu[j + 1] - 1 for j in range(3, 64, 8)]
-    rows = spread_rows(w.n, 6, 3, extra=ends)
-    check_rows(w.h, w.w, w.ids, logp, rows, "dsv3",
+    ends = [int(cu[j]) for j in range(64)] + [int(cu[j + 1]) - 1 for j in range(64)]
+    rng = np.random.default_rng(3)
+    rows = set(ends)
+    while len(rows) < 256:
+        rows.add(int(rng.integers(0, w.n)))
+    check_rows(w.h, w.w, w.ids, logp, sorted(rows), "dsv3",
                h_host=host("dsv3", "h"), w_host=host("dsv3", "w"))
     assert torch.all(torch.isfinite(logp))
 
 
-def test_fp32_head_sampled_rows_and_bf16_rerun():
+def test_fp32_head_128_oracle_rows_and_bf16_rerun():
     w = wl("fp32_head")
     say("fp32_head forward (fp32 MFMA)")
     logp32 = tim.tim_logprob_forward(w.h, w.w, w.ids)
     torch.cuda.synchronize()
-    rows = spread_rows(w.n, 12, 4, extra=[4095])
+    rows = tile_slot_rows(w.n, 128, 4)[::3][:96] + spread_rows(w.n, 40, 4, extra=[4095])
+    rows = sorted(set(rows))
+    assert len(rows) >= 128
     check_rows(w.h, w.w, w.ids, logp32, rows, "fp32_head",
                h_host=host("fp32_head", "h"), w_host=host("fp32_head", "w"))
     say("fp32_head rows rounded to bf16")
@@ -174,20 +195,22 @@ def test_fp32_head_sampled_rows_and_bf16_rerun():
 # closed forms on the GPU path
 # ---------------------------------------------------------------------------
 
-def test_equal_logits_and_bad_ids():
-    n, d, v = 70, 128, 151936
+@pytest.mark.parametrize("n", [70, 20, 3])      # 256-token kernel; small-batch kernel, 2 and 1 blocks
+def test_equal_logits_and_bad_ids(n):
+    d, v = 128, 151936
     h = torch.randn(n, d, device=DEV).to(torch.bfloat16)
     w = torch.zeros(v, d, device=DEV, dtype=torch.bfloat16)
     ids = torch.randint(0, v, (n,), device=DEV, dtype=torch.int32)
-    ids[3] = -100
-    ids[10] = v
-    say("equal logits")
+    bad = [1, 2] if n < 10 else [3, 10]
+    ids[bad[0]] = -100
+    ids[bad[1]] = v
+    say(f"equal logits, n={n}")
     logp, lse, nbad = tim.tim_logprob_forward(h, w, ids, return_lse=True)
     torch.cuda.synchronize()
     good = torch.ones(n, dtype=torch.bool)
-    good[[3, 10]] = False
+    good[bad] = False
     lp = logp.cpu()
-    assert torch.isnan(lp[3]) and torch.isnan(lp[10]) and int(nbad.item()) == 2
+    assert torch.isnan(lp[bad[0]]) and torch.isnan(lp[bad[1]]) and int(nbad.item()) == 2
     assert torch.all((lp[good].double() + math.log(v)).abs() < 2e-5)
     assert torch.all(torch.isfinite(lse))
 
@@ -250,6 +273,60 @@ def test_qwen3_8b_batch_invariance_sweep():
     say("qwen3_8b random partition")
     got = _sliced(w.h, w.w, w.ids, workloads.random_slices(w.n, 17))
     assert torch.equal(got.view(torch.int32).cpu(), full_bits)
+
+
+def test_qwen3_8b_small_batches_through_both_narrow_widths():
+    """Batches of 16 and fewer tokens take one token block per wave of the
+    small-batch kernel, 17..32 two; both must give the full batch's bits."""
+    w = wl("qwen3_8b")
+    full = tim.tim_logprob_forward(w.h, w.w, w.ids)
+    torch.cuda.synchronize()
+    full_bits = full.view(torch.int32).cpu()
+    for b in (16, 17, 31, 32, 33):
+        say(f"qwen3_8b sliced in batches of {b} (first 2048 rows)")
+        got = _sliced(w.h[:2048], w.w, w.ids[:2048], workloads.sweep_slices(2048, b))
+        diff = int((got.view(torch.int32).cpu() != full_bits[:2048]).sum())
+        assert diff == 0, f"batch {b}: {diff} rows differ"
+
+
+@pytest.mark.parametrize("name,sizes", [("dsv3", (1, 7, 64, 1000, 32768)),
+                                        ("small", (1, 7, 17, 64, 1000, 2048))])
+def test_batch_invariance_sweep_other_shapes(name, sizes):
+    w = wl(name)
+    say(f"{name} full batch (reference bits)")
+    full = tim.tim_logprob_forward(w.h, w.w, w.ids)
+    torch.cuda.synchronize()
+    full_bits = full.view(torch.int32).cpu()
+    for b in sizes:
+        say(f"{name} sliced in batches of {b}")
+        got = _sliced(w.h, w.w, w.ids, workloads.sweep_slices(w.n, b))
+        diff = int((got.view(torch.int32).cpu() != full_bits).sum())
+        assert diff == 0, f"{name} batch {b}: {diff} rows differ"
+    say(f"{name} random partition")
+    got = _sliced(w.h, w.w, w.ids, workloads.random_slices(w.n, 23))
+    assert torch.equal(got.view(torch.int32).cpu(), full_bits)
+
+
+def test_side_stream_gives_the_default_stream_bits():
+    """Calls on a caller's side stream: inputs written on the current stream
+    are waited for, and outputs equal the default-stream call bit for bit."""
+    w = wl("small")
+    ref = tim.tim_logprob_forward(w.h, w.w, w.ids)
+    ref_st = tim.tim_mismatch_stats(ref, w.logp_rollout, w.mask, w.cu_seqlens,
+                                    tis_clip=w.spec.clip_c, seq_bounds=(w.spec.seq_lo, w.spec.seq_hi))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    h2 = w.h * 1                                  # written on the current stream just before
+    got = tim.tim_logprob_forward(h2, w.w, w.ids, stream=side)
+    got_st = tim.tim_mismatch_stats(got, w.logp_rollout, w.mask, w.cu_seqlens,
+                                    tis_clip=w.spec.clip_c,
+                                    seq_bounds=(w.spec.seq_lo, w.spec.seq_hi), stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(got_st["batch"], ref_st["batch"])
+    for k in ref_st["seq"]:
+        assert torch.equal(got_st["seq"][k], ref_st["seq"][k]), k
 
 
 def test_same_row_in_different_tile_slots_and_shuffled_order():

@@ -202,7 +202,7 @@ def test_ex_rows_do_not_depend_on_the_batch():
     full = tim.tim_logprob_forward_ex(x, w, ids, **kw)
     again = tim.tim_logprob_forward_ex(x, w, ids, **kw)
     parts = [tim.tim_logprob_forward_ex(x[a:b].contiguous(), w, ids[a:b].contiguous(), **kw)
-             for a, b in ((0, 1), (1, 257), (257, 520))]
+             for a, b in ((0, 1), (1, 21), (21, 257), (257, 520))]
     # the fused norm equals the norm followed by the head
     hn = tim.tim_rmsnorm(x, g, eps=EPS)
     sep = tim.tim_logprob_forward_ex(hn, w, ids, temperature=0.7, entropy=True)
