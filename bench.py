@@ -28,7 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_mfma_counters.json")
 METRIC = "selected-token logprobs/s at D=4096,V=151936 (bf16) + MFMA util; batch-invariant"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_bf16_qwen3_8b_counters.json")
 # the sources the head kernel is built from (its tiles, pipeline and chunking)
@@ -90,6 +92,10 @@ def main():
                     help="only the tempered / entropy / RMSNorm scoring measurements")
     ap.add_argument("--ppo-scale-only", action="store_true",
                     help="run only the surrogate at 2^stats-log2 tokens (for a kernel trace)")
+    ap.add_argument("--mfma-from", nargs=2, metavar=("COUNTER_CSV", "KERNEL_TRACE_CSV"),
+                    help="turn a rocprofv3 --pmc MfmaUtil ... pass of --profile-pass (counter "
+                         "and kernel-trace CSV) into the matrix-unit summary and exit")
+    ap.add_argument("--mfma-out", default=MFMA_SUMMARY)
     ap.add_argument("--traffic-out", default=PMC_SUMMARY)
     ap.add_argument("--traffic-command", default="",
                     help="the commands that made the CSV files, recorded in the summary")
@@ -97,6 +103,9 @@ def main():
     if args.traffic_from:
         write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_out,
                       args.traffic_command)
+        return
+    if args.mfma_from:
+        write_mfma(args.mfma_from[0], args.mfma_from[1], args.mfma_out, args.traffic_command)
         return
     if args.profile_pass:
         args.no_extras = True
@@ -187,6 +196,9 @@ def main():
         f"stats avg {np.mean(t_st) * 1e3:.1f} us, {achieved:.1f} TFLOP/s")
     bsum = tim.batch_dict(res["batch"])
     log(f"is_approx_k3_kl {bsum['is_approx_k3_kl']:.3e}, reject_frac {bsum['reject_frac']}")
+    if args.profile_pass:
+        # the fp32 head's kernel in the same counter pass
+        fp32_head_measure(tim, workloads, torch, np, reps=3, compare_bf16=False)
 
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -199,11 +211,14 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(f"{name}:N={n}"),
                      "kernel": "lmhead8w_kernel (bf16) + lse_merge (one forward call)",
-                     "flops_per_launch": flops, "avg_launch_ms": lp_avg},
+                     "flops_per_launch": flops, "avg_launch_ms": lp_avg,
+                     **measured_mfma(LMHEAD_KERNEL)},
         "stats_step_us": float(np.mean(t_st)) * 1e3,
     }
 
     if not args.no_extras:
+        out["fp32_head"] = fp32_head_measure(tim, workloads, torch, np)
+        out["small_batch"] = small_batch_measure(tim, wl, torch, np)
         out["scoring_ex"] = scoring_ex_measure(tim, workloads, wl, torch, np)
         out["backward"] = backward_measure(tim, wl, torch, np)
         out["ppo"] = ppo_scale(tim, torch, np, args.stats_log2)
@@ -218,9 +233,135 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def fp32_head_measure(tim, workloads, torch, np, reps=5, compare_bf16=True):
+    """The fp32 LM head (fp32 h and W, fp32 MFMA; N = 4096 in 8 sequences of
+    512, D = 4096, V = 151936) against the fp32 matrix peak, and the same
+    rows rounded to bf16 through the bf16 kernel: the distribution of
+    |logp_bf16 - logp_fp32| over all 4096 tokens."""
+    wl = workloads.make("fp32_head", device="cuda")
+    sp = wl.spec
+    n, d, v = sp.n, sp.d, sp.v
+    lt = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = torch.empty(tim.logprob_workspace_bytes(n, d, v, tim.TIM_F32), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: tim.tim_logprob_forward(wl.h, wl.w, wl.ids, out=lt, workspace=ws)
+    ms = time_calls(fn, torch, np, reps=reps, warm=1)
+    flops = 2.0 * n * d * v
+    tf = flops / (ms / 1e3) / 1e12
+    log(f"fp32 head: {ms:.3f} ms, {tf:.1f} TFLOP/s ({tf / PEAK_F32_MFMA_TFLOPS:.1%} of fp32 MFMA peak)")
+    res = {"workload": sp.desc, "ms": ms, "flops": flops, "achieved_TFLOPs": tf,
+           "peak_TFLOPs": PEAK_F32_MFMA_TFLOPS, "frac": tf / PEAK_F32_MFMA_TFLOPS,
+           "tokens_per_s": n / (ms / 1e3), "kernel": "lmhead_partials_kernel (fp32) + lse_merge",
+           **measured_mfma(LMHEAD_F32_KERNEL)}
+    if compare_bf16:
+        hb, wb = wl.h.to(torch.bfloat16), wl.w.to(torch.bfloat16)
+        l16 = tim.tim_logprob_forward(hb, wb, wl.ids)
+        dd = (l16.double() - lt.double()).abs().cpu().numpy()
+        res["bf16_vs_fp32_abs_dlogp"] = {"tokens": n, "mean": float(dd.mean()),
+                                         "p99": float(np.quantile(dd, 0.99)),
+                                         "max": float(dd.max())}
+        log(f"|logp_bf16 - logp_fp32|: mean {dd.mean():.3e} p99 {np.quantile(dd, 0.99):.3e} "
+            f"max {dd.max():.3e}")
+        del hb, wb, l16
+    del wl, ws, lt
+    torch.cuda.empty_cache()
+    return res
+
+
+SMALL_BATCHES = (1, 7, 16, 32, 64)
+
+
+def small_batch_measure(tim, wl, torch, np):
+    """The forward on the first b rows of the workload: at these sizes the
+    call is bound by reading W once (V D 2 bytes), so it is reported as a
+    fraction of HBM bandwidth."""
+    sp = wl.spec
+    res = {}
+    wbytes = 2.0 * sp.v * sp.d
+    for b in SMALL_BATCHES:
+        h, ids = wl.h[:b], wl.ids[:b]
+        out = torch.empty(b, dtype=torch.float32, device="cuda")
+        ws = torch.empty(tim.logprob_workspace_bytes(b, sp.d, sp.v, tim.TIM_BF16),
+                         dtype=torch.uint8, device="cuda")
+        ms = time_calls(lambda: tim.tim_logprob_forward(h, wl.w, ids, out=out, workspace=ws),
+                        torch, np, reps=20)
+        gbs = wbytes / (ms / 1e3) / 1e9
+        res[str(b)] = {"ms": ms, "w_bytes": wbytes, "achieved_GBs": gbs,
+                       "frac_hbm": gbs / PEAK_HBM_GBS}
+        log(f"small batch b={b}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s of W ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    return res
+
+
+def measured_mfma(kernel_key):
+    """Matrix-unit counters of one kernel from the committed summary, or {}
+    if absent or taken on a different kernel source."""
+    try:
+        with open(MFMA_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if s.get("kernel_source_sha256_16") != source_digest(LMHEAD_SRC):
+        return {}
+    k = s.get("kernels", {}).get(kernel_key)
+    if not k:
+        return {}
+    return {"mfma_busy": k["mfma_util"], "clock_ghz": k.get("clock_ghz"),
+            "mfma_counters": os.path.relpath(MFMA_SUMMARY, ROOT)}
+
+
+def write_mfma(counter_csv, trace_csv, out_path, command):
+    """Per-kernel matrix-unit utilisation (rocprofv3's MfmaUtil: MFMA-busy
+    cycles summed over SIMDs / (GUI-active cycles x SIMDs)), the GUI-active
+    cycles per XCC divided by the kernel's duration (the clock it ran at), and
+    the MFMA work the counters saw against the algorithmic 2 N D V."""
+    import csv
+
+    import numpy as np
+    vals = {}
+    with open(counter_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            for key in (LMHEAD_KERNEL, LMHEAD_F32_KERNEL):
+                if key in name:
+                    d = vals.setdefault(key, {}).setdefault(row.get("Dispatch_Id", ""), {})
+                    d[row["Counter_Name"]] = float(row["Counter_Value"])
+    durs = {}
+    with open(trace_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            for key in (LMHEAD_KERNEL, LMHEAD_F32_KERNEL):
+                if key in row["Kernel_Name"]:
+                    durs.setdefault(key, []).append(
+                        (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e9)
+    summary = {"command": command, "kernel_source_sha256_16": source_digest(LMHEAD_SRC),
+               "definition": "mfma_util = sum of SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE "
+                             "x SIMD count) (rocprofv3 MfmaUtil); clock_ghz = GRBM_GUI_ACTIVE "
+                             "summed over the 8 XCDs / 8 / kernel duration",
+               "kernels": {}}
+    algo = {LMHEAD_KERNEL: 2.0 * 8192 * 4096 * 151936, LMHEAD_F32_KERNEL: 2.0 * 4096 * 4096 * 151936}
+    for key, dispatches in vals.items():
+        util = [d["MfmaUtil"] for d in dispatches.values() if "MfmaUtil" in d]
+        gui = [d["GRBM_GUI_ACTIVE"] for d in dispatches.values() if "GRBM_GUI_ACTIVE" in d]
+        mops = [d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+                for d in dispatches.values()]
+        dur = sorted(durs.get(key, []))
+        k = {"dispatches": len(dispatches), "mfma_util": float(np.mean(util)) / 100.0 if util else None,
+             "mfma_flops_per_dispatch": float(np.mean(mops)) * 512 if mops else None,
+             "algorithmic_flops": algo[key]}
+        if gui and dur:
+            med = dur[len(dur) // 2]
+            k["duration_ms_median"] = med * 1e3
+            k["clock_ghz"] = float(np.mean(gui)) / 8 / med / 1e9
+        summary["kernels"][key] = k
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    print(json.dumps(summary, indent=1))
+
+
 COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration kernel
 COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
 LMHEAD_KERNEL = "lmhead8w_kernel<false>"
+LMHEAD_F32_KERNEL = "lmhead_partials_kernel<false>"
 STATS_KERNEL = "stats_stream_kernel"
 EXTRAS_KERNEL = "xsel_pass_kernel"
 
@@ -530,15 +671,35 @@ def ppo_scale(tim, torch, np, log2n):
 
 
 def invariance_cost(tim, wl, torch, np):
-    """t(invariant) / t(free) - 1 for the forward at several batch sizes."""
+    """t(invariant) / t(schedule) - 1 for the forward at several batch sizes,
+    against the free schedule (the fastest configuration the library has for
+    that N, allowed to depend on N) and against the K-split schedule (an
+    N-dependent split with its own merge, at 33..256 tokens).  The schedules
+    are timed alternately, 5 rounds of 4 calls each; the median is kept."""
     res = {}
-    for b in (1, 7, 64, 1000, 8192):
+    for b in (1, 7, 64, 256, 1000, 8192):
         h, ids = wl.h[:b], wl.ids[:b]
-        ti = time_calls(lambda: tim.tim_logprob_forward(h, wl.w, ids), torch, np, reps=5)
-        tf = time_calls(lambda: tim.tim_logprob_forward(h, wl.w, ids, schedule="free"),
-                        torch, np, reps=5)
-        res[str(b)] = {"invariant_ms": ti, "free_ms": tf, "cost": ti / tf - 1.0}
-        log(f"invariance cost b={b}: {ti:.3f} ms vs {tf:.3f} ms ({ti / tf - 1:+.1%})")
+        t = {}
+        for sch in ("invariant", "free", "split_k"):
+            ws = torch.empty(tim.logprob_workspace_bytes(b, wl.spec.d, wl.spec.v, tim.TIM_BF16,
+                                                         sch), dtype=torch.uint8, device="cuda")
+            t[sch] = (ws, [])
+        for _ in range(5):
+            for sch, (ws, times) in t.items():
+                times.append(time_calls(
+                    lambda: tim.tim_logprob_forward(h, wl.w, ids, schedule=sch, workspace=ws),
+                    torch, np, reps=4, warm=1))
+        ms = {sch: float(np.median(times)) for sch, (_, times) in t.items()}
+        split_used = 32 < b <= 256
+        res[str(b)] = {"invariant_ms": ms["invariant"], "free_ms": ms["free"],
+                       "cost": ms["invariant"] / ms["free"] - 1.0,
+                       "split_k_ms": ms["split_k"] if split_used else None,
+                       "cost_vs_split_k": ms["invariant"] / ms["split_k"] - 1.0 if split_used else None}
+        log(f"invariance cost b={b}: invariant {ms['invariant']:.3f} ms, free {ms['free']:.3f} ms "
+            f"({ms['invariant'] / ms['free'] - 1:+.1%})"
+            + (f", K split {ms['split_k']:.3f} ms ({ms['invariant'] / ms['split_k'] - 1:+.1%})"
+               if split_used else ""))
+        del t
     return res
 
 
@@ -570,7 +731,12 @@ def cpu_baseline(wl, np, rows):
     t_st = time.perf_counter() - t
     per_token = t_lp / rows + t_st / wl.spec.n
     log(f"cpu baseline: {rows / t_lp:.2f} rows/s logprob, stats {t_st * 1e3:.1f} ms")
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": used, "kind": "oracle",
+    host_cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: {used} oracle threads on a host with {host_cores} cores available "
+        f"to this process ({os.cpu_count()} online)")
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": used,
+            "host_cores_affinity": host_cores, "host_cpus_online": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{rows} of {wl.spec.n} rows of the workload (fp64 logprob, evenly "
                       f"spaced) + stats over all {wl.spec.n} tokens; full-N time extrapolated "
                       f"from the sample", "logprob_rows_per_s": rows / t_lp,

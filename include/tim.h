@@ -84,9 +84,20 @@ typedef enum {
 enum {
     TIM_SCHED_INVARIANT = 0u, /* vocabulary split and tile order are functions
                                  of (V, D, dtype) only: batch invariant      */
-    TIM_SCHED_FREE = 1u       /* split chosen from N for speed; results are
-                                 deterministic for a fixed N but NOT batch
-                                 invariant.  Exists to price invariance.     */
+    TIM_SCHED_FREE = 1u,      /* the fastest configuration this library has
+                                 for the given N, allowed to depend on N
+                                 (deterministic for a fixed N, not promised
+                                 batch invariant).  On gfx950 that is the
+                                 invariant one for bf16 at every N measured
+                                 (the K split below is slower); for fp32 the
+                                 vocabulary chunks grow as N shrinks.  Exists
+                                 to price invariance.                        */
+    TIM_SCHED_SPLIT_K = 2u    /* bf16, 33..256 tokens, no entropy: K split in
+                                 two halves over twice the workgroups, the
+                                 partial logits added, then folded.  Depends
+                                 on N (not batch invariant); an N-dependent
+                                 schedule against which invariance is priced.
+                                 Other sizes: as TIM_SCHED_FREE.             */
 };
 
 /* Library version of this header (TIM_ABI_VERSION). */
@@ -126,7 +137,7 @@ size_t tim_logprob_workspace_bytes(int64_t n, int64_t d, int64_t v,
  *  d          hidden size, > 0, d % 64 == 0 (else TIM_EUNSUPPORTED).
  *  v          vocabulary size, 1 <= v <= 2^31 - 1.
  *  dtype      TIM_BF16 or TIM_F32.
- *  flags      TIM_SCHED_INVARIANT or TIM_SCHED_FREE.
+ *  flags      TIM_SCHED_INVARIANT, TIM_SCHED_FREE or TIM_SCHED_SPLIT_K.
  *  logp       [n] fp32 out.
  *  lse        [n] fp32 out, nullable: log sum_v exp z[t,v].
  *  n_bad_ids  [1] int32 out, nullable: number of ids outside [0, v).

@@ -49,7 +49,9 @@ from .build import LIB_PATH
 
 TIM_OK, TIM_EINVAL, TIM_EUNSUPPORTED, TIM_EWORKSPACE, TIM_EHIP = range(5)
 TIM_BF16, TIM_F32 = 0, 1
-TIM_SCHED_INVARIANT, TIM_SCHED_FREE = 0, 1
+TIM_SCHED_INVARIANT, TIM_SCHED_FREE, TIM_SCHED_SPLIT_K = 0, 1, 2
+_SCHEDULES = {"invariant": TIM_SCHED_INVARIANT, "free": TIM_SCHED_FREE,
+              "split_k": TIM_SCHED_SPLIT_K}
 
 # Names of the batch aggregate vector, in TIM_B_* index order.  The
 # is_approx_k3_kl / is_clip_ratio / is_nan_ratio names are the monitoring
@@ -251,7 +253,7 @@ _DTYPES = {torch.bfloat16: TIM_BF16, torch.float32: TIM_F32}
 
 
 def logprob_workspace_bytes(n: int, d: int, v: int, dtype: int, schedule: str = "invariant") -> int:
-    flags = TIM_SCHED_FREE if schedule == "free" else TIM_SCHED_INVARIANT
+    flags = _SCHEDULES[schedule]
     return int(load_library().tim_logprob_workspace_bytes(n, d, v, dtype, flags))
 
 
@@ -286,7 +288,7 @@ def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
     if d2 != d or ids.shape[0] != n:
         raise ValueError(f"shape mismatch: h {tuple(h.shape)}, w {tuple(w.shape)}, ids {tuple(ids.shape)}")
     dtype = _DTYPES[h.dtype]
-    flags = {"invariant": TIM_SCHED_INVARIANT, "free": TIM_SCHED_FREE}[schedule]
+    flags = _SCHEDULES[schedule]
     dev = h.device
     logp = out if out is not None else torch.empty(n, dtype=torch.float32, device=dev)
     lse = torch.empty(n, dtype=torch.float32, device=dev) if return_lse else None
@@ -335,7 +337,7 @@ def tim_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, *, eps: float = 1e-6,
 def logprob_ex_workspace_bytes(n: int, d: int, v: int, dtype: int, *, temperature: float = 1.0,
                                norm: bool = False, entropy: bool = False,
                                schedule: str = "invariant") -> int:
-    flags = TIM_SCHED_FREE if schedule == "free" else TIM_SCHED_INVARIANT
+    flags = _SCHEDULES[schedule]
     prm = _ForwardParams(float(temperature), 1 if norm else None, 1e-6)
     return int(load_library().tim_logprob_ex_workspace_bytes(n, d, v, dtype, flags,
                                                              ctypes.byref(prm), int(entropy)))
@@ -369,7 +371,7 @@ def tim_logprob_forward_ex(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, 
         if norm_gamma.dtype != h.dtype or norm_gamma.shape != (d,) or not norm_gamma.is_contiguous():
             raise ValueError("norm_gamma must be a contiguous [D] tensor of h's dtype")
     dtype = _DTYPES[h.dtype]
-    flags = {"invariant": TIM_SCHED_INVARIANT, "free": TIM_SCHED_FREE}[schedule]
+    flags = _SCHEDULES[schedule]
     dev = h.device
     res = {"logp": torch.empty(n, dtype=torch.float32, device=dev),
            "lse": torch.empty(n, dtype=torch.float32, device=dev),

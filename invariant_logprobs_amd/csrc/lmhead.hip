@@ -89,9 +89,8 @@ constexpr float kArgFloor = -3.0e38f;
 // W and h stages in that XCD's L2.  Changes only who computes a tile, never
 // how: results are unaffected.
 constexpr int kGroupChunks = 4;
-__device__ __forceinline__ void tile_of_block(int64_t nchunks, int64_t nttiles,
-                                              int64_t& chunk, int64_t& ttile) {
-    const int64_t G = gridDim.x, b = blockIdx.x;
+__device__ __forceinline__ void tile_of_block(int64_t b, int64_t G, int64_t nchunks,
+                                              int64_t nttiles, int64_t& chunk, int64_t& ttile) {
     const int64_t per = G >> 3, rem = G & 7, x = b & 7, i = b >> 3;
     const int64_t L = x * per + (x < rem ? x : rem) + i;
     const int64_t span = (int64_t)kGroupChunks * nttiles;
@@ -127,7 +126,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     if (blockIdx.x == 0 && tid == 0 && n_bad_ids) *n_bad_ids = 0;
 
     int64_t chunk, ttile;
-    tile_of_block(nchunks, nttiles, chunk, ttile);
+    tile_of_block(blockIdx.x, gridDim.x, nchunks, nttiles, chunk, ttile);
     const int64_t t0 = ttile * kTileT;
     const int64_t vt_first = chunk * chunk_tiles;
     const int ntiles_here = (int)((nvtiles - vt_first) < chunk_tiles ? (nvtiles - vt_first)
@@ -649,7 +648,13 @@ __device__ __forceinline__ void merge_row_groups(float (&m_run)[NB], float (&s_r
 // stage issues the same instructions, so the counts hold everywhere.  The
 // look-ahead reads of the last stage are waited for right after the K loop,
 // so that none of the fragment registers is live in the epilogue.
-template <bool kEnt>
+//
+// kStore (the K-split schedule, never the batch-invariant path): the
+// grid holds ksplit copies of the tile grid, copy s computing stages
+// s nk .. (s + 1) nk - 1 of K (nk is per copy), and the epilogue stores the
+// partial logits to slog[s][v][n] instead of folding them; a separate kernel
+// adds the copies and folds.
+template <bool kEnt, bool kStore = false>
 __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
@@ -657,7 +662,8 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                 const int32_t* __restrict__ ids, int64_t n, int64_t v,
                 int nk, int64_t nchunks, int64_t nttiles, float c2,
                 float2* __restrict__ part, float* __restrict__ upart,
-                float* __restrict__ zsel, int32_t* __restrict__ n_bad_ids) {
+                float* __restrict__ zsel, int32_t* __restrict__ n_bad_ids,
+                float* __restrict__ slog) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -671,9 +677,17 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     if (blockIdx.x == 0 && tid == 0 && n_bad_ids) *n_bad_ids = 0;
 
     int64_t chunk, ttile;
-    tile_of_block(nchunks, nttiles, chunk, ttile);
+    const int64_t tiles = nchunks * nttiles;
+    const int64_t split = kStore ? (int64_t)blockIdx.x / tiles : 0;
+    tile_of_block(kStore ? (int64_t)blockIdx.x % tiles : (int64_t)blockIdx.x,
+                  kStore ? tiles : (int64_t)gridDim.x, nchunks, nttiles, chunk, ttile);
     const int64_t t0 = ttile * kTileT;
     const int64_t vbase = chunk * kTileV;
+    if constexpr (kStore) {
+        // this copy's K range: move both operands' bases to its first stage
+        h += split * nk * kStageBytes;
+        w += split * nk * kStageBytes;
+    }
 
     // Copies: as in lmhead_partials_kernel, with eight waves: 8-row blocks
     // 4 wave .. 4 wave + 3 of both operands, swizzled chunks, rows past N or
@@ -835,6 +849,26 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3]),
                  "+v"(A[4]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7]));
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B0[0]), "+v"(B0[1]), "+v"(B0[2]), "+v"(B0[3]));
+
+    if constexpr (kStore) {
+        // partial logits of this K range: rows vbase + wv 128 + bi 16 + 4 grp
+        // + i, token t0 + wt 64 + bj 16 + col (16 tokens of a row group are
+        // 64 contiguous bytes)
+        float* base = slog + split * v * n;
+#pragma unroll
+        for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = vbase + wv * 128 + bi * 16 + grp * 4 + i;
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int64_t t = t0 + wt * 64 + bj * 16 + col;
+                    if (row < v && t < n) base[row * n + t] = acc[bi][bj][i];
+                }
+            }
+        wait_vmcnt<0>();
+        return;
+    }
 
     // ---- epilogue: online log-sum-exp + gather over the tile
     float m_run[4], s_run[4], u_run[4], zsel_reg[4];
@@ -1081,6 +1115,35 @@ lmhead_narrow_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     }
 }
 
+// The K-split schedule: adds the ksplit partial logits of each row
+// (in ascending copy order) and folds a chunk's 256 rows into (max, sum-exp)
+// per token, keeping the selected logit.  One thread per token, a block per
+// (chunk, 64 tokens); the row loads do not depend on the fold, so they run
+// ahead of it.
+__global__ void __launch_bounds__(64)
+splitk_combine_kernel(const float* __restrict__ slog, int ksplit,
+                      const int32_t* __restrict__ ids, int64_t n, int64_t v, float c2,
+                      float2* __restrict__ part, float* __restrict__ zsel) {
+    const int64_t chunk = blockIdx.x;
+    const int64_t t = (int64_t)blockIdx.y * 64 + threadIdx.x;
+    if (t >= n) return;
+    const int32_t id = ids[t];
+    const int64_t r0 = chunk * kTileV;
+    const int rows = (int)((v - r0) < kTileV ? (v - r0) : kTileV);
+    float m = -INFINITY, s = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < rows; ++r) {
+        float z = slog[(r0 + r) * n + t];
+        for (int sp = 1; sp < ksplit; ++sp) z += slog[((int64_t)sp * v + r0 + r) * n + t];
+        if (r0 + r == (int64_t)id) zsel[t] = z;
+        const float mn = fmaxf(m, z);
+        const float sc = m == mn ? 1.f : fast_exp2((m - mn) * c2);
+        s = fmaf(s, sc, fast_exp2((z - mn) * c2));
+        m = mn;
+    }
+    part[chunk * n + t] = make_float2(m, s);
+}
+
 // Merge of the vocabulary-chunk partials.  A block serves 64 tokens with
 // kMergeWaves waves: wave w folds chunks w, w + kMergeWaves, ... in ascending
 // order for its 64 tokens (coalesced 8-byte loads, kMergeUnroll in flight),
@@ -1250,7 +1313,7 @@ lse_merge_token_kernel(const float2* __restrict__ part, const float* __restrict_
 
 bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flags,
                        bool entropy, LogprobPlan* p) {
-    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != 0 && dtype != 1) || flags > 1u)
+    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != 0 && dtype != 1) || flags > 2u)
         return false;
     p->n = n; p->d = d; p->v = v; p->dtype = dtype;
     p->nvtiles = (v + kTileV - 1) / kTileV;
@@ -1268,13 +1331,20 @@ bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flag
     p->nchunks = (p->nvtiles + p->chunk_tiles - 1) / p->chunk_tiles;
     p->entropy = entropy;
     p->narrow = dtype == 0 && n >= 1 && n <= kNarrowMaxTokens;
+    // the K split (flags 2), bf16, one token tile past the small-batch
+    // kernel: twice the workgroups of half the work
+    p->ksplit = (flags == 2u && dtype == 0 && !entropy && !p->narrow && n <= kTileT &&
+                 (d / 64) % 2 == 0) ? 2 : 1;
     p->nb = n <= 16 ? 1 : 2;
     p->ntg = (int)((n + 16 * p->nb - 1) / (16 * p->nb));
     const size_t nparts = (size_t)p->nchunks * (p->narrow ? 2 : 1);
     p->part_bytes = align_up(nparts * (size_t)n * sizeof(float2), 256);
     p->zsel_off = p->part_bytes;
     p->upart_off = p->zsel_off + align_up((size_t)n * sizeof(float), 256);
-    p->total_bytes = p->upart_off + (entropy ? align_up(nparts * (size_t)n * sizeof(float), 256) : 0);
+    p->slog_off = p->upart_off + (entropy ? align_up(nparts * (size_t)n * sizeof(float), 256) : 0);
+    p->total_bytes = p->slog_off +
+                     (p->ksplit > 1 ? align_up((size_t)p->ksplit * (size_t)v * (size_t)n * sizeof(float), 256)
+                                    : 0);
     if (p->total_bytes == 0) p->total_bytes = 256;
     return true;
 }
@@ -1322,11 +1392,23 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
         }
     } else if (p.dtype == 0) {
         if (p.chunk_tiles != 1) return hipErrorInvalidValue;   // one tile per chunk
+        if (p.ksplit > 1) {
+            float* slog = (float*)((unsigned char*)workspace + p.slog_off);
+            if (grid * p.ksplit > INT32_MAX) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((lmhead8w_kernel<false, true>), dim3((unsigned)(grid * p.ksplit)),
+                               dim3(2 * kThreads), 0, st, (const unsigned char*)h, ldh * esz,
+                               (const unsigned char*)w, ldw * esz, ids, p.n, p.v, nk / p.ksplit,
+                               p.nchunks, p.nttiles, sc.c2, part, upart, zsel, n_bad_ids, slog);
+            hipLaunchKernelGGL(splitk_combine_kernel, dim3((unsigned)p.nchunks,
+                               (unsigned)((p.n + 63) / 64)), dim3(64), 0, st, slog, p.ksplit, ids,
+                               p.n, p.v, sc.c2, part, zsel);
+            return hipGetLastError();
+        }
         auto go8 = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(2 * kThreads), 0, st,
                                (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
                                ids, p.n, p.v, nk, p.nchunks, p.nttiles, sc.c2, part, upart, zsel,
-                               n_bad_ids);
+                               n_bad_ids, (float*)nullptr);
         };
         if (p.entropy) go8(lmhead8w_kernel<true>);
         else go8(lmhead8w_kernel<false>);

@@ -47,7 +47,7 @@ int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
                         unsigned flags, float* logp, float* lse, int32_t* n_bad_ids,
                         void* workspace, size_t workspace_bytes, void* stream) {
     if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != TIM_BF16 && dtype != TIM_F32) ||
-        flags > TIM_SCHED_FREE)
+        flags > TIM_SCHED_SPLIT_K)
         return TIM_EINVAL;
     if (ldh < d || ldw < d) return TIM_EINVAL;
     if (n == 0) return TIM_OK;
@@ -119,7 +119,7 @@ int tim_logprob_forward_ex(const void* h, int64_t ldh, const void* w, int64_t ld
                            float* entropy, int32_t* n_bad_ids, void* workspace,
                            size_t workspace_bytes, void* stream) {
     if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != TIM_BF16 && dtype != TIM_F32) ||
-        flags > TIM_SCHED_FREE || !prm)
+        flags > TIM_SCHED_SPLIT_K || !prm)
         return TIM_EINVAL;
     if (!(prm->temperature > 0.0) || !isfinite(prm->temperature)) return TIM_EINVAL;
     if (prm->norm_gamma && (!(prm->norm_eps >= 0.0) || !isfinite(prm->norm_eps))) return TIM_EINVAL;

@@ -39,9 +39,12 @@ struct LogprobPlan {
                           // partials per half chunk
     int nb;               // narrow: token column blocks of 16 per wave (1 or 2)
     int ntg;              // narrow: token groups of 16 nb (1 or 2)
-    // workspace: float2 part[P][n] | float zsel[n] | float upart[P][n], with
-    // P = nchunks, or 2 nchunks (one state per half chunk) when narrow
-    size_t part_bytes, zsel_off, upart_off, total_bytes;
+    int ksplit;           // K split (1: none); 2 only for TIM_SCHED_SPLIT_K, bf16,
+                          // 32 < n <= 256, no entropy
+    // workspace: float2 part[P][n] | float zsel[n] | float upart[P][n] |
+    // float slog[ksplit][v][n] (ksplit > 1 only), with P = nchunks, or
+    // 2 nchunks (one state per half chunk) when narrow
+    size_t part_bytes, zsel_off, upart_off, slog_off, total_bytes;
 };
 
 // Fills `p`; returns false for sizes the library does not accept.

@@ -52,6 +52,11 @@ def test_logprob_workspace_layout(lib):
     assert lib.tim_logprob_workspace_bytes(-1, d, v, 0, 0) == 0
     assert lib.tim_logprob_workspace_bytes(n, d, v, 7, 0) == 0
     assert lib.tim_logprob_workspace_bytes(n, d, v, 0, 5) == 0
+    # the K-split schedule keeps two partial-logit copies at 33..256 tokens
+    small = lib.tim_logprob_workspace_bytes(64, d, v, tim.TIM_BF16, tim.TIM_SCHED_INVARIANT)
+    split = lib.tim_logprob_workspace_bytes(64, d, v, tim.TIM_BF16, tim.TIM_SCHED_SPLIT_K)
+    assert split - small >= 2 * v * 64 * 4
+    assert lib.tim_logprob_workspace_bytes(64, d, v, tim.TIM_BF16, tim.TIM_SCHED_FREE) == small
     assert lib.tim_stats_workspace_bytes(1 << 20, 1000) > 0
     assert lib.tim_stats_workspace_bytes(-1, 3) == 0
 
@@ -71,7 +76,7 @@ def test_logprob_argument_errors(lib):
     assert _fwd(lib, v=0) == tim.TIM_EINVAL
     assert _fwd(lib, v=1 << 31) == tim.TIM_EINVAL
     assert _fwd(lib, dtype=2) == tim.TIM_EINVAL
-    assert _fwd(lib, flags=2) == tim.TIM_EINVAL
+    assert _fwd(lib, flags=3) == tim.TIM_EINVAL
     assert _fwd(lib, ldh=32) == tim.TIM_EINVAL
     assert _fwd(lib, ldw=63) == tim.TIM_EINVAL
     assert _fwd(lib, h=None) == tim.TIM_EINVAL

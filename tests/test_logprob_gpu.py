@@ -374,15 +374,35 @@ def test_run_to_run_determinism():
             assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
 
 
-def test_free_schedule_matches_oracle_and_is_deterministic():
+@pytest.mark.parametrize("n", [2048, 256, 200, 64, 33, 7])
+@pytest.mark.parametrize("schedule", ["free", "split_k"])
+def test_other_schedules_match_oracle_and_are_deterministic(n, schedule):
+    """The free and K-split schedules need not be batch invariant (the K
+    split is not at 33..256 tokens), but their results must still match the
+    oracle and repeat."""
     w = wl("small")
-    say("small: free schedule")
-    a = tim.tim_logprob_forward(w.h, w.w, w.ids, schedule="free")
-    b = tim.tim_logprob_forward(w.h, w.w, w.ids, schedule="free")
+    h, ids = w.h[:n], w.ids[:n]
+    say(f"small: {schedule} schedule, n={n}")
+    a = tim.tim_logprob_forward(h, w.w, ids, schedule=schedule)
+    b = tim.tim_logprob_forward(h, w.w, ids, schedule=schedule)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
-    check_rows(w.h, w.w, w.ids, a, spread_rows(w.n, 40, 9), "small free schedule",
-               h_host=host("small", "h"), w_host=host("small", "w"))
+    rows = spread_rows(n, 40, 9) if n > 64 else range(n)
+    check_rows(h, w.w, ids, a, rows, f"small {schedule} schedule n={n}",
+               h_host=host("small", "h")[:n], w_host=host("small", "w"))
+
+
+def test_split_k_schedule_at_the_qwen3_shape():
+    w = wl("qwen3_8b")
+    n = 100
+    say("qwen3_8b: K-split schedule, 100 tokens")
+    a = tim.tim_logprob_forward(w.h[:n], w.w, w.ids[:n], schedule="split_k")
+    inv = tim.tim_logprob_forward(w.h[:n], w.w, w.ids[:n])
+    torch.cuda.synchronize()
+    check_rows(w.h[:n], w.w, w.ids[:n], a, range(0, n, 3), "qwen3_8b free n=100",
+               h_host=host("qwen3_8b", "h")[:n], w_host=host("qwen3_8b", "w"))
+    # the two schedules agree to rounding (the K halves are summed separately)
+    assert (a.double() - inv.double()).abs().max().item() < 1e-4
 
 
 def test_empty_batch():
