@@ -360,7 +360,7 @@ def write_mfma(counter_csv, trace_csv, out_path, command):
 
 COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration kernel
 COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
-LMHEAD_KERNEL = "lmhead8w_kernel<false>"
+LMHEAD_KERNEL = "lmhead8w_kernel<false, false>"
 LMHEAD_F32_KERNEL = "lmhead_partials_kernel<false>"
 STATS_KERNEL = "stats_stream_kernel"
 EXTRAS_KERNEL = "xsel_pass_kernel"
