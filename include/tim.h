@@ -39,9 +39,12 @@
  * sequence's tokens; batch aggregates are reduced in a fixed order.
  *
  * Memory.  Every pointer is DEVICE memory unless marked (host).  The caller
- * owns every buffer; the library never allocates device memory and keeps
- * no pointer after a call returns.  Scratch memory is passed in as a
- * workspace whose size is returned by the *_workspace_bytes query.
+ * owns every buffer; no call allocates device memory and none keeps a
+ * pointer after it returns.  Scratch memory is passed in as a workspace
+ * whose size is returned by the *_workspace_bytes query.  The one exception,
+ * tim_logprob_forward_noalloc, uses a static device array instead, of
+ * TIM_NOALLOC_SCRATCH_BYTES on each device the library's kernels are loaded
+ * on, held until the process ends.
  *
  * Execution.  Calls enqueue kernels on `stream` (a hipStream_t; NULL means
  * the null stream) and return without synchronising.  They are re-entrant;
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TIM_ABI_VERSION 3
+#define TIM_ABI_VERSION 4
 
 typedef enum {
     TIM_OK = 0,
@@ -70,7 +73,9 @@ typedef enum {
     TIM_EUNSUPPORTED = 2,  /* d % 64 != 0, misaligned pointer or leading
                               dimension (see tim_logprob_forward)          */
     TIM_EWORKSPACE = 3,    /* workspace null or smaller than the query    */
-    TIM_EHIP = 4           /* a HIP launch or runtime call failed          */
+    TIM_EHIP = 4,          /* a HIP launch or runtime call failed          */
+    TIM_ESCRATCH = 5       /* tim_logprob_forward_noalloc: the request
+                              needs more than TIM_NOALLOC_SCRATCH_BYTES    */
 } tim_status;
 
 /* Element type shared by h and W. */
@@ -159,6 +164,39 @@ int tim_logprob_forward(const void* h, int64_t ldh,
                         float* logp, float* lse, int32_t* n_bad_ids,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Bytes of the static device scratch behind tim_logprob_forward_noalloc,
+ * per device (64 MiB). */
+#define TIM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * tim_logprob_forward without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid allocation.
+ *
+ * Arguments, results, checks and errors are those of tim_logprob_forward
+ * (same kernels, same schedule, bit-identical outputs), minus `workspace`
+ * and `workspace_bytes`.  The scratch is a file-scope device array of
+ * TIM_NOALLOC_SCRATCH_BYTES: a request whose tim_logprob_workspace_bytes(
+ * n, d, v, dtype, flags) exceeds it returns TIM_ESCRATCH before any launch
+ * (bf16 at V = 151936: up to about 14000 rows with the invariant schedule;
+ * the K-split schedule's partial logits rarely fit).  The call allocates
+ * nothing: the first call on a device looks up that device's copy of the
+ * array (the device of `stream`, made current for the lookup).
+ *
+ * Every call on one device shares that device's array, and the array keeps
+ * the last call's contents (nothing in it has to start at zero).  Calls
+ * that can overlap on one device — on streams not ordered with each other,
+ * or from several host threads — race on it and give wrong results; calls
+ * ordered on one stream do not.
+ */
+int tim_logprob_forward_noalloc(const void* h, int64_t ldh,
+                                const void* w, int64_t ldw,
+                                const int32_t* ids,
+                                int64_t n, int64_t d, int64_t v,
+                                int dtype, unsigned flags,
+                                float* logp, float* lse, int32_t* n_bad_ids,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * RMSNorm in front of the head, and scoring at a sampling temperature.

@@ -47,7 +47,7 @@ import torch
 
 from .build import LIB_PATH
 
-TIM_OK, TIM_EINVAL, TIM_EUNSUPPORTED, TIM_EWORKSPACE, TIM_EHIP = range(5)
+TIM_OK, TIM_EINVAL, TIM_EUNSUPPORTED, TIM_EWORKSPACE, TIM_EHIP, TIM_ESCRATCH = range(6)
 TIM_BF16, TIM_F32 = 0, 1
 TIM_SCHED_INVARIANT, TIM_SCHED_FREE, TIM_SCHED_SPLIT_K = 0, 1, 2
 _SCHEDULES = {"invariant": TIM_SCHED_INVARIANT, "free": TIM_SCHED_FREE,
@@ -71,7 +71,9 @@ EXTRAS_FIELDS = (
     "abs_q0", "abs_q1", "abs_q2", "abs_q3",
 )
 X_MAX_Q = 4
-ABI_VERSION = 3
+ABI_VERSION = 4
+# Bytes of the static per-device scratch of tim_logprob_forward_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 TIM_BWD_ACCUMULATE_DW = 1
 
 # Names of the tim_ppo_loss batch vector, in TIM_P_* index order.
@@ -84,7 +86,8 @@ EXPORTS = ("tim_abi_version", "tim_status_string", "tim_logprob_workspace_bytes"
            "tim_extras_workspace_bytes", "tim_mismatch_extras",
            "tim_logprob_backward_workspace_bytes", "tim_logprob_backward",
            "tim_ppo_workspace_bytes", "tim_ppo_loss", "tim_rmsnorm",
-           "tim_logprob_ex_workspace_bytes", "tim_logprob_forward_ex")
+           "tim_logprob_ex_workspace_bytes", "tim_logprob_forward_ex",
+           "tim_logprob_forward_noalloc")
 
 
 class TimError(RuntimeError):
@@ -157,6 +160,9 @@ def load_library():
         lib.tim_logprob_forward.restype = ctypes.c_int
         lib.tim_logprob_forward.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, ctypes.c_int,
                                             ctypes.c_uint, vp, vp, vp, vp, sz, vp]
+        lib.tim_logprob_forward_noalloc.restype = ctypes.c_int
+        lib.tim_logprob_forward_noalloc.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64,
+                                                    ctypes.c_int, ctypes.c_uint, vp, vp, vp, vp]
         lib.tim_rmsnorm.restype = ctypes.c_int
         lib.tim_rmsnorm.argtypes = [vp, i64, vp, i64, i64, ctypes.c_int, ctypes.c_double, vp, i64,
                                     vp, vp]
@@ -275,18 +281,7 @@ def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
     (default: torch's current stream).
     """
     lib = load_library()
-    for name, t in (("h", h), ("w", w), ("ids", ids)):
-        _require_gpu(name, t)
-    if h.dtype not in _DTYPES or w.dtype != h.dtype:
-        raise ValueError("h and w must share dtype bfloat16 or float32")
-    if h.dim() != 2 or w.dim() != 2 or h.stride(1) != 1 or w.stride(1) != 1:
-        raise ValueError("h and w must be 2-D with unit stride along D")
-    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
-        raise ValueError("ids must be a contiguous 1-D int32 tensor")
-    n, d = h.shape
-    v, d2 = w.shape
-    if d2 != d or ids.shape[0] != n:
-        raise ValueError(f"shape mismatch: h {tuple(h.shape)}, w {tuple(w.shape)}, ids {tuple(ids.shape)}")
+    n, d, v = _check_forward_args(h, w, ids)
     dtype = _DTYPES[h.dtype]
     flags = _SCHEDULES[schedule]
     dev = h.device
@@ -305,6 +300,58 @@ def tim_logprob_forward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
     if return_lse:
         return logp, lse, nbad
     return logp
+
+
+def _check_forward_args(h, w, ids):
+    for name, t in (("h", h), ("w", w), ("ids", ids)):
+        _require_gpu(name, t)
+    if h.dtype not in _DTYPES or w.dtype != h.dtype:
+        raise ValueError("h and w must share dtype bfloat16 or float32")
+    if h.dim() != 2 or w.dim() != 2 or h.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("h and w must be 2-D with unit stride along D")
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous 1-D int32 tensor")
+    n, d = h.shape
+    v, d2 = w.shape
+    if d2 != d or ids.shape[0] != n:
+        raise ValueError(f"shape mismatch: h {tuple(h.shape)}, w {tuple(w.shape)}, ids {tuple(ids.shape)}")
+    return n, d, v
+
+
+def _check_out(name, t, n, dtype, dev):
+    if t is not None and (not isinstance(t, torch.Tensor) or t.device != dev or t.dtype != dtype
+                          or t.dim() != 1 or t.shape[0] < n or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous 1-D {dtype} tensor of at least {n} "
+                         f"entries on {dev}")
+
+
+@_on_stream
+def tim_logprob_forward_noalloc(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, *,
+                                out: torch.Tensor, lse_out: Optional[torch.Tensor] = None,
+                                n_bad_ids_out: Optional[torch.Tensor] = None,
+                                schedule: str = "invariant", stream=None):
+    """``tim_logprob_forward`` with the library's static per-device scratch
+    instead of a workspace: no device memory is allocated, here or in the
+    library.  The caller passes every output: ``out`` (fp32 [N]) and,
+    optionally, ``lse_out`` (fp32 [N]) and ``n_bad_ids_out`` (int32 [1]).
+    Raises ``TimError`` with ``TIM_ESCRATCH`` when the request needs more
+    than ``NOALLOC_SCRATCH_BYTES``.  Calls that can overlap on one device
+    race on the shared scratch."""
+    lib = load_library()
+    n, d, v = _check_forward_args(h, w, ids)
+    dev = h.device
+    _check_out("out", out, n, torch.float32, dev)
+    if out is None:
+        raise ValueError("out is required")
+    _check_out("lse_out", lse_out, n, torch.float32, dev)
+    _check_out("n_bad_ids_out", n_bad_ids_out, 1, torch.int32, dev)
+    st = lib.tim_logprob_forward_noalloc(_dptr(h), h.stride(0), _dptr(w), w.stride(0),
+                                         _dptr(ids), n, d, v, _DTYPES[h.dtype],
+                                         _SCHEDULES[schedule], _dptr(out), _dptr(lse_out),
+                                         _dptr(n_bad_ids_out), _stream_handle(stream))
+    if st != TIM_OK:
+        raise TimError(st, "tim_logprob_forward_noalloc")
+    return out
 
 
 @_on_stream

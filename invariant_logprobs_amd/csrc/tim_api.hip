@@ -6,11 +6,46 @@
 #include "tim.h"
 #include "tim_internal.h"
 
+#include <atomic>
 #include <math.h>
+
+// Scratch memory of tim_logprob_forward_noalloc, for callers that cannot
+// allocate.  Every device the library's code object is loaded on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its address on a device comes from
+// hipGetSymbolAddress (scratch_on_device below) and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[TIM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Device address of `scratch` on device `dev`, looked up on the first call
+// for that device with the device current (then restored), and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+hipError_t scratch_on_device(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return hipSuccess;
+}
 
 // The tile kernels address an operand tile of `rows` rows through a buffer
 // descriptor whose extent, (rows - 1) * ld_bytes + k_bytes, and per-lane
@@ -32,6 +67,9 @@ const char* tim_status_string(int status) {
         case TIM_EUNSUPPORTED: return "TIM_EUNSUPPORTED: unsupported size, leading dimension or alignment";
         case TIM_EWORKSPACE: return "TIM_EWORKSPACE: workspace missing or too small";
         case TIM_EHIP: return "TIM_EHIP: HIP launch or runtime error";
+        case TIM_ESCRATCH:
+            return "TIM_ESCRATCH: the request needs more than the static scratch of "
+                   "tim_logprob_forward_noalloc (TIM_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown tim_status";
     }
 }
@@ -42,10 +80,13 @@ size_t tim_logprob_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype, u
     return p.total_bytes;
 }
 
-int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
-                        const int32_t* ids, int64_t n, int64_t d, int64_t v, int dtype,
-                        unsigned flags, float* logp, float* lse, int32_t* n_bad_ids,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Host checks of tim_logprob_forward and tim_logprob_forward_noalloc, in the
+// order the header documents; fills the plan on success.
+int forward_checks(const void* h, int64_t ldh, const void* w, int64_t ldw, const int32_t* ids,
+                   int64_t n, int64_t d, int64_t v, int dtype, unsigned flags, const float* logp,
+                   tim::LogprobPlan* p) {
     if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || (dtype != TIM_BF16 && dtype != TIM_F32) ||
         flags > TIM_SCHED_SPLIT_K)
         return TIM_EINVAL;
@@ -59,18 +100,53 @@ int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
     if (!tile_extent_ok(tim::kTileT, ldh * esz, d * esz) ||
         !tile_extent_ok(tim::kTileV, ldw * esz, d * esz))
         return TIM_EUNSUPPORTED;
-    tim::LogprobPlan p;
-    if (!tim::make_logprob_plan(n, d, v, dtype, flags, false, &p)) return TIM_EINVAL;
-    if (p.nchunks * p.nttiles > INT32_MAX) return TIM_EUNSUPPORTED;
-    if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
-    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
-    hipStream_t st = (hipStream_t)stream;
+    if (!tim::make_logprob_plan(n, d, v, dtype, flags, false, p)) return TIM_EINVAL;
+    if (p->nchunks * p->nttiles > INT32_MAX) return TIM_EUNSUPPORTED;
+    return TIM_OK;
+}
+
+int forward_launch(const tim::LogprobPlan& p, const void* h, int64_t ldh, const void* w,
+                   int64_t ldw, const int32_t* ids, float* logp, float* lse, int32_t* n_bad_ids,
+                   void* workspace, hipStream_t st) {
     const tim::ScoreScale sc = tim::make_score_scale(1.0);
     if (tim::launch_lmhead_partials(p, h, ldh, w, ldw, ids, sc, workspace, n_bad_ids, st) != hipSuccess)
         return TIM_EHIP;
     if (tim::launch_lse_merge(p, ids, sc, workspace, logp, lse, nullptr, n_bad_ids, st) != hipSuccess)
         return TIM_EHIP;
     return TIM_OK;
+}
+
+}  // namespace
+
+int tim_logprob_forward(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                        const int32_t* ids, int64_t n, int64_t d, int64_t v, int dtype,
+                        unsigned flags, float* logp, float* lse, int32_t* n_bad_ids,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    tim::LogprobPlan p;
+    const int chk = forward_checks(h, ldh, w, ldw, ids, n, d, v, dtype, flags, logp, &p);
+    if (chk != TIM_OK || n == 0) return chk;
+    if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;
+    return forward_launch(p, h, ldh, w, ldw, ids, logp, lse, n_bad_ids, workspace,
+                          (hipStream_t)stream);
+}
+
+int tim_logprob_forward_noalloc(const void* h, int64_t ldh, const void* w, int64_t ldw,
+                                const int32_t* ids, int64_t n, int64_t d, int64_t v, int dtype,
+                                unsigned flags, float* logp, float* lse, int32_t* n_bad_ids,
+                                void* stream) {
+    tim::LogprobPlan p;
+    const int chk = forward_checks(h, ldh, w, ldw, ids, n, d, v, dtype, flags, logp, &p);
+    if (chk != TIM_OK || n == 0) return chk;
+    if (p.total_bytes > TIM_NOALLOC_SCRATCH_BYTES) return TIM_ESCRATCH;
+    hipStream_t st = (hipStream_t)stream;
+    int dev = -1;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) return TIM_EHIP;
+    void* ws = nullptr;
+    if (scratch_on_device(dev, &ws) != hipSuccess) return TIM_EHIP;
+    // Nothing here has to start at zero: every scratch byte a kernel of this
+    // call reads was written earlier in the same call.
+    return forward_launch(p, h, ldh, w, ldw, ids, logp, lse, n_bad_ids, ws, st);
 }
 
 int tim_rmsnorm(const void* x, int64_t ldx, const void* gamma, int64_t n, int64_t d, int dtype,

@@ -31,12 +31,13 @@ def test_exports_every_declared_symbol(lib):
     assert declared == sorted(tim.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.tim_abi_version() == tim.ABI_VERSION == 3
+    assert lib.tim_abi_version() == tim.ABI_VERSION == 4
 
 
 def test_status_strings(lib):
-    for st in range(5):
+    for st in range(6):
         assert tim.status_string(st).startswith("TIM_")
+    assert "TIM_NOALLOC_SCRATCH_BYTES" in tim.status_string(tim.TIM_ESCRATCH)
     assert "unknown" in tim.status_string(99)
 
 
@@ -305,3 +306,41 @@ def test_buffer_extent_limits_are_refused_before_any_launch(lib):
     assert bwd(n=(1 << 22)) == tim.TIM_EUNSUPPORTED               # 512 Np >= 2^31
     assert bwd(v=(1 << 22)) == tim.TIM_EUNSUPPORTED
     assert bwd(ldh=big_ld) == tim.TIM_EUNSUPPORTED
+
+
+def _fwd_noalloc(lib, **kw):
+    a = dict(h=FAKE, ldh=64, w=FAKE, ldw=64, ids=FAKE, n=4, d=64, v=100, dtype=0, flags=0,
+             logp=FAKE, lse=None, nbad=None, stream=None)
+    a.update(kw)
+    return lib.tim_logprob_forward_noalloc(a["h"], a["ldh"], a["w"], a["ldw"], a["ids"], a["n"],
+                                           a["d"], a["v"], a["dtype"], a["flags"], a["logp"],
+                                           a["lse"], a["nbad"], a["stream"])
+
+
+def test_noalloc_checks_and_scratch_limit_before_any_device_call(lib):
+    """The no-allocation forward shares the workspace entry point's host
+    checks, and refuses a request whose workspace would exceed its static
+    scratch (TIM_NOALLOC_SCRATCH_BYTES) before touching the device."""
+    assert tim.NOALLOC_SCRATCH_BYTES == 64 << 20
+    hdr = open(HEADER).read()
+    assert "#define TIM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+    assert _fwd_noalloc(lib, n=0) == tim.TIM_OK
+    assert _fwd_noalloc(lib, n=-1) == tim.TIM_EINVAL
+    assert _fwd_noalloc(lib, d=32) == tim.TIM_EUNSUPPORTED
+    assert _fwd_noalloc(lib, flags=3) == tim.TIM_EINVAL
+    assert _fwd_noalloc(lib, logp=None) == tim.TIM_EINVAL
+    assert _fwd_noalloc(lib, h=FAKE + 8) == tim.TIM_EUNSUPPORTED
+    d, v = 4096, 151936
+    fits = big = 0
+    for n in (1, 64, 1000, 8192, 12000, 14000, 14100, 16384, 65536):
+        need = lib.tim_logprob_workspace_bytes(n, d, v, 0, 0)
+        if need > tim.NOALLOC_SCRATCH_BYTES:
+            big += 1
+            assert _fwd_noalloc(lib, n=n, d=d, v=v, ldh=d, ldw=d) == tim.TIM_ESCRATCH
+        else:
+            fits = n
+    assert big >= 2 and 12000 <= fits < 16384      # the headline 8192-row head fits
+    # the K-split schedule's partial logits at 256 tokens: 2 x 151936 x 256 fp32
+    assert lib.tim_logprob_workspace_bytes(256, d, v, 0, tim.TIM_SCHED_SPLIT_K) > (64 << 20)
+    assert _fwd_noalloc(lib, n=256, d=d, v=v, ldh=d, ldw=d,
+                        flags=tim.TIM_SCHED_SPLIT_K) == tim.TIM_ESCRATCH
