@@ -16,38 +16,44 @@
 //
 // The pass is HBM-bound: 9 bytes per token are read once.  Every sequence is
 // cut into sub-chunks of at most kSubChunk tokens that start at the
-// sequence's first token and every kSubChunk tokens after it; a sub-chunk's
+// sequence's first token and every kSubChunk tokens after it.  A sub-chunk's
 // sums are folded in an order that depends only on token offsets inside it,
+// and a sequence's sums are its sub-chunks' sums added in ascending order,
 // so a sequence's results never depend on the rest of the batch.
 //
-//   1. plan_count / plan_scan / plan_write: integer prefix sum of the
-//      sub-chunk counts; writes one (start, length) descriptor per
-//      sub-chunk, in token order, and each sequence's first descriptor.
-//   2. stats_stream: each wave takes a few (at most 16) consecutive
-//      descriptors and streams their tokens in kPiece-token pieces: lane l
-//      holds piece offsets l + 64 i (i = 0..3) of lt, lr and the mask in
-//      registers, with kBufs pieces in flight, and folds one piece while the
-//      next ones load.  A sub-chunk's lanes are folded across the wave with a
-//      fixed LDS transpose + DPP tree.  Sub-chunk partials are staged in LDS
-//      and written once when the wave is done.
-//   3. seq_finalize: one thread per sequence folds its sub-chunks in
-//      ascending order, writes means and flags; each block folds its
-//      sequences into a block partial with a fixed tree.
-//   4. batch_finalize: one block folds the block partials in a fixed tree.
+//   1. stats_stream: a fixed number of waves (at most kMaxStreamWaves), each
+//      owning a contiguous token range.  A wave finds its first sequence in
+//      cu_seqlens with a 64-way search, then walks sequences and sub-chunks
+//      in token order and folds every sub-chunk that starts in its range: the
+//      tokens stream in 256-token pieces through a ring of kBufs LDS slots
+//      filled by LDS DMA (lane l folds piece offsets 4 l .. 4 l + 3), and a
+//      finished sub-chunk is folded across the wave with a fixed LDS
+//      transpose + DPP tree.  A sequence whose sub-chunks all start in the range is finished
+//      by the wave (per-sequence outputs, and its share of the batch sums in
+//      the wave's partial).  Any other sub-chunk's sums go to slot
+//      floor(c_j / kSubChunk) + j + k (strictly increasing in (j, k), so no
+//      prefix sum is needed to place them), and the wave in whose range such
+//      a sequence starts names it for step 2.
+//   2. stats_final: one thread per streaming wave finishes the sequence that
+//      wave named (its slots added in ascending order, exactly as a wave adds
+//      them), adds the wave's partial; each block folds its threads with a
+//      fixed tree, and the last block to finish folds the block partials with
+//      a fixed tree into the batch aggregates.
 
 #include "tim_internal.h"
 
+#include <atomic>
 #include <math.h>
 
 namespace tim {
 namespace {
 
-// Partial sums of one sub-chunk (64 bytes).
+// Sums of one sub-chunk (48 bytes).
 struct alignas(16) SubPartial {
-    double sd, sk2, sk3, sw, sabs, maxabs;
+    double sd, sk2, sk3, sw;
     int32_t nvalid, nclip, nnan, pad;
 };
-static_assert(sizeof(SubPartial) == 64, "four 16-byte quarters");
+static_assert(sizeof(SubPartial) == 48, "three 16-byte quarters");
 
 // Contribution of one sequence to the batch, and the running fold of many.
 struct alignas(16) BatchAcc {
@@ -56,96 +62,37 @@ struct alignas(16) BatchAcc {
     int64_t nvalid, nclip, nnan, nonempty, rejected, rejected_k3;
 };
 
-struct SubDesc {
-    uint32_t start, len;
-};
-
 constexpr int kWave = 64;
 constexpr int kFinBlock = 256;
-constexpr int kScanBlock = 1024;
 constexpr int kPiece = 256;                 // tokens per piece (4 per lane)
-constexpr int kMaxSubPerWave = 16;          // descriptors per wave, at most
-constexpr int kStreamWaves = 4;             // waves per block
-constexpr uint32_t kBufs = 3;               // pieces in flight per wave (registers)
+constexpr int kStreamWaves = 4;             // waves per block (each works on its own)
+constexpr uint32_t kBufs = 3;               // pieces in flight per wave (LDS ring slots)
 constexpr int kFoldVals = 4;                // fp64 sums folded across lanes per sub-chunk
-constexpr int kWavesPerFinBlock = 4 * 256;  // streaming-wave partials per finalize block
+constexpr int64_t kMaxStreamWaves = 4096;   // streaming waves, at most (16 per CU)
+constexpr int64_t kMinRange = 512;          // tokens per streaming wave, at least
+constexpr uint32_t kSC = (uint32_t)kSubChunk;
 
-__device__ __forceinline__ int64_t clamp_cu(const int32_t* cu, int64_t j, int64_t n) {
-    // cu_seqlens is a documented precondition; clamping keeps a malformed one
-    // from producing an out-of-range access (it can only give wrong numbers)
-    const int64_t c = cu[j];
-    return c < 0 ? 0 : (c > n ? n : c);
+// piece record flags
+constexpr uint32_t kLastPiece = 1u;         // the piece ends its sub-chunk
+constexpr uint32_t kLastSub = 2u;           // ... and that sub-chunk ends its sequence
+constexpr uint32_t kComplete = 4u;          // the sequence is finished by this wave
+
+// cu_seqlens is a documented precondition; clamping keeps a malformed one
+// from producing an out-of-range access (it can only give wrong numbers)
+__device__ __forceinline__ uint32_t clamp_c(int32_t c, uint32_t n) {
+    return c < 0 ? 0u : ((uint32_t)c > n ? n : (uint32_t)c);
 }
 
-__device__ __forceinline__ uint32_t subchunks_of(const int32_t* cu, int64_t j, int64_t n) {
-    const int64_t a = clamp_cu(cu, j, n), e = clamp_cu(cu, j + 1, n);
-    return e > a ? (uint32_t)((e - a + kSubChunk - 1) / kSubChunk) : 0u;
-}
-
-// Inclusive scan of one value per thread over a kScanBlock-thread block.
-__device__ uint32_t block_scan_incl(uint32_t x, uint32_t* sh) {
-    const int tid = threadIdx.x;
-    sh[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < kScanBlock; off <<= 1) {
-        const uint32_t y = tid >= off ? sh[tid - off] : 0u;
-        __syncthreads();
-        sh[tid] += y;
-        __syncthreads();
-    }
-    const uint32_t r = sh[tid];
-    __syncthreads();
-    return r;
-}
-
-__global__ void __launch_bounds__(kScanBlock)
-plan_count_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, uint32_t* __restrict__ bsum) {
-    __shared__ uint32_t sh[kScanBlock];
-    const int64_t j = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
-    const uint32_t c = j < s ? subchunks_of(cu, j, n) : 0u;
-    const uint32_t incl = block_scan_incl(c, sh);
-    if (threadIdx.x == kScanBlock - 1) bsum[blockIdx.x] = incl;
-}
-
-__global__ void __launch_bounds__(kScanBlock)
-plan_scan_kernel(const uint32_t* __restrict__ bsum, int64_t nb, uint32_t* __restrict__ boff,
-                 uint32_t* __restrict__ total) {
-    __shared__ uint32_t sh[kScanBlock];
-    __shared__ uint32_t last;
-    uint32_t carry = 0;
-    for (int64_t b0 = 0; b0 < nb; b0 += kScanBlock) {
-        const int64_t b = b0 + threadIdx.x;
-        const uint32_t x = b < nb ? bsum[b] : 0u;
-        const uint32_t incl = block_scan_incl(x, sh);
-        if (b < nb) boff[b] = carry + incl - x;
-        if (threadIdx.x == kScanBlock - 1) last = incl;
-        __syncthreads();
-        carry += last;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *total = carry;
-}
-
-__global__ void __launch_bounds__(kScanBlock)
-plan_write_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_t tmax,
-                  const uint32_t* __restrict__ boff, uint32_t* __restrict__ seq_off,
-                  SubDesc* __restrict__ desc) {
-    __shared__ uint32_t sh[kScanBlock];
-    const int64_t j = (int64_t)blockIdx.x * kScanBlock + threadIdx.x;
-    const uint32_t c = j < s ? subchunks_of(cu, j, n) : 0u;
-    const uint32_t incl = block_scan_incl(c, sh);
-    if (j < s) {
-        const uint32_t off = boff[blockIdx.x] + incl - c;
-        seq_off[j] = off;
-        const int64_t a = clamp_cu(cu, j, n), e = clamp_cu(cu, j + 1, n);
-        // a well-formed cu_seqlens never reaches tmax; the bound keeps a
-        // malformed one inside the descriptor array
-        for (uint32_t k = 0; k < c && (int64_t)off + k < tmax; ++k) {
-            const int64_t st = a + (int64_t)k * kSubChunk;
-            const int64_t en = st + kSubChunk < e ? st + kSubChunk : e;
-            desc[off + k] = SubDesc{(uint32_t)st, (uint32_t)(en - st)};
-        }
-    }
+// clamp(cu[j]) for a wave-uniform j, through the scalar data cache: its
+// wait (lgkmcnt) leaves the vector-memory copies in flight alone.
+__device__ __forceinline__ uint32_t cu_scalar(const int32_t* __restrict__ cu, uint32_t j,
+                                              uint32_t n) {
+    int32_t c;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(c)
+                 : "s"(cu + j)
+                 : "memory");
+    return clamp_c(c, n);
 }
 
 struct TokOut {
@@ -199,40 +146,127 @@ struct Acc {
     __device__ void zero() { sd = sd2 = sk3 = sclip = 0; nvalid = nclip = nnan = 0; }
 };
 
-// A piece held in registers: the lane's tokens at piece offsets lane + 64 i.
+// A piece in registers for the fold: the lane's tokens 4 l .. 4 l + 3.
 struct Regs {
     float x[4], y[4];
     uint32_t m[4];
 };
 
-template <bool kMask>
-__device__ __forceinline__ void load_piece(Regs& r, const float* __restrict__ lt,
-                                           const float* __restrict__ lr,
-                                           const uint8_t* __restrict__ mask, uint32_t st,
-                                           uint32_t cnt, int lane) {
-    // uniform bases (scalar registers) and 32-bit lane offsets: one address
-    // computation per entry, shared by the three streams
-    const float* blt = lt + st;
-    const float* blr = lr + st;
-    const uint8_t* bm = kMask ? mask + st : mask;
-    if (cnt == (uint32_t)kPiece) {                 // full piece: fixed lane offsets
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+constexpr int kRsrcWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data, no swizzle
+
+// One ring slot in LDS: a piece's lt and lr (one dword per token, in token
+// order), then its mask: four bytes per lane-quad of tokens (kMaskDw), or
+// one zero-extended dword per token.
+template <bool kMaskDw>
+struct Slot {
+    static constexpr int kMaskBytes = kMaskDw ? kPiece : 4 * kPiece;
+    static constexpr int kBytes = 2 * 4 * kPiece + kMaskBytes;
+};
+// LDS DMA copies per piece: lt and lr as one 16-byte load per lane, the
+// mask as one 4-byte load per lane (kMaskDw) or four 1-byte loads.
+template <bool kMask, bool kMaskDw>
+struct PieceLoads { static constexpr int value = !kMask ? 2 : (kMaskDw ? 3 : 6); };
+
+// Copy the piece of tokens [st, st + 256) into a ring slot with LDS DMA.
+// Lane l moves tokens st + 4 l .. st + 4 l + 3 of lt and lr (offsets
+// relative to the descriptors' bases; the descriptors' extents end at the
+// arrays' ends, and a dword out of range reads as 0, so no address leaves
+// the arrays).  The mask: with kMaskDw lane l moves the four bytes from
+// moff + 4 l, where moff places the last lane-quad that reaches the array's
+// end on the array's last four bytes (a dword only partly in range would
+// read as 0); the fold shifts such a lane's bytes back.  Otherwise four
+// one-byte loads per lane (token 64 i + l of the piece, clamped to the
+// array's end).
+template <bool kMask, bool kMaskDw>
+__device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t rlt, __amdgpu_buffer_rsrc_t rlr,
+                                          __amdgpu_buffer_rsrc_t rm, unsigned char* slot,
+                                          uint32_t st, uint32_t mst, uint32_t mlast, int lane) {
+    const uint32_t o = (st + 4u * (uint32_t)lane) * 4u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rlt, (lds_void*)slot, 16, o, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rlr, (lds_void*)(slot + 4 * kPiece), 16, o, 0, 0, 0);
+    if constexpr (kMask) {
+        if constexpr (kMaskDw) {
+            uint32_t mo = mst + 4u * (uint32_t)lane;
+            mo = mo < mlast ? mo : mlast;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(slot + 8 * kPiece), 4, mo, 0,
+                                                     0, 0);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t o = (uint32_t)(i * kWave + lane);
-            r.x[i] = *(const float*)((const char*)blt + (o << 2));
-            r.y[i] = *(const float*)((const char*)blr + (o << 2));
-            r.m[i] = kMask ? (uint32_t)bm[o] : 1u;
+            for (int i = 0; i < 4; ++i) {
+                uint32_t mo = mst + (uint32_t)(i * kWave + lane);
+                mo = mo < mlast ? mo : mlast;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(slot + 8 * kPiece + i * 256),
+                                                         1, mo, 0, 0, 0);
+            }
         }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The lane's four tokens of a ring slot, read in one asm block: the slot is
+// filled by LDS DMA, which the compiler's own waits would otherwise guard
+// with a wait for every copy in flight.  The caller has waited for the
+// slot's copies.  lt and lr come out as float vectors: a bit cast of a
+// single element of an integer asm output gives element 0 with this
+// compiler.  mshift: bytes to drop from a kMaskDw mask quad (non-zero only
+// for the lane-quads placed back on the array's last four bytes).
+template <bool kMask, bool kMaskDw>
+__device__ __forceinline__ void read_slot(Regs& r, const unsigned char* slot, int lane,
+                                          uint32_t mshift) {
+    const uint32_t a = lds_addr(slot) + 16u * (uint32_t)lane;
+    f32x4 x, y;
+    if constexpr (kMask && kMaskDw) {
+        uint32_t m;
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %3 offset:1024\n\t"
+            "ds_read_b32 %2, %4 offset:2048\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x), "=&v"(y), "=&v"(m)
+            : "v"(a), "v"(lds_addr(slot) + 4u * (uint32_t)lane)
+            : "memory");
+        m >>= 8u * mshift;                         // mshift <= 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.m[i] = (m >> (8 * i)) & 0xffu;
+    } else if constexpr (kMask) {
+        u32x4 m;
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %3 offset:1024\n\t"
+            "ds_read_b128 %2, %3 offset:2048\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x), "=&v"(y), "=&v"(m)
+            : "v"(a)
+            : "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.m[i] = m[i];
     } else {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %2 offset:1024\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x), "=&v"(y)
+            : "v"(a)
+            : "memory");
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t o = (uint32_t)(i * kWave + lane);
-            o = o < cnt ? o : cnt - 1;             // clamped: a valid copy, ignored later
-            const uint32_t ob = o << 2;            // byte offset, 32-bit
-            r.x[i] = *(const float*)((const char*)blt + ob);
-            r.y[i] = *(const float*)((const char*)blr + ob);
-            r.m[i] = kMask ? (uint32_t)bm[o] : 1u;
-        }
+        for (int i = 0; i < 4; ++i) r.m[i] = 1u;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.x[i] = x[i];
+        r.y[i] = y[i];
     }
 }
 
@@ -261,80 +295,128 @@ __device__ __forceinline__ double fma_s(double a, double b, double c) {
     return r;
 }
 
-// Fold the piece of a sub-chunk (start sub_start, length len) that begins at
-// offset off0: lane l takes offsets off0 + l + 64 i, i ascending, so across a
-// sub-chunk's pieces each lane folds its offsets in ascending order.  A token
-// that does not count (outside the sub-chunk, masked out or non-finite) gets
-// d = 0, which makes its d, d^2, k3 and |d| contributions exactly 0 with no
-// further selects.  Counts are popcounts of the wave masks.  k2 is
-// accumulated as d^2 and halved once (a power-of-two scale: exact).  For the
-// truncated weight only the clipped tokens' e^d - 1 is summed (rare path);
-// the unclipped sum is recovered as (sum d + sum k3) - that.
-template <bool kTok, bool kMask>
-__device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg,
-                                           uint32_t sub_start, uint32_t off0, uint32_t len,
-                                           int lane, const StatsParamsDev& prm,
-                                           const TokOut& tok) {
-    static_assert(kPiece == 4 * kWave, "four piece entries per lane");
-    const uint32_t lim = len - off0;                          // valid piece offsets < lim
+// Fold a piece of a sub-chunk: lane l holds piece offsets 4 l + i
+// (i = 0..3, "row" i), lim of the piece's tokens lie inside the sub-chunk
+// (1 <= lim <= 256), tok0 is the piece's first token.  Lane l adds its
+// offsets in ascending order; the rows are independent until then, so their
+// arithmetic interleaves.  A token that does not count (outside the
+// sub-chunk, masked out or non-finite) gets d = 0, which makes its d, d^2,
+// k3 and |d| contributions exactly 0 with no further selects.  Counts are
+// popcounts of the wave masks; the rare ones (non-finite, clipped) are
+// counted in the rare branch, which any such token sends the wave into.  k2
+// is accumulated as d^2 and halved once (a power-of-two scale: exact).  For
+// the truncated weight only the clipped tokens' e^d - 1 is summed (rare
+// path); the unclipped sum is recovered as (sum d + sum k3) - that.
+template <bool kTok, bool kMask, bool kFull, bool kClipRare>
+__device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg, uint32_t tok0, uint32_t lim,
+                                          int lane, const StatsParamsDev& prm,
+                                          const TokOut& tok) {
+    // kClipRare: log C >= 1/32, so a clipped token (d > log C) is among the
+    // |d| > 1/32 tokens of the rare branch and needs no test of its own
+    static_assert(!(kTok && kClipRare), "per-token outputs test the clip on every row");
+    double draw[4], d[4], dp[4];
+    uint64_t m_fin[4];
+    uint64_t m_clip[kClipRare ? 1 : 4], m_sc[kTok ? 4 : 1];
+    double k3x[kTok ? 4 : 1];                          // per-token k3, for the outputs
+    uint64_t rare = 0;
 #pragma unroll
-    for (int i = 0; i < kPiece / kWave; ++i) {
-        if ((uint32_t)(i * kWave) >= lim) break;              // uniform: rest of piece empty
-        const uint32_t po = (uint32_t)(i * kWave + lane);      // offset in the piece
-        const double draw = (double)rg.x[i] - (double)rg.y[i];
+    for (int i = 0; i < 4; ++i) {
+        draw[i] = (double)rg.x[i] - (double)rg.y[i];
         // lane predicates as wave masks: each ballot is one compare, the
         // combinations are scalar, and inverse_ballot reads a lane's bit back
-        uint64_t m_in = ~0ull;                                    // full row: all lanes in
-        if ((uint32_t)((i + 1) * kWave) > lim) m_in = __builtin_amdgcn_ballot_w64(po < lim);
-        const uint64_t m_scored = m_in & (kMask ? __builtin_amdgcn_ballot_w64(rg.m[i] != 0) : ~0ull);
-        const uint64_t m_fin = m_scored & finite_mask(draw);
-        const uint64_t m_clip = m_fin & __builtin_amdgcn_ballot_w64(draw > prm.log_c);
-        A.nvalid += (uint32_t)__popcll(m_fin);
-        A.nnan += (uint32_t)__popcll(m_scored & ~m_fin);
-        A.nclip += (uint32_t)__popcll(m_clip);
-        const double d = __builtin_amdgcn_inverse_ballot_w64(m_fin) ? draw : 0.0;
-        // e^d - 1 - d for |d| <= 1/32: d^2 (1/2 + d/6 + d^2/24 + d^3/120),
-        // truncation below 4e-9 relative
-        double p = fma_s(d, 1.0 / 120.0, 1.0 / 24.0);
-        p = fma_s(p, d, 1.0 / 6.0);
-        p = fma_s(p, d, 0.5);
-        double k3 = d * (d * p);
-        const uint64_t m_big = __builtin_amdgcn_ballot_w64(!(fabs(d) <= 0.03125));
-        if ((m_big | m_clip) != 0) {                                    // rare, uniform test
-            if (__builtin_amdgcn_inverse_ballot_w64(m_big)) k3 = expm1_large(d) - d;
-            if (__builtin_amdgcn_inverse_ballot_w64(m_clip)) A.sclip += d + k3;
+        uint64_t sc = kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[i] != 0) : ~0ull;
+        if constexpr (!kFull) sc &= __builtin_amdgcn_ballot_w64((uint32_t)(4 * lane + i) < lim);
+        m_fin[i] = sc & finite_mask(draw[i]);
+        A.nvalid += (uint32_t)__popcll(m_fin[i]);
+        rare |= sc & ~m_fin[i];                        // non-finite: counted in the branch
+        if constexpr (kTok) m_sc[i] = sc;
+        if constexpr (!kClipRare) {
+            m_clip[i] = m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > prm.log_c);
+            rare |= m_clip[i];
         }
-        A.sd += d;
-        A.sd2 = fma(d, d, A.sd2);
-        A.sk3 += k3;
-        A.sabs += fabs(d);
-        A.mx = max_abs(A.mx, d);
-        if (kTok && po < lim) {
-            // per-token outputs; a non-finite delta reports exp/expm1 as computed
-            const bool scored = __builtin_amdgcn_inverse_ballot_w64(m_scored);
-            const bool fin = __builtin_amdgcn_inverse_ballot_w64(m_fin);
-            const bool clipped = __builtin_amdgcn_inverse_ballot_w64(m_clip);
-            const uint32_t t = sub_start + off0 + po;
-            const double dd = scored ? draw : 0.0;
-            const double em1 = d + k3;
-            const double r = 1.0 + em1;
-            const double wgt = clipped ? prm.clip_c : (fin ? r : 0.0);
-            const double rr = fin ? r : (scored ? exp(dd) : 1.0);
-            const double kk3 = fin ? k3 : (scored ? expm1(dd) - dd : 0.0);
-            if (tok.delta) tok.delta[t] = (float)dd;
-            if (tok.ratio) tok.ratio[t] = (float)rr;
-            if (tok.k1) tok.k1[t] = (float)(-dd);
-            if (tok.k2) tok.k2[t] = (float)(0.5 * (dd * dd));
-            if (tok.k3) tok.k3[t] = (float)kk3;
-            if (tok.tis_w) tok.tis_w[t] = (float)wgt;
-            if (tok.clipped) tok.clipped[t] = clipped ? 1 : 0;
+        d[i] = __builtin_amdgcn_inverse_ballot_w64(m_fin[i]) ? draw[i] : 0.0;
+        // e^d - 1 - d = d dp for |d| <= 1/32, dp = d (1/2 + d/6 + d^2/24 +
+        // d^3/120), truncation below 4e-9 relative
+        double p = fma_s(d[i], 1.0 / 120.0, 1.0 / 24.0);
+        p = fma_s(p, d[i], 1.0 / 6.0);
+        p = fma_s(p, d[i], 0.5);
+        dp[i] = d[i] * p;
+        rare |= __builtin_amdgcn_ballot_w64(!(fabs(d[i]) <= 0.03125));
+        if constexpr (kTok) k3x[i] = d[i] * dp[i];
+    }
+    if (rare != 0) {                                   // uniform test, rarely taken
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t sc = kTok ? m_sc[i]
+                                     : (kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[i] != 0)
+                                              : ~0ull) &
+                                           (kFull ? ~0ull
+                                                  : __builtin_amdgcn_ballot_w64(
+                                                        (uint32_t)(4 * lane + i) < lim));
+            A.nnan += (uint32_t)__popcll(sc & ~m_fin[i]);
+            const uint64_t clip = kClipRare
+                                      ? m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > prm.log_c)
+                                      : m_clip[i];
+            A.nclip += (uint32_t)__popcll(clip);
+            const bool big = !(fabs(d[i]) <= 0.03125);
+            double k3 = d[i] * dp[i];
+            if (big) {
+                // the exact e^d - 1 - d, added here; the row's fused add
+                // below then adds d * 0
+                k3 = expm1_large(d[i]) - d[i];
+                double e = k3;
+                asm volatile("" : "+v"(e));            // keeps this work inside the branch
+                A.sk3 += e;
+                dp[i] = 0.0;
+            }
+            if (__builtin_amdgcn_inverse_ballot_w64(clip)) {
+                double e = d[i] + k3;
+                asm volatile("" : "+v"(e));
+                A.sclip += e;
+            }
+            if constexpr (kTok) {
+                m_clip[i] = clip;
+                k3x[i] = k3;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        A.sd += d[i];
+        A.sd2 = fma(d[i], d[i], A.sd2);
+        A.sk3 = fma(d[i], dp[i], A.sk3);
+        A.sabs += fabs(d[i]);
+        A.mx = max_abs(A.mx, d[i]);
+    }
+    if constexpr (kTok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t po = (uint32_t)(4 * lane + i);          // offset in the piece
+            if (po < lim) {
+                // per-token outputs; a non-finite delta reports exp/expm1 as computed
+                const bool scored = __builtin_amdgcn_inverse_ballot_w64(m_sc[i]);
+                const bool fin = __builtin_amdgcn_inverse_ballot_w64(m_fin[i]);
+                const bool clipped = __builtin_amdgcn_inverse_ballot_w64(m_clip[i]);
+                const uint32_t t = tok0 + po;
+                const double dd = scored ? draw[i] : 0.0;
+                const double k3 = k3x[i];
+                const double em1 = d[i] + k3;
+                const double r = 1.0 + em1;
+                const double wgt = clipped ? prm.clip_c : (fin ? r : 0.0);
+                const double rr = fin ? r : (scored ? exp(dd) : 1.0);
+                const double kk3 = fin ? k3 : (scored ? expm1(dd) - dd : 0.0);
+                if (tok.delta) tok.delta[t] = (float)dd;
+                if (tok.ratio) tok.ratio[t] = (float)rr;
+                if (tok.k1) tok.k1[t] = (float)(-dd);
+                if (tok.k2) tok.k2[t] = (float)(0.5 * (dd * dd));
+                if (tok.k3) tok.k3[t] = (float)kk3;
+                if (tok.tis_w) tok.tis_w[t] = (float)wgt;
+                if (tok.clipped) tok.clipped[t] = clipped ? 1 : 0;
+            }
         }
     }
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // 64-bit value of the lane selected by a DPP control (both 32-bit halves
 // moved with v_mov_b32_dpp).
@@ -404,8 +486,6 @@ __device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int la
     q.sk3 = readlane_f64(t, 16);
     const double sem1 = (q.sd + q.sk3) - readlane_f64(t, 24);     // unclipped e^d - 1
     q.sw = ((double)(A.nvalid - A.nclip) + sem1) + clip_c * (double)A.nclip;
-    q.sabs = 0.0;                                                  // per wave instead
-    q.maxabs = 0.0;
     q.nvalid = (int32_t)A.nvalid; q.nclip = (int32_t)A.nclip;
     q.nnan = (int32_t)A.nnan; q.pad = 0;
     return q;
@@ -423,106 +503,6 @@ __device__ __forceinline__ double bfly_max(double x) {
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) x = fmax(x, __shfl_xor(x, m));
     return x;
-}
-
-// Descriptors per wave: enough waves to cover the chip several times over at
-// any size (a wave's descriptors are folded one after another, its pieces
-// streamed through one pipeline), at most kMaxSubPerWave: with many short
-// sequences the longer per-wave stream hides the pipeline's start (at 2^28
-// tokens in log-normal sequences, 16 per wave instead of 4 is ~7 % faster).
-// Which wave folds a sub-chunk never changes its result.
-inline uint32_t subs_per_wave(int64_t tmax) {
-    constexpr int64_t kTargetWaves = 16384;
-    int64_t k = (tmax + kTargetWaves - 1) / kTargetWaves;
-    if (k < 1) k = 1;
-    if (k > kMaxSubPerWave) k = kMaxSubPerWave;
-    return (uint32_t)k;
-}
-
-template <bool kTok, bool kMask>
-__global__ void __launch_bounds__(kWave * kStreamWaves)
-stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
-                    const uint8_t* __restrict__ mask, const SubDesc* __restrict__ desc,
-                    const uint32_t* __restrict__ total, uint32_t tmax, StatsParamsDev prm,
-                    TokOut tok, SubPartial* __restrict__ partial, uint32_t spw,
-                    double2* __restrict__ wpart) {
-    __shared__ __attribute__((aligned(16))) double scratch[kStreamWaves][kFoldVals * kWave];
-    __shared__ SubPartial stage[kStreamWaves][kMaxSubPerWave];
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    uint32_t T = __builtin_amdgcn_readfirstlane(*total);
-    T = T < tmax ? T : tmax;
-    const uint64_t wid = (uint64_t)blockIdx.x * kStreamWaves + wv;
-    const uint64_t k0 = wid * spw;
-    if (k0 >= T) {                                 // no sub-chunk for this wave
-        if (lane == 0) wpart[wid] = make_double2(0.0, 0.0);
-        return;
-    }
-    const uint32_t nsub = (uint32_t)(T - k0 < spw ? T - k0 : spw);
-
-    // this wave's descriptors, one per lane, read into scalar registers
-    const SubDesc my = lane < (int)nsub ? desc[k0 + lane] : SubDesc{0u, 0u};
-    auto d_start = [&](uint32_t k) { return (uint32_t)__builtin_amdgcn_readlane((int)my.start, (int)k); };
-    auto d_len = [&](uint32_t k) { return (uint32_t)__builtin_amdgcn_readlane((int)my.len, (int)k); };
-
-    uint32_t npieces = 0;
-    for (uint32_t k = 0; k < nsub; ++k) npieces += (d_len(k) + kPiece - 1) / kPiece;
-
-    // issue iterator: (sub-chunk ik, piece ip)
-    uint32_t ik = 0, ip = 0, is0 = d_start(0), il = d_len(0);
-    // Every call issues the same loads, on every path: past the last piece it
-    // reloads the first piece of the wave (never folded again).  The
-    // compiler's load counting then sees a fixed number of loads between a
-    // buffer's refill and its use, and waits for exactly that piece.
-    const uint32_t s_first = d_start(0);
-    const uint32_t c_first = d_len(0) < (uint32_t)kPiece ? d_len(0) : (uint32_t)kPiece;
-    auto issue = [&](Regs& r) {
-        if (ik < nsub) {
-            const uint32_t st = is0 + ip * kPiece;
-            const uint32_t en = st + kPiece < is0 + il ? st + kPiece : is0 + il;
-            load_piece<kMask>(r, lt, lr, mask, st, en - st, lane);
-            if (++ip * kPiece >= il) {
-                ip = 0;
-                if (++ik < nsub) { is0 = d_start(ik); il = d_len(ik); }
-            }
-        } else {
-            load_piece<kMask>(r, lt, lr, mask, s_first, c_first, lane);
-        }
-    };
-
-    Acc A;
-    A.zero();
-    A.sabs = 0.0;
-    A.mx = 0.0;
-    uint32_t fk = 0, fp = 0, fs = d_start(0), fl = d_len(0);
-    // fold piece c from r (if it exists), then refill r with piece c + kBufs
-    auto step = [&](Regs& r, uint32_t c) {
-        if (c < npieces) {
-            fold_piece<kTok, kMask>(A, r, fs, fp * kPiece, fl, lane, prm, tok);
-            if (++fp * kPiece >= fl) {
-                const SubPartial q = finish(A, prm.clip_c, lane, scratch[wv]);
-                if (lane == 0) stage[wv][fk] = q;
-                A.zero();
-                fp = 0;
-                if (++fk < nsub) { fs = d_start(fk); fl = d_len(fk); }
-            }
-        }
-        issue(r);
-    };
-    Regs b0, b1, b2;
-    issue(b0);
-    issue(b1);
-    issue(b2);
-    for (uint32_t c = 0; c < npieces; c += kBufs) {
-        step(b0, c);
-        step(b1, c + 1);
-        step(b2, c + 2);
-    }
-    // stage[wv] is this wave's own: lane 0's LDS writes precede these reads in order
-    const int e = lane >> 2, q4 = lane & 3;
-    if (e < (int)nsub) ((uint4*)&partial[k0 + e])[q4] = ((const uint4*)&stage[wv][e])[q4];
-    const double wsabs = bfly_sum(A.sabs), wmx = bfly_max(A.mx);
-    if (lane == 0) wpart[wid] = make_double2(wsabs, wmx);
 }
 
 __device__ __forceinline__ void acc_add(BatchAcc& x, const BatchAcc& y) {
@@ -555,39 +535,42 @@ struct SeqOut {
     uint8_t *reject, *reject_k3;
 };
 
-__global__ void __launch_bounds__(kFinBlock)
-seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_t tmax,
-                    StatsParamsDev prm,
-                    const uint32_t* __restrict__ seq_off, const SubPartial* __restrict__ partial,
-                    const double2* __restrict__ wpart, int64_t nw,
-                    SeqOut so, BatchAcc* __restrict__ blk) {
-    __shared__ BatchAcc buf[kFinBlock];
-    const int64_t j = (int64_t)blockIdx.x * kFinBlock + threadIdx.x;
-    BatchAcc c = acc_zero();
-    if (j < s) {
-        const uint32_t nsub = subchunks_of(cu, j, n);
-        double sd = 0, sk2 = 0, sk3 = 0, sw = 0, sabs = 0, mx = 0;
-        int64_t nvalid = 0, nclip = 0, nnan = 0;
-        if (nsub > 0) {
-            const uint32_t off = seq_off[j];
-            for (uint32_t k = 0; k < nsub && (int64_t)off + k < tmax; ++k) {
-                const SubPartial p = partial[off + k];
-                sd += p.sd; sk2 += p.sk2; sk3 += p.sk3; sw += p.sw; sabs += p.sabs;
-                mx = fmax(mx, p.maxabs);
-                nvalid += p.nvalid; nclip += p.nclip; nnan += p.nnan;
-            }
-        }
-        const double nv = (double)nvalid;
-        const double md = nvalid ? sd / nv : 0.0;
-        const double mk1 = nvalid ? (-sd) / nv : 0.0;
-        const double mk2 = nvalid ? sk2 / nv : 0.0;
-        const double mk3 = nvalid ? sk3 / nv : 0.0;
-        const double mw = nvalid ? sw / nv : 0.0;
-        const bool rej = nvalid > 0 && (md < prm.seq_lo || md > prm.seq_hi);
-        const bool rej_k3 = nvalid > 0 && mk3 > prm.seq_k3_hi;   // K3 form
+// A sequence's sums: its sub-chunks' sums added in ascending order, by the
+// streaming wave or by the finalize kernel with this same code.
+struct SeqSums {
+    double sd, sk2, sk3, sw;
+    int64_t nvalid, nclip, nnan;
+};
+
+__device__ __forceinline__ SeqSums seq_zero() {
+    SeqSums a;
+    a.sd = a.sk2 = a.sk3 = a.sw = 0.0;
+    a.nvalid = a.nclip = a.nnan = 0;
+    return a;
+}
+
+__device__ __forceinline__ void seq_add(SeqSums& a, const SubPartial& p) {
+    a.sd += p.sd; a.sk2 += p.sk2; a.sk3 += p.sk3; a.sw += p.sw;
+    a.nvalid += p.nvalid; a.nclip += p.nclip; a.nnan += p.nnan;
+}
+
+// Means and rejection flags of sequence j, written to the per-sequence
+// outputs when `writer`, and the sequence's contribution added to c.
+__device__ __forceinline__ void seq_finish(uint32_t j, const SeqSums& a, const StatsParamsDev& prm,
+                                           const SeqOut& so, bool writer, BatchAcc& c) {
+    const int64_t nvalid = a.nvalid;
+    const double nv = (double)nvalid;
+    const double md = nvalid ? a.sd / nv : 0.0;
+    const double mk1 = nvalid ? (-a.sd) / nv : 0.0;
+    const double mk2 = nvalid ? a.sk2 / nv : 0.0;
+    const double mk3 = nvalid ? a.sk3 / nv : 0.0;
+    const double mw = nvalid ? a.sw / nv : 0.0;
+    const bool rej = nvalid > 0 && (md < prm.seq_lo || md > prm.seq_hi);
+    const bool rej_k3 = nvalid > 0 && mk3 > prm.seq_k3_hi;   // K3 form
+    if (writer) {
         if (so.n_valid) so.n_valid[j] = (int32_t)nvalid;
-        if (so.n_clipped) so.n_clipped[j] = (int32_t)nclip;
-        if (so.n_nan) so.n_nan[j] = (int32_t)nnan;
+        if (so.n_clipped) so.n_clipped[j] = (int32_t)a.nclip;
+        if (so.n_nan) so.n_nan[j] = (int32_t)a.nnan;
         if (so.mean_delta) so.mean_delta[j] = md;
         if (so.mean_k1) so.mean_k1[j] = mk1;
         if (so.mean_k2) so.mean_k2[j] = mk2;
@@ -595,36 +578,381 @@ seq_finalize_kernel(const int32_t* __restrict__ cu, int64_t n, int64_t s, int64_
         if (so.mean_tis_w) so.mean_tis_w[j] = mw;
         if (so.reject) so.reject[j] = rej ? 1 : 0;
         if (so.reject_k3) so.reject_k3[j] = rej_k3 ? 1 : 0;
-        c.sd = sd; c.sk2 = sk2; c.sk3 = sk3; c.sw = sw; c.sabs = sabs; c.maxabs = mx;
-        c.nvalid = nvalid; c.nclip = nclip; c.nnan = nnan;
-        if (nvalid > 0) {
-            c.md = md; c.mk1 = mk1; c.mk2 = mk2; c.mk3 = mk3;
-            c.nonempty = 1;
-            c.rejected = rej ? 1 : 0;
-            c.rejected_k3 = rej_k3 ? 1 : 0;
-        }
     }
-    // this block's slice of the streaming waves' sum and maximum of |delta|
+    c.sd += a.sd; c.sk2 += a.sk2; c.sk3 += a.sk3; c.sw += a.sw;
+    c.nvalid += nvalid; c.nclip += a.nclip; c.nnan += a.nnan;
+    if (nvalid > 0) {
+        c.md += md; c.mk1 += mk1; c.mk2 += mk2; c.mk3 += mk3;
+        c.nonempty += 1;
+        c.rejected += rej ? 1 : 0;
+        c.rejected_k3 += rej_k3 ? 1 : 0;
+    }
+}
+
+// First j in [0, s) with clamp(cu[j]) >= x (s if none), for a monotone
+// cu_seqlens; 64 entries are probed per step.  For any input the result
+// lies in [0, s] and every probe inside cu[0 .. s - 1].
+__device__ uint32_t lower_bound_cu(const int32_t* __restrict__ cu, uint32_t s, uint32_t n,
+                                   uint32_t x, int lane) {
+    uint32_t lo = 0, hi = s;                        // the answer is in [lo, hi]
+    while (hi - lo > (uint32_t)kWave) {
+        const uint32_t step = (hi - lo + kWave - 1) / kWave;
+        const uint64_t idx = (uint64_t)lo + (uint64_t)lane * step;
+        const bool below = idx < hi && clamp_c(cu[idx], n) < x;
+        const uint32_t t = (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(below));
+        // probes 0 .. t - 1 are below x: the answer is in
+        // (lo + (t - 1) step, min(hi, lo + t step)]
+        const uint32_t nlo = t == 0 ? lo : lo + (t - 1) * step + 1;
+        const uint64_t up = (uint64_t)lo + (uint64_t)t * step;
+        hi = up < hi ? (uint32_t)up : hi;
+        lo = nlo < hi ? nlo : hi;
+    }
+    const uint32_t idx = lo + (uint32_t)lane;
+    const bool below = idx < hi && clamp_c(cu[idx], n) < x;
+    return lo + (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(below));
+}
+
+// One piece to fold: tokens [start, start + lim) of a sub-chunk; lim == 0:
+// none.  id: the sequence's index if the wave finishes it (kComplete), else
+// the sub-chunk's slot.
+struct PieceRec {
+    uint32_t start, lim_flags, id;     // lim_flags = lim | flags << 16
+};
+
+// A result waiting in LDS for the wave's next flush: a finished sequence's
+// sums (kind 0, id = its index) or a sub-chunk's sums (kind 1, id = slot).
+struct alignas(16) StageEnt {
+    SubPartial q;
+    uint32_t id, kind, pad0, pad1;
+};
+constexpr int kStage = 16;                      // entries per wave (one per lane at a flush)
+
+// Contribution of a lane's staged entry to the wave's batch sums, folded
+// over the wave's lanes with a fixed butterfly.
+__device__ __forceinline__ void wave_fold_acc(BatchAcc& c) {
+    c.sd = bfly_sum(c.sd); c.sk2 = bfly_sum(c.sk2); c.sk3 = bfly_sum(c.sk3);
+    c.sw = bfly_sum(c.sw);
+    c.md = bfly_sum(c.md); c.mk1 = bfly_sum(c.mk1); c.mk2 = bfly_sum(c.mk2);
+    c.mk3 = bfly_sum(c.mk3);
 #pragma unroll
-    for (int r = 0; r < kWavesPerFinBlock / kFinBlock; ++r) {
-        const int64_t i = (int64_t)blockIdx.x * kWavesPerFinBlock + r * kFinBlock + threadIdx.x;
-        if (i < nw) {
-            const double2 q = wpart[i];
-            c.sabs += q.x;
-            c.maxabs = fmax(c.maxabs, q.y);
+    for (int m = 1; m < kWave; m <<= 1) {
+        c.nvalid += __shfl_xor(c.nvalid, m);
+        c.nclip += __shfl_xor(c.nclip, m);
+        c.nnan += __shfl_xor(c.nnan, m);
+        c.nonempty += __shfl_xor(c.nonempty, m);
+        c.rejected += __shfl_xor(c.rejected, m);
+        c.rejected_k3 += __shfl_xor(c.rejected_k3, m);
+    }
+}
+
+template <bool kTok, bool kMask, bool kMaskDw>
+__global__ void __launch_bounds__(kWave * kStreamWaves)
+stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
+                    const uint8_t* __restrict__ mask, const int32_t* __restrict__ cu,
+                    uint32_t n, uint32_t s, uint32_t range, uint32_t nwaves, StatsParamsDev prm,
+                    TokOut tok, SeqOut so, SubPartial* __restrict__ slots,
+                    BatchAcc* __restrict__ wpart, int32_t* __restrict__ cross,
+                    uint32_t* __restrict__ ticket) {
+    __shared__ __attribute__((aligned(16)))
+    unsigned char ring[kStreamWaves][kBufs][Slot<kMaskDw>::kBytes];
+    __shared__ __attribute__((aligned(16))) double scratch[kStreamWaves][kFoldVals * kWave];
+    __shared__ StageEnt stage[kStreamWaves][kStage];
+    // per wave, touched by its lane 0 only: the sums of the sequence being
+    // finished, and the wave's share of the batch sums
+    __shared__ SeqSums seq_lds[kStreamWaves];
+    __shared__ BatchAcc acc_lds[kStreamWaves];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const uint32_t w = blockIdx.x * kStreamWaves + (uint32_t)wv;
+    if (w >= nwaves) return;
+    if (w == 0 && lane == 0) *ticket = 0u;         // the finalize kernel's counter
+    if (lane == 0) {
+        seq_lds[wv] = seq_zero();
+        acc_lds[wv] = acc_zero();
+    }
+    const bool last = w == nwaves - 1;
+    const uint32_t b0 = w * range;
+    const uint32_t b1 = last ? n : b0 + range;     // the last wave also owns c_j == n
+    const uint32_t ja = lower_bound_cu(cu, s, n, b0, lane);
+
+    // Owned empty sequences (c_j in this wave's range, c_{j+1} == c_j): zero
+    // outputs, nothing for the batch; 64 sequences per round.
+    for (uint32_t jb = ja;; jb += kWave) {
+        const uint32_t jj = jb + (uint32_t)lane;
+        bool more = false;
+        if (jj < s) {
+            const uint32_t c = clamp_c(cu[jj], n);
+            if (last || c < b1) {
+                more = true;
+                if (clamp_c(cu[jj + 1], n) <= c) {
+                    BatchAcc dummy = acc_zero();
+                    seq_finish(jj, seq_zero(), prm, so, true, dummy);
+                }
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(more) != ~0ull) break;
+    }
+
+    // ---- the walk over sequences and sub-chunks (wave-uniform state)
+    uint32_t j = 0, cj = 0, ej = 0, kidx = 0, ss = 0, se = 0, off = 0;
+    bool complete = false, done = false;
+    int32_t crossj = -1;                           // owned sequence left to step 2
+
+    // Enter the first sequence at or after jj that this wave owns and that
+    // has a token.
+    auto enter = [&](uint32_t jj) {
+        for (;;) {
+            if (jj >= s) { done = true; return; }
+            const uint32_t c = cu_scalar(cu, jj, n);
+            if (!last && c >= b1) { done = true; return; }
+            const uint32_t e = cu_scalar(cu, jj + 1, n);
+            if (e > c) {
+                j = jj; cj = c; ej = e; kidx = 0; ss = c; off = 0;
+                se = c + kSC < e ? c + kSC : e;
+                const uint32_t K = (e - c + kSC - 1) / kSC;
+                complete = last || c + (K - 1) * kSC < b1;
+                if (!complete) crossj = (int32_t)jj;
+                return;
+            }
+            ++jj;
+        }
+    };
+    {
+        bool cont = false;
+        if (ja > 0) {
+            // the sequence that contains token b0, started before it: its
+            // sub-chunks that start in [b0, b1)
+            const uint32_t c = cu_scalar(cu, ja - 1, n), e = cu_scalar(cu, ja, n);
+            if (c < b0 && e > b0) {
+                const uint32_t k = (b0 - c + kSC - 1) / kSC;
+                const uint32_t st = c + k * kSC;
+                if (st < e && st < b1) {
+                    j = ja - 1; cj = c; ej = e; kidx = k; ss = st; off = 0;
+                    se = st + kSC < e ? st + kSC : e;
+                    complete = false;
+                    cont = true;
+                }
+            }
+        }
+        if (!cont) enter(ja);
+    }
+    // The next piece of the walk, then advance.
+    auto next_rec = [&](PieceRec& r) {
+        r.start = ss + off;
+        const uint32_t left = se - r.start;
+        const bool lastp = left <= (uint32_t)kPiece;
+        const uint32_t flags = (lastp ? kLastPiece : 0u) | (complete ? kComplete : 0u) |
+                               (lastp && se == ej ? kLastSub : 0u);
+        r.lim_flags = (lastp ? left : (uint32_t)kPiece) | (flags << 16);
+        // slot: floor(c_j / SC) + j + k with c_j + k SC < c_{j+1} <= n and
+        // j < s (clamped values), so below floor(n / SC) + s + 1
+        r.id = complete ? j : cj / kSC + j + kidx;
+        if (!lastp) { off += kPiece; return; }
+        ++kidx; ss = se; off = 0;
+        if (ss < ej) {
+            // later sub-chunks of this sequence start in later waves' ranges
+            if (ss >= b1) { done = true; return; }
+            se = ss + kSC < ej ? ss + kSC : ej;
+            return;
+        }
+        enter(j + 1);
+    };
+
+    Acc A;
+    A.zero();
+    A.sabs = 0.0;
+    A.mx = 0.0;
+    uint32_t nstage = 0;                           // staged entries (uniform)
+    // Buffer descriptors based at the wave's first token: every copy's
+    // offset is 32-bit (the wave's tokens span less than a range plus a
+    // sub-chunk past it), and the extents end at the arrays' ends.
+    const uint32_t s0 = done ? 0u : ss;
+    const uint64_t span = (uint64_t)(n - s0);
+    const int ext4 = (int)(uint32_t)(span * 4 < 0xffffffffull ? span * 4 : 0xffffffffull);
+    const __amdgpu_buffer_rsrc_t rlt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(lt + s0), (short)0, ext4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rlr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(lr + s0), (short)0, ext4, kRsrcWord3);
+    // mask: kMaskDw (n >= 4) reads lane-quads, the last of which sits on the
+    // array's last four bytes, so its base is at most n - 4
+    const uint32_t mbase = kMaskDw ? (s0 < n - 4 ? s0 : n - 4) : s0;
+    const uint32_t mlast = kMaskDw ? n - 4 - mbase : (n > s0 ? n - 1 - s0 : 0u);
+    const __amdgpu_buffer_rsrc_t rm =
+        kMask ? __builtin_amdgcn_make_buffer_rsrc((void*)(mask + mbase), (short)0,
+                                                  (int)(n - mbase), kRsrcWord3)
+              : rlt;
+    constexpr int kLoads = PieceLoads<kMask, kMaskDw>::value;
+    const bool clip_rare = prm.log_c >= 0.03125;
+    // No global store happens between a round's first copy and its last
+    // fold, and every issue makes the same kLoads copies: a slot's copies
+    // are complete once at most (kBufs - 1) kLoads copies are in flight, and
+    // each fold waits for exactly that.  Results wait in LDS; a round stops
+    // issuing when the stage could overflow, and the stage is written out
+    // between rounds.
+    for (;;) {
+        if (!done) {
+            bool paused = false;
+            PieceRec r0, r1, r2;
+            next_rec(r0);
+            // Past the round's end every issue copies the round's first piece
+            // again (never folded): the same copies on every path.
+            const uint32_t d_start = r0.start;
+            dma_piece<kMask, kMaskDw>(rlt, rlr, rm, ring[wv][0], d_start - s0, d_start - mbase,
+                                      mlast, lane);
+            auto issue = [&](unsigned char* slot, PieceRec& r) {
+                const bool go = !done && !paused;
+                if (go) next_rec(r);
+                else r.lim_flags = 0u;
+                const uint32_t st = go ? r.start : d_start;
+                dma_piece<kMask, kMaskDw>(rlt, rlr, rm, slot, st - s0, st - mbase, mlast, lane);
+            };
+            issue(ring[wv][1], r1);
+            issue(ring[wv][2], r2);
+            // Fold the piece in slot (if any).  The slot is refilled as soon as
+            // its tokens are in registers, before the fold, so the copy runs
+            // under the fold's arithmetic.
+            auto step = [&](unsigned char* slot, PieceRec& r) -> bool {
+                const PieceRec cur = r;
+                const uint32_t lim = cur.lim_flags & 0xffffu, flags = cur.lim_flags >> 16;
+                if (lim == 0) return false;
+                uint32_t mshift = 0;
+                if constexpr (kMask && kMaskDw) {
+                    // lane-quads past the array's last four bytes were read
+                    // from there (uniform test: only the array's last piece)
+                    if (cur.start - mbase + 4u * (kWave - 1) > mlast) {
+                        const uint32_t mo = cur.start - mbase + 4u * (uint32_t)lane;
+                        mshift = mo > mlast ? (mo - mlast < 3u ? mo - mlast : 3u) : 0u;
+                    }
+                }
+                wait_vmcnt<(kBufs - 1) * kLoads>();
+                Regs g;
+                read_slot<kMask, kMaskDw>(g, slot, lane, mshift);
+                issue(slot, r);
+                if constexpr (kTok) {
+                    if (lim == (uint32_t)kPiece)
+                        fold_piece<kTok, kMask, true, false>(A, g, cur.start, lim, lane, prm, tok);
+                    else
+                        fold_piece<kTok, kMask, false, false>(A, g, cur.start, lim, lane, prm, tok);
+                } else if (clip_rare) {
+                    if (lim == (uint32_t)kPiece)
+                        fold_piece<kTok, kMask, true, true>(A, g, cur.start, lim, lane, prm, tok);
+                    else
+                        fold_piece<kTok, kMask, false, true>(A, g, cur.start, lim, lane, prm, tok);
+                } else {
+                    if (lim == (uint32_t)kPiece)
+                        fold_piece<kTok, kMask, true, false>(A, g, cur.start, lim, lane, prm, tok);
+                    else
+                        fold_piece<kTok, kMask, false, false>(A, g, cur.start, lim, lane, prm, tok);
+                }
+                if (flags & kLastPiece) {
+                    const SubPartial q = finish(A, prm.clip_c, lane, scratch[wv]);
+                    A.zero();
+                    if (flags & kComplete) {
+                        if (lane == 0) seq_add(seq_lds[wv], q);
+                        if (flags & kLastSub) {
+                            if (lane == 0) {
+                                const SeqSums& a = seq_lds[wv];
+                                StageEnt& e = stage[wv][nstage];
+                                e.q.sd = a.sd; e.q.sk2 = a.sk2; e.q.sk3 = a.sk3; e.q.sw = a.sw;
+                                e.q.nvalid = (int32_t)a.nvalid; e.q.nclip = (int32_t)a.nclip;
+                                e.q.nnan = (int32_t)a.nnan; e.q.pad = 0;
+                                e.id = cur.id; e.kind = 0u;
+                                seq_lds[wv] = seq_zero();
+                            }
+                            ++nstage;
+                        }
+                    } else {
+                        if (lane == 0) {
+                            StageEnt& e = stage[wv][nstage];
+                            e.q = q; e.id = cur.id; e.kind = 1u;
+                        }
+                        ++nstage;
+                    }
+                    // room for what the pieces in flight (issued ones included)
+                    // can still finish
+                    if (nstage + kBufs >= (uint32_t)kStage) paused = true;
+                }
+                return true;
+            };
+            for (;;) {
+                if (!step(ring[wv][0], r0)) break;
+                if (!step(ring[wv][1], r1)) break;
+                if (!step(ring[wv][2], r2)) break;
+            }
+        }
+        // write the staged results out, one per lane
+        {
+            BatchAcc c = acc_zero();
+            if ((uint32_t)lane < nstage) {
+                const StageEnt e = stage[wv][lane];
+                if (e.kind == 0u) {
+                    SeqSums a;
+                    a.sd = e.q.sd; a.sk2 = e.q.sk2; a.sk3 = e.q.sk3; a.sw = e.q.sw;
+                    a.nvalid = e.q.nvalid; a.nclip = e.q.nclip; a.nnan = e.q.nnan;
+                    seq_finish(e.id, a, prm, so, true, c);
+                } else {
+                    slots[e.id] = e.q;
+                }
+            }
+            if (nstage > 0) {
+                wave_fold_acc(c);
+                if (lane == 0) acc_add(acc_lds[wv], c);
+            }
+            nstage = 0;
+        }
+        if (done) break;
+    }
+    wait_vmcnt<0>();                               // no copy in flight into LDS at the end
+    const double wsabs = bfly_sum(A.sabs), wmx = bfly_max(A.mx);
+    if (lane == 0) {
+        BatchAcc c = acc_lds[wv];
+        c.sabs += wsabs;
+        c.maxabs = fmax(c.maxabs, wmx);
+        wpart[w] = c;
+        cross[w] = crossj;
+    }
+}
+
+__global__ void __launch_bounds__(kFinBlock)
+stats_final_kernel(const int32_t* __restrict__ cu, uint32_t n, uint32_t s, StatsParamsDev prm,
+                   const SubPartial* __restrict__ slots, uint64_t nslots,
+                   const BatchAcc* __restrict__ wpart, const int32_t* __restrict__ cross,
+                   uint32_t nwaves, SeqOut so, BatchAcc* __restrict__ blk,
+                   uint32_t* __restrict__ ticket, double* __restrict__ out) {
+    __shared__ BatchAcc buf[kFinBlock];
+    __shared__ uint32_t is_last;
+    const uint32_t w = blockIdx.x * kFinBlock + threadIdx.x;
+    BatchAcc c = acc_zero();
+    if (w < nwaves) {
+        c = wpart[w];
+        const int32_t jj = cross[w];
+        if (jj >= 0 && (uint32_t)jj < s) {
+            // the sequence that starts in wave w's range and ends past it
+            const uint32_t c0 = clamp_c(cu[jj], n), e0 = clamp_c(cu[jj + 1], n);
+            SeqSums a = seq_zero();
+            if (e0 > c0) {
+                const uint32_t K = (e0 - c0 + kSC - 1) / kSC;
+                const uint64_t base = (uint64_t)(c0 / kSC) + (uint32_t)jj;
+                for (uint32_t k = 0; k < K && base + k < nslots; ++k) seq_add(a, slots[base + k]);
+            }
+            seq_finish((uint32_t)jj, a, prm, so, true, c);
         }
     }
     buf[threadIdx.x] = c;
     __syncthreads();
     block_tree(buf);
-    if (threadIdx.x == 0) blk[blockIdx.x] = buf[0];
-}
-
-__global__ void __launch_bounds__(kFinBlock)
-batch_finalize_kernel(const BatchAcc* __restrict__ blk, int64_t nblk, double* __restrict__ out) {
-    __shared__ BatchAcc buf[kFinBlock];
-    BatchAcc c = acc_zero();
-    for (int64_t i = threadIdx.x; i < nblk; i += kFinBlock) acc_add(c, blk[i]);
+    if (!out) return;
+    // the last block to get here folds every block's partial
+    if (threadIdx.x == 0) {
+        blk[blockIdx.x] = buf[0];
+        __threadfence();
+        is_last = atomicAdd(ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    c = acc_zero();
+    for (uint32_t i = threadIdx.x; i < gridDim.x; i += kFinBlock) acc_add(c, blk[i]);
     buf[threadIdx.x] = c;
     __syncthreads();
     block_tree(buf);
@@ -657,36 +985,67 @@ batch_finalize_kernel(const BatchAcc* __restrict__ blk, int64_t nblk, double* __
     }
 }
 
+// Streaming waves the current device holds at once (the kernel's blocks
+// per CU from the occupancy query, times its CUs, times kStreamWaves),
+// looked up once per device.
+hipError_t stream_waves_per_device(bool with_mask, int64_t* out) {
+    constexpr int kDevs = 64;
+    static std::atomic<int64_t> cached[2][kDevs];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevs) return hipErrorInvalidDevice;
+    int64_t v = cached[with_mask][dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, blocks = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        // the mask variant has the larger LDS footprint of the two that
+        // stream large batches (with or without per-token outputs alike)
+        e = with_mask ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &blocks, stats_stream_kernel<false, true, true>, kWave * kStreamWaves, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &blocks, stats_stream_kernel<false, false, true>, kWave * kStreamWaves, 0);
+        if (e != hipSuccess) return e;
+        v = (int64_t)cus * (blocks > 0 ? blocks : 1) * kStreamWaves;
+        cached[with_mask][dev].store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return hipSuccess;
+}
+
 }  // namespace
+
+// Tokens per streaming wave (a multiple of kPiece, at least kMinRange) and
+// the number of waves, for n tokens and at most `waves` waves.
+void split_tokens(int64_t n, int64_t waves, int64_t* range, int64_t* nwaves) {
+    if (waves < 1) waves = 1;
+    int64_t r = (n + waves - 1) / waves;
+    r = (r + kPiece - 1) / kPiece * kPiece;
+    *range = r < kMinRange ? kMinRange : r;
+    *nwaves = n > 0 ? (n + *range - 1) / *range : 1;
+}
 
 bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     if (n < 0 || s < 0 || s > INT32_MAX - 1 || n > INT32_MAX) return false;
     p->n = n;
     p->s = s;
-    // sum over sequences of ceil(len / SC) <= n / SC + s
-    p->tmax = (n + kSubChunk - 1) / kSubChunk + s;
-    p->nblk_scan = (s + kScanBlock - 1) / kScanBlock;
-    p->nblk_seq = (s + kFinBlock - 1) / kFinBlock;
-    p->spw = subs_per_wave(p->tmax);
-    p->nwaves = ((p->tmax + p->spw - 1) / p->spw + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
-    {
-        const int64_t nbw = (p->nwaves + kWavesPerFinBlock - 1) / kWavesPerFinBlock;
-        p->nblk_fin = p->nblk_seq > nbw ? p->nblk_seq : nbw;
-    }
+    // the workspace holds the most waves any device gets
+    split_tokens(n, kMaxStreamWaves, &p->range, &p->nwaves);
+    // slot floor(c_j / SC) + j + k <= floor((n - 1) / SC) + s - 1
+    p->nslots = n / kSubChunk + s + 1;
+    p->nblk_fin = (p->nwaves + kFinBlock - 1) / kFinBlock;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
         off += align_up(bytes > 0 ? bytes : 1, 256);
         return o;
     };
-    p->bsum_off = take((size_t)p->nblk_scan * 4);
-    p->boff_off = take((size_t)p->nblk_scan * 4);
-    p->total_off = take(4);
-    p->seqoff_off = take((size_t)s * 4);
-    p->desc_off = take((size_t)p->tmax * sizeof(SubDesc));
-    p->part_off = take((size_t)p->tmax * sizeof(SubPartial));
-    p->blk_off = take((size_t)(p->nblk_fin > 0 ? p->nblk_fin : 1) * sizeof(BatchAcc));
-    p->wpart_off = take((size_t)p->nwaves * sizeof(double2));
+    p->slot_off = take((size_t)p->nslots * sizeof(SubPartial));
+    p->wpart_off = take((size_t)p->nwaves * sizeof(BatchAcc));
+    p->cross_off = take((size_t)p->nwaves * sizeof(int32_t));
+    p->blk_off = take((size_t)p->nblk_fin * sizeof(BatchAcc));
+    p->ticket_off = take(sizeof(uint32_t));
     p->total_bytes = off;
     return true;
 }
@@ -696,52 +1055,48 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
                                  const StatsParamsDev& prm, const TokenOutPtrs& tok,
                                  const SeqOutPtrs& seq, double* batch, void* workspace,
                                  hipStream_t st) {
+    if (p.s <= 0) return hipSuccess;               // no sequence: nothing to write
     unsigned char* ws = (unsigned char*)workspace;
-    uint32_t* bsum = (uint32_t*)(ws + p.bsum_off);
-    uint32_t* boff = (uint32_t*)(ws + p.boff_off);
-    uint32_t* total = (uint32_t*)(ws + p.total_off);
-    uint32_t* seq_off = (uint32_t*)(ws + p.seqoff_off);
-    SubDesc* desc = (SubDesc*)(ws + p.desc_off);
-    SubPartial* partial = (SubPartial*)(ws + p.part_off);
+    SubPartial* slots = (SubPartial*)(ws + p.slot_off);
+    BatchAcc* wpart = (BatchAcc*)(ws + p.wpart_off);
+    int32_t* cross = (int32_t*)(ws + p.cross_off);
     BatchAcc* blk = (BatchAcc*)(ws + p.blk_off);
-    double2* wpart = (double2*)(ws + p.wpart_off);
-    const bool streamed = p.s > 0 && p.n > 0;
+    uint32_t* ticket = (uint32_t*)(ws + p.ticket_off);
     TokOut to{tok.delta, tok.ratio, tok.k1, tok.k2, tok.k3, tok.tis_w, tok.clipped};
     SeqOut so{seq.n_valid, seq.n_clipped, seq.n_nan, seq.mean_delta, seq.mean_k1,
               seq.mean_k2, seq.mean_k3, seq.mean_tis_w, seq.reject, seq.reject_k3};
-    if (p.s > 0) {
-        hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
-                           cu, p.n, p.s, bsum);
-        hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kScanBlock), 0, st, bsum, p.nblk_scan,
-                           boff, total);
-        hipLaunchKernelGGL(plan_write_kernel, dim3((unsigned)p.nblk_scan), dim3(kScanBlock), 0, st,
-                           cu, p.n, p.s, p.tmax, boff, seq_off, desc);
-        if (p.n > 0) {
-            const uint32_t spw = p.spw;
-            const dim3 grid((unsigned)(p.nwaves / kStreamWaves));
-            const dim3 bdim(kWave * kStreamWaves);
-            const bool want_tok = to.delta || to.ratio || to.k1 || to.k2 || to.k3 || to.tis_w ||
-                                  to.clipped;
-            if (want_tok && mask)
-                hipLaunchKernelGGL((stats_stream_kernel<true, true>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
-            else if (want_tok)
-                hipLaunchKernelGGL((stats_stream_kernel<true, false>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
-            else if (mask)
-                hipLaunchKernelGGL((stats_stream_kernel<false, true>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
-            else
-                hipLaunchKernelGGL((stats_stream_kernel<false, false>), grid, bdim, 0, st, lt, lr,
-                                   mask, desc, total, (uint32_t)p.tmax, prm, to, partial, spw, wpart);
-        }
-        hipLaunchKernelGGL(seq_finalize_kernel, dim3((unsigned)p.nblk_fin), dim3(kFinBlock), 0, st,
-                           cu, p.n, p.s, p.tmax, prm, seq_off, partial, (const double2*)wpart,
-                           streamed ? p.nwaves : (int64_t)0, so, blk);
+    const uint32_t n = (uint32_t)p.n, s = (uint32_t)p.s;
+    // every streaming wave resident at once: as many waves as the device
+    // holds, at most the plan's (which sized the workspace)
+    int64_t waves_dev = 0;
+    {
+        const hipError_t e = stream_waves_per_device(mask != nullptr, &waves_dev);
+        if (e != hipSuccess) return e;
     }
-    if (batch)
-        hipLaunchKernelGGL(batch_finalize_kernel, dim3(1), dim3(kFinBlock), 0, st, blk,
-                           p.s > 0 ? p.nblk_fin : (int64_t)0, batch);
+    int64_t range64 = 0, nw64 = 0;
+    split_tokens(p.n, waves_dev < kMaxStreamWaves ? waves_dev : kMaxStreamWaves, &range64, &nw64);
+    const uint32_t range = (uint32_t)range64, nw = (uint32_t)nw64;
+    const uint64_t nslots = (uint64_t)p.nslots;
+    const dim3 grid((nw + kStreamWaves - 1) / kStreamWaves);
+    const dim3 bdim(kWave * kStreamWaves);
+    const bool want_tok = to.delta || to.ratio || to.k1 || to.k2 || to.k3 || to.tis_w ||
+                          to.clipped;
+#define TIM_STATS_STREAM(KT, KM, KD)                                                            \
+    hipLaunchKernelGGL((stats_stream_kernel<KT, KM, KD>), grid, bdim, 0, st, lt, lr, mask, cu, n,  \
+                       s, range, nw, prm, to, so, slots, wpart, cross, ticket)
+    // the mask is read four bytes per lane once the array has four
+    const bool mdw = n >= 4;
+    if (want_tok && mask && mdw) TIM_STATS_STREAM(true, true, true);
+    else if (want_tok && mask) TIM_STATS_STREAM(true, true, false);
+    else if (want_tok) TIM_STATS_STREAM(true, false, true);
+    else if (mask && mdw) TIM_STATS_STREAM(false, true, true);
+    else if (mask) TIM_STATS_STREAM(false, true, false);
+    else TIM_STATS_STREAM(false, false, true);
+#undef TIM_STATS_STREAM
+    hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((nw + kFinBlock - 1) / kFinBlock)),
+                       dim3(kFinBlock), 0, st, cu,
+                       n, s, prm, (const SubPartial*)slots, nslots, (const BatchAcc*)wpart,
+                       (const int32_t*)cross, nw, so, blk, ticket, batch);
     return hipGetLastError();
 }
 

@@ -84,17 +84,19 @@ struct StatsParamsDev {
     double clip_c, log_c, seq_lo, seq_hi, seq_k3_hi;
 };
 
-// Workspace layout of tim_mismatch_stats (offsets 256-byte aligned): scan
-// block sums and offsets, the sub-chunk count, each sequence's first
-// sub-chunk index, the sub-chunk descriptors and partials (at most
-// tmax = ceil(n / kSubChunk) + s of each), and per-block batch partials.
+// Workspace layout of tim_mismatch_stats (offsets 256-byte aligned): one
+// slot per possible sub-chunk (sequence j's sub-chunk k sits at slot
+// floor(c_j / kSubChunk) + j + k, strictly increasing, fewer than
+// floor(n / kSubChunk) + s + 1 slots), and per streaming wave its batch
+// partial and the sequence it leaves to the finalize kernel; then the
+// finalize blocks' batch partials and their completion ticket.
 struct StatsPlan {
-    int64_t n, s, tmax, nblk_scan, nblk_seq;
-    int64_t nblk_fin;    // finalize blocks: 256 sequences and 1024 streaming waves each
-    uint32_t spw;        // sub-chunk descriptors per streaming wave
-    int64_t nwaves;      // streaming waves launched (a multiple of the waves per block)
-    size_t bsum_off, boff_off, total_off, seqoff_off, desc_off, part_off, blk_off, wpart_off,
-        total_bytes;
+    int64_t n, s;
+    int64_t range;       // tokens per streaming wave (a multiple of 256)
+    int64_t nwaves;      // streaming waves, >= 1
+    int64_t nslots;      // sub-chunk slots
+    int64_t nblk_fin;    // finalize blocks (256 streaming waves each)
+    size_t slot_off, wpart_off, cross_off, blk_off, ticket_off, total_bytes;
 };
 
 bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p);

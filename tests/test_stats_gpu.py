@@ -209,3 +209,52 @@ def test_end_to_end_small_against_oracle():
     close = np.minimum(np.abs(md - sp.seq_lo), np.abs(md - sp.seq_hi)) < 2e-4
     diff = res["seq"]["reject"].cpu().numpy() != ref["seq"]["reject"]
     assert not np.any(diff & ~close)
+
+
+def _partition(name):
+    """Sequence lengths that put sequence, sub-chunk (1024 tokens) and
+    streaming-range (512 tokens at these sizes) boundaries in awkward places."""
+    rng = np.random.default_rng(31)
+    if name == "one_sequence":
+        return [300001]
+    if name == "all_one_token":
+        return [1] * 5000
+    if name == "empties_everywhere":
+        lens = []
+        for i in range(300):
+            lens += [0] * int(rng.integers(0, 3)) + [int(rng.integers(1, 3000))]
+        return [0, 0] + lens + [0, 0, 0]
+    if name == "aligned":
+        return [512] * 40 + [1024] * 20 + [2048] * 10 + [513, 511, 1023, 1025]
+    if name == "all_empty":
+        return [0] * 7
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["one_sequence", "all_one_token", "empties_everywhere",
+                                  "aligned", "all_empty"])
+def test_partition_edges_against_oracle(name):
+    lens = _partition(name)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    n = int(cu[-1])
+    g = torch.Generator(device=DEV).manual_seed(77)
+    lt = -torch.rand(n, generator=g, device=DEV) * 5
+    lr = lt + torch.randn(n, generator=g, device=DEV) * 0.004
+    mask = (torch.rand(n, generator=g, device=DEV) > 0.1).to(torch.uint8)
+    lo, hi = -0.0015, 0.0015
+    say(f"partition {name}: n {n}, s {len(lens)}")
+    res, ref = run_both(lt, lr, mask, cu, 1.5, lo, hi)
+    compare(res, ref, lo, hi, cu, f"partition {name}")
+    # each sequence alone gives the bits it has in the batch
+    cu_h = cu.cpu().numpy()
+    for j in [0, len(lens) // 2, len(lens) - 1]:
+        a, b = int(cu_h[j]), int(cu_h[j + 1])
+        one = tim.tim_mismatch_stats(lt[a:b].contiguous(), lr[a:b].contiguous(),
+                                     mask[a:b].contiguous(),
+                                     torch.tensor([0, b - a], dtype=torch.int32, device=DEV),
+                                     tis_clip=1.5, seq_bounds=(lo, hi))
+        torch.cuda.synchronize()
+        for k in ("mean_delta", "mean_k3", "mean_tis_w", "n_valid"):
+            x = res["seq"][k][j:j + 1].cpu()
+            y = one["seq"][k].cpu()
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"{name} seq {j} {k}"
