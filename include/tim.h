@@ -385,7 +385,8 @@ size_t tim_stats_workspace_bytes(int64_t n, int64_t s);
  *  finite positive number, seq_lo > seq_hi or a NaN bound (seq_k3_hi
  *  included), null lt/lr when
  *  n > 0, null cu_seqlens; TIM_EUNSUPPORTED for n or s beyond int32.
- *  n == 0 and s == 0 returns TIM_OK without a launch.
+ *  n == 0 and s == 0 returns TIM_OK without a launch; TIM_EUNSUPPORTED also
+ *  when floor(n / 1024) + s + 1 reaches 2^31.
  *
  * delta is computed in fp64 from the fp32 inputs, so both signs and the
  * clip decision are exact; exp/expm1 are evaluated in fp64.

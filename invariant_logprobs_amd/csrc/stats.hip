@@ -26,7 +26,7 @@
 //      cu_seqlens with a 64-way search, then walks sequences and sub-chunks
 //      in token order and folds every sub-chunk that starts in its range: the
 //      tokens stream in 256-token pieces through a ring of kBufs LDS slots
-//      filled by LDS DMA (lane l folds piece offsets 4 l .. 4 l + 3), and a
+//      filled by LDS DMA (lane l folds piece offsets l + 64 i), and a
 //      finished sub-chunk is folded across the wave with a fixed LDS
 //      transpose + DPP tree.  A sequence whose sub-chunks all start in the range is finished
 //      by the wave (per-sequence outputs, and its share of the batch sums in
@@ -215,58 +215,93 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// The lane's four tokens of a ring slot, read in one asm block: the slot is
-// filled by LDS DMA, which the compiler's own waits would otherwise guard
-// with a wait for every copy in flight.  The caller has waited for the
-// slot's copies.  lt and lr come out as float vectors: a bit cast of a
-// single element of an integer asm output gives element 0 with this
-// compiler.  mshift: bytes to drop from a kMaskDw mask quad (non-zero only
-// for the lane-quads placed back on the array's last four bytes).
-template <bool kMask, bool kMaskDw>
-__device__ __forceinline__ void read_slot(Regs& r, const unsigned char* slot, int lane,
-                                          uint32_t mshift) {
-    const uint32_t a = lds_addr(slot) + 16u * (uint32_t)lane;
-    f32x4 x, y;
+// Rows 0 .. 2 kHalf - 1 of a ring slot for lane l (row i: the piece's token
+// 64 i + l), read in asm: the slot is filled by LDS DMA, which the
+// compiler's own waits would otherwise guard with a wait for every copy in
+// flight.  The caller has waited for the slot's copies.  kMaskDw: the mask
+// byte of token t sits at byte t of the slot's mask, except in the array's
+// last piece (tail), where a lane-quad that reaches past the array's end
+// was read from the array's last four bytes: token t of such a quad q sits
+// at byte 4 q + (mst + t - mlast) (tokens beyond the array read bytes of
+// their own quad and are never counted).
+template <int kRows, bool kMask, bool kMaskDw>
+__device__ __forceinline__ void read_slot(Regs& r, const unsigned char* slot, int lane, bool tail,
+                                          uint32_t mst, uint32_t mlast) {
+    static_assert(kRows == 2 || kRows == 4, "two or four rows");
+    const uint32_t base = lds_addr(slot);
+    const uint32_t a = base + 4u * (uint32_t)lane;
+    if constexpr (kRows == 4)
+        asm volatile(
+            "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
+            "ds_read_b32 %2, %8 offset:512\n\tds_read_b32 %3, %8 offset:768\n\t"
+            "ds_read_b32 %4, %8 offset:1024\n\tds_read_b32 %5, %8 offset:1280\n\t"
+            "ds_read_b32 %6, %8 offset:1536\n\tds_read_b32 %7, %8 offset:1792"
+            : "=&v"(r.x[0]), "=&v"(r.x[1]), "=&v"(r.x[2]), "=&v"(r.x[3]), "=&v"(r.y[0]),
+              "=&v"(r.y[1]), "=&v"(r.y[2]), "=&v"(r.y[3])
+            : "v"(a)
+            : "memory");
+    else
+        asm volatile(
+            "ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:256\n\t"
+            "ds_read_b32 %2, %4 offset:1024\n\tds_read_b32 %3, %4 offset:1280"
+            : "=&v"(r.x[0]), "=&v"(r.x[1]), "=&v"(r.y[0]), "=&v"(r.y[1])
+            : "v"(a)
+            : "memory");
     if constexpr (kMask && kMaskDw) {
-        uint32_t m;
-        asm volatile(
-            "ds_read_b128 %0, %3\n\t"
-            "ds_read_b128 %1, %3 offset:1024\n\t"
-            "ds_read_b32 %2, %4 offset:2048\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(x), "=&v"(y), "=&v"(m)
-            : "v"(a), "v"(lds_addr(slot) + 4u * (uint32_t)lane)
-            : "memory");
-        m >>= 8u * mshift;                         // mshift <= 3
+        if (!tail) {
+            const uint32_t b = base + (uint32_t)lane;
+            if constexpr (kRows == 4)
+                asm volatile(
+                    "ds_read_u8 %0, %4 offset:2048\n\tds_read_u8 %1, %4 offset:2112\n\t"
+                    "ds_read_u8 %2, %4 offset:2176\n\tds_read_u8 %3, %4 offset:2240\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(r.m[0]), "=&v"(r.m[1]), "=&v"(r.m[2]), "=&v"(r.m[3])
+                    : "v"(b)
+                    : "memory");
+            else
+                asm volatile(
+                    "ds_read_u8 %0, %2 offset:2048\n\tds_read_u8 %1, %2 offset:2112\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(r.m[0]), "=&v"(r.m[1])
+                    : "v"(b)
+                    : "memory");
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.m[i] = (m >> (8 * i)) & 0xffu;
+            for (int i = 0; i < kRows; ++i) {
+                const uint32_t t = 64u * i + (uint32_t)lane;
+                const uint32_t q = t >> 2;
+                const uint32_t mo = mst + 4u * q;
+                uint32_t pos = t;
+                if (mo > mlast) {
+                    const uint32_t k = mst + t - mlast;
+                    pos = 4u * q + (k < 3u ? k : 3u);
+                }
+                asm volatile("ds_read_u8 %0, %1 offset:2048\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(r.m[i])
+                             : "v"(base + pos)
+                             : "memory");
+            }
+        }
     } else if constexpr (kMask) {
-        u32x4 m;
-        asm volatile(
-            "ds_read_b128 %0, %3\n\t"
-            "ds_read_b128 %1, %3 offset:1024\n\t"
-            "ds_read_b128 %2, %3 offset:2048\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(x), "=&v"(y), "=&v"(m)
-            : "v"(a)
-            : "memory");
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.m[i] = m[i];
+        if constexpr (kRows == 4)
+            asm volatile(
+                "ds_read_b32 %0, %4 offset:2048\n\tds_read_b32 %1, %4 offset:2304\n\t"
+                "ds_read_b32 %2, %4 offset:2560\n\tds_read_b32 %3, %4 offset:2816\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r.m[0]), "=&v"(r.m[1]), "=&v"(r.m[2]), "=&v"(r.m[3])
+                : "v"(a)
+                : "memory");
+        else
+            asm volatile(
+                "ds_read_b32 %0, %2 offset:2048\n\tds_read_b32 %1, %2 offset:2304\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r.m[0]), "=&v"(r.m[1])
+                : "v"(a)
+                : "memory");
     } else {
-        asm volatile(
-            "ds_read_b128 %0, %2\n\t"
-            "ds_read_b128 %1, %2 offset:1024\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(x), "=&v"(y)
-            : "v"(a)
-            : "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.m[i] = 1u;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r.x[i] = x[i];
-        r.y[i] = y[i];
+        for (int i = 0; i < kRows; ++i) r.m[i] = 1u;
     }
 }
 
@@ -287,19 +322,21 @@ __device__ __forceinline__ double max_abs(double m, double d) {
     return r;
 }
 
-// fma(a, b, c) as one v_fma_f64 with c in scalar registers (the compiler
-// otherwise copies loop-invariant constants before a two-address fmac)
+// fma(a, b, c) as one v_fma_f64 with c in vector registers, held across
+// the loop (the compiler otherwise copies loop-invariant constants before a
+// two-address fmac, and scalar registers are the scarcer kind here)
 __device__ __forceinline__ double fma_s(double a, double b, double c) {
     double r;
-    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
     return r;
 }
 
-// Fold a piece of a sub-chunk: lane l holds piece offsets 4 l + i
-// (i = 0..3, "row" i), lim of the piece's tokens lie inside the sub-chunk
-// (1 <= lim <= 256), tok0 is the piece's first token.  Lane l adds its
-// offsets in ascending order; the rows are independent until then, so their
-// arithmetic interleaves.  A token that does not count (outside the
+// Fold rows i0 and i0 + 1 of a piece of a sub-chunk: lane l of row i holds
+// piece offset 64 i + l; lim of the piece's tokens lie inside the sub-chunk
+// (64 i0 < lim <= 256), tok0 is the piece's first token.  A piece is folded
+// pair by pair, the second pair only when lim > 128, so lane l adds its
+// offsets in ascending order; the two rows of a pair are independent until
+// then, so their arithmetic interleaves.  A token that does not count (outside the
 // sub-chunk, masked out or non-finite) gets d = 0, which makes its d, d^2,
 // k3 and |d| contributions exactly 0 with no further selects.  Counts are
 // popcounts of the wave masks; the rare ones (non-finite, clipped) are
@@ -307,25 +344,25 @@ __device__ __forceinline__ double fma_s(double a, double b, double c) {
 // is accumulated as d^2 and halved once (a power-of-two scale: exact).  For
 // the truncated weight only the clipped tokens' e^d - 1 is summed (rare
 // path); the unclipped sum is recovered as (sum d + sum k3) - that.
-template <bool kTok, bool kMask, bool kFull, bool kClipRare>
-__device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg, uint32_t tok0, uint32_t lim,
+template <int kI0, bool kTok, bool kMask, bool kFull, bool kClipRare>
+__device__ __forceinline__ void fold_pair(Acc& A, const Regs& rg, uint32_t tok0, uint32_t lim,
                                           int lane, const StatsParamsDev& prm,
                                           const TokOut& tok) {
     // kClipRare: log C >= 1/32, so a clipped token (d > log C) is among the
     // |d| > 1/32 tokens of the rare branch and needs no test of its own
     static_assert(!(kTok && kClipRare), "per-token outputs test the clip on every row");
-    double draw[4], d[4], dp[4];
-    uint64_t m_fin[4];
-    uint64_t m_clip[kClipRare ? 1 : 4], m_sc[kTok ? 4 : 1];
-    double k3x[kTok ? 4 : 1];                          // per-token k3, for the outputs
+    double draw[2], d[2], dp[2];
+    uint64_t m_fin[2];
+    uint64_t m_clip[kClipRare ? 1 : 2], m_sc[kTok ? 2 : 1];
+    double k3x[kTok ? 2 : 1];                      // per-token k3, for the outputs
     uint64_t rare = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        draw[i] = (double)rg.x[i] - (double)rg.y[i];
+    for (int i = 0; i < 2; ++i) {
+        draw[i] = (double)rg.x[kI0 + i] - (double)rg.y[kI0 + i];
         // lane predicates as wave masks: each ballot is one compare, the
         // combinations are scalar, and inverse_ballot reads a lane's bit back
-        uint64_t sc = kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[i] != 0) : ~0ull;
-        if constexpr (!kFull) sc &= __builtin_amdgcn_ballot_w64((uint32_t)(4 * lane + i) < lim);
+        uint64_t sc = kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[kI0 + i] != 0) : ~0ull;
+        if constexpr (!kFull) sc &= __builtin_amdgcn_ballot_w64((uint32_t)(64 * (kI0 + i) + lane) < lim);
         m_fin[i] = sc & finite_mask(draw[i]);
         A.nvalid += (uint32_t)__popcll(m_fin[i]);
         rare |= sc & ~m_fin[i];                        // non-finite: counted in the branch
@@ -346,13 +383,13 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg, uint32_t tok0
     }
     if (rare != 0) {                                   // uniform test, rarely taken
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const uint64_t sc = kTok ? m_sc[i]
-                                     : (kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[i] != 0)
+                                     : (kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[kI0 + i] != 0)
                                               : ~0ull) &
                                            (kFull ? ~0ull
                                                   : __builtin_amdgcn_ballot_w64(
-                                                        (uint32_t)(4 * lane + i) < lim));
+                                                        (uint32_t)(64 * (kI0 + i) + lane) < lim));
             A.nnan += (uint32_t)__popcll(sc & ~m_fin[i]);
             const uint64_t clip = kClipRare
                                       ? m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > prm.log_c)
@@ -381,7 +418,7 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg, uint32_t tok0
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
         A.sd += d[i];
         A.sd2 = fma(d[i], d[i], A.sd2);
         A.sk3 = fma(d[i], dp[i], A.sk3);
@@ -390,8 +427,8 @@ __device__ __forceinline__ void fold_piece(Acc& A, const Regs& rg, uint32_t tok0
     }
     if constexpr (kTok) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t po = (uint32_t)(4 * lane + i);          // offset in the piece
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t po = (uint32_t)(64 * (kI0 + i) + lane);  // offset in the piece
             if (po < lim) {
                 // per-token outputs; a non-finite delta reports exp/expm1 as computed
                 const bool scored = __builtin_amdgcn_inverse_ballot_w64(m_sc[i]);
@@ -620,12 +657,11 @@ struct PieceRec {
 };
 
 // A result waiting in LDS for the wave's next flush: a finished sequence's
-// sums (kind 0, id = its index) or a sub-chunk's sums (kind 1, id = slot).
-struct alignas(16) StageEnt {
-    SubPartial q;
-    uint32_t id, kind, pad0, pad1;
-};
-constexpr int kStage = 16;                      // entries per wave (one per lane at a flush)
+// sums (id = its index) or a sub-chunk's sums (id = its slot), the id kept
+// in the sums' spare word with the kind in its top bit.
+typedef SubPartial StageEnt;
+constexpr uint32_t kSlotKind = 0x80000000u;     // set for a sub-chunk's sums
+constexpr int kStage = 21;                      // entries per wave (one per lane at a flush)
 
 // Contribution of a lane's staged entry to the wave's batch sums, folded
 // over the wave's lanes with a fixed butterfly.
@@ -657,19 +693,14 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     unsigned char ring[kStreamWaves][kBufs][Slot<kMaskDw>::kBytes];
     __shared__ __attribute__((aligned(16))) double scratch[kStreamWaves][kFoldVals * kWave];
     __shared__ StageEnt stage[kStreamWaves][kStage];
-    // per wave, touched by its lane 0 only: the sums of the sequence being
-    // finished, and the wave's share of the batch sums
-    __shared__ SeqSums seq_lds[kStreamWaves];
+    // per wave, touched by its lane 0 only: the wave's share of the batch sums
     __shared__ BatchAcc acc_lds[kStreamWaves];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const uint32_t w = blockIdx.x * kStreamWaves + (uint32_t)wv;
     if (w >= nwaves) return;
     if (w == 0 && lane == 0) *ticket = 0u;         // the finalize kernel's counter
-    if (lane == 0) {
-        seq_lds[wv] = seq_zero();
-        acc_lds[wv] = acc_zero();
-    }
+    if (lane == 0) acc_lds[wv] = acc_zero();
     const bool last = w == nwaves - 1;
     const uint32_t b0 = w * range;
     const uint32_t b1 = last ? n : b0 + range;     // the last wave also owns c_j == n
@@ -693,13 +724,16 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         if (__builtin_amdgcn_ballot_w64(more) != ~0ull) break;
     }
 
-    // ---- the walk over sequences and sub-chunks (wave-uniform state)
-    uint32_t j = 0, cj = 0, ej = 0, kidx = 0, ss = 0, se = 0, off = 0;
+    // ---- the walk over sequences and sub-chunks (wave-uniform state): the
+    // next piece starts at pos, inside the sub-chunk ending at se, of
+    // sequence j ending at ej; id is j if this wave finishes the sequence
+    // (complete), else the current sub-chunk's slot.
+    uint32_t pos = 0, se = 0, ej = 0, j = 0, id = 0;
     bool complete = false, done = false;
     int32_t crossj = -1;                           // owned sequence left to step 2
 
     // Enter the first sequence at or after jj that this wave owns and that
-    // has a token.
+    // has a token (owned empty sequences are written by the pass above).
     auto enter = [&](uint32_t jj) {
         for (;;) {
             if (jj >= s) { done = true; return; }
@@ -707,10 +741,13 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
             if (!last && c >= b1) { done = true; return; }
             const uint32_t e = cu_scalar(cu, jj + 1, n);
             if (e > c) {
-                j = jj; cj = c; ej = e; kidx = 0; ss = c; off = 0;
+                j = jj; ej = e; pos = c;
                 se = c + kSC < e ? c + kSC : e;
                 const uint32_t K = (e - c + kSC - 1) / kSC;
                 complete = last || c + (K - 1) * kSC < b1;
+                // slot of sub-chunk 0: floor(c / SC) + j (below floor(n / SC) +
+                // s + 1 for any clamped c_j <= n and j < s)
+                id = complete ? jj : c / kSC + jj;
                 if (!complete) crossj = (int32_t)jj;
                 return;
             }
@@ -727,9 +764,10 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 const uint32_t k = (b0 - c + kSC - 1) / kSC;
                 const uint32_t st = c + k * kSC;
                 if (st < e && st < b1) {
-                    j = ja - 1; cj = c; ej = e; kidx = k; ss = st; off = 0;
+                    j = ja - 1; ej = e; pos = st;
                     se = st + kSC < e ? st + kSC : e;
                     complete = false;
+                    id = c / kSC + (ja - 1) + k;
                     cont = true;
                 }
             }
@@ -738,21 +776,20 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     }
     // The next piece of the walk, then advance.
     auto next_rec = [&](PieceRec& r) {
-        r.start = ss + off;
-        const uint32_t left = se - r.start;
+        r.start = pos;
+        const uint32_t left = se - pos;
         const bool lastp = left <= (uint32_t)kPiece;
         const uint32_t flags = (lastp ? kLastPiece : 0u) | (complete ? kComplete : 0u) |
                                (lastp && se == ej ? kLastSub : 0u);
         r.lim_flags = (lastp ? left : (uint32_t)kPiece) | (flags << 16);
-        // slot: floor(c_j / SC) + j + k with c_j + k SC < c_{j+1} <= n and
-        // j < s (clamped values), so below floor(n / SC) + s + 1
-        r.id = complete ? j : cj / kSC + j + kidx;
-        if (!lastp) { off += kPiece; return; }
-        ++kidx; ss = se; off = 0;
-        if (ss < ej) {
+        r.id = id;
+        if (!lastp) { pos += kPiece; return; }
+        pos = se;
+        if (pos < ej) {
             // later sub-chunks of this sequence start in later waves' ranges
-            if (ss >= b1) { done = true; return; }
-            se = ss + kSC < ej ? ss + kSC : ej;
+            if (pos >= b1) { done = true; return; }
+            se = pos + kSC < ej ? pos + kSC : ej;
+            if (!complete) ++id;
             return;
         }
         enter(j + 1);
@@ -763,10 +800,11 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     A.sabs = 0.0;
     A.mx = 0.0;
     uint32_t nstage = 0;                           // staged entries (uniform)
+    SeqSums S = seq_zero();                        // the sequence being finished
     // Buffer descriptors based at the wave's first token: every copy's
     // offset is 32-bit (the wave's tokens span less than a range plus a
     // sub-chunk past it), and the extents end at the arrays' ends.
-    const uint32_t s0 = done ? 0u : ss;
+    const uint32_t s0 = done ? 0u : pos;
     const uint64_t span = (uint64_t)(n - s0);
     const int ext4 = (int)(uint32_t)(span * 4 < 0xffffffffull ? span * 4 : 0xffffffffull);
     const __amdgpu_buffer_rsrc_t rlt =
@@ -815,56 +853,50 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 const PieceRec cur = r;
                 const uint32_t lim = cur.lim_flags & 0xffffu, flags = cur.lim_flags >> 16;
                 if (lim == 0) return false;
-                uint32_t mshift = 0;
-                if constexpr (kMask && kMaskDw) {
-                    // lane-quads past the array's last four bytes were read
-                    // from there (uniform test: only the array's last piece)
-                    if (cur.start - mbase + 4u * (kWave - 1) > mlast) {
-                        const uint32_t mo = cur.start - mbase + 4u * (uint32_t)lane;
-                        mshift = mo > mlast ? (mo - mlast < 3u ? mo - mlast : 3u) : 0u;
-                    }
-                }
+                // the array's last piece, whose last lane-quads of the mask
+                // were read from the array's last four bytes
+                const bool tail = kMask && kMaskDw && cur.start - mbase + 4u * (kWave - 1) > mlast;
                 wait_vmcnt<(kBufs - 1) * kLoads>();
                 Regs g;
-                read_slot<kMask, kMaskDw>(g, slot, lane, mshift);
+                if (lim > 2u * kWave)
+                    read_slot<4, kMask, kMaskDw>(g, slot, lane, tail, cur.start - mbase, mlast);
+                else
+                    read_slot<2, kMask, kMaskDw>(g, slot, lane, tail, cur.start - mbase, mlast);
                 issue(slot, r);
-                if constexpr (kTok) {
-                    if (lim == (uint32_t)kPiece)
-                        fold_piece<kTok, kMask, true, false>(A, g, cur.start, lim, lane, prm, tok);
-                    else
-                        fold_piece<kTok, kMask, false, false>(A, g, cur.start, lim, lane, prm, tok);
-                } else if (clip_rare) {
-                    if (lim == (uint32_t)kPiece)
-                        fold_piece<kTok, kMask, true, true>(A, g, cur.start, lim, lane, prm, tok);
-                    else
-                        fold_piece<kTok, kMask, false, true>(A, g, cur.start, lim, lane, prm, tok);
+#define TIM_FOLD2(I0, F, C) fold_pair<I0, kTok, kMask, F, C>(A, g, cur.start, lim, lane, prm, tok)
+                if (lim == (uint32_t)kPiece) {
+                    if (!kTok && clip_rare) { TIM_FOLD2(0, true, !kTok); TIM_FOLD2(2, true, !kTok); }
+                    else { TIM_FOLD2(0, true, false); TIM_FOLD2(2, true, false); }
                 } else {
-                    if (lim == (uint32_t)kPiece)
-                        fold_piece<kTok, kMask, true, false>(A, g, cur.start, lim, lane, prm, tok);
-                    else
-                        fold_piece<kTok, kMask, false, false>(A, g, cur.start, lim, lane, prm, tok);
+                    if (!kTok && clip_rare) {
+                        TIM_FOLD2(0, false, !kTok);
+                        if (lim > 2u * kWave) TIM_FOLD2(2, false, !kTok);
+                    } else {
+                        TIM_FOLD2(0, false, false);
+                        if (lim > 2u * kWave) TIM_FOLD2(2, false, false);
+                    }
                 }
+#undef TIM_FOLD2
                 if (flags & kLastPiece) {
                     const SubPartial q = finish(A, prm.clip_c, lane, scratch[wv]);
                     A.zero();
                     if (flags & kComplete) {
-                        if (lane == 0) seq_add(seq_lds[wv], q);
+                        seq_add(S, q);
                         if (flags & kLastSub) {
                             if (lane == 0) {
-                                const SeqSums& a = seq_lds[wv];
                                 StageEnt& e = stage[wv][nstage];
-                                e.q.sd = a.sd; e.q.sk2 = a.sk2; e.q.sk3 = a.sk3; e.q.sw = a.sw;
-                                e.q.nvalid = (int32_t)a.nvalid; e.q.nclip = (int32_t)a.nclip;
-                                e.q.nnan = (int32_t)a.nnan; e.q.pad = 0;
-                                e.id = cur.id; e.kind = 0u;
-                                seq_lds[wv] = seq_zero();
+                                e.sd = S.sd; e.sk2 = S.sk2; e.sk3 = S.sk3; e.sw = S.sw;
+                                e.nvalid = (int32_t)S.nvalid; e.nclip = (int32_t)S.nclip;
+                                e.nnan = (int32_t)S.nnan; e.pad = (int32_t)cur.id;
                             }
+                            S = seq_zero();
                             ++nstage;
                         }
                     } else {
                         if (lane == 0) {
                             StageEnt& e = stage[wv][nstage];
-                            e.q = q; e.id = cur.id; e.kind = 1u;
+                            e = q;
+                            e.pad = (int32_t)(cur.id | kSlotKind);
                         }
                         ++nstage;
                     }
@@ -884,14 +916,16 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         {
             BatchAcc c = acc_zero();
             if ((uint32_t)lane < nstage) {
-                const StageEnt e = stage[wv][lane];
-                if (e.kind == 0u) {
+                StageEnt e = stage[wv][lane];
+                const uint32_t id = (uint32_t)e.pad;
+                if (!(id & kSlotKind)) {
                     SeqSums a;
-                    a.sd = e.q.sd; a.sk2 = e.q.sk2; a.sk3 = e.q.sk3; a.sw = e.q.sw;
-                    a.nvalid = e.q.nvalid; a.nclip = e.q.nclip; a.nnan = e.q.nnan;
-                    seq_finish(e.id, a, prm, so, true, c);
+                    a.sd = e.sd; a.sk2 = e.sk2; a.sk3 = e.sk3; a.sw = e.sw;
+                    a.nvalid = e.nvalid; a.nclip = e.nclip; a.nnan = e.nnan;
+                    seq_finish(id, a, prm, so, true, c);
                 } else {
-                    slots[e.id] = e.q;
+                    e.pad = 0;
+                    slots[id & ~kSlotKind] = e;
                 }
             }
             if (nstage > 0) {
@@ -1032,8 +1066,10 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     p->s = s;
     // the workspace holds the most waves any device gets
     split_tokens(n, kMaxStreamWaves, &p->range, &p->nwaves);
-    // slot floor(c_j / SC) + j + k <= floor((n - 1) / SC) + s - 1
+    // slot floor(c_j / SC) + j + k <= floor((n - 1) / SC) + s - 1; a slot
+    // index keeps its top bit free (the stage marks the kind there)
     p->nslots = n / kSubChunk + s + 1;
+    if (p->nslots >= ((int64_t)1 << 31)) return false;
     p->nblk_fin = (p->nwaves + kFinBlock - 1) / kFinBlock;
     size_t off = 0;
     auto take = [&](size_t bytes) {

@@ -24,8 +24,10 @@ pytestmark = pytest.mark.skipif(not ic.tools_available() or not os.path.exists(t
 MFMA_KERNELS = ("lmhead8w_kernel", "lmhead_narrow_kernel", "lmhead_partials_kernel",
                 "gemm8w_kernel")
 # kernels whose every value must stay in registers
+# the stats stream counts its own copies in flight (vmcnt): a scratch spill
+# would add memory operations of its own to that count
 NO_SCRATCH = ("lmhead8w_kernelILb0E", "lmhead_narrow_kernel", "gemm8w_kernelILi1E",
-              "gemm8w_kernelILi2E")
+              "gemm8w_kernelILi2E", "stats_stream_kernel")
 
 
 @pytest.fixture(scope="module")
@@ -60,14 +62,14 @@ def test_no_mfma_hazard(kernels, name):
     assert found
 
 
-def test_head_and_gemm_kernels_use_no_scratch():
+def test_head_gemm_and_stats_stream_kernels_use_no_scratch():
     sizes = ic.private_segment_sizes(tim.LIB_PATH)
     checked = 0
     for k, size in sizes.items():
         if any(n in k for n in NO_SCRATCH):
             checked += 1
             assert size == 0, f"{k}: {size} bytes of scratch per lane"
-    assert checked >= 5
+    assert checked >= 11
 
 
 def _head_kernel(kernels):
