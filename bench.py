@@ -470,8 +470,8 @@ def stats_scale(tim, workloads, torch, np, log2n):
                                         math.log(1.01)), workspace=ws)
     ms = time_calls(fn, torch, np)
     # algorithmic bytes: lt, lr (4 B) + mask (1 B) per token, cu_seqlens,
-    # per-sequence outputs (3 int32, 5 fp64, 1 u8), the batch vector
-    algo = 9 * n + 4 * (s + 1) + s * (12 + 40 + 1) + 8 * len(tim.BATCH_FIELDS)
+    # per-sequence outputs (3 int32, 5 fp64, 2 u8), the batch vector
+    algo = 9 * n + 4 * (s + 1) + s * (12 + 40 + 2) + 8 * len(tim.BATCH_FIELDS)
     gbs = algo / (ms / 1e3) / 1e9
     log(f"stats 2^{log2n}: {ms:.3f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
     del lt, lr, mask, cu, ws

@@ -447,8 +447,14 @@ def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
                        tis_clip: float = 2.0, seq_bounds=(-0.01, 0.01),
                        seq_k3_max: float = math.inf,
                        token_outputs: bool = False, seq_outputs: bool = True,
+                       check_cu_seqlens: bool = False,
                        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Mismatch statistics between trainer and rollout log-probabilities.
+
+    ``cu_seqlens`` must satisfy 0 = c0 <= c1 <= ... <= cs = n; the device does
+    not check it (offsets outside [0, n] are clamped).  ``check_cu_seqlens``
+    copies it to the host and raises ``ValueError`` if it does not (a debug
+    aid: it synchronises with the device).
 
     ``seq_bounds`` are log-domain bounds on a sequence's mean delta; a
     geometric-mean-ratio window ``[a, b]`` is ``(log a, log b)``.  A sequence
@@ -474,6 +480,8 @@ def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
     s = cu_seqlens.numel() - 1
     if logp_rollout.numel() != n or (mask is not None and mask.numel() != n) or s < 0:
         raise ValueError("inconsistent sizes")
+    if check_cu_seqlens:
+        _check_cu_seqlens(cu_seqlens, n)
     dev = logp_train.device
     res = {}
     batch = torch.empty(len(BATCH_FIELDS), dtype=torch.float64, device=dev)
@@ -513,6 +521,15 @@ def tim_mismatch_stats(logp_train: torch.Tensor, logp_rollout: torch.Tensor,
     if st != TIM_OK:
         raise TimError(st, "tim_mismatch_stats")
     return res
+
+
+def _check_cu_seqlens(cu_seqlens: torch.Tensor, n: int):
+    c = cu_seqlens.to("cpu").tolist()
+    if not c or c[0] != 0 or c[-1] != n:
+        raise ValueError(f"cu_seqlens must start at 0 and end at n = {n}")
+    for j in range(1, len(c)):
+        if c[j] < c[j - 1]:
+            raise ValueError(f"cu_seqlens decreases at index {j}: {c[j - 1]} > {c[j]}")
 
 
 def extras_workspace_bytes(n: int) -> int:

@@ -101,8 +101,10 @@ struct TokOut {
 };
 
 // e^d - 1 for finite |d| > 1/32 (the rare branch; |d| <= 1/32 uses a Taylor
-// polynomial for e^d - 1 - d).  Range reduction d = k ln2 + r with
-// |r| <= ln2 / 2 (ln2 split in a high part exact in 32 bits and a low part),
+// polynomial for e^d - 1 - d).  Cody and Waite's additive range reduction
+// (W. J. Cody, W. Waite, "Software Manual for the Elementary Functions",
+// 1980): d = k ln2 + r with |r| <= ln2 / 2, ln2 split in a high part whose
+// product with k is exact and a low part (the usual published pair),
 // e^r - 1 by a degree-12 Taylor polynomial (truncation < 1e-15 relative),
 // then e^d - 1 = 2^k (e^r - 1) + (2^k - 1); both terms are exact-sign sums, so
 // no cancellation beyond one rounding.  d > 709.78 overflows to +inf and

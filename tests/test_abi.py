@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import invariant_logprobs_amd as tim
 
@@ -344,3 +345,11 @@ def test_noalloc_checks_and_scratch_limit_before_any_device_call(lib):
     assert lib.tim_logprob_workspace_bytes(256, d, v, 0, tim.TIM_SCHED_SPLIT_K) > (64 << 20)
     assert _fwd_noalloc(lib, n=256, d=d, v=v, ldh=d, ldw=d,
                         flags=tim.TIM_SCHED_SPLIT_K) == tim.TIM_ESCRATCH
+
+
+def test_cu_seqlens_debug_check():
+    ok = torch.tensor([0, 3, 3, 10], dtype=torch.int32)
+    tim._check_cu_seqlens(ok, 10)
+    for bad, n in (([1, 3, 10], 10), ([0, 3, 9], 10), ([0, 5, 4, 10], 10), ([], 0)):
+        with pytest.raises(ValueError):
+            tim._check_cu_seqlens(torch.tensor(bad, dtype=torch.int32), n)
