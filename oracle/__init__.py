@@ -136,7 +136,8 @@ def _load():
                                             c_i64, vp, c_i64, vp, vp, c_i64, vp, c_int]
         lib.or_ppo_loss.restype = c_int
         lib.or_ppo_loss.argtypes = [vp, vp, vp, vp, vp, c_i64, ctypes.c_double,
-                                    ctypes.c_double, c_int, ctypes.c_double] + [vp] * 6
+                                    ctypes.c_double, c_int, ctypes.c_double,
+                                    ctypes.c_double] + [vp] * 6
         lib.or_ppo_nfields.restype = c_int
         assert lib.or_batch_nfields() == len(BATCH_FIELDS)
         assert lib.or_extras_nfields() == len(EXTRAS_FIELDS)
@@ -358,9 +359,11 @@ def logprob_backward(h, w, ids, g, *, dtype: int, dh_rows=None, dw_rows=None, nt
 
 
 def ppo_loss(logp, old_train, old_rollout, adv, mask, *, eps_lo: float, eps_hi: float,
-             bypass: bool = False, tis_c: float = 0.0, token_outputs: bool = True) -> dict:
-    """fp64 per-token loss, gradient (of the token mean), ratio,
-    contribution and clip flag, and the batch vector (``PPO_FIELDS``)."""
+             bypass: bool = False, tis_c: float = 0.0, grad_scale: float = 0.0,
+             token_outputs: bool = True) -> dict:
+    """fp64 per-token loss, gradient (of the token mean, or of
+    ``grad_scale`` times the token sum when it is > 0), ratio, contribution
+    and clip flag, and the batch vector (``PPO_FIELDS``)."""
     arrs = [_as_host_array(x, np.float32) for x in (logp, old_train, old_rollout, adv)]
     m = None if mask is None else _as_host_array(mask, np.uint8)
     n = arrs[0].size
@@ -371,7 +374,8 @@ def ppo_loss(logp, old_train, old_rollout, adv, mask, *, eps_lo: float, eps_hi: 
         out = {k: None for k in ("loss", "grad", "ratio", "contrib", "clipped")}
     batch = np.empty(len(PPO_FIELDS), np.float64)
     rc = _load().or_ppo_loss(*[_ptr(a) for a in arrs], _ptr(m), n, float(eps_lo), float(eps_hi),
-                             int(bool(bypass)), float(tis_c), _ptr(out["loss"]), _ptr(out["grad"]),
+                             int(bool(bypass)), float(tis_c), float(grad_scale),
+                             _ptr(out["loss"]), _ptr(out["grad"]),
                              _ptr(out["ratio"]), _ptr(out["contrib"]), _ptr(out["clipped"]),
                              _ptr(batch))
     if rc != 0:

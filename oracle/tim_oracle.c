@@ -814,16 +814,21 @@ int or_ppo_nfields(void) { return OP_NFIELDS; }
  * interval on the side that the advantage's sign favours).
  * A token whose inputs give a non-finite r, weight or advantage is counted
  * in n_nan and left out.  grad[t] is the derivative of the token mean of
- * loss over the valid tokens (0 for tokens left out).  Outputs nullable.
+ * loss over the valid tokens when grad_scale == 0, and of grad_scale times
+ * the token sum when grad_scale > 0 (VeXact eq. (2) writes the surrogate per
+ * token and leaves the normaliser of the sum open: a trainer divides by a
+ * token count taken over all its data-parallel ranks, or by a constant);
+ * 0 for tokens left out.  Outputs nullable.
  */
 int or_ppo_loss(const float* logp, const float* old_train, const float* old_rollout,
                 const float* adv, const uint8_t* mask, int64_t n,
-                double eps_lo, double eps_hi, int bypass, double tis_c,
+                double eps_lo, double eps_hi, int bypass, double tis_c, double grad_scale,
                 double* loss, double* grad, double* ratio, double* contrib,
                 uint8_t* clipped, double* batch)
 {
     if (n < 0 || (n > 0 && (!logp || !old_train || !old_rollout || !adv)) ||
-        !(eps_lo >= 0.0) || !(eps_hi >= 0.0) || isnan(tis_c))
+        !(eps_lo >= 0.0) || !(eps_hi >= 0.0) || isnan(tis_c) ||
+        !(grad_scale >= 0.0) || isinf(grad_scale))
         return -1;
     double s_loss = 0, s_r = 0, s_w = 0, s_c = 0;
     int64_t nv = 0, nclip = 0, nnan = 0;
@@ -857,7 +862,9 @@ int or_ppo_loss(const float* logp, const float* old_train, const float* old_roll
         if (contrib) contrib[t] = c_t;
         if (clipped) clipped[t] = (uint8_t)clip_t;
     }
-    if (grad && nv > 0)
+    if (grad && grad_scale > 0.0)
+        for (int64_t t = 0; t < n; ++t) grad[t] *= grad_scale;
+    else if (grad && nv > 0)
         for (int64_t t = 0; t < n; ++t) grad[t] /= (double)nv;
     if (batch) {
         const double dn = (double)nv;

@@ -556,10 +556,10 @@ def test_backward_invariants_and_row_selection():
 # PPO / GRPO clipped surrogate
 # ---------------------------------------------------------------------------
 
-def _ppo(lp, ot, orr, a, mask=None, lo=0.2, hi=0.28, bypass=False, c=0.0):
+def _ppo(lp, ot, orr, a, mask=None, lo=0.2, hi=0.28, bypass=False, c=0.0, scale=0.0):
     f = lambda x: np.asarray(x, np.float32)
     return oracle.ppo_loss(f(lp), f(ot), f(orr), f(a), mask, eps_lo=lo, eps_hi=hi,
-                           bypass=bypass, tis_c=c)
+                           bypass=bypass, tis_c=c, grad_scale=scale)
 
 
 def test_ppo_clip_branches_closed_form():
@@ -603,6 +603,43 @@ def test_ppo_gradient_matches_central_differences():
             fd = (_ppo(lpp, ot, orr, a, bypass=bypass, c=c)["batch"]["mean_loss"] -
                   _ppo(lpm, ot, orr, a, bypass=bypass, c=c)["batch"]["mean_loss"]) / (2 * eps)
             assert abs(fd - base["grad"][t]) < 1e-7, (bypass, c, t, fd, base["grad"][t])
+
+
+def test_ppo_scaled_gradient_is_that_of_the_scaled_token_sum():
+    # grad_scale > 0: the derivative of grad_scale * sum_t loss_t, by central
+    # differences of the per-token losses (masked tokens included as zeros)
+    rng = np.random.default_rng(35)
+    n = 24
+    ot = (-rng.uniform(0.5, 3, n)).astype(np.float32)
+    orr = (ot + rng.normal(0, 0.05, n)).astype(np.float32)
+    lp = (ot + rng.normal(0, 0.2, n)).astype(np.float32)
+    a = rng.normal(0, 1, n).astype(np.float32)
+    mask = (np.arange(n) % 5 != 0).astype(np.uint8)
+    scale = 1.0 / 4096
+    base = _ppo(lp, ot, orr, a, mask=mask, c=2.0, scale=scale)
+    eps = 2.0 ** -16
+    checked = 0
+    for t in range(n):
+        r_t = base["ratio"][t]
+        if min(abs(r_t - 1.28), abs(r_t - 0.8)) < 1e-3:
+            continue
+        lpp, lpm = lp.copy(), lp.copy()
+        lpp[t] += np.float32(eps)
+        lpm[t] -= np.float32(eps)
+        fd = scale * (_ppo(lpp, ot, orr, a, mask=mask, c=2.0)["loss"].sum() -
+                      _ppo(lpm, ot, orr, a, mask=mask, c=2.0)["loss"].sum()) / (2 * eps)
+        assert abs(fd - base["grad"][t]) < 1e-10, (t, fd, base["grad"][t])
+        checked += 1
+    assert checked >= 20 and base["grad"][0] == 0.0          # token 0 is masked
+    # the mean's gradient is the scaled one at scale 1 / n_valid, and every
+    # other output does not depend on the scale
+    mean = _ppo(lp, ot, orr, a, mask=mask, c=2.0)
+    nv = mean["batch"]["n_valid"]
+    assert np.allclose(_ppo(lp, ot, orr, a, mask=mask, c=2.0, scale=1.0 / nv)["grad"],
+                       mean["grad"], rtol=1e-15, atol=0)
+    for k in ("loss", "ratio", "contrib", "clipped"):
+        assert np.array_equal(base[k], mean[k])
+    assert base["batch"] == mean["batch"]
 
 
 def test_ppo_contribution_has_the_gradient_of_minus_r_a_and_tis_moves_the_ratio():
@@ -859,6 +896,9 @@ MUTATIONS = [
      "test_ppo_contribution_has_the_gradient_of_minus_r_a_and_tis_moves_the_ratio"),
     ("ppo gradient without weight", "g_t = active ? 0.0 : -w * r * a;", "g_t = active ? 0.0 : -r * a;",
      "test_ppo_gradient_matches_central_differences"),
+    ("ppo gradient scale ignored", "for (int64_t t = 0; t < n; ++t) grad[t] *= grad_scale;",
+     "for (int64_t t = 0; t < n; ++t) grad[t] *= 1.0;",
+     "test_ppo_scaled_gradient_is_that_of_the_scaled_token_sum"),
     ("temperature multiplies", "zr[c] = zr[c] / j->tau;", "zr[c] = zr[c] * j->tau;",
      "test_temperature_divides_the_logits"),
     ("entropy sign", "hsum += -exp(lp) * lp;", "hsum += exp(lp) * lp;",
