@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TIM_ABI_VERSION 4
+#define TIM_ABI_VERSION 5
 
 typedef enum {
     TIM_OK = 0,
@@ -539,6 +539,13 @@ typedef struct {
                           tis_c), the truncated r_corr of the VeXact
                           compensation table's TIS rows; <= 0: w = 1.  Not
                           NaN.                                               */
+    double grad_scale; /* 0: grad is the derivative of the token mean over
+                          this call's valid tokens (a second pass divides by
+                          n_valid once it is known); > 0 (finite): of
+                          grad_scale * (sum of the token losses), written in
+                          one pass, e.g. 1 / (valid tokens over every
+                          data-parallel rank).  Other outputs do not depend
+                          on it.                                             */
 } tim_ppo_params;
 
 /* (host struct) optional per-token outputs, each [n] fp32 (clipped uint8),
@@ -547,7 +554,8 @@ typedef struct {
 typedef struct {
     float* loss;       /* -w min(r A, clip(r, 1 - eps_low, 1 + eps_high) A)
                           (VeXact eq. (2))                                   */
-    float* grad;       /* d(mean loss)/d logp[t] = -w [not clipped] r A / n_valid */
+    float* grad;       /* -w [not clipped] r A / n_valid (d mean loss / d logp[t]),
+                          or times grad_scale instead of / n_valid           */
     float* ratio;      /* r = exp(logp - logp_old)                           */
     float* contrib;    /* -(r - 1) A, the zero-centred contribution (VeXact
                           eq. (5))                                           */
@@ -591,7 +599,8 @@ size_t tim_ppo_workspace_bytes(int64_t n);
  *  batch             [TIM_P_NFIELDS] fp64 out, nullable.
  *  workspace         >= tim_ppo_workspace_bytes(n) bytes, 256-byte aligned.
  *  Errors: TIM_EINVAL for n < 0, null p, negative or NaN eps, NaN tis_c,
- *  bypass not 0/1, null inputs when n > 0; TIM_EWORKSPACE, TIM_EUNSUPPORTED
+ *  bypass not 0/1, grad_scale negative, NaN or infinite, null inputs when
+ *  n > 0; TIM_EWORKSPACE, TIM_EUNSUPPORTED
  *  (alignment) as elsewhere.  n == 0 writes the batch vector (zeros).
  * Per-token arithmetic is fp64 from the fp32 inputs; the sums are reduced in
  * a fixed order that depends only on n.

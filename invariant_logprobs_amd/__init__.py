@@ -71,7 +71,7 @@ EXTRAS_FIELDS = (
     "abs_q0", "abs_q1", "abs_q2", "abs_q3",
 )
 X_MAX_Q = 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 # Bytes of the static per-device scratch of tim_logprob_forward_noalloc.
 NOALLOC_SCRATCH_BYTES = 64 << 20
 TIM_BWD_ACCUMULATE_DW = 1
@@ -114,7 +114,8 @@ class _ForwardParams(ctypes.Structure):
 
 class _PpoParams(ctypes.Structure):
     _fields_ = [("eps_low", ctypes.c_double), ("eps_high", ctypes.c_double),
-                ("bypass", ctypes.c_int32), ("tis_c", ctypes.c_double)]
+                ("bypass", ctypes.c_int32), ("tis_c", ctypes.c_double),
+                ("grad_scale", ctypes.c_double)]
 
 
 class _PpoTokenOut(ctypes.Structure):
@@ -649,11 +650,13 @@ def tim_logprob_backward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
 def tim_ppo_loss(logp: torch.Tensor, logp_old_train: torch.Tensor,
                  logp_old_rollout: torch.Tensor, advantages: torch.Tensor,
                  mask: Optional[torch.Tensor], *, eps_low: float = 0.2, eps_high: float = 0.28,
-                 bypass: bool = False, tis_c: float = 0.0, token_outputs: bool = True,
+                 bypass: bool = False, tis_c: float = 0.0, grad_scale: float = 0.0,
+                 token_outputs: bool = True,
                  workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """Clipped surrogate, gradient of its token mean by ``logp``, ratios,
-    zero-centred contributions and clip flags (GPU tensors), and the batch
-    vector (``"batch"``, ``PPO_FIELDS`` order)."""
+    """Clipped surrogate, gradient by ``logp`` of its token mean (or, with
+    ``grad_scale > 0``, of ``grad_scale`` times its token sum, in one pass),
+    ratios, zero-centred contributions and clip flags (GPU tensors), and the
+    batch vector (``"batch"``, ``PPO_FIELDS`` order)."""
     lib = load_library()
     ins = (logp, logp_old_train, logp_old_rollout, advantages)
     for name, t in zip(("logp", "logp_old_train", "logp_old_rollout", "advantages"), ins):
@@ -679,7 +682,8 @@ def tim_ppo_loss(logp: torch.Tensor, logp_old_train: torch.Tensor,
     need = lib.tim_ppo_workspace_bytes(n)
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
-    prm = _PpoParams(float(eps_low), float(eps_high), int(bool(bypass)), float(tis_c))
+    prm = _PpoParams(float(eps_low), float(eps_high), int(bool(bypass)), float(tis_c),
+                     float(grad_scale))
     st = lib.tim_ppo_loss(*[_dptr(x) for x in ins], _dptr(mask), n, ctypes.byref(prm),
                           ctypes.byref(tok) if tok is not None else None, _dptr(res["batch"]),
                           _dptr(workspace), workspace.numel() * workspace.element_size(),

@@ -438,7 +438,8 @@ gemm8w_kernel(GemmArgs p) {
 
 constexpr int kPpoThreads = 256;
 constexpr int kPpoMaxBlocks = 16384;
-constexpr int kPpoUnroll = 4;        // tokens per thread per loop trip, loads first
+constexpr int kPpoGroup = 4;         // consecutive tokens per thread step: one 16-byte access
+constexpr int kPpoUnroll = 2;        // groups per thread per loop trip, loads first
 
 struct PpoPart {
     double loss, ratio, w, contrib;
@@ -450,18 +451,22 @@ struct PpoArgs {
     const uint8_t* mask;
     int64_t n;
     double eps_lo, eps_hi, tis_c;
+    double gscale;                   // > 0: gradient of gscale * sum; 0: unscaled (rescaled later)
     int bypass;
     float *loss, *grad, *ratio, *contrib;
     uint8_t* clipped;
 };
 
-// Per token, fp64 from the fp32 inputs; block partials in a fixed tree.
-// Thread tid of block b takes tokens b*256 + tid + j*grid*256, kPpoUnroll of
-// them per loop trip with every load issued first.
-__device__ __forceinline__ void ppo_token(const PpoArgs& a, int64_t t, float lp, float ot,
-                                          float orr, float ad, bool in, PpoPart& acc) {
+struct PpoTok {
+    float l, g, r, c;
+    uint32_t clip;
+};
+
+// One token, fp64 from the fp32 inputs.
+__device__ __forceinline__ PpoTok ppo_token(const PpoArgs& a, float lp, float ot, float orr,
+                                            float ad, bool in, PpoPart& acc) {
     double l_t = 0, g_t = 0, r_t = 1, c_t = 0;
-    int clip_t = 0;
+    uint32_t clip_t = 0;
     if (in) {
         const double old = a.bypass ? (double)orr : (double)ot;
         const double r = exp((double)lp - old);
@@ -476,6 +481,7 @@ __device__ __forceinline__ void ppo_token(const PpoArgs& a, int64_t t, float lp,
             const bool active = (adv > 0.0 && r > hi) || (adv < 0.0 && r < lo);
             l_t = -w * sur;
             g_t = active ? 0.0 : -w * r * adv;
+            if (a.gscale > 0.0) g_t *= a.gscale;
             r_t = r;
             c_t = -(r - 1.0) * adv;
             clip_t = active;
@@ -487,37 +493,94 @@ __device__ __forceinline__ void ppo_token(const PpoArgs& a, int64_t t, float lp,
             acc.contrib += c_t;
         }
     }
-    if (a.loss) a.loss[t] = (float)l_t;
-    if (a.grad) a.grad[t] = (float)g_t;      // scaled by 1 / n_valid afterwards
-    if (a.ratio) a.ratio[t] = (float)r_t;
-    if (a.contrib) a.contrib[t] = (float)c_t;
-    if (a.clipped) a.clipped[t] = (uint8_t)clip_t;
+    return PpoTok{(float)l_t, (float)g_t, (float)r_t, (float)c_t, clip_t};
 }
 
+// Thread tid of block b takes token groups g = b*256 + tid + j*stride
+// (stride = grid*256), kPpoUnroll groups per loop trip with every load of
+// the trip issued first; group g is tokens 4g .. 4g + 3, folded in
+// ascending order.  kVec: every pointer is 16-byte aligned (the mask and the
+// clip flags 4-byte aligned), so a whole group moves with one access per
+// array; otherwise, and for the last group when n % 4 != 0, element by
+// element.  Both variants assign and fold tokens identically, so their bits
+// agree.  Block partials are folded by a fixed tree.
+template <bool kVec>
 __global__ void __launch_bounds__(kPpoThreads)
 ppo_token_kernel(PpoArgs a, PpoPart* __restrict__ part) {
     __shared__ PpoPart sh[kPpoThreads];
     PpoPart acc{0, 0, 0, 0, 0, 0, 0, 0};
+    const int64_t ng = (a.n + kPpoGroup - 1) / kPpoGroup;
     const int64_t stride = (int64_t)gridDim.x * kPpoThreads;
-    for (int64_t base = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; base < a.n;
+    for (int64_t base = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; base < ng;
          base += kPpoUnroll * stride) {
-        float lp[kPpoUnroll], ot[kPpoUnroll], orr[kPpoUnroll], ad[kPpoUnroll];
-        bool in[kPpoUnroll];
+        float4 lp[kPpoUnroll], ot[kPpoUnroll], orr[kPpoUnroll], ad[kPpoUnroll];
+        uint32_t mk[kPpoUnroll];
 #pragma unroll
         for (int j = 0; j < kPpoUnroll; ++j) {
-            const int64_t t = base + j * stride;
-            const int64_t tc = t < a.n ? t : base;             // base < n: in bounds
-            lp[j] = a.logp[tc];
-            ot[j] = a.old_train[tc];
-            orr[j] = a.old_rollout[tc];
-            ad[j] = a.adv[tc];
-            const uint32_t mk = a.mask ? (uint32_t)(a.mask[tc] != 0) : 1u;   // no short-circuit
-            in[j] = ((uint32_t)(t < a.n) & mk) != 0;
+            const int64_t g = base + j * stride;
+            const int64_t gc = g < ng ? g : base;              // base < ng: in bounds
+            const int64_t t0 = gc * kPpoGroup;
+            if (kVec && t0 + kPpoGroup <= a.n) {
+                lp[j] = *(const float4*)(a.logp + t0);
+                ot[j] = *(const float4*)(a.old_train + t0);
+                orr[j] = *(const float4*)(a.old_rollout + t0);
+                ad[j] = *(const float4*)(a.adv + t0);
+                mk[j] = a.mask ? *(const uint32_t*)(a.mask + t0) : 0x01010101u;
+            } else {
+                float x[4][4];
+                uint32_t m = 0;
+#pragma unroll
+                for (int i = 0; i < kPpoGroup; ++i) {
+                    const int64_t t = t0 + i < a.n ? t0 + i : a.n - 1;
+                    x[0][i] = a.logp[t];
+                    x[1][i] = a.old_train[t];
+                    x[2][i] = a.old_rollout[t];
+                    x[3][i] = a.adv[t];
+                    m |= (uint32_t)(a.mask ? a.mask[t] : 1) << (8 * i);
+                }
+                lp[j] = make_float4(x[0][0], x[0][1], x[0][2], x[0][3]);
+                ot[j] = make_float4(x[1][0], x[1][1], x[1][2], x[1][3]);
+                orr[j] = make_float4(x[2][0], x[2][1], x[2][2], x[2][3]);
+                ad[j] = make_float4(x[3][0], x[3][1], x[3][2], x[3][3]);
+                mk[j] = m;
+            }
         }
 #pragma unroll
         for (int j = 0; j < kPpoUnroll; ++j) {
-            const int64_t t = base + j * stride;
-            if (t < a.n) ppo_token(a, t, lp[j], ot[j], orr[j], ad[j], in[j], acc);
+            const int64_t g = base + j * stride;
+            if (g >= ng) continue;
+            const int64_t t0 = g * kPpoGroup;
+            const float lpv[4] = {lp[j].x, lp[j].y, lp[j].z, lp[j].w};
+            const float otv[4] = {ot[j].x, ot[j].y, ot[j].z, ot[j].w};
+            const float orv[4] = {orr[j].x, orr[j].y, orr[j].z, orr[j].w};
+            const float adv[4] = {ad[j].x, ad[j].y, ad[j].z, ad[j].w};
+            PpoTok o[kPpoGroup];
+#pragma unroll
+            for (int i = 0; i < kPpoGroup; ++i) {
+                const bool in = t0 + i < a.n && ((mk[j] >> (8 * i)) & 0xffu) != 0;
+                o[i] = ppo_token(a, lpv[i], otv[i], orv[i], adv[i], in, acc);
+            }
+            if (kVec && t0 + kPpoGroup <= a.n) {
+                if (a.loss) *(float4*)(a.loss + t0) = make_float4(o[0].l, o[1].l, o[2].l, o[3].l);
+                if (a.grad) *(float4*)(a.grad + t0) = make_float4(o[0].g, o[1].g, o[2].g, o[3].g);
+                if (a.ratio) *(float4*)(a.ratio + t0) = make_float4(o[0].r, o[1].r, o[2].r, o[3].r);
+                if (a.contrib)
+                    *(float4*)(a.contrib + t0) = make_float4(o[0].c, o[1].c, o[2].c, o[3].c);
+                if (a.clipped)
+                    *(uint32_t*)(a.clipped + t0) =
+                        o[0].clip | (o[1].clip << 8) | (o[2].clip << 16) | (o[3].clip << 24);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPpoGroup; ++i) {
+                    const int64_t t = t0 + i;
+                    if (t >= a.n) break;
+                    if (a.loss) a.loss[t] = o[i].l;
+                    if (a.grad) a.grad[t] = o[i].g;
+                    if (a.ratio) a.ratio[t] = o[i].r;
+                    if (a.contrib) a.contrib[t] = o[i].c;
+                    if (a.clipped) a.clipped[t] = (uint8_t)o[i].clip;
+                }
+            }
         }
     }
     sh[threadIdx.x] = acc;
@@ -573,13 +636,29 @@ ppo_final_kernel(const PpoPart* __restrict__ part, int nblk, double* __restrict_
     *inv_n = nv > 0 ? 1.0 / nv : 0.0;
 }
 
-// grad[t] *= 1 / n_valid (the derivative of the token mean)
+// grad[t] *= 1 / n_valid (the derivative of the token mean); kVec: grad is
+// 16-byte aligned and moves four values per access (the last n % 4 one by
+// one).  The product is the same either way.
+template <bool kVec>
 __global__ void __launch_bounds__(kPpoThreads)
 ppo_scale_kernel(float* __restrict__ grad, int64_t n, const double* __restrict__ inv_n) {
     const double s = *inv_n;
     const int64_t stride = (int64_t)gridDim.x * kPpoThreads;
-    for (int64_t t = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; t < n; t += stride)
-        grad[t] = (float)((double)grad[t] * s);
+    const int64_t tid = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x;
+    if constexpr (kVec) {
+        const int64_t n4 = n / 4;
+        for (int64_t i = tid; i < n4; i += stride) {
+            float4 g = *(const float4*)(grad + 4 * i);
+            g.x = (float)((double)g.x * s);
+            g.y = (float)((double)g.y * s);
+            g.z = (float)((double)g.z * s);
+            g.w = (float)((double)g.w * s);
+            *(float4*)(grad + 4 * i) = g;
+        }
+        if (tid < n - 4 * n4) grad[4 * n4 + tid] = (float)((double)grad[4 * n4 + tid] * s);
+    } else {
+        for (int64_t t = tid; t < n; t += stride) grad[t] = (float)((double)grad[t] * s);
+    }
 }
 
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -710,22 +789,39 @@ size_t ppo_workspace_bytes() {
 
 hipError_t launch_ppo_loss(const float* logp, const float* old_train, const float* old_rollout,
                            const float* adv, const uint8_t* mask, int64_t n, double eps_lo,
-                           double eps_hi, int bypass, double tis_c, float* loss, float* grad,
-                           float* ratio, float* contrib, uint8_t* clipped, double* batch,
-                           void* workspace, hipStream_t st) {
+                           double eps_hi, int bypass, double tis_c, double grad_scale,
+                           float* loss, float* grad, float* ratio, float* contrib,
+                           uint8_t* clipped, double* batch, void* workspace, hipStream_t st) {
     PpoPart* part = (PpoPart*)workspace;
     double* inv_n = (double*)((unsigned char*)workspace + align_up(sizeof(PpoPart) * kPpoMaxBlocks, 256));
-    int64_t nblk = (n + kPpoThreads * kPpoUnroll * 4 - 1) / (kPpoThreads * kPpoUnroll * 4);
+    // the block count is a function of n alone (it fixes the sum order)
+    const int64_t per_blk = (int64_t)kPpoThreads * kPpoUnroll * kPpoGroup * 2;
+    int64_t nblk = (n + per_blk - 1) / per_blk;
     if (nblk < 1) nblk = 1;
     if (nblk > kPpoMaxBlocks) nblk = kPpoMaxBlocks;
-    PpoArgs a{logp, old_train, old_rollout, adv, mask, n, eps_lo, eps_hi, tis_c, bypass,
-              loss, grad, ratio, contrib, clipped};
-    hipLaunchKernelGGL(ppo_token_kernel, dim3((unsigned)nblk), dim3(kPpoThreads), 0, st, a, part);
+    PpoArgs a{logp, old_train, old_rollout, adv, mask, n, eps_lo, eps_hi, tis_c, grad_scale,
+              bypass, loss, grad, ratio, contrib, clipped};
+    auto al = [](const void* p, uintptr_t b) { return ((uintptr_t)p & (b - 1)) == 0; };
+    const bool vec = al(logp, 16) && al(old_train, 16) && al(old_rollout, 16) && al(adv, 16) &&
+                     al(mask, 4) && al(loss, 16) && al(grad, 16) && al(ratio, 16) &&
+                     al(contrib, 16) && al(clipped, 4);
+    if (vec)
+        hipLaunchKernelGGL(ppo_token_kernel<true>, dim3((unsigned)nblk), dim3(kPpoThreads), 0, st,
+                           a, part);
+    else
+        hipLaunchKernelGGL(ppo_token_kernel<false>, dim3((unsigned)nblk), dim3(kPpoThreads), 0, st,
+                           a, part);
     hipLaunchKernelGGL(ppo_final_kernel, dim3(1), dim3(kPpoThreads), 0, st, (const PpoPart*)part,
                        (int)nblk, batch, inv_n);
-    if (grad && n > 0)
-        hipLaunchKernelGGL(ppo_scale_kernel, dim3((unsigned)nblk), dim3(kPpoThreads), 0, st, grad,
-                           n, (const double*)inv_n);
+    if (grad && n > 0 && !(grad_scale > 0.0))
+    {
+        if (al(grad, 16))
+            hipLaunchKernelGGL(ppo_scale_kernel<true>, dim3((unsigned)nblk), dim3(kPpoThreads), 0,
+                               st, grad, n, (const double*)inv_n);
+        else
+            hipLaunchKernelGGL(ppo_scale_kernel<false>, dim3((unsigned)nblk), dim3(kPpoThreads), 0,
+                               st, grad, n, (const double*)inv_n);
+    }
     return hipGetLastError();
 }
 

@@ -371,7 +371,7 @@ int tim_ppo_loss(const float* logp, const float* logp_old_train, const float* lo
     static_assert(TIM_P_NFIELDS == tim::kPpoOutFields, "ppo layout");
     if (n < 0 || !p) return TIM_EINVAL;
     if (!(p->eps_low >= 0.0) || !(p->eps_high >= 0.0) || isnan(p->tis_c) ||
-        (p->bypass != 0 && p->bypass != 1))
+        (p->bypass != 0 && p->bypass != 1) || !(p->grad_scale >= 0.0) || isinf(p->grad_scale))
         return TIM_EINVAL;
     if (n > 0 && (!logp || !logp_old_train || !logp_old_rollout || !advantages)) return TIM_EINVAL;
     if (!workspace || workspace_bytes < tim::ppo_workspace_bytes()) return TIM_EWORKSPACE;
@@ -379,7 +379,8 @@ int tim_ppo_loss(const float* logp, const float* logp_old_train, const float* lo
     tim_ppo_token_out t{};
     if (tok) t = *tok;
     if (tim::launch_ppo_loss(logp, logp_old_train, logp_old_rollout, advantages, mask, n,
-                             p->eps_low, p->eps_high, p->bypass, p->tis_c, t.loss, t.grad,
+                             p->eps_low, p->eps_high, p->bypass, p->tis_c, p->grad_scale,
+                             t.loss, t.grad,
                              t.ratio, t.contrib, t.clipped, batch, workspace,
                              (hipStream_t)stream) != hipSuccess)
         return TIM_EHIP;

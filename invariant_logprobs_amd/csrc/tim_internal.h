@@ -184,9 +184,9 @@ size_t ppo_workspace_bytes();
 
 hipError_t launch_ppo_loss(const float* logp, const float* old_train, const float* old_rollout,
                            const float* adv, const uint8_t* mask, int64_t n, double eps_lo,
-                           double eps_hi, int bypass, double tis_c, float* loss, float* grad,
-                           float* ratio, float* contrib, uint8_t* clipped, double* batch,
-                           void* workspace, hipStream_t st);
+                           double eps_hi, int bypass, double tis_c, double grad_scale,
+                           float* loss, float* grad, float* ratio, float* contrib,
+                           uint8_t* clipped, double* batch, void* workspace, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == sorted(tim.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.tim_abi_version() == tim.ABI_VERSION == 4
+    assert lib.tim_abi_version() == tim.ABI_VERSION == 5
 
 
 def test_status_strings(lib):
@@ -207,6 +207,8 @@ def test_backward_and_ppo_argument_errors(lib):
     assert ppo(p=tim._PpoParams(0.2, float("nan"), 0, 0.0)) == tim.TIM_EINVAL
     assert ppo(p=tim._PpoParams(0.2, 0.28, 2, 0.0)) == tim.TIM_EINVAL
     assert ppo(p=tim._PpoParams(0.2, 0.28, 0, float("nan"))) == tim.TIM_EINVAL
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert ppo(p=tim._PpoParams(0.2, 0.28, 0, 2.0, bad)) == tim.TIM_EINVAL
     assert ppo(ws=None) == tim.TIM_EWORKSPACE
     assert ppo(wsb=8) == tim.TIM_EWORKSPACE
     assert ppo(ws=FAKE + 8) == tim.TIM_EUNSUPPORTED

@@ -229,3 +229,40 @@ def test_ppo_parity(n, mode):
             assert got[k] == pytest.approx(ref["batch"][k], rel=2 * m * 2.0 ** -53 + 1e-15,
                                            abs=1e-300), k
     say(f"ppo {mode} n={n}: loss {got['mean_loss']:.4e}, clip {got['clip_frac']:.3f}")
+
+
+@pytest.mark.parametrize("n", [1, 1003, 100_003])
+def test_ppo_scaled_gradient_one_pass(n):
+    lp, ot, orr, adv, mask = _ppo_inputs(max(n, 6), seed=n + 7)
+    lp, ot, orr, adv, mask = (x[:n].contiguous() for x in (lp, ot, orr, adv, mask))
+    scale = 1.0 / 3000.0
+    kw = dict(eps_low=0.2, eps_high=0.28, tis_c=2.0)
+    res = tim.tim_ppo_loss(lp, ot, orr, adv, mask, grad_scale=scale, **kw)
+    mean = tim.tim_ppo_loss(lp, ot, orr, adv, mask, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.ppo_loss(lp.cpu(), ot.cpu(), orr.cpu(), adv.cpu(), mask.cpu(), eps_lo=0.2,
+                          eps_hi=0.28, tis_c=2.0, grad_scale=scale)
+    np.testing.assert_allclose(res["token"]["grad"].double().cpu().numpy(), ref["grad"],
+                               rtol=1e-6, atol=1e-30)
+    # everything else has the bits of the mean-gradient call
+    for k in ("loss", "ratio", "contrib", "clipped"):
+        assert torch.equal(res["token"][k], mean["token"][k]), k
+    assert torch.equal(res["batch"], mean["batch"])
+
+
+def test_ppo_unaligned_inputs_give_the_aligned_bits():
+    # a view one element in takes the element-wise variant; the same values in
+    # fresh (16-byte aligned) storage take the 16-byte one: same assignment
+    # of tokens to threads, same bits
+    n = 50_001
+    lp, ot, orr, adv, mask = _ppo_inputs(n + 1, seed=11)
+    views = [x[1:] for x in (lp, ot, orr, adv, mask)]
+    assert views[0].data_ptr() % 16 != 0
+    fresh = [x.clone() for x in views]
+    assert fresh[0].data_ptr() % 16 == 0
+    for scale in (0.0, 1e-4):
+        a = tim.tim_ppo_loss(*views, eps_low=0.2, eps_high=0.28, tis_c=2.0, grad_scale=scale)
+        b = tim.tim_ppo_loss(*fresh, eps_low=0.2, eps_high=0.28, tis_c=2.0, grad_scale=scale)
+        for k in ("loss", "grad", "ratio", "contrib", "clipped"):
+            assert torch.equal(a["token"][k], b["token"][k]), (scale, k)
+        assert torch.equal(a["batch"], b["batch"])
