@@ -93,10 +93,9 @@ enum {
                                  for the given N, allowed to depend on N
                                  (deterministic for a fixed N, not promised
                                  batch invariant).  On gfx950 that is the
-                                 invariant one for bf16 at every N measured
-                                 (the K split below is slower); for fp32 the
-                                 vocabulary chunks grow as N shrinks.  Exists
-                                 to price invariance.                        */
+                                 invariant one at every N measured (the K
+                                 split below is slower).  Exists to price
+                                 invariance.                                 */
     TIM_SCHED_SPLIT_K = 2u    /* bf16, 33..256 tokens, no entropy: K split in
                                  two halves over twice the workgroups, the
                                  partial logits added, then folded.  Depends

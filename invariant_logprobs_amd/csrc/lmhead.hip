@@ -128,9 +128,13 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     int64_t chunk, ttile;
     tile_of_block(blockIdx.x, gridDim.x, nchunks, nttiles, chunk, ttile);
     const int64_t t0 = ttile * kTileT;
+    // one vocabulary tile per chunk (chunk_tiles == 1, checked on the host):
+    // with several, the compiler copied the look-ahead fragments at the end
+    // of a tile's K loop before their reads had been waited for, and the
+    // next tile started from those copies
     const int64_t vt_first = chunk * chunk_tiles;
-    const int ntiles_here = (int)((nvtiles - vt_first) < chunk_tiles ? (nvtiles - vt_first)
-                                                                      : chunk_tiles);
+    constexpr int ntiles_here = 1;
+    (void)nvtiles;
 
     // the 4 tokens of this lane (one per 32-column block), their target ids
     int32_t my_id[4];
@@ -199,7 +203,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     // while stage st computes.  Past the last stage both wrap to K offset 0
     // (of the last W tile): the extra copies read valid rows into positions
     // that are never read again, and every stage issues the same copies.
-    int w_kb = 0, w_vt = 0, h_kb = 0;
+    int w_kb = 0, h_kb = 0;
     set_wtile(0);
     auto copy_w = [&](int part, int pos) {
         unsigned char* base = lds + pos * kOperandBytes;
@@ -220,10 +224,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
         }
     };
     auto advance_w = [&]() {
-        if (++w_kb == nk) {
-            w_kb = 0;
-            if (++w_vt < ntiles_here) set_wtile(w_vt);
-        }
+        if (++w_kb == nk) w_kb = 0;
     };
     auto advance_h = [&]() {
         if (++h_kb == nk) h_kb = 0;
@@ -277,7 +278,8 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     issue_frags(fa, rd_w, rd_h, 0);
 
     int st = 0;
-    for (int vt_local = 0; vt_local < ntiles_here; ++vt_local) {
+    {
+        constexpr int vt_local = 0;
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -1318,16 +1320,9 @@ bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flag
     p->n = n; p->d = d; p->v = v; p->dtype = dtype;
     p->nvtiles = (v + kTileV - 1) / kTileV;
     p->nttiles = (n + kTileT - 1) / kTileT;
-    if (flags == 0u || dtype == 0) {
-        p->chunk_tiles = kInvariantChunkTiles;
-    } else {
-        // free schedule: about two workgroups per compute unit, whatever N is
-        const int64_t want = 512;
-        int64_t ct = (p->nvtiles * (p->nttiles > 0 ? p->nttiles : 1) + want - 1) / want;
-        if (ct < 1) ct = 1;
-        if (ct > p->nvtiles) ct = p->nvtiles;
-        p->chunk_tiles = (int)ct;
-    }
+    // every schedule: one tile per chunk (the K split of flags 2 splits K,
+    // not the vocabulary)
+    p->chunk_tiles = kInvariantChunkTiles;
     p->nchunks = (p->nvtiles + p->chunk_tiles - 1) / p->chunk_tiles;
     p->entropy = entropy;
     p->narrow = dtype == 0 && n >= 1 && n <= kNarrowMaxTokens;
@@ -1413,6 +1408,7 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
         if (p.entropy) go8(lmhead8w_kernel<true>);
         else go8(lmhead8w_kernel<false>);
     } else {
+        if (p.chunk_tiles != 1) return hipErrorInvalidValue;   // one tile per chunk
         if (p.entropy) go(lmhead_partials_kernel<true>);
         else go(lmhead_partials_kernel<false>);
     }

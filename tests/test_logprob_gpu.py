@@ -392,6 +392,23 @@ def test_other_schedules_match_oracle_and_are_deterministic(n, schedule):
                h_host=host("small", "h")[:n], w_host=host("small", "w"))
 
 
+@pytest.mark.parametrize("n", [64, 300])
+def test_fp32_free_schedule_is_the_invariant_one(n):
+    """At the fp32 head's vocabulary and a few hundred tokens the free
+    schedule is the invariant one (one tile per chunk in every schedule):
+    the same bits, and the oracle's values."""
+    w = wl("fp32_head")
+    h, ids = w.h[:n], w.ids[:n]
+    say(f"fp32_head: free schedule, n={n}")
+    a = tim.tim_logprob_forward(h, w.w, ids, schedule="free")
+    inv = tim.tim_logprob_forward(h, w.w, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), inv.view(torch.int32))
+    check_rows(h, w.w, ids, a, spread_rows(n, 24, 5, extra=(0, n - 1)),
+               f"fp32_head free n={n}", h_host=host("fp32_head", "h")[:n],
+               w_host=host("fp32_head", "w"))
+
+
 def test_split_k_schedule_at_the_qwen3_shape():
     w = wl("qwen3_8b")
     n = 100
