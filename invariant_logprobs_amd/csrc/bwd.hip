@@ -90,11 +90,17 @@ transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t ro
 // NT GEMM tile kernel: C[m][n] = sum_k A[m][k] B[n][k], bf16, fp32 accumulate
 // ---------------------------------------------------------------------------
 
-enum { kEpiDz = 0, kEpiStore = 1, kEpiStoreAcc = 2 };
+// kEpiStore(Acc): C[m][n], a lane holding four consecutive n of one m;
+// kEpiStoreT(Acc): C stored transposed, out[n][m], a lane holding four
+// consecutive m of one n.  Acc: the chain continues from the stored value.
+enum { kEpiDz = 0, kEpiStore = 1, kEpiStoreAcc = 2, kEpiStoreT = 3, kEpiStoreTAcc = 4 };
 
 struct GemmArgs {
     const unsigned char* a; int64_t lda_b; int64_t m;   // A: m rows, K contiguous (bytes)
-    const unsigned char* b; int64_t ldb_b; int64_t n;   // B: n rows, K contiguous
+    // B: n rows, K contiguous; or, K-major kernels, [K][n] with row pitch
+    // ldb_b bytes, rows k >= bk_rows read as zero
+    const unsigned char* b; int64_t ldb_b; int64_t n;
+    int64_t bk_rows;
     int nk;                                             // K / 64 stages
     int64_t mtiles, ntiles;
     // kEpiStore, kEpiStoreAcc: c 16-byte aligned, ldc and n multiples of 4
@@ -144,15 +150,31 @@ __device__ __forceinline__ void gemm_tile_of_block(int64_t mtiles, int64_t ntile
 // kEpiDz gives the MFMAs the operands in the head kernel's order (A = W
 // fragments first, same K order from zero), so the recomputed logits are
 // the ones the forward formed; a lane then holds rows 4 grp + i of column
-// col of each block.  The store epilogues swap the two sources (B
-// fragments first), so that a lane holds four consecutive columns
-// 4 grp .. 4 grp + 3 of row col: one 16-byte store (and load) per block.
-template <int kEpi>
+// col of each block.  kEpiStore(Acc) swap the two sources (B fragments
+// first), so that a lane holds four consecutive columns 4 grp .. 4 grp + 3
+// of row col: one 16-byte store (and load) per block; kEpiStoreT(Acc) keep
+// the order and store the block transposed, four consecutive rows of one
+// column in one 16-byte store.
+//
+// kBT: B is stored K-major ([K][n], n contiguous: W itself for dh, dz for
+// dW), so no transposed copy of it is needed.  A stage of it is 64 K rows
+// of the tile's 256 columns (512 bytes each), copied two rows per
+// buffer-to-LDS copy; the 32-byte column blocks of row r are XOR-swizzled
+// with (r & 3) | ((r >> 3) & 1) << 2, so the eight rows that one half-wave
+// of a transposing read touches land on eight distinct 32-byte bank groups.
+// A fragment is two ds_read_b64_tr_b16 (lds_read_tr), which hand each lane the
+// same eight K values of its column that the K-contiguous read hands it:
+// the MFMAs, and so the results, are the same bit for bit.  Each fragment
+// costs two LDS reads instead of one, so the waits count 7 A reads + 8 B
+// reads (15, the largest lgkmcnt) where the K-contiguous kernel counts 11.
+template <int kEpi, bool kBT = false>
 __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm8w_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-    constexpr bool kSwap = kEpi != kEpiDz;
+    constexpr bool kSwap = kEpi == kEpiStore || kEpi == kEpiStoreAcc;
+    constexpr bool kStoreT = kEpi == kEpiStoreT || kEpi == kEpiStoreTAcc;
+    constexpr int kWaitFull = kBT ? 15 : 11;     // 7 A reads + 4 B fragments
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -172,7 +194,25 @@ gemm8w_kernel(GemmArgs p) {
     const int nk = p.nk;
 
     f32x4 acc[8][4];
-    if constexpr (kEpi == kEpiStoreAcc) {
+    if constexpr (kEpi == kEpiStoreTAcc) {
+        // transposed layout: rows mw + bi 16 + 4 grp .. + 3 of column
+        // nw + bj 16 + col are out[col][..]: one 16-byte load (m is a
+        // multiple of 4)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t cn = nw + bj * 16 + col;
+            const float* crow = p.c + (cn < p.n ? cn : 0) * p.ldc;
+#pragma unroll
+            for (int bi = 0; bi < 8; ++bi) {
+                const int64_t r0 = mw + bi * 16 + grp * 4;
+                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (cn < p.n && r0 < p.m) q = *(const float4*)(crow + r0);
+                acc[bi][bj] = f32x4{q.x, q.y, q.z, q.w};
+                asm volatile("" : "+a"(acc[bi][bj]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if constexpr (kEpi == kEpiStoreAcc) {
         // the chain continues from the stored value (swapped layout: row
         // mw + bi 16 + col, columns nw + bj 16 + 4 grp .. + 3: one 16-byte
         // load; n is a multiple of 4)
@@ -212,16 +252,48 @@ gemm8w_kernel(GemmArgs p) {
         if (ra > p.m - 1) ra = p.m - 1;
         if (rb > p.n - 1) rb = p.n - 1;
         aoff[j] = (uint32_t)((ra - m0) * p.lda_b) + cb;
-        boff[j] = (uint32_t)((rb - n0) * p.ldb_b) + cb;
+        if constexpr (kBT) {
+            // K-major B: copy j of this wave holds stage rows 2 u, 2 u + 1
+            // (u = 4 wave + j); lane l writes 16 bytes at l 16, i.e. row
+            // 2 u + (l >> 5), physical 32-byte block (l & 31) >> 1, which
+            // holds the logical block that the swizzle maps there
+            const int r = 2 * (wave * 4 + j) + (lane >> 5);
+            const int f = (r & 3) | (((r >> 3) & 1) << 2);
+            const int lb = ((lane & 31) >> 1) ^ f;
+            boff[j] = (uint32_t)(r * p.ldb_b) + (uint32_t)(lb * 32 + (lane & 1) * 16);
+        } else {
+            boff[j] = (uint32_t)((rb - n0) * p.ldb_b) + cb;
+        }
     }
     const int64_t arows = (p.m - m0) < kTileV ? (p.m - m0) : kTileV;
     const int64_t brows = (p.n - n0) < kTileT ? (p.n - n0) : kTileT;
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.a + m0 * p.lda_b), (short)0,
         (int)((arows - 1) * p.lda_b + (int64_t)nk * kStageBytes), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.b + n0 * p.ldb_b), (short)0,
-        (int)((brows - 1) * p.ldb_b + (int64_t)nk * kStageBytes), kRsrcWord3);
+    // K-contiguous B: one descriptor for the tile's rows over all of K.
+    // K-major B: one per stage (rebuilt in advance_b), over that stage's 64
+    // rows and the tile's columns: rows past bk_rows and columns past n at
+    // the last valid row lie outside it and read as zero, and no offset
+    // grows with K (a [K][n] operand can exceed 4 GiB)
+    auto b_stage_rsrc = [&](int kb) {
+        const int64_t k0 = (int64_t)kb * 64;
+        const int64_t nval = p.bk_rows - k0;
+        int64_t ext = 0;
+        // the range check is per dword (a dword that straddles the end
+        // reads as zero): the last row's extent is rounded up to whole
+        // dwords, which stays inside that row (dz rows are padded to 64
+        // entries; W rows hold D, a multiple of 64)
+        if (nval > 0) ext = ((nval < 64 ? nval : 64) - 1) * p.ldb_b + ((brows * 2 + 3) & ~(int64_t)3);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(p.b + k0 * p.ldb_b + n0 * 2), (short)0,
+                                                 (int)ext, kRsrcWord3);
+    };
+    __amdgpu_buffer_rsrc_t brs;
+    if constexpr (kBT)
+        brs = b_stage_rsrc(0);
+    else
+        brs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.b + n0 * p.ldb_b), (short)0,
+            (int)((brows - 1) * p.ldb_b + (int64_t)nk * kStageBytes), kRsrcWord3);
 
     // fragment addresses: row col of a 16-row block, logical chunk ks 4 + grp
     const uint32_t lds_base = lds_addr(lds);
@@ -237,12 +309,27 @@ gemm8w_kernel(GemmArgs p) {
     };
     auto copy_b = [&](int j, int pos) {
         dma16_buf(brs, lds + pos * kOperandBytes + (wave * 4 + j) * 1024, boff[j],
-                  (uint32_t)(b_kb * kStageBytes));
+                  kBT ? 0u : (uint32_t)(b_kb * kStageBytes));
     };
     auto advance_a = [&]() { if (++a_kb == nk) a_kb = 0; };
-    auto advance_b = [&]() { if (++b_kb == nk) b_kb = 0; };
+    auto advance_b = [&]() {
+        if (++b_kb == nk) b_kb = 0;
+        if constexpr (kBT) brs = b_stage_rsrc(b_kb);
+    };
     auto next_pos = [](int q) { return q + 2 >= kPos ? q + 2 - kPos : q + 2; };
 
+    // K-major B fragments: lane (g = l >> 4, p = l & 15) addresses stage
+    // row 8 g + (p >> 2) (+ 4 for the upper four K, + 32 for k-step 1) at
+    // the swizzled block of column block 4 wt + bj, 8 bytes at 4 (p & 3)
+    uint32_t xb[4];
+    if constexpr (kBT) {
+        const int tg = lane >> 4, tq = (lane & 15) >> 2;
+        const uint32_t f = (uint32_t)(tq | ((tg & 1) << 2));
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+            xb[bj] = (uint32_t)((8 * tg + tq) * 512) + ((((uint32_t)(4 * wt + bj)) ^ f) << 5) +
+                     (uint32_t)((lane & 3) << 3);
+    }
     u32x4 A[8], B0[4], B1[4];
     auto read_a = [&](int r, uint32_t base) {
         switch (r) {
@@ -256,14 +343,25 @@ gemm8w_kernel(GemmArgs p) {
             default: lds_read16<7 * 2048>(A[7], base); break;
         }
     };
-    auto read_b = [&](u32x4 (&B)[4], uint32_t base) {
-        lds_read16<0 * 2048>(B[0], base);
-        lds_read16<1 * 2048>(B[1], base);
-        lds_read16<2 * 2048>(B[2], base);
-        lds_read16<3 * 2048>(B[3], base);
+    // base: the B ring position (K-major) or that plus the wave's quarter
+    // and the k-step's chunk (K-contiguous); ks: the k-step (K-major only)
+    auto read_b = [&](u32x4 (&B)[4], uint32_t base, auto ks) {
+        if constexpr (kBT) {
+            constexpr int o = decltype(ks)::value * 16384;
+            lds_read_tr<o>(B[0], base + xb[0]);
+            lds_read_tr<o>(B[1], base + xb[1]);
+            lds_read_tr<o>(B[2], base + xb[2]);
+            lds_read_tr<o>(B[3], base + xb[3]);
+        } else {
+            lds_read16<0 * 2048>(B[0], base);
+            lds_read16<1 * 2048>(B[1], base);
+            lds_read16<2 * 2048>(B[2], base);
+            lds_read16<3 * 2048>(B[3], base);
+        }
     };
-    // tied-accumulator asm MFMAs (mfma_pipe.h); the store epilogues swap
-    // the sources
+    auto wait_b = [&](auto n, u32x4& a, u32x4 (&B)[4]) { wait16_4<decltype(n)::value>(a, B); };
+    // tied-accumulator asm MFMAs (mfma_pipe.h); kEpiStore(Acc) swap the
+    // sources
     auto mfma = [&](int r, int bj, const u32x4& b) {
         if constexpr (kSwap) mfma16_tied(acc[r][bj], b, A[r]);
         else mfma16_tied(acc[r][bj], A[r], b);
@@ -272,6 +370,8 @@ gemm8w_kernel(GemmArgs p) {
         if constexpr (kSwap) mfma16_tied_last(acc[7][3], b, A[7], last);
         else mfma16_tied_last(acc[7][3], A[7], b, last);
     };
+    const uint32_t bsel0 = kBT ? 0u : b_quarter + kofs0;   // added to the ring position
+    const uint32_t bsel1 = kBT ? 0u : b_quarter + kofs1;
 
     // kEpiDz: the per-token inputs of the epilogue, loaded before the K loop
     // so that their latency is hidden behind it
@@ -307,21 +407,21 @@ gemm8w_kernel(GemmArgs p) {
     __syncthreads();
     {
         const uint32_t aw = lds_base + (uint32_t)(rd_a * kOperandBytes) + a_half;
-        const uint32_t bw = lds_base + (uint32_t)(rd_b * kOperandBytes) + b_quarter;
-        read_b(B0, bw + kofs0);
+        const uint32_t bw = lds_base + (uint32_t)(rd_b * kOperandBytes);
+        read_b(B0, bw + bsel0, IntConst<0>{});
 #pragma unroll
         for (int r = 0; r < 8; ++r) read_a(r, aw + kofs0);
     }
 
     for (int kb = 0; kb < nk; ++kb) {
         const uint32_t aw = lds_base + (uint32_t)(rd_a * kOperandBytes) + a_half;
-        const uint32_t bw = lds_base + (uint32_t)(rd_b * kOperandBytes) + b_quarter;
+        const uint32_t bw = lds_base + (uint32_t)(rd_b * kOperandBytes);
         // ---- ks0: A(s+1) copies at rows 0-3
-        read_b(B1, bw + kofs1);
+        read_b(B1, bw + bsel1, IntConst<1>{});
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if (r == 0) wait16_4<11>(A[0], B0);
-            else wait16<11>(A[r]);
+            if (r == 0) wait_b(IntConst<kWaitFull>{}, A[0], B0);
+            else wait16<kWaitFull>(A[r]);
             mfma(r, 0, B0[0]); mfma(r, 1, B0[1]);
             if (r < 4) copy_a(r, cp_a);
             mfma(r, 2, B0[2]); mfma(r, 3, B0[3]);
@@ -331,7 +431,7 @@ gemm8w_kernel(GemmArgs p) {
         // ---- ks1, rows 0-3: B(s+2) copies
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if (r == 0) wait16_4<7>(A[0], B1);
+            if (r == 0) wait_b(IntConst<7>{}, A[0], B1);
             else if (r == 1) wait16<6>(A[1]);
             else if (r == 2) wait16<5>(A[2]);
             else wait16<4>(A[3]);
@@ -347,14 +447,14 @@ gemm8w_kernel(GemmArgs p) {
         rd_b = next_pos(rd_b);
         rd_a = next_pos(rd_a);
         const uint32_t aw2 = lds_base + (uint32_t)(rd_a * kOperandBytes) + a_half;
-        const uint32_t bw2 = lds_base + (uint32_t)(rd_b * kOperandBytes) + b_quarter;
-        read_b(B0, bw2 + kofs0);
+        const uint32_t bw2 = lds_base + (uint32_t)(rd_b * kOperandBytes);
+        read_b(B0, bw2 + bsel0, IntConst<0>{});
 #pragma unroll
         for (int r = 0; r < 4; ++r) read_a(r, aw2 + kofs0);
         // ---- ks1, rows 4-7
 #pragma unroll
         for (int r = 4; r < 8; ++r) {
-            wait16<11>(A[r]);
+            wait16<kWaitFull>(A[r]);
             mfma(r, 0, B1[0]); mfma(r, 1, B1[1]); mfma(r, 2, B1[2]);
             if (r < 7) mfma(r, 3, B1[3]);
             else mfma_last(B1[3], __builtin_amdgcn_readfirstlane(kb == nk - 1));   // + epilogue wait
@@ -371,7 +471,24 @@ gemm8w_kernel(GemmArgs p) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B0[0]), "+v"(B0[1]), "+v"(B0[2]), "+v"(B0[3]));
     wait_vmcnt<0>();
 
-    if constexpr (kEpi != kEpiDz) {
+    if constexpr (kStoreT) {
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int col_e = lane_e & 15, grp_e = lane_e >> 4;
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int64_t cn = nw + bj * 16 + col_e;
+            if (cn >= p.n) continue;
+            float* crow = p.c + cn * p.ldc;
+#pragma unroll
+            for (int bi = 0; bi < 8; ++bi) {
+                const int64_t r0 = mw + bi * 16 + grp_e * 4;
+                if (r0 < p.m)
+                    *(float4*)(crow + r0) = make_float4(acc[bi][bj][0], acc[bi][bj][1],
+                                                        acc[bi][bj][2], acc[bi][bj][3]);
+            }
+        }
+    } else if constexpr (kEpi != kEpiDz) {
         // addresses formed anew (an opaque copy of the lane index): shared
         // with the loads above, they would stay live across the K loop
         int lane_e = lane;
@@ -687,9 +804,7 @@ bool make_backward_plan(int64_t n, int64_t d, int64_t v, BackwardPlan* p) {
         off += align_up(bytes > 0 ? bytes : 1, 256);
         return o;
     };
-    p->wt_off = take((size_t)d * p->vpad * 2);
     p->ht_off = take((size_t)d * p->npad * 2);
-    p->dzt_off = take((size_t)p->vpad * p->npad * 2);
     p->dz_off = take((size_t)p->npad * p->vpad * 2);
     p->total_bytes = off;
     return true;
@@ -713,11 +828,14 @@ static hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
     if (grid <= 0 || grid > INT32_MAX) return hipErrorInvalidValue;
     const dim3 block(2 * kThreads);
     if (epi == kEpiDz)
-        hipLaunchKernelGGL(gemm8w_kernel<kEpiDz>, dim3((unsigned)grid), block, 0, st, a);
-    else if (epi == kEpiStore)
-        hipLaunchKernelGGL(gemm8w_kernel<kEpiStore>, dim3((unsigned)grid), block, 0, st, a);
+        hipLaunchKernelGGL((gemm8w_kernel<kEpiDz, false>), dim3((unsigned)grid), block, 0, st, a);
+    else if (epi == kEpiStore)      // dh: B = W, K-major
+        hipLaunchKernelGGL((gemm8w_kernel<kEpiStore, true>), dim3((unsigned)grid), block, 0, st, a);
+    else if (epi == kEpiStoreT)     // dW: B = dz, K-major
+        hipLaunchKernelGGL((gemm8w_kernel<kEpiStoreT, true>), dim3((unsigned)grid), block, 0, st, a);
     else
-        hipLaunchKernelGGL(gemm8w_kernel<kEpiStoreAcc>, dim3((unsigned)grid), block, 0, st, a);
+        hipLaunchKernelGGL((gemm8w_kernel<kEpiStoreTAcc, true>), dim3((unsigned)grid), block, 0, st,
+                           a);
     return hipGetLastError();
 }
 
@@ -726,14 +844,11 @@ hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t
                                    const float* lse, const float* g, float* dh, float* dw,
                                    bool accumulate_dw, void* workspace, hipStream_t st) {
     unsigned char* ws = (unsigned char*)workspace;
-    uint16_t* wt = (uint16_t*)(ws + p.wt_off);     // W^T [D][Vp]
     uint16_t* ht = (uint16_t*)(ws + p.ht_off);     // h^T [D][Np]
-    uint16_t* dzt = (uint16_t*)(ws + p.dzt_off);   // dz^T [Vp][Np]
     uint16_t* dz = (uint16_t*)(ws + p.dz_off);     // dz [Np][Vp]
     hipError_t e;
 
-    // 1. dz^T (for dW) and dz (for dh) from the recomputed logits (A = W
-    //    rows, B = h rows, K = D)
+    // 1. dz from the recomputed logits (A = W rows, B = h rows, K = D)
     GemmArgs z{};
     z.a = (const unsigned char*)w; z.lda_b = ldw * 2; z.m = p.v;
     z.b = (const unsigned char*)h; z.ldb_b = ldh * 2; z.n = p.n;
@@ -741,18 +856,16 @@ hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t
     z.mtiles = (p.vpad + kTileV - 1) / kTileV;
     z.ntiles = (p.npad + kTileT - 1) / kTileT;
     z.lse = lse; z.g = g; z.ids = ids; z.vtrue = p.v; z.ntrue = p.n;
-    z.dzt = dw ? dzt : nullptr; z.lddz = p.npad;
-    z.dz = dh ? dz : nullptr; z.ldz = p.vpad;
+    z.dzt = nullptr; z.lddz = 0;
+    z.dz = dz; z.ldz = p.vpad;
     z.vpad = p.vpad; z.npad = p.npad;
     if ((e = launch_gemm(z, kEpiDz, st)) != hipSuccess) return e;
 
     if (dh) {
-        // 2. W^T, then dh = dz W (K = vocabulary)
-        if ((e = launch_transpose((const uint16_t*)w, ldw, p.v, p.d, wt, p.vpad, p.vpad, st)) != hipSuccess)
-            return e;
+        // 2. dh = dz W (K = vocabulary; W read K-major, rows past V as zero)
         GemmArgs a{};
         a.a = (const unsigned char*)dz; a.lda_b = p.vpad * 2; a.m = p.n;
-        a.b = (const unsigned char*)wt; a.ldb_b = p.vpad * 2; a.n = p.d;
+        a.b = (const unsigned char*)w; a.ldb_b = ldw * 2; a.n = p.d; a.bk_rows = p.v;
         a.nk = (int)(p.vpad / 64);
         a.mtiles = (p.n + kTileV - 1) / kTileV;
         a.ntiles = (p.d + kTileT - 1) / kTileT;
@@ -760,17 +873,19 @@ hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t
         if ((e = launch_gemm(a, kEpiStore, st)) != hipSuccess) return e;
     }
     if (dw) {
-        // 3. h^T, then dW = dz^T h (K = tokens, ascending)
+        // 3. h^T, then dW^T = h^T dz computed as C[d][v] (K = tokens,
+        //    ascending; dz read K-major) and stored transposed into dW[v][d]
         if ((e = launch_transpose((const uint16_t*)h, ldh, p.n, p.d, ht, p.npad, p.npad, st)) != hipSuccess)
             return e;
         GemmArgs b{};
-        b.a = (const unsigned char*)dzt; b.lda_b = p.npad * 2; b.m = p.v;
-        b.b = (const unsigned char*)ht; b.ldb_b = p.npad * 2; b.n = p.d;
+        b.a = (const unsigned char*)ht; b.lda_b = p.npad * 2; b.m = p.d;
+        b.b = (const unsigned char*)dz; b.ldb_b = p.vpad * 2; b.n = p.v; b.bk_rows = p.n;
         b.nk = (int)(p.npad / 64);
-        b.mtiles = (p.v + kTileV - 1) / kTileV;
-        b.ntiles = (p.d + kTileT - 1) / kTileT;
+        b.mtiles = (p.d + kTileV - 1) / kTileV;
+        b.ntiles = (p.v + kTileT - 1) / kTileT;
         b.c = dw; b.ldc = p.d;
-        if ((e = launch_gemm(b, accumulate_dw ? kEpiStoreAcc : kEpiStore, st)) != hipSuccess) return e;
+        if ((e = launch_gemm(b, accumulate_dw ? kEpiStoreTAcc : kEpiStoreT, st)) != hipSuccess)
+            return e;
     }
     return hipSuccess;
 }

@@ -16,6 +16,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -115,6 +116,28 @@ __device__ __forceinline__ void wait16(u32x4& a, u32x4 (&b)[8]) {
                  : "+v"(a), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]),
                    "+v"(b[5]), "+v"(b[6]), "+v"(b[7])
                  : "i"(N));
+}
+
+// A fragment of an operand stored K-major ([K][M], M contiguous) in LDS:
+// two transposing reads (ds_read_b64_tr_b16), K elements 0-3 and 4-7 of the
+// lane's eight, written into the two halves of one 128-bit fragment.
+// Within each 16-lane group, lane i receives element (i & 3) of the 8-byte
+// row addressed by lane (i >> 2) + 4 j as its element j, so lane p of the
+// group addresses K row (p >> 2) of its four at M offset 4 (p & 3): lane i
+// then holds M = i, K = j of the group's four rows, the layout of a
+// 16x16x32 MFMA source (row l & 15, K 8 (l >> 4) + 0..7).  The halves are
+// outputs of the asm (so not waited for, like lds_read16's) that the
+// register allocator places as the two halves of the fragment's register
+// tuple; a copy in between would read them before their wait, which the
+// library's code check rules out.
+template <int kOff>
+__device__ __forceinline__ void lds_read_tr(u32x4& r, uint32_t addr) {
+    static_assert(kOff >= 0 && kOff + 2048 < 65536, "ds_read immediate offset");
+    u32x2 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(kOff) : "memory");
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi) : "v"(addr), "i"(kOff + 2048) : "memory");
+    r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
 }
 
 template <int N>

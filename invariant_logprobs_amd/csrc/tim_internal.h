@@ -163,7 +163,7 @@ hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const fl
 // vocabulary and token counts rounded up to multiples of 64.
 struct BackwardPlan {
     int64_t n, d, v, npad, vpad;
-    size_t wt_off, ht_off, dzt_off, dz_off, total_bytes;
+    size_t ht_off, dz_off, total_bytes;
 };
 
 bool make_backward_plan(int64_t n, int64_t d, int64_t v, BackwardPlan* p);

@@ -297,6 +297,42 @@ def check_kernel(code):
     return bad
 
 
+def check_lds_reads(code):
+    """Violations of one rule in one kernel: no instruction reads a register
+    that an LDS read (ds_read*) writes before an s_waitcnt that counts LDS
+    operations has followed that read.  The MFMA kernels issue their LDS
+    reads from asm and wait for them with counted waits of their own; a
+    copy of a read's destination that the compiler places in between (for
+    instance to join the two halves of a transposed fragment) would read
+    registers whose data has not arrived."""
+    index_of = {ins.addr: k for k, ins in enumerate(code)}
+    bad = []
+    for i, ins in enumerate(code):
+        if not ins.op.startswith("ds_read") or not ins.dst:
+            continue
+        dst = ins.dst
+        stack = list(successors(code, i, index_of))
+        seen = set()
+        while stack:
+            j = stack.pop()
+            if j in seen:
+                continue
+            seen.add(j)
+            nxt = code[j]
+            if nxt.op == "s_waitcnt" and "lgkmcnt" in nxt.args:
+                continue
+            srcs = nxt.regs - nxt.dst if not nxt.op.startswith(("ds_", "buffer_", "global_")) \
+                else nxt.regs - (nxt.dst if nxt.op.startswith("ds_read") else set())
+            if srcs & dst:
+                bad.append(f"{nxt.op} {nxt.args} at {nxt.addr:#x} reads the destination of "
+                           f"{ins.op} {ins.args} at {ins.addr:#x} before any LDS wait")
+                continue
+            if nxt.dst and dst <= nxt.dst and not nxt.op.startswith("ds_read"):
+                continue        # overwritten: the pending value is no longer read
+            stack.extend(successors(code, j, index_of))
+    return bad
+
+
 @functools.lru_cache(maxsize=4)
 def private_segment_sizes(lib_path):
     """{kernel symbol: private (scratch) bytes per work-item} from the code

@@ -62,6 +62,28 @@ def test_no_mfma_hazard(kernels, name):
     assert found
 
 
+@pytest.mark.parametrize("name", MFMA_KERNELS)
+def test_no_lds_read_destination_is_read_before_its_wait(kernels, name):
+    found = 0
+    for k, code in kernels.items():
+        if name not in k:
+            continue
+        found += 1
+        bad = ic.check_lds_reads(code)
+        assert not bad, f"{k}:\n" + "\n".join(bad[:10])
+    assert found
+
+
+def test_checker_catches_a_copy_planted_between_a_read_and_its_wait(kernels):
+    code = next(c for k, c in kernels.items() if "gemm8w_kernelILi3ELb1E" in k)
+    assert not ic.check_lds_reads(code)
+    k = next(i for i, ins in enumerate(code) if ins.op == "ds_read_b64_tr_b16")
+    r = sorted(r for f, r in code[k].dst if f == "v")[-1]
+    plant = ic.Insn(code[k].addr + 1, "v_mov_b32_e32", f"v0, v{r}", None)
+    bad = ic.check_lds_reads(code[:k + 1] + [plant] + code[k + 1:])
+    assert any(f"v_mov_b32_e32 v0, v{r}" in b for b in bad)
+
+
 def test_head_gemm_and_stats_stream_kernels_use_no_scratch():
     sizes = ic.private_segment_sizes(tim.LIB_PATH)
     checked = 0
