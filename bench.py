@@ -142,7 +142,12 @@ def main():
     log(f"generating workload {name}")
     wl = workloads.make(name, device=dev)
     if args.backward_only:
-        print(json.dumps(backward_measure(tim, wl, torch, np)), flush=True)
+        res = backward_measure(tim, wl, torch, np)
+        del wl
+        torch.cuda.empty_cache()
+        res["fp32_head"] = backward_measure(tim, workloads.make("fp32_head", device=dev), torch,
+                                            np, reps=3)
+        print(json.dumps(res), flush=True)
         return
     if args.ex_only:
         print(json.dumps(scoring_ex_measure(tim, workloads, wl, torch, np)), flush=True)
@@ -221,6 +226,8 @@ def main():
         out["small_batch"] = small_batch_measure(tim, wl, torch, np)
         out["scoring_ex"] = scoring_ex_measure(tim, workloads, wl, torch, np)
         out["backward"] = backward_measure(tim, wl, torch, np)
+        out["backward"]["fp32_head"] = backward_measure(
+            tim, workloads.make("fp32_head", device=dev), torch, np, reps=3)
         out["ppo"] = ppo_scale(tim, torch, np, args.stats_log2)
         out["extras"] = extras_measure(tim, workloads, wl, torch, np, args.stats_log2)
         out["stats_scale"] = stats_scale(tim, workloads, torch, np, args.stats_log2)
@@ -557,25 +564,33 @@ def dsv3_measure(tim, workloads, torch, np):
 def backward_measure(tim, wl, torch, np, reps=5):
     """tim_logprob_backward on the workload with a dense upstream gradient:
     the logits recomputed (2 N D V FLOP), dh = dz W and dW = dz^T h (2 N D V
-    each), against dense bf16 MFMA peak."""
+    each), against the dense MFMA peak of the inputs' type (bf16, or fp32 for
+    the FP32 head)."""
     sp = wl.spec
     n, d, v = sp.n, sp.d, sp.v
+    f32 = wl.h.dtype == torch.float32
+    dtype = tim.TIM_F32 if f32 else tim.TIM_BF16
+    peak = PEAK_F32_MFMA_TFLOPS if f32 else PEAK_BF16_TFLOPS
     _, lse, _ = tim.tim_logprob_forward(wl.h, wl.w, wl.ids, return_lse=True)
     g = torch.Generator(device="cuda").manual_seed(11)
     grad = torch.randn(n, generator=g, device="cuda", dtype=torch.float32) / n
-    ws = torch.empty(tim.backward_workspace_bytes(n, d, v), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tim.backward_workspace_bytes(n, d, v, dtype), dtype=torch.uint8,
+                     device="cuda")
     dh = torch.empty(n, d, dtype=torch.float32, device="cuda")
     dw = torch.empty(v, d, dtype=torch.float32, device="cuda")
     fn = lambda: tim.tim_logprob_backward(wl.h, wl.w, wl.ids, lse, grad, dw=dw, workspace=ws)
     ms = time_calls(fn, torch, np, reps=reps, warm=1)
     flops = 3 * 2.0 * n * d * v
     tf = flops / (ms / 1e3) / 1e12
-    log(f"backward: {ms:.3f} ms, {tf:.1f} TFLOP/s ({tf / PEAK_BF16_TFLOPS:.1%} of bf16 peak), "
+    kind = "fp32" if f32 else "bf16"
+    log(f"backward ({kind}): {ms:.3f} ms, {tf:.1f} TFLOP/s ({tf / peak:.1%} of {kind} peak), "
         f"workspace {ws.numel() / 2**30:.2f} GiB")
+    res = {"ms": ms, "flops": flops, "achieved_TFLOPs": tf, "peak_TFLOPs": peak,
+           "frac": tf / peak, "tokens": n, "hidden": d, "vocab": v, "dtype": kind,
+           "workspace_GiB": ws.numel() / 2**30}
     del ws, dh, dw
     torch.cuda.empty_cache()
-    return {"ms": ms, "flops": flops, "achieved_TFLOPs": tf, "peak_TFLOPs": PEAK_BF16_TFLOPS,
-            "frac": tf / PEAK_BF16_TFLOPS, "tokens": n, "hidden": d, "vocab": v}
+    return res
 
 
 EX_TAU = 0.7

@@ -480,7 +480,7 @@ enum {
 };
 
 /* Bytes of device workspace tim_logprob_backward needs; 0 for sizes or a
- * dtype it does not accept (only TIM_BF16 is).  Pure host function. */
+ * dtype it does not accept.  Pure host function. */
 size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype);
 
 /*
@@ -492,8 +492,10 @@ size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int
  * ("RL: Training Inference Mismatch", the "log p" chain differentiated; the
  * policy-gradient term g_t grad log q_t of its importance-sampling section.)
  *
- *  h, ldh, w, ldw, ids, n, d, v  as for tim_logprob_forward; dtype must be
- *             TIM_BF16 (else TIM_EUNSUPPORTED).
+ *  h, ldh, w, ldw, ids, n, d, v, dtype  as for tim_logprob_forward
+ *             (TIM_F32: the FP32 LM head of "Train-Inference Consistency",
+ *             section 3, which keeps the output layer's weights and compute
+ *             in FP32 during training).
  *  lse        [n] fp32: the lse output of tim_logprob_forward on the same
  *             inputs (the softmax is exp(z - lse)).
  *  grad_logp  [n] fp32.  A token with grad 0, or an id outside [0, v),
@@ -508,9 +510,11 @@ size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int
  *             256-byte aligned.
  *
  * Arithmetic: the logits are recomputed exactly as tim_logprob_forward does
- * (same K order and instructions); dz is rounded to bf16 once; dh and dw are
- * bf16 x bf16 products accumulated in fp32, one chain per output element in
- * ascending K, no split-K and no atomics.  dh[t] depends only on token t.
+ * (same K order and instructions).  TIM_BF16: dz is rounded to bf16 once;
+ * dh and dw are bf16 x bf16 products accumulated in fp32.  TIM_F32: dz stays
+ * fp32; dh and dw are fp32 products accumulated in fp32.  One chain per
+ * output element in ascending K, no split-K and no atomics.  dh[t] depends
+ * only on token t.
  * dw's chain over tokens continues across calls in accumulate mode, so
  * accumulating batches whose sizes are multiples of 64 tokens reproduces
  * the bits of one call over their concatenation.

@@ -591,8 +591,8 @@ def extras_dict(out: torch.Tensor, n_ratio_q: int = 3, n_abs_q: int = 1) -> dict
     return res
 
 
-def backward_workspace_bytes(n: int, d: int, v: int) -> int:
-    return int(load_library().tim_logprob_backward_workspace_bytes(n, d, v, TIM_BF16))
+def backward_workspace_bytes(n: int, d: int, v: int, dtype: int = TIM_BF16) -> int:
+    return int(load_library().tim_logprob_backward_workspace_bytes(n, d, v, dtype))
 
 
 @_on_stream
@@ -603,14 +603,15 @@ def tim_logprob_backward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
                          stream=None):
     """``(dh, dw)`` (fp32, ``[N, D]`` and ``[V, D]``) of ``L`` through
     ``logp = log softmax(h W^T)[ids]`` given ``grad_logp = dL/dlogp`` and the
-    forward's ``lse``.  bf16 ``h`` and ``W`` only.  With ``accumulate_dw`` the
+    forward's ``lse``.  ``h`` and ``W`` both bf16 or both fp32.  With ``accumulate_dw`` the
     given ``dw`` is read and the sum over this batch's tokens continues from
     it."""
     lib = load_library()
     for name, t in (("h", h), ("w", w), ("ids", ids), ("lse", lse), ("grad_logp", grad_logp)):
         _require_gpu(name, t)
-    if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
-        raise ValueError("the backward takes bf16 h and W")
+    if h.dtype != w.dtype or h.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("h and W must both be bfloat16 or both float32")
+    dtype = TIM_BF16 if h.dtype == torch.bfloat16 else TIM_F32
     if h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
         raise ValueError("h must be [N, D] and w [V, D]")
     if h.stride(1) != 1 or w.stride(1) != 1:
@@ -632,12 +633,12 @@ def tim_logprob_backward(h: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
             raise ValueError("dw must be a contiguous fp32 [V, D] tensor")
     else:
         dw = None
-    need = lib.tim_logprob_backward_workspace_bytes(n, d, v, TIM_BF16)
+    need = lib.tim_logprob_backward_workspace_bytes(n, d, v, dtype)
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
     flags = TIM_BWD_ACCUMULATE_DW if accumulate_dw else 0
     st = lib.tim_logprob_backward(_dptr(h), h.stride(0), _dptr(w), w.stride(0), _dptr(ids),
-                                  _dptr(lse), _dptr(grad_logp), n, d, v, TIM_BF16, flags,
+                                  _dptr(lse), _dptr(grad_logp), n, d, v, dtype, flags,
                                   _dptr(dh), _dptr(dw), _dptr(workspace),
                                   workspace.numel() * workspace.element_size(),
                                   _stream_handle(stream))

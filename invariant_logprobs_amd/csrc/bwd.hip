@@ -47,42 +47,49 @@ using namespace mfma;
 
 constexpr int kTrTile = 64;
 constexpr int kTrThreads = 256;
-constexpr int kTrPitch = kTrTile + 8;   // LDS row pitch in elements: rows stay 16-byte aligned
 
 // out[c][r] = in[r][c] for r < rows, c < cols; out[c][r] = 0 for
-// rows <= r < out_cols.  Grid: (out_cols / 64, ceil(cols / 64)).  Every
-// global access moves 16 bytes: a thread loads 8 consecutive elements of an
-// input row into the LDS tile, then gathers 8 consecutive rows of one tile
-// column and stores them as 8 consecutive elements of an output row.
-// Requires cols % 8 == 0, out_cols % 64 == 0, in, out, ld_in and ld_out
-// 16-byte aligned (in elements: multiples of 8), which the backward's
-// operands meet (D % 64 == 0, 16-byte aligned rows, padded sizes).
+// rows <= r < out_cols.  T: uint16_t (bf16) or uint32_t (fp32); kV = 16 /
+// sizeof(T) elements move in every global access.  Grid: (out_cols / 64,
+// ceil(cols / 64)).  A thread loads kV consecutive elements of an input row
+// into the LDS tile, then gathers kV consecutive rows of one tile column and
+// stores them as kV consecutive elements of an output row.  Requires
+// cols % kV == 0, out_cols % 64 == 0, in, out, ld_in and ld_out 16-byte
+// aligned (in elements: multiples of kV), which the backward's operands
+// meet (D % 64 == 0, 16-byte aligned rows, padded sizes).
+template <typename T>
 __global__ void __launch_bounds__(kTrThreads)
-transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t rows, int64_t cols,
-                      uint16_t* __restrict__ out, int64_t ld_out, int64_t out_cols) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kTrTile][kTrPitch];
+transpose_kernel(const T* __restrict__ in, int64_t ld_in, int64_t rows, int64_t cols,
+                 T* __restrict__ out, int64_t ld_out, int64_t out_cols) {
+    constexpr int kV = 16 / (int)sizeof(T);
+    constexpr int kG = kTrTile / kV;             // kV-element groups per tile row
+    constexpr int kRows = kTrThreads / kG;       // tile rows per pass
+    constexpr int kPitch = kTrTile + kV;         // LDS row pitch: rows stay 16-byte aligned
+    __shared__ __attribute__((aligned(16))) T tile[kTrTile][kPitch];
     const int64_t r0 = (int64_t)blockIdx.x * kTrTile, c0 = (int64_t)blockIdx.y * kTrTile;
-    const int g = threadIdx.x & 7;          // 8-element group
-    const int q = threadIdx.x >> 3;         // 0..31
+    const int g = threadIdx.x % kG;
+    const int q = threadIdx.x / kG;
 #pragma unroll
-    for (int k = 0; k < kTrTile / 32; ++k) {
-        const int lr = q + 32 * k;
-        const int64_t r = r0 + lr, c = c0 + g * 8;
+    for (int k = 0; k < kTrTile / kRows; ++k) {
+        const int lr = q + kRows * k;
+        const int64_t r = r0 + lr, c = c0 + g * kV;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (r < rows && c < cols) v = *(const uint4*)(in + r * ld_in + c);
-        *(uint4*)&tile[lr][g * 8] = v;
+        *(uint4*)&tile[lr][g * kV] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kTrTile / 32; ++k) {
-        const int lc = q + 32 * k;                 // tile column = output row
-        const int64_t c = c0 + lc, r = r0 + g * 8; // output row, first output column
-        uint32_t e[8];
+    for (int k = 0; k < kTrTile / kRows; ++k) {
+        const int lc = q + kRows * k;                  // tile column = output row
+        const int64_t c = c0 + lc, r = r0 + g * kV;    // output row, first output column
+        T e[kV];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = tile[g * 8 + j][lc];
-        if (c < cols && r < out_cols)
-            *(uint4*)(out + c * ld_out + r) = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
-                                                         e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+        for (int j = 0; j < kV; ++j) e[j] = tile[g * kV + j][lc];
+        if (c < cols && r < out_cols) {
+            uint4 o;
+            __builtin_memcpy(&o, e, 16);
+            *(uint4*)(out + c * ld_out + r) = o;
+        }
     }
 }
 
@@ -793,9 +800,10 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ x, i
 // host side
 // ---------------------------------------------------------------------------
 
-bool make_backward_plan(int64_t n, int64_t d, int64_t v, BackwardPlan* p) {
-    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || n > INT32_MAX) return false;
-    p->n = n; p->d = d; p->v = v;
+bool make_backward_plan(int64_t n, int64_t d, int64_t v, int dtype, BackwardPlan* p) {
+    if (n < 0 || d <= 0 || v <= 0 || v > INT32_MAX || n > INT32_MAX || (dtype != 0 && dtype != 1))
+        return false;
+    p->n = n; p->d = d; p->v = v; p->dtype = dtype;
     p->npad = round_up(n > 0 ? n : 1, 64);
     p->vpad = round_up(v, 64);
     size_t off = 0;
@@ -804,21 +812,30 @@ bool make_backward_plan(int64_t n, int64_t d, int64_t v, BackwardPlan* p) {
         off += align_up(bytes > 0 ? bytes : 1, 256);
         return o;
     };
-    p->ht_off = take((size_t)d * p->npad * 2);
-    p->dz_off = take((size_t)p->npad * p->vpad * 2);
+    if (dtype == 0) {
+        p->wt_off = p->dzt_off = 0;                    // not used
+        p->ht_off = take((size_t)d * p->npad * 2);
+        p->dz_off = take((size_t)p->npad * p->vpad * 2);
+    } else {
+        p->wt_off = take((size_t)d * p->vpad * 4);
+        p->ht_off = take((size_t)d * p->npad * 4);
+        p->dzt_off = take((size_t)p->vpad * p->npad * 4);
+        p->dz_off = take((size_t)p->npad * p->vpad * 4);
+    }
     p->total_bytes = off;
     return true;
 }
 
-static hipError_t launch_transpose(const uint16_t* in, int64_t ld_in, int64_t rows, int64_t cols,
-                                   uint16_t* out, int64_t ld_out, int64_t out_cols,
-                                   hipStream_t st) {
+template <typename T>
+static hipError_t launch_transpose(const T* in, int64_t ld_in, int64_t rows, int64_t cols, T* out,
+                                   int64_t ld_out, int64_t out_cols, hipStream_t st) {
+    constexpr int kV = 16 / (int)sizeof(T);
     const int64_t gx = (out_cols + kTrTile - 1) / kTrTile, gy = (cols + kTrTile - 1) / kTrTile;
     if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
-    if (cols % 8 != 0 || out_cols % kTrTile != 0 || ld_in % 8 != 0 || ld_out % 8 != 0 ||
+    if (cols % kV != 0 || out_cols % kTrTile != 0 || ld_in % kV != 0 || ld_out % kV != 0 ||
         (uintptr_t)in % 16 != 0 || (uintptr_t)out % 16 != 0)
         return hipErrorInvalidValue;                   // the kernel's 16-byte accesses
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kTrThreads),
+    hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)gx, (unsigned)gy), dim3(kTrThreads),
                        0, st, in, ld_in, rows, cols, out, ld_out, out_cols);
     return hipGetLastError();
 }
@@ -839,10 +856,63 @@ static hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
     return hipGetLastError();
 }
 
+// fp32 (the FP32 LM head's backward): the fp32 forward's tile kernel forms
+// the logits with the forward's MFMA sequence and writes dz in fp32 in both
+// layouts (no rounding: the head trains in fp32); W^T and h^T make the two
+// products NT GEMMs of the same kernel.  Each output element is one fp32
+// MFMA chain in ascending K, as in the bf16 path.
+static hipError_t launch_backward_f32(const BackwardPlan& p, const float* h, int64_t ldh,
+                                      const float* w, int64_t ldw, const int32_t* ids,
+                                      const float* lse, const float* g, float* dh, float* dw,
+                                      bool accumulate_dw, unsigned char* ws, hipStream_t st) {
+    float* wt = (float*)(ws + p.wt_off);       // W^T [D][Vp]
+    float* ht = (float*)(ws + p.ht_off);       // h^T [D][Np]
+    float* dzt = (float*)(ws + p.dzt_off);     // dz^T [Vp][Np]
+    float* dz = (float*)(ws + p.dz_off);       // dz [Np][Vp]
+    hipError_t e;
+    F32Gemm z{};
+    z.mode = kF32Dz;
+    z.a = w; z.lda = ldw; z.b = h; z.ldb = ldh; z.ids = ids;
+    z.m = p.v; z.n = p.n; z.k = p.d;
+    z.ep.lse = lse; z.ep.g = g;
+    z.ep.dz = dh ? dz : nullptr; z.ep.ldz = p.vpad;
+    z.ep.dzt = dw ? dzt : nullptr; z.ep.lddzt = p.npad;
+    z.ep.vpad = p.vpad; z.ep.npad = p.npad;
+    if ((e = launch_f32_gemm(z, st)) != hipSuccess) return e;
+    if (dh) {
+        // dh[t][d] = sum_v dz[t][v] W^T[d][v]
+        if ((e = launch_transpose<uint32_t>((const uint32_t*)w, ldw, p.v, p.d, (uint32_t*)wt,
+                                            p.vpad, p.vpad, st)) != hipSuccess)
+            return e;
+        F32Gemm a{};
+        a.mode = kF32Store;
+        a.a = dz; a.lda = p.vpad; a.b = wt; a.ldb = p.vpad;
+        a.m = p.n; a.n = p.d; a.k = p.vpad;
+        a.ep.c = dh; a.ep.ldc = p.d;
+        if ((e = launch_f32_gemm(a, st)) != hipSuccess) return e;
+    }
+    if (dw) {
+        // dW[v][d] = sum_t dz^T[v][t] h^T[d][t] (K = tokens, ascending)
+        if ((e = launch_transpose<uint32_t>((const uint32_t*)h, ldh, p.n, p.d, (uint32_t*)ht,
+                                            p.npad, p.npad, st)) != hipSuccess)
+            return e;
+        F32Gemm b{};
+        b.mode = accumulate_dw ? kF32StoreAcc : kF32Store;
+        b.a = dzt; b.lda = p.npad; b.b = ht; b.ldb = p.npad;
+        b.m = p.v; b.n = p.d; b.k = p.npad;
+        b.ep.c = dw; b.ep.ldc = p.d;
+        if ((e = launch_f32_gemm(b, st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t ldh,
                                    const void* w, int64_t ldw, const int32_t* ids,
                                    const float* lse, const float* g, float* dh, float* dw,
                                    bool accumulate_dw, void* workspace, hipStream_t st) {
+    if (p.dtype == 1)
+        return launch_backward_f32(p, (const float*)h, ldh, (const float*)w, ldw, ids, lse, g, dh,
+                                   dw, accumulate_dw, (unsigned char*)workspace, st);
     unsigned char* ws = (unsigned char*)workspace;
     uint16_t* ht = (uint16_t*)(ws + p.ht_off);     // h^T [D][Np]
     uint16_t* dz = (uint16_t*)(ws + p.dz_off);     // dz [Np][Vp]
@@ -875,7 +945,7 @@ hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t
     if (dw) {
         // 3. h^T, then dW^T = h^T dz computed as C[d][v] (K = tokens,
         //    ascending; dz read K-major) and stored transposed into dW[v][d]
-        if ((e = launch_transpose((const uint16_t*)h, ldh, p.n, p.d, ht, p.npad, p.npad, st)) != hipSuccess)
+        if ((e = launch_transpose<uint16_t>((const uint16_t*)h, ldh, p.n, p.d, ht, p.npad, p.npad, st)) != hipSuccess)
             return e;
         GemmArgs b{};
         b.a = (const unsigned char*)ht; b.lda_b = p.npad * 2; b.m = p.d;

@@ -103,7 +103,19 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t G, int64_t nchu
 }
 
 // fp32 inputs.  kEnt: also carry u (entropy).  c2 = log2(e) / tau.
-template <bool kEnt>
+//
+// kMode selects what becomes of a tile of fp32 products (F32Gemm in
+// tim_internal.h): the forward's fold (kF32Fold), or, for the backward of
+// the fp32 head, with W as the A rows (v) and h as the B rows (n):
+//   kF32Dz        the logits, formed by the very MFMA sequence of the
+//                 forward, turned into dz[t][v] = g_t ([v == a_t] - p_t[v])
+//                 (fp32, zero outside V x N up to the padded sizes), written
+//                 as dz [Np][Vp] and/or dz^T [Vp][Np];
+//   kF32Store     C[m][n] = sum_k A[m][k] B[n][k] stored (fp32);
+//   kF32StoreAcc  the same, the chain continuing from the stored C.
+// A lane holds rows 8 q + 4 lhalf + i (i = 0..3) of column lrow of each
+// 32 x 32 block (acc register 4 q + i).
+template <bool kEnt, int kMode = kF32Fold>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
@@ -112,7 +124,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                        int nk, int chunk_tiles, int64_t nvtiles, int64_t nchunks,
                        int64_t nttiles, float c2, float2* __restrict__ part,
                        float* __restrict__ upart, float* __restrict__ zsel,
-                       int32_t* __restrict__ n_bad_ids) {
+                       int32_t* __restrict__ n_bad_ids, F32Epi ep) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -141,7 +153,8 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
         int64_t t = t0 + wt * 128 + bj * 32 + lrow;
-        my_id[bj] = t < n ? ids[t] : -1;
+        if constexpr (kMode == kF32Fold || kMode == kF32Dz) my_id[bj] = t < n ? ids[t] : -1;
+        else my_id[bj] = -1;
     }
 
     f32x16 acc[4][4];
@@ -278,14 +291,40 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     issue_frags(fa, rd_w, rd_h, 0);
 
     int st = 0;
+    // row of A (vocabulary for the head) of acc register 4 q + i of block bi:
+    // arow0 + bi 32 + q 8 + i
+    const int64_t arow0 = vt_first * kTileV + wv * 128 + lhalf * 4;
     {
         constexpr int vt_local = 0;
+        if constexpr (kMode == kF32StoreAcc) {
+            // one base pointer per column, 32-bit row offsets (a tile spans
+            // 256 rows of C)
+            const uint32_t ldc = (uint32_t)ep.ldc;
+            const int64_t mlim = v - arow0;                  // rows arow0 + mrel < v
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
+            for (int bj = 0; bj < 4; ++bj) {
+                const int64_t cn = t0 + wt * 128 + bj * 32 + lrow;
+                const bool cv = cn < n;
+                const float* cb = ep.c + arow0 * ep.ldc + (cv ? cn : 0);
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
+                for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+                    for (int r = 0; r < 16; ++r) {
+                        const int mrel = bi * 32 + (r >> 2) * 8 + (r & 3);
+                        acc[bi][bj][r] = (cv && mrel < mlim) ? cb[(uint32_t)mrel * ldc] : 0.f;
+                    }
+                    asm volatile("" : "+a"(acc[bi][bj]));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+        }
 
         for (int kb = 0; kb < nk; ++kb, ++st) {
             issue_frags(fb, rd_w, rd_h, 1);
@@ -351,6 +390,7 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
             cp_h = next_pos(cp_h);
         }
 
+        if constexpr (kMode == kF32Fold) {
         // ---- epilogue of one vocabulary tile: online log-sum-exp + gather.
         // Per token column, the lane's 64 rows are folded block by block
         // (32-row MFMA blocks bi = 0..3, 16 rows per lane each) into the
@@ -439,6 +479,69 @@ lmhead_partials_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                         zsel_reg[bj] = tgt[bj] == bi * 16 + r ? acc[bi][bj][r] : zsel_reg[bj];
             have_zsel |= any_tgt;
         }
+        }
+    }
+    if constexpr (kMode != kF32Fold) {
+        // the backward's tiles: drain the look-ahead reads and the extra
+        // copies, then write the tile
+        frags_ready<0>(fa);
+        wait_vmcnt<0>();
+        if constexpr (kMode == kF32Dz) {
+            // dz = g_t ([v == a_t] - exp(z - lse_t)) for v < V, t < N; 0 in
+            // the padding up to (Vp, Np).  Rows past V of the tile hold
+            // finite logits of a clamped row, and their dz is selected away.
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+                const int64_t t = t0 + wt * 128 + bj * 32 + lrow;
+                const bool tv = t < n;
+                const float g = tv ? ep.g[t] : 0.f;
+                const float l = tv ? ep.lse[t] : 0.f;
+                const int32_t a = my_id[bj];
+                const bool ok = tv && a >= 0 && (int64_t)a < v && g != 0.f;
+                const bool t_in = t < ep.npad;
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t v0 = arow0 + bi * 32 + q * 8;   // four rows v0 .. v0 + 3
+                        float d[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int64_t vv = v0 + i;
+                            const float pz = fast_exp2((acc[bi][bj][q * 4 + i] - l) * kLog2e);
+                            const float dz = g * ((vv == (int64_t)a ? 1.f : 0.f) - pz);
+                            d[i] = (ok && vv < v) ? dz : 0.f;
+                        }
+                        if (t_in && v0 < ep.vpad) {
+                            if (ep.dz)
+                                *(float4*)(ep.dz + t * ep.ldz + v0) = make_float4(d[0], d[1], d[2], d[3]);
+                            if (ep.dzt) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) ep.dzt[(v0 + i) * ep.lddzt + t] = d[i];
+                            }
+                        }
+                    }
+                }
+            }
+        } else {
+            // C[m][n]: lanes of a row hold 32 consecutive n (128 bytes)
+            const uint32_t ldc = (uint32_t)ep.ldc;
+            const int64_t mlim = v - arow0;
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+                const int64_t cn = t0 + wt * 128 + bj * 32 + lrow;
+                if (cn >= n) continue;
+                float* cb = ep.c + arow0 * ep.ldc + cn;
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int mrel = bi * 32 + (r >> 2) * 8 + (r & 3);
+                        if (mrel < mlim) cb[(uint32_t)mrel * ldc] = acc[bi][bj][r];
+                    }
+            }
+        }
+        return;
     }
     // drain: the last stage's look-ahead read and the extra copies; the ring
     // is reused for the wave exchange below
@@ -1366,7 +1469,7 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, st,
                            (const unsigned char*)h, ldh * esz, (const unsigned char*)w, ldw * esz,
                            ids, p.n, p.v, nk, p.chunk_tiles, p.nvtiles, p.nchunks, p.nttiles,
-                           sc.c2, part, upart, zsel, n_bad_ids);
+                           sc.c2, part, upart, zsel, n_bad_ids, F32Epi{});
     };
     if (p.dtype == 0 && p.narrow) {
         // units (chunk halves) rounded up to the 8 XCDs, times the token groups
@@ -1412,6 +1515,25 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
         if (p.entropy) go(lmhead_partials_kernel<true>);
         else go(lmhead_partials_kernel<false>);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_f32_gemm(const F32Gemm& g, hipStream_t st) {
+    if (g.m <= 0 || g.n <= 0 || g.k <= 0 || g.k % 32 != 0) return hipErrorInvalidValue;
+    const int64_t mtiles = (g.m + kTileV - 1) / kTileV, ntiles = (g.n + kTileT - 1) / kTileT;
+    const int64_t grid = mtiles * ntiles;
+    if (grid > INT32_MAX || g.k / 32 > INT32_MAX) return hipErrorInvalidValue;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           (const unsigned char*)g.b, g.ldb * 4, (const unsigned char*)g.a,
+                           g.lda * 4, g.ids, g.n, g.m, (int)(g.k / 32), 1, mtiles, mtiles, ntiles,
+                           kLog2e, (float2*)nullptr, (float*)nullptr, (float*)nullptr,
+                           (int32_t*)nullptr, g.ep);
+    };
+    if (g.mode == kF32Dz) go(lmhead_partials_kernel<false, kF32Dz>);
+    else if (g.mode == kF32Store) go(lmhead_partials_kernel<false, kF32Store>);
+    else if (g.mode == kF32StoreAcc) go(lmhead_partials_kernel<false, kF32StoreAcc>);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

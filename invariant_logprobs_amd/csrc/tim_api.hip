@@ -314,9 +314,9 @@ int tim_mismatch_extras(const float* logp_train, const float* logp_rollout, cons
 }
 
 size_t tim_logprob_backward_workspace_bytes(int64_t n, int64_t d, int64_t v, int dtype) {
-    if (dtype != TIM_BF16) return 0;
+    if (dtype != TIM_BF16 && dtype != TIM_F32) return 0;
     tim::BackwardPlan p;
-    if (!tim::make_backward_plan(n, d, v, &p)) return 0;
+    if (!tim::make_backward_plan(n, d, v, dtype, &p)) return 0;
     return p.total_bytes;
 }
 
@@ -329,21 +329,22 @@ int tim_logprob_backward(const void* h, int64_t ldh, const void* w, int64_t ldw,
         flags > TIM_BWD_ACCUMULATE_DW)
         return TIM_EINVAL;
     if (ldh < d || ldw < d) return TIM_EINVAL;
-    if (dtype != TIM_BF16) return TIM_EUNSUPPORTED;
     if ((dh && !aligned(dh, 16)) || (dw && !aligned(dw, 16))) return TIM_EUNSUPPORTED;
     if (n == 0 && !(dw && !(flags & TIM_BWD_ACCUMULATE_DW))) return TIM_OK;
     if (!w || (n > 0 && (!h || !ids || !lse || !grad_logp))) return TIM_EINVAL;
     if (d % 64 != 0) return TIM_EUNSUPPORTED;
-    if ((ldh * 2) % 16 != 0 || (ldw * 2) % 16 != 0) return TIM_EUNSUPPORTED;
+    const int64_t esz = dtype == TIM_BF16 ? 2 : 4;
+    if ((ldh * esz) % 16 != 0 || (ldw * esz) % 16 != 0) return TIM_EUNSUPPORTED;
     if ((h && !aligned(h, 16)) || !aligned(w, 16)) return TIM_EUNSUPPORTED;
     if (n > INT32_MAX) return TIM_EUNSUPPORTED;
     tim::BackwardPlan p;
-    if (!tim::make_backward_plan(n, d, v, &p)) return TIM_EINVAL;
-    // the three GEMMs: W and h tiles (K = D), dz and W^T tiles (K = Vp, rows
-    // of Vp bf16), dz^T and h^T tiles (K = Np, rows of Np bf16)
-    if (!tile_extent_ok(tim::kTileV, ldw * 2, d * 2) || !tile_extent_ok(tim::kTileT, ldh * 2, d * 2) ||
-        !tile_extent_ok(tim::kTileV, p.vpad * 2, p.vpad * 2) ||
-        !tile_extent_ok(tim::kTileV, p.npad * 2, p.npad * 2))
+    if (!tim::make_backward_plan(n, d, v, dtype, &p)) return TIM_EINVAL;
+    // the three GEMMs' row tiles: W and h (K = D), dz and W (K = Vp, rows of
+    // Vp elements), h^T and dz (K = Np, rows of Np elements)
+    if (!tile_extent_ok(tim::kTileV, ldw * esz, d * esz) ||
+        !tile_extent_ok(tim::kTileT, ldh * esz, d * esz) ||
+        !tile_extent_ok(tim::kTileV, p.vpad * esz, p.vpad * esz) ||
+        !tile_extent_ok(tim::kTileV, p.npad * esz, p.npad * esz))
         return TIM_EUNSUPPORTED;
     if (!workspace || workspace_bytes < p.total_bytes) return TIM_EWORKSPACE;
     if (!aligned(workspace, 256)) return TIM_EUNSUPPORTED;

@@ -66,6 +66,27 @@ hipError_t launch_lse_merge(const LogprobPlan& p, const int32_t* ids, const Scor
                             const void* workspace, float* logp, float* lse, float* entropy,
                             int32_t* n_bad_ids, hipStream_t st);
 
+// The fp32 head's tile kernel (lmhead.hip) as a GEMM for the fp32 backward:
+// C[m][n] = sum_k A[m][k] B[n][k], A and B fp32 rows with K contiguous,
+// the tile pipeline, MFMA sequence and K order of the fp32 forward.
+enum { kF32Fold = 0, kF32Dz = 1, kF32Store = 2, kF32StoreAcc = 3 };
+struct F32Epi {
+    const float* lse; const float* g;   // kF32Dz: the forward's lse, dL/dlogp per token
+    float* dz; int64_t ldz;             // kF32Dz: dz [Np][Vp], or null
+    float* dzt; int64_t lddzt;          // kF32Dz: dz^T [Vp][Np], or null
+    int64_t vpad, npad;                 // kF32Dz: padded sizes written (zeros past V, N)
+    float* c; int64_t ldc;              // kF32Store(Acc): C [m][n]
+};
+struct F32Gemm {
+    int mode;                           // kF32Dz, kF32Store or kF32StoreAcc
+    const void* a; int64_t lda;         // A [m][k] (elements); W for kF32Dz
+    const void* b; int64_t ldb;         // B [n][k]; h for kF32Dz
+    const int32_t* ids;                 // kF32Dz: the selected ids
+    int64_t m, n, k;                    // k a multiple of 32; kF32Dz: m = V, n = N
+    F32Epi ep;
+};
+hipError_t launch_f32_gemm(const F32Gemm& g, hipStream_t st);
+
 // RMSNorm (norm.hip): one wave per row, fp64 row sums, one rounding.
 hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, int64_t n, int64_t d,
                           int dtype, double eps, void* y, int64_t ldy, float* rstd,
@@ -163,10 +184,12 @@ hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const fl
 // vocabulary and token counts rounded up to multiples of 64.
 struct BackwardPlan {
     int64_t n, d, v, npad, vpad;
-    size_t ht_off, dz_off, total_bytes;
+    int dtype;                          // 0 bf16, 1 fp32
+    // bf16: h^T, dz; fp32: W^T, h^T, dz^T, dz (each of the element type)
+    size_t wt_off, ht_off, dzt_off, dz_off, total_bytes;
 };
 
-bool make_backward_plan(int64_t n, int64_t d, int64_t v, BackwardPlan* p);
+bool make_backward_plan(int64_t n, int64_t d, int64_t v, int dtype, BackwardPlan* p);
 
 hipError_t launch_logprob_backward(const BackwardPlan& p, const void* h, int64_t ldh,
                                    const void* w, int64_t ldw, const int32_t* ids,

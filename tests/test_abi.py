@@ -182,7 +182,8 @@ def test_backward_and_ppo_argument_errors(lib):
         kw.get("dh", FAKE), kw.get("dw", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
     assert fwd(n=-1) == tim.TIM_EINVAL
     assert fwd(flags=2) == tim.TIM_EINVAL
-    assert fwd(dtype=1) == tim.TIM_EUNSUPPORTED                     # bf16 only
+    assert fwd(dtype=2) == tim.TIM_EINVAL
+    assert fwd(dtype=1, ldh=66, ldw=64) == tim.TIM_EUNSUPPORTED     # fp32, 264 B rows
     assert fwd(lse=None) == tim.TIM_EINVAL
     assert fwd(g=None) == tim.TIM_EINVAL
     assert fwd(d=96, ldh=96, ldw=96) == tim.TIM_EUNSUPPORTED
@@ -191,7 +192,11 @@ def test_backward_and_ppo_argument_errors(lib):
     assert fwd(dh=FAKE + 4) == tim.TIM_EUNSUPPORTED                 # 16-byte aligned outputs
     assert fwd(dw=FAKE + 8) == tim.TIM_EUNSUPPORTED
     assert fwd(n=0, dw=FAKE + 8) == tim.TIM_EUNSUPPORTED
-    assert lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 1) == 0
+    assert lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 2) == 0
+    # fp32: W^T, h^T and dz in both layouts, fp32
+    b32 = lib.tim_logprob_backward_workspace_bytes(4096, 4096, 151936, 1)
+    assert 4 * (4096 * 151936 + 4096 * 4096 + 2 * 151936 * 4096) <= b32 \
+        <= 4 * (4096 * 151936 + 4096 * 4096 + 2 * 151936 * 4096) + 1024
     b = lib.tim_logprob_backward_workspace_bytes(8192, 4096, 151936, 0)
     # h^T and dz (once), bf16, vocabulary padded to 151936 (a multiple of
     # 64 already); W and dz are read K-major, so neither W^T nor dz^T

@@ -266,3 +266,134 @@ def test_ppo_unaligned_inputs_give_the_aligned_bits():
         for k in ("loss", "grad", "ratio", "contrib", "clipped"):
             assert torch.equal(a["token"][k], b["token"][k]), (scale, k)
         assert torch.equal(a["batch"], b["batch"])
+
+
+# ---------------------------------------------------------------------------
+# fp32 head ("Train-Inference Consistency", section 3: the output layer's
+# weights and compute stay in FP32).  dz is not rounded; the error comes
+# from fp32 arithmetic alone.  With u = 2^-24, S_t = max_v sum_k |h_tk w_vk|:
+# the logits and lse carry at most D u S_t each, so p_tv is off by at most
+# p_tv (2 D u S_t + 5 u) (the exponential's own few ulps included), and the
+# fp32 chains over V (dh) or N (dW) add at most V u or N u of the sum of
+# their absolute terms.  The bounds below take M_tv = |g_t| (p_tv + [v = a_t])
+# >= |dz_tv| for those sums, with a 4x margin.
+# ---------------------------------------------------------------------------
+
+U32 = 2.0 ** -24
+
+
+def _case32(n, d, v, seed, zero_frac=0.2):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    h = torch.randn(n, d, generator=g)
+    w = torch.randn(v, d, generator=g) * 0.05
+    ids = torch.randint(0, v, (n,), generator=g, dtype=torch.int32)
+    gr = torch.randn(n, generator=g, dtype=torch.float32)
+    gr[torch.rand(n, generator=g) < zero_frac] = 0.0
+    return h.to(DEV), w.to(DEV), ids.to(DEV), gr.to(DEV)
+
+
+def _bounds32(h, w, ids, gr, rows_t, rows_v):
+    """(per-token relative error of p, M[rows_t, rows_v]) in fp64."""
+    hd = h.double().cpu().numpy()[rows_t]
+    wd = w.double().cpu().numpy()
+    _, lse, _, _ = oracle.logprob(h.cpu()[rows_t], w.cpu(), ids.cpu()[rows_t], dtype=oracle.F32)
+    s = (np.abs(hd) @ np.abs(wd).T).max(axis=1)                       # S_t
+    rel = U32 * (2 * hd.shape[1] * s + 5)
+    z = hd @ wd[rows_v].T
+    p = np.exp(z - lse[:, None])
+    onehot = (ids.cpu().numpy()[rows_t][:, None] == np.asarray(rows_v)[None, :])
+    m = np.abs(gr.double().cpu().numpy()[rows_t])[:, None] * (p + onehot)
+    return rel, m
+
+
+def check_dh32(dh, dh_ref, h, w, ids, gr, rows, label):
+    v = w.shape[0]
+    rel, m = _bounds32(h, w, ids, gr, rows, np.arange(v))
+    wa = w.abs().double().cpu().numpy()
+    tol = 4 * ((m * rel[:, None]) @ wa + v * U32 * (m @ wa)) + 1e-12
+    err = np.abs(dh - dh_ref)
+    say(f"{label}: dh worst err {err.max():.3e}, worst err/tol {(err / tol).max():.3f}")
+    assert np.all(err <= tol), f"{label}: dh"
+
+
+def check_dw32(dw, dw_ref, h, w, ids, gr, rows_t, rows_v, label):
+    rel, m = _bounds32(h, w, ids, gr, rows_t, rows_v)
+    ha = h.abs().double().cpu().numpy()[rows_t]
+    n = h.shape[0]
+    tol = 4 * ((m * rel[:, None]).T @ ha + n * U32 * (m.T @ ha)) + 1e-12
+    err = np.abs(dw - dw_ref)
+    say(f"{label}: dW worst err {err.max():.3e}, worst err/tol {(err / tol).max():.3f}")
+    assert np.all(err <= tol), f"{label}: dW"
+
+
+@pytest.mark.parametrize("n,d,v", [(300, 256, 2000), (1, 64, 5), (3, 64, 257), (65, 128, 64),
+                                   (256, 64, 1)])
+def test_fp32_backward_parity(n, d, v):
+    h, w, ids, gr = _case32(n, d, v, seed=n * 7 + v)
+    if n > 20:
+        ids[17] = v + 5                              # out of range: contributes nothing
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    torch.cuda.synchronize()
+    dh_ref, dw_ref = oracle.logprob_backward(h.cpu(), w.cpu(), ids.cpu(), gr.cpu(),
+                                             dtype=oracle.F32)
+    gr_eff, ids_c = gr.clone(), ids.clone()
+    if n > 20:
+        gr_eff[17], ids_c[17] = 0.0, 0
+        assert torch.all(dh[17] == 0)
+    label = f"fp32 n={n} d={d} v={v}"
+    check_dh32(dh.double().cpu().numpy(), dh_ref, h, w, ids_c, gr_eff, np.arange(n), label)
+    check_dw32(dw.double().cpu().numpy(), dw_ref, h, w, ids_c, gr_eff, np.arange(n),
+               np.arange(v), label)
+    if v == 1:
+        assert torch.all(dh == 0) and torch.all(dw == 0)
+
+
+def test_fp32_backward_invariance_repeat_and_accumulation():
+    n, d, v = 640, 256, 1500
+    h, w, ids, gr = _case32(n, d, v, seed=4)
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    dh2, dw2 = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    a, b = 64, 197
+    dh_s, _ = tim.tim_logprob_backward(h[a:b].contiguous(), w, ids[a:b].contiguous(),
+                                       lse[a:b].contiguous(), gr[a:b].contiguous(), want_dw=False)
+    acc = torch.zeros(v, d, dtype=torch.float32, device=DEV)
+    for a2, b2 in ((0, 256), (256, 448), (448, 640)):     # multiples of 64 tokens
+        tim.tim_logprob_backward(h[a2:b2].contiguous(), w, ids[a2:b2].contiguous(),
+                                 lse[a2:b2].contiguous(), gr[a2:b2].contiguous(), want_dh=False,
+                                 dw=acc, accumulate_dw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dh.view(torch.int32), dh2.view(torch.int32))
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+    assert torch.equal(dh_s.view(torch.int32), dh[a:b].view(torch.int32))
+    assert torch.equal(acc.view(torch.int32), dw.view(torch.int32))
+
+
+def test_fp32_backward_full_size_sparse_gradient():
+    # the FP32 head at its full size (N = 4096, D = 4096, V = 151936), an
+    # upstream gradient on 8 tokens so that the oracle computes only those
+    wl = workloads.make("fp32_head", device=DEV)
+    h, w, ids = wl.h, wl.w, wl.ids
+    n, v = h.shape[0], w.shape[0]
+    rng = np.random.default_rng(6)
+    tok = np.sort(rng.choice(n, 8, replace=False))
+    gr = torch.zeros(n, dtype=torch.float32, device=DEV)
+    gr[torch.as_tensor(tok, device=DEV)] = torch.as_tensor(rng.normal(0, 1, 8), dtype=torch.float32,
+                                                          device=DEV)
+    say("fp32 full size: forward + backward")
+    _, lse, _ = tim.tim_logprob_forward(h, w, ids, return_lse=True)
+    dh, dw = tim.tim_logprob_backward(h, w, ids, lse, gr)
+    torch.cuda.synchronize()
+    rows_v = np.unique(np.concatenate([ids.cpu().numpy()[tok], rng.choice(v, 8, replace=False),
+                                       [v - 1]]))
+    dh_rows = np.concatenate([tok, np.setdiff1d(np.arange(n), tok)[:3]])
+    say("fp32 full size: oracle rows")
+    dh_ref, dw_ref = oracle.logprob_backward(h.cpu(), w.cpu(), ids.cpu(), gr.cpu(),
+                                             dtype=oracle.F32, dh_rows=dh_rows, dw_rows=rows_v)
+    tt = torch.as_tensor(tok, device=DEV)
+    check_dh32(dh[torch.as_tensor(dh_rows, device=DEV)].double().cpu().numpy(), dh_ref, h, w, ids,
+               gr, dh_rows, "fp32 full size")
+    # dW rows see only the 8 tokens with a gradient
+    check_dw32(dw[torch.as_tensor(rows_v, device=DEV)].double().cpu().numpy(), dw_ref, h[tt], w,
+               ids[tt], gr[tt], np.arange(len(tok)), rows_v, "fp32 full size")
