@@ -1034,9 +1034,9 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 //
 // At a few tokens the 256-token tile of lmhead8w_kernel spends almost all
 // of its MFMA work on padding, while the call is bound by reading W once
-// (V D 2 bytes).  This kernel streams W straight from HBM into registers:
-// no LDS ring and no barrier, and at the Qwen3-8B shape 1187 independent
-// waves keep the whole matrix in flight.  It computes each logit with the
+// (V D 2 bytes).  This kernel streams W through a two-slot LDS ring of its
+// own, one wave per workgroup and no barrier, and at the Qwen3-8B shape
+// 1187 independent waves keep the whole matrix in flight.  It computes each logit with the
 // same instruction as lmhead8w_kernel (v_mfma_f32_16x16x32_bf16, W rows as
 // the first source, tokens as the second, the same K -> lane assignment, k
 // steps in ascending order from a zero accumulator) and folds it with the
@@ -1054,21 +1054,25 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 //
 // Operand path: k-step j of this wave (32 K; 2 per 128-byte stage) needs 8 A
 // fragments (row block r: lane l holds row r*16 + (l & 15), K 8 (l >> 4) ..
-// + 7) and NB B fragments, each one 16-byte buffer load per lane.  They go
-// to a ring of R register sets, R - 1 k-steps ahead of the MFMAs; every
-// k-step issues the same number of loads (past the last k-step the loads
-// repeat the last k-step's addresses, cache hits).  The descriptors are
-// built from the tensors' own pointers; rows past V or N are redirected to
-// the last valid row (their results are masked or dropped), and every
-// access stays inside the descriptor's extent.
+// + 7) and NB B fragments.  Loading the A fragments straight from memory
+// touches 16 rows x 64 bytes per instruction, half of each 128-byte line;
+// measured on this chip a wave-per-128-rows read of the whole matrix in
+// that shape moves 4.0 TB/s, in 8 rows x 128 bytes 5.8 TB/s.  So W goes to
+// LDS by buffer-to-LDS copies of 8 rows x 128 bytes (XOR-swizzled chunks,
+// as in the tile kernels) two stages ahead, and each k-step's A fragments
+// are read back with ds_read_b128; the B fragments (a few tokens, in L2)
+// are 16-byte buffer loads into a ring of three register sets.  Every
+// stage issues the same copies and loads (past the last stage they repeat
+// the last one, into a slot not read again), so the vmcnt waits count
+// them.  The descriptors are built from the tensors' own pointers; W rows
+// past V read as zero through the descriptor's range check, h rows past N
+// are redirected to the last valid row, and results of either are masked
+// or dropped.
 //
 // Work map: unit u = (chunk u >> 1, half u & 1), token group g.  Block b
 // serves unit ((b >> 3) / ntg) * 8 + (b & 7) and group (b >> 3) % ntg: the
 // groups of a unit run on one XCD (b & 7) next to each other, so W is read
 // from HBM once and from that XCD's L2 by the other group.
-template <int NB> struct NarrowCfg;
-template <> struct NarrowCfg<1> { static constexpr int R = 4; };
-template <> struct NarrowCfg<2> { static constexpr int R = 4; };
 constexpr int kNarrowMaxTokens = 32;   // above: two token groups re-read W, and the
                                         // 256-token kernel is faster
 
@@ -1080,8 +1084,6 @@ lmhead_narrow_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
                      int64_t nchunks, int ntg, float c2, float2* __restrict__ hpart,
                      float* __restrict__ hupart, float* __restrict__ zsel,
                      int32_t* __restrict__ n_bad_ids) {
-    constexpr int R = NarrowCfg<NB>::R;
-    constexpr int L = 8 + NB;                 // loads per k-step
     const int lane = threadIdx.x;
     const int col = lane & 15, grp = lane >> 4;
     if (blockIdx.x == 0 && lane == 0 && n_bad_ids) *n_bad_ids = 0;
@@ -1117,75 +1119,136 @@ lmhead_narrow_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
     const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(h + t0 * ldh_b), (short)0,
         (int)((hrows - 1) * ldh_b + (int64_t)nk * kStageBytes), kRsrcWord3);
-    uint32_t aoff[8], boff[NB];
+    // W: stage s (128 bytes of K, two k-steps) of the wave's 128 rows goes
+    // to LDS slot s & 1 by 16 buffer-to-LDS copies of 8 rows x 128 bytes
+    // (copy q: rows 8 q .. 8 q + 7; lane l writes 16 bytes at 16 l, i.e.
+    // row 8 q + (l >> 3), physical chunk l & 7, which holds logical chunk
+    // (l & 7) ^ ((row >> 1) & 7)).  The logical chunk depends on q only
+    // through q & 1, so two per-lane offsets, plus the copy's rows, address
+    // them.  The row offset stays in the per-lane offset, which the
+    // descriptor's range check covers (the scalar offset, the stage's K
+    // offset, is not checked): rows past V then read as zero, with no
+    // access (their logits are masked in the fold).
+    uint32_t avoff[2], boff[NB];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int64_t row = r * 16 + col < wrows ? r * 16 + col : wrows - 1;
-        aoff[r] = (uint32_t)(row * ldw_b) + (uint32_t)(grp * 16);
+    for (int pq = 0; pq < 2; ++pq) {
+        const int lc = (lane & 7) ^ ((4 * pq + (lane >> 4)) & 7);
+        avoff[pq] = (uint32_t)((8 * pq + (lane >> 3)) * ldw_b) + (uint32_t)(lc * 16);
     }
 #pragma unroll
     for (int bj = 0; bj < NB; ++bj) {
         const int64_t row = bj * 16 + col < hrows ? bj * 16 + col : hrows - 1;
         boff[bj] = (uint32_t)(row * ldh_b) + (uint32_t)(grp * 16);
     }
+    // fragment reads: row block rb (immediate 2048 rb), lane row col, logical
+    // chunk 4 h + grp of k-step h: its physical chunk is the same in every
+    // row block (the swizzle takes row bits 1-3, which rb does not change)
+    uint32_t afrag[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        afrag[hh] = (uint32_t)(col * 128) + (uint32_t)((((4 * hh + grp) ^ (col >> 1)) & 7) * 16);
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * 16384];
+    const uint32_t lds_base = lds_addr(lds);
 
-    u32x4 A[R][8], B[R][NB];
+    u32x4 A[2][8], B[3][2][NB];
     f32x4 acc[8][NB];
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
         for (int bj = 0; bj < NB; ++bj) acc[r][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nks = 2 * nk;                   // k-steps of 32 K
-    // loads of k-step j (clamped to the last one) into ring slot `slot`
-    auto issue = [&](auto slot_tag, int j) {
-        constexpr int slot = decltype(slot_tag)::value;
-        const int jj = j < nks ? j : nks - 1;
-        const uint32_t koff = (uint32_t)__builtin_amdgcn_readfirstlane(jj * 64);
+    // every stage issues the same loads (past the last stage they repeat
+    // the last one, into a slot that is not read again): 16 copies, then
+    // 2 NB h loads
+    constexpr int L2 = 16 + 2 * NB;
+    static_assert(L2 <= 63, "vmcnt range");
+    // copies q0 .. q0 + 7 (rows 8 q0 .. 8 q0 + 63) of stage st
+    auto issue_rows = [&](int st, auto q0_tag) {
+        constexpr int q0 = decltype(q0_tag)::value;
+        const int ss = __builtin_amdgcn_readfirstlane(st < nk ? st : nk - 1);
+        unsigned char* slot = lds + (st & 1) * 16384;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            A[slot][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       wrs, aoff[r], koff, 0));
-#pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
-            B[slot][bj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        hrs, boff[bj], koff, 0));
+        for (int q = q0; q < q0 + 8; ++q)
+            dma16_buf(wrs, slot + q * 1024, avoff[q & 1] + (uint32_t)((q >> 1) * 16 * ldw_b),
+                      (uint32_t)(ss * kStageBytes));
     };
-    auto compute = [&](auto slot_tag) {
-        constexpr int slot = decltype(slot_tag)::value;
+    auto issue_h = [&](auto bslot_tag, int st) {
+        constexpr int bs = decltype(bslot_tag)::value;
+        const int ss = __builtin_amdgcn_readfirstlane(st < nk ? st : nk - 1);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int bj = 0; bj < NB; ++bj) mfma16_tied(acc[r][bj], A[slot][r], B[slot][bj]);
+            for (int bj = 0; bj < NB; ++bj)
+                B[bs][hh][bj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    hrs, boff[bj], (uint32_t)(ss * kStageBytes + hh * 64), 0));
     };
-    // k-step j: its loads were issued R - 1 k-steps ago; issue j + R - 1
-    // into the slot k-step j - 1 freed, then wait for k-step j's.
-    auto step = [&](auto slot_tag, int j) {
-        constexpr int slot = decltype(slot_tag)::value;
-        issue(IntConst<(slot + R - 1) % R>{}, j + R - 1);
-        __builtin_amdgcn_sched_barrier(0);      // keep the load order the counts assume
-        wait_vmcnt<(R - 1) * L>();
-        compute(slot_tag);
+    auto issue = [&](auto bslot_tag, int st) {
+        issue_rows(st, IntConst<0>{});
+        issue_rows(st, IntConst<8>{});
+        issue_h(bslot_tag, st);
+    };
+    // stage st: its copies and loads were issued two stages ago.  Wait for
+    // them and read the 16 fragments, rows 0-63 first; as soon as those
+    // reads are done their rows of the slot take stage st + 2's copies, then
+    // the rest.  Then the stage's MFMAs: k-step 0 then 1, row blocks in
+    // order, token blocks in order (the order lmhead8w_kernel's wave applies
+    // to the same fragments).
+    auto stage = [&](auto bslot_tag, int st) {
+        constexpr int bs = decltype(bslot_tag)::value;
+        wait_vmcnt<L2>();
+        const uint32_t base = lds_base + (uint32_t)((st & 1) * 16384);
+        const uint32_t a0 = base + afrag[0], a1 = base + afrag[1];
+        lds_read16<0 * 2048>(A[0][0], a0);
+        lds_read16<0 * 2048>(A[1][0], a1);
+        lds_read16<1 * 2048>(A[0][1], a0);
+        lds_read16<1 * 2048>(A[1][1], a1);
+        lds_read16<2 * 2048>(A[0][2], a0);
+        lds_read16<2 * 2048>(A[1][2], a1);
+        lds_read16<3 * 2048>(A[0][3], a0);
+        lds_read16<3 * 2048>(A[1][3], a1);
+        lds_read16<4 * 2048>(A[0][4], a0);
+        lds_read16<4 * 2048>(A[1][4], a1);
+        lds_read16<5 * 2048>(A[0][5], a0);
+        lds_read16<5 * 2048>(A[1][5], a1);
+        lds_read16<6 * 2048>(A[0][6], a0);
+        lds_read16<6 * 2048>(A[1][6], a1);
+        lds_read16<7 * 2048>(A[0][7], a0);
+        lds_read16<7 * 2048>(A[1][7], a1);
+        // LDS operations of a wave complete in order: 8 outstanding means
+        // the reads of rows 0-63 are done
+        asm volatile("s_waitcnt lgkmcnt(8)"
+                     : "+v"(A[0][0]), "+v"(A[1][0]), "+v"(A[0][1]), "+v"(A[1][1]),
+                       "+v"(A[0][2]), "+v"(A[1][2]), "+v"(A[0][3]), "+v"(A[1][3]));
+        __builtin_amdgcn_sched_barrier(0);
+        issue_rows(st + 2, IntConst<0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(A[0][4]), "+v"(A[1][4]), "+v"(A[0][5]), "+v"(A[1][5]),
+                       "+v"(A[0][6]), "+v"(A[1][6]), "+v"(A[0][7]), "+v"(A[1][7]));
+        __builtin_amdgcn_sched_barrier(0);
+        issue_rows(st + 2, IntConst<8>{});
+        issue_h(IntConst<(bs + 2) % 3>{}, st + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int bj = 0; bj < NB; ++bj) mfma16_tied(acc[r][bj], A[hh][r], B[bs][hh][bj]);
         __builtin_amdgcn_sched_barrier(0);
     };
-#pragma unroll
-    for (int i = 0; i < R - 1; ++i) {
-        if (i == 0) issue(IntConst<0>{}, 0);
-        if (i == 1) issue(IntConst<1 % R>{}, 1);
-        if (i == 2) issue(IntConst<2 % R>{}, 2);
+    issue(IntConst<0>{}, 0);
+    issue(IntConst<1>{}, 1);
+    // whole rounds of three stages (the h ring), then the remainder
+    int st = 0;
+    for (; st + 3 <= nk; st += 3) {
+        stage(IntConst<0>{}, st);
+        stage(IntConst<1>{}, st + 1);
+        stage(IntConst<2>{}, st + 2);
     }
-    // whole rounds of R k-steps (no branch inside), then the remainder
-    int j = 0;
-    for (; j + R <= nks; j += R) {
-        step(IntConst<0>{}, j);
-        step(IntConst<1 % R>{}, j + 1);
-        if constexpr (R > 2) step(IntConst<2 % R>{}, j + 2);
-        if constexpr (R > 3) step(IntConst<3 % R>{}, j + 3);
-    }
-    const int rem = __builtin_amdgcn_readfirstlane(nks - j);
-    if (rem >= 1) step(IntConst<0>{}, j);
-    if constexpr (R > 2) { if (rem >= 2) step(IntConst<1 % R>{}, j + 1); }
-    if constexpr (R > 3) { if (rem >= 3) step(IntConst<2 % R>{}, j + 2); }
+    const int rem = __builtin_amdgcn_readfirstlane(nk - st);
+    if (rem >= 1) stage(IntConst<0>{}, st);
+    if (rem >= 2) stage(IntConst<1>{}, st + 1);
     wait_vmcnt<0>();
     mfma_drain<NB>(acc);
 
@@ -1384,6 +1447,9 @@ lse_merge_token_kernel(const float2* __restrict__ part, const float* __restrict_
     if (threadIdx.x < kMergeWaves) {
         const int w = threadIdx.x;
         float m = -INFINITY, s = 0.f, uu = 0.f;
+        // unrolled so that the LDS reads of several chunks are in flight
+        // ahead of the (sequential) folds
+#pragma unroll 8
         for (int64_t c = w; c < nchunks; c += kMergeWaves) {
             const float2 p = cs[c];
             if constexpr (kEnt) lse_combine3(m, s, uu, p.x, p.y, cu[c], c2);

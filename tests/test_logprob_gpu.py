@@ -289,6 +289,26 @@ def test_qwen3_8b_small_batches_through_both_narrow_widths():
         assert diff == 0, f"batch {b}: {diff} rows differ"
 
 
+@pytest.mark.parametrize("d,v", [(64, 5), (256, 129), (128, 1000), (64, 32001)])
+def test_small_batch_kernel_at_ragged_vocabularies(d, v):
+    """Batches of at most 32 tokens take the small-batch kernel, whose last
+    half-chunk of a vocabulary that is not a multiple of 128 reads its
+    missing rows as zeros: the oracle's values, and the bits the 256-token
+    kernel gives the same rows inside a batch of 300."""
+    g = torch.Generator(device="cpu").manual_seed(d + v)
+    h = torch.randn(300, d, generator=g).to(torch.bfloat16)
+    w = (torch.randn(v, d, generator=g) * 0.05).to(torch.bfloat16)
+    ids = torch.randint(0, v, (300,), generator=g, dtype=torch.int32)
+    hd, wd, idd = h.to("cuda"), w.to("cuda"), ids.to("cuda")
+    big = tim.tim_logprob_forward(hd, wd, idd)
+    for b in (1, 5, 17, 32):
+        say(f"d={d} v={v}: batch of {b}")
+        got = tim.tim_logprob_forward(hd[:b].contiguous(), wd, idd[:b].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), big[:b].view(torch.int32)), b
+        check_rows(hd[:b], wd, idd[:b], got, range(b), f"d={d} v={v} b={b}")
+
+
 @pytest.mark.parametrize("name,sizes", [("dsv3", (1, 7, 64, 1000, 32768)),
                                         ("small", (1, 7, 17, 64, 1000, 2048))])
 def test_batch_invariance_sweep_other_shapes(name, sizes):
