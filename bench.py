@@ -97,6 +97,14 @@ def main():
                          "and kernel-trace CSV) into the matrix-unit summary and exit")
     ap.add_argument("--mfma-out", default=MFMA_SUMMARY)
     ap.add_argument("--traffic-out", default=PMC_SUMMARY)
+    ap.add_argument("--small-batch-only", action="store_true",
+                    help="only the forward at b = 1 .. 64 tokens (for a kernel trace)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_DIR", "OUT_MD"),
+                    help="write a markdown summary of a rocprofv3 --kernel-trace --stats "
+                         "output directory (this library's kernels per call, launch "
+                         "shapes) and exit")
+    ap.add_argument("--title", default="", help="--trace-summary: heading")
+    ap.add_argument("--notes", default="", help="--trace-summary: workload text")
     ap.add_argument("--traffic-command", default="",
                     help="the commands that made the CSV files, recorded in the summary")
     args = ap.parse_args()
@@ -106,6 +114,10 @@ def main():
         return
     if args.mfma_from:
         write_mfma(args.mfma_from[0], args.mfma_from[1], args.mfma_out, args.traffic_command)
+        return
+    if args.trace_summary:
+        write_trace_summary(args.trace_summary[0], args.trace_summary[1], args.title,
+                            args.notes, args.traffic_command)
         return
     if args.profile_pass:
         args.no_extras = True
@@ -141,6 +153,9 @@ def main():
     name = "qwen3_8b"
     log(f"generating workload {name}")
     wl = workloads.make(name, device=dev)
+    if args.small_batch_only:
+        print(json.dumps(small_batch_measure(tim, wl, torch, np)), flush=True)
+        return
     if args.backward_only:
         res = backward_measure(tim, wl, torch, np)
         del wl
@@ -365,10 +380,72 @@ def write_mfma(counter_csv, trace_csv, out_path, command):
     print(json.dumps(summary, indent=1))
 
 
+def write_trace_summary(trace_dir, out_path, title, notes, command):
+    """Markdown from a rocprofv3 --kernel-trace --stats directory: the stats
+    table of this library's kernels (tim::), every call's duration in launch
+    order, and each kernel's launch shape (grid, workgroup, LDS, registers,
+    scratch)."""
+    import csv
+    import glob
+    import re
+
+    def one(pattern):
+        hits = glob.glob(os.path.join(trace_dir, "**", pattern), recursive=True)
+        if not hits:
+            raise SystemExit(f"no {pattern} under {trace_dir}")
+        return hits[0]
+
+    def short(name):
+        name = re.sub(r"\(anonymous namespace\)::", "", name)
+        name = name.replace("void ", "", 1)
+        return name.split("(")[0]
+
+    trace = list(csv.DictReader(open(one("*kernel_trace.csv"), newline="")))
+    lines = [f"# {title}", ""]
+    if notes:
+        lines += [notes, ""]
+    lines += ["Command (repo root):", "", f"    {command}", "",
+              "## Kernel durations (this library's kernels; all calls, warmup included)", "",
+              "| kernel | calls | avg us | min us | max us | total ms |",
+              "|---|---:|---:|---:|---:|---:|"]
+    agg, other = {}, 0.0
+    for r in trace:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "tim::" in r["Kernel_Name"]:
+            agg.setdefault(short(r["Kernel_Name"]), []).append(dur)
+        else:
+            other += dur * 1e3
+    for k, us in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(us)} | {sum(us) / len(us):.1f} | {min(us):.1f} | "
+                     f"{max(us):.1f} | {sum(us) / 1e3:.3f} |")
+    lines += ["", f"Other kernels (torch: input generation, reference ops): {other / 1e6:.3f} ms in total.",
+              "", "## Per call (us, launch order) and launch shape", ""]
+    per = {}
+    for r in trace:
+        if "tim::" not in r["Kernel_Name"]:
+            continue
+        k = short(r["Kernel_Name"])
+        d = per.setdefault(k, {"us": [], "row": r})
+        d["us"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for k, d in per.items():
+        us = d["us"]
+        r = d["row"]
+        med = sorted(us)[len(us) // 2]
+        shown = ", ".join(f"{x:.0f}" if x >= 100 else f"{x:.1f}" for x in us[:40])
+        more = f" ... ({len(us)} calls)" if len(us) > 40 else ""
+        lines += [f"- `{k}`: median {med:.1f} us; {shown}{more}",
+                  f"  grid {r['Grid_Size_X']} work-items, workgroup {r['Workgroup_Size_X']}, "
+                  f"LDS {r['LDS_Block_Size']} B, VGPR {r['VGPR_Count']}, AGPR {r['Accum_VGPR_Count']}, "
+                  f"SGPR {r['SGPR_Count']}, scratch {r['Scratch_Size']} B"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 COPY_BYTES = 1 << 30          # bytes read and bytes written by the calibration kernel
 COPY_KERNEL = "bitwise_not_kernel"   # one coalesced 4-byte read and write per element
 LMHEAD_KERNEL = "lmhead8w_kernel<false, false>"
-LMHEAD_F32_KERNEL = "lmhead_partials_kernel<false>"
+LMHEAD_F32_KERNEL = "lmhead_partials_kernel<false, 0>"
 STATS_KERNEL = "stats_stream_kernel"
 EXTRAS_KERNEL = "xsel_pass_kernel"
 
