@@ -32,14 +32,29 @@
 // each pass is three launches:
 //
 //   xsel_pass    every block histograms its share in LDS and writes it with
-//                plain stores, with its key range per slot.  Pass 1 also
-//                copies the keys that lie in any slot into a region of the
-//                workspace owned by the block (capped; an overflow is
-//                flagged), and passes 2-5 read those regions instead of the
-//                9 bytes per token of the inputs.
+//                plain stores, with its key range per slot.  Pass 0 also
+//                copies the keys whose first digit lies in a predicted
+//                window of some target into a region of the workspace owned
+//                by the block (capped; an overflow is flagged), and passes
+//                1-5 read those regions instead of the 9 bytes per token of
+//                the inputs, so the inputs are read once.  The windows come
+//                from a sample (below); whether they hold every target is
+//                checked exactly after pass 0's select step, from the full
+//                first-digit histogram.  If one does not (or a region
+//                overflowed), pass 1 reads the inputs again and copies the
+//                keys that lie in any slot, as it would without a sample,
+//                and passes 2-5 read those.
 //   xsel_reduce  sums the block histograms bin by bin (integers: the order
 //                does not matter).
 //   xsel_select  one block runs the select step.
+//
+// The sample (xsel_sample, xsel_predict): 16 consecutive tokens out of
+// every 1024 (about 1.6 % of the tokens, each group most often a sequence of
+// its own), their delta keys' first digits histogrammed; each target's
+// window is the first-digit bins holding the sample ranks within
+// 8 sqrt(m q (1 - q)) + 64 of q (m - 1), m the sample's valid tokens.  The
+// sample only decides how much is copied: which keys are selected, and so
+// every result, does not depend on it.
 //
 // Once every target is resolved the remaining launches return at once.
 //
@@ -537,18 +552,134 @@ xsel_fused_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
 // Above kXFusedMax tokens: pass / reduce / select launches.
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(64)
-xsel_init_kernel(XParamsDev prm, XState* __restrict__ st, uint32_t* __restrict__ cflag) {
+// cflag[0]: pass 0's regions overflowed; cflag[1]: pass 0's regions are
+// not usable (overflow, or a target outside the predicted windows);
+// cflag[2]: pass 1's regions overflowed (pass 1 copies only when cflag[1]);
+// cflag[3]: valid tokens in the sample.
+constexpr int kXSampleGroup = 16;        // consecutive tokens per sample group
+constexpr int kXSampleEvery = 1024;      // one group per this many tokens
+constexpr int kXSampleBlocks = 128;
+// Below this many tokens the second read of the inputs costs less than the
+// sample's two launches: no sample, no window, pass 1 reads the tokens.
+constexpr uint32_t kXSampleMinN = 1u << 25;
+
+__global__ void __launch_bounds__(256)
+xsel_init_kernel(XParamsDev prm, XState* __restrict__ st, uint32_t* __restrict__ cflag,
+                 uint32_t* __restrict__ shist, uint32_t* __restrict__ pmark) {
+    for (int i = threadIdx.x; i < (1 << 14); i += 256) shist[i] = 0;
+    for (int i = threadIdx.x; i < (1 << 14) / 32; i += 256) pmark[i] = 0;
+    if (threadIdx.x < 4) cflag[threadIdx.x] = 0;
     if (threadIdx.x != 0) return;
     init_state(st, prm);
-    *cflag = 0;
 }
 
-// One histogram pass; kMode 0: pass 0, 1: pass 1, 2: passes 2-5.  Passes
-// 0 and 1 (and later passes when a candidate region overflowed) read the
-// tokens: block b takes tokens b*1024 + tid + j*stride, stride = grid *
-// 1024.  Pass 1 copies the keys that any slot takes into the block's region
-// cand[b*cap ...]; passes 2-5 read the region.
+// First digits of the sample's delta keys into shist (integer atomics: the
+// counts do not depend on their order), and the sample's valid count.
+template <bool kMask>
+__global__ void __launch_bounds__(kXThreads)
+xsel_sample_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
+                   const uint8_t* __restrict__ mask, uint32_t n, uint32_t* __restrict__ shist,
+                   uint32_t* __restrict__ cflag) {
+    __shared__ uint32_t hist[1 << 14];
+    __shared__ uint32_t cnt;
+    for (int i = threadIdx.x; i < (1 << 14); i += kXThreads) hist[i] = 0;
+    if (threadIdx.x == 0) cnt = 0;
+    __syncthreads();
+    const uint32_t groups = (n + kXSampleEvery - 1) / kXSampleEvery;
+    const uint32_t total = groups * kXSampleGroup;
+    uint32_t nv = 0;
+    for (uint32_t i = blockIdx.x * kXThreads + threadIdx.x; i < total;
+         i += gridDim.x * kXThreads) {
+        const uint32_t t = (i / kXSampleGroup) * kXSampleEvery + (i % kXSampleGroup);
+        if (t >= n) continue;
+        const double d = (double)lt[t] - (double)lr[t];
+        if ((kMask ? mask[t] != 0 : true) && isfinite(d)) {
+            atomicAdd(&hist[(uint32_t)(key_delta(d) >> 50)], 1u);
+            ++nv;
+        }
+    }
+    atomicAdd(&cnt, nv);
+    __syncthreads();
+    for (int i = threadIdx.x; i < (1 << 14); i += kXThreads)
+        if (hist[i]) atomicAdd(&shist[i], hist[i]);
+    if (threadIdx.x == 0) atomicAdd(&cflag[3], cnt);
+}
+
+// The predicted windows as a bitmap over delta's first digits (pmark): for
+// each probability, the bins (in the kind's key order) that hold the sample
+// ranks within the margin of q (m - 1); a |delta| bin marks the two delta
+// bins it counts.  One block.
+__global__ void __launch_bounds__(kXThreads)
+xsel_predict_kernel(XParamsDev prm, const uint32_t* __restrict__ shist,
+                    const uint32_t* __restrict__ cflag, uint32_t* __restrict__ pmark) {
+    constexpr int kPer = (1 << 14) / kXThreads;      // 16 bins per thread
+    __shared__ uint32_t h[1 << 14];
+    __shared__ uint32_t mk[(1 << 14) / 32];
+    __shared__ uint64_t sh[kXThreads / 64];
+    __shared__ uint32_t c0[1 << 14];                 // cumulative counts before each bin
+    const int tid = threadIdx.x;
+    for (int i = tid; i < (1 << 14); i += kXThreads) h[i] = shist[i];
+    for (int i = tid; i < (1 << 14) / 32; i += kXThreads) mk[i] = 0;
+    __syncthreads();
+    const double m = (double)cflag[3];
+    for (int kind = 0; kind < 2; ++kind) {
+        const int nq = kind == 0 ? prm.nrq : prm.naq;
+        if (nq == 0 || m == 0.0) continue;
+        const int nb = kind == 0 ? 1 << 14 : 1 << 13;
+        // bin b of this kind, in key order: delta's own, or |delta|'s root
+        // bin counting two delta bins
+        uint64_t local = 0;
+        uint32_t v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int b = tid * kPer + j;
+            v[j] = b < nb ? (kind == 0 ? h[b] : abs_root_bin(h, b)) : 0u;
+            local += v[j];
+        }
+        uint64_t run = block_excl_scan<kXThreads>(local, sh);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            c0[tid * kPer + j] = (uint32_t)run;
+            run += v[j];
+        }
+        __syncthreads();
+        for (int i = 0; i < nq; ++i) {
+            const double q = kind == 0 ? prm.rq[i] : prm.aq[i];
+            const double r = q * (m - 1.0);
+            const double delta = 8.0 * sqrt(m * q * (1.0 - q)) + 64.0;
+            const double lo = r - delta, hi = r + delta;
+            // bin b holds sample ranks [c0[b], c0[b] + count); mark it if
+            // that range meets [lo, hi]
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int b = tid * kPer + j;
+                if (b >= nb) continue;
+                const double a = (double)c0[b], e = a + (double)v[j];
+                // empty bins between the window's first and last are marked
+                // too: c0 does not move across them
+                if (e >= lo && a <= hi) {
+                    if (kind == 0) {
+                        atomicOr(&mk[b >> 5], 1u << (b & 31));
+                    } else {
+                        const int d0 = 0x2000 | b, d1 = 0x1FFF ^ b;
+                        atomicOr(&mk[d0 >> 5], 1u << (d0 & 31));
+                        atomicOr(&mk[d1 >> 5], 1u << (d1 & 31));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < (1 << 14) / 32; i += kXThreads) pmark[i] = mk[i];
+}
+
+// One histogram pass; kMode 0: pass 0, 1: pass 1, 2: passes 2-5.  Reading
+// the tokens, block b takes tokens b*1024 + tid + j*stride, stride = grid *
+// 1024.  Pass 0 copies the keys whose first digit is marked in pmark into
+// the block's region cand[b*cap ...]; passes 1-5 read the region when
+// pass 0's copy is usable (cflag[1] == 0).  Otherwise pass 1 reads the
+// tokens and copies the keys that any slot takes, and passes 2-5 read that
+// copy unless it overflowed too.
 template <bool kMask, int kMode>
 __global__ void __launch_bounds__(kXThreads)
 xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
@@ -556,14 +687,18 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                  const XState* __restrict__ st, uint32_t* __restrict__ bhist,
                  ulonglong2* __restrict__ bmm, XPart* __restrict__ part,
                  uint64_t* __restrict__ cand, uint32_t* __restrict__ ccnt, uint32_t cap,
-                 uint32_t* __restrict__ cflag) {
+                 uint32_t* __restrict__ cflag, const uint32_t* __restrict__ pmark) {
     __shared__ uint32_t hist[kXLdsBins];
     __shared__ unsigned long long smn[kXMaxSlots], smx[kXMaxSlots];
     __shared__ double rsh[kXThreads];
     __shared__ uint32_t lcount;
-    __shared__ uint32_t mark[(1 << 14) / 32];   // pass 1: root digits some slot covers
+    __shared__ uint32_t mark[(1 << 14) / 32];   // root digits whose keys are copied
     constexpr bool first = kMode == 0;
     if (!first && st->all_done) return;
+    // pass 1 reads pass 0's copy when it is usable; passes 2-5 read the
+    // regions unless the last copy made overflowed
+    const bool from_cand = kMode == 1 ? cflag[1] == 0
+                         : kMode == 2 ? (cflag[1] == 0 || cflag[2] == 0) : false;
     Slots sl;
     load_slots(sl, st);
     const int bits = digit_bits(pass), before = bits_before(pass);
@@ -573,8 +708,10 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     for (int i = tid; i < nbins; i += kXThreads) hist[i] = 0;
     if (tid < kXMaxSlots) { smn[tid] = ~0ull; smx[tid] = 0ull; }
     if (tid == 0) lcount = 0;
-    constexpr bool collect = kMode == 1;
-    if (collect) {
+    const bool collect = kMode == 0 || (kMode == 1 && !from_cand);
+    if (kMode == 0) {
+        for (int i = tid; i < (1 << 14) / 32; i += kXThreads) mark[i] = pmark[i];
+    } else if (collect) {
         for (int i = tid; i < (1 << 14) / 32; i += kXThreads) mark[i] = 0;
         __syncthreads();
         if (tid < sl.n) {
@@ -588,7 +725,6 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
             }
         }
     }
-    const bool from_cand = kMode == 2 && *cflag == 0;
     __syncthreads();
 
     uint64_t lmn[kXMaxSlots], lmx[kXMaxSlots];
@@ -632,6 +768,8 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                     k0 = key_delta(d);
                     if (first) {
                         visit_root(k0, hist, lmn[0], lmx[0]);
+                        const uint32_t r = (uint32_t)(k0 >> 50);
+                        take = (mark[r >> 5] >> (r & 31)) & 1u;
                     } else if (collect) {
                         const uint32_t r = (uint32_t)(k0 >> 50);
                         if ((mark[r >> 5] >> (r & 31)) & 1u)
@@ -655,7 +793,7 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                             base_pos + (uint32_t)__popcll(ball & ((1ull << (tid & 63)) - 1));
                         if (take) {
                             if (pos < cap) reg[pos] = k0;
-                            else *cflag = 1;               // every writer stores the same value
+                            else cflag[first ? 0 : 2] = 1;    // every writer stores the same value
                         }
                     }
                 }
@@ -713,7 +851,8 @@ xsel_reduce_kernel(const uint32_t* __restrict__ bhist, int nblk, int pass,
 __global__ void __launch_bounds__(kXThreads)
 xsel_select_kernel(int pass, int nblk, XParamsDev prm, XState* __restrict__ gst,
                    const uint32_t* __restrict__ ghist, const ulonglong2* __restrict__ bmm,
-                   const XPart* __restrict__ part) {
+                   const XPart* __restrict__ part, uint32_t* __restrict__ cflag,
+                   const uint32_t* __restrict__ pmark) {
     __shared__ XState st;                    // working copy; thread 0 writes it back
     __shared__ uint64_t sh[kXThreads];
     __shared__ unsigned long long mn[kXMaxSlots], mx[kXMaxSlots];
@@ -758,7 +897,22 @@ xsel_select_kernel(int pass, int nblk, XParamsDev prm, XState* __restrict__ gst,
     }
     __syncthreads();
     select_step(st, pass, ghist, mn, mx, sh, fdig, frank);
-    if (tid == 0) *gst = st;
+    if (tid == 0) {
+        if (pass == 0) {
+            // pass 0's copy serves the later passes iff it did not overflow
+            // and every unresolved target's first digit was copied
+            bool usable = cflag[0] == 0;
+            for (int t = 0; t < st.ntgt; ++t) {
+                if (st.tgt[t].resolved) continue;
+                const uint32_t d = (uint32_t)st.tgt[t].prefix;
+                auto marked = [&](uint32_t b) { return (pmark[b >> 5] >> (b & 31)) & 1u; };
+                usable = usable && (st.tgt[t].kind == 0 ? marked(d) != 0
+                                                        : (marked(0x2000 | d) && marked(0x1FFF ^ d)));
+            }
+            cflag[1] = usable ? 0u : 1u;
+        }
+        *gst = st;
+    }
 }
 
 __global__ void __launch_bounds__(kXFinThreads)
@@ -800,7 +954,7 @@ bool make_extras_plan(int64_t n, ExtrasPlan* p) {
     };
     if (p->fused) {
         p->state_off = p->bhist_off = p->bmm_off = p->ghist_off = p->part_off = 0;
-        p->cand_off = p->ccnt_off = p->cflag_off = 0;
+        p->cand_off = p->ccnt_off = p->cflag_off = p->shist_off = p->pmark_off = 0;
         p->total_bytes = 256;                      // unused: the fused kernel keeps all in LDS
         return true;
     }
@@ -811,7 +965,9 @@ bool make_extras_plan(int64_t n, ExtrasPlan* p) {
     p->part_off = take((size_t)g * sizeof(XPart));
     p->cand_off = take((size_t)g * p->cap * sizeof(uint64_t));
     p->ccnt_off = take((size_t)g * sizeof(uint32_t));
-    p->cflag_off = take(sizeof(uint32_t));
+    p->cflag_off = take(4 * sizeof(uint32_t));
+    p->shist_off = take((size_t)(1 << 14) * sizeof(uint32_t));
+    p->pmark_off = take((size_t)(1 << 14) / 32 * sizeof(uint32_t));
     p->total_bytes = off;
     return true;
 }
@@ -838,16 +994,30 @@ hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const fl
     uint64_t* cand = (uint64_t*)(ws + p.cand_off);
     uint32_t* ccnt = (uint32_t*)(ws + p.ccnt_off);
     uint32_t* cflag = (uint32_t*)(ws + p.cflag_off);
+    uint32_t* shist = (uint32_t*)(ws + p.shist_off);
+    uint32_t* pmark = (uint32_t*)(ws + p.pmark_off);
     const int nblk = (int)p.nblk;
     const uint32_t n = (uint32_t)p.n;
-    hipLaunchKernelGGL(xsel_init_kernel, dim3(1), dim3(64), 0, st, prm, state, cflag);
+    hipLaunchKernelGGL(xsel_init_kernel, dim3(1), dim3(256), 0, st, prm, state, cflag, shist,
+                       pmark);
+    if (n >= kXSampleMinN) {
+        if (mask)
+            hipLaunchKernelGGL((xsel_sample_kernel<true>), dim3(kXSampleBlocks), dim3(kXThreads), 0,
+                               st, lt, lr, mask, n, shist, cflag);
+        else
+            hipLaunchKernelGGL((xsel_sample_kernel<false>), dim3(kXSampleBlocks), dim3(kXThreads),
+                               0, st, lt, lr, mask, n, shist, cflag);
+        hipLaunchKernelGGL(xsel_predict_kernel, dim3(1), dim3(kXThreads), 0, st, prm,
+                           (const uint32_t*)shist, (const uint32_t*)cflag, pmark);
+    }
     static_assert(bits_before(1) + digit_bits(1) <= 32, "pass 1 tests upper halves");
     for (int pass = 0; pass < kXPasses; ++pass) {
         auto kern = pass == 0 ? (mask ? xsel_pass_kernel<true, 0> : xsel_pass_kernel<false, 0>)
                   : pass == 1 ? (mask ? xsel_pass_kernel<true, 1> : xsel_pass_kernel<false, 1>)
                               : (mask ? xsel_pass_kernel<true, 2> : xsel_pass_kernel<false, 2>);
         hipLaunchKernelGGL(kern, dim3(nblk), dim3(kXThreads), 0, st, lt, lr, mask, n, pass, prm,
-                           (const XState*)state, bhist, bmm, part, cand, ccnt, p.cap, cflag);
+                           (const XState*)state, bhist, bmm, part, cand, ccnt, p.cap, cflag,
+                           (const uint32_t*)pmark);
         const int nbins_max = pass == 0 ? 1 << digit_bits(0) : kXMaxSlots << digit_bits(pass);
         hipLaunchKernelGGL(xsel_reduce_kernel,
                            dim3((nbins_max + kXReduceBins - 1) / kXReduceBins),
@@ -855,7 +1025,7 @@ hipError_t launch_mismatch_extras(const ExtrasPlan& p, const float* lt, const fl
                            (const XState*)state, ghist);
         hipLaunchKernelGGL(xsel_select_kernel, dim3(1), dim3(kXThreads), 0, st, pass, nblk, prm,
                            state, (const uint32_t*)ghist, (const ulonglong2*)bmm,
-                           (const XPart*)part);
+                           (const XPart*)part, cflag, (const uint32_t*)pmark);
     }
     if (out)
         hipLaunchKernelGGL(xsel_final_kernel, dim3(1), dim3(kXFinThreads), 0, st, nblk, prm,

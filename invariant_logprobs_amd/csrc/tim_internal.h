@@ -166,7 +166,7 @@ struct ExtrasPlan {
     bool fused;        // n <= kXFusedMax: one block, no workspace use
     uint32_t cap;      // keys per block in the candidate regions
     size_t state_off, bhist_off, bmm_off, ghist_off, part_off, cand_off, ccnt_off, cflag_off,
-        total_bytes;
+        shist_off, pmark_off, total_bytes;
 };
 
 bool make_extras_plan(int64_t n, ExtrasPlan* p);

@@ -62,7 +62,7 @@ def test_workload_extras_parity(name):
     check(w.logp_sampler, w.logp_rollout, w.mask, w.spec.tok_tau, label=name)
 
 
-@pytest.mark.parametrize("n", [1, 7, 1000, 8192, 8193, 16384 + 37, 200_003, 1 << 22])
+@pytest.mark.parametrize("n", [1, 7, 1000, 8192, 8193, 16384 + 37, 200_003, 1 << 22, (1 << 25) + 7])
 def test_stress_extras_parity(n):
     # lognormal lengths, per-sequence drift, spikes of +1, NaN entries and a
     # masked prompt; sizes across one block, many blocks and a ragged tail
@@ -127,6 +127,24 @@ def test_candidate_overflow_falls_back_to_the_inputs():
     m = (torch.rand(n, generator=g) < 0.1).to(torch.uint8)
     check(lt.to(DEV), lr.to(DEV), m.to(DEV), 1.2, rq=(0.01, 0.5, 0.99), aq=(0.95,),
           label="masked to a tenth")
+
+
+def test_sample_that_misleads_the_windows_falls_back_to_the_inputs():
+    # the tokens the sample reads (the first 16 of every 1024) carry one
+    # delta, the others a spread: every predicted window sits on the sampled
+    # value's bin, misses the true order statistics, and pass 1 reads the
+    # tokens again; the results are the oracle's all the same
+    n = (1 << 25) + 12345                # the sample runs from 2^25 tokens
+    g = torch.Generator(device="cpu").manual_seed(12)
+    lr = -torch.rand(n, generator=g) * 3
+    dl = torch.randn(n, generator=g, dtype=torch.float64) * 0.01
+    sampled = (torch.arange(n) % 1024) < 16
+    dl[sampled] = 0.3
+    lt = (lr.double() + dl).float()
+    m = (torch.rand(n, generator=g) < 0.9).to(torch.uint8)
+    check(lt.to(DEV), lr.to(DEV), m.to(DEV), 0.1, label="misleading sample")
+    check(lt.to(DEV), lr.to(DEV), None, 0.1, rq=(0.2, 0.7), aq=(0.5, 0.99),
+          label="misleading sample, unmasked")
 
 
 def test_extras_run_to_run_determinism():
