@@ -756,7 +756,10 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
 #pragma unroll
             for (int j = 0; j < kXUnroll; ++j) {
                 const double d = (double)x[j] - (double)y[j];
-                const bool valid = m[j] && isfinite(d);
+                // not short-circuit: d, and so its loads, stay ahead of the
+                // branch (else the compiler issues a load behind the mask's
+                // wait and then waits for it)
+                const bool valid = (m[j] != 0) & isfinite(d);
                 bool take = false;
                 uint64_t k0 = 0;
                 if (valid) {
@@ -779,22 +782,14 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                     }
                 }
                 if (collect) {
-                    // wave-aggregated append to this block's region; near the
-                    // end of the loop some lanes have left it, so the first
-                    // active lane leads
-                    const uint64_t ball = __ballot(take);
-                    if (ball) {
-                        const int leader = __ffsll((unsigned long long)__ballot(1)) - 1;
-                        uint32_t base_pos = 0;
-                        if ((tid & 63) == leader)
-                            base_pos = atomicAdd(&lcount, (uint32_t)__popcll(ball));
-                        base_pos = __shfl(base_pos, leader);
-                        const uint32_t pos =
-                            base_pos + (uint32_t)__popcll(ball & ((1ull << (tid & 63)) - 1));
-                        if (take) {
-                            if (pos < cap) reg[pos] = k0;
-                            else cflag[first ? 0 : 2] = 1;    // every writer stores the same value
-                        }
+                    // append to this block's region: the compiler's atomic
+                    // optimizer turns the takers' increments into one LDS
+                    // atomic per wave and gives each taker the old count
+                    // plus the number of takers in lower lanes
+                    if (take) {
+                        const uint32_t pos = atomicAdd(&lcount, 1u);
+                        if (pos < cap) reg[pos] = k0;
+                        else cflag[first ? 0 : 2] = 1;    // every writer stores the same value
                     }
                 }
             }
