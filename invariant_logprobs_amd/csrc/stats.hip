@@ -346,10 +346,23 @@ __device__ __forceinline__ double fma_s(double a, double b, double c) {
 // is accumulated as d^2 and halved once (a power-of-two scale: exact).  For
 // the truncated weight only the clipped tokens' e^d - 1 is summed (rare
 // path); the unclipped sum is recovered as (sum d + sum k3) - that.
+// The series' coefficients 1/120, 1/24, 1/6 in vector registers for the
+// whole kernel: formed once and made opaque, so that the compiler keeps them
+// rather than moving each into registers again before every use (v_fma_f64
+// reads at most one scalar operand).
+struct SeriesC {
+    double c5, c4, c3;
+};
+__device__ __forceinline__ SeriesC series_c() {
+    SeriesC c{1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0};
+    asm volatile("" : "+v"(c.c5), "+v"(c.c4), "+v"(c.c3));
+    return c;
+}
+
 template <int kI0, bool kTok, bool kMask, bool kFull, bool kClipRare>
 __device__ __forceinline__ void fold_pair(Acc& A, const Regs& rg, uint32_t tok0, uint32_t lim,
                                           int lane, const StatsParamsDev& prm,
-                                          const TokOut& tok) {
+                                          const TokOut& tok, const SeriesC& sc3) {
     // kClipRare: log C >= 1/32, so a clipped token (d > log C) is among the
     // |d| > 1/32 tokens of the rare branch and needs no test of its own
     static_assert(!(kTok && kClipRare), "per-token outputs test the clip on every row");
@@ -376,8 +389,8 @@ __device__ __forceinline__ void fold_pair(Acc& A, const Regs& rg, uint32_t tok0,
         d[i] = __builtin_amdgcn_inverse_ballot_w64(m_fin[i]) ? draw[i] : 0.0;
         // e^d - 1 - d = d dp for |d| <= 1/32, dp = d (1/2 + d/6 + d^2/24 +
         // d^3/120), truncation below 4e-9 relative
-        double p = fma_s(d[i], 1.0 / 120.0, 1.0 / 24.0);
-        p = fma_s(p, d[i], 1.0 / 6.0);
+        double p = fma_s(d[i], sc3.c5, sc3.c4);
+        p = fma_s(p, d[i], sc3.c3);
         p = fma_s(p, d[i], 0.5);
         dp[i] = d[i] * p;
         rare |= __builtin_amdgcn_ballot_w64(!(fabs(d[i]) <= 0.03125));
@@ -801,6 +814,7 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     A.zero();
     A.sabs = 0.0;
     A.mx = 0.0;
+    const SeriesC sc3 = series_c();
     uint32_t nstage = 0;                           // staged entries (uniform)
     SeqSums S = seq_zero();                        // the sequence being finished
     // Buffer descriptors based at the wave's first token: every copy's
@@ -865,7 +879,8 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 else
                     read_slot<2, kMask, kMaskDw>(g, slot, lane, tail, cur.start - mbase, mlast);
                 issue(slot, r);
-#define TIM_FOLD2(I0, F, C) fold_pair<I0, kTok, kMask, F, C>(A, g, cur.start, lim, lane, prm, tok)
+#define TIM_FOLD2(I0, F, C) \
+    fold_pair<I0, kTok, kMask, F, C>(A, g, cur.start, lim, lane, prm, tok, sc3)
                 if (lim == (uint32_t)kPiece) {
                     if (!kTok && clip_rare) { TIM_FOLD2(0, true, !kTok); TIM_FOLD2(2, true, !kTok); }
                     else { TIM_FOLD2(0, true, false); TIM_FOLD2(2, true, false); }
