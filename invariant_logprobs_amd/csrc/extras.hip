@@ -125,6 +125,33 @@ __device__ __forceinline__ uint64_t key_delta(double d) {
     const uint64_t u = __builtin_bit_cast(uint64_t, d);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
+// a / b for finite a >= 0 and b in [1e-8, 2^128]: the hardware reciprocal
+// refined by two Newton steps, then one correction of the quotient
+// (Markstein's sequence).  It is the compiler's IEEE division without the
+// operand scaling and special-value fixup steps, which change nothing for
+// such operands (no quotient or reciprocal can overflow, underflow or be
+// special), so the result is the correctly rounded quotient.
+__device__ __forceinline__ double div_in_range(double a, double b) {
+    double y = __builtin_amdgcn_rcp(b);
+    double e = fma(-b, y, 1.0);
+    y = fma(y, e, y);
+    e = fma(-b, y, 1.0);
+    y = fma(y, e, y);
+    const double q = a * y;
+    return fma(fma(-b, q, a), y, q);
+}
+// min and max of finite doubles as single instructions (no NaN can reach
+// them, so no canonicalisation)
+__device__ __forceinline__ double min_fin(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ double max_fin(double a, double b) {
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 // |delta|'s key from delta's key: the bit pattern of |delta|
 __device__ __forceinline__ uint64_t key_abs_of(uint64_t k0) {
     return ((k0 >> 63) ? k0 : ~k0) & 0x7FFFFFFFFFFFFFFFull;
@@ -731,6 +758,7 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
 #pragma unroll
     for (int s = 0; s < kXMaxSlots; ++s) { lmn[s] = ~0ull; lmx[s] = 0; }
     double rel = 0.0;
+    double dmin = INFINITY, dmax = -INFINITY;     // pass 0: the range of delta
     uint32_t next = 0, nval = 0;
     if (from_cand) {
         const uint32_t cnt = ccnt[blockIdx.x];
@@ -764,13 +792,17 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 uint64_t k0 = 0;
                 if (valid) {
                     if (first) {
-                        rel += fabs(d) / (fabs((double)x[j]) + 1e-8);
+                        rel += div_in_range(fabs(d), fabs((double)x[j]) + 1e-8);
                         next += fabs(d) > prm.tok_tau ? 1u : 0u;
                         ++nval;
                     }
                     k0 = key_delta(d);
                     if (first) {
-                        visit_root(k0, hist, lmn[0], lmx[0]);
+                        // the range as values (two instructions rather than
+                        // six on 64-bit keys), made keys once at the end
+                        atomicAdd(&hist[(uint32_t)(k0 >> 50)], 1u);
+                        dmin = min_fin(dmin, d);
+                        dmax = max_fin(dmax, d);
                         const uint32_t r = (uint32_t)(k0 >> 50);
                         take = (mark[r >> 5] >> (r & 31)) & 1u;
                     } else if (collect) {
@@ -794,6 +826,15 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 }
             }
         }
+    }
+    if (first && nval > 0) {
+        // the key order is the value order, except that -0 and +0 (equal as
+        // values) have two keys: a range whose ends are zeros of either sign
+        // may then end on the same key though both occur, which resolves the
+        // targets to a zero of one sign, and every output is the same for
+        // either (ratio 1, |delta| 0)
+        lmn[0] = key_delta(dmin);
+        lmx[0] = key_delta(dmax);
     }
     flush_range(nranges, lmn, lmx, smn, smx);
     if (first) {
