@@ -763,8 +763,17 @@ xsel_pass_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     if (from_cand) {
         const uint32_t cnt = ccnt[blockIdx.x];
         const uint64_t* reg = cand + (size_t)blockIdx.x * cap;
-        for (uint32_t i = tid; i < cnt; i += kXThreads)
-            visit<false>(reg[i], sl, before, bits, hist, lmn, lmx);
+        // kXUnroll keys per thread per trip, loaded before any is visited
+        // (counts and ranges do not depend on the order of the visits)
+        uint32_t i = tid;
+        for (; i + (kXUnroll - 1) * kXThreads < cnt; i += kXUnroll * kXThreads) {
+            uint64_t k[kXUnroll];
+#pragma unroll
+            for (int j = 0; j < kXUnroll; ++j) k[j] = reg[i + j * kXThreads];
+#pragma unroll
+            for (int j = 0; j < kXUnroll; ++j) visit<false>(k[j], sl, before, bits, hist, lmn, lmx);
+        }
+        for (; i < cnt; i += kXThreads) visit<false>(reg[i], sl, before, bits, hist, lmn, lmx);
     } else {
         const uint32_t stride = gridDim.x * kXThreads;
         uint64_t* reg = cand + (size_t)blockIdx.x * cap;
