@@ -350,12 +350,14 @@ __device__ __forceinline__ double fma_s(double a, double b, double c) {
 // whole kernel: formed once and made opaque, so that the compiler keeps them
 // rather than moving each into registers again before every use (v_fma_f64
 // reads at most one scalar operand).
+// log C, the clip threshold, rides along the same way: a vector operand of
+// its compares instead of two scalar registers the kernel runs short of.
 struct SeriesC {
-    double c5, c4, c3;
+    double c5, c4, c3, log_c;
 };
-__device__ __forceinline__ SeriesC series_c() {
-    SeriesC c{1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0};
-    asm volatile("" : "+v"(c.c5), "+v"(c.c4), "+v"(c.c3));
+__device__ __forceinline__ SeriesC series_c(double log_c) {
+    SeriesC c{1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0, log_c};
+    asm volatile("" : "+v"(c.c5), "+v"(c.c4), "+v"(c.c3), "+v"(c.log_c));
     return c;
 }
 
@@ -383,7 +385,7 @@ __device__ __forceinline__ void fold_pair(Acc& A, const Regs& rg, uint32_t tok0,
         rare |= sc & ~m_fin[i];                        // non-finite: counted in the branch
         if constexpr (kTok) m_sc[i] = sc;
         if constexpr (!kClipRare) {
-            m_clip[i] = m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > prm.log_c);
+            m_clip[i] = m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > sc3.log_c);
             rare |= m_clip[i];
         }
         d[i] = __builtin_amdgcn_inverse_ballot_w64(m_fin[i]) ? draw[i] : 0.0;
@@ -407,7 +409,7 @@ __device__ __forceinline__ void fold_pair(Acc& A, const Regs& rg, uint32_t tok0,
                                                         (uint32_t)(64 * (kI0 + i) + lane) < lim));
             A.nnan += (uint32_t)__popcll(sc & ~m_fin[i]);
             const uint64_t clip = kClipRare
-                                      ? m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > prm.log_c)
+                                      ? m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > sc3.log_c)
                                       : m_clip[i];
             A.nclip += (uint32_t)__popcll(clip);
             const bool big = !(fabs(d[i]) <= 0.03125);
@@ -814,7 +816,7 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     A.zero();
     A.sabs = 0.0;
     A.mx = 0.0;
-    const SeriesC sc3 = series_c();
+    const SeriesC sc3 = series_c(prm.log_c);
     uint32_t nstage = 0;                           // staged entries (uniform)
     SeqSums S = seq_zero();                        // the sequence being finished
     // Buffer descriptors based at the wave's first token: every copy's
