@@ -115,6 +115,31 @@ def test_keys_differing_only_in_the_last_bits():
     assert got["n_extreme"] == int((d > 1.0).sum())
 
 
+def test_signed_zero_deltas_and_magnitudes_across_the_fp32_range():
+    # several pass blocks (N > 8192).  First every delta is a zero, -0 on a
+    # third of the tokens ((-0) - (+0)), +0 elsewhere: two keys for one
+    # value, resolved to a zero either way, ratio 1 and |delta| 0.
+    n = 300_000
+    g = torch.Generator(device="cpu").manual_seed(11)
+    lt = torch.zeros(n, dtype=torch.float32)
+    lt[torch.rand(n, generator=g) < 1.0 / 3.0] = -0.0
+    lr = torch.zeros(n, dtype=torch.float32)
+    assert int(torch.signbit(lt.double() - lr.double()).sum()) > n // 4
+    got, _ = check(lt.to(DEV), lr.to(DEV), None, 0.1, label="signed zeros")
+    assert got["ratio_q"] == [1.0, 1.0, 1.0] and got["abs_q"] == [0.0]
+    # then lt and lr drawn from magnitudes across the fp32 range with random
+    # signs: rel_diff's divisor |lt| + 1e-8 runs from 1e-8 to 3.4e38 and its
+    # numerator |delta| up to 6.8e38, the keys span every binade
+    mags = torch.tensor([0.0, 1e-45, 1e-38, 1e-8, 0.5, 1.0, 3.0, 1e20, 3.4e38],
+                        dtype=torch.float32)
+    pick = lambda: mags[torch.randint(0, len(mags), (n,), generator=g)] * \
+        torch.where(torch.rand(n, generator=g) < 0.5, -1.0, 1.0)
+    lt, lr = pick(), pick()
+    check(lt.to(DEV), lr.to(DEV), None, 1.0, label="fp32 range")
+    check(lt.to(DEV), lr.to(DEV), None, 1.0, rq=(0.2, 0.8), aq=(0.1, 0.9),
+          label="fp32 range, other quantiles")
+
+
 def test_candidate_overflow_falls_back_to_the_inputs():
     # every delta in [1, 1.4): one first-pass bucket holds all keys, more than
     # the candidate regions take, so the later passes read the tokens again
