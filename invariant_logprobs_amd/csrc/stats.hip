@@ -24,21 +24,23 @@
 //   1. stats_stream: a fixed number of waves (at most kMaxStreamWaves), each
 //      owning a contiguous token range.  A wave finds its first sequence in
 //      cu_seqlens with a 64-way search, then walks sequences and sub-chunks
-//      in token order and folds every sub-chunk that starts in its range: the
-//      tokens stream in 256-token pieces through a ring of kBufs LDS slots
-//      filled by LDS DMA (lane l folds piece offsets l + 64 i), and a
-//      finished sub-chunk is folded across the wave with a fixed LDS
-//      transpose + DPP tree.  A sequence whose sub-chunks all start in the range is finished
-//      by the wave (per-sequence outputs, and its share of the batch sums in
-//      the wave's partial).  Any other sub-chunk's sums go to slot
+//      in token order and folds every sub-chunk that starts in its range.
+//      Tokens stream as 64-token rows (lane l: token 64 R + l) through a
+//      ring of kRing rows held in registers, loaded with non-temporal
+//      buffer loads kRing rows ahead; a row inside one sub-chunk is folded
+//      as is, a row that holds sub-chunk boundaries is folded lane range by
+//      lane range.  Because every boundary of a sequence's sub-chunks sits
+//      at the same lane, each lane adds the same tokens in the same order
+//      as it would with rows taken from the sub-chunk's start; a finished
+//      sub-chunk is folded across the wave with a fixed LDS transpose + DPP
+//      tree that undoes that rotation.  Every sub-chunk's sums go to slot
 //      floor(c_j / kSubChunk) + j + k (strictly increasing in (j, k), so no
-//      prefix sum is needed to place them), and the wave in whose range such
-//      a sequence starts names it for step 2.
-//   2. stats_final: one thread per streaming wave finishes the sequence that
-//      wave named (its slots added in ascending order, exactly as a wave adds
-//      them), adds the wave's partial; each block folds its threads with a
-//      fixed tree, and the last block to finish folds the block partials with
-//      a fixed tree into the batch aggregates.
+//      prefix sum is needed to place them).
+//   2. stats_final: one thread per sequence adds the sequence's slots in
+//      ascending order and writes its outputs; the sums and maxima of |d|
+//      the streaming waves carried are added in too.  Each block folds its
+//      threads with a fixed tree, and the last block to finish folds the
+//      block partials with a fixed tree into the batch aggregates.
 
 #include "tim_internal.h"
 
@@ -64,18 +66,13 @@ struct alignas(16) BatchAcc {
 
 constexpr int kWave = 64;
 constexpr int kFinBlock = 256;
-constexpr int kPiece = 256;                 // tokens per piece (4 per lane)
+constexpr int kRangeQuantum = 256;          // a streaming wave's range is a multiple of this
 constexpr int kStreamWaves = 4;             // waves per block (each works on its own)
-constexpr uint32_t kBufs = 3;               // pieces in flight per wave (LDS ring slots)
+constexpr int kRing = 8;                    // rows in flight per wave (register ring)
 constexpr int kFoldVals = 4;                // fp64 sums folded across lanes per sub-chunk
-constexpr int64_t kMaxStreamWaves = 4096;   // streaming waves, at most (16 per CU)
+constexpr int64_t kMaxStreamWaves = 8192;   // streaming waves, at most (32 per CU)
 constexpr int64_t kMinRange = 512;          // tokens per streaming wave, at least
 constexpr uint32_t kSC = (uint32_t)kSubChunk;
-
-// piece record flags
-constexpr uint32_t kLastPiece = 1u;         // the piece ends its sub-chunk
-constexpr uint32_t kLastSub = 2u;           // ... and that sub-chunk ends its sequence
-constexpr uint32_t kComplete = 4u;          // the sequence is finished by this wave
 
 // cu_seqlens is a documented precondition; clamping keeps a malformed one
 // from producing an out-of-range access (it can only give wrong numbers)
@@ -109,7 +106,7 @@ struct TokOut {
 // then e^d - 1 = 2^k (e^r - 1) + (2^k - 1); both terms are exact-sign sums, so
 // no cancellation beyond one rounding.  d > 709.78 overflows to +inf and
 // d < -745 gives -1, as the exact value rounds.
-__device__ __attribute__((noinline)) double expm1_large(double d) {
+__device__ __forceinline__ double expm1_large(double d) {
     if (d > 709.782712893384) return INFINITY;
     if (d < -745.0) return -1.0;
     const double kLn2Hi = 6.93147180369123816490e-01;   // 0x3FE62E42FEE00000
@@ -145,13 +142,13 @@ struct Acc {
     // Per wave, over all its sub-chunks: sum and maximum of |d|, which only
     // the batch aggregates use (no per-sequence output depends on them).
     double sabs, mx;
-    __device__ void zero() { sd = sd2 = sk3 = sclip = 0; nvalid = nclip = nnan = 0; }
-};
-
-// A piece in registers for the fold: the lane's tokens 4 l .. 4 l + 3.
-struct Regs {
-    float x[4], y[4];
-    uint32_t m[4];
+    // Zeroed in place (tied asm), so that the sums keep their registers
+    // across every path of the row loop (see acc_row).
+    __device__ void zero() {
+        asm volatile("v_mov_b64 %0, 0\n\tv_mov_b64 %1, 0\n\tv_mov_b64 %2, 0\n\tv_mov_b64 %3, 0"
+                     : "+v"(sd), "+v"(sd2), "+v"(sk3), "+v"(sclip));
+        nvalid = nclip = nnan = 0;
+    }
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -159,152 +156,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kRsrcWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data, no swizzle
 
-// One ring slot in LDS: a piece's lt and lr (one dword per token, in token
-// order), then its mask: four bytes per lane-quad of tokens (kMaskDw), or
-// one zero-extended dword per token.
-template <bool kMaskDw>
-struct Slot {
-    static constexpr int kMaskBytes = kMaskDw ? kPiece : 4 * kPiece;
-    static constexpr int kBytes = 2 * 4 * kPiece + kMaskBytes;
-};
-// LDS DMA copies per piece: lt and lr as one 16-byte load per lane, the
-// mask as one 4-byte load per lane (kMaskDw) or four 1-byte loads.
-template <bool kMask, bool kMaskDw>
-struct PieceLoads { static constexpr int value = !kMask ? 2 : (kMaskDw ? 3 : 6); };
-
-// Copy the piece of tokens [st, st + 256) into a ring slot with LDS DMA.
-// Lane l moves tokens st + 4 l .. st + 4 l + 3 of lt and lr (offsets
-// relative to the descriptors' bases; the descriptors' extents end at the
-// arrays' ends, and a dword out of range reads as 0, so no address leaves
-// the arrays).  The mask: with kMaskDw lane l moves the four bytes from
-// moff + 4 l, where moff places the last lane-quad that reaches the array's
-// end on the array's last four bytes (a dword only partly in range would
-// read as 0); the fold shifts such a lane's bytes back.  Otherwise four
-// one-byte loads per lane (token 64 i + l of the piece, clamped to the
-// array's end).
-template <bool kMask, bool kMaskDw>
-__device__ __forceinline__ void dma_piece(__amdgpu_buffer_rsrc_t rlt, __amdgpu_buffer_rsrc_t rlr,
-                                          __amdgpu_buffer_rsrc_t rm, unsigned char* slot,
-                                          uint32_t st, uint32_t mst, uint32_t mlast, int lane) {
-    const uint32_t o = (st + 4u * (uint32_t)lane) * 4u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rlt, (lds_void*)slot, 16, o, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rlr, (lds_void*)(slot + 4 * kPiece), 16, o, 0, 0, 0);
-    if constexpr (kMask) {
-        if constexpr (kMaskDw) {
-            uint32_t mo = mst + 4u * (uint32_t)lane;
-            mo = mo < mlast ? mo : mlast;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(slot + 8 * kPiece), 4, mo, 0,
-                                                     0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t mo = mst + (uint32_t)(i * kWave + lane);
-                mo = mo < mlast ? mo : mlast;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(slot + 8 * kPiece + i * 256),
-                                                         1, mo, 0, 0, 0);
-            }
-        }
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Rows 0 .. 2 kHalf - 1 of a ring slot for lane l (row i: the piece's token
-// 64 i + l), read in asm: the slot is filled by LDS DMA, which the
-// compiler's own waits would otherwise guard with a wait for every copy in
-// flight.  The caller has waited for the slot's copies.  kMaskDw: the mask
-// byte of token t sits at byte t of the slot's mask, except in the array's
-// last piece (tail), where a lane-quad that reaches past the array's end
-// was read from the array's last four bytes: token t of such a quad q sits
-// at byte 4 q + (mst + t - mlast) (tokens beyond the array read bytes of
-// their own quad and are never counted).
-template <int kRows, bool kMask, bool kMaskDw>
-__device__ __forceinline__ void read_slot(Regs& r, const unsigned char* slot, int lane, bool tail,
-                                          uint32_t mst, uint32_t mlast) {
-    static_assert(kRows == 2 || kRows == 4, "two or four rows");
-    const uint32_t base = lds_addr(slot);
-    const uint32_t a = base + 4u * (uint32_t)lane;
-    if constexpr (kRows == 4)
-        asm volatile(
-            "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
-            "ds_read_b32 %2, %8 offset:512\n\tds_read_b32 %3, %8 offset:768\n\t"
-            "ds_read_b32 %4, %8 offset:1024\n\tds_read_b32 %5, %8 offset:1280\n\t"
-            "ds_read_b32 %6, %8 offset:1536\n\tds_read_b32 %7, %8 offset:1792"
-            : "=&v"(r.x[0]), "=&v"(r.x[1]), "=&v"(r.x[2]), "=&v"(r.x[3]), "=&v"(r.y[0]),
-              "=&v"(r.y[1]), "=&v"(r.y[2]), "=&v"(r.y[3])
-            : "v"(a)
-            : "memory");
-    else
-        asm volatile(
-            "ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:256\n\t"
-            "ds_read_b32 %2, %4 offset:1024\n\tds_read_b32 %3, %4 offset:1280"
-            : "=&v"(r.x[0]), "=&v"(r.x[1]), "=&v"(r.y[0]), "=&v"(r.y[1])
-            : "v"(a)
-            : "memory");
-    if constexpr (kMask && kMaskDw) {
-        if (!tail) {
-            const uint32_t b = base + (uint32_t)lane;
-            if constexpr (kRows == 4)
-                asm volatile(
-                    "ds_read_u8 %0, %4 offset:2048\n\tds_read_u8 %1, %4 offset:2112\n\t"
-                    "ds_read_u8 %2, %4 offset:2176\n\tds_read_u8 %3, %4 offset:2240\n\t"
-                    "s_waitcnt lgkmcnt(0)"
-                    : "=&v"(r.m[0]), "=&v"(r.m[1]), "=&v"(r.m[2]), "=&v"(r.m[3])
-                    : "v"(b)
-                    : "memory");
-            else
-                asm volatile(
-                    "ds_read_u8 %0, %2 offset:2048\n\tds_read_u8 %1, %2 offset:2112\n\t"
-                    "s_waitcnt lgkmcnt(0)"
-                    : "=&v"(r.m[0]), "=&v"(r.m[1])
-                    : "v"(b)
-                    : "memory");
-        } else {
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const uint32_t t = 64u * i + (uint32_t)lane;
-                const uint32_t q = t >> 2;
-                const uint32_t mo = mst + 4u * q;
-                uint32_t pos = t;
-                if (mo > mlast) {
-                    const uint32_t k = mst + t - mlast;
-                    pos = 4u * q + (k < 3u ? k : 3u);
-                }
-                asm volatile("ds_read_u8 %0, %1 offset:2048\n\ts_waitcnt lgkmcnt(0)"
-                             : "=&v"(r.m[i])
-                             : "v"(base + pos)
-                             : "memory");
-            }
-        }
-    } else if constexpr (kMask) {
-        if constexpr (kRows == 4)
-            asm volatile(
-                "ds_read_b32 %0, %4 offset:2048\n\tds_read_b32 %1, %4 offset:2304\n\t"
-                "ds_read_b32 %2, %4 offset:2560\n\tds_read_b32 %3, %4 offset:2816\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(r.m[0]), "=&v"(r.m[1]), "=&v"(r.m[2]), "=&v"(r.m[3])
-                : "v"(a)
-                : "memory");
-        else
-            asm volatile(
-                "ds_read_b32 %0, %2 offset:2048\n\tds_read_b32 %1, %2 offset:2304\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(r.m[0]), "=&v"(r.m[1])
-                : "v"(a)
-                : "memory");
-    } else {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) r.m[i] = 1u;
-    }
 }
 
 // Wave mask of the lanes whose x is finite (v_cmp_class with the six finite
@@ -316,14 +169,6 @@ __device__ __forceinline__ uint64_t finite_mask(double x) {
     return m;
 }
 
-// max(m, |d|) as one v_max_f64 (both operands are finite, so no
-// canonicalisation is needed)
-__device__ __forceinline__ double max_abs(double m, double d) {
-    double r;
-    asm("v_max_f64 %0, %1, |%2|" : "=v"(r) : "v"(m), "v"(d));
-    return r;
-}
-
 // fma(a, b, c) as one v_fma_f64 with c in vector registers, held across
 // the loop (the compiler otherwise copies loop-invariant constants before a
 // two-address fmac, and scalar registers are the scarcer kind here)
@@ -333,19 +178,6 @@ __device__ __forceinline__ double fma_s(double a, double b, double c) {
     return r;
 }
 
-// Fold rows i0 and i0 + 1 of a piece of a sub-chunk: lane l of row i holds
-// piece offset 64 i + l; lim of the piece's tokens lie inside the sub-chunk
-// (64 i0 < lim <= 256), tok0 is the piece's first token.  A piece is folded
-// pair by pair, the second pair only when lim > 128, so lane l adds its
-// offsets in ascending order; the two rows of a pair are independent until
-// then, so their arithmetic interleaves.  A token that does not count (outside the
-// sub-chunk, masked out or non-finite) gets d = 0, which makes its d, d^2,
-// k3 and |d| contributions exactly 0 with no further selects.  Counts are
-// popcounts of the wave masks; the rare ones (non-finite, clipped) are
-// counted in the rare branch, which any such token sends the wave into.  k2
-// is accumulated as d^2 and halved once (a power-of-two scale: exact).  For
-// the truncated weight only the clipped tokens' e^d - 1 is summed (rare
-// path); the unclipped sum is recovered as (sum d + sum k3) - that.
 // The series' coefficients 1/120, 1/24, 1/6 in vector registers for the
 // whole kernel: formed once and made opaque, so that the compiler keeps them
 // rather than moving each into registers again before every use (v_fma_f64
@@ -361,117 +193,146 @@ __device__ __forceinline__ SeriesC series_c(double log_c) {
     return c;
 }
 
-template <int kI0, bool kTok, bool kMask, bool kFull, bool kClipRare>
-__device__ __forceinline__ void fold_pair(Acc& A, const Regs& rg, uint32_t tok0, uint32_t lim,
-                                          int lane, const StatsParamsDev& prm,
-                                          const TokOut& tok, const SeriesC& sc3) {
-    // kClipRare: log C >= 1/32, so a clipped token (d > log C) is among the
-    // |d| > 1/32 tokens of the rare branch and needs no test of its own
-    static_assert(!(kTok && kClipRare), "per-token outputs test the clip on every row");
-    double draw[2], d[2], dp[2];
-    uint64_t m_fin[2];
-    uint64_t m_clip[kClipRare ? 1 : 2], m_sc[kTok ? 2 : 1];
-    double k3x[kTok ? 2 : 1];                      // per-token k3, for the outputs
-    uint64_t rare = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        draw[i] = (double)rg.x[kI0 + i] - (double)rg.y[kI0 + i];
-        // lane predicates as wave masks: each ballot is one compare, the
-        // combinations are scalar, and inverse_ballot reads a lane's bit back
-        uint64_t sc = kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[kI0 + i] != 0) : ~0ull;
-        if constexpr (!kFull) sc &= __builtin_amdgcn_ballot_w64((uint32_t)(64 * (kI0 + i) + lane) < lim);
-        m_fin[i] = sc & finite_mask(draw[i]);
-        A.nvalid += (uint32_t)__popcll(m_fin[i]);
-        rare |= sc & ~m_fin[i];                        // non-finite: counted in the branch
-        if constexpr (kTok) m_sc[i] = sc;
-        if constexpr (!kClipRare) {
-            m_clip[i] = m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > sc3.log_c);
-            rare |= m_clip[i];
-        }
-        d[i] = __builtin_amdgcn_inverse_ballot_w64(m_fin[i]) ? draw[i] : 0.0;
-        // e^d - 1 - d = d dp for |d| <= 1/32, dp = d (1/2 + d/6 + d^2/24 +
-        // d^3/120), truncation below 4e-9 relative
-        double p = fma_s(d[i], sc3.c5, sc3.c4);
-        p = fma_s(p, d[i], sc3.c3);
-        p = fma_s(p, d[i], 0.5);
-        dp[i] = d[i] * p;
-        rare |= __builtin_amdgcn_ballot_w64(!(fabs(d[i]) <= 0.03125));
-        if constexpr (kTok) k3x[i] = d[i] * dp[i];
+// The row's additions to the sums, each accumulator updated in place: sd +=
+// d, sd2 = fma(d, d, sd2), sk3 = fma(d, dp, sk3), sabs += |d|, mx = max(mx,
+// |d|) (both finite: no canonicalisation needed).  Written as one asm block
+// with the accumulators tied, so that every path through a row leaves them
+// in the same registers (with separate destinations the register allocator
+// moved all six between two register sets at every join of the row paths).
+// The trailing wait states separate a v_max_f64 from the next read of its
+// result, as the compiler's hazard recognizer does for that instruction.
+__device__ __forceinline__ void acc_row(Acc& A, double d, double dp) {
+    asm volatile(
+        "v_add_f64 %0, %0, %5\n\t"
+        "v_fma_f64 %1, %5, %5, %1\n\t"
+        "v_fma_f64 %2, %5, %6, %2\n\t"
+        "v_add_f64 %3, %3, |%5|\n\t"
+        "v_max_f64 %4, %4, |%5|\n\t"
+        "s_nop 1"
+        : "+v"(A.sd), "+v"(A.sd2), "+v"(A.sk3), "+v"(A.sabs), "+v"(A.mx)
+        : "v"(d), "v"(dp));
+}
+// acc += x in place (the rare branch's additions)
+__device__ __forceinline__ void acc_inc(double& acc, double x) {
+    asm volatile("v_add_f64 %0, %0, %1" : "+v"(acc) : "v"(x));
+}
+
+// One row of the stream in a lane's registers: token 64 R + lane of the
+// wave's rows (lt, lr and the mask byte, zero-extended).
+struct Row {
+    float x, y;
+    uint32_t m;
+};
+
+// Cache policy of the stream's loads: non-temporal (every token is read
+// once, so its lines need not stay in the caches).
+constexpr int kStreamCpol = 2;
+
+// Row loads: one dword of lt and lr and one byte of the mask per lane, at
+// token offset `off` from the descriptors' bases.  The offset is in the
+// vector operand, which the descriptor's range check covers: a token past
+// the extent reads as 0 and no memory is touched for it.
+template <bool kMask>
+__device__ __forceinline__ void load_row(Row& r, __amdgpu_buffer_rsrc_t rlt,
+                                         __amdgpu_buffer_rsrc_t rlr, __amdgpu_buffer_rsrc_t rm,
+                                         uint32_t off) {
+    r.x = __builtin_bit_cast(float,
+                             __builtin_amdgcn_raw_buffer_load_b32(rlt, off * 4u, 0, kStreamCpol));
+    r.y = __builtin_bit_cast(float,
+                             __builtin_amdgcn_raw_buffer_load_b32(rlr, off * 4u, 0, kStreamCpol));
+    if constexpr (kMask) r.m = __builtin_amdgcn_raw_buffer_load_b8(rm, off, 0, kStreamCpol);
+    else r.m = 1u;
+}
+
+// Wave mask of lanes a .. b - 1 (0 <= a < b <= 64).
+__device__ __forceinline__ uint64_t lane_range(uint32_t a, uint32_t b) {
+    const uint64_t hi = b >= 64u ? ~0ull : ((1ull << b) - 1ull);
+    return hi & (~0ull << a);
+}
+
+// Fold one row into a sub-chunk's sums: the lanes of `sel` (all lanes when
+// kAll) hold tokens of the sub-chunk, lane l adds its token after every
+// earlier token of the sub-chunk it holds.  A token that does not count
+// (outside sel, masked out or non-finite) gets d = 0, which makes its d,
+// d^2, k3 and |d| contributions exactly 0 with no further selects.  Counts
+// are popcounts of wave masks; the rare ones (non-finite, clipped) are
+// counted in the rare branch, which any such token sends the wave into.  k2
+// is accumulated as d^2 and halved once (a power-of-two scale: exact).  For
+// the truncated weight only the clipped tokens' e^d - 1 is summed (rare
+// path); the unclipped sum is recovered as (sum d + sum k3) - that.
+// kClipRare: log C >= 1/32, so a clipped token (d > log C) is among the
+// |d| > 1/32 tokens of the rare branch and needs no test of its own.
+template <bool kTok, bool kMask, bool kAll, bool kClipRare>
+__device__ __forceinline__ void fold_row(Acc& A, const Row& rw, uint64_t sel, uint32_t t0, int lane,
+                                         const StatsParamsDev& prm, const TokOut& tok,
+                                         const SeriesC& sc3) {
+    static_assert(!(kTok && kClipRare), "per-token outputs test the clip on every token");
+    const double draw = (double)rw.x - (double)rw.y;
+    // lane predicates as wave masks: each ballot is one compare, the
+    // combinations are scalar, and inverse_ballot reads a lane's bit back
+    uint64_t sc = kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rw.m != 0) : ~0ull;
+    if constexpr (!kAll) sc &= sel;
+    const uint64_t m_fin = sc & finite_mask(draw);
+    A.nvalid += (uint32_t)__popcll(m_fin);
+    uint64_t rare = sc & ~m_fin;                       // non-finite: counted in the branch
+    uint64_t m_clip = 0;
+    if constexpr (!kClipRare) {
+        m_clip = m_fin & __builtin_amdgcn_ballot_w64(draw > sc3.log_c);
+        rare |= m_clip;
     }
+    const double d = __builtin_amdgcn_inverse_ballot_w64(m_fin) ? draw : 0.0;
+    // e^d - 1 - d = d dp for |d| <= 1/32, dp = d (1/2 + d/6 + d^2/24 +
+    // d^3/120), truncation below 4e-9 relative
+    double p = fma_s(d, sc3.c5, sc3.c4);
+    p = fma_s(p, d, sc3.c3);
+    p = fma_s(p, d, 0.5);
+    double dp = d * p;
+    rare |= __builtin_amdgcn_ballot_w64(!(fabs(d) <= 0.03125));
+    double k3x = 0.0;                                  // the token's k3, for the outputs
+    if constexpr (kTok) k3x = d * dp;
     if (rare != 0) {                                   // uniform test, rarely taken
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint64_t sc = kTok ? m_sc[i]
-                                     : (kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rg.m[kI0 + i] != 0)
-                                              : ~0ull) &
-                                           (kFull ? ~0ull
-                                                  : __builtin_amdgcn_ballot_w64(
-                                                        (uint32_t)(64 * (kI0 + i) + lane) < lim));
-            A.nnan += (uint32_t)__popcll(sc & ~m_fin[i]);
-            const uint64_t clip = kClipRare
-                                      ? m_fin[i] & __builtin_amdgcn_ballot_w64(draw[i] > sc3.log_c)
-                                      : m_clip[i];
-            A.nclip += (uint32_t)__popcll(clip);
-            const bool big = !(fabs(d[i]) <= 0.03125);
-            double k3 = d[i] * dp[i];
-            if (big) {
-                // the exact e^d - 1 - d, added here; the row's fused add
-                // below then adds d * 0
-                k3 = expm1_large(d[i]) - d[i];
-                double e = k3;
-                asm volatile("" : "+v"(e));            // keeps this work inside the branch
-                A.sk3 += e;
-                dp[i] = 0.0;
-            }
-            if (__builtin_amdgcn_inverse_ballot_w64(clip)) {
-                double e = d[i] + k3;
-                asm volatile("" : "+v"(e));
-                A.sclip += e;
-            }
-            if constexpr (kTok) {
-                m_clip[i] = clip;
-                k3x[i] = k3;
-            }
+        A.nnan += (uint32_t)__popcll(sc & ~m_fin);
+        const uint64_t clip =
+            kClipRare ? m_fin & __builtin_amdgcn_ballot_w64(draw > sc3.log_c) : m_clip;
+        A.nclip += (uint32_t)__popcll(clip);
+        double k3 = d * dp;
+        if (!(fabs(d) <= 0.03125)) {
+            // the exact e^d - 1 - d, added here; the fused add below then
+            // adds d * 0
+            k3 = expm1_large(d) - d;
+            acc_inc(A.sk3, k3);
+            dp = 0.0;
+        }
+        if (__builtin_amdgcn_inverse_ballot_w64(clip)) acc_inc(A.sclip, d + k3);
+        if constexpr (kTok) {
+            m_clip = clip;
+            k3x = k3;
         }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        A.sd += d[i];
-        A.sd2 = fma(d[i], d[i], A.sd2);
-        A.sk3 = fma(d[i], dp[i], A.sk3);
-        A.sabs += fabs(d[i]);
-        A.mx = max_abs(A.mx, d[i]);
-    }
+    acc_row(A, d, dp);
     if constexpr (kTok) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t po = (uint32_t)(64 * (kI0 + i) + lane);  // offset in the piece
-            if (po < lim) {
-                // per-token outputs; a non-finite delta reports exp/expm1 as computed
-                const bool scored = __builtin_amdgcn_inverse_ballot_w64(m_sc[i]);
-                const bool fin = __builtin_amdgcn_inverse_ballot_w64(m_fin[i]);
-                const bool clipped = __builtin_amdgcn_inverse_ballot_w64(m_clip[i]);
-                const uint32_t t = tok0 + po;
-                const double dd = scored ? draw[i] : 0.0;
-                const double k3 = k3x[i];
-                const double em1 = d[i] + k3;
-                const double r = 1.0 + em1;
-                const double wgt = clipped ? prm.clip_c : (fin ? r : 0.0);
-                const double rr = fin ? r : (scored ? exp(dd) : 1.0);
-                const double kk3 = fin ? k3 : (scored ? expm1(dd) - dd : 0.0);
-                if (tok.delta) tok.delta[t] = (float)dd;
-                if (tok.ratio) tok.ratio[t] = (float)rr;
-                if (tok.k1) tok.k1[t] = (float)(-dd);
-                if (tok.k2) tok.k2[t] = (float)(0.5 * (dd * dd));
-                if (tok.k3) tok.k3[t] = (float)kk3;
-                if (tok.tis_w) tok.tis_w[t] = (float)wgt;
-                if (tok.clipped) tok.clipped[t] = clipped ? 1 : 0;
-            }
+        if (kAll || __builtin_amdgcn_inverse_ballot_w64(sel)) {
+            // per-token outputs; a non-finite delta reports exp/expm1 as computed
+            const bool scored = __builtin_amdgcn_inverse_ballot_w64(sc);
+            const bool fin = __builtin_amdgcn_inverse_ballot_w64(m_fin);
+            const bool clipped = __builtin_amdgcn_inverse_ballot_w64(m_clip);
+            const uint32_t t = t0 + (uint32_t)lane;
+            const double dd = scored ? draw : 0.0;
+            const double em1 = d + k3x;
+            const double r = 1.0 + em1;
+            const double wgt = clipped ? prm.clip_c : (fin ? r : 0.0);
+            const double rr = fin ? r : (scored ? exp(dd) : 1.0);
+            const double kk3 = fin ? k3x : (scored ? expm1(dd) - dd : 0.0);
+            if (tok.delta) tok.delta[t] = (float)dd;
+            if (tok.ratio) tok.ratio[t] = (float)rr;
+            if (tok.k1) tok.k1[t] = (float)(-dd);
+            if (tok.k2) tok.k2[t] = (float)(0.5 * (dd * dd));
+            if (tok.k3) tok.k3[t] = (float)kk3;
+            if (tok.tis_w) tok.tis_w[t] = (float)wgt;
+            if (tok.clipped) tok.clipped[t] = clipped ? 1 : 0;
         }
     }
 }
-
-
 // 64-bit value of the lane selected by a DPP control (both 32-bit halves
 // moved with v_mov_b32_dpp).
 template <int kCtrl>
@@ -491,8 +352,11 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
 }
 
 // Cross-lane fold of a sub-chunk's four fp64 sums, in a fixed order that
-// depends on lane positions only:
-//   1. every lane stores its four values to the wave's scratch: v[value][lane];
+// depends on offsets inside the sub-chunk only.  Lane l holds the sums of
+// the sub-chunk's offsets congruent to l - rot (mod 64), rot being the lane
+// of its first token:
+//   1. every lane stores its four values to the wave's scratch at that
+//      offset class: v[value][(l - rot) mod 64];
 //   2. lane j < 32 sums v[j / 8][8 (j % 8) .. 8 (j % 8) + 7] left to right;
 //   3. the eight partials of a value (lanes 8 v .. 8 v + 7) are combined by
 //      three DPP steps: neighbours (quad_perm 1,0,3,2), pairs (quad_perm
@@ -500,9 +364,10 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
 //   4. lane 8 v holds value v and is read into scalar registers.
 // A wave's LDS operations complete in issue order, so the reads see the
 // writes without a wait between them; the read block ends in lgkmcnt(0).
-__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int lane, const double* scratch) {
+__device__ __forceinline__ SubPartial finish(const Acc& A, double clip_c, int lane, const double* scratch,
+                                             uint32_t rot) {
     const uint32_t base = lds_addr(scratch);
-    const uint32_t aw = base + 8u * (uint32_t)lane;               // v[0][lane]
+    const uint32_t aw = base + 8u * (((uint32_t)lane - rot) & 63u);   // v[0][(lane - rot) mod 64]
     asm volatile(
         "ds_write2st64_b64 %0, %1, %2 offset1:1\n\t"
         "ds_write2st64_b64 %0, %3, %4 offset0:2 offset1:3"
@@ -666,106 +531,56 @@ __device__ uint32_t lower_bound_cu(const int32_t* __restrict__ cu, uint32_t s, u
     return lo + (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(below));
 }
 
-// One piece to fold: tokens [start, start + lim) of a sub-chunk; lim == 0:
-// none.  id: the sequence's index if the wave finishes it (kComplete), else
-// the sub-chunk's slot.
-struct PieceRec {
-    uint32_t start, lim_flags, id;     // lim_flags = lim | flags << 16
+// A streaming wave's share of the batch sums that no sequence carries: the
+// sum and maximum of |d| over the tokens it folded.
+struct alignas(16) WavePart {
+    double sabs, maxabs;
 };
 
-// A result waiting in LDS for the wave's next flush: a finished sequence's
-// sums (id = its index) or a sub-chunk's sums (id = its slot), the id kept
-// in the sums' spare word with the kind in its top bit.
-typedef SubPartial StageEnt;
-constexpr uint32_t kSlotKind = 0x80000000u;     // set for a sub-chunk's sums
-constexpr int kStage = 21;                      // entries per wave (one per lane at a flush)
-
-// Contribution of a lane's staged entry to the wave's batch sums, folded
-// over the wave's lanes with a fixed butterfly.
-__device__ __forceinline__ void wave_fold_acc(BatchAcc& c) {
-    c.sd = bfly_sum(c.sd); c.sk2 = bfly_sum(c.sk2); c.sk3 = bfly_sum(c.sk3);
-    c.sw = bfly_sum(c.sw);
-    c.md = bfly_sum(c.md); c.mk1 = bfly_sum(c.mk1); c.mk2 = bfly_sum(c.mk2);
-    c.mk3 = bfly_sum(c.mk3);
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        c.nvalid += __shfl_xor(c.nvalid, m);
-        c.nclip += __shfl_xor(c.nclip, m);
-        c.nnan += __shfl_xor(c.nnan, m);
-        c.nonempty += __shfl_xor(c.nonempty, m);
-        c.rejected += __shfl_xor(c.rejected, m);
-        c.rejected_k3 += __shfl_xor(c.rejected_k3, m);
-    }
-}
-
-template <bool kTok, bool kMask, bool kMaskDw>
+template <bool kTok, bool kMask, bool kClipRare>
 __global__ void __launch_bounds__(kWave * kStreamWaves)
 stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                     const uint8_t* __restrict__ mask, const int32_t* __restrict__ cu,
                     uint32_t n, uint32_t s, uint32_t range, uint32_t nwaves, StatsParamsDev prm,
-                    TokOut tok, SeqOut so, SubPartial* __restrict__ slots,
-                    BatchAcc* __restrict__ wpart, int32_t* __restrict__ cross,
+                    TokOut tok, SubPartial* __restrict__ slots, WavePart* __restrict__ wpart,
                     uint32_t* __restrict__ ticket) {
-    __shared__ __attribute__((aligned(16)))
-    unsigned char ring[kStreamWaves][kBufs][Slot<kMaskDw>::kBytes];
     __shared__ __attribute__((aligned(16))) double scratch[kStreamWaves][kFoldVals * kWave];
-    __shared__ StageEnt stage[kStreamWaves][kStage];
-    // per wave, touched by its lane 0 only: the wave's share of the batch sums
-    __shared__ BatchAcc acc_lds[kStreamWaves];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const uint32_t w = blockIdx.x * kStreamWaves + (uint32_t)wv;
     if (w >= nwaves) return;
     if (w == 0 && lane == 0) *ticket = 0u;         // the finalize kernel's counter
-    if (lane == 0) acc_lds[wv] = acc_zero();
     const bool last = w == nwaves - 1;
     const uint32_t b0 = w * range;
     const uint32_t b1 = last ? n : b0 + range;     // the last wave also owns c_j == n
     const uint32_t ja = lower_bound_cu(cu, s, n, b0, lane);
 
-    // Owned empty sequences (c_j in this wave's range, c_{j+1} == c_j): zero
-    // outputs, nothing for the batch; 64 sequences per round.
-    for (uint32_t jb = ja;; jb += kWave) {
-        const uint32_t jj = jb + (uint32_t)lane;
-        bool more = false;
-        if (jj < s) {
-            const uint32_t c = clamp_c(cu[jj], n);
-            if (last || c < b1) {
-                more = true;
-                if (clamp_c(cu[jj + 1], n) <= c) {
-                    BatchAcc dummy = acc_zero();
-                    seq_finish(jj, seq_zero(), prm, so, true, dummy);
-                }
-            }
-        }
-        if (__builtin_amdgcn_ballot_w64(more) != ~0ull) break;
-    }
-
     // ---- the walk over sequences and sub-chunks (wave-uniform state): the
-    // next piece starts at pos, inside the sub-chunk ending at se, of
-    // sequence j ending at ej; id is j if this wave finishes the sequence
-    // (complete), else the current sub-chunk's slot.
-    uint32_t pos = 0, se = 0, ej = 0, j = 0, id = 0;
-    bool complete = false, done = false;
-    int32_t crossj = -1;                           // owned sequence left to step 2
+    // current sub-chunk is tokens [ss, se) of sequence j, which ends at ej,
+    // and its sums go to slot id.  A wave folds the sub-chunks that start in
+    // its range [b0, b1).
+    uint32_t ss = 0, se = 0, ej = 0, j = 0, id = 0;
+    bool done = false;
+    // the walk never goes back: a sequence starts at or after the end of the
+    // last sub-chunk entered (or b0), which holds for any monotone
+    // cu_seqlens and keeps a malformed one from sending the walk backwards
+    uint32_t floor_pos = b0;
 
-    // Enter the first sequence at or after jj that this wave owns and that
-    // has a token (owned empty sequences are written by the pass above).
-    auto enter = [&](uint32_t jj) {
+    // Enter the first sequence at or after jj that starts in this wave's
+    // range and has a token (the finalize kernel writes empty ones).
+    auto enter = [&](uint32_t jj) __attribute__((always_inline)) {
         for (;;) {
             if (jj >= s) { done = true; return; }
-            const uint32_t c = cu_scalar(cu, jj, n);
+            uint32_t c = cu_scalar(cu, jj, n);
+            c = c > floor_pos ? c : floor_pos;
             if (!last && c >= b1) { done = true; return; }
             const uint32_t e = cu_scalar(cu, jj + 1, n);
             if (e > c) {
-                j = jj; ej = e; pos = c;
+                j = jj; ej = e; ss = c;
                 se = c + kSC < e ? c + kSC : e;
-                const uint32_t K = (e - c + kSC - 1) / kSC;
-                complete = last || c + (K - 1) * kSC < b1;
                 // slot of sub-chunk 0: floor(c / SC) + j (below floor(n / SC) +
                 // s + 1 for any clamped c_j <= n and j < s)
-                id = complete ? jj : c / kSC + jj;
-                if (!complete) crossj = (int32_t)jj;
+                id = c / kSC + jj;
                 return;
             }
             ++jj;
@@ -781,9 +596,8 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 const uint32_t k = (b0 - c + kSC - 1) / kSC;
                 const uint32_t st = c + k * kSC;
                 if (st < e && st < b1) {
-                    j = ja - 1; ej = e; pos = st;
+                    j = ja - 1; ej = e; ss = st;
                     se = st + kSC < e ? st + kSC : e;
-                    complete = false;
                     id = c / kSC + (ja - 1) + k;
                     cont = true;
                 }
@@ -791,205 +605,145 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         }
         if (!cont) enter(ja);
     }
-    // The next piece of the walk, then advance.
-    auto next_rec = [&](PieceRec& r) {
-        r.start = pos;
-        const uint32_t left = se - pos;
-        const bool lastp = left <= (uint32_t)kPiece;
-        const uint32_t flags = (lastp ? kLastPiece : 0u) | (complete ? kComplete : 0u) |
-                               (lastp && se == ej ? kLastSub : 0u);
-        r.lim_flags = (lastp ? left : (uint32_t)kPiece) | (flags << 16);
-        r.id = id;
-        if (!lastp) { pos += kPiece; return; }
-        pos = se;
-        if (pos < ej) {
-            // later sub-chunks of this sequence start in later waves' ranges
-            if (pos >= b1) { done = true; return; }
-            se = pos + kSC < ej ? pos + kSC : ej;
-            if (!complete) ++id;
-            return;
-        }
-        enter(j + 1);
+
+    // Rows: row R is tokens tb + 64 R .. tb + 64 R + 63, lane l holds token
+    // tb + 64 R + l.  Every boundary of a sequence's sub-chunks (its start,
+    // and the later sub-chunk starts, kSubChunk = 16 rows apart) sits at lane
+    // c_j mod 64, so lane l holds the sub-chunk offsets o = l - ss (mod 64)
+    // + 64 i in ascending order: the same tokens, in the same order, as lane
+    // (l - ss) mod 64 of rows taken from ss.  The cross-lane fold (finish)
+    // undoes the rotation, so a sub-chunk's sums depend on its tokens only.
+    const uint32_t tb = done ? 0u : (ss & ~63u);
+    // rows [flo, flo + fcnt) lie inside the current sub-chunk and do not end it
+    uint32_t flo = 0, fcnt = 0;
+    auto set_fast = [&]() __attribute__((always_inline)) {
+        if (done) { fcnt = 0; return; }
+        flo = (ss - tb + 63u) >> 6;
+        const uint32_t fhi = (se - 1u - tb) >> 6;    // the row of the sub-chunk's last token
+        fcnt = fhi > flo ? fhi - flo : 0u;
     };
+    set_fast();
+
+    // Descriptors based at tb: offsets are 32-bit (a wave's rows span less
+    // than its range plus a sub-chunk and the ring past it); the extents end
+    // at the arrays' ends.
+    const uint64_t span = (uint64_t)(n - tb);
+    const int ext4 = (int)(uint32_t)(span * 4 < 0xffffffffull ? span * 4 : 0xffffffffull);
+    const __amdgpu_buffer_rsrc_t rlt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(lt + tb), (short)0, ext4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rlr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(lr + tb), (short)0, ext4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rm =
+        kMask ? __builtin_amdgcn_make_buffer_rsrc((void*)(mask + tb), (short)0, (int)(uint32_t)span,
+                                                  kRsrcWord3)
+              : rlt;
 
     Acc A;
     A.zero();
     A.sabs = 0.0;
     A.mx = 0.0;
     const SeriesC sc3 = series_c(prm.log_c);
-    uint32_t nstage = 0;                           // staged entries (uniform)
-    SeqSums S = seq_zero();                        // the sequence being finished
-    // Buffer descriptors based at the wave's first token: every copy's
-    // offset is 32-bit (the wave's tokens span less than a range plus a
-    // sub-chunk past it), and the extents end at the arrays' ends.
-    const uint32_t s0 = done ? 0u : pos;
-    const uint64_t span = (uint64_t)(n - s0);
-    const int ext4 = (int)(uint32_t)(span * 4 < 0xffffffffull ? span * 4 : 0xffffffffull);
-    const __amdgpu_buffer_rsrc_t rlt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(lt + s0), (short)0, ext4, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rlr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(lr + s0), (short)0, ext4, kRsrcWord3);
-    // mask: kMaskDw (n >= 4) reads lane-quads, the last of which sits on the
-    // array's last four bytes, so its base is at most n - 4
-    const uint32_t mbase = kMaskDw ? (s0 < n - 4 ? s0 : n - 4) : s0;
-    const uint32_t mlast = kMaskDw ? n - 4 - mbase : (n > s0 ? n - 1 - s0 : 0u);
-    const __amdgpu_buffer_rsrc_t rm =
-        kMask ? __builtin_amdgcn_make_buffer_rsrc((void*)(mask + mbase), (short)0,
-                                                  (int)(n - mbase), kRsrcWord3)
-              : rlt;
-    constexpr int kLoads = PieceLoads<kMask, kMaskDw>::value;
-    const bool clip_rare = prm.log_c >= 0.03125;
-    // No global store happens between a round's first copy and its last
-    // fold, and every issue makes the same kLoads copies: a slot's copies
-    // are complete once at most (kBufs - 1) kLoads copies are in flight, and
-    // each fold waits for exactly that.  Results wait in LDS; a round stops
-    // issuing when the stage could overflow, and the stage is written out
-    // between rounds.
-    for (;;) {
-        if (!done) {
-            bool paused = false;
-            PieceRec r0, r1, r2;
-            next_rec(r0);
-            // Past the round's end every issue copies the round's first piece
-            // again (never folded): the same copies on every path.
-            const uint32_t d_start = r0.start;
-            dma_piece<kMask, kMaskDw>(rlt, rlr, rm, ring[wv][0], d_start - s0, d_start - mbase,
-                                      mlast, lane);
-            auto issue = [&](unsigned char* slot, PieceRec& r) {
-                const bool go = !done && !paused;
-                if (go) next_rec(r);
-                else r.lim_flags = 0u;
-                const uint32_t st = go ? r.start : d_start;
-                dma_piece<kMask, kMaskDw>(rlt, rlr, rm, slot, st - s0, st - mbase, mlast, lane);
-            };
-            issue(ring[wv][1], r1);
-            issue(ring[wv][2], r2);
-            // Fold the piece in slot (if any).  The slot is refilled as soon as
-            // its tokens are in registers, before the fold, so the copy runs
-            // under the fold's arithmetic.
-            auto step = [&](unsigned char* slot, PieceRec& r) -> bool {
-                const PieceRec cur = r;
-                const uint32_t lim = cur.lim_flags & 0xffffu, flags = cur.lim_flags >> 16;
-                if (lim == 0) return false;
-                // the array's last piece, whose last lane-quads of the mask
-                // were read from the array's last four bytes
-                const bool tail = kMask && kMaskDw && cur.start - mbase + 4u * (kWave - 1) > mlast;
-                wait_vmcnt<(kBufs - 1) * kLoads>();
-                Regs g;
-                if (lim > 2u * kWave)
-                    read_slot<4, kMask, kMaskDw>(g, slot, lane, tail, cur.start - mbase, mlast);
-                else
-                    read_slot<2, kMask, kMaskDw>(g, slot, lane, tail, cur.start - mbase, mlast);
-                issue(slot, r);
-#define TIM_FOLD2(I0, F, C) \
-    fold_pair<I0, kTok, kMask, F, C>(A, g, cur.start, lim, lane, prm, tok, sc3)
-                if (lim == (uint32_t)kPiece) {
-                    if (!kTok && clip_rare) { TIM_FOLD2(0, true, !kTok); TIM_FOLD2(2, true, !kTok); }
-                    else { TIM_FOLD2(0, true, false); TIM_FOLD2(2, true, false); }
-                } else {
-                    if (!kTok && clip_rare) {
-                        TIM_FOLD2(0, false, !kTok);
-                        if (lim > 2u * kWave) TIM_FOLD2(2, false, !kTok);
-                    } else {
-                        TIM_FOLD2(0, false, false);
-                        if (lim > 2u * kWave) TIM_FOLD2(2, false, false);
-                    }
-                }
-#undef TIM_FOLD2
-                if (flags & kLastPiece) {
-                    const SubPartial q = finish(A, prm.clip_c, lane, scratch[wv]);
-                    A.zero();
-                    if (flags & kComplete) {
-                        seq_add(S, q);
-                        if (flags & kLastSub) {
-                            if (lane == 0) {
-                                StageEnt& e = stage[wv][nstage];
-                                e.sd = S.sd; e.sk2 = S.sk2; e.sk3 = S.sk3; e.sw = S.sw;
-                                e.nvalid = (int32_t)S.nvalid; e.nclip = (int32_t)S.nclip;
-                                e.nnan = (int32_t)S.nnan; e.pad = (int32_t)cur.id;
-                            }
-                            S = seq_zero();
-                            ++nstage;
-                        }
-                    } else {
-                        if (lane == 0) {
-                            StageEnt& e = stage[wv][nstage];
-                            e = q;
-                            e.pad = (int32_t)(cur.id | kSlotKind);
-                        }
-                        ++nstage;
-                    }
-                    // room for what the pieces in flight (issued ones included)
-                    // can still finish
-                    if (nstage + kBufs >= (uint32_t)kStage) paused = true;
-                }
-                return true;
-            };
-            for (;;) {
-                if (!step(ring[wv][0], r0)) break;
-                if (!step(ring[wv][1], r1)) break;
-                if (!step(ring[wv][2], r2)) break;
+
+    // The current sub-chunk is complete: fold it across the wave, write its
+    // sums to its slot, go on to the next sub-chunk (the sequence's next
+    // one, or the next sequence's first).
+    auto end_sub = [&]() __attribute__((always_inline)) {
+        SubPartial q = finish(A, prm.clip_c, lane, scratch[wv], ss & 63u);
+        A.zero();
+        if (lane == 0) slots[id] = q;
+        floor_pos = se;
+        if (se < ej) {
+            // later sub-chunks of this sequence may start in later waves' ranges
+            if (se >= b1) {
+                done = true;
+            } else {
+                ss = se;
+                se = ss + kSC < ej ? ss + kSC : ej;
+                ++id;
             }
+        } else {
+            enter(j + 1);
         }
-        // write the staged results out, one per lane
-        {
-            BatchAcc c = acc_zero();
-            if ((uint32_t)lane < nstage) {
-                StageEnt e = stage[wv][lane];
-                const uint32_t id = (uint32_t)e.pad;
-                if (!(id & kSlotKind)) {
-                    SeqSums a;
-                    a.sd = e.sd; a.sk2 = e.sk2; a.sk3 = e.sk3; a.sw = e.sw;
-                    a.nvalid = e.nvalid; a.nclip = e.nclip; a.nnan = e.nnan;
-                    seq_finish(id, a, prm, so, true, c);
-                } else {
-                    e.pad = 0;
-                    slots[id & ~kSlotKind] = e;
-                }
-            }
-            if (nstage > 0) {
-                wave_fold_acc(c);
-                if (lane == 0) acc_add(acc_lds[wv], c);
-            }
-            nstage = 0;
+        set_fast();
+    };
+
+    // A row that holds a sub-chunk boundary (or lies outside every owned
+    // sub-chunk): the lanes of each sub-chunk in it, in token order.
+    auto slow_row = [&](const Row& rw, uint32_t R) __attribute__((always_inline)) {
+        const uint32_t t0 = tb + 64u * R, t1 = t0 + 64u;
+        while (!done && ss < t1) {
+            const uint32_t a = ss > t0 ? ss - t0 : 0u;
+            const uint32_t b = se < t1 ? se - t0 : 64u;
+            fold_row<kTok, kMask, false, kClipRare>(A, rw, lane_range(a, b), t0, lane, prm, tok,
+                                                    sc3);
+            if (se > t1) break;                        // the sub-chunk goes on
+            end_sub();
         }
-        if (done) break;
+    };
+
+    if (!done) {
+        Row ring[kRing];
+#pragma unroll
+        for (int i = 0; i < kRing; ++i)
+            load_row<kMask>(ring[i], rlt, rlr, rm, (uint32_t)(64 * i + lane));
+        uint32_t R = 0;                                // the next row to fold
+        // Fold row R from its ring slot, then refill the slot with the row
+        // kRing ahead.  Once the walk has ended the rows left in the block
+        // fold nothing (no row is fast and no sub-chunk is current).
+        auto step = [&](Row& slot) __attribute__((always_inline)) {
+            if (R - flo < fcnt)
+                fold_row<kTok, kMask, true, kClipRare>(A, slot, ~0ull, tb + 64u * R, lane, prm,
+                                                       tok, sc3);
+            else
+                slow_row(slot, R);
+            load_row<kMask>(slot, rlt, rlr, rm, 64u * (R + kRing) + (uint32_t)lane);
+            ++R;
+        };
+        static_assert(kRing == 8, "the ring is unrolled by hand below");
+        do {
+            step(ring[0]); step(ring[1]); step(ring[2]); step(ring[3]);
+            step(ring[4]); step(ring[5]); step(ring[6]); step(ring[7]);
+        } while (!done);
     }
-    wait_vmcnt<0>();                               // no copy in flight into LDS at the end
     const double wsabs = bfly_sum(A.sabs), wmx = bfly_max(A.mx);
     if (lane == 0) {
-        BatchAcc c = acc_lds[wv];
-        c.sabs += wsabs;
-        c.maxabs = fmax(c.maxabs, wmx);
-        wpart[w] = c;
-        cross[w] = crossj;
+        WavePart p;
+        p.sabs = wsabs;
+        p.maxabs = wmx;
+        wpart[w] = p;
     }
 }
 
+// Step 2: thread t finishes sequence t (its sub-chunks' sums, from their
+// slots, added in ascending order; per-sequence outputs; its contribution
+// to the batch) and adds streaming wave t's partial.  Each block folds its
+// threads with a fixed tree; the last block to finish (a ticket counter,
+// then a device-scope fence) folds the block partials with a fixed tree
+// into the batch vector and resets the ticket for the next call.
 __global__ void __launch_bounds__(kFinBlock)
 stats_final_kernel(const int32_t* __restrict__ cu, uint32_t n, uint32_t s, StatsParamsDev prm,
                    const SubPartial* __restrict__ slots, uint64_t nslots,
-                   const BatchAcc* __restrict__ wpart, const int32_t* __restrict__ cross,
-                   uint32_t nwaves, SeqOut so, BatchAcc* __restrict__ blk,
-                   uint32_t* __restrict__ ticket, double* __restrict__ out) {
+                   const WavePart* __restrict__ wpart, uint32_t nwaves, SeqOut so,
+                   BatchAcc* __restrict__ blk, uint32_t* __restrict__ ticket,
+                   double* __restrict__ out) {
     __shared__ BatchAcc buf[kFinBlock];
     __shared__ uint32_t is_last;
-    const uint32_t w = blockIdx.x * kFinBlock + threadIdx.x;
+    const uint32_t t = blockIdx.x * kFinBlock + threadIdx.x;
     BatchAcc c = acc_zero();
-    if (w < nwaves) {
-        c = wpart[w];
-        const int32_t jj = cross[w];
-        if (jj >= 0 && (uint32_t)jj < s) {
-            // the sequence that starts in wave w's range and ends past it
-            const uint32_t c0 = clamp_c(cu[jj], n), e0 = clamp_c(cu[jj + 1], n);
-            SeqSums a = seq_zero();
-            if (e0 > c0) {
-                const uint32_t K = (e0 - c0 + kSC - 1) / kSC;
-                const uint64_t base = (uint64_t)(c0 / kSC) + (uint32_t)jj;
-                for (uint32_t k = 0; k < K && base + k < nslots; ++k) seq_add(a, slots[base + k]);
-            }
-            seq_finish((uint32_t)jj, a, prm, so, true, c);
+    if (t < s) {
+        const uint32_t c0 = clamp_c(cu[t], n), e0 = clamp_c(cu[t + 1], n);
+        SeqSums a = seq_zero();
+        if (e0 > c0) {
+            const uint32_t K = (e0 - c0 + kSC - 1) / kSC;
+            const uint64_t base = (uint64_t)(c0 / kSC) + t;
+            for (uint32_t k = 0; k < K && base + k < nslots; ++k) seq_add(a, slots[base + k]);
         }
+        seq_finish(t, a, prm, so, true, c);
+    }
+    if (t < nwaves) {
+        const WavePart p = wpart[t];
+        c.sabs += p.sabs;
+        c.maxabs = fmax(c.maxabs, p.maxabs);
     }
     buf[threadIdx.x] = c;
     __syncthreads();
@@ -1069,12 +823,12 @@ hipError_t stream_waves_per_device(bool with_mask, int64_t* out) {
 
 }  // namespace
 
-// Tokens per streaming wave (a multiple of kPiece, at least kMinRange) and
+// Tokens per streaming wave (a multiple of kRangeQuantum, at least kMinRange) and
 // the number of waves, for n tokens and at most `waves` waves.
 void split_tokens(int64_t n, int64_t waves, int64_t* range, int64_t* nwaves) {
     if (waves < 1) waves = 1;
     int64_t r = (n + waves - 1) / waves;
-    r = (r + kPiece - 1) / kPiece * kPiece;
+    r = (r + kRangeQuantum - 1) / kRangeQuantum * kRangeQuantum;
     *range = r < kMinRange ? kMinRange : r;
     *nwaves = n > 0 ? (n + *range - 1) / *range : 1;
 }
@@ -1085,11 +839,12 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     p->s = s;
     // the workspace holds the most waves any device gets
     split_tokens(n, kMaxStreamWaves, &p->range, &p->nwaves);
-    // slot floor(c_j / SC) + j + k <= floor((n - 1) / SC) + s - 1; a slot
-    // index keeps its top bit free (the stage marks the kind there)
+    // slot floor(c_j / SC) + j + k <= floor((n - 1) / SC) + s - 1
     p->nslots = n / kSubChunk + s + 1;
     if (p->nslots >= ((int64_t)1 << 31)) return false;
-    p->nblk_fin = (p->nwaves + kFinBlock - 1) / kFinBlock;
+    // finalize threads: one per sequence and one per streaming wave
+    const int64_t nfin = s > p->nwaves ? s : p->nwaves;
+    p->nblk_fin = (nfin + kFinBlock - 1) / kFinBlock;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -1097,8 +852,7 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
         return o;
     };
     p->slot_off = take((size_t)p->nslots * sizeof(SubPartial));
-    p->wpart_off = take((size_t)p->nwaves * sizeof(BatchAcc));
-    p->cross_off = take((size_t)p->nwaves * sizeof(int32_t));
+    p->wpart_off = take((size_t)p->nwaves * sizeof(WavePart));
     p->blk_off = take((size_t)p->nblk_fin * sizeof(BatchAcc));
     p->ticket_off = take(sizeof(uint32_t));
     p->total_bytes = off;
@@ -1113,8 +867,7 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
     if (p.s <= 0) return hipSuccess;               // no sequence: nothing to write
     unsigned char* ws = (unsigned char*)workspace;
     SubPartial* slots = (SubPartial*)(ws + p.slot_off);
-    BatchAcc* wpart = (BatchAcc*)(ws + p.wpart_off);
-    int32_t* cross = (int32_t*)(ws + p.cross_off);
+    WavePart* wpart = (WavePart*)(ws + p.wpart_off);
     BatchAcc* blk = (BatchAcc*)(ws + p.blk_off);
     uint32_t* ticket = (uint32_t*)(ws + p.ticket_off);
     TokOut to{tok.delta, tok.ratio, tok.k1, tok.k2, tok.k3, tok.tis_w, tok.clipped};
@@ -1136,22 +889,22 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
     const dim3 bdim(kWave * kStreamWaves);
     const bool want_tok = to.delta || to.ratio || to.k1 || to.k2 || to.k3 || to.tis_w ||
                           to.clipped;
-#define TIM_STATS_STREAM(KT, KM, KD)                                                            \
-    hipLaunchKernelGGL((stats_stream_kernel<KT, KM, KD>), grid, bdim, 0, st, lt, lr, mask, cu, n,  \
-                       s, range, nw, prm, to, so, slots, wpart, cross, ticket)
-    // the mask is read four bytes per lane once the array has four
-    const bool mdw = n >= 4;
-    if (want_tok && mask && mdw) TIM_STATS_STREAM(true, true, true);
-    else if (want_tok && mask) TIM_STATS_STREAM(true, true, false);
-    else if (want_tok) TIM_STATS_STREAM(true, false, true);
-    else if (mask && mdw) TIM_STATS_STREAM(false, true, true);
+#define TIM_STATS_STREAM(KT, KM, KC)                                                            \
+    hipLaunchKernelGGL((stats_stream_kernel<KT, KM, KC>), grid, bdim, 0, st, lt, lr, mask, cu, n,  \
+                       s, range, nw, prm, to, slots, wpart, ticket)
+    // log C >= 1/32: a clipped token is also a rare-branch token (|d| > 1/32)
+    const bool clip_rare = prm.log_c >= 0.03125;
+    if (want_tok && mask) TIM_STATS_STREAM(true, true, false);
+    else if (want_tok) TIM_STATS_STREAM(true, false, false);
+    else if (mask && clip_rare) TIM_STATS_STREAM(false, true, true);
     else if (mask) TIM_STATS_STREAM(false, true, false);
-    else TIM_STATS_STREAM(false, false, true);
+    else if (clip_rare) TIM_STATS_STREAM(false, false, true);
+    else TIM_STATS_STREAM(false, false, false);
 #undef TIM_STATS_STREAM
-    hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((nw + kFinBlock - 1) / kFinBlock)),
-                       dim3(kFinBlock), 0, st, cu,
-                       n, s, prm, (const SubPartial*)slots, nslots, (const BatchAcc*)wpart,
-                       (const int32_t*)cross, nw, so, blk, ticket, batch);
+    const uint32_t nfin = s > nw ? s : nw;
+    hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((nfin + kFinBlock - 1) / kFinBlock)),
+                       dim3(kFinBlock), 0, st, cu, n, s, prm, (const SubPartial*)slots, nslots,
+                       (const WavePart*)wpart, nw, so, blk, ticket, batch);
     return hipGetLastError();
 }
 

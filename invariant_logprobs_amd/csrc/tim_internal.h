@@ -108,16 +108,16 @@ struct StatsParamsDev {
 // Workspace layout of tim_mismatch_stats (offsets 256-byte aligned): one
 // slot per possible sub-chunk (sequence j's sub-chunk k sits at slot
 // floor(c_j / kSubChunk) + j + k, strictly increasing, fewer than
-// floor(n / kSubChunk) + s + 1 slots), and per streaming wave its batch
-// partial and the sequence it leaves to the finalize kernel; then the
-// finalize blocks' batch partials and their completion ticket.
+// floor(n / kSubChunk) + s + 1 slots), and per streaming wave the sum and
+// maximum of |delta| over its tokens; then the finalize blocks' batch
+// partials and their completion ticket.
 struct StatsPlan {
     int64_t n, s;
     int64_t range;       // tokens per streaming wave (a multiple of 256)
     int64_t nwaves;      // streaming waves, >= 1
     int64_t nslots;      // sub-chunk slots
-    int64_t nblk_fin;    // finalize blocks (256 streaming waves each)
-    size_t slot_off, wpart_off, cross_off, blk_off, ticket_off, total_bytes;
+    int64_t nblk_fin;    // finalize blocks (256 sequences or streaming waves each)
+    size_t slot_off, wpart_off, blk_off, ticket_off, total_bytes;
 };
 
 bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p);
