@@ -440,12 +440,36 @@ __device__ __forceinline__ BatchAcc acc_zero() {
     return a;
 }
 
-// Fixed-shape tree over the kFinBlock entries of `buf`, result in buf[0].
-__device__ void block_tree(BatchAcc* buf) {
-    for (int stride = kFinBlock / 2; stride > 0; stride >>= 1) {
-        if ((int)threadIdx.x < stride) acc_add(buf[threadIdx.x], buf[threadIdx.x + stride]);
-        __syncthreads();
+// The 64 lanes' partials combined by a fixed xor butterfly (partner
+// distance 1, 2, ..., 32), field by field; every lane ends with the same
+// bits.
+__device__ __forceinline__ void wave_reduce(BatchAcc& c) {
+    c.sd = bfly_sum(c.sd); c.sk2 = bfly_sum(c.sk2); c.sk3 = bfly_sum(c.sk3);
+    c.sw = bfly_sum(c.sw); c.sabs = bfly_sum(c.sabs); c.maxabs = bfly_max(c.maxabs);
+    c.md = bfly_sum(c.md); c.mk1 = bfly_sum(c.mk1); c.mk2 = bfly_sum(c.mk2);
+    c.mk3 = bfly_sum(c.mk3);
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        c.nvalid += __shfl_xor(c.nvalid, m);
+        c.nclip += __shfl_xor(c.nclip, m);
+        c.nnan += __shfl_xor(c.nnan, m);
+        c.nonempty += __shfl_xor(c.nonempty, m);
+        c.rejected += __shfl_xor(c.rejected, m);
+        c.rejected_k3 += __shfl_xor(c.rejected_k3, m);
     }
+}
+
+// A block's partials in a fixed order: each wave's by the butterfly, then
+// the waves' in ascending order.  The result is returned to every thread.
+__device__ BatchAcc block_fold(BatchAcc c, BatchAcc* wbuf) {
+    wave_reduce(c);
+    if ((threadIdx.x & (kWave - 1)) == 0) wbuf[threadIdx.x / kWave] = c;
+    __syncthreads();
+    BatchAcc r = wbuf[0];
+#pragma unroll
+    for (int i = 1; i < kFinBlock / kWave; ++i) acc_add(r, wbuf[i]);
+    __syncthreads();                                   // wbuf may be written again
+    return r;
 }
 
 struct SeqOut {
@@ -726,7 +750,7 @@ stats_final_kernel(const int32_t* __restrict__ cu, uint32_t n, uint32_t s, Stats
                    const WavePart* __restrict__ wpart, uint32_t nwaves, SeqOut so,
                    BatchAcc* __restrict__ blk, uint32_t* __restrict__ ticket,
                    double* __restrict__ out) {
-    __shared__ BatchAcc buf[kFinBlock];
+    __shared__ BatchAcc wbuf[kFinBlock / kWave];
     __shared__ uint32_t is_last;
     const uint32_t t = blockIdx.x * kFinBlock + threadIdx.x;
     BatchAcc c = acc_zero();
@@ -745,13 +769,11 @@ stats_final_kernel(const int32_t* __restrict__ cu, uint32_t n, uint32_t s, Stats
         c.sabs += p.sabs;
         c.maxabs = fmax(c.maxabs, p.maxabs);
     }
-    buf[threadIdx.x] = c;
-    __syncthreads();
-    block_tree(buf);
+    const BatchAcc bsum = block_fold(c, wbuf);
     if (!out) return;
     // the last block to get here folds every block's partial
     if (threadIdx.x == 0) {
-        blk[blockIdx.x] = buf[0];
+        blk[blockIdx.x] = bsum;
         __threadfence();
         is_last = atomicAdd(ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
     }
@@ -760,11 +782,8 @@ stats_final_kernel(const int32_t* __restrict__ cu, uint32_t n, uint32_t s, Stats
     __threadfence();
     c = acc_zero();
     for (uint32_t i = threadIdx.x; i < gridDim.x; i += kFinBlock) acc_add(c, blk[i]);
-    buf[threadIdx.x] = c;
-    __syncthreads();
-    block_tree(buf);
+    const BatchAcc a = block_fold(c, wbuf);
     if (threadIdx.x == 0) {
-        const BatchAcc& a = buf[0];
         const double nv = (double)a.nvalid, ns = (double)a.nonempty;
         const double nin = (double)(a.nvalid + a.nnan);
         auto dv = [](double x, double y) { return y != 0.0 ? x / y : 0.0; };
