@@ -250,8 +250,8 @@ __device__ __forceinline__ uint64_t lane_range(uint32_t a, uint32_t b) {
     return hi & (~0ull << a);
 }
 
-// Fold one row into a sub-chunk's sums: the lanes of `sel` (all lanes when
-// kAll) hold tokens of the sub-chunk, lane l adds its token after every
+// Fold one row into a sub-chunk's sums: the lanes of `sel` hold tokens of
+// the sub-chunk, lane l adds its token after every
 // earlier token of the sub-chunk it holds.  A token that does not count
 // (outside sel, masked out or non-finite) gets d = 0, which makes its d,
 // d^2, k3 and |d| contributions exactly 0 with no further selects.  Counts
@@ -262,7 +262,7 @@ __device__ __forceinline__ uint64_t lane_range(uint32_t a, uint32_t b) {
 // path); the unclipped sum is recovered as (sum d + sum k3) - that.
 // kClipRare: log C >= 1/32, so a clipped token (d > log C) is among the
 // |d| > 1/32 tokens of the rare branch and needs no test of its own.
-template <bool kTok, bool kMask, bool kAll, bool kClipRare>
+template <bool kTok, bool kMask, bool kClipRare>
 __device__ __forceinline__ void fold_row(Acc& A, const Row& rw, uint64_t sel, uint32_t t0, int lane,
                                          const StatsParamsDev& prm, const TokOut& tok,
                                          const SeriesC& sc3) {
@@ -271,7 +271,7 @@ __device__ __forceinline__ void fold_row(Acc& A, const Row& rw, uint64_t sel, ui
     // lane predicates as wave masks: each ballot is one compare, the
     // combinations are scalar, and inverse_ballot reads a lane's bit back
     uint64_t sc = kMask ? __builtin_amdgcn_ballot_w64((uint8_t)rw.m != 0) : ~0ull;
-    if constexpr (!kAll) sc &= sel;
+    sc &= sel;
     const uint64_t m_fin = sc & finite_mask(draw);
     A.nvalid += (uint32_t)__popcll(m_fin);
     uint64_t rare = sc & ~m_fin;                       // non-finite: counted in the branch
@@ -311,7 +311,7 @@ __device__ __forceinline__ void fold_row(Acc& A, const Row& rw, uint64_t sel, ui
     }
     acc_row(A, d, dp);
     if constexpr (kTok) {
-        if (kAll || __builtin_amdgcn_inverse_ballot_w64(sel)) {
+        if (__builtin_amdgcn_inverse_ballot_w64(sel)) {
             // per-token outputs; a non-finite delta reports exp/expm1 as computed
             const bool scored = __builtin_amdgcn_inverse_ballot_w64(sc);
             const bool fin = __builtin_amdgcn_inverse_ballot_w64(m_fin);
@@ -638,16 +638,6 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     // (l - ss) mod 64 of rows taken from ss.  The cross-lane fold (finish)
     // undoes the rotation, so a sub-chunk's sums depend on its tokens only.
     const uint32_t tb = done ? 0u : (ss & ~63u);
-    // rows [flo, flo + fcnt) lie inside the current sub-chunk and do not end it
-    uint32_t flo = 0, fcnt = 0;
-    auto set_fast = [&]() __attribute__((always_inline)) {
-        if (done) { fcnt = 0; return; }
-        flo = (ss - tb + 63u) >> 6;
-        const uint32_t fhi = (se - 1u - tb) >> 6;    // the row of the sub-chunk's last token
-        fcnt = fhi > flo ? fhi - flo : 0u;
-    };
-    set_fast();
-
     // Descriptors based at tb: offsets are 32-bit (a wave's rows span less
     // than its range plus a sub-chunk and the ring past it); the extents end
     // at the arrays' ends.
@@ -688,18 +678,19 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         } else {
             enter(j + 1);
         }
-        set_fast();
     };
 
-    // A row that holds a sub-chunk boundary (or lies outside every owned
-    // sub-chunk): the lanes of each sub-chunk in it, in token order.
-    auto slow_row = [&](const Row& rw, uint32_t R) __attribute__((always_inline)) {
+    // Fold a row: the lanes of each sub-chunk in it, in token order (one
+    // pass for a row inside a sub-chunk).  Every row takes this one path:
+    // with a separate path for rows inside a sub-chunk, the register
+    // allocator moved all six sums between two register sets at every row.
+    auto fold_rows_of = [&](const Row& rw, uint32_t R) __attribute__((always_inline)) {
         const uint32_t t0 = tb + 64u * R, t1 = t0 + 64u;
         while (!done && ss < t1) {
-            const uint32_t a = ss > t0 ? ss - t0 : 0u;
-            const uint32_t b = se < t1 ? se - t0 : 64u;
-            fold_row<kTok, kMask, false, kClipRare>(A, rw, lane_range(a, b), t0, lane, prm, tok,
-                                                    sc3);
+            const uint64_t sel = ss <= t0 && se >= t1
+                                     ? ~0ull
+                                     : lane_range(ss > t0 ? ss - t0 : 0u, se < t1 ? se - t0 : 64u);
+            fold_row<kTok, kMask, kClipRare>(A, rw, sel, t0, lane, prm, tok, sc3);
             if (se > t1) break;                        // the sub-chunk goes on
             end_sub();
         }
@@ -713,20 +704,15 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         uint32_t R = 0;                                // the next row to fold
         // Fold row R from its ring slot, then refill the slot with the row
         // kRing ahead.  Once the walk has ended the rows left in the block
-        // fold nothing (no row is fast and no sub-chunk is current).
+        // fold nothing.
         auto step = [&](Row& slot) __attribute__((always_inline)) {
-            if (R - flo < fcnt)
-                fold_row<kTok, kMask, true, kClipRare>(A, slot, ~0ull, tb + 64u * R, lane, prm,
-                                                       tok, sc3);
-            else
-                slow_row(slot, R);
+            fold_rows_of(slot, R);
             load_row<kMask>(slot, rlt, rlr, rm, 64u * (R + kRing) + (uint32_t)lane);
             ++R;
         };
-        static_assert(kRing == 8, "the ring is unrolled by hand below");
         do {
-            step(ring[0]); step(ring[1]); step(ring[2]); step(ring[3]);
-            step(ring[4]); step(ring[5]); step(ring[6]); step(ring[7]);
+#pragma unroll
+            for (int i = 0; i < kRing; ++i) step(ring[i]);
         } while (!done);
     }
     const double wsabs = bfly_sum(A.sabs), wmx = bfly_max(A.mx);
