@@ -66,6 +66,7 @@ struct alignas(16) BatchAcc {
 
 constexpr int kWave = 64;
 constexpr int kFinBlock = 256;
+constexpr int64_t kMaxFinBlocks = 512;      // finalize blocks, at most
 constexpr int kRangeQuantum = 256;          // a streaming wave's range is a multiple of this
 constexpr int kStreamWaves = 4;             // waves per block (each works on its own)
 constexpr int kRing = 8;                    // rows in flight per wave (register ring)
@@ -738,19 +739,30 @@ stats_final_kernel(const int32_t* __restrict__ cu, uint32_t n, uint32_t s, Stats
                    double* __restrict__ out) {
     __shared__ BatchAcc wbuf[kFinBlock / kWave];
     __shared__ uint32_t is_last;
-    const uint32_t t = blockIdx.x * kFinBlock + threadIdx.x;
+    // thread t takes sequences t, t + T, t + 2T, ... (T threads in the
+    // grid, a function of the call's sizes only) and the streaming waves
+    // with the same indices
+    const uint32_t T = gridDim.x * kFinBlock;
     BatchAcc c = acc_zero();
-    if (t < s) {
+    for (uint32_t t = blockIdx.x * kFinBlock + threadIdx.x; t < s; t += T) {
         const uint32_t c0 = clamp_c(cu[t], n), e0 = clamp_c(cu[t + 1], n);
         SeqSums a = seq_zero();
         if (e0 > c0) {
             const uint32_t K = (e0 - c0 + kSC - 1) / kSC;
             const uint64_t base = (uint64_t)(c0 / kSC) + t;
-            for (uint32_t k = 0; k < K && base + k < nslots; ++k) seq_add(a, slots[base + k]);
+            // the first four sub-chunks' loads issued together, added in order
+            SubPartial q[4];
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k)
+                if (k < K && base + k < nslots) q[k] = slots[base + k];
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k)
+                if (k < K && base + k < nslots) seq_add(a, q[k]);
+            for (uint32_t k = 4; k < K && base + k < nslots; ++k) seq_add(a, slots[base + k]);
         }
         seq_finish(t, a, prm, so, true, c);
     }
-    if (t < nwaves) {
+    for (uint32_t t = blockIdx.x * kFinBlock + threadIdx.x; t < nwaves; t += T) {
         const WavePart p = wpart[t];
         c.sabs += p.sabs;
         c.maxabs = fmax(c.maxabs, p.maxabs);
@@ -828,6 +840,15 @@ hipError_t stream_waves_per_device(bool with_mask, int64_t* out) {
 
 }  // namespace
 
+// Finalize blocks for s sequences and nw streaming waves: one thread each,
+// at most kMaxFinBlocks blocks (their threads then take several; fewer
+// blocks, fewer completion tickets on the one counter).
+static int64_t fin_blocks(int64_t s, int64_t nw) {
+    const int64_t nfin = s > nw ? s : nw;
+    const int64_t b = (nfin + kFinBlock - 1) / kFinBlock;
+    return b < 1 ? 1 : (b > kMaxFinBlocks ? kMaxFinBlocks : b);
+}
+
 // Tokens per streaming wave (a multiple of kRangeQuantum, at least kMinRange) and
 // the number of waves, for n tokens and at most `waves` waves.
 void split_tokens(int64_t n, int64_t waves, int64_t* range, int64_t* nwaves) {
@@ -848,8 +869,7 @@ bool make_stats_plan(int64_t n, int64_t s, StatsPlan* p) {
     p->nslots = n / kSubChunk + s + 1;
     if (p->nslots >= ((int64_t)1 << 31)) return false;
     // finalize threads: one per sequence and one per streaming wave
-    const int64_t nfin = s > p->nwaves ? s : p->nwaves;
-    p->nblk_fin = (nfin + kFinBlock - 1) / kFinBlock;
+    p->nblk_fin = fin_blocks(s, p->nwaves);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -906,8 +926,7 @@ hipError_t launch_mismatch_stats(const StatsPlan& p, const float* lt, const floa
     else if (clip_rare) TIM_STATS_STREAM(false, false, true);
     else TIM_STATS_STREAM(false, false, false);
 #undef TIM_STATS_STREAM
-    const uint32_t nfin = s > nw ? s : nw;
-    hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)((nfin + kFinBlock - 1) / kFinBlock)),
+    hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)fin_blocks(s, nw)),
                        dim3(kFinBlock), 0, st, cu, n, s, prm, (const SubPartial*)slots, nslots,
                        (const WavePart*)wpart, nw, so, blk, ticket, batch);
     return hipGetLastError();
