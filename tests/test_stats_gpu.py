@@ -123,6 +123,21 @@ def test_stress_input_parity():
     assert nv[4].item() == 0            # the all-masked sequence
 
 
+@pytest.mark.parametrize("with_mask", [True, False])
+@pytest.mark.parametrize("token_outputs", [False, True])
+def test_clip_bound_inside_the_series_range(with_mask, token_outputs):
+    # C = 1.01: log C < 1/32, so the kernel tests the clip on every token
+    # instead of leaving it to the rare branch (|delta| > 1/32); ~half the
+    # tokens of this input are clipped
+    lt, lr, mask, cu = _stress(1 << 16, 23)
+    lo, hi = math.log(0.99), math.log(1.01)
+    say(f"clip 1.01, mask {with_mask}, token outputs {token_outputs}")
+    res, ref = run_both(lt, lr, mask if with_mask else None, cu, 1.01, lo, hi,
+                        token_outputs=token_outputs)
+    got = compare(res, ref, lo, hi, cu, "clip 1.01", token=token_outputs)
+    assert got["n_clipped"] > 0
+
+
 def test_large_stats_parity_without_token_outputs():
     n = 1 << 24
     lt, lr, mask, cu = workloads.stats_scale(n, seed=5, device=DEV)
