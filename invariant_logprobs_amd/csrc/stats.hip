@@ -586,18 +586,15 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
     // its range [b0, b1).
     uint32_t ss = 0, se = 0, ej = 0, j = 0, id = 0;
     bool done = false;
-    // the walk never goes back: a sequence starts at or after the end of the
-    // last sub-chunk entered (or b0), which holds for any monotone
-    // cu_seqlens and keeps a malformed one from sending the walk backwards
-    uint32_t floor_pos = b0;
-
     // Enter the first sequence at or after jj that starts in this wave's
-    // range and has a token (the finalize kernel writes empty ones).
-    auto enter = [&](uint32_t jj) __attribute__((always_inline)) {
+    // range and has a token (the finalize kernel writes empty ones); c is
+    // where sequence jj starts, the end of the one before (already read).
+    // One entry of cu_seqlens is read per sequence.  The walk never goes
+    // back: a sequence whose end lies before its start (a malformed
+    // cu_seqlens) is taken as empty and the next one starts at c again.
+    auto enter = [&](uint32_t jj, uint32_t c) __attribute__((always_inline)) {
         for (;;) {
             if (jj >= s) { done = true; return; }
-            uint32_t c = cu_scalar(cu, jj, n);
-            c = c > floor_pos ? c : floor_pos;
             if (!last && c >= b1) { done = true; return; }
             const uint32_t e = cu_scalar(cu, jj + 1, n);
             if (e > c) {
@@ -628,7 +625,10 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 }
             }
         }
-        if (!cont) enter(ja);
+        if (!cont) {
+            const uint32_t c = ja < s ? cu_scalar(cu, ja, n) : n;
+            enter(ja, c > b0 ? c : b0);
+        }
     }
 
     // Rows: row R is tokens tb + 64 R .. tb + 64 R + 63, lane l holds token
@@ -666,7 +666,6 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
         SubPartial q = finish(A, prm.clip_c, lane, scratch[wv], ss & 63u);
         A.zero();
         if (lane == 0) slots[id] = q;
-        floor_pos = se;
         if (se < ej) {
             // later sub-chunks of this sequence may start in later waves' ranges
             if (se >= b1) {
@@ -677,7 +676,7 @@ stats_stream_kernel(const float* __restrict__ lt, const float* __restrict__ lr,
                 ++id;
             }
         } else {
-            enter(j + 1);
+            enter(j + 1, ej);
         }
     };
 
