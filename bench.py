@@ -123,8 +123,9 @@ def main():
         args.no_extras = True
         args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the hot path shards by rows with no exchange; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(scoring shards by rows with no exchange; only the ~21 batch aggregates "
+              "of the statistics would need one)",
               file=sys.stderr)
         sys.exit(2)
 
