@@ -1029,8 +1029,9 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 }
 
 // bf16 partials for small batches: one wave per 128-row half of a
-// vocabulary chunk and 16 NB tokens (NB = 1 or 2 column blocks; the kernel
-// also takes several token groups of 32, unused while kNarrowMaxTokens is 32).
+// vocabulary chunk and 16 NB tokens (NB = 1, 2 or 4 column blocks; the
+// kernel also takes several token groups, unused while kNarrowMaxTokens is
+// one group of 4 blocks).
 //
 // At a few tokens the 256-token tile of lmhead8w_kernel spends almost all
 // of its MFMA work on padding, while the call is bound by reading W once
@@ -1073,7 +1074,7 @@ lmhead8w_kernel(const unsigned char* __restrict__ h, int64_t ldh_b,
 // serves unit ((b >> 3) / ntg) * 8 + (b & 7) and group (b >> 3) % ntg: the
 // groups of a unit run on one XCD (b & 7) next to each other, so W is read
 // from HBM once and from that XCD's L2 by the other group.
-constexpr int kNarrowMaxTokens = 32;   // above: two token groups re-read W, and the
+constexpr int kNarrowMaxTokens = 64;   // above: token groups re-read W, and the
                                         // 256-token kernel is faster
 
 template <bool kEnt, int NB>
@@ -1494,12 +1495,13 @@ bool make_logprob_plan(int64_t n, int64_t d, int64_t v, int dtype, unsigned flag
     p->chunk_tiles = kInvariantChunkTiles;
     p->nchunks = (p->nvtiles + p->chunk_tiles - 1) / p->chunk_tiles;
     p->entropy = entropy;
-    p->narrow = dtype == 0 && n >= 1 && n <= kNarrowMaxTokens;
-    // the K split (flags 2), bf16, one token tile past the small-batch
-    // kernel: twice the workgroups of half the work
-    p->ksplit = (flags == 2u && dtype == 0 && !entropy && !p->narrow && n <= kTileT &&
+    // the K split (flags 2), bf16, 33..256 tokens (one token tile, more than
+    // a 32-token group): twice the workgroups of half the work; asked for,
+    // it takes those sizes from the small-batch kernel too
+    p->ksplit = (flags == 2u && dtype == 0 && !entropy && n > 32 && n <= kTileT &&
                  (d / 64) % 2 == 0) ? 2 : 1;
-    p->nb = n <= 16 ? 1 : 2;
+    p->narrow = dtype == 0 && n >= 1 && n <= kNarrowMaxTokens && p->ksplit == 1;
+    p->nb = n <= 16 ? 1 : (n <= 32 ? 2 : 4);
     p->ntg = (int)((n + 16 * p->nb - 1) / (16 * p->nb));
     const size_t nparts = (size_t)p->nchunks * (p->narrow ? 2 : 1);
     p->part_bytes = align_up(nparts * (size_t)n * sizeof(float2), 256);
@@ -1549,10 +1551,12 @@ hipError_t launch_lmhead_partials(const LogprobPlan& p, const void* h, int64_t l
         };
         if (p.entropy) {
             if (p.nb == 1) gon(lmhead_narrow_kernel<true, 1>);
-            else gon(lmhead_narrow_kernel<true, 2>);
+            else if (p.nb == 2) gon(lmhead_narrow_kernel<true, 2>);
+            else gon(lmhead_narrow_kernel<true, 4>);
         } else {
             if (p.nb == 1) gon(lmhead_narrow_kernel<false, 1>);
-            else gon(lmhead_narrow_kernel<false, 2>);
+            else if (p.nb == 2) gon(lmhead_narrow_kernel<false, 2>);
+            else gon(lmhead_narrow_kernel<false, 4>);
         }
     } else if (p.dtype == 0) {
         if (p.chunk_tiles != 1) return hipErrorInvalidValue;   // one tile per chunk

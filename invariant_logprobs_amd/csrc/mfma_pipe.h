@@ -182,7 +182,7 @@ __device__ __forceinline__ void mfma16_tied_last(f32x4& acc, const u32x4& a, con
 // 20 wait states, more than any MFMA result needs before another instruction
 // reads it, with every accumulator block an operand so that no read of one
 // can be placed before it.  For the small accumulator sets of the narrow
-// kernels (NB = 1, 2).
+// kernels (NB = 1, 2, 4).
 template <int NB>
 __device__ __forceinline__ void mfma_drain(f32x4 (&acc)[8][NB]);
 template <>
@@ -190,6 +190,23 @@ __device__ __forceinline__ void mfma_drain<1>(f32x4 (&a)[8][1]) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
                  : "+a"(a[0][0]), "+a"(a[1][0]), "+a"(a[2][0]), "+a"(a[3][0]), "+a"(a[4][0]),
                    "+a"(a[5][0]), "+a"(a[6][0]), "+a"(a[7][0]));
+}
+// Four blocks: the wait in a first statement that takes blocks 0 and 1 of
+// every row, a second (empty) one taking blocks 2 and 3 right after it (an
+// asm statement takes at most 30 operands); volatile statements keep their
+// order, so no read of any block comes before the wait.
+template <>
+__device__ __forceinline__ void mfma_drain<4>(f32x4 (&a)[8][4]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+a"(a[0][0]), "+a"(a[1][0]), "+a"(a[2][0]), "+a"(a[3][0]), "+a"(a[4][0]),
+                   "+a"(a[5][0]), "+a"(a[6][0]), "+a"(a[7][0]), "+a"(a[0][1]), "+a"(a[1][1]),
+                   "+a"(a[2][1]), "+a"(a[3][1]), "+a"(a[4][1]), "+a"(a[5][1]), "+a"(a[6][1]),
+                   "+a"(a[7][1]));
+    asm volatile(""
+                 : "+a"(a[0][2]), "+a"(a[1][2]), "+a"(a[2][2]), "+a"(a[3][2]), "+a"(a[4][2]),
+                   "+a"(a[5][2]), "+a"(a[6][2]), "+a"(a[7][2]), "+a"(a[0][3]), "+a"(a[1][3]),
+                   "+a"(a[2][3]), "+a"(a[3][3]), "+a"(a[4][3]), "+a"(a[5][3]), "+a"(a[6][3]),
+                   "+a"(a[7][3]));
 }
 template <>
 __device__ __forceinline__ void mfma_drain<2>(f32x4 (&a)[8][2]) {

@@ -55,9 +55,13 @@ def test_logprob_workspace_layout(lib):
     assert lib.tim_logprob_workspace_bytes(n, d, v, 7, 0) == 0
     assert lib.tim_logprob_workspace_bytes(n, d, v, 0, 5) == 0
     # the K-split schedule keeps two partial-logit copies at 33..256 tokens
+    # (at 64 tokens the invariant schedule takes the small-batch kernel,
+    # whose partials are per half chunk; the K split, asked for, takes the
+    # 256-token tile's chunk partials plus the two copies)
     small = lib.tim_logprob_workspace_bytes(64, d, v, tim.TIM_BF16, tim.TIM_SCHED_INVARIANT)
     split = lib.tim_logprob_workspace_bytes(64, d, v, tim.TIM_BF16, tim.TIM_SCHED_SPLIT_K)
-    assert split - small >= 2 * v * 64 * 4
+    assert small == -(-(2 * chunks * 64 * 8) // 256) * 256 + 256
+    assert split >= -(-(chunks * 64 * 8) // 256) * 256 + 256 + 2 * v * 64 * 4
     assert lib.tim_logprob_workspace_bytes(64, d, v, tim.TIM_BF16, tim.TIM_SCHED_FREE) == small
     assert lib.tim_stats_workspace_bytes(1 << 20, 1000) > 0
     assert lib.tim_stats_workspace_bytes(-1, 3) == 0

@@ -275,14 +275,15 @@ def test_qwen3_8b_batch_invariance_sweep():
     assert torch.equal(got.view(torch.int32).cpu(), full_bits)
 
 
-def test_qwen3_8b_small_batches_through_both_narrow_widths():
+def test_qwen3_8b_small_batches_through_every_narrow_width():
     """Batches of 16 and fewer tokens take one token block per wave of the
-    small-batch kernel, 17..32 two; both must give the full batch's bits."""
+    small-batch kernel, 17..32 two, 33..64 four; each must give the full
+    batch's bits, and 65 the 256-token kernel's."""
     w = wl("qwen3_8b")
     full = tim.tim_logprob_forward(w.h, w.w, w.ids)
     torch.cuda.synchronize()
     full_bits = full.view(torch.int32).cpu()
-    for b in (16, 17, 31, 32, 33):
+    for b in (16, 17, 31, 32, 33, 48, 63, 64, 65):
         say(f"qwen3_8b sliced in batches of {b} (first 2048 rows)")
         got = _sliced(w.h[:2048], w.w, w.ids[:2048], workloads.sweep_slices(2048, b))
         diff = int((got.view(torch.int32).cpu() != full_bits[:2048]).sum())
@@ -291,7 +292,7 @@ def test_qwen3_8b_small_batches_through_both_narrow_widths():
 
 @pytest.mark.parametrize("d,v", [(64, 5), (256, 129), (128, 1000), (64, 32001)])
 def test_small_batch_kernel_at_ragged_vocabularies(d, v):
-    """Batches of at most 32 tokens take the small-batch kernel, whose last
+    """Batches of at most 64 tokens take the small-batch kernel, whose last
     half-chunk of a vocabulary that is not a multiple of 128 reads its
     missing rows as zeros: the oracle's values, and the bits the 256-token
     kernel gives the same rows inside a batch of 300."""
@@ -301,7 +302,7 @@ def test_small_batch_kernel_at_ragged_vocabularies(d, v):
     ids = torch.randint(0, v, (300,), generator=g, dtype=torch.int32)
     hd, wd, idd = h.to("cuda"), w.to("cuda"), ids.to("cuda")
     big = tim.tim_logprob_forward(hd, wd, idd)
-    for b in (1, 5, 17, 32):
+    for b in (1, 5, 17, 32, 33, 64):
         say(f"d={d} v={v}: batch of {b}")
         got = tim.tim_logprob_forward(hd[:b].contiguous(), wd, idd[:b].contiguous())
         torch.cuda.synchronize()
