@@ -107,24 +107,38 @@ struct TokOut {
 // then e^d - 1 = 2^k (e^r - 1) + (2^k - 1); both terms are exact-sign sums, so
 // no cancellation beyond one rounding.  d > 709.78 overflows to +inf and
 // d < -745 gives -1, as the exact value rounds.
+// A double formed in scalar registers where it is used: two s_mov_b32 of
+// its bit pattern in a volatile asm, which the compiler cannot hoist out of
+// the rare branch.  As immediates, the compiler kept all of expm1_large's
+// constants in vector registers across the whole row loop, which cost the
+// kernel a wave per SIMD.
+template <uint32_t kLo, uint32_t kHi>
+__device__ __forceinline__ double sconst() {
+    uint32_t lo, hi;
+    asm volatile("s_mov_b32 %0, %2\n\ts_mov_b32 %1, %3" : "=s"(lo), "=s"(hi) : "i"(kLo), "i"(kHi));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ double expm1_large(double d) {
-    if (d > 709.782712893384) return INFINITY;
-    if (d < -745.0) return -1.0;
-    const double kLn2Hi = 6.93147180369123816490e-01;   // 0x3FE62E42FEE00000
-    const double kLn2Lo = 1.90821492927058770002e-10;
-    const double k = rint(d * 1.4426950408889634);
-    const double r = fma(-k, kLn2Lo, fma(-k, kLn2Hi, d));
-    // e^r - 1 = r + r^2/2! + ... + r^12/12!
-    double q = 1.0 / 479001600.0;
-    q = fma(q, r, 1.0 / 39916800.0);
-    q = fma(q, r, 1.0 / 3628800.0);
-    q = fma(q, r, 1.0 / 362880.0);
-    q = fma(q, r, 1.0 / 40320.0);
-    q = fma(q, r, 1.0 / 5040.0);
-    q = fma(q, r, 1.0 / 720.0);
-    q = fma(q, r, 1.0 / 120.0);
-    q = fma(q, r, 1.0 / 24.0);
-    q = fma(q, r, 1.0 / 6.0);
+    if (d > sconst<0xFEFA39EFu, 0x40862E42u>()) return INFINITY;     // 709.782712893384
+    if (d < sconst<0x00000000u, 0xC0874800u>()) return -1.0;         // -745
+    // log2(e), and ln2 split into a high part whose product with k is exact
+    // (0x3FE62E42FEE00000) and a low part
+    const double k = rint(d * sconst<0x652B82FEu, 0x3FF71547u>());
+    const double r = fma(-k, sconst<0x35793C76u, 0x3DEA39EFu>(),
+                         fma(-k, sconst<0xFEE00000u, 0x3FE62E42u>(), d));
+    // e^r - 1 = r + r^2/2! + ... + r^12/12!; the coefficients 1/12! .. 1/3!
+    // are the doubles nearest to them (the bit patterns of 1.0 / k!)
+    double q = sconst<0xEFF8D898u, 0x3E21EED8u>();                    // 1/12!
+    q = fma(q, r, sconst<0x67F544E4u, 0x3E5AE645u>());                // 1/11!
+    q = fma(q, r, sconst<0xB7789F5Cu, 0x3E927E4Fu>());                // 1/10!
+    q = fma(q, r, sconst<0xA556C734u, 0x3EC71DE3u>());                // 1/9!
+    q = fma(q, r, sconst<0x1A01A01Au, 0x3EFA01A0u>());                // 1/8!
+    q = fma(q, r, sconst<0x1A01A01Au, 0x3F2A01A0u>());                // 1/7!
+    q = fma(q, r, sconst<0x16C16C17u, 0x3F56C16Cu>());                // 1/6!
+    q = fma(q, r, sconst<0x11111111u, 0x3F811111u>());                // 1/5!
+    q = fma(q, r, sconst<0x55555555u, 0x3FA55555u>());                // 1/4!
+    q = fma(q, r, sconst<0x55555555u, 0x3FC55555u>());                // 1/3!
     q = fma(q, r, 0.5);
     const double er1 = fma(q * r, r, r);                 // e^r - 1
     const int ki = (int)k;
