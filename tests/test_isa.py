@@ -23,9 +23,9 @@ pytestmark = pytest.mark.skipif(not ic.tools_available() or not os.path.exists(t
 
 MFMA_KERNELS = ("lmhead8w_kernel", "lmhead_narrow_kernel", "lmhead_partials_kernel",
                 "gemm8w_kernel")
-# kernels whose every value must stay in registers
-# the stats stream counts its own copies in flight (vmcnt): a scratch spill
-# would add memory operations of its own to that count
+# kernels whose every value must stay in registers (the statistics stream
+# keeps its row ring in registers: a scratch spill would put memory
+# operations between a row's loads and the waits that count them)
 NO_SCRATCH = ("lmhead8w_kernelILb0E", "lmhead_narrow_kernel", "gemm8w_kernelILi1E",
               "gemm8w_kernelILi2E", "stats_stream_kernel")
 
